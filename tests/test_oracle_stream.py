@@ -1,0 +1,193 @@
+"""Pins for oracle.guidance and oracle.stream: R-CFG identities, the DDIM round
+trip, the identity pipeline, the Stream Batch invariant and the integer
+state machine."""
+import numpy as np
+import pytest
+
+from oracle import guidance, schedule
+from oracle.dit import Denoiser
+from oracle.stream import NotReady, OracleStream, denoise_sequential
+from workloads import gen, get_config
+
+
+def vec(seed, n=50):
+    return np.random.default_rng(seed).standard_normal(n)
+
+
+# ------------------------------------------------------------------ R-CFG identities
+def test_rcfg_gamma_one_returns_conditional():
+    ec, ep = vec(0), vec(1)
+    for delta in (0.0, 0.5, 1.0, 2.0):
+        assert np.allclose(guidance.rcfg(ec, ep, 1.0, delta), ec, atol=1e-15)
+
+
+def test_rcfg_delta_zero_scales_conditional():
+    ec, ep = vec(0), vec(1)
+    assert np.allclose(guidance.rcfg(ec, ep, 1.4, 0.0), 1.4 * ec, atol=1e-15)
+
+
+def test_rcfg_is_extrapolation_away_from_the_negative():
+    # eps_cfg - delta eps' = gamma (eps_c - delta eps'): the guidance direction
+    ec, ep = vec(2), vec(3)
+    g, dl = 1.4, 0.7
+    assert np.allclose(guidance.rcfg(ec, ep, g, dl) - dl * ep, g * (ec - dl * ep), atol=1e-14)
+
+
+def test_virtual_residual_at_entry_is_the_entry_noise():
+    a, b = schedule.sched_coeffs(get_config("tiny"))
+    x0, eps = vec(4), vec(5)
+    for tau in (999, 359, 99, 0):
+        x = guidance.entry_noise(x0, eps, a[tau], b[tau])
+        assert np.allclose(guidance.virtual_residual(x, x0, a[tau], b[tau]), eps, atol=1e-12 / b[tau])
+
+
+def test_true_noise_recovers_x0():
+    a, b = schedule.sched_coeffs(get_config("tiny"))
+    x0, eps = vec(6), vec(7)
+    tau = 359
+    x = guidance.entry_noise(x0, eps, a[tau], b[tau])
+    assert np.allclose(guidance.predict_x0(x, eps, a[tau], b[tau]), x0, atol=1e-14)
+    # renoise to a lower timestep with the same noise equals noising x0 there
+    y = guidance.renoise(x0, eps, a[99], b[99])
+    assert np.allclose(y, guidance.entry_noise(x0, eps, a[99], b[99]), atol=0)
+
+
+# ------------------------------------------------------------------ identity pipeline
+@pytest.mark.parametrize("t_index,cfg_type", [((32,), "self"), ((32, 45), "self"),
+                                              ((0, 16, 32, 45), "self"), ((0, 16, 32, 45), "onetime")])
+def test_identity_pipeline_emits_inputs(t_index, cfg_type):
+    """Denoiser replaced by eps_c := eps'.  With delta = 1 every slot has
+    eps_cfg = eps' and x0_hat = x0*, so each frame leaves as it came in, in
+    push order, n-1 steps after entering -- for any gamma."""
+    cfg = get_config("tiny", t_index=t_index, cfg_type=cfg_type, gamma=3.7, delta=1.0, ssf_on=False)
+    st = OracleStream(cfg, None, identity_denoiser=True)
+    src, nz = gen.LatentSource(cfg), gen.NoiseSource(cfg)
+    n = cfg.n_slots
+    inputs, outs = [], []
+    for k in range(10):
+        x0 = src.next()
+        inputs.append(x0)
+        st.push_frame(x0, nz.next())
+        out, info = st.step()
+        assert info.has_output == (k >= n - 1)
+        if out is not None:
+            assert info.frame_id == k - (n - 1)
+            outs.append(out)
+    assert len(outs) == 10 - (n - 1)
+    for k, o in enumerate(outs):
+        assert np.allclose(o, inputs[k], atol=1e-11)
+
+
+def test_step_without_push_is_not_ready():
+    cfg = get_config("tiny", ssf_on=False)
+    st = OracleStream(cfg, None, identity_denoiser=True)
+    with pytest.raises(NotReady):
+        st.step()
+
+
+# ------------------------------------------------------------------ Stream Batch invariant
+def small_cfg(**kw):
+    base = dict(n_blocks=1, d_model=32, n_heads=2, d_ffn=64, d_freq=16, latent_h=8, latent_w=8,
+                ssf_on=False, sink_tokens=4, window_tokens=48)
+    base.update(kw)
+    return get_config("tiny", **base)
+
+
+@pytest.mark.parametrize("t_index", [(32, 45), (0, 16, 32, 45)])
+def test_stream_batch_equals_sequential_with_frozen_cache(t_index):
+    cfg = small_cfg(t_index=t_index)
+    w = gen.make_weights(cfg)
+    st = OracleStream(cfg, w, freeze_cache=True)
+    net = Denoiser(cfg, w)
+    a, b = schedule.sched_coeffs(cfg)
+    src, nz = gen.LatentSource(cfg), gen.NoiseSource(cfg)
+    frames = []
+    outs = []
+    for k in range(7):
+        x0, e = src.next(), nz.next()
+        info = st.push_frame(x0, e)
+        frames.append((x0, e, info.t0))
+        out, _ = st.step()
+        if out is not None:
+            outs.append(out)
+    taus = schedule.taus_from_t_index(cfg)
+    for k, o in enumerate(outs):
+        x0, e, t0 = frames[k]
+        ref = denoise_sequential(cfg, net, x0.astype(np.float64), e.astype(np.float64), taus, t0, a, b)
+        assert np.array_equal(o, ref)          # bit-identical: same operations, same order
+
+
+def test_stream_batch_equals_sequential_with_live_cache():
+    """With the cache live, frame k's i-th step reads the snapshot of step
+    k+i; replaying each frame alone against those snapshots gives the
+    pipeline's output bit for bit."""
+    cfg = small_cfg(t_index=(0, 16, 32, 45))
+    w = gen.make_weights(cfg)
+    st = OracleStream(cfg, w)
+    net = Denoiser(cfg, w)
+    a, b = schedule.sched_coeffs(cfg)
+    src, nz = gen.LatentSource(cfg), gen.NoiseSource(cfg)
+    frames, outs, snaps = [], [], []
+    for k in range(8):
+        x0, e = src.next(), nz.next()
+        info = st.push_frame(x0, e)
+        frames.append((x0, e, info.t0))
+        snaps.append(st.cache_snapshot())
+        out, _ = st.step()
+        if out is not None:
+            outs.append(out)
+    assert st.kv_valid == cfg.window_tokens and st.sink_count == 1
+    taus = schedule.taus_from_t_index(cfg)
+    n = cfg.n_slots
+    for k, o in enumerate(outs):
+        x0, e, t0 = frames[k]
+        ref = denoise_sequential(cfg, net, x0.astype(np.float64), e.astype(np.float64), taus, t0, a, b,
+                                 snapshots=[snaps[k + i] for i in range(n)])
+        assert np.array_equal(o, ref)
+
+
+# ------------------------------------------------------------------ integer state
+def test_ring_pointer_valid_and_sink_trace():
+    cfg = small_cfg(t_index=(32, 45), window_tokens=40)     # L = 16 tokens per chunk
+    st = OracleStream(cfg, gen.make_weights(cfg))
+    src, nz = gen.LatentSource(cfg), gen.NoiseSource(cfg)
+    trace = []
+    for k in range(7):
+        st.push_frame(src.next(), nz.next())
+        _, info = st.step()
+        trace.append((info.has_output, info.kv_ptr, info.kv_valid, info.sink_count))
+    assert trace == [(False, 0, 0, 0), (True, 16, 16, 1), (True, 32, 32, 1), (True, 8, 40, 1),
+                     (True, 24, 40, 1), (True, 0, 40, 1), (True, 16, 40, 1)]
+    st.kv_reset()
+    assert (st.kv_ptr, st.kv_valid, st.sink_count, st.rope_p) == (0, 0, 0, 0)
+
+
+@pytest.mark.parametrize("T,reset,expect", [(1, 3, [0, 1, 2, 3, 0, 1, 2, 3, 0]),
+                                           (2, 3, [0, 2, 0, 2, 0]),
+                                           (2, 4, [0, 2, 0, 2, 0]),
+                                           (2, 5, [0, 2, 4, 0, 2])])
+def test_rope_temporal_positions_wrap(T, reset, expect):
+    cfg = small_cfg(latent_t=T, rope_reset=reset)
+    st = OracleStream(cfg, None, identity_denoiser=True)
+    src, nz = gen.LatentSource(cfg), gen.NoiseSource(cfg)
+    got = [st.push_frame(src.next(), nz.next()).t0 for _ in expect]
+    assert got == expect
+
+
+def test_ssf_skip_cap_trace():
+    cfg = get_config("tiny", max_skip_frame=3)
+    st = OracleStream(cfg, None, identity_denoiser=True)
+    frame = np.full(cfg.ssf_shape, 9, np.uint8)             # identical frames: p = 1
+    src, nz = gen.LatentSource(cfg), gen.NoiseSource(cfg)
+    skipped = [st.push_frame(src.next(), nz.next(), frame, 0.0).skipped for _ in range(10)]
+    assert skipped == [False, True, True, True, False, True, True, True, False, True]
+    # u at or above p never skips (strict u < p)
+    st2 = OracleStream(cfg, None, identity_denoiser=True)
+    half = frame.copy()
+    r = [st2.push_frame(src.next(), nz.next(), half, 0.999999).skipped for _ in range(3)]
+    assert r == [False, True, True]            # p = 1 > 0.999999
+    st3 = OracleStream(cfg, None, identity_denoiser=True)
+    g = np.zeros(cfg.ssf_shape, np.uint8); g[0, 0, 0] = 5
+    h = np.zeros(cfg.ssf_shape, np.uint8); h[0, 0, 1] = 5
+    r = [st3.push_frame(src.next(), nz.next(), f, 0.0).skipped for f in (g, h, g)]
+    assert r == [False, False, False]           # cos = 0 -> p = 0, u = 0 is not < 0
