@@ -1,0 +1,209 @@
+/*
+ * sd_stream.h -- C ABI of the Stream Batch denoising library for MI355X (gfx950).
+ *
+ * One Stream Batch iteration (StreamDiffusion paper notes, section 1 "Stream
+ * Batch"): n frames that sit at n different denoising steps are stacked into
+ * one batch and advanced by a single denoiser forward; a frame that enters at
+ * step t leaves n steps later.  The denoiser is a DiT whose self-attention
+ * reads a sink-token plus rolling-window KV cache with a RoPE phase reset
+ * (StreamDiffusionV2 summary: "sink-token guided rolling KV cache",
+ * "adaptive sink and RoPE refresh").  The forward is followed by the Residual
+ * CFG estimate and the per-slot latent update (StreamDiffusion paper notes,
+ * section 2 "R-CFG"), and the per-frame controls: the Stochastic Similarity
+ * Filter (section 3 "SSF"; the max_skip_frame cap of the project intro's usage
+ * section), the motion-aware noise rate (StreamDiffusionV2 summary, "motion-aware
+ * noise scheduler") and the adaptive sink refresh.
+ *
+ * The calls mirror the pages' problem statement: a stream is prepared once
+ * (create + set_context: the project intro's prepare(prompt), with the
+ * prompt-side attention K/V pre-computed, feature 5 "Pre-Computation for
+ * KV-Caches"), then frames are pushed one at a time (the intro's stream(image))
+ * and each step advances the pipeline by one denoising step.
+ *
+ * Conventions
+ * -----------
+ * - Every call returns sd_status (0 = OK, < 0 = error); no exceptions cross
+ *   the ABI.  After an error, sd_stream_last_error() describes it.
+ * - Arguments are validated before any HIP call; a failed validation leaves
+ *   the stream unchanged.
+ * - Memory: the caller allocates all device memory (weights, workspace,
+ *   inputs, outputs) and keeps it alive for the lifetime of the handle (weights,
+ *   workspace) or the call (inputs, outputs).  The library allocates no device
+ *   memory; it owns only the opaque host-side handle.
+ * - Streams: all device work is ordered on the hipStream_t given at create.
+ *   push_frame synchronises that stream once to read back a few bytes (SSF
+ *   sums, motion sums); step never synchronises.
+ * - Latents cross the boundary as fp32 [T][C][H][W]; internal precision
+ *   follows config.dtype.
+ * - A handle is not thread-safe; separate handles are independent.
+ */
+#ifndef SD_STREAM_H
+#define SD_STREAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SD_ABI_VERSION 1
+#define SD_MAX_SLOTS 8       /* n, denoising steps in flight */
+#define SD_MAX_ROWS 40       /* rows per forward: B*n (+B for onetime-negative) */
+#define SD_MAX_SINK 8        /* sink entries M */
+
+typedef enum {
+  SD_OK = 0,
+  SD_ERR_ARG = -1,        /* null pointer, out-of-range value */
+  SD_ERR_SHAPE = -2,      /* inconsistent dimensions */
+  SD_ERR_STATE = -3,      /* call not valid in the current state (e.g. queue full) */
+  SD_ERR_WORKSPACE = -4,  /* workspace too small or misaligned */
+  SD_ERR_HIP = -5,        /* a HIP runtime call failed */
+  SD_ERR_NOT_READY = -6   /* step() with no pending frame */
+} sd_status;
+
+typedef enum { SD_DTYPE_F32 = 0, SD_DTYPE_BF16 = 1 } sd_dtype;
+/* R-CFG variants (StreamDiffusion paper notes, section 2): self-negative uses
+ * the frame's own input latent as x0*; onetime-negative adds one forward of
+ * the entering frame under the negative prompt and uses its x0 estimate. */
+typedef enum { SD_CFG_SELF = 0, SD_CFG_ONETIME = 1 } sd_cfg_type;
+typedef enum { SD_SSF_U8 = 0, SD_SSF_LATENT = 1 } sd_ssf_kind;
+
+typedef struct {
+  uint32_t abi_version;            /* must be SD_ABI_VERSION */
+  int32_t dtype;                   /* sd_dtype: weights, activations, KV cache */
+  /* latent chunk geometry [T][C][H][W]; patch is 1 x patch x patch */
+  int32_t latent_t, latent_c, latent_h, latent_w, patch;
+  /* denoiser */
+  int32_t n_blocks, d_model, n_heads, d_ffn, d_freq;
+  int32_t ctx_len;                 /* prompt tokens; 0 = no cross-attention */
+  /* stream batch */
+  int32_t n_slots;                 /* n = number of denoising steps in flight */
+  int32_t t_index[SD_MAX_SLOTS];   /* 50-step grid index per slot: tau = 999 - 20 k */
+  int32_t chunks_per_step;         /* B; this version supports 1 */
+  int32_t cfg_type;                /* sd_cfg_type */
+  double gamma, delta;             /* R-CFG guidance scale and residual weight */
+  /* KV cache, in tokens */
+  int32_t sink_tokens;             /* S, split into sink_entries entries */
+  int32_t sink_entries;            /* M >= 1 when S > 0 */
+  int32_t window_tokens;           /* W (0 or >= tokens per chunk) */
+  double sink_tau;                 /* refresh iff cosine < sink_tau */
+  int32_t rope_reset;              /* temporal RoPE position restarts past this */
+  double rope_base;
+  /* scaled-linear schedule */
+  int32_t n_train_steps;
+  double beta_start, beta_end;
+  /* stochastic similarity filter */
+  int32_t ssf_on, ssf_kind;        /* sd_ssf_kind */
+  int32_t ssf_h, ssf_w, ssf_c;     /* uint8 frame shape [h][w][c] for SD_SSF_U8 */
+  double ssf_eta;                  /* similarity threshold eta < 1 */
+  int32_t max_skip_frame;          /* at most this many consecutive skips */
+  /* motion-aware noise rate */
+  int32_t motion_on, motion_k;
+  double motion_lambda, s_min, s_max, motion_sigma;
+} sd_stream_config;
+
+/*
+ * Denoiser weights: device pointers owned by the caller, element type =
+ * config.dtype (fp32, or bf16 stored as uint16).  Linear weights are
+ * [out][in] row-major; tensors marked [nb] hold all blocks contiguously.
+ * Cross-attention pointers may be NULL when ctx_len == 0.
+ */
+typedef struct {
+  const void *t_w1, *t_b1;     /* [d][d_freq], [d]   timestep MLP, layer 1 */
+  const void *t_w2, *t_b2;     /* [d][d], [d]        timestep MLP, layer 2 */
+  const void *mod_w, *mod_b;   /* [6d][d], [6d]      shared adaLN projection */
+  const void *blk_mod;         /* [nb][6d]           per-block modulation table */
+  const void *pe_w, *pe_b;     /* [d][p*p*C], [d]    patch embedding */
+  const void *qkv_w, *qkv_b;   /* [nb][3d][d], [nb][3d] */
+  const void *o_w, *o_b;       /* [nb][d][d], [nb][d] */
+  const void *cq_w, *cq_b;     /* [nb][d][d], [nb][d]      cross-attention query */
+  const void *ckv_w, *ckv_b;   /* [nb][2d][d], [nb][2d]    prompt-side K/V */
+  const void *co_w, *co_b;     /* [nb][d][d], [nb][d]      cross-attention output */
+  const void *f1_w, *f1_b;     /* [nb][F][d], [nb][F] */
+  const void *f2_w, *f2_b;     /* [nb][d][F], [nb][d] */
+  const void *fin_w, *fin_b;   /* [2d][d], [2d]      final (shift, scale) */
+  const void *head_w, *head_b; /* [p*p*C][d], [p*p*C] */
+} sd_weights;
+
+typedef struct {
+  int32_t skipped;             /* 1: frame dropped by the SSF, nothing queued */
+  int32_t t0;                  /* temporal RoPE base assigned to the chunk (-1 if skipped) */
+  int64_t frame_id;            /* id of the queued frame (-1 if skipped) */
+  double sim;                  /* SSF cosine similarity to the reference (1 if first) */
+  double p;                    /* SSF skip probability */
+  double d;                    /* last motion distance (RMS, latent units) */
+  double s;                    /* noise rate after this push */
+  int32_t taus[SD_MAX_SLOTS];  /* timestep per slot for this frame */
+} sd_push_info;
+
+typedef struct {
+  int64_t step;                /* index of this step */
+  int32_t has_output;          /* 1 if a frame left the pipeline */
+  int32_t rows;                /* rows in the forward */
+  int64_t frame_id;            /* id of the emitted frame (-1 if none) */
+  int32_t kv_ptr, kv_valid;    /* ring write position and valid tokens after the step */
+  int32_t sink_count;          /* filled sink entries after the step */
+  int32_t rope_next;           /* next temporal RoPE base */
+} sd_step_info;
+
+/* Result of the last adaptive sink decision (read back on request). */
+typedef struct {
+  int32_t evaluated;           /* 1 if the last exiting chunk met a full sink set */
+  int32_t entry;               /* least similar entry j* */
+  int32_t refreshed;           /* 1 if entry j* was overwritten */
+  float sim;                   /* cosine of entry j* */
+} sd_sink_info;
+
+typedef struct sd_stream sd_stream;
+
+/* Bytes of device workspace the stream needs (256-byte aligned base). 0 on an
+ * invalid config. */
+size_t sd_stream_workspace_bytes(const sd_stream_config* cfg);
+
+/* Validate cfg, carve the workspace, build the schedule and RoPE tables and
+ * zero the state.  hip_stream is a hipStream_t (NULL = default stream). */
+sd_status sd_stream_create(const sd_stream_config* cfg, const sd_weights* w, void* workspace,
+                           size_t workspace_bytes, void* hip_stream, sd_stream** out);
+
+/* Pre-compute the prompt-side cross-attention K/V of every block from the
+ * positive (and, for onetime-negative, negative) context, [ctx_len][d] device
+ * arrays of config.dtype.  Required before the first step when ctx_len > 0. */
+sd_status sd_stream_set_context(sd_stream* s, const void* ctx_pos, const void* ctx_neg);
+
+/* Offer one chunk.  x0 and noise are device fp32 [T][C][H][W] (noise ~ N(0,1),
+ * the entry noise of this frame); ssf_frame is a device uint8 [h][w][c] image
+ * for SD_SSF_U8 (ignored otherwise); u is the host uniform in [0,1) for the
+ * SSF draw.  A skipped frame changes nothing but the skip counter. */
+sd_status sd_stream_push_frame(sd_stream* s, const float* x0, const float* noise,
+                               const void* ssf_frame, double u, sd_push_info* info);
+
+/* Advance the pipeline by one denoising step.  If a frame leaves, its clean
+ * latent estimate is written to out_latent (device fp32 [T][C][H][W]). */
+sd_status sd_stream_step(sd_stream* s, float* out_latent, sd_step_info* info);
+
+/* Clear the ring, the sink and the RoPE counter (frames in flight continue). */
+sd_status sd_stream_kv_reset(sd_stream* s);
+
+/* Synchronise the stream and report the last adaptive sink decision. */
+sd_status sd_stream_sink_info(sd_stream* s, sd_sink_info* info);
+
+/* Device views of internal buffers, for inspection by tests. */
+typedef enum {
+  SD_BUF_EPS = 0,      /* fp32 [rows][T*C*H*W] denoiser output of the last step, row order of the forward */
+  SD_BUF_RING_K = 1,   /* [nb][H][W][hd] dtype, token at ring position w */
+  SD_BUF_RING_V = 2,   /* [nb][H][hd][W] dtype (V stored transposed) */
+  SD_BUF_SINK_K = 3,   /* [nb][H][S8][hd] dtype, S8 = S rounded up to 8, entry j at j*S/M */
+  SD_BUF_SINK_V = 4,   /* [nb][H][hd][S8] dtype */
+  SD_BUF_RESID = 5,    /* fp32 [rows*L][d] residual stream after the last block */
+  SD_BUF_MOD = 6       /* fp32 [rows][6d] shared modulation of the last step */
+} sd_buffer;
+sd_status sd_stream_buffer(sd_stream* s, int32_t which, void** ptr, size_t* bytes);
+
+void sd_stream_destroy(sd_stream* s);
+const char* sd_stream_last_error(const sd_stream* s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SD_STREAM_H */

@@ -222,6 +222,11 @@ class OracleStream:
         results = {}
         for i, f in rows:
             results[i] = self._denoise(f, f.taus[i], snapshot, self.ctx_kv, collect=(i == n - 1))
+        if not self.identity:
+            # denoiser outputs in forward row order (slots, then the negative row)
+            self.last_eps = [results[i][0] if i == n - 1 else results[i] for i, _ in rows]
+            if cfg.cfg_type == "onetime":
+                self.last_eps.append(eps_neg)
         out = None
         exiting = None
         exit_kv = exit_hidden = None

@@ -1,0 +1,95 @@
+// Shared device-side definitions for the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/sd_stream.h"
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+#define SD_DEV __device__ __forceinline__
+
+SD_DEV float to_f(float x) { return x; }
+SD_DEV float to_f(bf16 x) { return (float)x; }
+template <typename T> SD_DEV T from_f(float x);
+template <> SD_DEV float from_f<float>(float x) { return x; }
+template <> SD_DEV bf16 from_f<bf16>(float x) { return (bf16)x; }
+
+SD_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+SD_DEV double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+SD_DEV long long wave_sum_i64(long long v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Per-row description of one forward.  Passed by value as a kernel argument.
+struct RowInfo {
+  int32_t frame;      // frame-store record of the row's latent
+  int32_t tau;        // timestep
+  int32_t t0;         // temporal RoPE base
+  int32_t kind;       // 0 = denoise slot, 1 = negative-prompt row (onetime R-CFG)
+  int32_t last;       // 1 if this slot is the last (the frame leaves)
+  int32_t ctx;        // 0 = positive context, 1 = negative
+  float a, b;         // sqrt(alpha_tau), sqrt(1 - alpha_tau)
+  float an, bn;       // coefficients of the next slot's timestep
+  float a0, b0;       // entry timestep coefficients (negative row)
+};
+struct RowTable {
+  int32_t R;
+  RowInfo r[SD_MAX_ROWS];
+};
+
+// GEMM epilogue modes: C[m][n] = sum_k A[m][k] * W[n][k], then:
+enum EpiMode {
+  EPI_STORE = 0,      // out[m][n] = T(acc + bias[n])
+  EPI_GELU = 1,       // out[m][n] = T(gelu(acc + bias[n]))
+  EPI_GATE_RESID = 2, // resid[m][n] += gate[r][n] * (acc + bias[n])
+  EPI_RESID = 3,      // resid[m][n] += acc + bias[n]
+  EPI_PATCH = 4,      // resid[m][n] = acc + bias[n]
+  EPI_QKV = 5,        // split q|k|v, RoPE on q,k, scatter to per-head layouts
+  EPI_HEAD = 6,       // eps[r][unpatchify(m, n)] = acc + bias[n]   (fp32)
+  EPI_CTXKV = 7,      // split k|v of a context to per-head cache layouts
+  EPI_F32 = 8         // outf[m][n] = acc + bias[n]  (fp32 out, tests)
+};
+
+struct Epi {
+  int mode;
+  const void* bias;     // [N], element type of the GEMM (may be null)
+  void* out;            // EPI_STORE / EPI_GELU / EPI_F32 output, leading dim ldo
+  int ldo;
+  float* resid;         // fp32 [M][N]
+  const float* mod;     // [R][6d] shared modulation (gate source)
+  const void* blk;      // [6d] block table (element type of the GEMM)
+  int gate_off;         // offset of the gate inside 6d
+  int six_d;            // 6d
+  int L;                // tokens per row
+  // EPI_QKV / EPI_CTXKV destinations (element type of the GEMM)
+  void* q;              // [R][H][L][hd]
+  void* k;              // [R][H][kstride][hd]
+  void* vt;             // [R][H][hd][kstride]   (V stored transposed)
+  int kstride;          // token capacity of the k/vt destination per (row, head)
+  int H, hd, d;
+  int rope;             // apply RoPE to q and k
+  int Hp, Wp;           // token grid of one latent frame
+  int dt, dh;           // RoPE section widths (t, h); w = hd - dt - dh
+  const float2* rope_t; // [positions][dt/2] (cos, sin)
+  const float2* rope_h; // [Hp][dh/2]
+  const float2* rope_w; // [Wp][dw/2]
+  int t0[SD_MAX_ROWS];
+  // EPI_HEAD
+  float* eps;           // [R][T][C][Hl][Wl]
+  int C, Hl, Wl, p, T;
+};

@@ -1,0 +1,276 @@
+// GEMMs of the denoiser: C[m][n] = sum_k A[m][k] W[n][k] with the fused
+// epilogues of the DiT block (bias, GELU, gate * (.) + residual, q|k|v split
+// with 3D RoPE and per-head scatter, unpatchify).
+//
+// bf16: MFMA v_mfma_f32_32x32x16_bf16 on LDS-staged tiles, BK = 64, two LDS
+// stages with register prefetch of the next k-tile, fp32 accumulation.
+// fp32: a vector-ALU tiled kernel (64 x 64 tile, 4 x 4 outputs per thread)
+// for the fp32 configuration.
+#include <cmath>
+
+#include "kernels.h"
+
+namespace sdk {
+
+// ---------------------------------------------------------------------------
+// Epilogue.  acc is C[m][n] (fp32); partner is C[m][n ^ 1] (the other half of
+// a RoPE pair).  T is the element type of the GEMM.
+template <typename T, int MODE>
+SD_DEV void epi_apply(const Epi& E, int m, int n, int N, float acc, float partner) {
+  switch (MODE) {
+    case EPI_STORE: {
+      const float v = acc + (E.bias ? to_f(((const T*)E.bias)[n]) : 0.f);
+      ((T*)E.out)[(int64_t)m * E.ldo + n] = from_f<T>(v);
+      break;
+    }
+    case EPI_F32: {
+      const float v = acc + (E.bias ? to_f(((const T*)E.bias)[n]) : 0.f);
+      ((float*)E.out)[(int64_t)m * E.ldo + n] = v;
+      break;
+    }
+    case EPI_GELU: {
+      const float v = acc + (E.bias ? to_f(((const T*)E.bias)[n]) : 0.f);
+      const float g = 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
+      ((T*)E.out)[(int64_t)m * E.ldo + n] = from_f<T>(g);
+      break;
+    }
+    case EPI_GATE_RESID: {
+      const int r = m / E.L;
+      const float v = acc + to_f(((const T*)E.bias)[n]);
+      const float g = E.mod[(int64_t)r * E.six_d + E.gate_off + n] + to_f(((const T*)E.blk)[E.gate_off + n]);
+      E.resid[(int64_t)m * N + n] += g * v;
+      break;
+    }
+    case EPI_RESID: {
+      const float v = acc + to_f(((const T*)E.bias)[n]);
+      E.resid[(int64_t)m * N + n] += v;
+      break;
+    }
+    case EPI_PATCH: {
+      E.resid[(int64_t)m * N + n] = acc + to_f(((const T*)E.bias)[n]);
+      break;
+    }
+    case EPI_QKV:
+    case EPI_CTXKV: {
+      const int which = n / E.d;
+      const int nn = n - which * E.d;
+      const int h = nn / E.hd, e = nn - h * E.hd;
+      float v = acc + to_f(((const T*)E.bias)[n]);
+      const int r = m / E.L, t = m - r * E.L;
+      const int sec = (MODE == EPI_CTXKV) ? which + 1 : which;   // 0 q, 1 k, 2 v
+      if (E.rope && sec < 2) {
+        const float pv = partner + to_f(((const T*)E.bias)[n ^ 1]);
+        const int hw = E.Hp * E.Wp;
+        const int f = t / hw, y = (t / E.Wp) % E.Hp, x = t % E.Wp;
+        float2 cs;
+        if (e < E.dt)
+          cs = E.rope_t[(E.t0[r] + f) * (E.dt >> 1) + (e >> 1)];
+        else if (e < E.dt + E.dh)
+          cs = E.rope_h[y * (E.dh >> 1) + ((e - E.dt) >> 1)];
+        else
+          cs = E.rope_w[x * ((E.hd - E.dt - E.dh) >> 1) + ((e - E.dt - E.dh) >> 1)];
+        v = (e & 1) ? (pv * cs.y + v * cs.x) : (v * cs.x - pv * cs.y);
+      }
+      const int64_t rh = (int64_t)r * E.H + h;
+      if (sec == 0)
+        ((T*)E.q)[(rh * E.L + t) * E.hd + e] = from_f<T>(v);
+      else if (sec == 1)
+        ((T*)E.k)[(rh * E.kstride + t) * E.hd + e] = from_f<T>(v);
+      else
+        ((T*)E.vt)[(rh * E.hd + e) * E.kstride + t] = from_f<T>(v);
+      break;
+    }
+    case EPI_HEAD: {
+      const int r = m / E.L, t = m - r * E.L;
+      const int hw = E.Hp * E.Wp;
+      const int f = t / hw, y = (t / E.Wp) % E.Hp, x = t % E.Wp;
+      const int c = n % E.C, px = (n / E.C) % E.p, py = n / (E.C * E.p);
+      const int64_t lat = (int64_t)E.T * E.C * E.Hl * E.Wl;
+      const float v = acc + to_f(((const T*)E.bias)[n]);
+      E.eps[r * lat + (((int64_t)f * E.C + c) * E.Hl + y * E.p + py) * E.Wl + x * E.p + px] = v;
+      break;
+    }
+    default:
+      break;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA GEMM.  256 threads = 4 waves arranged WM x WN; each wave owns a
+// (BM/WM) x (BN/WN) block of 32x32 MFMA tiles.
+template <int BM, int BN, int WM, int WN, int MODE>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
+                                                        int M, int N, int K, Epi E, int tiles_m) {
+  constexpr int BK = 64, PAD = 8, LDK = BK + PAD;
+  constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
+  constexpr int CA = BM * (BK / 8) / 256, CB = BN * (BK / 8) / 256;
+  static_assert(FM >= 1 && FN >= 1 && CA >= 1 && CB >= 1, "tile shape");
+  __shared__ __attribute__((aligned(16))) bf16 As[2][BM * LDK];
+  __shared__ __attribute__((aligned(16))) bf16 Bs[2][BN * LDK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WM, wn = wave / WM;
+  const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  bf16x8 ra[CA], rb[CB];
+  const bf16x8 zero8 = {};
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < CA; ++i) {
+      const int c = tid + i * 256, row = c >> 3, kc = (c & 7) * 8;
+      const int gm = m0 + row, gk = k0 + kc;
+      ra[i] = (gm < M && gk < K) ? *(const bf16x8*)(A + (int64_t)gm * K + gk) : zero8;
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      const int c = tid + i * 256, row = c >> 3, kc = (c & 7) * 8;
+      const int gn = n0 + row, gk = k0 + kc;
+      rb[i] = (gn < N && gk < K) ? *(const bf16x8*)(W + (int64_t)gn * K + gk) : zero8;
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CA; ++i) {
+      const int c = tid + i * 256, row = c >> 3, kc = (c & 7) * 8;
+      *(bf16x8*)(&As[buf][row * LDK + kc]) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      const int c = tid + i * 256, row = c >> 3, kc = (c & 7) * 8;
+      *(bf16x8*)(&Bs[buf][row * LDK + kc]) = rb[i];
+    }
+  };
+
+  const int KT = (K + BK - 1) / BK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  const int lr = lane & 31, lk = (lane >> 5) * 8;
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < KT) gload((kt + 1) * BK);
+    const bf16* as = &As[buf][(wm * TM + lr) * LDK + lk];
+    const bf16* bs = &Bs[buf][(wn * TN + lr) * LDK + lk];
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 16) {
+      bf16x8 fa[FM], fb[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) fa[i] = *(const bf16x8*)(as + i * 32 * LDK + kk);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) fb[j] = *(const bf16x8*)(bs + j * 32 * LDK + kk);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < KT) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // C layout of a 32x32 tile: lane holds column lane%32 and rows
+  // 8*(q/4) + 4*(lane/32) + q%4.
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const float v = acc[i][j][q];
+        const float pv = __shfl_xor(v, 1, 64);
+        const int m = m0 + wm * TM + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+        const int n = n0 + wn * TN + j * 32 + (lane & 31);
+        if (m < M && n < N) epi_apply<bf16, MODE>(E, m, n, N, v, pv);
+      }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 vector-ALU GEMM: 64 x 64 tile, BK = 16, 4 x 4 outputs per thread.
+template <int MODE>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A, const float* __restrict__ W,
+                                                       int M, int N, int K, Epi E, int tiles_m) {
+  constexpr int BM = 64, BN = 64, BK = 16;
+  __shared__ float As[BK][BM + 4];
+  __shared__ float Bs[BK][BN + 4];
+  const int tid = threadIdx.x;
+  const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int ty = tid >> 4, tx = tid & 15;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += BK) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + i * 256, row = c >> 4, kk = c & 15;
+      const int gm = m0 + row, gn = n0 + row, gk = k0 + kk;
+      As[kk][row] = (gm < M && gk < K) ? A[(int64_t)gm * K + gk] : 0.f;
+      Bs[kk][row] = (gn < N && gk < K) ? W[(int64_t)gn * K + gk] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BK; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] += a[i] * b[j];
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + ty * 4 + i, n = n0 + tx * 4 + j;
+      if (m < M && n < N) epi_apply<float, MODE>(E, m, n, N, acc[i][j], acc[i][j ^ 1]);
+    }
+}
+
+template <int MODE>
+static hipError_t gemm_mode(hipStream_t s, bool bf, const void* A, const void* W, int M, int N, int K, const Epi& E) {
+  if (!bf) {
+    const int tm = (M + 63) / 64, tn = (N + 63) / 64;
+    gemm_f32_kernel<MODE><<<tm * tn, 256, 0, s>>>((const float*)A, (const float*)W, M, N, K, E, tm);
+    return hipGetLastError();
+  }
+  // Large problems: 256 x 128 tiles; otherwise 128 x 128.
+  const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 127) / 128);
+  if (t256 >= 512) {
+    const int tm = (M + 255) / 256, tn = (N + 127) / 128;
+    gemm_bf16_kernel<256, 128, 2, 2, MODE><<<tm * tn, 256, 0, s>>>((const bf16*)A, (const bf16*)W, M, N, K, E, tm);
+  } else {
+    const int tm = (M + 127) / 128, tn = (N + 127) / 128;
+    gemm_bf16_kernel<128, 128, 2, 2, MODE><<<tm * tn, 256, 0, s>>>((const bf16*)A, (const bf16*)W, M, N, K, E, tm);
+  }
+  return hipGetLastError();
+}
+
+hipError_t gemm(hipStream_t s, bool bf, const void* A, const void* W, int M, int N, int K, const Epi& E) {
+  if (M == 0 || N == 0) return hipSuccess;
+  switch (E.mode) {
+    case EPI_STORE: return gemm_mode<EPI_STORE>(s, bf, A, W, M, N, K, E);
+    case EPI_GELU: return gemm_mode<EPI_GELU>(s, bf, A, W, M, N, K, E);
+    case EPI_GATE_RESID: return gemm_mode<EPI_GATE_RESID>(s, bf, A, W, M, N, K, E);
+    case EPI_RESID: return gemm_mode<EPI_RESID>(s, bf, A, W, M, N, K, E);
+    case EPI_PATCH: return gemm_mode<EPI_PATCH>(s, bf, A, W, M, N, K, E);
+    case EPI_QKV: return gemm_mode<EPI_QKV>(s, bf, A, W, M, N, K, E);
+    case EPI_HEAD: return gemm_mode<EPI_HEAD>(s, bf, A, W, M, N, K, E);
+    case EPI_CTXKV: return gemm_mode<EPI_CTXKV>(s, bf, A, W, M, N, K, E);
+    case EPI_F32: return gemm_mode<EPI_F32>(s, bf, A, W, M, N, K, E);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace sdk

@@ -1,0 +1,496 @@
+// Memory-bound kernels of the step: entry noising, the fused R-CFG / update
+// epilogue, patch gathering, LayerNorm + adaLN modulation, the timestep
+// embedding and its GEMVs, KV ring append and sink copies, and the exact
+// reductions of the per-frame controls (SSF, motion, sink cosine).
+#include <cmath>
+
+#include "kernels.h"
+
+namespace sdk {
+
+static inline unsigned grid1(int64_t n, int block) { return (unsigned)((n + block - 1) / block); }
+
+// ---------------------------------------------------------------------------
+// Entry noising of a new frame (x_tau0 = a x0 + b eps): the start of a frame's
+// trajectory through the slots.
+__global__ void entry_noise_kernel(const float* __restrict__ x0, const float* __restrict__ noise,
+                                   float* __restrict__ xs, float* __restrict__ x0s, int64_t n, float a, float b) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float v = x0[i];
+  xs[i] = a * v + b * noise[i];
+  if (x0s) x0s[i] = v;
+}
+
+hipError_t entry_noise(hipStream_t s, const float* x0, const float* noise, float* xs, float* x0s, int64_t n,
+                       float a, float b) {
+  if (n == 0) return hipSuccess;
+  entry_noise_kernel<<<grid1(n, 256), 256, 0, s>>>(x0, noise, xs, x0s, n, a, b);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Residual CFG (StreamDiffusion paper notes, section 2): virtual residual
+// noise eps' = (x - a x0*) / b, eps_cfg = delta eps' + gamma (eps_c - delta eps'),
+// then x0_hat = (x - b eps_cfg) / a and either re-noise to the next slot's
+// timestep or emit x0_hat.  For onetime-negative R-CFG the entering row first
+// turns the negative row's output into its x0* estimate.
+__global__ void rcfg_update_kernel(RowTable rt, float* __restrict__ store_x, float* __restrict__ store_x0s,
+                                   const float* __restrict__ eps, float* __restrict__ out, int64_t lat, float gamma,
+                                   float delta, int neg_row) {
+  const int r = blockIdx.y;
+  const RowInfo ri = rt.r[r];
+  if (ri.kind != 0) return;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= lat) return;
+  const int64_t off = (int64_t)ri.frame * lat + i;
+  const float x = store_x[off];
+  float x0s;
+  if (neg_row >= 0 && r == 0) {
+    const float en = eps[(int64_t)neg_row * lat + i];
+    x0s = (x - ri.b0 * en) / ri.a0;
+    store_x0s[off] = x0s;
+  } else {
+    x0s = store_x0s[off];
+  }
+  const float ep = (x - ri.a * x0s) / ri.b;
+  const float ec = eps[(int64_t)r * lat + i];
+  const float ecfg = delta * ep + gamma * (ec - delta * ep);
+  const float x0h = (x - ri.b * ecfg) / ri.a;
+  if (ri.last) {
+    out[i] = x0h;
+  } else {
+    store_x[off] = ri.an * x0h + ri.bn * ecfg;
+  }
+}
+
+hipError_t rcfg_update(hipStream_t s, const RowTable& rt, float* store_x, float* store_x0s, const float* eps,
+                       float* out, int64_t lat, float gamma, float delta, int neg_row) {
+  dim3 g(grid1(lat, 256), rt.R);
+  rcfg_update_kernel<<<g, 256, 0, s>>>(rt, store_x, store_x0s, eps, out, lat, gamma, delta, neg_row);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Patch gather: token (t, y, x) of row r gets the p x p x C patch in
+// (py, px, c) order.
+template <typename T>
+__global__ void patchify_kernel(RowTable rt, const float* __restrict__ store_x, T* __restrict__ out, int64_t lat,
+                                int Tn, int C, int Hl, int Wl, int p) {
+  const int r = blockIdx.y;
+  const int Hp = Hl / p, Wp = Wl / p;
+  const int P = p * p * C;
+  const int64_t per_row = (int64_t)Tn * Hp * Wp * P;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= per_row) return;
+  const int v = (int)(i % P);
+  const int64_t tok = i / P;
+  const int xq = (int)(tok % Wp), yq = (int)((tok / Wp) % Hp), f = (int)(tok / ((int64_t)Wp * Hp));
+  const int c = v % C, px = (v / C) % p, py = v / (C * p);
+  const float* src = store_x + (int64_t)rt.r[r].frame * lat;
+  const float val = src[(((int64_t)f * C + c) * Hl + (yq * p + py)) * Wl + (xq * p + px)];
+  out[(int64_t)r * per_row + i] = from_f<T>(val);
+}
+
+hipError_t patchify(hipStream_t s, bool bf, const RowTable& rt, const float* store_x, void* out, int64_t lat,
+                    int T, int C, int Hl, int Wl, int p) {
+  const int64_t per_row = (int64_t)T * (Hl / p) * (Wl / p) * p * p * C;
+  dim3 g(grid1(per_row, 256), rt.R);
+  if (bf)
+    patchify_kernel<bf16><<<g, 256, 0, s>>>(rt, store_x, (bf16*)out, lat, T, C, Hl, Wl, p);
+  else
+    patchify_kernel<float><<<g, 256, 0, s>>>(rt, store_x, (float*)out, lat, T, C, Hl, Wl, p);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// LayerNorm + adaLN modulation, one wave per token row.  Mean and variance
+// are two passes over the row (population variance); the row stays in cache.
+template <typename T>
+__global__ __launch_bounds__(256) void ln_mod_kernel(const float* __restrict__ x, T* __restrict__ out, int M, int d,
+                                                     int L, const float* __restrict__ mod, const T* __restrict__ blk,
+                                                     int shift_off, int scale_off, int six_d, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const float4* xr = (const float4*)(x + (int64_t)row * d);
+  const int nv = d >> 2;
+  float sum = 0.f;
+  for (int j = lane; j < nv; j += 64) {
+    const float4 v = xr[j];
+    sum += (v.x + v.y) + (v.z + v.w);
+  }
+  const float mu = wave_sum(sum) / (float)d;
+  float sq = 0.f;
+  for (int j = lane; j < nv; j += 64) {
+    const float4 v = xr[j];
+    const float a = v.x - mu, b = v.y - mu, c = v.z - mu, e = v.w - mu;
+    sq += (a * a + b * b) + (c * c + e * e);
+  }
+  const float rstd = 1.0f / sqrtf(wave_sum(sq) / (float)d + eps);
+  const int r = row / L;
+  const float* mr = mod ? mod + (int64_t)r * six_d : nullptr;
+  T* orow = out + (int64_t)row * d;
+  for (int j = lane; j < nv; j += 64) {
+    const float4 v = xr[j];
+    float o[4] = {(v.x - mu) * rstd, (v.y - mu) * rstd, (v.z - mu) * rstd, (v.w - mu) * rstd};
+    if (mr) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = 4 * j + q;
+        const float sh = mr[shift_off + c] + (blk ? to_f(blk[shift_off + c]) : 0.f);
+        const float sc = mr[scale_off + c] + (blk ? to_f(blk[scale_off + c]) : 0.f);
+        o[q] = o[q] * (1.0f + sc) + sh;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) orow[4 * j + q] = from_f<T>(o[q]);
+  }
+}
+
+hipError_t ln_mod(hipStream_t s, bool bf, const float* x, void* out, int M, int d, int L, const float* mod,
+                  const void* blk, int shift_off, int scale_off, int six_d, float eps) {
+  if (M == 0) return hipSuccess;
+  const unsigned g = (unsigned)((M + 3) / 4);
+  if (bf)
+    ln_mod_kernel<bf16><<<g, 256, 0, s>>>(x, (bf16*)out, M, d, L, mod, (const bf16*)blk, shift_off, scale_off, six_d,
+                                          eps);
+  else
+    ln_mod_kernel<float><<<g, 256, 0, s>>>(x, (float*)out, M, d, L, mod, (const float*)blk, shift_off, scale_off,
+                                           six_d, eps);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Sinusoidal timestep embedding in fp64: e = [cos(tau w_j), sin(tau w_j)],
+// w_j = 10000^(-j / (D/2)).
+__global__ void temb_embed_kernel(RowTable rt, float* __restrict__ out, int d_freq) {
+  const int r = blockIdx.x;
+  const int half = d_freq / 2;
+  for (int j = threadIdx.x; j < half; j += blockDim.x) {
+    const double w = pow(10000.0, -(double)j / (double)half);
+    const double arg = (double)rt.r[r].tau * w;
+    out[(int64_t)r * d_freq + j] = (float)cos(arg);
+    out[(int64_t)r * d_freq + half + j] = (float)sin(arg);
+  }
+}
+
+hipError_t temb_embed(hipStream_t s, const RowTable& rt, float* out, int d_freq) {
+  temb_embed_kernel<<<rt.R, 128, 0, s>>>(rt, out, d_freq);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Small-batch GEMV: the weight matrix is streamed once for all R rows.  One
+// wave per output feature, 8 weights (16 B bf16 / 32 B fp32) per lane per load.
+template <typename T>
+__global__ __launch_bounds__(256) void gemv_kernel(const float* __restrict__ x, const T* __restrict__ W,
+                                                   const T* __restrict__ bias, float* __restrict__ y, int R, int N,
+                                                   int K, int act) {
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nw = gridDim.x * 4;
+  const int K8 = K >> 3;
+  for (int n = wave; n < N; n += nw) {
+    float acc[SD_MAX_ROWS];
+#pragma unroll
+    for (int r = 0; r < SD_MAX_ROWS; ++r) acc[r] = 0.f;
+    const T* wr = W + (int64_t)n * K;
+    for (int c = lane; c < K8; c += 64) {
+      float w[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) w[q] = to_f(wr[8 * c + q]);
+#pragma unroll
+      for (int r = 0; r < SD_MAX_ROWS; ++r) {
+        if (r < R) {
+          const float4* xr = (const float4*)(x + (int64_t)r * K + 8 * c);
+          const float4 a = xr[0], b = xr[1];
+          acc[r] += w[0] * a.x + w[1] * a.y + w[2] * a.z + w[3] * a.w + w[4] * b.x + w[5] * b.y + w[6] * b.z +
+                    w[7] * b.w;
+        }
+      }
+    }
+    const float bn = bias ? to_f(bias[n]) : 0.f;
+#pragma unroll
+    for (int r = 0; r < SD_MAX_ROWS; ++r) {
+      if (r < R) {
+        float v = wave_sum(acc[r]) + bn;
+        if (act == 1) v = v / (1.0f + expf(-v));
+        if (lane == 0) y[(int64_t)r * N + n] = v;
+      }
+    }
+  }
+}
+
+hipError_t gemv(hipStream_t s, bool bf, const float* x, const void* W, const void* b, float* y, int R, int N, int K,
+                int act) {
+  const int blocks = (N + 3) / 4 < 2048 ? (N + 3) / 4 : 2048;
+  if (bf)
+    gemv_kernel<bf16><<<blocks, 256, 0, s>>>(x, (const bf16*)W, (const bf16*)b, y, R, N, K, act);
+  else
+    gemv_kernel<float><<<blocks, 256, 0, s>>>(x, (const float*)W, (const float*)b, y, R, N, K, act);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// KV ring append: the exiting chunk's own K [H][L][hd] and V^T [H][hd][L]
+// go to ring positions (ptr + t) mod W; its first Se tokens optionally become
+// a sink entry.
+template <typename T>
+__global__ void kv_append_kernel(const T* __restrict__ kown, const T* __restrict__ vtown, T* __restrict__ ringK,
+                                 T* __restrict__ ringVT, int H, int hd, int L, int W, int ptr, T* __restrict__ sinkK,
+                                 T* __restrict__ sinkVT, int S8, int sink_off, int Se) {
+  const int64_t per_head = (int64_t)L * hd;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= per_head * H) return;
+  const int h = (int)(i / per_head);
+  const int64_t j = i % per_head;
+  // K element (t, e)
+  {
+    const int t = (int)(j / hd), e = (int)(j % hd);
+    const T v = kown[i];
+    if (W > 0) ringK[((int64_t)h * W + (ptr + t) % W) * hd + e] = v;
+    if (sinkK && t < Se) sinkK[((int64_t)h * S8 + sink_off + t) * hd + e] = v;
+  }
+  // V^T element (e, t)
+  {
+    const int e = (int)(j / L), t = (int)(j % L);
+    const T v = vtown[i];
+    if (W > 0) ringVT[((int64_t)h * hd + e) * W + (ptr + t) % W] = v;
+    if (sinkVT && t < Se) sinkVT[((int64_t)h * hd + e) * S8 + sink_off + t] = v;
+  }
+}
+
+hipError_t kv_append(hipStream_t s, bool bf, const void* kown, const void* vtown, void* ringK, void* ringVT, int H,
+                     int hd, int L, int W, int ptr, void* sinkK, void* sinkVT, int S8, int sink_off, int Se) {
+  const int64_t n = (int64_t)H * L * hd;
+  if (bf)
+    kv_append_kernel<bf16><<<grid1(n, 256), 256, 0, s>>>((const bf16*)kown, (const bf16*)vtown, (bf16*)ringK,
+                                                         (bf16*)ringVT, H, hd, L, W, ptr, (bf16*)sinkK,
+                                                         (bf16*)sinkVT, S8, sink_off, Se);
+  else
+    kv_append_kernel<float><<<grid1(n, 256), 256, 0, s>>>((const float*)kown, (const float*)vtown, (float*)ringK,
+                                                          (float*)ringVT, H, hd, L, W, ptr, (float*)sinkK,
+                                                          (float*)sinkVT, S8, sink_off, Se);
+  return hipGetLastError();
+}
+
+// Sink refresh copy: entry flag[1] <- ring tokens (ptr_old + t) mod W, t < Se,
+// at every block, when flag[0] is set by sink_score.
+template <typename T>
+__global__ void sink_copy_kernel(const int* __restrict__ flag, const T* __restrict__ ringK,
+                                 const T* __restrict__ ringVT, T* __restrict__ sinkK, T* __restrict__ sinkVT, int nb,
+                                 int H, int hd, int W, int S8, int ptr_old, int Se) {
+  if (flag[0] == 0) return;
+  const int j = flag[1];
+  const int64_t per = (int64_t)Se * hd;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= per * H * nb) return;
+  const int64_t bh = i / per;          // block * H + head
+  const int64_t w = i % per;
+  {
+    const int t = (int)(w / hd), e = (int)(w % hd);
+    sinkK[(bh * S8 + j * Se + t) * hd + e] = ringK[(bh * W + (ptr_old + t) % W) * hd + e];
+  }
+  {
+    const int e = (int)(w / Se), t = (int)(w % Se);
+    sinkVT[(bh * hd + e) * S8 + j * Se + t] = ringVT[(bh * hd + e) * W + (ptr_old + t) % W];
+  }
+}
+
+hipError_t sink_copy(hipStream_t s, bool bf, const int* flag, const void* ringK, const void* ringVT, void* sinkK,
+                     void* sinkVT, int nb, int H, int hd, int W, int S8, int ptr_old, int Se) {
+  const int64_t n = (int64_t)nb * H * Se * hd;
+  if (n == 0) return hipSuccess;
+  if (bf)
+    sink_copy_kernel<bf16><<<grid1(n, 256), 256, 0, s>>>(flag, (const bf16*)ringK, (const bf16*)ringVT,
+                                                         (bf16*)sinkK, (bf16*)sinkVT, nb, H, hd, W, S8, ptr_old, Se);
+  else
+    sink_copy_kernel<float><<<grid1(n, 256), 256, 0, s>>>(flag, (const float*)ringK, (const float*)ringVT,
+                                                          (float*)sinkK, (float*)sinkVT, nb, H, hd, W, S8, ptr_old,
+                                                          Se);
+  return hipGetLastError();
+}
+
+__global__ void fill_zero_kernel(uint32_t* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+hipError_t fill_zero(hipStream_t s, void* p, size_t bytes) {
+  const int64_t n = (int64_t)(bytes / 4);
+  if (n == 0) return hipSuccess;
+  fill_zero_kernel<<<grid1(n, 256), 256, 0, s>>>((uint32_t*)p, n);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Stochastic Similarity Filter sums (StreamDiffusion paper notes, section 3):
+// exact int64 dot products of integer frames, one workgroup, fixed order.
+SD_DEV long long ssf_code(int kind, const void* p, int64_t i) {
+  if (kind == 0) return (long long)((const uint8_t*)p)[i];
+  const double v = rint((double)((const float*)p)[i] * 4096.0);
+  const double c = v < -1048576.0 ? -1048576.0 : (v > 1048576.0 ? 1048576.0 : v);
+  return (long long)c;
+}
+
+__global__ __launch_bounds__(1024) void ssf_sums_kernel(int kind, const void* __restrict__ a,
+                                                        const void* __restrict__ b, int64_t n,
+                                                        long long* __restrict__ out) {
+  __shared__ long long red[3][16];
+  long long d = 0, n1 = 0, n2 = 0;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+    const long long x = ssf_code(kind, a, i), y = ssf_code(kind, b, i);
+    d += x * y;
+    n1 += x * x;
+    n2 += y * y;
+  }
+  d = wave_sum_i64(d);
+  n1 = wave_sum_i64(n1);
+  n2 = wave_sum_i64(n2);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red[0][w] = d;
+    red[1][w] = n1;
+    red[2][w] = n2;
+  }
+  __syncthreads();
+  if (threadIdx.x < 3) {
+    long long t = 0;
+    for (int k = 0; k < (int)(blockDim.x >> 6); ++k) t += red[threadIdx.x][k];
+    out[threadIdx.x] = t;
+  }
+}
+
+hipError_t ssf_sums(hipStream_t s, int kind, const void* a, const void* b, int64_t n, long long* out3) {
+  ssf_sums_kernel<<<1, 1024, 0, s>>>(kind, a, b, n, out3);
+  return hipGetLastError();
+}
+
+// Motion (StreamDiffusionV2 summary, motion-aware noise scheduler): exact
+// sum of squared differences of consecutive 2^-12-quantised latent frames.
+__global__ __launch_bounds__(1024) void motion_sums_kernel(const float* __restrict__ cur,
+                                                           const float* __restrict__ prev_last, int64_t n,
+                                                           long long* __restrict__ out) {
+  __shared__ long long red[16];
+  const int t = blockIdx.x;
+  const float* a = (t == 0) ? prev_last : cur + (int64_t)(t - 1) * n;
+  const float* b = cur + (int64_t)t * n;
+  long long acc = 0;
+  if (a) {
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+      const long long x = ssf_code(1, a, i), y = ssf_code(1, b, i);
+      acc += (y - x) * (y - x);
+    }
+  }
+  acc = wave_sum_i64(acc);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    long long s = 0;
+    for (int k = 0; k < (int)(blockDim.x >> 6); ++k) s += red[k];
+    out[t] = s;
+  }
+}
+
+hipError_t motion_sums(hipStream_t s, const float* cur, const float* prev_last, int T, int64_t n, long long* out) {
+  motion_sums_kernel<<<T, 1024, 0, s>>>(cur, prev_last, n, out);
+  return hipGetLastError();
+}
+
+// Adaptive sink refresh (StreamDiffusionV2 summary): chunk embedding h = token
+// mean of the last block's output; cosine against each sink embedding; the
+// least similar entry is refreshed when its cosine is below tau.
+#define SINK_PARTS 64
+__global__ __launch_bounds__(256) void sink_partial_kernel(const float* __restrict__ x, float* __restrict__ part,
+                                                           int L, int d) {
+  const int g = blockIdx.y;
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= d) return;
+  const int per = (L + SINK_PARTS - 1) / SINK_PARTS;
+  const int t0 = g * per, t1 = min(L, t0 + per);
+  float s = 0.f;
+  for (int t = t0; t < t1; ++t) s += x[(int64_t)t * d + c];
+  part[(int64_t)g * d + c] = s;
+}
+
+__global__ __launch_bounds__(1024) void sink_decide_kernel(const float* __restrict__ part, int L, int d,
+                                                           float* __restrict__ emb, int M, int capture_entry,
+                                                           float tau, int* __restrict__ flag,
+                                                           float* __restrict__ sim_out) {
+  extern __shared__ float h[];
+  __shared__ double red[3][16];
+  __shared__ double sims[SD_MAX_SINK];
+  for (int c = threadIdx.x; c < d; c += blockDim.x) {
+    float s = 0.f;
+    for (int g = 0; g < SINK_PARTS; ++g) s += part[(int64_t)g * d + c];
+    h[c] = s / (float)L;
+  }
+  __syncthreads();
+  if (capture_entry >= 0) {
+    for (int c = threadIdx.x; c < d; c += blockDim.x) emb[(int64_t)capture_entry * d + c] = h[c];
+    if (threadIdx.x == 0) {
+      flag[0] = 0;
+      flag[1] = capture_entry;
+      flag[2] = 0;
+      sim_out[0] = 1.0f;
+    }
+    return;
+  }
+  for (int j = 0; j < M; ++j) {
+    double dot = 0, hh = 0, ee = 0;
+    for (int c = threadIdx.x; c < d; c += blockDim.x) {
+      const double a = h[c], b = emb[(int64_t)j * d + c];
+      dot += a * b;
+      hh += a * a;
+      ee += b * b;
+    }
+    dot = wave_sum_d(dot);
+    hh = wave_sum_d(hh);
+    ee = wave_sum_d(ee);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+      red[0][w] = dot;
+      red[1][w] = hh;
+      red[2][w] = ee;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      double D = 0, A = 0, B = 0;
+      for (int k = 0; k < (int)(blockDim.x >> 6); ++k) {
+        D += red[0][k];
+        A += red[1][k];
+        B += red[2][k];
+      }
+      sims[j] = (A == 0.0 || B == 0.0) ? 0.0 : D / (sqrt(A) * sqrt(B));
+    }
+    __syncthreads();
+  }
+  __shared__ int jstar;
+  if (threadIdx.x == 0) {
+    int js = 0;
+    for (int j = 1; j < M; ++j)
+      if (sims[j] < sims[js]) js = j;
+    jstar = js;
+    const int refresh = sims[js] < (double)tau ? 1 : 0;
+    flag[0] = refresh;
+    flag[1] = js;
+    flag[2] = 1;
+    sim_out[0] = (float)sims[js];
+  }
+  __syncthreads();
+  if (sims[jstar] < (double)tau)
+    for (int c = threadIdx.x; c < d; c += blockDim.x) emb[(int64_t)jstar * d + c] = h[c];
+}
+
+hipError_t sink_score(hipStream_t s, const float* x, float* partial, int L, int d, float* emb, int M,
+                      int capture_entry, float tau, int* flag, float* sim) {
+  dim3 g1((d + 255) / 256, SINK_PARTS);
+  sink_partial_kernel<<<g1, 256, 0, s>>>(x, partial, L, d);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  sink_decide_kernel<<<1, 1024, d * sizeof(float), s>>>(partial, L, d, emb, M, capture_entry, tau, flag, sim);
+  return hipGetLastError();
+}
+
+}  // namespace sdk

@@ -1,0 +1,76 @@
+// Launchers of the gfx950 kernels.  Every launcher enqueues on the given
+// stream and returns the launch status; shapes are checked by the caller.
+#pragma once
+#include "common.h"
+
+namespace sdk {
+
+// ---------------------------------------------------------------- elementwise
+// xs = a*x0 + b*noise; x0s = x0 (when x0s != nullptr).
+hipError_t entry_noise(hipStream_t s, const float* x0, const float* noise, float* xs, float* x0s, int64_t n,
+                       float a, float b);
+// R-CFG, x0 prediction and re-noise for every denoise row of rt.
+hipError_t rcfg_update(hipStream_t s, const RowTable& rt, float* store_x, float* store_x0s, const float* eps,
+                       float* out, int64_t lat, float gamma, float delta, int neg_row);
+// Gather patches of each row's latent into [R*L][p*p*C] (element type by bf).
+hipError_t patchify(hipStream_t s, bool bf, const RowTable& rt, const float* store_x, void* out, int64_t lat,
+                    int T, int C, int Hl, int Wl, int p);
+// LayerNorm (no affine, population variance) then optional modulation
+// x*(1+scale)+shift with scale/shift = mod[r][off] + blk[off]; output element type by bf.
+hipError_t ln_mod(hipStream_t s, bool bf, const float* x, void* out, int M, int d, int L, const float* mod,
+                  const void* blk, int shift_off, int scale_off, int six_d, float eps);
+// Sinusoidal timestep embedding per row: [cos(tau w_j), sin(tau w_j)], fp64 math.
+hipError_t temb_embed(hipStream_t s, const RowTable& rt, float* out, int d_freq);
+// y[r][n] = act(sum_k x[r][k] W[n][k] + b[n]); act 0 = none, 1 = SiLU.
+hipError_t gemv(hipStream_t s, bool bf, const float* x, const void* W, const void* b, float* y, int R, int N, int K,
+                int act);
+// Append the exiting row's own K / V^T to the ring; optionally capture its
+// first Se tokens as sink entry (sink_off .. sink_off+Se).
+hipError_t kv_append(hipStream_t s, bool bf, const void* kown, const void* vtown, void* ringK, void* ringVT, int H,
+                     int hd, int L, int W, int ptr, void* sinkK, void* sinkVT, int S8, int sink_off, int Se);
+// Predicated sink refresh copy over all blocks (flag[0] != 0 -> entry flag[1]).
+hipError_t sink_copy(hipStream_t s, bool bf, const int* flag, const void* ringK, const void* ringVT, void* sinkK,
+                     void* sinkVT, int nb, int H, int hd, int W, int S8, int ptr_old, int Se);
+hipError_t fill_zero(hipStream_t s, void* p, size_t bytes);
+
+// ---------------------------------------------------------------- reductions
+// Exact int64 (sum a*b, sum a*a, sum b*b); kind 0 = uint8, 1 = fp32 latents
+// quantised to rint(x * 2^12) clamped to +-2^20.
+hipError_t ssf_sums(hipStream_t s, int kind, const void* a, const void* b, int64_t n, long long* out3);
+// Exact int64 sum of squared differences of quantised frames for each of the
+// T frame pairs (prev_last, cur[0]), (cur[0], cur[1]), ...; pair 0 skipped
+// (written 0) when prev_last is null.
+hipError_t motion_sums(hipStream_t s, const float* cur, const float* prev_last, int T, int64_t n, long long* out);
+// Chunk embedding (token mean of x [L][d]) and cosine decision against the
+// sink embeddings.  capture_entry >= 0 stores h as that entry instead.
+hipError_t sink_score(hipStream_t s, const float* x, float* partial, int L, int d, float* emb, int M,
+                      int capture_entry, float tau, int* flag, float* sim);
+
+// ---------------------------------------------------------------- GEMM
+// C = A[M][K] * W[N][K]^T with epilogue E; element type by bf (bf16 on MFMA,
+// fp32 on the vector ALUs).
+hipError_t gemm(hipStream_t s, bool bf, const void* A, const void* W, int M, int N, int K, const Epi& E);
+
+// ---------------------------------------------------------------- attention
+struct KvSeg {
+  const void* k;          // K   [.][cap][hd]  (head stride k_hs, row stride k_rs)
+  const void* vt;         // V^T [.][hd][cap]  (head stride vt_hs, row stride vt_rs)
+  long long k_hs, vt_hs, k_rs, vt_rs;
+  int cap;                // token capacity (V^T row pitch, ring modulus)
+  int start;              // position of the first valid token
+  int count;              // valid tokens
+  int wrap;               // positions are taken modulo cap
+};
+struct AttnArgs {
+  const void* q;          // q(r,h,t) = q + r*q_rs + h*q_hs + t*hd
+  long long q_rs, q_hs;
+  void* o;                // token-major [R*L][d]
+  int R, H, L, hd, d;
+  int r0;                 // first row of this launch (rows r0 .. r0+R-1)
+  int nseg;
+  KvSeg seg[3];
+  float scale;            // 1/sqrt(hd)
+};
+hipError_t attention(hipStream_t s, bool bf, const AttnArgs& a);
+
+}  // namespace sdk

@@ -1,0 +1,681 @@
+// sd_stream_* : the Stream Batch runtime.  Holds the integer state machine
+// (frame store, slots, KV ring pointer and valid count, sink entries, RoPE
+// counter, SSF and motion state) and enqueues the kernels of one step.
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <deque>
+#include <string>
+#include <vector>
+
+#include "host_state.h"
+#include "kernels.h"
+
+using sdk::AttnArgs;
+using sdk::KvSeg;
+
+namespace {
+
+constexpr int kPendingMax = 4;
+
+struct FrameRec {
+  bool used = false;
+  int64_t fid = -1;
+  int32_t taus[SD_MAX_SLOTS] = {};
+  int32_t t0 = 0;
+};
+
+}  // namespace
+
+struct sd_stream {
+  sd_stream_config cfg;
+  sd_weights w;
+  hipStream_t st = nullptr;
+  std::string err;
+  bool bf = false;
+  size_t es = 4;  // element size of weights / activations
+  // dims
+  int L = 0, d = 0, H = 0, hd = 0, F = 0, nb = 0, P = 0, Tn = 0, Hp = 0, Wp = 0;
+  int64_t lat = 0, frame_elems = 0;
+  int S = 0, S8 = 0, Se = 0, Ment = 0, Wt = 0, ctx8 = 0, Rmax = 0, n = 0, NF = 0;
+  int dt = 0, dh = 0, dw = 0, rope_pos = 0;
+  std::vector<double> a, b;
+  // device regions
+  float *fx = nullptr, *fx0s = nullptr;
+  void* ssf_ref = nullptr;
+  long long* sums = nullptr;      // [0..2] ssf, [4..4+T) motion
+  float* mprev = nullptr;
+  float *emb = nullptr, *h1 = nullptr, *sc = nullptr, *mod = nullptr, *fmod = nullptr;
+  float* resid = nullptr;
+  void *xm = nullptr, *q = nullptr, *kown = nullptr, *vtown = nullptr, *ao = nullptr, *hid = nullptr;
+  float* eps = nullptr;
+  void *ringK = nullptr, *ringVT = nullptr, *sinkK = nullptr, *sinkVT = nullptr;
+  void *ctxK = nullptr, *ctxVT = nullptr;
+  float *sink_emb = nullptr, *sink_part = nullptr, *sink_sim = nullptr;
+  int* sink_flag = nullptr;
+  float2 *rope_t = nullptr, *rope_h = nullptr, *rope_w = nullptr;
+  size_t ws_used = 0;
+  // host state
+  std::vector<FrameRec> frames;
+  std::deque<int> pending;
+  int slots[SD_MAX_SLOTS];
+  sd::Controls ctl;
+  int64_t n_pushed = 0, n_steps = 0;
+  int kv_ptr = 0, kv_valid = 0, sink_count = 0;
+  bool ctx_set = false;
+  bool has_ref_frame = false;
+};
+
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Carver {
+  char* base;
+  size_t off = 0;
+  template <typename T>
+  T* take(size_t bytes) {
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += align256(bytes);
+    return p;
+  }
+};
+
+void dims(sd_stream* s) {
+  const sd_stream_config& c = s->cfg;
+  s->bf = c.dtype == SD_DTYPE_BF16;
+  s->es = s->bf ? 2 : 4;
+  s->L = (int)sd::tokens_per_chunk(c);
+  s->d = c.d_model;
+  s->H = c.n_heads;
+  s->hd = c.d_model / c.n_heads;
+  s->F = c.d_ffn;
+  s->nb = c.n_blocks;
+  s->P = c.patch * c.patch * c.latent_c;
+  s->Tn = c.latent_t;
+  s->Hp = c.latent_h / c.patch;
+  s->Wp = c.latent_w / c.patch;
+  s->lat = sd::latent_elems(c);
+  s->frame_elems = (int64_t)c.latent_c * c.latent_h * c.latent_w;
+  s->S = c.sink_tokens;
+  s->S8 = (c.sink_tokens + 7) & ~7;
+  s->Ment = c.sink_tokens > 0 ? c.sink_entries : 0;
+  s->Se = c.sink_tokens > 0 ? c.sink_tokens / c.sink_entries : 0;
+  s->Wt = c.window_tokens;
+  s->ctx8 = (c.ctx_len + 7) & ~7;
+  s->Rmax = sd::rows_max(c);
+  s->n = c.n_slots;
+  s->NF = c.n_slots + kPendingMax + 1;
+  s->dh = 2 * (s->hd / 6);
+  s->dw = s->dh;
+  s->dt = s->hd - 2 * s->dh;
+  s->rope_pos = std::max(c.rope_reset, s->Tn - 1) + 1;
+}
+
+// Lay out (or, with base == nullptr, measure) the workspace.
+size_t carve(sd_stream* s, char* base) {
+  const sd_stream_config& c = s->cfg;
+  Carver cv{base};
+  const size_t es = s->es;
+  const int64_t M = (int64_t)s->Rmax * s->L;
+  const int nctx = c.cfg_type == SD_CFG_ONETIME ? 2 : 1;
+  s->fx = cv.take<float>((size_t)s->NF * s->lat * 4);
+  s->fx0s = cv.take<float>((size_t)s->NF * s->lat * 4);
+  if (c.ssf_on) {
+    const size_t rb = c.ssf_kind == SD_SSF_U8 ? (size_t)c.ssf_h * c.ssf_w * c.ssf_c : (size_t)s->lat * 4;
+    s->ssf_ref = cv.take<void>(rb);
+  }
+  s->sums = cv.take<long long>(sizeof(long long) * (4 + s->Tn));
+  if (c.motion_on) s->mprev = cv.take<float>((size_t)s->frame_elems * 4);
+  s->emb = cv.take<float>((size_t)s->Rmax * c.d_freq * 4);
+  s->h1 = cv.take<float>((size_t)s->Rmax * s->d * 4);
+  s->sc = cv.take<float>((size_t)s->Rmax * s->d * 4);
+  s->mod = cv.take<float>((size_t)s->Rmax * 6 * s->d * 4);
+  s->fmod = cv.take<float>((size_t)s->Rmax * 2 * s->d * 4);
+  s->resid = cv.take<float>((size_t)M * s->d * 4);
+  s->xm = cv.take<void>((size_t)M * std::max(s->d, s->P) * es);
+  s->q = cv.take<void>((size_t)M * s->d * es);
+  s->kown = cv.take<void>((size_t)M * s->d * es);
+  s->vtown = cv.take<void>((size_t)M * s->d * es);
+  s->ao = cv.take<void>((size_t)M * s->d * es);
+  s->hid = cv.take<void>((size_t)M * s->F * es);
+  s->eps = cv.take<float>((size_t)s->Rmax * s->lat * 4);
+  s->ringK = cv.take<void>((size_t)s->nb * s->H * s->Wt * s->hd * es);
+  s->ringVT = cv.take<void>((size_t)s->nb * s->H * s->Wt * s->hd * es);
+  s->sinkK = cv.take<void>((size_t)s->nb * s->H * s->S8 * s->hd * es);
+  s->sinkVT = cv.take<void>((size_t)s->nb * s->H * s->S8 * s->hd * es);
+  if (c.ctx_len > 0) {
+    s->ctxK = cv.take<void>((size_t)s->nb * nctx * s->H * s->ctx8 * s->hd * es);
+    s->ctxVT = cv.take<void>((size_t)s->nb * nctx * s->H * s->ctx8 * s->hd * es);
+  }
+  s->sink_emb = cv.take<float>((size_t)std::max(1, s->Ment) * s->d * 4);
+  s->sink_part = cv.take<float>((size_t)64 * s->d * 4);
+  s->sink_flag = cv.take<int>(16);
+  s->sink_sim = cv.take<float>(16);
+  s->rope_t = cv.take<float2>((size_t)s->rope_pos * std::max(1, s->dt / 2) * sizeof(float2));
+  s->rope_h = cv.take<float2>((size_t)s->Hp * std::max(1, s->dh / 2) * sizeof(float2));
+  s->rope_w = cv.take<float2>((size_t)s->Wp * std::max(1, s->dw / 2) * sizeof(float2));
+  return cv.off;
+}
+
+sd_status set_err(sd_stream* s, sd_status code, const std::string& msg) {
+  if (s) s->err = msg;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                              \
+  do {                                                                             \
+    hipError_t _e = (expr);                                                        \
+    if (_e != hipSuccess)                                                          \
+      return set_err(s, SD_ERR_HIP, std::string(#expr) + ": " + hipGetErrorString(_e)); \
+  } while (0)
+
+const char* P(const void* base, int64_t elem_off, size_t es) { return (const char*)base + elem_off * (int64_t)es; }
+char* Pm(void* base, int64_t elem_off, size_t es) { return (char*)base + elem_off * (int64_t)es; }
+
+void rope_tables(const sd_stream* s, std::vector<float2>& t, std::vector<float2>& h, std::vector<float2>& w) {
+  const double base = s->cfg.rope_base;
+  auto fill = [&](std::vector<float2>& out, int npos, int width) {
+    const int np = width / 2;
+    out.assign((size_t)npos * std::max(1, np), float2{1.f, 0.f});
+    for (int p = 0; p < npos; ++p)
+      for (int j = 0; j < np; ++j) {
+        const double th = (double)p * std::pow(base, -2.0 * j / (double)width);
+        out[(size_t)p * np + j] = float2{(float)std::cos(th), (float)std::sin(th)};
+      }
+  };
+  fill(t, s->rope_pos, s->dt);
+  fill(h, s->Hp, s->dh);
+  fill(w, s->Wp, s->dw);
+}
+
+Epi epi_base(const sd_stream* s, int mode) {
+  Epi E;
+  std::memset(&E, 0, sizeof(E));
+  E.mode = mode;
+  E.L = s->L;
+  E.six_d = 6 * s->d;
+  E.H = s->H;
+  E.hd = s->hd;
+  E.d = s->d;
+  E.Hp = s->Hp;
+  E.Wp = s->Wp;
+  E.dt = s->dt;
+  E.dh = s->dh;
+  E.rope_t = s->rope_t;
+  E.rope_h = s->rope_h;
+  E.rope_w = s->rope_w;
+  E.C = s->cfg.latent_c;
+  E.Hl = s->cfg.latent_h;
+  E.Wl = s->cfg.latent_w;
+  E.p = s->cfg.patch;
+  E.T = s->Tn;
+  return E;
+}
+
+int free_frame(sd_stream* s) {
+  for (int i = 0; i < s->NF; ++i)
+    if (!s->frames[i].used) return i;
+  return -1;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sd_stream_workspace_bytes(const sd_stream_config* cfg) {
+  if (!cfg) return 0;
+  if (sd::validate_config(*cfg, nullptr) != SD_OK) return 0;
+  sd_stream tmp;
+  tmp.cfg = *cfg;
+  dims(&tmp);
+  return carve(&tmp, nullptr);
+}
+
+sd_status sd_stream_create(const sd_stream_config* cfg, const sd_weights* w, void* workspace, size_t ws_bytes,
+                           void* hip_stream, sd_stream** out) {
+  if (!cfg || !w || !out) return SD_ERR_ARG;
+  *out = nullptr;
+  std::string err;
+  const int rc = sd::validate_config(*cfg, &err);
+  if (rc != SD_OK) return (sd_status)rc;
+  const void* need[] = {w->t_w1, w->t_b1, w->t_w2, w->t_b2, w->mod_w, w->mod_b, w->blk_mod, w->pe_w,
+                        w->pe_b, w->qkv_w, w->qkv_b, w->o_w, w->o_b, w->f1_w, w->f1_b, w->f2_w,
+                        w->f2_b, w->fin_w, w->fin_b, w->head_w, w->head_b};
+  for (const void* p : need)
+    if (!p) return SD_ERR_ARG;
+  if (cfg->ctx_len > 0 && (!w->cq_w || !w->cq_b || !w->ckv_w || !w->ckv_b || !w->co_w || !w->co_b))
+    return SD_ERR_ARG;
+  if (!workspace || ((uintptr_t)workspace & 255)) return SD_ERR_WORKSPACE;
+  sd_stream* s = new sd_stream();
+  s->cfg = *cfg;
+  s->w = *w;
+  s->st = (hipStream_t)hip_stream;
+  dims(s);
+  const size_t need_ws = carve(s, nullptr);
+  if (ws_bytes < need_ws) {
+    delete s;
+    return SD_ERR_WORKSPACE;
+  }
+  s->ws_used = carve(s, (char*)workspace);
+  sd::make_schedule(s->cfg, s->a, s->b);
+  s->frames.assign(s->NF, FrameRec());
+  for (int i = 0; i < SD_MAX_SLOTS; ++i) s->slots[i] = -1;
+  s->ctl.s = s->cfg.s_max;
+  // zero the caches (padding keys must stay finite) and upload RoPE tables
+  std::vector<float2> rt, rh, rw;
+  rope_tables(s, rt, rh, rw);
+  hipError_t e = hipSuccess;
+  const size_t cache_bytes[] = {(size_t)s->nb * s->H * s->Wt * s->hd * s->es,
+                                (size_t)s->nb * s->H * s->S8 * s->hd * s->es};
+  if (e == hipSuccess) e = sdk::fill_zero(s->st, s->ringK, cache_bytes[0]);
+  if (e == hipSuccess) e = sdk::fill_zero(s->st, s->ringVT, cache_bytes[0]);
+  if (e == hipSuccess) e = sdk::fill_zero(s->st, s->sinkK, cache_bytes[1]);
+  if (e == hipSuccess) e = sdk::fill_zero(s->st, s->sinkVT, cache_bytes[1]);
+  if (e == hipSuccess) e = sdk::fill_zero(s->st, s->sink_emb, (size_t)std::max(1, s->Ment) * s->d * 4);
+  if (e == hipSuccess) e = sdk::fill_zero(s->st, s->sink_flag, 16);
+  if (e == hipSuccess) e = hipMemcpyAsync(s->rope_t, rt.data(), rt.size() * sizeof(float2), hipMemcpyHostToDevice, s->st);
+  if (e == hipSuccess) e = hipMemcpyAsync(s->rope_h, rh.data(), rh.size() * sizeof(float2), hipMemcpyHostToDevice, s->st);
+  if (e == hipSuccess) e = hipMemcpyAsync(s->rope_w, rw.data(), rw.size() * sizeof(float2), hipMemcpyHostToDevice, s->st);
+  if (e == hipSuccess) e = hipStreamSynchronize(s->st);
+  if (e != hipSuccess) {
+    delete s;
+    return SD_ERR_HIP;
+  }
+  s->ctx_set = (cfg->ctx_len == 0);
+  *out = s;
+  return SD_OK;
+}
+
+sd_status sd_stream_set_context(sd_stream* s, const void* ctx_pos, const void* ctx_neg) {
+  if (!s) return SD_ERR_ARG;
+  const sd_stream_config& c = s->cfg;
+  if (c.ctx_len == 0) return set_err(s, SD_ERR_STATE, "no cross-attention configured (ctx_len == 0)");
+  if (!ctx_pos) return set_err(s, SD_ERR_ARG, "ctx_pos is null");
+  if (c.cfg_type == SD_CFG_ONETIME && !ctx_neg)
+    return set_err(s, SD_ERR_ARG, "onetime-negative R-CFG needs ctx_neg");
+  const int nctx = c.cfg_type == SD_CFG_ONETIME ? 2 : 1;
+  const size_t per = (size_t)s->H * s->ctx8 * s->hd;   // elements per (block, context)
+  HIP_TRY(sdk::fill_zero(s->st, s->ctxK, (size_t)s->nb * nctx * per * s->es));
+  HIP_TRY(sdk::fill_zero(s->st, s->ctxVT, (size_t)s->nb * nctx * per * s->es));
+  for (int b = 0; b < s->nb; ++b)
+    for (int ci = 0; ci < nctx; ++ci) {
+      Epi E = epi_base(s, EPI_CTXKV);
+      E.bias = P(s->w.ckv_b, (int64_t)b * 2 * s->d, s->es);
+      E.L = c.ctx_len;
+      E.k = Pm(s->ctxK, ((int64_t)b * nctx + ci) * per, s->es);
+      E.vt = Pm(s->ctxVT, ((int64_t)b * nctx + ci) * per, s->es);
+      E.kstride = s->ctx8;
+      E.rope = 0;
+      HIP_TRY(sdk::gemm(s->st, s->bf, ci == 0 ? ctx_pos : ctx_neg, P(s->w.ckv_w, (int64_t)b * 2 * s->d * s->d, s->es),
+                        c.ctx_len, 2 * s->d, s->d, E));
+    }
+  s->ctx_set = true;
+  return SD_OK;
+}
+
+sd_status sd_stream_push_frame(sd_stream* s, const float* x0, const float* noise, const void* ssf_frame, double u,
+                               sd_push_info* info) {
+  if (!s) return SD_ERR_ARG;
+  const sd_stream_config& c = s->cfg;
+  if (!x0 || !noise || !info) return set_err(s, SD_ERR_ARG, "null x0, noise or info");
+  if (c.ssf_on && c.ssf_kind == SD_SSF_U8 && !ssf_frame) return set_err(s, SD_ERR_ARG, "ssf_frame is null");
+  if (!(u >= 0.0 && u <= 1.0)) return set_err(s, SD_ERR_ARG, "u must be in [0, 1]");
+  if ((int)s->pending.size() >= kPendingMax) return set_err(s, SD_ERR_STATE, "pending queue full; call step()");
+  std::memset(info, 0, sizeof(*info));
+  info->t0 = -1;
+  info->frame_id = -1;
+  info->sim = 1.0;
+  info->s = s->ctl.s;
+  // device reductions for the SSF and motion decisions, one read-back
+  const void* ssf_cur = c.ssf_kind == SD_SSF_U8 ? ssf_frame : (const void*)x0;
+  const int64_t ssf_n = c.ssf_kind == SD_SSF_U8 ? (int64_t)c.ssf_h * c.ssf_w * c.ssf_c : s->lat;
+  const bool do_ssf = c.ssf_on && s->ctl.has_ref;
+  long long hs[4 + 64] = {};
+  if (do_ssf) HIP_TRY(sdk::ssf_sums(s->st, c.ssf_kind, ssf_cur, s->ssf_ref, ssf_n, s->sums));
+  if (c.motion_on)
+    HIP_TRY(sdk::motion_sums(s->st, x0, s->ctl.has_prev ? s->mprev : nullptr, s->Tn, s->frame_elems, s->sums + 4));
+  if (do_ssf || c.motion_on) {
+    HIP_TRY(hipMemcpyAsync(hs, s->sums, sizeof(long long) * (4 + s->Tn), hipMemcpyDeviceToHost, s->st));
+    HIP_TRY(hipStreamSynchronize(s->st));
+  }
+  if (c.ssf_on) {
+    double sim = 1.0, p = 0.0;
+    const bool skip = sd::ssf_decide(s->ctl, c, hs[0], hs[1], hs[2], u, &sim, &p);
+    info->sim = sim;
+    info->p = p;
+    if (skip) {
+      info->skipped = 1;
+      return SD_OK;
+    }
+    const size_t rb = c.ssf_kind == SD_SSF_U8 ? (size_t)ssf_n : (size_t)ssf_n * 4;
+    HIP_TRY(hipMemcpyAsync(s->ssf_ref, ssf_cur, rb, hipMemcpyDeviceToDevice, s->st));
+  }
+  const int f = free_frame(s);
+  if (f < 0) return set_err(s, SD_ERR_STATE, "frame store full");
+  FrameRec& fr = s->frames[f];
+  if (c.motion_on) {
+    double dist[64];
+    int nd = 0;
+    for (int t = (s->ctl.has_prev ? 0 : 1); t < s->Tn; ++t) dist[nd++] = sd::motion_distance(hs[4 + t], s->frame_elems);
+    sd::motion_push(s->ctl, c, dist, nd);
+    if (nd > 0) info->d = dist[nd - 1];
+    HIP_TRY(hipMemcpyAsync(s->mprev, x0 + (int64_t)(s->Tn - 1) * s->frame_elems, s->frame_elems * 4,
+                           hipMemcpyDeviceToDevice, s->st));
+    s->ctl.has_prev = true;
+    sd::taus_from_noise_rate(s->ctl.s, s->n, c.n_train_steps, fr.taus);
+  } else {
+    sd::taus_from_t_index(c, fr.taus);
+  }
+  info->s = s->ctl.s;
+  fr.t0 = sd::rope_assign(s->ctl, s->Tn, c.rope_reset);
+  fr.fid = s->n_pushed++;
+  fr.used = true;
+  const int tau0 = fr.taus[0];
+  HIP_TRY(sdk::entry_noise(s->st, x0, noise, s->fx + (int64_t)f * s->lat, s->fx0s + (int64_t)f * s->lat, s->lat,
+                           (float)s->a[tau0], (float)s->b[tau0]));
+  s->pending.push_back(f);
+  info->t0 = fr.t0;
+  info->frame_id = fr.fid;
+  for (int i = 0; i < s->n; ++i) info->taus[i] = fr.taus[i];
+  return SD_OK;
+}
+
+sd_status sd_stream_step(sd_stream* s, float* out_latent, sd_step_info* info) {
+  if (!s) return SD_ERR_ARG;
+  const sd_stream_config& c = s->cfg;
+  if (!info) return set_err(s, SD_ERR_ARG, "info is null");
+  if (s->pending.empty()) return set_err(s, SD_ERR_NOT_READY, "no pending frame");
+  if (!s->ctx_set) return set_err(s, SD_ERR_STATE, "set_context() must be called first");
+  const int n = s->n;
+  const bool will_exit = (n == 1) || (s->slots[n - 2] >= 0);
+  if (will_exit && !out_latent) return set_err(s, SD_ERR_ARG, "out_latent is null but a frame leaves this step");
+  std::memset(info, 0, sizeof(*info));
+
+  // ---- slot shift and row table
+  const int enter = s->pending.front();
+  s->pending.pop_front();
+  for (int i = n - 1; i >= 1; --i) s->slots[i] = s->slots[i - 1];
+  s->slots[0] = enter;
+  RowTable rt;
+  std::memset(&rt, 0, sizeof(rt));
+  int R = 0, r_exit = -1;
+  for (int i = 0; i < n; ++i) {
+    const int f = s->slots[i];
+    if (f < 0) continue;
+    const FrameRec& fr = s->frames[f];
+    RowInfo& ri = rt.r[R];
+    ri.frame = f;
+    ri.tau = fr.taus[i];
+    ri.t0 = fr.t0;
+    ri.kind = 0;
+    ri.last = (i == n - 1);
+    ri.ctx = 0;
+    ri.a = (float)s->a[ri.tau];
+    ri.b = (float)s->b[ri.tau];
+    if (i + 1 < n) {
+      ri.an = (float)s->a[fr.taus[i + 1]];
+      ri.bn = (float)s->b[fr.taus[i + 1]];
+    }
+    ri.a0 = (float)s->a[fr.taus[0]];
+    ri.b0 = (float)s->b[fr.taus[0]];
+    if (ri.last) r_exit = R;
+    ++R;
+  }
+  const int R_pos = R;
+  int neg_row = -1;
+  if (c.cfg_type == SD_CFG_ONETIME) {
+    rt.r[R] = rt.r[0];
+    rt.r[R].kind = 1;
+    rt.r[R].last = 0;
+    rt.r[R].ctx = 1;
+    neg_row = R;
+    ++R;
+  }
+  rt.R = R;
+  const int L = s->L, d = s->d, H = s->H, hd = s->hd, M = R * L;
+  const size_t es = s->es;
+  const bool bf = s->bf;
+  hipStream_t st = s->st;
+  const bool capture = r_exit >= 0 && s->S > 0 && s->sink_count < s->Ment;
+  const int ptr_old = s->kv_ptr;
+
+  // ---- conditioning: timestep embedding -> MLP -> SiLU(c) -> adaLN vectors
+  HIP_TRY(sdk::temb_embed(st, rt, s->emb, c.d_freq));
+  HIP_TRY(sdk::gemv(st, bf, s->emb, s->w.t_w1, s->w.t_b1, s->h1, R, d, c.d_freq, 1));
+  HIP_TRY(sdk::gemv(st, bf, s->h1, s->w.t_w2, s->w.t_b2, s->sc, R, d, d, 1));
+  HIP_TRY(sdk::gemv(st, bf, s->sc, s->w.mod_w, s->w.mod_b, s->mod, R, 6 * d, d, 0));
+  HIP_TRY(sdk::gemv(st, bf, s->sc, s->w.fin_w, s->w.fin_b, s->fmod, R, 2 * d, d, 0));
+
+  // ---- patch embedding into the fp32 residual stream
+  HIP_TRY(sdk::patchify(st, bf, rt, s->fx, s->xm, s->lat, s->Tn, c.latent_c, c.latent_h, c.latent_w, c.patch));
+  {
+    Epi E = epi_base(s, EPI_PATCH);
+    E.bias = s->w.pe_b;
+    E.resid = s->resid;
+    HIP_TRY(sdk::gemm(st, bf, s->xm, s->w.pe_w, M, d, s->P, E));
+  }
+
+  const int nctx = c.cfg_type == SD_CFG_ONETIME ? 2 : 1;
+  const int64_t own_stride = (int64_t)H * L * hd;
+  for (int b = 0; b < s->nb; ++b) {
+    const void* blk = P(s->w.blk_mod, (int64_t)b * 6 * d, es);
+    // self-attention
+    HIP_TRY(sdk::ln_mod(st, bf, s->resid, s->xm, M, d, L, s->mod, blk, 0, d, 6 * d, 1e-6f));
+    {
+      Epi E = epi_base(s, EPI_QKV);
+      E.bias = P(s->w.qkv_b, (int64_t)b * 3 * d, es);
+      E.q = s->q;
+      E.k = s->kown;
+      E.vt = s->vtown;
+      E.kstride = L;
+      E.rope = 1;
+      for (int r = 0; r < R; ++r) E.t0[r] = rt.r[r].t0;
+      HIP_TRY(sdk::gemm(st, bf, s->xm, P(s->w.qkv_w, (int64_t)b * 3 * d * d, es), M, 3 * d, d, E));
+    }
+    {
+      AttnArgs A;
+      std::memset(&A, 0, sizeof(A));
+      A.q = s->q;
+      A.q_rs = own_stride;
+      A.q_hs = (int64_t)L * hd;
+      A.o = s->ao;
+      A.R = R;
+      A.H = H;
+      A.L = L;
+      A.hd = hd;
+      A.d = d;
+      A.scale = 1.0f / std::sqrt((float)hd);
+      int ns = 0;
+      KvSeg& sk = A.seg[ns++];
+      sk.k = P(s->sinkK, (int64_t)b * H * s->S8 * hd, es);
+      sk.vt = P(s->sinkVT, (int64_t)b * H * s->S8 * hd, es);
+      sk.k_hs = sk.vt_hs = (int64_t)s->S8 * hd;
+      sk.cap = std::max(8, s->S8);
+      sk.start = 0;
+      sk.count = s->sink_count * s->Se;
+      KvSeg& sw = A.seg[ns++];
+      sw.k = P(s->ringK, (int64_t)b * H * s->Wt * hd, es);
+      sw.vt = P(s->ringVT, (int64_t)b * H * s->Wt * hd, es);
+      sw.k_hs = sw.vt_hs = (int64_t)s->Wt * hd;
+      sw.cap = std::max(8, s->Wt);
+      sw.count = s->kv_valid;
+      sw.start = s->Wt > 0 ? (s->kv_ptr - s->kv_valid + s->Wt) % s->Wt : 0;
+      sw.wrap = 1;
+      KvSeg& so = A.seg[ns++];
+      so.k = s->kown;
+      so.vt = s->vtown;
+      so.k_rs = so.vt_rs = own_stride;
+      so.k_hs = so.vt_hs = (int64_t)L * hd;
+      so.cap = L;
+      so.count = L;
+      A.nseg = ns;
+      HIP_TRY(sdk::attention(st, bf, A));
+    }
+    if (r_exit >= 0 && (s->Wt > 0 || capture)) {
+      const int64_t cb = (int64_t)b * H * s->S8 * hd;
+      HIP_TRY(sdk::kv_append(st, bf, P(s->kown, r_exit * own_stride, es), P(s->vtown, r_exit * own_stride, es),
+                             Pm(s->ringK, (int64_t)b * H * s->Wt * hd, es), Pm(s->ringVT, (int64_t)b * H * s->Wt * hd, es),
+                             H, hd, L, s->Wt, s->kv_ptr, capture ? Pm(s->sinkK, cb, es) : nullptr,
+                             capture ? Pm(s->sinkVT, cb, es) : nullptr, s->S8, s->sink_count * s->Se, s->Se));
+    }
+    {
+      Epi E = epi_base(s, EPI_GATE_RESID);
+      E.bias = P(s->w.o_b, (int64_t)b * d, es);
+      E.resid = s->resid;
+      E.mod = s->mod;
+      E.blk = blk;
+      E.gate_off = 2 * d;
+      HIP_TRY(sdk::gemm(st, bf, s->ao, P(s->w.o_w, (int64_t)b * d * d, es), M, d, d, E));
+    }
+    // cross-attention to the pre-computed prompt K/V
+    if (c.ctx_len > 0) {
+      HIP_TRY(sdk::ln_mod(st, bf, s->resid, s->xm, M, d, L, nullptr, nullptr, 0, 0, 6 * d, 1e-6f));
+      {
+        Epi E = epi_base(s, EPI_QKV);
+        E.bias = P(s->w.cq_b, (int64_t)b * d, es);
+        E.q = s->q;
+        E.rope = 0;
+        HIP_TRY(sdk::gemm(st, bf, s->xm, P(s->w.cq_w, (int64_t)b * d * d, es), M, d, d, E));
+      }
+      const size_t per = (size_t)H * s->ctx8 * hd;
+      for (int part = 0; part < (neg_row >= 0 ? 2 : 1); ++part) {
+        AttnArgs A;
+        std::memset(&A, 0, sizeof(A));
+        A.q = s->q;
+        A.q_rs = own_stride;
+        A.q_hs = (int64_t)L * hd;
+        A.o = s->ao;
+        A.r0 = part == 0 ? 0 : neg_row;
+        A.R = part == 0 ? R_pos : 1;
+        A.H = H;
+        A.L = L;
+        A.hd = hd;
+        A.d = d;
+        A.scale = 1.0f / std::sqrt((float)hd);
+        A.nseg = 1;
+        KvSeg& g = A.seg[0];
+        g.k = P(s->ctxK, ((int64_t)b * nctx + part) * per, es);
+        g.vt = P(s->ctxVT, ((int64_t)b * nctx + part) * per, es);
+        g.k_hs = g.vt_hs = (int64_t)s->ctx8 * hd;
+        g.cap = s->ctx8;
+        g.count = c.ctx_len;
+        HIP_TRY(sdk::attention(st, bf, A));
+      }
+      {
+        Epi E = epi_base(s, EPI_RESID);
+        E.bias = P(s->w.co_b, (int64_t)b * d, es);
+        E.resid = s->resid;
+        HIP_TRY(sdk::gemm(st, bf, s->ao, P(s->w.co_w, (int64_t)b * d * d, es), M, d, d, E));
+      }
+    }
+    // feed-forward
+    HIP_TRY(sdk::ln_mod(st, bf, s->resid, s->xm, M, d, L, s->mod, blk, 3 * d, 4 * d, 6 * d, 1e-6f));
+    {
+      Epi E = epi_base(s, EPI_GELU);
+      E.bias = P(s->w.f1_b, (int64_t)b * s->F, es);
+      E.out = s->hid;
+      E.ldo = s->F;
+      HIP_TRY(sdk::gemm(st, bf, s->xm, P(s->w.f1_w, (int64_t)b * s->F * d, es), M, s->F, d, E));
+    }
+    {
+      Epi E = epi_base(s, EPI_GATE_RESID);
+      E.bias = P(s->w.f2_b, (int64_t)b * d, es);
+      E.resid = s->resid;
+      E.mod = s->mod;
+      E.blk = blk;
+      E.gate_off = 5 * d;
+      HIP_TRY(sdk::gemm(st, bf, s->hid, P(s->w.f2_w, (int64_t)b * d * s->F, es), M, d, s->F, E));
+    }
+  }
+
+  // ---- adaptive sink: embedding of the exiting chunk, decision, predicated copy
+  if (r_exit >= 0 && s->S > 0) {
+    const int cap_entry = capture ? s->sink_count : -1;
+    HIP_TRY(sdk::sink_score(st, s->resid + (int64_t)r_exit * L * d, s->sink_part, L, d, s->sink_emb, s->Ment, cap_entry,
+                            (float)c.sink_tau, s->sink_flag, s->sink_sim));
+    if (!capture)
+      HIP_TRY(sdk::sink_copy(st, bf, s->sink_flag, s->ringK, s->ringVT, s->sinkK, s->sinkVT, s->nb, H, hd, s->Wt,
+                             s->S8, ptr_old, s->Se));
+  }
+
+  // ---- final layer and unpatchify -> eps_c
+  HIP_TRY(sdk::ln_mod(st, bf, s->resid, s->xm, M, d, L, s->fmod, nullptr, 0, d, 2 * d, 1e-6f));
+  {
+    Epi E = epi_base(s, EPI_HEAD);
+    E.bias = s->w.head_b;
+    E.eps = s->eps;
+    HIP_TRY(sdk::gemm(st, bf, s->xm, s->w.head_w, M, s->P, d, E));
+  }
+  // ---- R-CFG, x0 prediction, re-noise / emit
+  HIP_TRY(sdk::rcfg_update(st, rt, s->fx, s->fx0s, s->eps, out_latent, s->lat, (float)c.gamma, (float)c.delta,
+                           neg_row));
+
+  // ---- host bookkeeping
+  info->step = s->n_steps++;
+  info->rows = R;
+  info->frame_id = -1;
+  if (r_exit >= 0) {
+    const int f = s->slots[n - 1];
+    info->has_output = 1;
+    info->frame_id = s->frames[f].fid;
+    s->frames[f].used = false;
+    s->slots[n - 1] = -1;
+    if (s->Wt > 0) {
+      s->kv_ptr = (s->kv_ptr + L) % s->Wt;
+      s->kv_valid = std::min(s->Wt, s->kv_valid + L);
+    }
+    if (capture) s->sink_count += 1;
+  }
+  info->kv_ptr = s->kv_ptr;
+  info->kv_valid = s->kv_valid;
+  info->sink_count = s->sink_count;
+  info->rope_next = s->ctl.rope_p;
+  return SD_OK;
+}
+
+sd_status sd_stream_kv_reset(sd_stream* s) {
+  if (!s) return SD_ERR_ARG;
+  s->kv_ptr = 0;
+  s->kv_valid = 0;
+  s->sink_count = 0;
+  s->ctl.rope_p = 0;
+  return SD_OK;
+}
+
+sd_status sd_stream_sink_info(sd_stream* s, sd_sink_info* info) {
+  if (!s || !info) return SD_ERR_ARG;
+  int fl[4] = {};
+  float sim = 0.f;
+  HIP_TRY(hipMemcpyAsync(fl, s->sink_flag, sizeof(int) * 3, hipMemcpyDeviceToHost, s->st));
+  HIP_TRY(hipMemcpyAsync(&sim, s->sink_sim, sizeof(float), hipMemcpyDeviceToHost, s->st));
+  HIP_TRY(hipStreamSynchronize(s->st));
+  info->refreshed = fl[0];
+  info->entry = fl[1];
+  info->evaluated = fl[2];
+  info->sim = sim;
+  return SD_OK;
+}
+
+sd_status sd_stream_buffer(sd_stream* s, int32_t which, void** ptr, size_t* bytes) {
+  if (!s || !ptr || !bytes) return SD_ERR_ARG;
+  const size_t es = s->es;
+  switch (which) {
+    case SD_BUF_EPS: *ptr = s->eps; *bytes = (size_t)s->Rmax * s->lat * 4; break;
+    case SD_BUF_RING_K: *ptr = s->ringK; *bytes = (size_t)s->nb * s->H * s->Wt * s->hd * es; break;
+    case SD_BUF_RING_V: *ptr = s->ringVT; *bytes = (size_t)s->nb * s->H * s->Wt * s->hd * es; break;
+    case SD_BUF_SINK_K: *ptr = s->sinkK; *bytes = (size_t)s->nb * s->H * s->S8 * s->hd * es; break;
+    case SD_BUF_SINK_V: *ptr = s->sinkVT; *bytes = (size_t)s->nb * s->H * s->S8 * s->hd * es; break;
+    case SD_BUF_RESID: *ptr = s->resid; *bytes = (size_t)s->Rmax * s->L * s->d * 4; break;
+    case SD_BUF_MOD: *ptr = s->mod; *bytes = (size_t)s->Rmax * 6 * s->d * 4; break;
+    default: return set_err(s, SD_ERR_ARG, "unknown buffer");
+  }
+  return SD_OK;
+}
+
+void sd_stream_destroy(sd_stream* s) { delete s; }
+
+const char* sd_stream_last_error(const sd_stream* s) { return s ? s->err.c_str() : "null stream"; }
+
+}  // extern "C"

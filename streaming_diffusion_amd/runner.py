@@ -1,0 +1,156 @@
+"""Thin driver around the C ABI: turns a workload configuration into an
+sd_stream_config, places weights and workspace in device memory with torch,
+and forwards push/step calls.  All computation happens in libsdstream.
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+def make_config(cfg) -> L.sd_stream_config:
+    c = L.sd_stream_config()
+    c.abi_version = L.SD_ABI_VERSION
+    c.dtype = L.SD_DTYPE_BF16 if cfg.dtype == "bf16" else L.SD_DTYPE_F32
+    c.latent_t, c.latent_c, c.latent_h, c.latent_w = cfg.latent_t, cfg.latent_c, cfg.latent_h, cfg.latent_w
+    c.patch = cfg.patch
+    c.n_blocks, c.d_model, c.n_heads, c.d_ffn = cfg.n_blocks, cfg.d_model, cfg.n_heads, cfg.d_ffn
+    c.d_freq, c.ctx_len = cfg.d_freq, cfg.ctx_len
+    c.n_slots = cfg.n_slots
+    for i, k in enumerate(cfg.t_index):
+        c.t_index[i] = int(k)
+    c.chunks_per_step = cfg.chunks_per_step
+    c.cfg_type = L.SD_CFG_ONETIME if cfg.cfg_type == "onetime" else L.SD_CFG_SELF
+    c.gamma, c.delta = cfg.gamma, cfg.delta
+    c.sink_tokens = cfg.sink_tokens
+    c.sink_entries = getattr(cfg, "sink_entries", 1) if cfg.sink_tokens else 0
+    c.window_tokens = cfg.window_tokens
+    c.sink_tau = cfg.sink_tau
+    c.rope_reset, c.rope_base = cfg.rope_reset, cfg.rope_base
+    c.n_train_steps, c.beta_start, c.beta_end = cfg.n_train_steps, cfg.beta_start, cfg.beta_end
+    c.ssf_on = int(cfg.ssf_on)
+    c.ssf_kind = L.SD_SSF_U8 if cfg.ssf_kind == "u8" else L.SD_SSF_LATENT
+    if cfg.ssf_on and cfg.ssf_kind == "u8":
+        c.ssf_h, c.ssf_w, c.ssf_c = cfg.ssf_shape
+    c.ssf_eta, c.max_skip_frame = cfg.ssf_eta, cfg.max_skip_frame
+    c.motion_on, c.motion_k = int(cfg.motion_on), cfg.motion_k
+    c.motion_lambda, c.s_min, c.s_max, c.motion_sigma = cfg.motion_lambda, cfg.s_min, cfg.s_max, cfg.motion_sigma
+    return c
+
+
+def torch_dtype(cfg):
+    return torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+
+def upload_weights(cfg, weights: dict, device="cuda") -> dict:
+    """Host float32 arrays (already bf16-representable for bf16 configs) ->
+    contiguous device tensors of the config's element type."""
+    dt = torch_dtype(cfg)
+    return {k: torch.from_numpy(np.ascontiguousarray(v)).to(device=device).to(dt).contiguous()
+            for k, v in weights.items()}
+
+
+def random_device_weights(cfg, seed: int = 0, std: float = 0.02, device="cuda") -> dict:
+    """N(0, std) weights drawn on the device (for timing runs of large shapes)."""
+    from workloads.gen import param_specs
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    dt = torch_dtype(cfg)
+    out = {}
+    for name, shape in param_specs(cfg):
+        out[name] = (torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std).to(dt)
+    return out
+
+
+def ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+class StreamRunner:
+    """One sd_stream handle plus the device memory it needs."""
+
+    def __init__(self, cfg, dev_weights: dict, device="cuda", stream=None):
+        self.lib = L.load()
+        self.cfg = cfg
+        self.device = device
+        self.c = make_config(cfg)
+        ws = self.lib.sd_stream_workspace_bytes(C.byref(self.c))
+        if ws == 0:
+            raise L.SDError(L.SD_ERR_ARG, "invalid configuration")
+        self.ws_bytes = ws
+        self._ws = torch.empty(ws + 256, dtype=torch.uint8, device=device)
+        base = ptr(self._ws)
+        self.ws_ptr = (base + 255) & ~255
+        self.weights = dev_weights
+        self.w = L.sd_weights()
+        for name in L.WEIGHT_FIELDS:
+            t = dev_weights.get(name)
+            setattr(self.w, name, ptr(t) if t is not None else None)
+        self.stream = stream if stream is not None else torch.cuda.current_stream(device)
+        h = C.c_void_p()
+        L.check(self.lib.sd_stream_create(C.byref(self.c), C.byref(self.w), C.c_void_p(self.ws_ptr), ws,
+                                          C.c_void_p(self.stream.cuda_stream), C.byref(h)))
+        self.h = h
+        self.lat_shape = (cfg.latent_t, cfg.latent_c, cfg.latent_h, cfg.latent_w)
+        self.out = torch.empty(self.lat_shape, dtype=torch.float32, device=device)
+
+    def close(self):
+        if getattr(self, "h", None):
+            self.lib.sd_stream_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def set_context(self, ctx_pos, ctx_neg=None):
+        self._ctx = (ctx_pos, ctx_neg)
+        L.check(self.lib.sd_stream_set_context(self.h, C.c_void_p(ptr(ctx_pos)), C.c_void_p(ptr(ctx_neg))), self.h)
+
+    def push(self, x0, noise, ssf_frame=None, u: float = 0.0) -> L.sd_push_info:
+        info = L.sd_push_info()
+        L.check(self.lib.sd_stream_push_frame(self.h, C.c_void_p(ptr(x0)), C.c_void_p(ptr(noise)),
+                                              C.c_void_p(ptr(ssf_frame)), float(u), C.byref(info)), self.h)
+        return info
+
+    def step(self, out=None) -> L.sd_step_info:
+        info = L.sd_step_info()
+        o = self.out if out is None else out
+        L.check(self.lib.sd_stream_step(self.h, C.c_void_p(ptr(o)), C.byref(info)), self.h)
+        return info
+
+    def kv_reset(self):
+        L.check(self.lib.sd_stream_kv_reset(self.h), self.h)
+
+    def sink_info(self) -> L.sd_sink_info:
+        info = L.sd_sink_info()
+        L.check(self.lib.sd_stream_sink_info(self.h, C.byref(info)), self.h)
+        return info
+
+    def buffer(self, which: int, dtype, shape):
+        """A torch view of an internal device buffer (no copy)."""
+        p = C.c_void_p()
+        n = C.c_size_t()
+        L.check(self.lib.sd_stream_buffer(self.h, which, C.byref(p), C.byref(n)), self.h)
+        count = int(np.prod(shape))
+        esz = torch.tensor([], dtype=dtype).element_size()
+        if count * esz > n.value:
+            raise ValueError("view larger than the buffer")
+        return _wrap_device(p.value, dtype, shape, self.device, self._ws)
+
+
+def _wrap_device(addr, dtype, shape, device, owner):
+    """View device memory at addr (inside owner's allocation) as a tensor."""
+    base = owner.data_ptr()
+    off = addr - base
+    esz = torch.tensor([], dtype=dtype).element_size()
+    count = int(np.prod(shape))
+    if off < 0 or off + count * esz > owner.numel() * owner.element_size():
+        raise ValueError("address outside the workspace")
+    return owner[off:off + count * esz].view(dtype).view(*shape)

@@ -1,0 +1,167 @@
+"""CPU checks of the boundary: the library loads and exports every symbol the
+headers declare, argument validation happens before any device call, and the
+host state module's fp64 decisions equal the oracle's bit for bit."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import controls, schedule
+from workloads import CONFIGS, get_config
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+L = pytest.importorskip("streaming_diffusion_amd._lib")
+
+
+def header_symbols():
+    syms = set()
+    for h in ("sd_stream.h", "sd_kernels.h"):
+        src = open(os.path.join(ROOT, "include", h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        syms |= set(re.findall(r"\b(sd_(?:stream|k)_\w+)\s*\(", src))
+    return sorted(syms)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.load()
+
+
+@pytest.fixture(scope="module")
+def state():
+    return L.load_state()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    syms = header_symbols()
+    assert len(syms) >= 14
+    for s in syms:
+        assert hasattr(lib, s), s
+    assert set(syms) == set(L.SIGNATURES), "binding and headers disagree"
+
+
+def test_struct_sizes_match_a_c_compiler(tmp_path):
+    """Compile a probe against the header and compare sizeof/offsetof with ctypes."""
+    probe = tmp_path / "probe.c"
+    fields = [f for f, _ in L.sd_stream_config._fields_]
+    lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{ROOT}/include/sd_kernels.h"', "int main(void){"]
+    lines.append('printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(sd_stream_config), sizeof(sd_weights), '
+                 'sizeof(sd_push_info), sizeof(sd_step_info), sizeof(sd_sink_info), sizeof(sd_kv_segment));')
+    for f in fields:
+        lines.append(f'printf("%zu\\n", offsetof(sd_stream_config, {f}));')
+    lines.append("return 0;}")
+    probe.write_text("\n".join(lines))
+    exe = tmp_path / "probe"
+    assert os.system(f"gcc -o {exe} {probe}") == 0
+    out = os.popen(str(exe)).read().split()
+    sizes = [int(v) for v in out[:6]]
+    assert sizes == [C.sizeof(L.sd_stream_config), C.sizeof(L.sd_weights), C.sizeof(L.sd_push_info),
+                     C.sizeof(L.sd_step_info), C.sizeof(L.sd_sink_info), C.sizeof(L.sd_kv_segment)]
+    offs = [int(v) for v in out[6:]]
+    assert offs == [getattr(L.sd_stream_config, f).offset for f in fields]
+
+
+def cfg_struct(name, **kw):
+    from streaming_diffusion_amd.runner import make_config
+    return make_config(get_config(name, **kw))
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_workload_configs_validate(lib, state, name):
+    c = cfg_struct(name)
+    msg = C.create_string_buffer(256)
+    assert state.sdstate_validate(C.byref(c), msg, 256) == 0, msg.value
+    assert lib.sd_stream_workspace_bytes(C.byref(c)) > 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_heads=5), L.SD_ERR_SHAPE),
+    (dict(t_index=(32, 51)), L.SD_ERR_ARG),
+    (dict(window_tokens=32), L.SD_ERR_ARG),          # window smaller than a chunk
+    (dict(ssf_eta=1.0), L.SD_ERR_ARG),
+    (dict(chunks_per_step=2), L.SD_ERR_ARG),
+    (dict(cfg_type="onetime"), L.SD_ERR_ARG),        # tiny has no context
+    (dict(latent_h=15), L.SD_ERR_SHAPE),
+])
+def test_invalid_configs_are_rejected(lib, state, kw, code):
+    c = cfg_struct("tiny", **kw)
+    assert state.sdstate_validate(C.byref(c), None, 0) == code
+    assert lib.sd_stream_workspace_bytes(C.byref(c)) == 0
+
+
+def test_create_rejects_bad_arguments_before_any_device_call(lib):
+    c = cfg_struct("tiny")
+    w = L.sd_weights()
+    h = C.c_void_p()
+    assert lib.sd_stream_create(None, C.byref(w), None, 0, None, C.byref(h)) == L.SD_ERR_ARG
+    assert lib.sd_stream_create(C.byref(c), C.byref(w), C.c_void_p(256), 1 << 30, None, C.byref(h)) == L.SD_ERR_ARG
+    for f in L.WEIGHT_FIELDS:
+        setattr(w, f, 4096)
+    assert lib.sd_stream_create(C.byref(c), C.byref(w), None, 1 << 30, None, C.byref(h)) == L.SD_ERR_WORKSPACE
+    assert lib.sd_stream_create(C.byref(c), C.byref(w), C.c_void_p(4097), 1 << 30, None, C.byref(h)) == L.SD_ERR_WORKSPACE
+    assert lib.sd_stream_create(C.byref(c), C.byref(w), C.c_void_p(4096), 16, None, C.byref(h)) == L.SD_ERR_WORKSPACE
+    assert lib.sd_stream_push_frame(None, None, None, None, 0.0, None) == L.SD_ERR_ARG
+    assert lib.sd_stream_step(None, None, None) == L.SD_ERR_ARG
+    assert lib.sd_stream_kv_reset(None) == L.SD_ERR_ARG
+    assert lib.sd_k_gemm(0, None, None, None, None, 1, 1, 8, None) == L.SD_ERR_ARG
+    assert lib.sd_k_gemm(1, 8, 8, None, 8, 1, 1, 12, None) == L.SD_ERR_SHAPE
+    seg = L.sd_kv_segment(k=8, vt=8, cap=64, start=0, count=100, wrap=0)
+    assert lib.sd_k_attention(1, 8, 0, 0, 8, 1, 1, 8, 64, 1, C.byref(seg), None) == L.SD_ERR_SHAPE
+    assert lib.sd_k_attention(1, 8, 0, 0, 8, 1, 1, 8, 48, 1, C.byref(seg), None) == L.SD_ERR_SHAPE
+
+
+# ------------------------------------------------------------------ host state vs oracle, bit for bit
+def test_schedule_bit_exact(state):
+    c = cfg_struct("tiny")
+    a = (C.c_double * 1000)()
+    b = (C.c_double * 1000)()
+    state.sdstate_schedule(C.byref(c), a, b)
+    ab = schedule.alphas_cumprod()
+    assert np.array_equal(np.frombuffer(a, np.float64), np.sqrt(ab))
+    assert np.array_equal(np.frombuffer(b, np.float64), np.sqrt(1.0 - ab))
+
+
+def test_timesteps_bit_exact(state):
+    out = (C.c_int32 * 8)()
+    c = cfg_struct("fourstep")
+    state.sdstate_taus_t_index(C.byref(c), out)
+    assert list(out)[:4] == schedule.taus_from_t_index(get_config("fourstep"))
+    rng = np.random.default_rng(0)
+    for s in list(rng.uniform(0.3, 0.9, 500)) + [0.5, 0.3, 0.9, 1.0 / 3.0]:
+        for n in (1, 2, 3, 4):
+            state.sdstate_taus_noise_rate(float(s), n, 1000, out)
+            assert list(out)[:n] == schedule.taus_from_noise_rate(float(s), n)
+
+
+def test_ssf_tail_bit_exact(state):
+    rng = np.random.default_rng(1)
+    for _ in range(300):
+        a = rng.integers(0, 256, 500)
+        b = np.clip(a + rng.integers(-9, 10, 500), 0, 255)
+        D, N1, N2 = controls.ssf_sums(a, b)
+        sim = state.sdstate_ssf_cosine(D, N1, N2)
+        assert sim == controls.cosine_from_sums(D, N1, N2)
+        for eta in (0.5, 0.95, 0.98):
+            assert state.sdstate_ssf_probability(sim, eta) == controls.skip_probability(sim, eta)
+    assert state.sdstate_ssf_cosine(0, 0, 0) == 1.0
+    assert state.sdstate_ssf_cosine(0, 0, 5) == 0.0
+
+
+def test_motion_bit_exact(state):
+    cfg = get_config("video13b")
+    c = cfg_struct("video13b")
+    rng = np.random.default_rng(2)
+    s = cfg.s_max
+    win = []
+    for _ in range(200):
+        ss = int(rng.integers(0, 1 << 50))
+        dist = state.sdstate_motion_distance(ss, 99840)
+        assert dist == controls.motion_distance(ss, 99840)
+        win = (win + [dist])[-cfg.motion_k:]
+        arr = (C.c_double * len(win))(*win)
+        s_c = state.sdstate_motion_update(s, arr, len(win), C.byref(c))
+        s_o = controls.motion_update(s, win, cfg)
+        assert s_c == s_o
+        s = s_o

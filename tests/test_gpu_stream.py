@@ -1,0 +1,172 @@
+"""GPU parity of whole Stream Batch steps through the C ABI (sd_stream_*)
+against the CPU oracle: denoiser outputs per row, emitted frames, SSF
+decisions and every integer of the step state, KV ring contents and sink
+decisions.  Shapes are reduced versions of the workloads (same code paths:
+head dims, tile tails, cross-attention, onetime-negative rows, motion)."""
+import numpy as np
+import pytest
+import torch
+
+import streaming_diffusion_amd._lib as L
+from oracle.stream import OracleStream
+from streaming_diffusion_amd.runner import StreamRunner, upload_weights
+from workloads import gen, get_config
+
+from gpu_helpers import check_close, device, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def reduced(name, **kw):
+    base = {
+        "tiny": {},
+        "image": dict(n_blocks=2),
+        "fourstep": dict(n_blocks=2, d_model=256, n_heads=4, d_ffn=1024),
+        "video13b": dict(n_blocks=2, d_model=256, n_heads=2, d_ffn=512, latent_h=16, latent_w=24,
+                         sink_tokens=96, window_tokens=576),
+    }[name]
+    base.update(kw)
+    return get_config(name, **base)
+
+
+def run_parity(cfg, steps, check_ring=True):
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    weights = gen.make_weights(cfg)
+    ctx_pos = gen.make_context(cfg)
+    ctx_neg = gen.make_context(cfg, negative=True) if cfg.cfg_type == "onetime" else None
+    orc = OracleStream(cfg, weights, ctx_pos, ctx_neg)
+    run = StreamRunner(cfg, upload_weights(cfg, weights))
+    if cfg.ctx_len:
+        run.set_context(to_dev(ctx_pos, tdt), to_dev(ctx_neg, tdt) if ctx_neg is not None else None)
+    src, nz, us = gen.LatentSource(cfg), gen.NoiseSource(cfg), gen.UniformSource()
+    ssf_src = gen.SSFFrameSource(cfg) if cfg.ssf_on and cfg.ssf_kind == "u8" else None
+    lat = cfg.latent_elems
+    done = pushes = 0
+    worst = 0.0
+    while done < steps:
+        x0, e, u = src.next(), nz.next(), us.next()
+        frame = ssf_src.next() if ssf_src else None
+        po = orc.push_frame(x0, e, frame, u)
+        pg = run.push(to_dev(x0, torch.float32), to_dev(e, torch.float32),
+                      to_dev(frame, torch.uint8) if frame is not None else None, u)
+        pushes += 1
+        # SSF decision, probability and similarity: bit-exact
+        assert bool(pg.skipped) == po.skipped, f"push {pushes}"
+        assert pg.p == po.p and pg.sim == po.sim, (pushes, pg.p, po.p)
+        if po.skipped:
+            continue
+        assert list(pg.taus)[:cfg.n_slots] == po.taus and pg.t0 == po.t0 and pg.s == po.s
+        out_o, so = orc.step()
+        sg = run.step()
+        torch.cuda.synchronize()
+        assert (sg.has_output, sg.rows, sg.frame_id) == (int(so.has_output), so.rows, so.frame_id)
+        assert (sg.kv_ptr, sg.kv_valid, sg.sink_count, sg.rope_next) == (so.kv_ptr, so.kv_valid, so.sink_count,
+                                                                         so.rope_next)
+        eps = run.buffer(L.SD_BUF_EPS, torch.float32, (sg.rows, lat)).cpu().numpy()
+        for r in range(sg.rows):
+            worst = max(worst, check_close(eps[r], orc.last_eps[r].ravel(), cfg.dtype, f"step {done} eps row {r}"))
+        if out_o is not None:
+            worst = max(worst, check_close(run.out.cpu().numpy(), out_o, cfg.dtype, f"step {done} output"))
+        if not np.isnan(so.sink_sim):
+            si = run.sink_info()
+            assert si.evaluated == 1 and si.entry == so.sink_entry
+            if abs(so.sink_sim - cfg.sink_tau) > 1e-2:
+                assert bool(si.refreshed) == so.sink_refreshed, (done, si.sim, so.sink_sim)
+        done += 1
+    if check_ring and cfg.window_tokens:
+        H, hd, W = cfg.n_heads, cfg.head_dim, cfg.window_tokens
+        ringK = run.buffer(L.SD_BUF_RING_K, tdt, (cfg.n_blocks, H, W, hd)).float().cpu().numpy()
+        ringV = run.buffer(L.SD_BUF_RING_V, tdt, (cfg.n_blocks, H, hd, W)).float().cpu().numpy()
+        valid = [(orc.kv_ptr - orc.kv_valid + j) % W for j in range(orc.kv_valid)]
+        for b in range(cfg.n_blocks):
+            check_close(ringK[b].transpose(1, 0, 2)[valid], orc.ringK[b][valid], cfg.dtype, f"ring K block {b}",
+                          stored_bf16=True)
+            check_close(ringV[b].transpose(2, 0, 1)[valid], orc.ringV[b][valid], cfg.dtype, f"ring V block {b}",
+                          stored_bf16=True)
+    print(f"{cfg.name}: {done} steps over {pushes} pushes, worst error {worst:.3e}", flush=True)
+    run.close()
+    return orc, run
+
+
+def test_tiny_fp32_sixteen_steps_with_ssf():
+    device()
+    cfg = reduced("tiny")
+    print("tiny fp32 16 steps", flush=True)
+    orc, _ = run_parity(cfg, 16)
+    assert orc.sink_count == 1
+
+
+def test_tiny_fp32_without_ssf_three_slots_and_kv_reset():
+    device()
+    cfg = reduced("tiny", ssf_on=False, t_index=(10, 32, 45), window_tokens=128)
+    print("tiny fp32 n=3 W=128", flush=True)
+    run_parity(cfg, 7)
+
+
+def test_image_bf16_two_slots_cross_attention():
+    device()
+    cfg = reduced("image")
+    print("image bf16 reduced", flush=True)
+    run_parity(cfg, 5)
+
+
+def test_image_bf16_single_slot():
+    device()
+    cfg = reduced("image", t_index=(32,))
+    print("image bf16 n=1", flush=True)
+    run_parity(cfg, 3)
+
+
+def test_fourstep_bf16_onetime_negative_with_latent_ssf():
+    device()
+    cfg = reduced("fourstep")
+    print("fourstep bf16 reduced", flush=True)
+    run_parity(cfg, 6)
+
+
+def test_video_bf16_motion_sink_refresh():
+    device()
+    cfg = reduced("video13b")
+    print("video bf16 reduced", flush=True)
+    orc, _ = run_parity(cfg, 8)
+    assert orc.kv_valid == cfg.window_tokens
+
+
+def test_kv_reset_mid_stream_matches_oracle():
+    device()
+    cfg = reduced("tiny", ssf_on=False)
+    weights = gen.make_weights(cfg)
+    orc = OracleStream(cfg, weights)
+    run = StreamRunner(cfg, upload_weights(cfg, weights))
+    src, nz = gen.LatentSource(cfg), gen.NoiseSource(cfg)
+    for k in range(6):
+        if k == 3:
+            orc.kv_reset()
+            run.kv_reset()
+        x0, e = src.next(), nz.next()
+        po = orc.push_frame(x0, e)
+        pg = run.push(to_dev(x0, torch.float32), to_dev(e, torch.float32))
+        assert pg.t0 == po.t0
+        out_o, so = orc.step()
+        sg = run.step()
+        torch.cuda.synchronize()
+        assert (sg.kv_ptr, sg.kv_valid, sg.sink_count) == (so.kv_ptr, so.kv_valid, so.sink_count)
+        if out_o is not None:
+            check_close(run.out.cpu().numpy(), out_o, "f32", f"step {k}")
+    run.close()
+
+
+def test_step_errors():
+    device()
+    cfg = reduced("tiny", ssf_on=False)
+    run = StreamRunner(cfg, upload_weights(cfg, gen.make_weights(cfg)))
+    with pytest.raises(L.SDError) as ei:
+        run.step()
+    assert ei.value.code == L.SD_ERR_NOT_READY
+    x = torch.zeros(run.lat_shape, device=device())
+    for _ in range(4):
+        run.push(x, x)
+    with pytest.raises(L.SDError) as ei:
+        run.push(x, x)
+    assert ei.value.code == L.SD_ERR_STATE
+    run.close()
