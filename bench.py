@@ -1,0 +1,207 @@
+"""Throughput of the Stream Batch hot path on one MI355X.
+
+A step is one push_frame (motion reduction, noise rate, entry noising) plus
+one sd_stream_step (the whole stream-batched DiT forward over sink + window
+KV, R-CFG, latent update, KV append, sink decision) on the 1.3B-shaped video
+workload: 30 blocks, d 1536, 12 heads, FFN 8960, chunks of T=2 latent frames
+of 16 x 60 x 104 (3120 tokens), 1560 sink + 9360 window tokens, n = 2 slots,
+self-negative R-CFG, 77-token context, motion-aware noise on.  Inputs are
+synthetic (seeded blob-motion latents, N(0,1) noise, N(0,0.02) weights) and
+resident in device memory before timing starts.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=6)
+    ap.add_argument("--workload", default="video13b")
+    ap.add_argument("--n-slots", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-blocks", type=int, default=2, help="DiT blocks in the oracle sample")
+    return ap.parse_args()
+
+
+def slot_indices(n):
+    return {1: (32,), 2: (32, 45), 3: (16, 32, 45), 4: (0, 16, 32, 45)}[n]
+
+
+def cpu_baseline(cfg, n_blocks_sample: int):
+    """Time the CPU oracle on a bounded sample of the same workload: the full
+    forward of one row through `n_blocks_sample` DiT blocks at the real shapes
+    (3120 queries against a full 1560-sink + 9360-window cache plus its own
+    tokens), fp32, then scale to one stream-batch step (n_blocks x rows)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle.dit import Denoiser
+    from workloads import gen
+
+    sample_cfg = cfg.replace(n_blocks=n_blocks_sample)
+    w = gen.make_weights(sample_cfg)
+    net = Denoiser(sample_cfg, w, dtype=np.float32)
+    rng = np.random.default_rng(0)
+    H, hd = cfg.n_heads, cfg.head_dim
+    n_cache = cfg.sink_tokens + cfg.window_tokens
+    cache = [(rng.standard_normal((n_cache, H, hd), dtype=np.float32),
+              rng.standard_normal((n_cache, H, hd), dtype=np.float32)) for _ in range(n_blocks_sample)]
+    ctx = gen.make_context(sample_cfg)
+    ctx_kv = [net.cross_kv(ctx, b) for b in range(n_blocks_sample)] if ctx is not None else None
+    x = gen.LatentSource(cfg).next()
+    t0 = time.perf_counter()
+    net.forward_row(x, 359, 0, cache, ctx_kv)
+    dt = time.perf_counter() - t0
+    rows = cfg.rows_per_step
+    step_s = dt / n_blocks_sample * cfg.n_blocks * rows
+    threads = 0
+    for p in threadpool_info():
+        if p.get("user_api") == "blas":
+            threads = max(threads, int(p.get("num_threads", 0)))
+    return {
+        "value": cfg.latent_t / step_s,
+        "unit": "frames/s",
+        "cores": threads or len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": (f"one row through {n_blocks_sample} of {cfg.n_blocks} DiT blocks at full shape (fp32 NumPy, "
+                   f"{dt:.2f} s), scaled x{cfg.n_blocks // n_blocks_sample * rows} to one {rows}-row step "
+                   f"({step_s:.1f} s/step)"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU sharding of this path is "
+              "described in DESIGN.md and not run.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from streaming_diffusion_amd.runner import StreamRunner, random_device_weights
+    from workloads import gen, get_config
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cfg = get_config(args.workload, t_index=slot_indices(args.n_slots))
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    weights = random_device_weights(cfg, seed=gen.SEED_WEIGHTS)
+    run = StreamRunner(cfg, weights)
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    if cfg.ctx_len:
+        ctx = torch.from_numpy(gen.make_context(cfg)).to(dev).to(tdt)
+        ctx_neg = torch.from_numpy(gen.make_context(cfg, True)).to(dev).to(tdt) if cfg.cfg_type == "onetime" else None
+        run.set_context(ctx, ctx_neg)
+    total = args.warmup + args.steps + 2
+    src, nz = gen.LatentSource(cfg), gen.NoiseSource(cfg)
+    xs = [torch.from_numpy(src.next()).to(dev) for _ in range(total)]
+    ns = [torch.from_numpy(nz.next()).to(dev) for _ in range(total)]
+    out = torch.empty_like(xs[0])
+    torch.cuda.synchronize()
+
+    # warm-up (fills the slots, the window and the sink); time to first frame
+    k = 0
+    ttff_ms = None
+    t_first = time.perf_counter()
+    for _ in range(args.warmup):
+        run.push(xs[k], ns[k])
+        info = run.step(out)
+        k += 1
+        if info.has_output and ttff_ms is None:
+            torch.cuda.synchronize()
+            ttff_ms = (time.perf_counter() - t_first) * 1e3
+    torch.cuda.synchronize()
+
+    # timed region: the dominant kernel (self-attention) is timed live with events
+    run.profile(["attn_self"])
+    run.profile_read()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    emitted = 0
+    for _ in range(args.steps):
+        run.push(xs[k], ns[k])
+        info = run.step(out)
+        emitted += info.has_output * cfg.latent_t
+        k += 1
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    attn = run.profile_read().get("attn_self")
+    elapsed = t1 - t0
+    ms_per_step = elapsed / args.steps * 1e3
+
+    # untimed breakdown pass over every kernel kind (one step)
+    run.profile(list(__import__("streaming_diffusion_amd._lib", fromlist=["PROF_KINDS"]).PROF_KINDS))
+    run.push(xs[k], ns[k])
+    run.step(out)
+    k += 1
+    breakdown = run.profile_read()
+    run.profile([])
+
+    roofline = None
+    if attn and attn["launches"]:
+        per_launch_ms = attn["ms"] / attn["launches"]
+        per_launch_flop = attn["flops"] / attn["launches"]
+        achieved = per_launch_flop / (per_launch_ms * 1e-3) / 1e12
+        roofline = {"kernel": "attn_bf16_kernel<128> (self-attention over sink + window + own)",
+                    "bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "avg_launch_ms": round(per_launch_ms, 4), "flop_per_launch": per_launch_flop,
+                    "launches": attn["launches"]}
+    bd = {}
+    for name, v in breakdown.items():
+        if v["ms"] <= 0:
+            continue
+        bd[name] = {"ms": round(v["ms"], 3), "launches": v["launches"],
+                    "tflops": round(v["flops"] / (v["ms"] * 1e-3) / 1e12, 1) if v["flops"] else None,
+                    "gbs": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1)}
+
+    res = {
+        "metric": "denoised latent frames/s, one Stream Batch step per call (1.3B-shaped video DiT)",
+        "value": round(emitted / elapsed, 3),
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.n_blocks} blocks d{cfg.d_model} h{cfg.n_heads} ffn{cfg.d_ffn}, "
+                               f"chunk T={cfg.latent_t} {cfg.latent_c}x{cfg.latent_h}x{cfg.latent_w} "
+                               f"({cfg.tokens} tokens), sink {cfg.sink_tokens} + window {cfg.window_tokens}, "
+                               f"n={cfg.n_slots} slots, R-CFG {cfg.cfg_type}, ctx {cfg.ctx_len}, motion on",
+                   "rows_per_step": cfg.rows_per_step, "tokens_per_row": cfg.tokens,
+                   "frames_per_step": cfg.latent_t, "parallelism": "single GPU"},
+        "ttff_ms": round(ttff_ms, 2) if ttff_ms else None,
+        "roofline": roofline,
+        "breakdown_one_step": bd,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_blocks)
+    run.close()
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -200,6 +200,28 @@ typedef enum {
 } sd_buffer;
 sd_status sd_stream_buffer(sd_stream* s, int32_t which, void** ptr, size_t* bytes);
 
+/* Live kernel timing.  For every kernel kind whose bit is set in kind_mask,
+ * each launch is bracketed by HIP events on the stream; profile_read
+ * synchronises, returns per-kind totals (launches, milliseconds and the
+ * algorithmic flops and bytes of those launches) since the previous read, and
+ * resets them.  Events are created on first use and reused. */
+typedef enum {
+  SD_PROF_ATTN_SELF = 0, SD_PROF_ATTN_CROSS = 1, SD_PROF_GEMM_QKV = 2, SD_PROF_GEMM_O = 3,
+  SD_PROF_GEMM_FFN1 = 4, SD_PROF_GEMM_FFN2 = 5, SD_PROF_GEMM_CROSS = 6, SD_PROF_OTHER = 7,
+  SD_PROF_LN = 8, SD_PROF_GEMV = 9, SD_PROF_KV = 10, SD_PROF_EPILOGUE = 11, SD_PROF_CONTROLS = 12,
+  SD_PROF_KINDS = 13
+} sd_prof_kind;
+typedef struct {
+  int32_t kind;
+  int32_t reserved;
+  int64_t launches;
+  double ms;                   /* summed event time */
+  double flops;                /* summed algorithmic flops */
+  double bytes;                /* summed algorithmic bytes */
+} sd_kernel_stat;
+sd_status sd_stream_profile(sd_stream* s, uint32_t kind_mask);
+sd_status sd_stream_profile_read(sd_stream* s, sd_kernel_stat* out, int32_t n_max, int32_t* n_out);
+
 void sd_stream_destroy(sd_stream* s);
 const char* sd_stream_last_error(const sd_stream* s);
 

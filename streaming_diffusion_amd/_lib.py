@@ -69,6 +69,15 @@ class sd_sink_info(C.Structure):
     _fields_ = [("evaluated", C.c_int32), ("entry", C.c_int32), ("refreshed", C.c_int32), ("sim", C.c_float)]
 
 
+class sd_kernel_stat(C.Structure):
+    _fields_ = [("kind", C.c_int32), ("reserved", C.c_int32), ("launches", C.c_int64), ("ms", C.c_double),
+                ("flops", C.c_double), ("bytes", C.c_double)]
+
+
+PROF_KINDS = ["attn_self", "attn_cross", "gemm_qkv", "gemm_o", "gemm_ffn1", "gemm_ffn2", "gemm_cross", "other",
+              "ln_mod", "gemv", "kv_cache", "epilogue", "controls"]
+
+
 class sd_kv_segment(C.Structure):
     _fields_ = [("k", C.c_void_p), ("vt", C.c_void_p), ("k_head_stride", C.c_int64), ("vt_head_stride", C.c_int64),
                 ("k_row_stride", C.c_int64), ("vt_row_stride", C.c_int64), ("cap", C.c_int32), ("start", C.c_int32),
@@ -87,6 +96,8 @@ SIGNATURES = {
     "sd_stream_kv_reset": (C.c_int, [C.c_void_p]),
     "sd_stream_sink_info": (C.c_int, [C.c_void_p, C.POINTER(sd_sink_info)]),
     "sd_stream_buffer": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_void_p), C.POINTER(C.c_size_t)]),
+    "sd_stream_profile": (C.c_int, [C.c_void_p, C.c_uint32]),
+    "sd_stream_profile_read": (C.c_int, [C.c_void_p, C.POINTER(sd_kernel_stat), C.c_int32, C.POINTER(C.c_int32)]),
     "sd_stream_destroy": (None, [C.c_void_p]),
     "sd_stream_last_error": (C.c_char_p, [C.c_void_p]),
     "sd_k_gemm": (C.c_int, [C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,

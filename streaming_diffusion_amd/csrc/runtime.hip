@@ -65,6 +65,16 @@ struct sd_stream {
   int kv_ptr = 0, kv_valid = 0, sink_count = 0;
   bool ctx_set = false;
   bool has_ref_frame = false;
+  // live kernel timing (HIP events on the stream), per kind
+  uint32_t prof_mask = 0;
+  struct ProfRec { int kind; int ev; double flops, bytes; };
+  std::vector<hipEvent_t> ev_pool;
+  int ev_used = 0;
+  std::vector<ProfRec> prof_pending;
+  sd_kernel_stat prof_acc[SD_PROF_KINDS];
+  ~sd_stream() {
+    for (hipEvent_t e : ev_pool) (void)hipEventDestroy(e);
+  }
 };
 
 namespace {
@@ -164,6 +174,13 @@ sd_status set_err(sd_stream* s, sd_status code, const std::string& msg) {
   return code;
 }
 
+#define PROF(kind, flops, bytes, expr)              \
+  do {                                              \
+    const int _ev = prof_begin(s, kind);            \
+    HIP_TRY(expr);                                  \
+    prof_end(s, kind, _ev, (flops), (bytes));       \
+  } while (0)
+
 #define HIP_TRY(expr)                                                              \
   do {                                                                             \
     hipError_t _e = (expr);                                                        \
@@ -212,6 +229,32 @@ Epi epi_base(const sd_stream* s, int mode) {
   E.p = s->cfg.patch;
   E.T = s->Tn;
   return E;
+}
+
+// Start timing a launch of `kind` (returns -1 when that kind is not profiled).
+int prof_begin(sd_stream* s, int kind) {
+  if (!(s->prof_mask & (1u << kind))) return -1;
+  while ((int)s->ev_pool.size() < s->ev_used + 2) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return -1;
+    s->ev_pool.push_back(e);
+  }
+  const int ev = s->ev_used;
+  s->ev_used += 2;
+  if (hipEventRecord(s->ev_pool[ev], s->st) != hipSuccess) return -1;
+  return ev;
+}
+
+void prof_end(sd_stream* s, int kind, int ev, double flops, double bytes) {
+  if (ev < 0) return;
+  if (hipEventRecord(s->ev_pool[ev + 1], s->st) != hipSuccess) return;
+  s->prof_pending.push_back({kind, ev, flops, bytes});
+}
+
+double gflop(int64_t M, int64_t N, int64_t K) { return 2.0 * M * N * K; }
+// algorithmic bytes of a GEMM: both operands once plus the output traffic
+double gbytes(int64_t M, int64_t N, int64_t K, size_t es, double out_bytes) {
+  return (double)(M * K + N * K) * es + (double)M * N * out_bytes;
 }
 
 int free_frame(sd_stream* s) {
@@ -263,6 +306,7 @@ sd_status sd_stream_create(const sd_stream_config* cfg, const sd_weights* w, voi
   s->frames.assign(s->NF, FrameRec());
   for (int i = 0; i < SD_MAX_SLOTS; ++i) s->slots[i] = -1;
   s->ctl.s = s->cfg.s_max;
+  std::memset(s->prof_acc, 0, sizeof(s->prof_acc));
   // zero the caches (padding keys must stay finite) and upload RoPE tables
   std::vector<float2> rt, rh, rw;
   rope_tables(s, rt, rh, rw);
@@ -333,9 +377,12 @@ sd_status sd_stream_push_frame(sd_stream* s, const float* x0, const float* noise
   const int64_t ssf_n = c.ssf_kind == SD_SSF_U8 ? (int64_t)c.ssf_h * c.ssf_w * c.ssf_c : s->lat;
   const bool do_ssf = c.ssf_on && s->ctl.has_ref;
   long long hs[4 + 64] = {};
-  if (do_ssf) HIP_TRY(sdk::ssf_sums(s->st, c.ssf_kind, ssf_cur, s->ssf_ref, ssf_n, s->sums));
+  if (do_ssf)
+    PROF(SD_PROF_CONTROLS, 0.0, 2.0 * ssf_n * (c.ssf_kind == SD_SSF_U8 ? 1 : 4),
+         sdk::ssf_sums(s->st, c.ssf_kind, ssf_cur, s->ssf_ref, ssf_n, s->sums));
   if (c.motion_on)
-    HIP_TRY(sdk::motion_sums(s->st, x0, s->ctl.has_prev ? s->mprev : nullptr, s->Tn, s->frame_elems, s->sums + 4));
+    PROF(SD_PROF_CONTROLS, 0.0, 4.0 * (s->Tn + 1) * s->frame_elems,
+         sdk::motion_sums(s->st, x0, s->ctl.has_prev ? s->mprev : nullptr, s->Tn, s->frame_elems, s->sums + 4));
   if (do_ssf || c.motion_on) {
     HIP_TRY(hipMemcpyAsync(hs, s->sums, sizeof(long long) * (4 + s->Tn), hipMemcpyDeviceToHost, s->st));
     HIP_TRY(hipStreamSynchronize(s->st));
@@ -373,8 +420,9 @@ sd_status sd_stream_push_frame(sd_stream* s, const float* x0, const float* noise
   fr.fid = s->n_pushed++;
   fr.used = true;
   const int tau0 = fr.taus[0];
-  HIP_TRY(sdk::entry_noise(s->st, x0, noise, s->fx + (int64_t)f * s->lat, s->fx0s + (int64_t)f * s->lat, s->lat,
-                           (float)s->a[tau0], (float)s->b[tau0]));
+  PROF(SD_PROF_EPILOGUE, 2.0 * s->lat, 16.0 * s->lat,
+       sdk::entry_noise(s->st, x0, noise, s->fx + (int64_t)f * s->lat, s->fx0s + (int64_t)f * s->lat, s->lat,
+                        (float)s->a[tau0], (float)s->b[tau0]));
   s->pending.push_back(f);
   info->t0 = fr.t0;
   info->frame_id = fr.fid;
@@ -442,19 +490,23 @@ sd_status sd_stream_step(sd_stream* s, float* out_latent, sd_step_info* info) {
   const int ptr_old = s->kv_ptr;
 
   // ---- conditioning: timestep embedding -> MLP -> SiLU(c) -> adaLN vectors
-  HIP_TRY(sdk::temb_embed(st, rt, s->emb, c.d_freq));
-  HIP_TRY(sdk::gemv(st, bf, s->emb, s->w.t_w1, s->w.t_b1, s->h1, R, d, c.d_freq, 1));
-  HIP_TRY(sdk::gemv(st, bf, s->h1, s->w.t_w2, s->w.t_b2, s->sc, R, d, d, 1));
-  HIP_TRY(sdk::gemv(st, bf, s->sc, s->w.mod_w, s->w.mod_b, s->mod, R, 6 * d, d, 0));
-  HIP_TRY(sdk::gemv(st, bf, s->sc, s->w.fin_w, s->w.fin_b, s->fmod, R, 2 * d, d, 0));
+  PROF(SD_PROF_GEMV, 0.0, 4.0 * R * c.d_freq, sdk::temb_embed(st, rt, s->emb, c.d_freq));
+  PROF(SD_PROF_GEMV, 2.0 * R * d * c.d_freq, (double)d * c.d_freq * es,
+       sdk::gemv(st, bf, s->emb, s->w.t_w1, s->w.t_b1, s->h1, R, d, c.d_freq, 1));
+  PROF(SD_PROF_GEMV, 2.0 * R * d * d, (double)d * d * es, sdk::gemv(st, bf, s->h1, s->w.t_w2, s->w.t_b2, s->sc, R, d, d, 1));
+  PROF(SD_PROF_GEMV, 12.0 * R * d * d, 6.0 * d * d * es,
+       sdk::gemv(st, bf, s->sc, s->w.mod_w, s->w.mod_b, s->mod, R, 6 * d, d, 0));
+  PROF(SD_PROF_GEMV, 4.0 * R * d * d, 2.0 * d * d * es,
+       sdk::gemv(st, bf, s->sc, s->w.fin_w, s->w.fin_b, s->fmod, R, 2 * d, d, 0));
 
   // ---- patch embedding into the fp32 residual stream
-  HIP_TRY(sdk::patchify(st, bf, rt, s->fx, s->xm, s->lat, s->Tn, c.latent_c, c.latent_h, c.latent_w, c.patch));
+  PROF(SD_PROF_OTHER, 0.0, (4.0 + es) * R * s->lat,
+       sdk::patchify(st, bf, rt, s->fx, s->xm, s->lat, s->Tn, c.latent_c, c.latent_h, c.latent_w, c.patch));
   {
     Epi E = epi_base(s, EPI_PATCH);
     E.bias = s->w.pe_b;
     E.resid = s->resid;
-    HIP_TRY(sdk::gemm(st, bf, s->xm, s->w.pe_w, M, d, s->P, E));
+    PROF(SD_PROF_OTHER, gflop(M, d, s->P), gbytes(M, d, s->P, es, 4), sdk::gemm(st, bf, s->xm, s->w.pe_w, M, d, s->P, E));
   }
 
   const int nctx = c.cfg_type == SD_CFG_ONETIME ? 2 : 1;
@@ -462,7 +514,7 @@ sd_status sd_stream_step(sd_stream* s, float* out_latent, sd_step_info* info) {
   for (int b = 0; b < s->nb; ++b) {
     const void* blk = P(s->w.blk_mod, (int64_t)b * 6 * d, es);
     // self-attention
-    HIP_TRY(sdk::ln_mod(st, bf, s->resid, s->xm, M, d, L, s->mod, blk, 0, d, 6 * d, 1e-6f));
+    PROF(SD_PROF_LN, 0.0, (4.0 + es) * M * d, sdk::ln_mod(st, bf, s->resid, s->xm, M, d, L, s->mod, blk, 0, d, 6 * d, 1e-6f));
     {
       Epi E = epi_base(s, EPI_QKV);
       E.bias = P(s->w.qkv_b, (int64_t)b * 3 * d, es);
@@ -472,7 +524,8 @@ sd_status sd_stream_step(sd_stream* s, float* out_latent, sd_step_info* info) {
       E.kstride = L;
       E.rope = 1;
       for (int r = 0; r < R; ++r) E.t0[r] = rt.r[r].t0;
-      HIP_TRY(sdk::gemm(st, bf, s->xm, P(s->w.qkv_w, (int64_t)b * 3 * d * d, es), M, 3 * d, d, E));
+      PROF(SD_PROF_GEMM_QKV, gflop(M, 3 * d, d), gbytes(M, 3 * d, d, es, es),
+           sdk::gemm(st, bf, s->xm, P(s->w.qkv_w, (int64_t)b * 3 * d * d, es), M, 3 * d, d, E));
     }
     {
       AttnArgs A;
@@ -511,11 +564,13 @@ sd_status sd_stream_step(sd_stream* s, float* out_latent, sd_step_info* info) {
       so.cap = L;
       so.count = L;
       A.nseg = ns;
-      HIP_TRY(sdk::attention(st, bf, A));
+      const double shared = (double)sk.count + sw.count;
+      PROF(SD_PROF_ATTN_SELF, 4.0 * R * L * (shared + L) * d,
+           (double)es * d * (2.0 * R * L + 2.0 * shared + 2.0 * R * L), sdk::attention(st, bf, A));
     }
     if (r_exit >= 0 && (s->Wt > 0 || capture)) {
       const int64_t cb = (int64_t)b * H * s->S8 * hd;
-      HIP_TRY(sdk::kv_append(st, bf, P(s->kown, r_exit * own_stride, es), P(s->vtown, r_exit * own_stride, es),
+      PROF(SD_PROF_KV, 0.0, 4.0 * L * d * es, sdk::kv_append(st, bf, P(s->kown, r_exit * own_stride, es), P(s->vtown, r_exit * own_stride, es),
                              Pm(s->ringK, (int64_t)b * H * s->Wt * hd, es), Pm(s->ringVT, (int64_t)b * H * s->Wt * hd, es),
                              H, hd, L, s->Wt, s->kv_ptr, capture ? Pm(s->sinkK, cb, es) : nullptr,
                              capture ? Pm(s->sinkVT, cb, es) : nullptr, s->S8, s->sink_count * s->Se, s->Se));
@@ -527,17 +582,20 @@ sd_status sd_stream_step(sd_stream* s, float* out_latent, sd_step_info* info) {
       E.mod = s->mod;
       E.blk = blk;
       E.gate_off = 2 * d;
-      HIP_TRY(sdk::gemm(st, bf, s->ao, P(s->w.o_w, (int64_t)b * d * d, es), M, d, d, E));
+      PROF(SD_PROF_GEMM_O, gflop(M, d, d), gbytes(M, d, d, es, 8),
+           sdk::gemm(st, bf, s->ao, P(s->w.o_w, (int64_t)b * d * d, es), M, d, d, E));
     }
     // cross-attention to the pre-computed prompt K/V
     if (c.ctx_len > 0) {
-      HIP_TRY(sdk::ln_mod(st, bf, s->resid, s->xm, M, d, L, nullptr, nullptr, 0, 0, 6 * d, 1e-6f));
+      PROF(SD_PROF_LN, 0.0, (4.0 + es) * M * d,
+           sdk::ln_mod(st, bf, s->resid, s->xm, M, d, L, nullptr, nullptr, 0, 0, 6 * d, 1e-6f));
       {
         Epi E = epi_base(s, EPI_QKV);
         E.bias = P(s->w.cq_b, (int64_t)b * d, es);
         E.q = s->q;
         E.rope = 0;
-        HIP_TRY(sdk::gemm(st, bf, s->xm, P(s->w.cq_w, (int64_t)b * d * d, es), M, d, d, E));
+        PROF(SD_PROF_GEMM_CROSS, gflop(M, d, d), gbytes(M, d, d, es, es),
+             sdk::gemm(st, bf, s->xm, P(s->w.cq_w, (int64_t)b * d * d, es), M, d, d, E));
       }
       const size_t per = (size_t)H * s->ctx8 * hd;
       for (int part = 0; part < (neg_row >= 0 ? 2 : 1); ++part) {
@@ -561,23 +619,27 @@ sd_status sd_stream_step(sd_stream* s, float* out_latent, sd_step_info* info) {
         g.k_hs = g.vt_hs = (int64_t)s->ctx8 * hd;
         g.cap = s->ctx8;
         g.count = c.ctx_len;
-        HIP_TRY(sdk::attention(st, bf, A));
+        PROF(SD_PROF_ATTN_CROSS, 4.0 * A.R * L * c.ctx_len * d, (double)es * d * (2.0 * A.R * L + 2.0 * c.ctx_len),
+             sdk::attention(st, bf, A));
       }
       {
         Epi E = epi_base(s, EPI_RESID);
         E.bias = P(s->w.co_b, (int64_t)b * d, es);
         E.resid = s->resid;
-        HIP_TRY(sdk::gemm(st, bf, s->ao, P(s->w.co_w, (int64_t)b * d * d, es), M, d, d, E));
+        PROF(SD_PROF_GEMM_CROSS, gflop(M, d, d), gbytes(M, d, d, es, 8),
+             sdk::gemm(st, bf, s->ao, P(s->w.co_w, (int64_t)b * d * d, es), M, d, d, E));
       }
     }
     // feed-forward
-    HIP_TRY(sdk::ln_mod(st, bf, s->resid, s->xm, M, d, L, s->mod, blk, 3 * d, 4 * d, 6 * d, 1e-6f));
+    PROF(SD_PROF_LN, 0.0, (4.0 + es) * M * d,
+         sdk::ln_mod(st, bf, s->resid, s->xm, M, d, L, s->mod, blk, 3 * d, 4 * d, 6 * d, 1e-6f));
     {
       Epi E = epi_base(s, EPI_GELU);
       E.bias = P(s->w.f1_b, (int64_t)b * s->F, es);
       E.out = s->hid;
       E.ldo = s->F;
-      HIP_TRY(sdk::gemm(st, bf, s->xm, P(s->w.f1_w, (int64_t)b * s->F * d, es), M, s->F, d, E));
+      PROF(SD_PROF_GEMM_FFN1, gflop(M, s->F, d), gbytes(M, s->F, d, es, es),
+           sdk::gemm(st, bf, s->xm, P(s->w.f1_w, (int64_t)b * s->F * d, es), M, s->F, d, E));
     }
     {
       Epi E = epi_base(s, EPI_GATE_RESID);
@@ -586,30 +648,31 @@ sd_status sd_stream_step(sd_stream* s, float* out_latent, sd_step_info* info) {
       E.mod = s->mod;
       E.blk = blk;
       E.gate_off = 5 * d;
-      HIP_TRY(sdk::gemm(st, bf, s->hid, P(s->w.f2_w, (int64_t)b * d * s->F, es), M, d, s->F, E));
+      PROF(SD_PROF_GEMM_FFN2, gflop(M, d, s->F), gbytes(M, d, s->F, es, 8),
+           sdk::gemm(st, bf, s->hid, P(s->w.f2_w, (int64_t)b * d * s->F, es), M, d, s->F, E));
     }
   }
 
   // ---- adaptive sink: embedding of the exiting chunk, decision, predicated copy
   if (r_exit >= 0 && s->S > 0) {
     const int cap_entry = capture ? s->sink_count : -1;
-    HIP_TRY(sdk::sink_score(st, s->resid + (int64_t)r_exit * L * d, s->sink_part, L, d, s->sink_emb, s->Ment, cap_entry,
+    PROF(SD_PROF_CONTROLS, 0.0, 4.0 * L * d, sdk::sink_score(st, s->resid + (int64_t)r_exit * L * d, s->sink_part, L, d, s->sink_emb, s->Ment, cap_entry,
                             (float)c.sink_tau, s->sink_flag, s->sink_sim));
     if (!capture)
-      HIP_TRY(sdk::sink_copy(st, bf, s->sink_flag, s->ringK, s->ringVT, s->sinkK, s->sinkVT, s->nb, H, hd, s->Wt,
+      PROF(SD_PROF_KV, 0.0, 4.0 * s->nb * s->Se * d * es, sdk::sink_copy(st, bf, s->sink_flag, s->ringK, s->ringVT, s->sinkK, s->sinkVT, s->nb, H, hd, s->Wt,
                              s->S8, ptr_old, s->Se));
   }
 
   // ---- final layer and unpatchify -> eps_c
-  HIP_TRY(sdk::ln_mod(st, bf, s->resid, s->xm, M, d, L, s->fmod, nullptr, 0, d, 2 * d, 1e-6f));
+  PROF(SD_PROF_LN, 0.0, (4.0 + es) * M * d, sdk::ln_mod(st, bf, s->resid, s->xm, M, d, L, s->fmod, nullptr, 0, d, 2 * d, 1e-6f));
   {
     Epi E = epi_base(s, EPI_HEAD);
     E.bias = s->w.head_b;
     E.eps = s->eps;
-    HIP_TRY(sdk::gemm(st, bf, s->xm, s->w.head_w, M, s->P, d, E));
+    PROF(SD_PROF_OTHER, gflop(M, s->P, d), gbytes(M, s->P, d, es, 4), sdk::gemm(st, bf, s->xm, s->w.head_w, M, s->P, d, E));
   }
   // ---- R-CFG, x0 prediction, re-noise / emit
-  HIP_TRY(sdk::rcfg_update(st, rt, s->fx, s->fx0s, s->eps, out_latent, s->lat, (float)c.gamma, (float)c.delta,
+  PROF(SD_PROF_EPILOGUE, 12.0 * R * s->lat, 16.0 * R * s->lat, sdk::rcfg_update(st, rt, s->fx, s->fx0s, s->eps, out_latent, s->lat, (float)c.gamma, (float)c.delta,
                            neg_row));
 
   // ---- host bookkeeping
@@ -671,6 +734,35 @@ sd_status sd_stream_buffer(sd_stream* s, int32_t which, void** ptr, size_t* byte
     case SD_BUF_MOD: *ptr = s->mod; *bytes = (size_t)s->Rmax * 6 * s->d * 4; break;
     default: return set_err(s, SD_ERR_ARG, "unknown buffer");
   }
+  return SD_OK;
+}
+
+sd_status sd_stream_profile(sd_stream* s, uint32_t kind_mask) {
+  if (!s) return SD_ERR_ARG;
+  s->prof_mask = kind_mask;
+  return SD_OK;
+}
+
+sd_status sd_stream_profile_read(sd_stream* s, sd_kernel_stat* out, int32_t n_max, int32_t* n_out) {
+  if (!s || !out || !n_out || n_max < 1) return SD_ERR_ARG;
+  HIP_TRY(hipStreamSynchronize(s->st));
+  for (int k = 0; k < SD_PROF_KINDS; ++k) s->prof_acc[k].kind = k;
+  for (const auto& r : s->prof_pending) {
+    float ms = 0.f;
+    HIP_TRY(hipEventElapsedTime(&ms, s->ev_pool[r.ev], s->ev_pool[r.ev + 1]));
+    sd_kernel_stat& a = s->prof_acc[r.kind];
+    a.launches += 1;
+    a.ms += ms;
+    a.flops += r.flops;
+    a.bytes += r.bytes;
+  }
+  s->prof_pending.clear();
+  s->ev_used = 0;
+  int n = 0;
+  for (int k = 0; k < SD_PROF_KINDS && n < n_max; ++k)
+    if (s->prof_acc[k].launches > 0) out[n++] = s->prof_acc[k];
+  *n_out = n;
+  std::memset(s->prof_acc, 0, sizeof(s->prof_acc));
   return SD_OK;
 }
 

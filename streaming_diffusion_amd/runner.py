@@ -133,6 +133,21 @@ class StreamRunner:
         L.check(self.lib.sd_stream_sink_info(self.h, C.byref(info)), self.h)
         return info
 
+    def profile(self, kinds):
+        """Time every launch of the named kinds (see _lib.PROF_KINDS) with HIP events."""
+        mask = 0
+        for k in kinds:
+            mask |= 1 << L.PROF_KINDS.index(k)
+        L.check(self.lib.sd_stream_profile(self.h, mask), self.h)
+
+    def profile_read(self) -> dict:
+        """Per-kind totals since the last read: {kind: dict(launches, ms, flops, bytes)}."""
+        arr = (L.sd_kernel_stat * len(L.PROF_KINDS))()
+        n = C.c_int32()
+        L.check(self.lib.sd_stream_profile_read(self.h, arr, len(L.PROF_KINDS), C.byref(n)), self.h)
+        return {L.PROF_KINDS[a.kind]: dict(launches=a.launches, ms=a.ms, flops=a.flops, bytes=a.bytes)
+                for a in arr[:n.value]}
+
     def buffer(self, which: int, dtype, shape):
         """A torch view of an internal device buffer (no copy)."""
         p = C.c_void_p()
