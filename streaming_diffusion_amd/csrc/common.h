@@ -35,6 +35,18 @@ SD_DEV long long wave_sum_i64(long long v) {
   return v;
 }
 
+// MI355X dispatches consecutive workgroups of a launch round-robin over its
+// 8 XCDs, each with a private L2.  xcd_remap turns the hardware workgroup id
+// into a logical id such that each XCD receives one contiguous range of
+// logical ids (a bijection on [0, n)); neighbouring logical work items --
+// which share operands -- then meet in the same L2.
+#define SD_NUM_XCD 8
+SD_DEV int xcd_remap(int pid, int n) {
+  const int xcd = pid % SD_NUM_XCD, k = pid / SD_NUM_XCD;
+  const int base = n / SD_NUM_XCD, rem = n % SD_NUM_XCD;
+  return (xcd < rem ? xcd * (base + 1) : rem * (base + 1) + (xcd - rem) * base) + k;
+}
+
 // Per-row description of one forward.  Passed by value as a kernel argument.
 struct RowInfo {
   int32_t frame;      // frame-store record of the row's latent

@@ -59,14 +59,18 @@ SD_DEV int key_pos(const KvSeg& g, int u) {
 
 // ---------------------------------------------------------------------------
 template <int HD>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   constexpr int BQ = 128, KB = 64, PK = 8, PV = 8;
   constexpr int LK = HD + PK, LV = KB + PV;
   __shared__ __attribute__((aligned(16))) bf16 Ks[2][KB * LK];
   __shared__ __attribute__((aligned(16))) bf16 Vs[2][HD * LV];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int qt = blockIdx.x, h = blockIdx.y, r = a.r0 + blockIdx.z;
+  // logical order (row, head, q-tile) with q-tiles fastest; all q-tiles of a
+  // (row, head) share its keys, so they are kept on one XCD
+  const int nqt = (a.L + BQ - 1) / BQ;
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int qt = lid % nqt, h = (lid / nqt) % a.H, r = a.r0 + lid / (nqt * a.H);
   const int q0 = qt * BQ;
   const SegRt sr = seg_layout(a);
   const int NK = sr.end[2];
@@ -90,6 +94,33 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   bf16x8 rk[CK > 0 ? CK : 1], rv[CV > 0 ? CV : 1];
   auto gload = [&](int tile) {
     const bf16x8 z = {};
+    // Fast path (all but a few tiles of a row): the whole tile is valid keys
+    // of one segment at contiguous positions.  Everything below is uniform
+    // over the workgroup.
+    {
+      const int jb = tile * KB;
+      const int s0 = key_seg(sr, jb);
+      const int b0 = s0 == 0 ? sr.begin[0] : (s0 == 1 ? sr.begin[1] : sr.begin[2]);
+      const KvSeg g = seg_pick(a, s0);
+      const int u0 = jb - b0;
+      int p0 = g.start + u0;
+      if (g.wrap && p0 >= g.cap) p0 -= g.cap;
+      if (u0 + KB <= g.count && p0 + KB <= g.cap) {
+        const bf16* kb = (const bf16*)g.k + (int64_t)r * g.k_rs + (int64_t)h * g.k_hs + (int64_t)p0 * HD;
+        const bf16* vb = (const bf16*)g.vt + (int64_t)r * g.vt_rs + (int64_t)h * g.vt_hs + p0;
+#pragma unroll
+        for (int i = 0; i < CK; ++i) {
+          const int c = tid + i * 256, key = c / (HD / 8), e0 = (c % (HD / 8)) * 8;
+          rk[i] = *(const bf16x8*)(kb + key * HD + e0);
+        }
+#pragma unroll
+        for (int i = 0; i < CV; ++i) {
+          const int c = tid + i * 256, e = c / (KB / 8), k0 = (c % (KB / 8)) * 8;
+          rv[i] = *(const bf16x8*)(vb + (int64_t)e * g.cap + k0);
+        }
+        return;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < CK; ++i) {
       const int c = tid + i * 256, key = c / (HD / 8), e0 = (c % (HD / 8)) * 8;
@@ -179,39 +210,47 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
     const bool full = (jb + KB <= sr.begin[0] + sr.count[0]) ||
                       (jb >= sr.begin[1] && jb + KB <= sr.begin[1] + sr.count[1]) ||
                       (jb >= sr.begin[2] && jb + KB <= sr.begin[2] + sr.count[2]);
+    // running max in raw score units (the scale is positive); the scale and
+    // the log2(e) factor are folded into one FMA in front of exp2
     float mx = -INFINITY;
+    if (!full) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int j = jb + kt * 32 + 16 * (q >> 3) + 8 * half + (q & 7);
+          if (!key_valid(sr, j)) s[kt][q] = -INFINITY;
+        }
+    }
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        float v = s[kt][q] * sl2;
-        if (!full) {
-          const int j = jb + kt * 32 + 16 * (q >> 3) + 8 * half + (q & 7);
-          if (!key_valid(sr, j)) v = -INFINITY;
-        }
-        s[kt][q] = v;
-        mx = fmaxf(mx, v);
-      }
+      for (int q = 0; q < 16; ++q) mx = fmaxf(mx, s[kt][q]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(m_run, mx);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+    const float alpha = exp2f((m_run - m_use) * sl2);
+    const float moff = -m_use * sl2;
     float psum = 0.f;
     bf16x8 pb[4];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const float p = exp2f(s[kt][q] - m_use);
+        const float p = exp2f(fmaf(s[kt][q], sl2, moff));
         psum += p;
         pb[kt * 2 + (q >> 3)][q & 7] = (bf16)p;
       }
     l_run = l_run * alpha + psum;
     m_run = m_new;
+    // rescale only when some query of the wave raised its maximum (exact:
+    // alpha is 1 otherwise)
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
-    for (int t = 0; t < HD / 32; ++t)
+      for (int t = 0; t < HD / 32; ++t)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) o[t][q] *= alpha;
+        for (int q = 0; q < 16; ++q) o[t][q] *= alpha;
+    }
     // O^T += V^T P^T over 4 key blocks of 16
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -328,7 +367,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
 hipError_t attention(hipStream_t s, bool bf, const AttnArgs& a) {
   if (a.R == 0 || a.L == 0) return hipSuccess;
   if (bf) {
-    dim3 g((a.L + 127) / 128, a.H, a.R);
+    const dim3 g(((a.L + 127) / 128) * a.H * a.R);
     switch (a.hd) {
       case 32: attn_bf16_kernel<32><<<g, 256, 0, s>>>(a); break;
       case 64: attn_bf16_kernel<64><<<g, 256, 0, s>>>(a); break;

@@ -110,7 +110,15 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const bf16* __restrict__
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WM, wn = wave / WM;
-  const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
+  // XCD-contiguous logical ids, then groups of GM tile-rows walked column by
+  // column so that the workgroups resident on one XCD share A and W tiles
+  constexpr int GM = 4;
+  const int tiles_n = (N + BN - 1) / BN;
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int grp = lid / (GM * tiles_n), first_m = grp * GM;
+  const int gm = min(tiles_m - first_m, GM);
+  const int within = lid - grp * GM * tiles_n;
+  const int tm = first_m + within % gm, tn = within / gm;
   const int m0 = tm * BM, n0 = tn * BN;
 
   f32x16 acc[FM][FN];
