@@ -1,11 +1,9 @@
-// GEMMs of the denoiser: C[m][n] = sum_k A[m][k] W[n][k] with the fused
+// GEMMs of the denoiser, C[m][n] = sum_k A[m][k] W[n][k], with the fused
 // epilogues of the DiT block (bias, GELU, gate * (.) + residual, q|k|v split
-// with 3D RoPE and per-head scatter, unpatchify).
-//
-// bf16: MFMA v_mfma_f32_32x32x16_bf16 on LDS-staged tiles, BK = 64, two LDS
-// stages with register prefetch of the next k-tile, fp32 accumulation.
-// fp32: a vector-ALU tiled kernel (64 x 64 tile, 4 x 4 outputs per thread)
-// for the fp32 configuration.
+// with 3D RoPE and per-head scatter, unpatchify).  bf16 problems go to the
+// matrix-core kernel (k_gemm_mfma.hip); this file holds the fp32 path, a
+// vector-ALU tiled kernel (64 x 64 tile, 4 x 4 outputs per thread) used by the
+// fp32 configuration, and the dispatch.
 #include <cmath>
 
 #include "kernels.h"
@@ -96,112 +94,6 @@ SD_DEV void epi_apply(const Epi& E, int m, int n, int N, float acc, float partne
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA GEMM.  256 threads = 4 waves arranged WM x WN; each wave owns a
-// (BM/WM) x (BN/WN) block of 32x32 MFMA tiles.
-template <int BM, int BN, int WM, int WN, int MODE>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
-                                                        int M, int N, int K, Epi E, int tiles_m) {
-  constexpr int BK = 64, PAD = 8, LDK = BK + PAD;
-  constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
-  constexpr int CA = BM * (BK / 8) / 256, CB = BN * (BK / 8) / 256;
-  static_assert(FM >= 1 && FN >= 1 && CA >= 1 && CB >= 1, "tile shape");
-  __shared__ __attribute__((aligned(16))) bf16 As[2][BM * LDK];
-  __shared__ __attribute__((aligned(16))) bf16 Bs[2][BN * LDK];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave % WM, wn = wave / WM;
-  // XCD-contiguous logical ids, then groups of GM tile-rows walked column by
-  // column so that the workgroups resident on one XCD share A and W tiles
-  constexpr int GM = 4;
-  const int tiles_n = (N + BN - 1) / BN;
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int grp = lid / (GM * tiles_n), first_m = grp * GM;
-  const int gm = min(tiles_m - first_m, GM);
-  const int within = lid - grp * GM * tiles_n;
-  const int tm = first_m + within % gm, tn = within / gm;
-  const int m0 = tm * BM, n0 = tn * BN;
-
-  f32x16 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-
-  bf16x8 ra[CA], rb[CB];
-  const bf16x8 zero8 = {};
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      const int c = tid + i * 256, row = c >> 3, kc = (c & 7) * 8;
-      const int gm = m0 + row, gk = k0 + kc;
-      ra[i] = (gm < M && gk < K) ? *(const bf16x8*)(A + (int64_t)gm * K + gk) : zero8;
-    }
-#pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      const int c = tid + i * 256, row = c >> 3, kc = (c & 7) * 8;
-      const int gn = n0 + row, gk = k0 + kc;
-      rb[i] = (gn < N && gk < K) ? *(const bf16x8*)(W + (int64_t)gn * K + gk) : zero8;
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      const int c = tid + i * 256, row = c >> 3, kc = (c & 7) * 8;
-      *(bf16x8*)(&As[buf][row * LDK + kc]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      const int c = tid + i * 256, row = c >> 3, kc = (c & 7) * 8;
-      *(bf16x8*)(&Bs[buf][row * LDK + kc]) = rb[i];
-    }
-  };
-
-  const int KT = (K + BK - 1) / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  const int lr = lane & 31, lk = (lane >> 5) * 8;
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) gload((kt + 1) * BK);
-    const bf16* as = &As[buf][(wm * TM + lr) * LDK + lk];
-    const bf16* bs = &Bs[buf][(wn * TN + lr) * LDK + lk];
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8 fa[FM], fb[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) fa[i] = *(const bf16x8*)(as + i * 32 * LDK + kk);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) fb[j] = *(const bf16x8*)(bs + j * 32 * LDK + kk);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < KT) sstore(buf ^ 1);
-    __syncthreads();
-  }
-
-  // C layout of a 32x32 tile: lane holds column lane%32 and rows
-  // 8*(q/4) + 4*(lane/32) + q%4.
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const float v = acc[i][j][q];
-        const float pv = __shfl_xor(v, 1, 64);
-        const int m = m0 + wm * TM + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-        const int n = n0 + wn * TN + j * 32 + (lane & 31);
-        if (m < M && n < N) epi_apply<bf16, MODE>(E, m, n, N, v, pv);
-      }
-}
-
-// ---------------------------------------------------------------------------
 // fp32 vector-ALU GEMM: 64 x 64 tile, BK = 16, 4 x 4 outputs per thread.
 template <int MODE>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A, const float* __restrict__ W,
@@ -247,36 +139,25 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 }
 
 template <int MODE>
-static hipError_t gemm_mode(hipStream_t s, bool bf, const void* A, const void* W, int M, int N, int K, const Epi& E) {
-  if (!bf) {
-    const int tm = (M + 63) / 64, tn = (N + 63) / 64;
-    gemm_f32_kernel<MODE><<<tm * tn, 256, 0, s>>>((const float*)A, (const float*)W, M, N, K, E, tm);
-    return hipGetLastError();
-  }
-  // Large problems: 256 x 128 tiles; otherwise 128 x 128.
-  const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 127) / 128);
-  if (t256 >= 512) {
-    const int tm = (M + 255) / 256, tn = (N + 127) / 128;
-    gemm_bf16_kernel<256, 128, 2, 2, MODE><<<tm * tn, 256, 0, s>>>((const bf16*)A, (const bf16*)W, M, N, K, E, tm);
-  } else {
-    const int tm = (M + 127) / 128, tn = (N + 127) / 128;
-    gemm_bf16_kernel<128, 128, 2, 2, MODE><<<tm * tn, 256, 0, s>>>((const bf16*)A, (const bf16*)W, M, N, K, E, tm);
-  }
+static hipError_t gemm_f32_mode(hipStream_t s, const void* A, const void* W, int M, int N, int K, const Epi& E) {
+  const int tm = (M + 63) / 64, tn = (N + 63) / 64;
+  gemm_f32_kernel<MODE><<<tm * tn, 256, 0, s>>>((const float*)A, (const float*)W, M, N, K, E, tm);
   return hipGetLastError();
 }
 
 hipError_t gemm(hipStream_t s, bool bf, const void* A, const void* W, int M, int N, int K, const Epi& E) {
   if (M == 0 || N == 0) return hipSuccess;
+  if (bf) return gemm_mfma(s, A, W, M, N, K, E);
   switch (E.mode) {
-    case EPI_STORE: return gemm_mode<EPI_STORE>(s, bf, A, W, M, N, K, E);
-    case EPI_GELU: return gemm_mode<EPI_GELU>(s, bf, A, W, M, N, K, E);
-    case EPI_GATE_RESID: return gemm_mode<EPI_GATE_RESID>(s, bf, A, W, M, N, K, E);
-    case EPI_RESID: return gemm_mode<EPI_RESID>(s, bf, A, W, M, N, K, E);
-    case EPI_PATCH: return gemm_mode<EPI_PATCH>(s, bf, A, W, M, N, K, E);
-    case EPI_QKV: return gemm_mode<EPI_QKV>(s, bf, A, W, M, N, K, E);
-    case EPI_HEAD: return gemm_mode<EPI_HEAD>(s, bf, A, W, M, N, K, E);
-    case EPI_CTXKV: return gemm_mode<EPI_CTXKV>(s, bf, A, W, M, N, K, E);
-    case EPI_F32: return gemm_mode<EPI_F32>(s, bf, A, W, M, N, K, E);
+    case EPI_STORE: return gemm_f32_mode<EPI_STORE>(s, A, W, M, N, K, E);
+    case EPI_GELU: return gemm_f32_mode<EPI_GELU>(s, A, W, M, N, K, E);
+    case EPI_GATE_RESID: return gemm_f32_mode<EPI_GATE_RESID>(s, A, W, M, N, K, E);
+    case EPI_RESID: return gemm_f32_mode<EPI_RESID>(s, A, W, M, N, K, E);
+    case EPI_PATCH: return gemm_f32_mode<EPI_PATCH>(s, A, W, M, N, K, E);
+    case EPI_QKV: return gemm_f32_mode<EPI_QKV>(s, A, W, M, N, K, E);
+    case EPI_HEAD: return gemm_f32_mode<EPI_HEAD>(s, A, W, M, N, K, E);
+    case EPI_CTXKV: return gemm_f32_mode<EPI_CTXKV>(s, A, W, M, N, K, E);
+    case EPI_F32: return gemm_f32_mode<EPI_F32>(s, A, W, M, N, K, E);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,0 +1,363 @@
+// bf16 GEMM on the matrix cores: C[m][n] = sum_k A[m][k] W[n][k], both
+// operands K-contiguous, fp32 accumulation, fused DiT epilogues.
+//
+// Tiles of BM x BN (256x256, 256x128 or 128x128) per workgroup of 4 waves
+// (2 x 2); each wave owns a (BM/2) x (BN/2) block of v_mfma_f32_32x32x16_bf16
+// tiles.  BK = 64; A and W tiles are staged in LDS (rows padded by 16 bytes),
+// two stages, with the next k-tile prefetched into registers while the
+// current one is multiplied.
+//
+// Epilogue: the accumulators leave through LDS in strips of 64 rows, so every
+// global store is a 16-byte vector: row-major outputs, the per-head Q/K
+// layouts (8 consecutive head-dim elements of one token, RoPE applied to the
+// pairs in registers) and the transposed V layout (8 consecutive tokens of one
+// head-dim element).
+#include <cmath>
+
+#include "kernels.h"
+
+namespace sdk {
+
+// Launch-bound-checked helpers shared with the epilogue.
+SD_DEV float gelu_f(float v) { return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f)); }
+
+SD_DEV void load8_bf16(const bf16* p, float* o) {
+  const bf16x8 v = *(const bf16x8*)p;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = (float)v[i];
+}
+
+SD_DEV void store8_bf16(bf16* p, const float* v) {
+  bf16x8 o;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = (bf16)v[i];
+  *(bf16x8*)p = o;
+}
+
+// RoPE angle (cos, sin) for head-dim element e (even) of token t of a row
+// whose temporal base is t0.
+SD_DEV float2 rope_cs(const Epi& E, int t0, int t, int e) {
+  const int hw = E.Hp * E.Wp;
+  const int f = t / hw, y = (t / E.Wp) % E.Hp, x = t % E.Wp;
+  if (e < E.dt) return E.rope_t[(t0 + f) * (E.dt >> 1) + (e >> 1)];
+  if (e < E.dt + E.dh) return E.rope_h[y * (E.dh >> 1) + ((e - E.dt) >> 1)];
+  return E.rope_w[x * ((E.hd - E.dt - E.dh) >> 1) + ((e - E.dt - E.dh) >> 1)];
+}
+
+// Epilogue of one 64-row strip held in LDS (fp32, row pitch LC).
+template <int BN, int MODE>
+SD_DEV void epi_strip(const Epi& E, const float* stg, int LC, int m_base, int n0, int M, int N, int tid,
+                      const int* t0s) {
+  constexpr int G = BN / 8;       // 8-column groups per row
+  if constexpr (MODE == EPI_HEAD) {
+    for (int idx = tid; idx < 64 * BN; idx += 256) {
+      const int row = idx / BN, col = idx % BN;
+      const int m = m_base + row, n = n0 + col;
+      if (m >= M || n >= N) continue;
+      const int r = m / E.L, t = m - r * E.L;
+      const int hw = E.Hp * E.Wp;
+      const int f = t / hw, y = (t / E.Wp) % E.Hp, x = t % E.Wp;
+      const int c = n % E.C, px = (n / E.C) % E.p, py = n / (E.C * E.p);
+      const int64_t lat = (int64_t)E.T * E.C * E.Hl * E.Wl;
+      E.eps[r * lat + (((int64_t)f * E.C + c) * E.Hl + y * E.p + py) * E.Wl + x * E.p + px] =
+          stg[row * LC + col] + (float)((const bf16*)E.bias)[n];
+    }
+    return;
+  }
+  if constexpr (MODE == EPI_QKV || MODE == EPI_CTXKV) {
+    // q and k sections: groups of 8 head-dim elements of one token
+    for (int g = tid; g < 64 * G; g += 256) {
+      const int row = g / G, cg = g % G;
+      const int m = m_base + row, n = n0 + cg * 8;
+      if (m >= M || n >= N) continue;
+      const int which = n / E.d;
+      const int sec = (MODE == EPI_CTXKV) ? which + 1 : which;     // 0 q, 1 k, 2 v
+      if (sec == 2) continue;
+      const int nn = n - which * E.d, h = nn / E.hd, e0 = nn - h * E.hd;
+      const int r = m / E.L, t = m - r * E.L;
+      float v[8], b[8];
+      const float4* sp = (const float4*)(stg + row * LC + cg * 8);
+      const float4 v0 = sp[0], v1 = sp[1];
+      v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w; v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+      load8_bf16((const bf16*)E.bias + n, b);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] += b[i];
+      if (E.rope) {
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+          const float2 cs = rope_cs(E, t0s[r], t, e0 + i);
+          const float x0 = v[i], x1 = v[i + 1];
+          v[i] = x0 * cs.x - x1 * cs.y;
+          v[i + 1] = x0 * cs.y + x1 * cs.x;
+        }
+      }
+      const int64_t rh = (int64_t)r * E.H + h;
+      if (sec == 0)
+        store8_bf16((bf16*)E.q + (rh * E.L + t) * E.hd + e0, v);
+      else
+        store8_bf16((bf16*)E.k + (rh * E.kstride + t) * E.hd + e0, v);
+    }
+    // v section: groups of 8 tokens of one head-dim element (transposed store)
+    for (int g = tid; g < 8 * BN; g += 256) {
+      const int col = g % BN, rg = g / BN;
+      const int m = m_base + rg * 8, n = n0 + col;
+      if (m >= M || n >= N) continue;
+      const int which = n / E.d;
+      const int sec = (MODE == EPI_CTXKV) ? which + 1 : which;
+      if (sec != 2) continue;
+      const int nn = n - which * E.d, h = nn / E.hd, e = nn - h * E.hd;
+      const float bn = (float)((const bf16*)E.bias)[n];
+      const int r = m / E.L, t = m - r * E.L;
+      const int64_t rh = (int64_t)r * E.H + h;
+      bf16* dst = (bf16*)E.vt + (rh * E.hd + e) * E.kstride + t;
+      if (m + 8 <= M && t + 8 <= E.L) {
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = stg[(rg * 8 + i) * LC + col] + bn;
+        store8_bf16(dst, v);
+      } else {
+        for (int i = 0; i < 8 && m + i < M; ++i) {
+          const int mi = m + i, ri = mi / E.L, ti = mi - ri * E.L;
+          bf16* di = (bf16*)E.vt + (((int64_t)ri * E.H + h) * E.hd + e) * E.kstride + ti;
+          *di = (bf16)(stg[(rg * 8 + i) * LC + col] + bn);
+        }
+      }
+    }
+    return;
+  }
+  // row-major modes: groups of 8 consecutive columns of one row
+  for (int g = tid; g < 64 * G; g += 256) {
+    const int row = g / G, cg = g % G;
+    const int m = m_base + row, n = n0 + cg * 8;
+    if (m >= M || n >= N) continue;
+    if (n + 8 > N || (E.ldo & 7) || (N & 7)) {
+      // ragged right edge or unaligned rows: element by element
+      for (int i = 0; i < 8 && n + i < N; ++i) {
+        float v = stg[row * LC + cg * 8 + i] + (E.bias ? (float)((const bf16*)E.bias)[n + i] : 0.f);
+        if constexpr (MODE == EPI_STORE) {
+          ((bf16*)E.out)[(int64_t)m * E.ldo + n + i] = (bf16)v;
+        } else if constexpr (MODE == EPI_GELU) {
+          ((bf16*)E.out)[(int64_t)m * E.ldo + n + i] = (bf16)gelu_f(v);
+        } else if constexpr (MODE == EPI_F32) {
+          ((float*)E.out)[(int64_t)m * E.ldo + n + i] = v;
+        } else if constexpr (MODE == EPI_PATCH) {
+          E.resid[(int64_t)m * N + n + i] = v;
+        } else if constexpr (MODE == EPI_RESID || MODE == EPI_GATE_RESID) {
+          if constexpr (MODE == EPI_GATE_RESID)
+            v *= E.mod[(int64_t)(m / E.L) * E.six_d + E.gate_off + n + i] +
+                 (float)((const bf16*)E.blk)[E.gate_off + n + i];
+          E.resid[(int64_t)m * N + n + i] += v;
+        }
+      }
+      continue;
+    }
+    float v[8], b[8];
+    const float4* sp = (const float4*)(stg + row * LC + cg * 8);
+    const float4 v0 = sp[0], v1 = sp[1];
+    v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w; v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+    if (E.bias) {
+      load8_bf16((const bf16*)E.bias + n, b);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] += b[i];
+    }
+    if constexpr (MODE == EPI_STORE) {
+      store8_bf16((bf16*)E.out + (int64_t)m * E.ldo + n, v);
+    } else if constexpr (MODE == EPI_GELU) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = gelu_f(v[i]);
+      store8_bf16((bf16*)E.out + (int64_t)m * E.ldo + n, v);
+    } else if constexpr (MODE == EPI_F32) {
+      float4* o = (float4*)((float*)E.out + (int64_t)m * E.ldo + n);
+      o[0] = make_float4(v[0], v[1], v[2], v[3]);
+      o[1] = make_float4(v[4], v[5], v[6], v[7]);
+    } else if constexpr (MODE == EPI_PATCH) {
+      float4* o = (float4*)(E.resid + (int64_t)m * N + n);
+      o[0] = make_float4(v[0], v[1], v[2], v[3]);
+      o[1] = make_float4(v[4], v[5], v[6], v[7]);
+    } else if constexpr (MODE == EPI_RESID || MODE == EPI_GATE_RESID) {
+      if constexpr (MODE == EPI_GATE_RESID) {
+        const int r = m / E.L;
+        const float4* gm = (const float4*)(E.mod + (int64_t)r * E.six_d + E.gate_off + n);
+        const float4 g0 = gm[0], g1 = gm[1];
+        float gb[8];
+        load8_bf16((const bf16*)E.blk + E.gate_off + n, gb);
+        v[0] *= g0.x + gb[0]; v[1] *= g0.y + gb[1]; v[2] *= g0.z + gb[2]; v[3] *= g0.w + gb[3];
+        v[4] *= g1.x + gb[4]; v[5] *= g1.y + gb[5]; v[6] *= g1.z + gb[6]; v[7] *= g1.w + gb[7];
+      }
+      float4* o = (float4*)(E.resid + (int64_t)m * N + n);
+      float4 r0 = o[0], r1 = o[1];
+      r0.x += v[0]; r0.y += v[1]; r0.z += v[2]; r0.w += v[3];
+      r1.x += v[4]; r1.y += v[5]; r1.z += v[6]; r1.w += v[7];
+      o[0] = r0;
+      o[1] = r1;
+    }
+  }
+}
+
+template <int BM, int BN, int MODE>
+__global__ __launch_bounds__(256) void gemm_mfma_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
+                                                        int M, int N, int K, Epi E) {
+  constexpr int BK = 64, PAD = 8, LDK = BK + PAD;
+  constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 32, FN = TN / 32;
+  constexpr int CA = BM * (BK / 8) / 256, CB = BN * (BK / 8) / 256;
+  constexpr int STAGE = (BM + BN) * LDK;                 // bf16 elements per LDS stage
+  constexpr int LC = BN + 4;                             // fp32 pitch of the epilogue strip
+  static_assert(64 * LC * 4 <= 2 * STAGE * 2, "epilogue strip must fit in the stage buffers");
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * STAGE];
+  __shared__ int t0s[SD_MAX_ROWS];     // per-row temporal RoPE base (read with a dynamic row index)
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  // XCD-contiguous logical ids; groups of GM tile-rows walked column by column
+  constexpr int GM = 4;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int grp = lid / (GM * tiles_n), first_m = grp * GM;
+  const int gm = min(tiles_m - first_m, GM);
+  const int within = lid - grp * GM * tiles_n;
+  const int tm = first_m + within % gm, tn = within / gm;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  bf16x8 ra[CA], rb[CB];
+  const bf16x8 zero8 = {};
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < CA; ++i) {
+      const int c = tid + i * 256, row = c >> 3, kc = (c & 7) * 8;
+      const int gm_ = m0 + row, gk = k0 + kc;
+      ra[i] = (gm_ < M && gk < K) ? *(const bf16x8*)(A + (int64_t)gm_ * K + gk) : zero8;
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      const int c = tid + i * 256, row = c >> 3, kc = (c & 7) * 8;
+      const int gn = n0 + row, gk = k0 + kc;
+      rb[i] = (gn < N && gk < K) ? *(const bf16x8*)(W + (int64_t)gn * K + gk) : zero8;
+    }
+  };
+  auto sstore = [&](int buf) {
+    bf16* as = smem + buf * STAGE;
+    bf16* bs = as + BM * LDK;
+#pragma unroll
+    for (int i = 0; i < CA; ++i) {
+      const int c = tid + i * 256, row = c >> 3, kc = (c & 7) * 8;
+      *(bf16x8*)(as + row * LDK + kc) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      const int c = tid + i * 256, row = c >> 3, kc = (c & 7) * 8;
+      *(bf16x8*)(bs + row * LDK + kc) = rb[i];
+    }
+  };
+
+  if constexpr (MODE == EPI_QKV) {
+    if (tid == 0) {
+#pragma unroll
+      for (int i = 0; i < SD_MAX_ROWS; ++i) t0s[i] = E.t0[i];
+    }
+  }
+  const int KT = (K + BK - 1) / BK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  const int lr = lane & 31, lk = (lane >> 5) * 8;
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < KT) gload((kt + 1) * BK);
+    const bf16* as = smem + buf * STAGE + (wm * TM + lr) * LDK + lk;
+    const bf16* bs = smem + buf * STAGE + BM * LDK + (wn * TN + lr) * LDK + lk;
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 16) {
+      bf16x8 fa[FM], fb[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) fa[i] = *(const bf16x8*)(as + i * 32 * LDK + kk);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) fb[j] = *(const bf16x8*)(bs + j * 32 * LDK + kk);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < KT) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue through LDS, 64 rows at a time.  C layout of a 32x32 tile: lane
+  // holds column lane%32, rows 8*(q/4) + 4*(lane/32) + q%4.
+  float* stg = (float*)smem;
+  constexpr int SPW = TM / 64;          // strips per wave-row
+#pragma unroll
+  for (int s = 0; s < BM / 64; ++s) {
+    if (wm == s / SPW) {
+      const int i0 = (s % SPW) * 2;
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int row = ii * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+            const int col = wn * TN + j * 32 + (lane & 31);
+            stg[row * LC + col] = acc[i0 + ii][j][q];
+          }
+    }
+    __syncthreads();
+    epi_strip<BN, MODE>(E, stg, LC, m0 + s * 64, n0, M, N, tid, t0s);
+    __syncthreads();
+  }
+}
+
+template <int MODE>
+hipError_t gemm_mfma_mode(hipStream_t s, const bf16* A, const bf16* W, int M, int N, int K, const Epi& E) {
+  // pick the largest tile that still gives most CUs work: estimated time
+  // ~ rounds of 256 workgroups x per-tile cost (larger tiles cost less per flop)
+  struct Opt { int bm, bn; double eff; };
+  const Opt opts[3] = {{256, 256, 1.0}, {256, 128, 0.85}, {128, 128, 0.7}};
+  int best = 0;
+  double best_t = 1e30;
+  for (int i = 0; i < 3; ++i) {
+    const int64_t tiles = (int64_t)((M + opts[i].bm - 1) / opts[i].bm) * ((N + opts[i].bn - 1) / opts[i].bn);
+    const int64_t rounds = (tiles + 255) / 256;
+    const double t = (double)rounds * opts[i].bm * opts[i].bn / opts[i].eff;
+    if (t < best_t * 0.999) {
+      best_t = t;
+      best = i;
+    }
+  }
+  const int bm = opts[best].bm, bn = opts[best].bn;
+  const unsigned grid = (unsigned)(((M + bm - 1) / bm) * ((N + bn - 1) / bn));
+  if (best == 0)
+    gemm_mfma_kernel<256, 256, MODE><<<grid, 256, 0, s>>>(A, W, M, N, K, E);
+  else if (best == 1)
+    gemm_mfma_kernel<256, 128, MODE><<<grid, 256, 0, s>>>(A, W, M, N, K, E);
+  else
+    gemm_mfma_kernel<128, 128, MODE><<<grid, 256, 0, s>>>(A, W, M, N, K, E);
+  return hipGetLastError();
+}
+
+hipError_t gemm_mfma(hipStream_t s, const void* A, const void* W, int M, int N, int K, const Epi& E) {
+  const bf16* a = (const bf16*)A;
+  const bf16* w = (const bf16*)W;
+  switch (E.mode) {
+    case EPI_STORE: return gemm_mfma_mode<EPI_STORE>(s, a, w, M, N, K, E);
+    case EPI_GELU: return gemm_mfma_mode<EPI_GELU>(s, a, w, M, N, K, E);
+    case EPI_GATE_RESID: return gemm_mfma_mode<EPI_GATE_RESID>(s, a, w, M, N, K, E);
+    case EPI_RESID: return gemm_mfma_mode<EPI_RESID>(s, a, w, M, N, K, E);
+    case EPI_PATCH: return gemm_mfma_mode<EPI_PATCH>(s, a, w, M, N, K, E);
+    case EPI_QKV: return gemm_mfma_mode<EPI_QKV>(s, a, w, M, N, K, E);
+    case EPI_HEAD: return gemm_mfma_mode<EPI_HEAD>(s, a, w, M, N, K, E);
+    case EPI_CTXKV: return gemm_mfma_mode<EPI_CTXKV>(s, a, w, M, N, K, E);
+    case EPI_F32: return gemm_mfma_mode<EPI_F32>(s, a, w, M, N, K, E);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace sdk

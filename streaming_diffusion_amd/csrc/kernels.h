@@ -50,6 +50,8 @@ hipError_t sink_score(hipStream_t s, const float* x, float* partial, int L, int 
 // C = A[M][K] * W[N][K]^T with epilogue E; element type by bf (bf16 on MFMA,
 // fp32 on the vector ALUs).
 hipError_t gemm(hipStream_t s, bool bf, const void* A, const void* W, int M, int N, int K, const Epi& E);
+// bf16 matrix-core path of gemm() (K a multiple of 8).
+hipError_t gemm_mfma(hipStream_t s, const void* A, const void* W, int M, int N, int K, const Epi& E);
 
 // ---------------------------------------------------------------- attention
 struct KvSeg {
