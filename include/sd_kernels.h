@@ -40,10 +40,15 @@ typedef struct {
 /* O = softmax(Q K^T / sqrt(hd)) V over the concatenation of up to three
  * segments (sink, window, own chunk), per query row r < R and head h < H.
  * q(r,h,t) = q + r*q_row_stride + h*q_head_stride + t*hd; o is token-major
- * [R*L][H*hd].  StreamDiffusionV2 summary: sink-token guided rolling KV cache. */
+ * [R*L][H*hd].  StreamDiffusionV2 summary: sink-token guided rolling KV cache.
+ * nsplit > 1 (bf16 only) splits every query tile's key sequence over nsplit
+ * workgroups whose partial results are combined in a second pass; it needs
+ * sd_k_attention_workspace_bytes() bytes of device workspace (256-byte
+ * aligned), otherwise workspace may be NULL. */
 sd_status sd_k_attention(int32_t dtype, const void* q, int64_t q_row_stride, int64_t q_head_stride, void* o,
                          int32_t R, int32_t H, int32_t L, int32_t hd, int32_t nseg, const sd_kv_segment* segs,
-                         void* stream);
+                         int32_t nsplit, void* workspace, size_t workspace_bytes, void* stream);
+size_t sd_k_attention_workspace_bytes(int32_t R, int32_t H, int32_t L, int32_t hd, int32_t nsplit);
 
 /* Exact int64 sums (sum a*b, sum a*a, sum b*b) of two frames: kind SD_SSF_U8
  * (uint8) or SD_SSF_LATENT (fp32 quantised to rint(x*2^12) clamped to +-2^20).

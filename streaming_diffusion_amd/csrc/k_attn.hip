@@ -58,7 +58,9 @@ SD_DEV int key_pos(const KvSeg& g, int u) {
 }
 
 // ---------------------------------------------------------------------------
-template <int HD>
+// ONESEG = 1 instantiates the same code for single-segment calls (the
+// prompt cross-attention), so that profiles tell the two uses apart.
+template <int HD, int ONESEG>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   constexpr int BQ = 128, KB = 64, PK = 8, PV = 8;
   constexpr int LK = HD + PK, LV = KB + PV;
@@ -70,11 +72,14 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   // (row, head) share its keys, so they are kept on one XCD
   const int nqt = (a.L + BQ - 1) / BQ;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int qt = lid % nqt, h = (lid / nqt) % a.H, r = a.r0 + lid / (nqt * a.H);
+  const int sp = lid % a.nsplit, unit = lid / a.nsplit;
+  const int qt = unit % nqt, h = (unit / nqt) % a.H, r = a.r0 + unit / (nqt * a.H);
   const int q0 = qt * BQ;
   const SegRt sr = seg_layout(a);
   const int NK = sr.end[2];
-  const int NT = (NK + KB - 1) / KB;
+  const int NT_all = (NK + KB - 1) / KB;
+  const int tps = (NT_all + a.nsplit - 1) / a.nsplit;
+  const int T0 = min(NT_all, sp * tps), NT = min(NT_all, T0 + tps);   // this split's key tiles [T0, NT)
 
   // Q fragments (B operand): lane -> query q0 + wave*32 + lane%32, hd block
   // kk*16 + 8*(lane/32).
@@ -184,13 +189,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   const int rho = lane & 31;
   const int krow = (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1);
 
-  if (NT > 0) {
-    gload(0);
+  if (T0 < NT) {
+    gload(T0);
     sstore(0);
   }
   __syncthreads();
-  for (int tile = 0; tile < NT; ++tile) {
-    const int buf = tile & 1;
+  for (int tile = T0; tile < NT; ++tile) {
+    const int buf = (tile - T0) & 1;
     if (tile + 1 < NT) gload(tile + 1);
     // S^T for two 32-key halves of the tile
     f32x16 s[2];
@@ -264,8 +269,23 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     __syncthreads();
   }
 
-  // normalise and write O (token-major) through LDS: Os[query][hd]
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (a.nsplit > 1) {
+    // partial result of this key range: unnormalised O and (max, sum)
+    const int tq = q0 + wave * 32 + (lane & 31);
+    if (tq < a.L) {
+      float* po = a.part_o + sp * a.part_so + ((int64_t)r * a.L + tq) * a.d + (int64_t)h * HD;
+#pragma unroll
+      for (int t = 0; t < HD / 32; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *(float4*)(po + t * 32 + 8 * g + 4 * half) =
+              make_float4(o[t][4 * g], o[t][4 * g + 1], o[t][4 * g + 2], o[t][4 * g + 3]);
+      if (half == 0) a.part_ml[sp * a.part_sml + ((int64_t)r * a.H + h) * a.L + tq] = make_float2(m_run, l_tot);
+    }
+    return;
+  }
+  // normalise and write O (token-major) through LDS: Os[query][hd]
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   bf16* Os = &Ks[0][0];                // BQ x (HD + PK) fits in one K stage
   constexpr int LO = HD + PK;
@@ -364,15 +384,87 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   }
 }
 
-hipError_t attention(hipStream_t s, bool bf, const AttnArgs& a) {
-  if (a.R == 0 || a.L == 0) return hipSuccess;
+// ---------------------------------------------------------------------------
+// Combine of split-KV partials: O = sum_s w_s O_s / sum_s w_s l_s with
+// w_s = 2^((m_s - max_s m_s) * scale * log2 e).  One thread per 4 head-dim
+// elements of one (token, head).
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int hd4 = a.hd / 4;
+  const int64_t per_tok = (int64_t)a.H * hd4;
+  if (i >= (int64_t)a.R * a.L * per_tok) return;
+  const int64_t tok = i / per_tok;                // r_rel * L + t
+  const int h = (int)((i % per_tok) / hd4), e = (int)(i % hd4) * 4;
+  const int rr = (int)(tok / a.L), t = (int)(tok % a.L);
+  const int r = a.r0 + rr;
+  const float sl2 = a.scale * 1.4426950408889634f;
+  float mmax = -INFINITY;
+  for (int sp = 0; sp < a.nsplit; ++sp)
+    mmax = fmaxf(mmax, a.part_ml[sp * a.part_sml + ((int64_t)r * a.H + h) * a.L + t].x);
+  float l = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int sp = 0; sp < a.nsplit; ++sp) {
+    const float2 ml = a.part_ml[sp * a.part_sml + ((int64_t)r * a.H + h) * a.L + t];
+    if (ml.x == -INFINITY) continue;
+    const float w = exp2f((ml.x - mmax) * sl2);
+    l += w * ml.y;
+    const float4 v = *(const float4*)(a.part_o + sp * a.part_so + ((int64_t)r * a.L + t) * a.d + (int64_t)h * a.hd + e);
+    acc.x += w * v.x;
+    acc.y += w * v.y;
+    acc.z += w * v.z;
+    acc.w += w * v.w;
+  }
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  bf16x4 ov;
+  ov[0] = (bf16)(acc.x * inv);
+  ov[1] = (bf16)(acc.y * inv);
+  ov[2] = (bf16)(acc.z * inv);
+  ov[3] = (bf16)(acc.w * inv);
+  *(bf16x4*)((bf16*)a.o + ((int64_t)r * a.L + t) * a.d + (int64_t)h * a.hd + e) = ov;
+}
+
+int attention_pick_split(int units, int tiles, int max_split, int concurrent) {
+  int best = 1;
+  double best_cost = (double)((units + concurrent - 1) / concurrent);
+  for (int sp = 2; sp <= max_split; ++sp) {
+    if (tiles / sp < 4) break;
+    const double rounds = (double)(((int64_t)units * sp + concurrent - 1) / concurrent);
+    const double cost = rounds / sp * 1.04;     // 4% for the partial traffic and the combine pass
+    if (cost < best_cost * 0.98) {
+      best_cost = cost;
+      best = sp;
+    }
+  }
+  return best;
+}
+
+hipError_t attention(hipStream_t s, bool bf, const AttnArgs& args) {
+  if (args.R == 0 || args.L == 0) return hipSuccess;
+  AttnArgs a = args;
+  if (a.nsplit < 1 || !bf) a.nsplit = 1;
   if (bf) {
-    const dim3 g(((a.L + 127) / 128) * a.H * a.R);
+    const int nsplit = a.nsplit;
+    const dim3 g(((a.L + 127) / 128) * a.H * a.R * nsplit);
     switch (a.hd) {
-      case 32: attn_bf16_kernel<32><<<g, 256, 0, s>>>(a); break;
-      case 64: attn_bf16_kernel<64><<<g, 256, 0, s>>>(a); break;
-      case 128: attn_bf16_kernel<128><<<g, 256, 0, s>>>(a); break;
+      case 32:
+        if (a.nseg == 1) attn_bf16_kernel<32, 1><<<g, 256, 0, s>>>(a);
+        else attn_bf16_kernel<32, 0><<<g, 256, 0, s>>>(a);
+        break;
+      case 64:
+        if (a.nseg == 1) attn_bf16_kernel<64, 1><<<g, 256, 0, s>>>(a);
+        else attn_bf16_kernel<64, 0><<<g, 256, 0, s>>>(a);
+        break;
+      case 128:
+        if (a.nseg == 1) attn_bf16_kernel<128, 1><<<g, 256, 0, s>>>(a);
+        else attn_bf16_kernel<128, 0><<<g, 256, 0, s>>>(a);
+        break;
       default: return hipErrorInvalidValue;
+    }
+    if (nsplit > 1) {
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const int64_t n = (int64_t)a.R * a.L * a.H * (a.hd / 4);
+      attn_combine_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a);
     }
   } else {
     dim3 g((a.L + 63) / 64, a.H, a.R);

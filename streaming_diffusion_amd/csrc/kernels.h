@@ -72,7 +72,19 @@ struct AttnArgs {
   int nseg;
   KvSeg seg[3];
   float scale;            // 1/sqrt(hd)
+  // split over the key sequence (bf16 path): nsplit workgroups share one
+  // query tile, each writes unnormalised O (fp32) and its (max, sum) to
+  // part_o [nsplit][rows*L][d] / part_ml [nsplit][rows][H][L] (row index
+  // absolute, strides part_so / part_sml elements), then a combine pass
+  // normalises.  nsplit = 1 writes O directly.
+  int nsplit;
+  float* part_o;
+  float2* part_ml;
+  long long part_so, part_sml;
 };
 hipError_t attention(hipStream_t s, bool bf, const AttnArgs& a);
+// Split count that best fills `concurrent` resident workgroups for `units`
+// query tiles over `tiles` key tiles (1 .. max_split).
+int attention_pick_split(int units, int tiles, int max_split, int concurrent);
 
 }  // namespace sdk

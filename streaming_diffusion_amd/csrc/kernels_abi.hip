@@ -23,9 +23,24 @@ sd_status sd_k_gemm(int32_t dtype, const void* A, const void* W, const void* bia
                                                                                              : SD_ERR_HIP;
 }
 
+static size_t part_o_bytes(int32_t R, int32_t H, int32_t L, int32_t hd, int32_t nsplit) {
+  return (((size_t)nsplit * R * L * H * hd * 4) + 255) & ~(size_t)255;
+}
+
+size_t sd_k_attention_workspace_bytes(int32_t R, int32_t H, int32_t L, int32_t hd, int32_t nsplit) {
+  if (R < 1 || H < 1 || L < 1 || hd < 1 || nsplit < 1) return 0;
+  if (nsplit == 1) return 0;
+  return part_o_bytes(R, H, L, hd, nsplit) + (size_t)nsplit * R * H * L * 8;
+}
+
 sd_status sd_k_attention(int32_t dtype, const void* q, int64_t q_row_stride, int64_t q_head_stride, void* o,
                          int32_t R, int32_t H, int32_t L, int32_t hd, int32_t nseg, const sd_kv_segment* segs,
-                         void* stream) {
+                         int32_t nsplit, void* workspace, size_t workspace_bytes, void* stream) {
+  if (nsplit < 1 || nsplit > 64) return SD_ERR_ARG;
+  if (nsplit > 1) {
+    if (dtype != SD_DTYPE_BF16 || !workspace || ((uintptr_t)workspace & 255)) return SD_ERR_ARG;
+    if (workspace_bytes < sd_k_attention_workspace_bytes(R, H, L, hd, nsplit)) return SD_ERR_WORKSPACE;
+  }
   if (dtype != SD_DTYPE_F32 && dtype != SD_DTYPE_BF16) return SD_ERR_ARG;
   if (!q || !o || !segs || nseg < 1 || nseg > 3 || R < 0 || H < 1 || L < 0) return SD_ERR_ARG;
   const bool bf = dtype == SD_DTYPE_BF16;
@@ -64,6 +79,13 @@ sd_status sd_k_attention(int32_t dtype, const void* q, int64_t q_row_stride, int
     s.start = g.start;
     s.count = g.count;
     s.wrap = g.wrap;
+  }
+  a.nsplit = nsplit;
+  if (nsplit > 1) {
+    a.part_o = (float*)workspace;
+    a.part_ml = (float2*)((char*)workspace + part_o_bytes(R, H, L, hd, nsplit));
+    a.part_so = (long long)R * L * H * hd;
+    a.part_sml = (long long)R * H * L;
   }
   return sdk::attention((hipStream_t)stream, bf, a) == hipSuccess ? SD_OK : SD_ERR_HIP;
 }

@@ -55,6 +55,11 @@ struct sd_stream {
   float *sink_emb = nullptr, *sink_part = nullptr, *sink_sim = nullptr;
   int* sink_flag = nullptr;
   float2 *rope_t = nullptr, *rope_h = nullptr, *rope_w = nullptr;
+  // split-KV partials of the self-attention
+  int attn_split_max = 1;
+  float* part_o = nullptr;
+  float2* part_ml = nullptr;
+  int concurrent_wg = 512;      // resident attention workgroups (2 per CU)
   size_t ws_used = 0;
   // host state
   std::vector<FrameRec> frames;
@@ -166,6 +171,15 @@ size_t carve(sd_stream* s, char* base) {
   s->rope_t = cv.take<float2>((size_t)s->rope_pos * std::max(1, s->dt / 2) * sizeof(float2));
   s->rope_h = cv.take<float2>((size_t)s->Hp * std::max(1, s->dh / 2) * sizeof(float2));
   s->rope_w = cv.take<float2>((size_t)s->Wp * std::max(1, s->dw / 2) * sizeof(float2));
+  if (s->bf) {
+    // split-KV partials, at most 8 splits and 1 GiB
+    const size_t per = (size_t)M * s->d * 4 + (size_t)M * s->H * sizeof(float2);
+    s->attn_split_max = (int)std::max<size_t>(1, std::min<size_t>(8, ((size_t)1 << 30) / per));
+    if (s->attn_split_max > 1) {
+      s->part_o = cv.take<float>((size_t)s->attn_split_max * M * s->d * 4);
+      s->part_ml = cv.take<float2>((size_t)s->attn_split_max * M * s->H * sizeof(float2));
+    }
+  }
   return cv.off;
 }
 
@@ -307,6 +321,12 @@ sd_status sd_stream_create(const sd_stream_config* cfg, const sd_weights* w, voi
   for (int i = 0; i < SD_MAX_SLOTS; ++i) s->slots[i] = -1;
   s->ctl.s = s->cfg.s_max;
   std::memset(s->prof_acc, 0, sizeof(s->prof_acc));
+  {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+      s->concurrent_wg = 2 * cus;
+  }
   // zero the caches (padding keys must stay finite) and upload RoPE tables
   std::vector<float2> rt, rh, rw;
   rope_tables(s, rt, rh, rw);
@@ -564,6 +584,15 @@ sd_status sd_stream_step(sd_stream* s, float* out_latent, sd_step_info* info) {
       so.cap = L;
       so.count = L;
       A.nseg = ns;
+      if (s->attn_split_max > 1) {
+        const int nk = ((sk.count + 7) & ~7) + sw.count + L;
+        A.nsplit = sdk::attention_pick_split(R * H * ((L + 127) / 128), (nk + 63) / 64, s->attn_split_max,
+                                             s->concurrent_wg);
+        A.part_o = s->part_o;
+        A.part_ml = s->part_ml;
+        A.part_so = (long long)s->Rmax * L * d;
+        A.part_sml = (long long)s->Rmax * H * L;
+      }
       const double shared = (double)sk.count + sw.count;
       PROF(SD_PROF_ATTN_SELF, 4.0 * R * L * (shared + L) * d,
            (double)es * d * (2.0 * R * L + 2.0 * shared + 2.0 * R * L), sdk::attention(st, bf, A));

@@ -108,8 +108,13 @@ def test_create_rejects_bad_arguments_before_any_device_call(lib):
     assert lib.sd_k_gemm(0, None, None, None, None, 1, 1, 8, None) == L.SD_ERR_ARG
     assert lib.sd_k_gemm(1, 8, 8, None, 8, 1, 1, 12, None) == L.SD_ERR_SHAPE
     seg = L.sd_kv_segment(k=8, vt=8, cap=64, start=0, count=100, wrap=0)
-    assert lib.sd_k_attention(1, 8, 0, 0, 8, 1, 1, 8, 64, 1, C.byref(seg), None) == L.SD_ERR_SHAPE
-    assert lib.sd_k_attention(1, 8, 0, 0, 8, 1, 1, 8, 48, 1, C.byref(seg), None) == L.SD_ERR_SHAPE
+    assert lib.sd_k_attention(1, 8, 0, 0, 8, 1, 1, 8, 64, 1, C.byref(seg), 1, None, 0, None) == L.SD_ERR_SHAPE
+    assert lib.sd_k_attention(1, 8, 0, 0, 8, 1, 1, 8, 48, 1, C.byref(seg), 1, None, 0, None) == L.SD_ERR_SHAPE
+    assert lib.sd_k_attention(1, 8, 0, 0, 8, 1, 1, 8, 64, 1, C.byref(seg), 2, None, 0, None) == L.SD_ERR_ARG
+    assert lib.sd_k_attention(1, 8, 0, 0, 8, 1, 1, 8, 64, 1, C.byref(seg), 2, 256, 16, None) == L.SD_ERR_WORKSPACE
+    assert lib.sd_k_attention_workspace_bytes(2, 3, 40, 64, 1) == 0
+    assert lib.sd_k_attention_workspace_bytes(2, 3, 40, 64, 3) == ((3 * 2 * 40 * 3 * 64 * 4 + 255) // 256 * 256
+                                                                  + 3 * 2 * 3 * 40 * 8)
 
 
 # ------------------------------------------------------------------ host state vs oracle, bit for bit

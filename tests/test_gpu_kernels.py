@@ -97,15 +97,18 @@ def make_segments(rng, H, hd, R, L, sink_count, sink_cap, W, ring_start, ring_co
     return dev, segs, keys, vals
 
 
-@pytest.mark.parametrize("dtype,hd,L,sink_count,W,ring_start,ring_count", [
-    ("bf16", 64, 72, 4, 64, 40, 48),        # ring wraps, sink padding, ragged queries
-    ("bf16", 128, 200, 12, 160, 152, 160),   # full ring starting at 152 (wraps)
-    ("bf16", 32, 64, 0, 64, 0, 0),           # empty sink and ring (plain self-attention)
-    ("bf16", 128, 136, 8, 256, 0, 256),
-    ("f32", 32, 64, 4, 64, 40, 48),
-    ("f32", 16, 40, 3, 24, 16, 20),
+@pytest.mark.parametrize("dtype,hd,L,sink_count,W,ring_start,ring_count,nsplit", [
+    ("bf16", 64, 72, 4, 64, 40, 48, 1),        # ring wraps, sink padding, ragged queries
+    ("bf16", 128, 200, 12, 160, 152, 160, 1),  # full ring starting at 152 (wraps)
+    ("bf16", 32, 64, 0, 64, 0, 0, 1),          # empty sink and ring (plain self-attention)
+    ("bf16", 128, 136, 8, 256, 0, 256, 1),
+    ("bf16", 64, 72, 4, 64, 40, 48, 2),        # split over the keys, partial combine
+    ("bf16", 128, 200, 12, 512, 136, 504, 3),
+    ("bf16", 128, 136, 8, 256, 0, 256, 5),     # more splits than some key ranges fill
+    ("f32", 32, 64, 4, 64, 40, 48, 1),
+    ("f32", 16, 40, 3, 24, 16, 20, 1),
 ])
-def test_attention_segments_match_oracle(lib, dtype, hd, L, sink_count, W, ring_start, ring_count):
+def test_attention_segments_match_oracle(lib, dtype, hd, L, sink_count, W, ring_start, ring_count, nsplit):
     print(f"attention {dtype} hd={hd} L={L} sink={sink_count} W={W} start={ring_start} count={ring_count}", flush=True)
     rng = np.random.default_rng(hd + L)
     H, R = 2, 2
@@ -117,8 +120,12 @@ def test_attention_segments_match_oracle(lib, dtype, hd, L, sink_count, W, ring_
         q = bf16_round(q)
     qd = to_dev(q, tdt)
     o = torch.empty((R * L, H * hd), dtype=tdt, device=device())
+    wsb = lib.sd_k_attention_workspace_bytes(R, H, L, hd, nsplit)
+    ws = torch.empty(max(wsb, 1) + 256, dtype=torch.uint8, device=device())
+    wsp = (ws.data_ptr() + 255) // 256 * 256 if wsb else None
+    print(f"  nsplit={nsplit} workspace={wsb}", flush=True)
     call(lib.sd_k_attention(1 if dtype == "bf16" else 0, qd.data_ptr(), H * L * hd, L * hd, o.data_ptr(), R, H, L,
-                            hd, 3, segs, stream_ptr()))
+                            hd, 3, segs, nsplit, wsp, wsb, stream_ptr()))
     torch.cuda.synchronize()
     got = o.float().cpu().numpy().reshape(R, L, H, hd)
     for r in range(R):
@@ -138,7 +145,11 @@ def test_attention_full_video_shape_sampled(lib):
     q = bf16_round(rng.standard_normal((R, H, L, hd)).astype(np.float32))
     qd = to_dev(q, torch.bfloat16)
     o = torch.empty((R * L, H * hd), dtype=torch.bfloat16, device=device())
-    call(lib.sd_k_attention(1, qd.data_ptr(), H * L * hd, L * hd, o.data_ptr(), R, H, L, hd, 3, segs, stream_ptr()))
+    nsplit = 5
+    wsb = lib.sd_k_attention_workspace_bytes(R, H, L, hd, nsplit)
+    ws = torch.empty(wsb + 256, dtype=torch.uint8, device=device())
+    call(lib.sd_k_attention(1, qd.data_ptr(), H * L * hd, L * hd, o.data_ptr(), R, H, L, hd, 3, segs, nsplit,
+                            (ws.data_ptr() + 255) // 256 * 256, wsb, stream_ptr()))
     torch.cuda.synchronize()
     got = o.float().cpu().numpy().reshape(R, L, H, hd)
     sample = np.concatenate([np.arange(0, 5), rng.integers(0, L, 40), np.arange(L - 5, L)])
