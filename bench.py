@@ -38,11 +38,35 @@ def parse():
     ap.add_argument("--n-slots", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-blocks", type=int, default=2, help="DiT blocks in the oracle sample")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="after the run, copy MIB MiB device-to-device once (reference dispatch for HBM counters)")
     return ap.parse_args()
 
 
 def slot_indices(n):
     return {1: (32,), 2: (32, 45), 3: (16, 32, 45), 4: (0, 16, 32, 45)}[n]
+
+
+PMC_FILE = os.path.join(ROOT, "profiles", "attn_self_video13b_pmc.json")
+ATTN_SOURCE = os.path.join(ROOT, "streaming_diffusion_amd", "csrc", "k_attn.hip")
+
+
+def measured_traffic():
+    """HBM bytes per self-attention launch from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE runs, each scaled by what the counter read for a
+    device copy of known size.  None when the kernel source changed since."""
+    import hashlib
+    try:
+        rec = json.load(open(PMC_FILE))
+        sha = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != sha:
+        return None
+    cal = rec["copy_calibration"]
+    f_scale = cal["bytes"] / (cal["fetch_kib"] * 1024.0)
+    w_scale = cal["bytes"] / (cal["write_kib"] * 1024.0)
+    return round(rec["fetch_kib_per_dispatch"] * 1024.0 * f_scale + rec["write_kib_per_dispatch"] * 1024.0 * w_scale)
 
 
 def cpu_baseline(cfg, n_blocks_sample: int):
@@ -155,16 +179,26 @@ def main():
     k += 1
     breakdown = run.profile_read()
     run.profile([])
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 18          # float32 elements in MIB MiB
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     roofline = None
     if attn and attn["launches"]:
         per_launch_ms = attn["ms"] / attn["launches"]
         per_launch_flop = attn["flops"] / attn["launches"]
         achieved = per_launch_flop / (per_launch_ms * 1e-3) / 1e12
-        roofline = {"kernel": "attn_bf16_kernel<128> (self-attention over sink + window + own)",
+        roofline = {"kernel": "attn_bf16_kernel<128, 0> (self-attention over sink + window + own)",
                     "bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                    "traffic": measured_traffic(),
                     "avg_launch_ms": round(per_launch_ms, 4), "flop_per_launch": per_launch_flop,
+                    "algorithmic_bytes_per_launch": attn["bytes"] / attn["launches"],
                     "launches": attn["launches"]}
     bd = {}
     for name, v in breakdown.items():

@@ -209,7 +209,7 @@ typedef enum {
   SD_PROF_ATTN_SELF = 0, SD_PROF_ATTN_CROSS = 1, SD_PROF_GEMM_QKV = 2, SD_PROF_GEMM_O = 3,
   SD_PROF_GEMM_FFN1 = 4, SD_PROF_GEMM_FFN2 = 5, SD_PROF_GEMM_CROSS = 6, SD_PROF_OTHER = 7,
   SD_PROF_LN = 8, SD_PROF_GEMV = 9, SD_PROF_KV = 10, SD_PROF_EPILOGUE = 11, SD_PROF_CONTROLS = 12,
-  SD_PROF_KINDS = 13
+  SD_PROF_ATTN_COMBINE = 13, SD_PROF_KINDS = 14
 } sd_prof_kind;
 typedef struct {
   int32_t kind;

@@ -75,7 +75,7 @@ class sd_kernel_stat(C.Structure):
 
 
 PROF_KINDS = ["attn_self", "attn_cross", "gemm_qkv", "gemm_o", "gemm_ffn1", "gemm_ffn2", "gemm_cross", "other",
-              "ln_mod", "gemv", "kv_cache", "epilogue", "controls"]
+              "ln_mod", "gemv", "kv_cache", "epilogue", "controls", "attn_combine"]
 
 
 class sd_kv_segment(C.Structure):

@@ -72,8 +72,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   // (row, head) share its keys, so they are kept on one XCD
   const int nqt = (a.L + BQ - 1) / BQ;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int sp = lid % a.nsplit, unit = lid / a.nsplit;
-  const int qt = unit % nqt, h = (unit / nqt) % a.H, r = a.r0 + unit / (nqt * a.H);
+  // order (row, head, split, q-tile): the workgroups resident on one XCD at
+  // a time are q-tiles of the same key range, which then streams through L2
+  const int qt = lid % nqt, sp = (lid / nqt) % a.nsplit;
+  const int h = (lid / (nqt * a.nsplit)) % a.H, r = a.r0 + lid / (nqt * a.nsplit * a.H);
   const int q0 = qt * BQ;
   const SegRt sr = seg_layout(a);
   const int NK = sr.end[2];
@@ -438,7 +440,14 @@ int attention_pick_split(int units, int tiles, int max_split, int concurrent) {
   return best;
 }
 
-hipError_t attention(hipStream_t s, bool bf, const AttnArgs& args) {
+hipError_t attention_combine(hipStream_t s, const AttnArgs& a) {
+  if (a.nsplit <= 1 || a.R == 0 || a.L == 0) return hipSuccess;
+  const int64_t n = (int64_t)a.R * a.L * a.H * (a.hd / 4);
+  attn_combine_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t attention(hipStream_t s, bool bf, const AttnArgs& args, bool combine) {
   if (args.R == 0 || args.L == 0) return hipSuccess;
   AttnArgs a = args;
   if (a.nsplit < 1 || !bf) a.nsplit = 1;
@@ -460,11 +469,10 @@ hipError_t attention(hipStream_t s, bool bf, const AttnArgs& args) {
         break;
       default: return hipErrorInvalidValue;
     }
-    if (nsplit > 1) {
+    if (nsplit > 1 && combine) {
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      const int64_t n = (int64_t)a.R * a.L * a.H * (a.hd / 4);
-      attn_combine_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a);
+      return attention_combine(s, a);
     }
   } else {
     dim3 g((a.L + 63) / 64, a.H, a.R);

@@ -82,7 +82,10 @@ struct AttnArgs {
   float2* part_ml;
   long long part_so, part_sml;
 };
-hipError_t attention(hipStream_t s, bool bf, const AttnArgs& a);
+// With combine = false a split launch leaves its partials for a separate
+// attention_combine() call (so the two passes can be timed apart).
+hipError_t attention(hipStream_t s, bool bf, const AttnArgs& a, bool combine = true);
+hipError_t attention_combine(hipStream_t s, const AttnArgs& a);
 // Split count that best fills `concurrent` resident workgroups for `units`
 // query tiles over `tiles` key tiles (1 .. max_split).
 int attention_pick_split(int units, int tiles, int max_split, int concurrent);

@@ -595,7 +595,10 @@ sd_status sd_stream_step(sd_stream* s, float* out_latent, sd_step_info* info) {
       }
       const double shared = (double)sk.count + sw.count;
       PROF(SD_PROF_ATTN_SELF, 4.0 * R * L * (shared + L) * d,
-           (double)es * d * (2.0 * R * L + 2.0 * shared + 2.0 * R * L), sdk::attention(st, bf, A));
+           (double)es * d * (2.0 * R * L + 2.0 * shared + 2.0 * R * L), sdk::attention(st, bf, A, false));
+      if (A.nsplit > 1)
+        PROF(SD_PROF_ATTN_COMBINE, 0.0, (double)A.nsplit * R * L * (d * 4.0 + H * 8.0) + (double)R * L * d * es,
+             sdk::attention_combine(st, A));
     }
     if (r_exit >= 0 && (s->Wt > 0 || capture)) {
       const int64_t cb = (int64_t)b * H * s->S8 * hd;
