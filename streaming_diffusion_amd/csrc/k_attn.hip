@@ -236,7 +236,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(m_run, mx);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2f((m_run - m_use) * sl2);
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * sl2);
     const float moff = -m_use * sl2;
     float psum = 0.f;
     bf16x8 pb[4];
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const float p = exp2f(fmaf(s[kt][q], sl2, moff));
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][q], sl2, moff));   // v_exp_f32: tiny results flush to 0
         psum += p;
         pb[kt * 2 + (q >> 3)][q & 7] = (bf16)p;
       }

@@ -45,12 +45,12 @@ SD_DEV float2 rope_cs(const Epi& E, int t0, int t, int e) {
 }
 
 // Epilogue of one 64-row strip held in LDS (fp32, row pitch LC).
-template <int BN, int MODE>
+template <int BN, int NT, int MODE>
 SD_DEV void epi_strip(const Epi& E, const float* stg, int LC, int m_base, int n0, int M, int N, int tid,
                       const int* t0s) {
   constexpr int G = BN / 8;       // 8-column groups per row
   if constexpr (MODE == EPI_HEAD) {
-    for (int idx = tid; idx < 64 * BN; idx += 256) {
+    for (int idx = tid; idx < 64 * BN; idx += NT) {
       const int row = idx / BN, col = idx % BN;
       const int m = m_base + row, n = n0 + col;
       if (m >= M || n >= N) continue;
@@ -66,7 +66,7 @@ SD_DEV void epi_strip(const Epi& E, const float* stg, int LC, int m_base, int n0
   }
   if constexpr (MODE == EPI_QKV || MODE == EPI_CTXKV) {
     // q and k sections: groups of 8 head-dim elements of one token
-    for (int g = tid; g < 64 * G; g += 256) {
+    for (int g = tid; g < 64 * G; g += NT) {
       const int row = g / G, cg = g % G;
       const int m = m_base + row, n = n0 + cg * 8;
       if (m >= M || n >= N) continue;
@@ -98,7 +98,7 @@ SD_DEV void epi_strip(const Epi& E, const float* stg, int LC, int m_base, int n0
         store8_bf16((bf16*)E.k + (rh * E.kstride + t) * E.hd + e0, v);
     }
     // v section: groups of 8 tokens of one head-dim element (transposed store)
-    for (int g = tid; g < 8 * BN; g += 256) {
+    for (int g = tid; g < 8 * BN; g += NT) {
       const int col = g % BN, rg = g / BN;
       const int m = m_base + rg * 8, n = n0 + col;
       if (m >= M || n >= N) continue;
@@ -126,7 +126,7 @@ SD_DEV void epi_strip(const Epi& E, const float* stg, int LC, int m_base, int n0
     return;
   }
   // row-major modes: groups of 8 consecutive columns of one row
-  for (int g = tid; g < 64 * G; g += 256) {
+  for (int g = tid; g < 64 * G; g += NT) {
     const int row = g / G, cg = g % G;
     const int m = m_base + row, n = n0 + cg * 8;
     if (m >= M || n >= N) continue;
@@ -194,12 +194,13 @@ SD_DEV void epi_strip(const Epi& E, const float* stg, int LC, int m_base, int n0
   }
 }
 
-template <int BM, int BN, int MODE>
-__global__ __launch_bounds__(256) void gemm_mfma_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
+template <int BM, int BN, int NW, int MODE>
+__global__ __launch_bounds__(64 * NW) void gemm_mfma_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
                                                         int M, int N, int K, Epi E) {
   constexpr int BK = 64, PAD = 8, LDK = BK + PAD;
-  constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 32, FN = TN / 32;
-  constexpr int CA = BM * (BK / 8) / 256, CB = BN * (BK / 8) / 256;
+  constexpr int NT = 64 * NW, WN = NW / 2;          // waves arranged 2 x WN
+  constexpr int TM = BM / 2, TN = BN / WN, FM = TM / 32, FN = TN / 32;
+  constexpr int CA = BM * (BK / 8) / NT, CB = BN * (BK / 8) / NT;
   constexpr int STAGE = (BM + BN) * LDK;                 // bf16 elements per LDS stage
   constexpr int LC = BN + 4;                             // fp32 pitch of the epilogue strip
   static_assert(64 * LC * 4 <= 2 * STAGE * 2, "epilogue strip must fit in the stage buffers");
@@ -226,34 +227,85 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(const bf16* __restrict__
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-  bf16x8 ra[CA], rb[CB];
+  // Global -> register staging.  Rows beyond M (N) are clamped to the last
+  // row: they only feed output rows/columns that are never stored, so full
+  // k-tiles load without branches; only a ragged last k-tile checks K.
+  uint32_t a_off[CA], b_off[CB];
+#pragma unroll
+  for (int i = 0; i < CA; ++i) {
+    const int c = tid + i * NT, row = c >> 3, kc = (c & 7) * 8;
+    a_off[i] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)K + kc;
+  }
+#pragma unroll
+  for (int i = 0; i < CB; ++i) {
+    const int c = tid + i * NT, row = c >> 3, kc = (c & 7) * 8;
+    b_off[i] = (uint32_t)min(n0 + row, N - 1) * (uint32_t)K + kc;
+  }
+  const int KT = (K + BK - 1) / BK;
+  const bool ragged = (K % BK) != 0;
   const bf16x8 zero8 = {};
-  auto gload = [&](int k0) {
+  auto gload = [&](bf16x8* ra, bf16x8* rb, int kt) {
+    const uint32_t k0 = (uint32_t)kt * BK;
+    if (!ragged || kt + 1 < KT) {
 #pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      const int c = tid + i * 256, row = c >> 3, kc = (c & 7) * 8;
-      const int gm_ = m0 + row, gk = k0 + kc;
-      ra[i] = (gm_ < M && gk < K) ? *(const bf16x8*)(A + (int64_t)gm_ * K + gk) : zero8;
-    }
+      for (int i = 0; i < CA; ++i) ra[i] = *(const bf16x8*)(A + a_off[i] + k0);
 #pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      const int c = tid + i * 256, row = c >> 3, kc = (c & 7) * 8;
-      const int gn = n0 + row, gk = k0 + kc;
-      rb[i] = (gn < N && gk < K) ? *(const bf16x8*)(W + (int64_t)gn * K + gk) : zero8;
+      for (int i = 0; i < CB; ++i) rb[i] = *(const bf16x8*)(W + b_off[i] + k0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < CA; ++i) {
+        const int kc = ((tid + i * NT) & 7) * 8;
+        ra[i] = ((int)k0 + kc < K) ? *(const bf16x8*)(A + a_off[i] + k0) : zero8;
+      }
+#pragma unroll
+      for (int i = 0; i < CB; ++i) {
+        const int kc = ((tid + i * NT) & 7) * 8;
+        rb[i] = ((int)k0 + kc < K) ? *(const bf16x8*)(W + b_off[i] + k0) : zero8;
+      }
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](const bf16x8* ra, const bf16x8* rb, int buf) {
     bf16* as = smem + buf * STAGE;
     bf16* bs = as + BM * LDK;
 #pragma unroll
     for (int i = 0; i < CA; ++i) {
-      const int c = tid + i * 256, row = c >> 3, kc = (c & 7) * 8;
+      const int c = tid + i * NT, row = c >> 3, kc = (c & 7) * 8;
       *(bf16x8*)(as + row * LDK + kc) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
-      const int c = tid + i * 256, row = c >> 3, kc = (c & 7) * 8;
+      const int c = tid + i * NT, row = c >> 3, kc = (c & 7) * 8;
       *(bf16x8*)(bs + row * LDK + kc) = rb[i];
+    }
+  };
+  const int lr = lane & 31, lk = (lane >> 5) * 8;
+  // The fragments of k-step kk+1 are read from LDS before the MFMAs of step
+  // kk are issued, so LDS latency hides behind matrix-core work; the
+  // scheduling barriers keep the compiler from regrouping the reads.
+  auto compute = [&](int buf) {
+    const bf16* as = smem + buf * STAGE + (wm * TM + lr) * LDK + lk;
+    const bf16* bs = smem + buf * STAGE + BM * LDK + (wn * TN + lr) * LDK + lk;
+    bf16x8 fa[2][FM], fb[2][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[0][i] = *(const bf16x8*)(as + i * 32 * LDK);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[0][j] = *(const bf16x8*)(bs + j * 32 * LDK);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int cur = ks & 1, nxt = cur ^ 1;
+      if (ks + 1 < BK / 16) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[nxt][i] = *(const bf16x8*)(as + i * 32 * LDK + (ks + 1) * 16);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[nxt][j] = *(const bf16x8*)(bs + j * 32 * LDK + (ks + 1) * 16);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -263,30 +315,17 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(const bf16* __restrict__
       for (int i = 0; i < SD_MAX_ROWS; ++i) t0s[i] = E.t0[i];
     }
   }
-  const int KT = (K + BK - 1) / BK;
-  gload(0);
-  sstore(0);
+  // One register stage, two LDS stages: the loads of k-tile t+1 are issued
+  // before tile t is multiplied and stored to the free LDS stage after it.
+  bf16x8 ra[CA], rb[CB];
+  gload(ra, rb, 0);
+  sstore(ra, rb, 0);
   __syncthreads();
-  const int lr = lane & 31, lk = (lane >> 5) * 8;
   for (int kt = 0; kt < KT; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < KT) gload((kt + 1) * BK);
-    const bf16* as = smem + buf * STAGE + (wm * TM + lr) * LDK + lk;
-    const bf16* bs = smem + buf * STAGE + BM * LDK + (wn * TN + lr) * LDK + lk;
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8 fa[FM], fb[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) fa[i] = *(const bf16x8*)(as + i * 32 * LDK + kk);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) fb[j] = *(const bf16x8*)(bs + j * 32 * LDK + kk);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < KT) sstore(buf ^ 1);
+    if (kt + 1 < KT) gload(ra, rb, kt + 1);
+    compute(buf);
+    if (kt + 1 < KT) sstore(ra, rb, buf ^ 1);
     __syncthreads();
   }
 
@@ -310,23 +349,25 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(const bf16* __restrict__
           }
     }
     __syncthreads();
-    epi_strip<BN, MODE>(E, stg, LC, m0 + s * 64, n0, M, N, tid, t0s);
+    epi_strip<BN, NT, MODE>(E, stg, LC, m0 + s * 64, n0, M, N, tid, t0s);
     __syncthreads();
   }
 }
 
 template <int MODE>
 hipError_t gemm_mfma_mode(hipStream_t s, const bf16* A, const bf16* W, int M, int N, int K, const Epi& E) {
-  // pick the largest tile that still gives most CUs work: estimated time
-  // ~ rounds of 256 workgroups x per-tile cost (larger tiles cost less per flop)
-  struct Opt { int bm, bn; double eff; };
-  const Opt opts[3] = {{256, 256, 1.0}, {256, 128, 0.85}, {128, 128, 0.7}};
+  // pick the tile that minimises (rounds of resident workgroups) x (cost per
+  // tile); larger tiles cost less per flop.  256 x 256 with 8 waves keeps two
+  // waves per SIMD; the 4-wave tiles run one.
+  struct Opt { int bm, bn, per_cu; double eff; };
+  const Opt opts[3] = {{256, 256, 1, 1.0}, {256, 128, 1, 0.85}, {128, 128, 2, 0.7}};
   int best = 0;
   double best_t = 1e30;
   for (int i = 0; i < 3; ++i) {
     const int64_t tiles = (int64_t)((M + opts[i].bm - 1) / opts[i].bm) * ((N + opts[i].bn - 1) / opts[i].bn);
-    const int64_t rounds = (tiles + 255) / 256;
-    const double t = (double)rounds * opts[i].bm * opts[i].bn / opts[i].eff;
+    const int64_t slots = 256 * opts[i].per_cu;
+    const int64_t rounds = (tiles + slots - 1) / slots;
+    const double t = (double)rounds * opts[i].bm * opts[i].bn / (opts[i].eff * opts[i].per_cu);
     if (t < best_t * 0.999) {
       best_t = t;
       best = i;
@@ -335,15 +376,17 @@ hipError_t gemm_mfma_mode(hipStream_t s, const bf16* A, const bf16* W, int M, in
   const int bm = opts[best].bm, bn = opts[best].bn;
   const unsigned grid = (unsigned)(((M + bm - 1) / bm) * ((N + bn - 1) / bn));
   if (best == 0)
-    gemm_mfma_kernel<256, 256, MODE><<<grid, 256, 0, s>>>(A, W, M, N, K, E);
+    gemm_mfma_kernel<256, 256, 8, MODE><<<grid, 512, 0, s>>>(A, W, M, N, K, E);
   else if (best == 1)
-    gemm_mfma_kernel<256, 128, MODE><<<grid, 256, 0, s>>>(A, W, M, N, K, E);
+    gemm_mfma_kernel<256, 128, 4, MODE><<<grid, 256, 0, s>>>(A, W, M, N, K, E);
   else
-    gemm_mfma_kernel<128, 128, MODE><<<grid, 256, 0, s>>>(A, W, M, N, K, E);
+    gemm_mfma_kernel<128, 128, 4, MODE><<<grid, 256, 0, s>>>(A, W, M, N, K, E);
   return hipGetLastError();
 }
 
 hipError_t gemm_mfma(hipStream_t s, const void* A, const void* W, int M, int N, int K, const Epi& E) {
+  // operand offsets are 32-bit
+  if ((uint64_t)M * K >= (1ull << 32) || (uint64_t)N * K >= (1ull << 32)) return hipErrorInvalidValue;
   const bf16* a = (const bf16*)A;
   const bf16* w = (const bf16*)W;
   switch (E.mode) {
