@@ -354,6 +354,146 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_kernel(const bf16* __restri
   }
 }
 
+// ---------------------------------------------------------------------------
+// Direct-to-LDS variant (K a multiple of 64).  Operand tiles move from global
+// memory into LDS with global_load_lds_dwordx4: one wave instruction fills
+// 1 KB = 8 rows x 64 bf16 of a stage, lane l landing at byte 16*l.  No
+// registers are involved, so the wave's instruction stream carries only the
+// DMA issue, the LDS fragment reads and the MFMAs.  Rows are stored unpadded
+// with an XOR swizzle of their eight 16-byte chunks (chunk c of row r sits at
+// position c ^ ((r >> 1) & 7)), which keeps the MFMA fragment reads free of
+// bank conflicts for 8- and 16-lane LDS passes.  Two stages: the DMA of k-tile
+// t+1 is issued right after the barrier that retires tile t-1.
+SD_DEV int swz(int row) { return (row >> 1) & 7; }
+
+template <int BM, int BN, int NW, int MODE>
+__global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
+                                                          int M, int N, int K, Epi E) {
+  constexpr int BK = 64;
+  constexpr int NT = 64 * NW, WN = NW / 2;
+  constexpr int TM = BM / 2, TN = BN / WN, FM = TM / 32, FN = TN / 32;
+  constexpr int AQ = BM / 8 / NW, BQ = BN / 8 / NW;     // 1 KB DMA blocks per wave per k-tile
+  constexpr int STAGE = (BM + BN) * BK;                   // bf16 elements per stage
+  constexpr int LC = BN + 4;
+  static_assert(AQ >= 1 && BQ >= 1, "tile shape");
+  static_assert(64 * LC * 4 <= 2 * STAGE * 2, "epilogue strip must fit in the stage buffers");
+  __shared__ __attribute__((aligned(1024))) bf16 smem[2 * STAGE];
+  __shared__ int t0s[SD_MAX_ROWS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  constexpr int GM = 4;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int grp = lid / (GM * tiles_n), first_m = grp * GM;
+  const int gm = min(tiles_m - first_m, GM);
+  const int within = lid - grp * GM * tiles_n;
+  const int tm = first_m + within % gm, tn = within / gm;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  // per-lane source offsets (elements) of this wave's DMA blocks, k-tile 0;
+  // rows beyond M / N are clamped (they feed outputs that are never stored)
+  uint32_t a_src[AQ], b_src[BQ];
+  const int lrow = lane >> 3, lpos = lane & 7;
+#pragma unroll
+  for (int q = 0; q < AQ; ++q) {
+    const int r = (wave * AQ + q) * 8 + lrow;
+    a_src[q] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)K + (uint32_t)((lpos ^ swz(r)) * 8);
+  }
+#pragma unroll
+  for (int q = 0; q < BQ; ++q) {
+    const int r = (wave * BQ + q) * 8 + lrow;
+    b_src[q] = (uint32_t)min(n0 + r, N - 1) * (uint32_t)K + (uint32_t)((lpos ^ swz(r)) * 8);
+  }
+  auto issue = [&](int kt, int buf) {
+    const uint32_t k0 = (uint32_t)kt * BK;
+    bf16* as = smem + buf * STAGE;
+    bf16* bs = as + BM * BK;
+#pragma unroll
+    for (int q = 0; q < AQ; ++q)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(A + a_src[q] + k0),
+                                       (__attribute__((address_space(3))) void*)(as + (wave * AQ + q) * 8 * BK),
+                                       16, 0, 0);
+#pragma unroll
+    for (int q = 0; q < BQ; ++q)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(W + b_src[q] + k0),
+                                       (__attribute__((address_space(3))) void*)(bs + (wave * BQ + q) * 8 * BK),
+                                       16, 0, 0);
+  };
+  // fragment rows of this lane and their swizzle
+  const int lr = lane & 31, lh = lane >> 5;
+  auto compute = [&](int buf) {
+    const bf16* as = smem + buf * STAGE;
+    const bf16* bs = as + BM * BK;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int c = ks * 2 + lh;           // logical 16-byte chunk of this lane
+      bf16x8 fa[FM], fb[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int row = wm * TM + i * 32 + lr;
+        fa[i] = *(const bf16x8*)(as + row * BK + ((c ^ swz(row)) * 8));
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int row = wn * TN + j * 32 + lr;
+        fb[j] = *(const bf16x8*)(bs + row * BK + ((c ^ swz(row)) * 8));
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  if constexpr (MODE == EPI_QKV) {
+    if (tid == 0) {
+#pragma unroll
+      for (int i = 0; i < SD_MAX_ROWS; ++i) t0s[i] = E.t0[i];
+    }
+  }
+  const int KT = K / BK;
+  issue(0, 0);
+  for (int kt = 0; kt < KT; ++kt) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");    // this wave's DMA of tile kt has landed
+    __syncthreads();                                     // everyone's has; tile kt-1 is retired
+    if (kt + 1 < KT) issue(kt + 1, (kt + 1) & 1);
+    compute(kt & 1);
+  }
+  __syncthreads();
+
+  float* stg = (float*)smem;
+  constexpr int SPW = TM / 64;
+#pragma unroll
+  for (int s = 0; s < BM / 64; ++s) {
+    if (wm == s / SPW) {
+      const int i0 = (s % SPW) * 2;
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int row = ii * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+            const int col = wn * TN + j * 32 + (lane & 31);
+            stg[row * LC + col] = acc[i0 + ii][j][q];
+          }
+    }
+    __syncthreads();
+    epi_strip<BN, NT, MODE>(E, stg, LC, m0 + s * 64, n0, M, N, tid, t0s);
+    __syncthreads();
+  }
+}
+
 template <int MODE>
 hipError_t gemm_mfma_mode(hipStream_t s, const bf16* A, const bf16* W, int M, int N, int K, const Epi& E) {
   // pick the tile that minimises (rounds of resident workgroups) x (cost per
@@ -372,6 +512,19 @@ hipError_t gemm_mfma_mode(hipStream_t s, const bf16* A, const bf16* W, int M, in
       best_t = t;
       best = i;
     }
+  }
+  if (K % 64 == 0) {
+    // direct-to-LDS kernels: 256 x 256 (8 waves) once there are enough tiles
+    // to occupy the CUs, 128 x 128 (4 waves, two workgroups per CU) otherwise
+    const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+    if (t256 >= 128) {
+      const unsigned grid = (unsigned)t256;
+      gemm_dma_kernel<256, 256, 8, MODE><<<grid, 512, 0, s>>>(A, W, M, N, K, E);
+    } else {
+      const unsigned grid = (unsigned)(((M + 127) / 128) * ((N + 127) / 128));
+      gemm_dma_kernel<128, 128, 4, MODE><<<grid, 256, 0, s>>>(A, W, M, N, K, E);
+    }
+    return hipGetLastError();
   }
   const int bm = opts[best].bm, bn = opts[best].bn;
   const unsigned grid = (unsigned)(((M + bm - 1) / bm) * ((N + bn - 1) / bn));
