@@ -41,9 +41,13 @@ SD_DEV SegRt seg_layout(const AttnArgs& a) {
   return s;
 }
 
+// Branch-free: each segment is one unsigned range test, combined with
+// bitwise ors (no short-circuit control flow inside the masking loops).
 SD_DEV bool key_valid(const SegRt& s, int j) {
-  return (j < s.begin[0] + s.count[0]) || (j >= s.begin[1] && j < s.begin[1] + s.count[1]) ||
-         (j >= s.begin[2] && j < s.begin[2] + s.count[2]);
+  const bool v0 = (unsigned)(j - s.begin[0]) < (unsigned)s.count[0];
+  const bool v1 = (unsigned)(j - s.begin[1]) < (unsigned)s.count[1];
+  const bool v2 = (unsigned)(j - s.begin[2]) < (unsigned)s.count[2];
+  return v0 | v1 | v2;
 }
 
 // Physical position and segment of virtual key j (j inside a segment's padded range).
@@ -58,18 +62,67 @@ SD_DEV int key_pos(const KvSeg& g, int u) {
 }
 
 // ---------------------------------------------------------------------------
+// K and V^T tiles move from global memory straight into LDS
+// (global_load_lds_dwordx4: 16 bytes per lane, a wave instruction fills 1 KB,
+// lane l at byte 16*l); no register staging.  LDS rows are unpadded and their
+// 16-byte chunks XOR-swizzled by row (chunk c of row r at c ^ chunk_swz<W>(r),
+// W the row width in elements) so that the 16-lane passes of the MFMA
+// fragment reads fall on distinct banks.
+// one of three values, chosen by value (a conditional over lvalues would
+// select an address and force its operands into memory)
+template <typename T>
+SD_DEV T pick3(bool first, bool second, T x, T y, T z) {
+  return first ? x : (second ? y : z);
+}
+
+template <int W>
+SD_DEV int chunk_swz(int row) {
+  return (row / (128 / W)) & (W / 8 - 1);
+}
+
+SD_DEV void dma16(const bf16* src, bf16* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+// this wave's loads have landed; meet the workgroup (no fence: the wait
+// orders the DMA writes, the LDS reads of the previous tile were consumed)
+SD_DEV void dma_wait_barrier() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// max / sum of a lane's value and the value of lane ^ 32
+SD_DEV float halves_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+SD_DEV float halves_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 path.  The keys of one (row, head) are walked segment by segment in
+// tiles of 64 that never straddle two segments (a segment's last tile is
+// partial and masked), so the segment, its base pointers and its ring wrap
+// are uniform per tile and every per-lane address is plain arithmetic.
+// One workgroup = 4 waves = 128 queries; two workgroups share a CU.
+//
 // ONESEG = 1 instantiates the same code for single-segment calls (the
 // prompt cross-attention), so that profiles tell the two uses apart.
 template <int HD, int ONESEG>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
-  constexpr int BQ = 128, KB = 64, PK = 8, PV = 8;
-  constexpr int LK = HD + PK, LV = KB + PV;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][KB * LK];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2][HD * LV];
+  constexpr int BQ = 128, KB = 64;
+  constexpr int CKR = HD / 8, RK = 64 / CKR;              // K: chunks per key row, key rows per DMA
+  constexpr int IK = KB / RK / 4, IV = HD / 8 / 4;        // DMA instructions per wave per tile (K, V^T)
+  constexpr int KT_EL = KB * HD, STAGE = 2 * KB * HD;     // bf16 elements: K tile, K + V^T tile
+  constexpr int LO = HD + 8;
+  static_assert(IK >= 1 && IV >= 1, "tile shape");
+  static_assert(BQ * LO <= 2 * STAGE, "output staging must fit in the stages");
+  // growth of the running maximum (in exp2 units) that forces a rescale, so
+  // probabilities stay below 2^8 between rescales
+  constexpr float RESCALE_LOG2 = 8.0f;
+  __shared__ __attribute__((aligned(1024))) bf16 smem[2 * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // logical order (row, head, q-tile) with q-tiles fastest; all q-tiles of a
-  // (row, head) share its keys, so they are kept on one XCD
   const int nqt = (a.L + BQ - 1) / BQ;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
   // order (row, head, split, q-tile): the workgroups resident on one XCD at
@@ -77,105 +130,88 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   const int qt = lid % nqt, sp = (lid / nqt) % a.nsplit;
   const int h = (lid / (nqt * a.nsplit)) % a.H, r = a.r0 + lid / (nqt * a.nsplit * a.H);
   const int q0 = qt * BQ;
-  const SegRt sr = seg_layout(a);
-  const int NK = sr.end[2];
-  const int NT_all = (NK + KB - 1) / KB;
+
+  // segments of this (row, head) as plain scalars, uniform over the
+  // workgroup (unused segments have no keys)
+  const int c0 = a.nseg > 0 ? a.seg[0].count : 0;
+  const int c1 = a.nseg > 1 ? a.seg[1].count : 0;
+  const int c2 = a.nseg > 2 ? a.seg[2].count : 0;
+  const int nt0 = (c0 + KB - 1) / KB, nt1 = (c1 + KB - 1) / KB, nt2 = (c2 + KB - 1) / KB;
+  const int NT_all = nt0 + nt1 + nt2;
   const int tps = (NT_all + a.nsplit - 1) / a.nsplit;
   const int T0 = min(NT_all, sp * tps), NT = min(NT_all, T0 + tps);   // this split's key tiles [T0, NT)
+  const bf16* const kbase0 = (const bf16*)a.seg[0].k + (int64_t)r * a.seg[0].k_rs + (int64_t)h * a.seg[0].k_hs;
+  const bf16* const kbase1 = (const bf16*)a.seg[1].k + (int64_t)r * a.seg[1].k_rs + (int64_t)h * a.seg[1].k_hs;
+  const bf16* const kbase2 = (const bf16*)a.seg[2].k + (int64_t)r * a.seg[2].k_rs + (int64_t)h * a.seg[2].k_hs;
+  const bf16* const vbase0 = (const bf16*)a.seg[0].vt + (int64_t)r * a.seg[0].vt_rs + (int64_t)h * a.seg[0].vt_hs;
+  const bf16* const vbase1 = (const bf16*)a.seg[1].vt + (int64_t)r * a.seg[1].vt_rs + (int64_t)h * a.seg[1].vt_hs;
+  const bf16* const vbase2 = (const bf16*)a.seg[2].vt + (int64_t)r * a.seg[2].vt_rs + (int64_t)h * a.seg[2].vt_hs;
+  const int cap0 = a.seg[0].cap, cap1 = a.seg[1].cap, cap2 = a.seg[2].cap;
+  const int st0 = a.seg[0].start, st1 = a.seg[1].start, st2 = a.seg[2].start;
+  const int wr0 = a.seg[0].wrap, wr1 = a.seg[1].wrap, wr2 = a.seg[2].wrap;
+
+  // tile t -> its segment's bases, the position of its first key, the
+  // segment's capacity and ring flag, and the number of valid keys in it
+  struct TileRef {
+    const bf16* kb;
+    const bf16* vb;
+    int p0, cap, wrap, nvalid;
+  };
+  auto tile_ref = [=](int t) {
+    const bool in0 = t < nt0, in1 = !in0 && t < nt0 + nt1;
+    const int u0 = (t - pick3(in0, in1, 0, nt0, nt0 + nt1)) * KB;
+    TileRef f;
+    f.kb = pick3(in0, in1, kbase0, kbase1, kbase2);
+    f.vb = pick3(in0, in1, vbase0, vbase1, vbase2);
+    f.cap = pick3(in0, in1, cap0, cap1, cap2);
+    f.wrap = pick3(in0, in1, wr0, wr1, wr2);
+    f.nvalid = min(KB, pick3(in0, in1, c0, c1, c2) - u0);
+    int p0 = pick3(in0, in1, st0, st1, st2) + u0;
+    if (f.wrap && p0 >= f.cap) p0 -= f.cap;
+    f.p0 = p0;
+    return f;
+  };
 
   // Q fragments (B operand): lane -> query q0 + wave*32 + lane%32, hd block
   // kk*16 + 8*(lane/32).
+  const int half = lane >> 5;
   const int myq = q0 + wave * 32 + (lane & 31);
   bf16x8 qf[HD / 16];
   {
-    const bf16* qp = (const bf16*)a.q + (int64_t)r * a.q_rs + (int64_t)h * a.q_hs + (int64_t)myq * HD;
-    const bf16x8 z = {};
+    const bf16* qp = (const bf16*)a.q + (int64_t)r * a.q_rs + (int64_t)h * a.q_hs + (int64_t)min(myq, a.L - 1) * HD;
 #pragma unroll
-    for (int kk = 0; kk < HD / 16; ++kk)
-      qf[kk] = (myq < a.L) ? *(const bf16x8*)(qp + kk * 16 + 8 * (lane >> 5)) : z;
+    for (int kk = 0; kk < HD / 16; ++kk) qf[kk] = *(const bf16x8*)(qp + kk * 16 + 8 * half);
   }
+  // the Q fragments have landed (a wait the compiler sees: without it, the
+  // first MFMA of every tile would wait for all outstanding tile DMA)
+  __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0), expcnt and lgkmcnt unconstrained
 
-  // Tile loaders: K tile KB x HD (HD/8 chunks per key), V^T tile HD x KB
-  // (KB/8 chunks per hd row).  Chunks per thread:
-  constexpr int CK = KB * (HD / 8) / 256, CV = HD * (KB / 8) / 256;
-  bf16x8 rk[CK > 0 ? CK : 1], rv[CV > 0 ? CV : 1];
-  auto gload = [&](int tile) {
-    const bf16x8 z = {};
-    // Fast path (all but a few tiles of a row): the whole tile is valid keys
-    // of one segment at contiguous positions.  Everything below is uniform
-    // over the workgroup.
-    {
-      const int jb = tile * KB;
-      const int s0 = key_seg(sr, jb);
-      const int b0 = s0 == 0 ? sr.begin[0] : (s0 == 1 ? sr.begin[1] : sr.begin[2]);
-      const KvSeg g = seg_pick(a, s0);
-      const int u0 = jb - b0;
-      int p0 = g.start + u0;
-      if (g.wrap && p0 >= g.cap) p0 -= g.cap;
-      if (u0 + KB <= g.count && p0 + KB <= g.cap) {
-        const bf16* kb = (const bf16*)g.k + (int64_t)r * g.k_rs + (int64_t)h * g.k_hs + (int64_t)p0 * HD;
-        const bf16* vb = (const bf16*)g.vt + (int64_t)r * g.vt_rs + (int64_t)h * g.vt_hs + p0;
+  // DMA of key tile t into stage buf.  This lane moves K key row
+  // kr = wave*(KB/4) + i*RK + lane/CKR (logical chunk kc) and V^T head-dim row
+  // ve = wave*(HD/4) + i*8 + lane/8 (logical 8-key group vc).  Keys past the
+  // segment's count are read from the tile's first key: finite data whose
+  // scores are masked.  An 8-key group that starts inside the valid range may
+  // end in the zero-filled padding of the segment's storage (positions up to
+  // the next multiple of 8 exist).
+  auto issue = [&](int t, int buf) {
+    bf16* ks = smem + buf * STAGE;
+    bf16* vs = ks + KT_EL;
+    const TileRef f = tile_ref(t);
 #pragma unroll
-        for (int i = 0; i < CK; ++i) {
-          const int c = tid + i * 256, key = c / (HD / 8), e0 = (c % (HD / 8)) * 8;
-          rk[i] = *(const bf16x8*)(kb + key * HD + e0);
-        }
-#pragma unroll
-        for (int i = 0; i < CV; ++i) {
-          const int c = tid + i * 256, e = c / (KB / 8), k0 = (c % (KB / 8)) * 8;
-          rv[i] = *(const bf16x8*)(vb + (int64_t)e * g.cap + k0);
-        }
-        return;
-      }
+    for (int i = 0; i < IK; ++i) {
+      const int kr = wave * (KB / 4) + i * RK + lane / CKR;
+      const int kc = (lane % CKR) ^ chunk_swz<HD>(kr);
+      int pos = f.p0 + (kr < f.nvalid ? kr : 0);
+      if (f.wrap && pos >= f.cap) pos -= f.cap;
+      dma16(f.kb + (int64_t)pos * HD + kc * 8, ks + (wave * (KB / 4) + i * RK) * HD);
     }
 #pragma unroll
-    for (int i = 0; i < CK; ++i) {
-      const int c = tid + i * 256, key = c / (HD / 8), e0 = (c % (HD / 8)) * 8;
-      const int j = tile * KB + key;
-      bf16x8 v = z;
-      if (j < NK) {
-        const int s = key_seg(sr, j);
-        const KvSeg g = seg_pick(a, s);
-        const int u = j - (s == 0 ? sr.begin[0] : (s == 1 ? sr.begin[1] : sr.begin[2]));
-        // padding keys are never loaded (their scores are masked)
-        if (u < g.count) {
-          const int pos = key_pos(g, u);
-          const bf16* kp = (const bf16*)g.k + (int64_t)r * g.k_rs + (int64_t)h * g.k_hs;
-          v = *(const bf16x8*)(kp + (int64_t)pos * HD + e0);
-        }
-      }
-      rk[i] = v;
-    }
-#pragma unroll
-    for (int i = 0; i < CV; ++i) {
-      const int c = tid + i * 256, e = c / (KB / 8), k0 = (c % (KB / 8)) * 8;
-      const int j = tile * KB + k0;
-      bf16x8 v = z;
-      if (j < NK) {
-        const int s = key_seg(sr, j);
-        const KvSeg g = seg_pick(a, s);
-        const int u = j - (s == 0 ? sr.begin[0] : (s == 1 ? sr.begin[1] : sr.begin[2]));
-        // a chunk that starts inside the valid range may end in the zero-filled
-        // padding of its segment's storage (capacity is a multiple of 8)
-        if (u < g.count) {
-          const int pos = key_pos(g, u);
-          const bf16* vp = (const bf16*)g.vt + (int64_t)r * g.vt_rs + (int64_t)h * g.vt_hs;
-          v = *(const bf16x8*)(vp + (int64_t)e * g.cap + pos);
-        }
-      }
-      rv[i] = v;
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CK; ++i) {
-      const int c = tid + i * 256, key = c / (HD / 8), e0 = (c % (HD / 8)) * 8;
-      *(bf16x8*)&Ks[buf][key * LK + e0] = rk[i];
-    }
-#pragma unroll
-    for (int i = 0; i < CV; ++i) {
-      const int c = tid + i * 256, e = c / (KB / 8), k0 = (c % (KB / 8)) * 8;
-      *(bf16x8*)&Vs[buf][e * LV + k0] = rv[i];
+    for (int i = 0; i < IV; ++i) {
+      const int ve = wave * (HD / 4) + i * 8 + lane / 8;
+      const int vc = (lane % 8) ^ chunk_swz<KB>(ve);
+      int pos = f.p0 + (vc * 8 < f.nvalid ? vc * 8 : 0);
+      if (f.wrap && pos >= f.cap) pos -= f.cap;
+      dma16(f.vb + (int64_t)ve * f.cap + pos, vs + (wave * (HD / 4) + i * 8) * KB);
     }
   };
 
@@ -184,60 +220,68 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   for (int t = 0; t < HD / 32; ++t)
 #pragma unroll
     for (int q = 0; q < 16; ++q) o[t][q] = 0.f;
+  // m_run: reference maximum (raw score units) of the exponentials; it is
+  // raised only when a score exceeds it by RESCALE_LOG2 in exp2 units
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.scale * 1.4426950408889634f;
-  const int half = lane >> 5;
-  // permuted key row read by this lane for the S^T A operand
+  const float grow = RESCALE_LOG2 / sl2;
+  // permuted key row read by this lane for the S^T A operand (bits 2 and 3
+  // swapped), so that the accumulators are the B operand of O^T = V^T P^T
   const int rho = lane & 31;
   const int krow = (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1);
+  const int vrow = lane & 31;
 
-  if (T0 < NT) {
-    gload(T0);
-    sstore(0);
-  }
-  __syncthreads();
+  if (T0 < NT) issue(T0, 0);
   for (int tile = T0; tile < NT; ++tile) {
     const int buf = (tile - T0) & 1;
-    if (tile + 1 < NT) gload(tile + 1);
+    dma_wait_barrier();                               // tile landed everywhere; tile-1 retired
+    if (tile + 1 < NT) issue(tile + 1, buf ^ 1);
+    const bf16* ks = smem + buf * STAGE;
+    const bf16* vs = ks + KT_EL;
     // S^T for two 32-key halves of the tile
     f32x16 s[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
+      const int row = kt * 32 + krow;
+      const bf16* kp = ks + row * HD;
+      const int sw = chunk_swz<HD>(row);
+      bf16x8 ka[HD / 16];
+#pragma unroll
+      for (int kk = 0; kk < HD / 16; ++kk) ka[kk] = *(const bf16x8*)(kp + (((kk * 2 + half) ^ sw) * 8));
 #pragma unroll
       for (int q = 0; q < 16; ++q) s[kt][q] = 0.f;
-      const bf16* kp = &Ks[buf][(kt * 32 + krow) * LK + 8 * half];
 #pragma unroll
-      for (int kk = 0; kk < HD / 16; ++kk) {
-        const bf16x8 ka = *(const bf16x8*)(kp + kk * 16);
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s[kt], 0, 0, 0);
-      }
+      for (int kk = 0; kk < HD / 16; ++kk) s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qf[kk], s[kt], 0, 0, 0);
     }
-    // accumulator q of half kt holds key kt*32 + 16*(q/8) + 8*half + (q%8)
-    const int jb = tile * KB;
-    const bool full = (jb + KB <= sr.begin[0] + sr.count[0]) ||
-                      (jb >= sr.begin[1] && jb + KB <= sr.begin[1] + sr.count[1]) ||
-                      (jb >= sr.begin[2] && jb + KB <= sr.begin[2] + sr.count[2]);
-    // running max in raw score units (the scale is positive); the scale and
-    // the log2(e) factor are folded into one FMA in front of exp2
-    float mx = -INFINITY;
-    if (!full) {
+    // accumulator q of half kt holds tile key kt*32 + 16*(q/8) + 8*half + (q%8)
+    const int nvalid = tile_ref(tile).nvalid;
+    if (nvalid < KB) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int j = jb + kt * 32 + 16 * (q >> 3) + 8 * half + (q & 7);
-          if (!key_valid(sr, j)) s[kt][q] = -INFINITY;
-        }
+        for (int q = 0; q < 16; ++q)
+          s[kt][q] = kt * 32 + 16 * (q >> 3) + 8 * half + (q & 7) < nvalid ? s[kt][q] : -INFINITY;
     }
+    float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int q = 0; q < 16; ++q) mx = fmaxf(mx, s[kt][q]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * sl2);
-    const float moff = -m_use * sl2;
+    mx = halves_max(mx);
+    // raise the reference maximum (and rescale O and l) only when some query
+    // of the wave outgrew it by the threshold; a lane whose maximum is -inf
+    // keeps m_run, so -inf - -inf never occurs
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + grow)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f((m_run - m_new) * sl2);
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < HD / 32; ++t)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) o[t][q] *= alpha;
+      m_run = m_new;
+    }
+    const float moff = m_run == -INFINITY ? 0.f : -m_run * sl2;
     float psum = 0.f;
     bf16x8 pb[4];
 #pragma unroll
@@ -248,50 +292,40 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         psum += p;
         pb[kt * 2 + (q >> 3)][q & 7] = (bf16)p;
       }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    // rescale only when some query of the wave raised its maximum (exact:
-    // alpha is 1 otherwise)
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-#pragma unroll
-      for (int t = 0; t < HD / 32; ++t)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) o[t][q] *= alpha;
-    }
+    l_run += psum;
     // O^T += V^T P^T over 4 key blocks of 16
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
+      bf16x8 va[HD / 32];
 #pragma unroll
       for (int t = 0; t < HD / 32; ++t) {
-        const bf16x8 va = *(const bf16x8*)&Vs[buf][(t * 32 + (lane & 31)) * LV + kb * 16 + 8 * half];
-        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kb], o[t], 0, 0, 0);
+        const int row = t * 32 + vrow;
+        va[t] = *(const bf16x8*)(vs + row * KB + (((kb * 2 + half) ^ chunk_swz<KB>(row)) * 8));
       }
+#pragma unroll
+      for (int t = 0; t < HD / 32; ++t) o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t], pb[kb], o[t], 0, 0, 0);
     }
-    if (tile + 1 < NT) sstore(buf ^ 1);
-    __syncthreads();
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_tot = halves_sum(l_run);
   if (a.nsplit > 1) {
-    // partial result of this key range: unnormalised O and (max, sum)
-    const int tq = q0 + wave * 32 + (lane & 31);
-    if (tq < a.L) {
-      float* po = a.part_o + sp * a.part_so + ((int64_t)r * a.L + tq) * a.d + (int64_t)h * HD;
+    // partial result of this key range: unnormalised O and (reference max, sum)
+    if (myq < a.L) {
+      float* po = a.part_o + sp * a.part_so + ((int64_t)r * a.L + myq) * a.d + (int64_t)h * HD;
 #pragma unroll
       for (int t = 0; t < HD / 32; ++t)
 #pragma unroll
         for (int g = 0; g < 4; ++g)
           *(float4*)(po + t * 32 + 8 * g + 4 * half) =
               make_float4(o[t][4 * g], o[t][4 * g + 1], o[t][4 * g + 2], o[t][4 * g + 3]);
-      if (half == 0) a.part_ml[sp * a.part_sml + ((int64_t)r * a.H + h) * a.L + tq] = make_float2(m_run, l_tot);
+      if (half == 0) a.part_ml[sp * a.part_sml + ((int64_t)r * a.H + h) * a.L + myq] = make_float2(m_run, l_tot);
     }
     return;
   }
   // normalise and write O (token-major) through LDS: Os[query][hd]
+  __syncthreads();
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  bf16* Os = &Ks[0][0];                // BQ x (HD + PK) fits in one K stage
-  constexpr int LO = HD + PK;
-  static_assert(BQ * LO <= 2 * KB * LK, "O staging must fit in the K buffers");
+  bf16* Os = smem;
   const int ql = wave * 32 + (lane & 31);
 #pragma unroll
   for (int t = 0; t < HD / 32; ++t)
@@ -424,6 +458,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   ov[3] = (bf16)(acc.w * inv);
   *(bf16x4*)((bf16*)a.o + ((int64_t)r * a.L + t) * a.d + (int64_t)h * a.hd + e) = ov;
 }
+
+int attention_q_tile(bool bf, int hd) { return !bf ? 64 : 128; }
+
+int attention_wg_per_cu(bool bf, int hd) { return !bf ? 1 : 2; }
 
 int attention_pick_split(int units, int tiles, int max_split, int concurrent) {
   int best = 1;

@@ -14,6 +14,8 @@
 // head-dim element).
 #include <cmath>
 
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace sdk {
@@ -355,29 +357,44 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_kernel(const bf16* __restri
 }
 
 // ---------------------------------------------------------------------------
-// Direct-to-LDS variant (K a multiple of 64).  Operand tiles move from global
+// Direct-to-LDS variant (K a multiple of BK).  Operand tiles move from global
 // memory into LDS with global_load_lds_dwordx4: one wave instruction fills
-// 1 KB = 8 rows x 64 bf16 of a stage, lane l landing at byte 16*l.  No
-// registers are involved, so the wave's instruction stream carries only the
-// DMA issue, the LDS fragment reads and the MFMAs.  Rows are stored unpadded
-// with an XOR swizzle of their eight 16-byte chunks (chunk c of row r sits at
-// position c ^ ((r >> 1) & 7)), which keeps the MFMA fragment reads free of
-// bank conflicts for 8- and 16-lane LDS passes.  Two stages: the DMA of k-tile
-// t+1 is issued right after the barrier that retires tile t-1.
-SD_DEV int swz(int row) { return (row >> 1) & 7; }
+// 1 KB of a stage (1024 / (2 BK) rows of BK bf16), lane l landing at byte
+// 16*l.  No registers are involved, so the wave's instruction stream carries
+// only the DMA issue, the LDS fragment reads and the MFMAs.  Rows are stored
+// unpadded with an XOR swizzle of their 16-byte chunks: chunk c of row r sits
+// at position c ^ ((r / RP) % CPR), CPR = BK / 8 chunks per row, RP = 128 / BK
+// rows per 256 bytes, which keeps the 16-lane passes of the MFMA fragment
+// reads on distinct banks.  NS stages: the DMA of k-tile t + NS - 1 is issued
+// right after the barrier that retires tile t - 1, and the wait before tile t
+// leaves the later tiles' DMA in flight.
+template <int BK>
+SD_DEV int swz(int row) {
+  return (row / (128 / BK)) & (BK / 8 - 1);
+}
 
-template <int BM, int BN, int NW, int MODE>
+// wait until at most n of this wave's vector-memory operations are in flight,
+// then meet the workgroup at a barrier (no fence: the DMA writes are ordered
+// by the wait, the LDS reads of the previous tile were consumed by its MFMAs)
+template <int n>
+SD_DEV void wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(n) : "memory");
+}
+
+template <int BM, int BN, int NW, int BK, int NS, bool SPREAD, int MODE>
 __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
                                                           int M, int N, int K, Epi E) {
-  constexpr int BK = 64;
   constexpr int NT = 64 * NW, WN = NW / 2;
   constexpr int TM = BM / 2, TN = BN / WN, FM = TM / 32, FN = TN / 32;
-  constexpr int AQ = BM / 8 / NW, BQ = BN / 8 / NW;     // 1 KB DMA blocks per wave per k-tile
+  constexpr int CPR = BK / 8, RPB = 64 / CPR;             // chunks per row, rows per DMA block
+  constexpr int AQ = BM / RPB / NW, BQ = BN / RPB / NW;   // DMA blocks per wave per k-tile
+  constexpr int DQ = AQ + BQ;
   constexpr int STAGE = (BM + BN) * BK;                   // bf16 elements per stage
   constexpr int LC = BN + 4;
-  static_assert(AQ >= 1 && BQ >= 1, "tile shape");
-  static_assert(64 * LC * 4 <= 2 * STAGE * 2, "epilogue strip must fit in the stage buffers");
-  __shared__ __attribute__((aligned(1024))) bf16 smem[2 * STAGE];
+  static_assert(AQ >= 1 && BQ >= 1 && AQ * RPB * NW == BM && BQ * RPB * NW == BN, "tile shape");
+  static_assert(NS >= 2 && NS <= 4 && DQ * (NS - 2) < 64, "stages");
+  static_assert(64 * LC * 4 <= NS * STAGE * 2, "epilogue strip must fit in the stage buffers");
+  __shared__ __attribute__((aligned(1024))) bf16 smem[NS * STAGE];
   __shared__ int t0s[SD_MAX_ROWS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -402,50 +419,57 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restric
   // per-lane source offsets (elements) of this wave's DMA blocks, k-tile 0;
   // rows beyond M / N are clamped (they feed outputs that are never stored)
   uint32_t a_src[AQ], b_src[BQ];
-  const int lrow = lane >> 3, lpos = lane & 7;
+  const int lrow = lane / CPR, lpos = lane % CPR;
 #pragma unroll
   for (int q = 0; q < AQ; ++q) {
-    const int r = (wave * AQ + q) * 8 + lrow;
-    a_src[q] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)K + (uint32_t)((lpos ^ swz(r)) * 8);
+    const int r = (wave * AQ + q) * RPB + lrow;
+    a_src[q] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)K + (uint32_t)((lpos ^ swz<BK>(r)) * 8);
   }
 #pragma unroll
   for (int q = 0; q < BQ; ++q) {
-    const int r = (wave * BQ + q) * 8 + lrow;
-    b_src[q] = (uint32_t)min(n0 + r, N - 1) * (uint32_t)K + (uint32_t)((lpos ^ swz(r)) * 8);
+    const int r = (wave * BQ + q) * RPB + lrow;
+    b_src[q] = (uint32_t)min(n0 + r, N - 1) * (uint32_t)K + (uint32_t)((lpos ^ swz<BK>(r)) * 8);
   }
-  auto issue = [&](int kt, int buf) {
+  // DMA of k-tile kt into stage buf; part < 0 issues every block of this
+  // wave, part p in [0, BK/16) only the blocks j with j * (BK/16) / DQ == p
+  auto issue = [&](int kt, int buf, int part) {
     const uint32_t k0 = (uint32_t)kt * BK;
     bf16* as = smem + buf * STAGE;
     bf16* bs = as + BM * BK;
 #pragma unroll
     for (int q = 0; q < AQ; ++q)
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(A + a_src[q] + k0),
-                                       (__attribute__((address_space(3))) void*)(as + (wave * AQ + q) * 8 * BK),
-                                       16, 0, 0);
+      if (part < 0 || q * (BK / 16) / DQ == part)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(A + a_src[q] + k0),
+                                         (__attribute__((address_space(3))) void*)(as + (wave * AQ + q) * RPB * BK),
+                                         16, 0, 0);
 #pragma unroll
     for (int q = 0; q < BQ; ++q)
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(W + b_src[q] + k0),
-                                       (__attribute__((address_space(3))) void*)(bs + (wave * BQ + q) * 8 * BK),
-                                       16, 0, 0);
+      if (part < 0 || (AQ + q) * (BK / 16) / DQ == part)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(W + b_src[q] + k0),
+                                         (__attribute__((address_space(3))) void*)(bs + (wave * BQ + q) * RPB * BK),
+                                         16, 0, 0);
   };
   // fragment rows of this lane and their swizzle
   const int lr = lane & 31, lh = lane >> 5;
-  auto compute = [&](int buf) {
+  // MFMAs over stage buf; with SPREAD and WI the DMA of k-tile nkt into stage
+  // nbuf is issued a part per 16-wide k step
+  auto compute = [&](int buf, int nkt, int nbuf, auto wi) {
     const bf16* as = smem + buf * STAGE;
     const bf16* bs = as + BM * BK;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
+      if constexpr (SPREAD && decltype(wi)::value) issue(nkt, nbuf, ks);
       const int c = ks * 2 + lh;           // logical 16-byte chunk of this lane
       bf16x8 fa[FM], fb[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int row = wm * TM + i * 32 + lr;
-        fa[i] = *(const bf16x8*)(as + row * BK + ((c ^ swz(row)) * 8));
+        fa[i] = *(const bf16x8*)(as + row * BK + ((c ^ swz<BK>(row)) * 8));
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int row = wn * TN + j * 32 + lr;
-        fb[j] = *(const bf16x8*)(bs + row * BK + ((c ^ swz(row)) * 8));
+        fb[j] = *(const bf16x8*)(bs + row * BK + ((c ^ swz<BK>(row)) * 8));
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
@@ -462,13 +486,31 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restric
     }
   }
   const int KT = K / BK;
-  issue(0, 0);
-  for (int kt = 0; kt < KT; ++kt) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");    // this wave's DMA of tile kt has landed
-    __syncthreads();                                     // everyone's has; tile kt-1 is retired
-    if (kt + 1 < KT) issue(kt + 1, (kt + 1) & 1);
-    compute(kt & 1);
-  }
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t)
+    if (t < KT) issue(t, t, -1);
+  // one k-tile: tiles kt+1 .. kt+NS-2 may stay in flight; tile kt must have
+  // landed in every wave, and every wave must be done reading tile kt-1.  WI:
+  // k-tile kt+NS-1 exists and its DMA goes out during this tile's MFMAs.
+  auto step = [&](int kt, auto wi) {
+    const int ahead = min(NS - 2, KT - 1 - kt);
+    if constexpr (NS >= 4) {
+      if (ahead >= 2) wait_vm_barrier<DQ * 2>();
+      else if (ahead == 1) wait_vm_barrier<DQ>();
+      else wait_vm_barrier<0>();
+    } else if constexpr (NS == 3) {
+      if (ahead >= 1) wait_vm_barrier<DQ>();
+      else wait_vm_barrier<0>();
+    } else {
+      wait_vm_barrier<0>();
+    }
+    const int nkt = kt + NS - 1;
+    if constexpr (!SPREAD && decltype(wi)::value) issue(nkt, nkt % NS, -1);
+    compute(kt % NS, nkt, nkt % NS, wi);
+  };
+  int kt = 0;
+  for (; kt + NS - 1 < KT; ++kt) step(kt, std::true_type{});
+  for (; kt < KT; ++kt) step(kt, std::false_type{});
   __syncthreads();
 
   float* stg = (float*)smem;
@@ -494,6 +536,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restric
   }
 }
 
+template <int BM, int BN, int NW, int BK, int NS, bool SPREAD, int MODE>
+hipError_t launch_dma(hipStream_t s, const bf16* A, const bf16* W, int M, int N, int K, const Epi& E) {
+  const unsigned grid = (unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
+  gemm_dma_kernel<BM, BN, NW, BK, NS, SPREAD, MODE><<<grid, 64 * NW, 0, s>>>(A, W, M, N, K, E);
+  return hipGetLastError();
+}
+
 template <int MODE>
 hipError_t gemm_mfma_mode(hipStream_t s, const bf16* A, const bf16* W, int M, int N, int K, const Epi& E) {
   // pick the tile that minimises (rounds of resident workgroups) x (cost per
@@ -513,19 +562,8 @@ hipError_t gemm_mfma_mode(hipStream_t s, const bf16* A, const bf16* W, int M, in
       best = i;
     }
   }
-  if (K % 64 == 0) {
-    // direct-to-LDS kernels: 256 x 256 (8 waves) once there are enough tiles
-    // to occupy the CUs, 128 x 128 (4 waves, two workgroups per CU) otherwise
-    const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-    if (t256 >= 128) {
-      const unsigned grid = (unsigned)t256;
-      gemm_dma_kernel<256, 256, 8, MODE><<<grid, 512, 0, s>>>(A, W, M, N, K, E);
-    } else {
-      const unsigned grid = (unsigned)(((M + 127) / 128) * ((N + 127) / 128));
-      gemm_dma_kernel<128, 128, 4, MODE><<<grid, 256, 0, s>>>(A, W, M, N, K, E);
-    }
-    return hipGetLastError();
-  }
+  if (K % 64 == 0)   // direct-to-LDS, 256 x 256 tiles, DMA spread over the MFMAs
+    return launch_dma<256, 256, 8, 64, 2, true, MODE>(s, A, W, M, N, K, E);
   const int bm = opts[best].bm, bn = opts[best].bn;
   const unsigned grid = (unsigned)(((M + bm - 1) / bm) * ((N + bn - 1) / bn));
   if (best == 0)

@@ -86,6 +86,9 @@ struct AttnArgs {
 // attention_combine() call (so the two passes can be timed apart).
 hipError_t attention(hipStream_t s, bool bf, const AttnArgs& a, bool combine = true);
 hipError_t attention_combine(hipStream_t s, const AttnArgs& a);
+// Queries per attention workgroup and resident attention workgroups per CU.
+int attention_q_tile(bool bf, int hd);
+int attention_wg_per_cu(bool bf, int hd);
 // Split count that best fills `concurrent` resident workgroups for `units`
 // query tiles over `tiles` key tiles (1 .. max_split).
 int attention_pick_split(int units, int tiles, int max_split, int concurrent);

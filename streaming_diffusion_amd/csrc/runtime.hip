@@ -59,7 +59,7 @@ struct sd_stream {
   int attn_split_max = 1;
   float* part_o = nullptr;
   float2* part_ml = nullptr;
-  int concurrent_wg = 512;      // resident attention workgroups (2 per CU)
+  int cus = 256;                // compute units of the device
   size_t ws_used = 0;
   // host state
   std::vector<FrameRec> frames;
@@ -325,7 +325,7 @@ sd_status sd_stream_create(const sd_stream_config* cfg, const sd_weights* w, voi
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
-      s->concurrent_wg = 2 * cus;
+      s->cus = cus;
   }
   // zero the caches (padding keys must stay finite) and upload RoPE tables
   std::vector<float2> rt, rh, rw;
@@ -586,8 +586,9 @@ sd_status sd_stream_step(sd_stream* s, float* out_latent, sd_step_info* info) {
       A.nseg = ns;
       if (s->attn_split_max > 1) {
         const int nk = ((sk.count + 7) & ~7) + sw.count + L;
-        A.nsplit = sdk::attention_pick_split(R * H * ((L + 127) / 128), (nk + 63) / 64, s->attn_split_max,
-                                             s->concurrent_wg);
+        const int qt = sdk::attention_q_tile(bf, hd);
+        A.nsplit = sdk::attention_pick_split(R * H * ((L + qt - 1) / qt), (nk + 63) / 64, s->attn_split_max,
+                                             s->cus * sdk::attention_wg_per_cu(bf, hd));
         A.part_o = s->part_o;
         A.part_ml = s->part_ml;
         A.part_so = (long long)s->Rmax * L * d;
