@@ -193,10 +193,32 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   // scores are masked.  An 8-key group that starts inside the valid range may
   // end in the zero-filled padding of the segment's storage (positions up to
   // the next multiple of 8 exist).
+  // per-lane byte offsets of this lane's K rows inside a contiguous tile
+  uint32_t koff[IK];
+#pragma unroll
+  for (int i = 0; i < IK; ++i) {
+    const int kr = wave * (KB / 4) + i * RK + lane / CKR;
+    koff[i] = (uint32_t)((kr * HD + ((lane % CKR) ^ chunk_swz<HD>(kr)) * 8) * 2);
+  }
   auto issue = [&](int t, int buf) {
     bf16* ks = smem + buf * STAGE;
     bf16* vs = ks + KT_EL;
     const TileRef f = tile_ref(t);
+    if (f.nvalid == KB && (!f.wrap || f.p0 + KB <= f.cap)) {
+      // whole tile of valid keys at contiguous positions: uniform base plus
+      // a per-lane 32-bit offset
+      const char* kb = (const char*)(f.kb + (int64_t)f.p0 * HD);
+      const char* vb = (const char*)(f.vb + f.p0);
+#pragma unroll
+      for (int i = 0; i < IK; ++i) dma16((const bf16*)(kb + koff[i]), ks + (wave * (KB / 4) + i * RK) * HD);
+#pragma unroll
+      for (int i = 0; i < IV; ++i) {
+        const int ve = wave * (HD / 4) + i * 8 + lane / 8;
+        const uint32_t vo = (uint32_t)(ve * f.cap + ((lane % 8) ^ chunk_swz<KB>(ve)) * 8) * 2u;
+        dma16((const bf16*)(vb + vo), vs + (wave * (HD / 4) + i * 8) * KB);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < IK; ++i) {
       const int kr = wave * (KB / 4) + i * RK + lane / CKR;
@@ -255,7 +277,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     }
     // accumulator q of half kt holds tile key kt*32 + 16*(q/8) + 8*half + (q%8)
     const int nvalid = tile_ref(tile).nvalid;
-    if (nvalid < KB) {
+    if (__builtin_expect(nvalid < KB, 0)) {
+      asm volatile("");      // keeps the masking out of line (a segment's last tile only)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
