@@ -61,6 +61,13 @@ SD_DEV int key_pos(const KvSeg& g, int u) {
   return g.wrap ? p % g.cap : p;
 }
 
+// One of three values, chosen by value (a conditional over lvalues would
+// select an address and force its operands into memory)
+template <typename T>
+SD_DEV T pick3(bool first, bool second, T x, T y, T z) {
+  return first ? x : (second ? y : z);
+}
+
 // ---------------------------------------------------------------------------
 // K and V^T tiles move from global memory straight into LDS
 // (global_load_lds_dwordx4: 16 bytes per lane, a wave instruction fills 1 KB,
@@ -68,13 +75,6 @@ SD_DEV int key_pos(const KvSeg& g, int u) {
 // 16-byte chunks XOR-swizzled by row (chunk c of row r at c ^ chunk_swz<W>(r),
 // W the row width in elements) so that the 16-lane passes of the MFMA
 // fragment reads fall on distinct banks.
-// one of three values, chosen by value (a conditional over lvalues would
-// select an address and force its operands into memory)
-template <typename T>
-SD_DEV T pick3(bool first, bool second, T x, T y, T z) {
-  return first ? x : (second ? y : z);
-}
-
 template <int W>
 SD_DEV int chunk_swz(int row) {
   return (row / (128 / W)) & (W / 8 - 1);
@@ -305,17 +305,26 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
       m_run = m_new;
     }
     const float moff = m_run == -INFINITY ? 0.f : -m_run * sl2;
-    float psum = 0.f;
     bf16x8 pb[4];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][q], sl2, moff));   // v_exp_f32: tiny results flush to 0
-        psum += p;
-        pb[kt * 2 + (q >> 3)][q & 7] = (bf16)p;
-      }
-    l_run += psum;
+      for (int q = 0; q < 16; ++q)     // v_exp_f32: tiny results flush to 0
+        pb[kt * 2 + (q >> 3)][q & 7] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[kt][q], sl2, moff));
+    // the row sum of the bf16 probabilities (the values the PV product
+    // uses), two at a time with v_dot2c_f32_bf16 against (1, 1)
+    {
+      const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+      float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 8; i += 4) {
+          ps0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[kb][i], pb[kb][i + 1]}, ones, ps0, false);
+          ps1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[kb][i + 2], pb[kb][i + 3]}, ones, ps1, false);
+        }
+      l_run += ps0 + ps1;
+    }
     // O^T += V^T P^T over 4 key blocks of 16
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
