@@ -513,27 +513,43 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restric
   for (; kt < KT; ++kt) step(kt, std::false_type{});
   __syncthreads();
 
+  // epilogue in 64-row strips staged through LDS; a strip gathers the
+  // 32-row fragment rows of whichever waves hold them (TM may be 96)
   float* stg = (float*)smem;
-  constexpr int SPW = TM / 64;
 #pragma unroll
   for (int s = 0; s < BM / 64; ++s) {
-    if (wm == s / SPW) {
-      const int i0 = (s % SPW) * 2;
 #pragma unroll
-      for (int ii = 0; ii < 2; ++ii)
+    for (int i = 0; i < FM; ++i) {
+      const int rb = wm * TM + i * 32;
+      if (rb / 64 == s) {
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
           for (int q = 0; q < 16; ++q) {
-            const int row = ii * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+            const int row = rb % 64 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
             const int col = wn * TN + j * 32 + (lane & 31);
-            stg[row * LC + col] = acc[i0 + ii][j][q];
+            stg[row * LC + col] = acc[i][j][q];
           }
+      }
     }
     __syncthreads();
     epi_strip<BN, NT, MODE>(E, stg, LC, m0 + s * 64, n0, M, N, tid, t0s);
     __syncthreads();
   }
+}
+
+// compute units of the current device (queried once; 256 on MI355X)
+static int device_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  return cus;
 }
 
 template <int BM, int BN, int NW, int BK, int NS, bool SPREAD, int MODE>
@@ -562,8 +578,18 @@ hipError_t gemm_mfma_mode(hipStream_t s, const bf16* A, const bf16* W, int M, in
       best = i;
     }
   }
-  if (K % 64 == 0)   // direct-to-LDS, 256 x 256 tiles, DMA spread over the MFMAs
+  if (K % 64 == 0) {
+    // direct-to-LDS, DMA spread over the MFMAs, one workgroup per CU: 256 x 256
+    // or 192 x 256 tiles, whichever needs the smaller (rounds of resident
+    // tiles) x (tile area); 192-row tiles fill more CUs when the 256-row
+    // grid leaves many idle (N = 1536: 150 vs 198 tiles on 256 CUs)
+    const int64_t cus = device_cus();
+    const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+    const int64_t t192 = (int64_t)((M + 191) / 192) * ((N + 255) / 256);
+    const int64_t c256 = (t256 + cus - 1) / cus * 256, c192 = (t192 + cus - 1) / cus * 192;
+    if (c192 < c256) return launch_dma<192, 256, 8, 64, 2, true, MODE>(s, A, W, M, N, K, E);
     return launch_dma<256, 256, 8, 64, 2, true, MODE>(s, A, W, M, N, K, E);
+  }
   const int bm = opts[best].bm, bn = opts[best].bn;
   const unsigned grid = (unsigned)(((M + bm - 1) / bm) * ((N + bn - 1) / bn));
   if (best == 0)

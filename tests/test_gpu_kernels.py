@@ -26,7 +26,7 @@ def lib():
 
 
 # ------------------------------------------------------------------ GEMM
-@pytest.mark.parametrize("M,N,K", [(300, 200, 136), (64, 64, 16), (1, 8, 8), (257, 129, 1040),
+@pytest.mark.parametrize("M,N,K", [(300, 200, 136), (64, 64, 16), (1, 8, 8), (257, 129, 1040), (400, 300, 128),
                                    (6240, 4608, 1536), (6240, 1536, 8960)])
 def test_gemm_bf16_exact_integers(lib, M, N, K):
     """Inputs k/16 with |k| <= 8 are exact in bf16 and every product and
