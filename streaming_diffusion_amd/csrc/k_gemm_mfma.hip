@@ -36,20 +36,30 @@ SD_DEV void store8_bf16(bf16* p, const float* v) {
   *(bf16x8*)p = o;
 }
 
-// RoPE angle (cos, sin) for head-dim element e (even) of token t of a row
-// whose temporal base is t0.
-SD_DEV float2 rope_cs(const Epi& E, int t0, int t, int e) {
-  const int hw = E.Hp * E.Wp;
-  const int f = t / hw, y = (t / E.Wp) % E.Hp, x = t % E.Wp;
-  if (e < E.dt) return E.rope_t[(t0 + f) * (E.dt >> 1) + (e >> 1)];
-  if (e < E.dt + E.dh) return E.rope_h[y * (E.dh >> 1) + ((e - E.dt) >> 1)];
-  return E.rope_w[x * ((E.hd - E.dt - E.dh) >> 1) + ((e - E.dt - E.dh) >> 1)];
+// Row table of a 64-row strip for the q/k/v scatters: (row << 20 | token),
+// and the token's offsets into the RoPE frame, row and column tables.
+template <int MODE>
+SD_DEV void epi_rows(const Epi& E, int4* rowtab, int m_base, int M, int tid, const int* t0s) {
+  if constexpr (MODE == EPI_QKV || MODE == EPI_CTXKV) {
+    if (tid < 64) {
+      const int m = min(m_base + tid, M - 1);
+      const int r = m / E.L, t = m - r * E.L;
+      int4 v = make_int4((r << 20) | t, 0, 0, 0);
+      if (E.rope) {
+        const int hw = E.Hp * E.Wp;
+        const int f = t / hw, y = (t / E.Wp) % E.Hp, x = t % E.Wp;
+        v.y = (t0s[r] + f) * (E.dt >> 1);
+        v.z = y * (E.dh >> 1);
+        v.w = x * ((E.hd - E.dt - E.dh) >> 1);
+      }
+      rowtab[tid] = v;
+    }
+  }
 }
 
-// Epilogue of one 64-row strip held in LDS (fp32, row pitch LC).
 template <int BN, int NT, int MODE>
 SD_DEV void epi_strip(const Epi& E, const float* stg, int LC, int m_base, int n0, int M, int N, int tid,
-                      const int* t0s) {
+                      const int4* rowtab) {
   constexpr int G = BN / 8;       // 8-column groups per row
   if constexpr (MODE == EPI_HEAD) {
     for (int idx = tid; idx < 64 * BN; idx += NT) {
@@ -67,61 +77,82 @@ SD_DEV void epi_strip(const Epi& E, const float* stg, int LC, int m_base, int n0
     return;
   }
   if constexpr (MODE == EPI_QKV || MODE == EPI_CTXKV) {
+    // Row facts come from the strip's row table, column facts are fixed per
+    // thread (the thread -> column mapping repeats every NT groups).
     // q and k sections: groups of 8 head-dim elements of one token
-    for (int g = tid; g < 64 * G; g += NT) {
-      const int row = g / G, cg = g % G;
-      const int m = m_base + row, n = n0 + cg * 8;
-      if (m >= M || n >= N) continue;
+    static_assert(NT % G == 0 && (64 * G) % NT == 0, "q/k thread mapping");
+    {
+      const int cg = tid % G, n = n0 + cg * 8;
       const int which = n / E.d;
       const int sec = (MODE == EPI_CTXKV) ? which + 1 : which;     // 0 q, 1 k, 2 v
-      if (sec == 2) continue;
-      const int nn = n - which * E.d, h = nn / E.hd, e0 = nn - h * E.hd;
-      const int r = m / E.L, t = m - r * E.L;
-      float v[8], b[8];
-      const float4* sp = (const float4*)(stg + row * LC + cg * 8);
-      const float4 v0 = sp[0], v1 = sp[1];
-      v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w; v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
-      load8_bf16((const bf16*)E.bias + n, b);
+      if (n < N && sec != 2) {
+        const int nn = n - which * E.d, h = nn / E.hd, e0 = nn - h * E.hd;
+        float b[8];
+        load8_bf16((const bf16*)E.bias + n, b);
+        // RoPE section (0 t, 1 h, 2 w) and in-section pair index of each pair
+        int tp[4], jp[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] += b[i];
-      if (E.rope) {
+        for (int p = 0; p < 4; ++p) {
+          const int e = e0 + 2 * p;
+          tp[p] = e < E.dt ? 0 : (e < E.dt + E.dh ? 1 : 2);
+          jp[p] = (tp[p] == 0 ? e : (tp[p] == 1 ? e - E.dt : e - E.dt - E.dh)) >> 1;
+        }
+        bf16* const dst = sec == 0 ? (bf16*)E.q : (bf16*)E.k;
+        const int dstride = sec == 0 ? E.L : E.kstride;
 #pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-          const float2 cs = rope_cs(E, t0s[r], t, e0 + i);
-          const float x0 = v[i], x1 = v[i + 1];
-          v[i] = x0 * cs.x - x1 * cs.y;
-          v[i + 1] = x0 * cs.y + x1 * cs.x;
+        for (int it = 0; it < 64 * G / NT; ++it) {
+          const int row = tid / G + it * (NT / G);
+          if (m_base + row >= M) continue;
+          const int4 ri = rowtab[row];
+          const int r = ri.x >> 20, t = ri.x & 0xFFFFF;
+          float v[8];
+          const float4* sp = (const float4*)(stg + row * LC + cg * 8);
+          const float4 v0 = sp[0], v1 = sp[1];
+          v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w; v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] += b[i];
+          if (E.rope) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              const float2 cs = tp[p] == 0 ? E.rope_t[ri.y + jp[p]]
+                                           : (tp[p] == 1 ? E.rope_h[ri.z + jp[p]] : E.rope_w[ri.w + jp[p]]);
+              const float x0 = v[2 * p], x1 = v[2 * p + 1];
+              v[2 * p] = x0 * cs.x - x1 * cs.y;
+              v[2 * p + 1] = x0 * cs.y + x1 * cs.x;
+            }
+          }
+          store8_bf16(dst + (((int64_t)r * E.H + h) * dstride + t) * E.hd + e0, v);
         }
       }
-      const int64_t rh = (int64_t)r * E.H + h;
-      if (sec == 0)
-        store8_bf16((bf16*)E.q + (rh * E.L + t) * E.hd + e0, v);
-      else
-        store8_bf16((bf16*)E.k + (rh * E.kstride + t) * E.hd + e0, v);
     }
     // v section: groups of 8 tokens of one head-dim element (transposed store)
-    for (int g = tid; g < 8 * BN; g += NT) {
-      const int col = g % BN, rg = g / BN;
-      const int m = m_base + rg * 8, n = n0 + col;
-      if (m >= M || n >= N) continue;
+    static_assert(NT % BN == 0 && (8 * BN) % NT == 0, "v thread mapping");
+    {
+      const int col = tid % BN, n = n0 + col;
       const int which = n / E.d;
       const int sec = (MODE == EPI_CTXKV) ? which + 1 : which;
-      if (sec != 2) continue;
-      const int nn = n - which * E.d, h = nn / E.hd, e = nn - h * E.hd;
-      const float bn = (float)((const bf16*)E.bias)[n];
-      const int r = m / E.L, t = m - r * E.L;
-      const int64_t rh = (int64_t)r * E.H + h;
-      bf16* dst = (bf16*)E.vt + (rh * E.hd + e) * E.kstride + t;
-      if (m + 8 <= M && t + 8 <= E.L) {
-        float v[8];
+      if (n < N && sec == 2) {
+        const int nn = n - which * E.d, h = nn / E.hd, e = nn - h * E.hd;
+        const float bn = (float)((const bf16*)E.bias)[n];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = stg[(rg * 8 + i) * LC + col] + bn;
-        store8_bf16(dst, v);
-      } else {
-        for (int i = 0; i < 8 && m + i < M; ++i) {
-          const int mi = m + i, ri = mi / E.L, ti = mi - ri * E.L;
-          bf16* di = (bf16*)E.vt + (((int64_t)ri * E.H + h) * E.hd + e) * E.kstride + ti;
-          *di = (bf16)(stg[(rg * 8 + i) * LC + col] + bn);
+        for (int it = 0; it < 8 * BN / NT; ++it) {
+          const int rg = tid / BN + it * (NT / BN);
+          const int m = m_base + rg * 8;
+          if (m >= M) continue;
+          const int4 ri = rowtab[rg * 8];
+          const int r = ri.x >> 20, t = ri.x & 0xFFFFF;
+          if (m + 8 <= M && t + 8 <= E.L) {
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = stg[(rg * 8 + i) * LC + col] + bn;
+            store8_bf16((bf16*)E.vt + (((int64_t)r * E.H + h) * E.hd + e) * E.kstride + t, v);
+          } else {
+            for (int i = 0; i < 8 && m + i < M; ++i) {
+              const int rx = rowtab[rg * 8 + i].x;
+              bf16* di = (bf16*)E.vt + (((int64_t)(rx >> 20) * E.H + h) * E.hd + e) * E.kstride + (rx & 0xFFFFF);
+              *di = (bf16)(stg[(rg * 8 + i) * LC + col] + bn);
+            }
+          }
         }
       }
     }
@@ -208,6 +239,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_kernel(const bf16* __restri
   static_assert(64 * LC * 4 <= 2 * STAGE * 2, "epilogue strip must fit in the stage buffers");
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * STAGE];
   __shared__ int t0s[SD_MAX_ROWS];     // per-row temporal RoPE base (read with a dynamic row index)
+  __shared__ int4 rowtab[64];          // per-strip row facts of the q/k/v scatters
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
@@ -350,8 +382,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_kernel(const bf16* __restri
             stg[row * LC + col] = acc[i0 + ii][j][q];
           }
     }
+    epi_rows<MODE>(E, rowtab, m0 + s * 64, M, tid, t0s);
     __syncthreads();
-    epi_strip<BN, NT, MODE>(E, stg, LC, m0 + s * 64, n0, M, N, tid, t0s);
+    epi_strip<BN, NT, MODE>(E, stg, LC, m0 + s * 64, n0, M, N, tid, rowtab);
     __syncthreads();
   }
 }
@@ -396,6 +429,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restric
   static_assert(64 * LC * 4 <= NS * STAGE * 2, "epilogue strip must fit in the stage buffers");
   __shared__ __attribute__((aligned(1024))) bf16 smem[NS * STAGE];
   __shared__ int t0s[SD_MAX_ROWS];
+  __shared__ int4 rowtab[64];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
@@ -532,8 +566,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restric
           }
       }
     }
+    epi_rows<MODE>(E, rowtab, m0 + s * 64, M, tid, t0s);
     __syncthreads();
-    epi_strip<BN, NT, MODE>(E, stg, LC, m0 + s * 64, n0, M, N, tid, t0s);
+    epi_strip<BN, NT, MODE>(E, stg, LC, m0 + s * 64, n0, M, N, tid, rowtab);
     __syncthreads();
   }
 }
