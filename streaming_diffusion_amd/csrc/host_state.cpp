@@ -24,6 +24,7 @@ int validate_config(const sd_stream_config& c, std::string* err) {
   const int hd = c.d_model / c.n_heads;
   if (hd % 8 || hd > 128 || hd < 16) return fail(err, SD_ERR_SHAPE, "head dim must be a multiple of 8 in [16, 128]");
   if (c.d_model % 64) return fail(err, SD_ERR_SHAPE, "d_model must be a multiple of 64");
+  if (c.d_model > 5120) return fail(err, SD_ERR_SHAPE, "d_model must be at most 5120");
   if (c.d_ffn < 8 || c.d_ffn % 64) return fail(err, SD_ERR_SHAPE, "d_ffn must be a positive multiple of 64");
   if (c.d_freq < 2 || c.d_freq % 8) return fail(err, SD_ERR_SHAPE, "d_freq must be a positive multiple of 8");
   if (c.ctx_len < 0 || c.ctx_len > 4096) return fail(err, SD_ERR_SHAPE, "ctx_len out of range");

@@ -104,9 +104,35 @@ hipError_t patchify(hipStream_t s, bool bf, const RowTable& rt, const float* sto
 }
 
 // ---------------------------------------------------------------------------
-// LayerNorm + adaLN modulation, one wave per token row.  Mean and variance
-// are two passes over the row (population variance); the row stays in cache.
+// LayerNorm + adaLN modulation, one wave per token row.  The row is read
+// once into registers (NV float4 per lane, d <= 256 NV); mean and variance
+// are two passes over the registers (population variance).  Shift / scale
+// vectors (per forward row, cache resident) load four at a time; outputs
+// store four at a time.
+constexpr int LN_MAXV = 20;     // largest NV: d up to 5120
+
 template <typename T>
+SD_DEV void store4(T* p, const float* o);
+template <>
+SD_DEV void store4<float>(float* p, const float* o) { *(float4*)p = make_float4(o[0], o[1], o[2], o[3]); }
+template <>
+SD_DEV void store4<bf16>(bf16* p, const float* o) {
+  bf16x4 v;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = (bf16)o[q];
+  *(bf16x4*)p = v;
+}
+SD_DEV void load4(const float* p, float* o) {
+  const float4 v = *(const float4*)p;
+  o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+}
+SD_DEV void load4(const bf16* p, float* o) {
+  const bf16x4 v = *(const bf16x4*)p;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) o[q] = (float)v[q];
+}
+
+template <typename T, int NV>
 __global__ __launch_bounds__(256) void ln_mod_kernel(const float* __restrict__ x, T* __restrict__ out, int M, int d,
                                                      int L, const float* __restrict__ mod, const T* __restrict__ blk,
                                                      int shift_off, int scale_off, int six_d, float eps) {
@@ -115,49 +141,74 @@ __global__ __launch_bounds__(256) void ln_mod_kernel(const float* __restrict__ x
   if (row >= M) return;
   const float4* xr = (const float4*)(x + (int64_t)row * d);
   const int nv = d >> 2;
+  float4 v[NV];
   float sum = 0.f;
-  for (int j = lane; j < nv; j += 64) {
-    const float4 v = xr[j];
-    sum += (v.x + v.y) + (v.z + v.w);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int j = lane + 64 * i;
+    v[i] = j < nv ? xr[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+    sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
   }
   const float mu = wave_sum(sum) / (float)d;
   float sq = 0.f;
-  for (int j = lane; j < nv; j += 64) {
-    const float4 v = xr[j];
-    const float a = v.x - mu, b = v.y - mu, c = v.z - mu, e = v.w - mu;
-    sq += (a * a + b * b) + (c * c + e * e);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    if (lane + 64 * i < nv) {
+      const float a = v[i].x - mu, b = v[i].y - mu, c = v[i].z - mu, e = v[i].w - mu;
+      sq += (a * a + b * b) + (c * c + e * e);
+    }
   }
   const float rstd = 1.0f / sqrtf(wave_sum(sq) / (float)d + eps);
   const int r = row / L;
   const float* mr = mod ? mod + (int64_t)r * six_d : nullptr;
   T* orow = out + (int64_t)row * d;
-  for (int j = lane; j < nv; j += 64) {
-    const float4 v = xr[j];
-    float o[4] = {(v.x - mu) * rstd, (v.y - mu) * rstd, (v.z - mu) * rstd, (v.w - mu) * rstd};
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int j = lane + 64 * i;
+    if (j >= nv) continue;
+    float o[4] = {(v[i].x - mu) * rstd, (v[i].y - mu) * rstd, (v[i].z - mu) * rstd, (v[i].w - mu) * rstd};
     if (mr) {
+      float sh[4], sc[4];
+      load4(mr + shift_off + 4 * j, sh);
+      load4(mr + scale_off + 4 * j, sc);
+      if (blk) {
+        float bs[4], bc[4];
+        load4(blk + shift_off + 4 * j, bs);
+        load4(blk + scale_off + 4 * j, bc);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = 4 * j + q;
-        const float sh = mr[shift_off + c] + (blk ? to_f(blk[shift_off + c]) : 0.f);
-        const float sc = mr[scale_off + c] + (blk ? to_f(blk[scale_off + c]) : 0.f);
-        o[q] = o[q] * (1.0f + sc) + sh;
+        for (int q = 0; q < 4; ++q) {
+          sh[q] += bs[q];
+          sc[q] += bc[q];
+        }
       }
-    }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) orow[4 * j + q] = from_f<T>(o[q]);
+      for (int q = 0; q < 4; ++q) o[q] = o[q] * (1.0f + sc[q]) + sh[q];
+    }
+    store4<T>(orow + 4 * j, o);
   }
 }
 
 hipError_t ln_mod(hipStream_t s, bool bf, const float* x, void* out, int M, int d, int L, const float* mod,
                   const void* blk, int shift_off, int scale_off, int six_d, float eps) {
   if (M == 0) return hipSuccess;
+  if ((d & 3) || d > 4 * 64 * LN_MAXV || (shift_off & 3) || (scale_off & 3) || (six_d & 3)) return hipErrorInvalidValue;
   const unsigned g = (unsigned)((M + 3) / 4);
-  if (bf)
-    ln_mod_kernel<bf16><<<g, 256, 0, s>>>(x, (bf16*)out, M, d, L, mod, (const bf16*)blk, shift_off, scale_off, six_d,
-                                          eps);
+#define SD_LN_LAUNCH(NV)                                                                                           \
+  do {                                                                                                             \
+    if (bf)                                                                                                        \
+      ln_mod_kernel<bf16, NV><<<g, 256, 0, s>>>(x, (bf16*)out, M, d, L, mod, (const bf16*)blk, shift_off, scale_off, \
+                                                six_d, eps);                                                       \
+    else                                                                                                           \
+      ln_mod_kernel<float, NV><<<g, 256, 0, s>>>(x, (float*)out, M, d, L, mod, (const float*)blk, shift_off,       \
+                                                 scale_off, six_d, eps);                                           \
+  } while (0)
+  if (d <= 1024)
+    SD_LN_LAUNCH(4);
+  else if (d <= 2048)
+    SD_LN_LAUNCH(8);
   else
-    ln_mod_kernel<float><<<g, 256, 0, s>>>(x, (float*)out, M, d, L, mod, (const float*)blk, shift_off, scale_off,
-                                           six_d, eps);
+    SD_LN_LAUNCH(LN_MAXV);
+#undef SD_LN_LAUNCH
   return hipGetLastError();
 }
 

@@ -84,6 +84,7 @@ def test_workload_configs_validate(lib, state, name):
     (dict(chunks_per_step=2), L.SD_ERR_ARG),
     (dict(cfg_type="onetime"), L.SD_ERR_ARG),        # tiny has no context
     (dict(latent_h=15), L.SD_ERR_SHAPE),
+    (dict(d_model=5184, n_heads=81), L.SD_ERR_SHAPE),  # beyond the register-resident LayerNorm rows
 ])
 def test_invalid_configs_are_rejected(lib, state, kw, code):
     c = cfg_struct("tiny", **kw)
