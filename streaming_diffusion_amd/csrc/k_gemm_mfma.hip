@@ -36,10 +36,14 @@ SD_DEV void store8_bf16(bf16* p, const float* v) {
   *(bf16x8*)p = o;
 }
 
-// Row table of a 64-row strip for the q/k/v scatters: (row << 20 | token),
-// and the token's offsets into the RoPE frame, row and column tables.
+// Row table of a 64-row strip: for the q/k/v scatters (row << 20 | token)
+// and the token's offsets into the RoPE frame, row and column tables; for
+// the gated residual the forward row of each token.
 template <int MODE>
 SD_DEV void epi_rows(const Epi& E, int4* rowtab, int m_base, int M, int tid, const int* t0s) {
+  if constexpr (MODE == EPI_GATE_RESID) {
+    if (tid < 64) rowtab[tid] = make_int4(min(m_base + tid, M - 1) / E.L, 0, 0, 0);
+  }
   if constexpr (MODE == EPI_QKV || MODE == EPI_CTXKV) {
     if (tid < 64) {
       const int m = min(m_base + tid, M - 1);
@@ -99,12 +103,27 @@ SD_DEV void epi_strip(const Epi& E, const float* stg, int LC, int m_base, int n0
         }
         bf16* const dst = sec == 0 ? (bf16*)E.q : (bf16*)E.k;
         const int dstride = sec == 0 ? E.L : E.kstride;
+        constexpr int IT = 64 * G / NT;
+        // phase 1: every (cos, sin) of the strip (table reads are not
+        // ordered behind the stores of phase 2)
+        float2 cs[IT][4];
+        if (E.rope) {
 #pragma unroll
-        for (int it = 0; it < 64 * G / NT; ++it) {
+          for (int it = 0; it < IT; ++it) {
+            const int4 ri = rowtab[tid / G + it * (NT / G)];
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+              cs[it][p] = tp[p] == 0 ? E.rope_t[ri.y + jp[p]]
+                                     : (tp[p] == 1 ? E.rope_h[ri.z + jp[p]] : E.rope_w[ri.w + jp[p]]);
+          }
+        }
+        // phase 2: rotate and store
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
           const int row = tid / G + it * (NT / G);
           if (m_base + row >= M) continue;
-          const int4 ri = rowtab[row];
-          const int r = ri.x >> 20, t = ri.x & 0xFFFFF;
+          const int rt = rowtab[row].x;
+          const int r = rt >> 20, t = rt & 0xFFFFF;
           float v[8];
           const float4* sp = (const float4*)(stg + row * LC + cg * 8);
           const float4 v0 = sp[0], v1 = sp[1];
@@ -114,11 +133,9 @@ SD_DEV void epi_strip(const Epi& E, const float* stg, int LC, int m_base, int n0
           if (E.rope) {
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
-              const float2 cs = tp[p] == 0 ? E.rope_t[ri.y + jp[p]]
-                                           : (tp[p] == 1 ? E.rope_h[ri.z + jp[p]] : E.rope_w[ri.w + jp[p]]);
               const float x0 = v[2 * p], x1 = v[2 * p + 1];
-              v[2 * p] = x0 * cs.x - x1 * cs.y;
-              v[2 * p + 1] = x0 * cs.y + x1 * cs.x;
+              v[2 * p] = x0 * cs[it][p].x - x1 * cs[it][p].y;
+              v[2 * p + 1] = x0 * cs[it][p].y + x1 * cs[it][p].x;
             }
           }
           store8_bf16(dst + (((int64_t)r * E.H + h) * dstride + t) * E.hd + e0, v);
@@ -158,13 +175,19 @@ SD_DEV void epi_strip(const Epi& E, const float* stg, int LC, int m_base, int n0
     }
     return;
   }
-  // row-major modes: groups of 8 consecutive columns of one row
-  for (int g = tid; g < 64 * G; g += NT) {
-    const int row = g / G, cg = g % G;
-    const int m = m_base + row, n = n0 + cg * 8;
-    if (m >= M || n >= N) continue;
-    if (n + 8 > N || (E.ldo & 7) || (N & 7)) {
-      // ragged right edge or unaligned rows: element by element
+  // row-major modes: groups of 8 consecutive columns of one row.  A thread's
+  // columns are fixed (bias and block gate load once); all global loads of
+  // the strip are issued before any store, since a store to the residual
+  // would otherwise order the next group's load behind it.
+  static_assert(NT % G == 0 && (64 * G) % NT == 0, "row-major thread mapping");
+  constexpr int IT = 64 * G / NT;
+  const int cg = tid % G, n = n0 + cg * 8;
+  if (n >= N) return;
+  if (n + 8 > N || (E.ldo & 7) || (N & 7)) {
+    // ragged right edge or unaligned rows: element by element
+    for (int it = 0; it < IT; ++it) {
+      const int row = tid / G + it * (NT / G), m = m_base + row;
+      if (m >= M) continue;
       for (int i = 0; i < 8 && n + i < N; ++i) {
         float v = stg[row * LC + cg * 8 + i] + (E.bias ? (float)((const bf16*)E.bias)[n + i] : 0.f);
         if constexpr (MODE == EPI_STORE) {
@@ -182,17 +205,44 @@ SD_DEV void epi_strip(const Epi& E, const float* stg, int LC, int m_base, int n0
           E.resid[(int64_t)m * N + n + i] += v;
         }
       }
-      continue;
     }
-    float v[8], b[8];
+    return;
+  }
+  float b[8];
+  if (E.bias) {
+    load8_bf16((const bf16*)E.bias + n, b);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) b[i] = 0.f;
+  }
+  constexpr bool RES = MODE == EPI_RESID || MODE == EPI_GATE_RESID;
+  float gb[8];
+  if constexpr (MODE == EPI_GATE_RESID) load8_bf16((const bf16*)E.blk + E.gate_off + n, gb);
+  float4 rin[IT][2], gin[IT][2];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int row = tid / G + it * (NT / G), m = m_base + row;
+    if (m >= M) continue;
+    if constexpr (RES) {
+      const float4* o = (const float4*)(E.resid + (int64_t)m * N + n);
+      rin[it][0] = o[0];
+      rin[it][1] = o[1];
+    }
+    if constexpr (MODE == EPI_GATE_RESID) {
+      const float4* gm = (const float4*)(E.mod + (int64_t)rowtab[row].x * E.six_d + E.gate_off + n);
+      gin[it][0] = gm[0];
+      gin[it][1] = gm[1];
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int row = tid / G + it * (NT / G), m = m_base + row;
+    if (m >= M) continue;
+    float v[8];
     const float4* sp = (const float4*)(stg + row * LC + cg * 8);
     const float4 v0 = sp[0], v1 = sp[1];
-    v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w; v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
-    if (E.bias) {
-      load8_bf16((const bf16*)E.bias + n, b);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] += b[i];
-    }
+    v[0] = v0.x + b[0]; v[1] = v0.y + b[1]; v[2] = v0.z + b[2]; v[3] = v0.w + b[3];
+    v[4] = v1.x + b[4]; v[5] = v1.y + b[5]; v[6] = v1.z + b[6]; v[7] = v1.w + b[7];
     if constexpr (MODE == EPI_STORE) {
       store8_bf16((bf16*)E.out + (int64_t)m * E.ldo + n, v);
     } else if constexpr (MODE == EPI_GELU) {
@@ -207,20 +257,16 @@ SD_DEV void epi_strip(const Epi& E, const float* stg, int LC, int m_base, int n0
       float4* o = (float4*)(E.resid + (int64_t)m * N + n);
       o[0] = make_float4(v[0], v[1], v[2], v[3]);
       o[1] = make_float4(v[4], v[5], v[6], v[7]);
-    } else if constexpr (MODE == EPI_RESID || MODE == EPI_GATE_RESID) {
+    } else if constexpr (RES) {
       if constexpr (MODE == EPI_GATE_RESID) {
-        const int r = m / E.L;
-        const float4* gm = (const float4*)(E.mod + (int64_t)r * E.six_d + E.gate_off + n);
-        const float4 g0 = gm[0], g1 = gm[1];
-        float gb[8];
-        load8_bf16((const bf16*)E.blk + E.gate_off + n, gb);
+        const float4 g0 = gin[it][0], g1 = gin[it][1];
         v[0] *= g0.x + gb[0]; v[1] *= g0.y + gb[1]; v[2] *= g0.z + gb[2]; v[3] *= g0.w + gb[3];
         v[4] *= g1.x + gb[4]; v[5] *= g1.y + gb[5]; v[6] *= g1.z + gb[6]; v[7] *= g1.w + gb[7];
       }
-      float4* o = (float4*)(E.resid + (int64_t)m * N + n);
-      float4 r0 = o[0], r1 = o[1];
+      float4 r0 = rin[it][0], r1 = rin[it][1];
       r0.x += v[0]; r0.y += v[1]; r0.z += v[2]; r0.w += v[3];
       r1.x += v[4]; r1.y += v[5]; r1.z += v[6]; r1.w += v[7];
+      float4* o = (float4*)(E.resid + (int64_t)m * N + n);
       o[0] = r0;
       o[1] = r1;
     }
@@ -427,9 +473,15 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restric
   static_assert(AQ >= 1 && BQ >= 1 && AQ * RPB * NW == BM && BQ * RPB * NW == BN, "tile shape");
   static_assert(NS >= 2 && NS <= 4 && DQ * (NS - 2) < 64, "stages");
   static_assert(64 * LC * 4 <= NS * STAGE * 2, "epilogue strip must fit in the stage buffers");
-  __shared__ __attribute__((aligned(1024))) bf16 smem[NS * STAGE];
-  __shared__ int t0s[SD_MAX_ROWS];
-  __shared__ int4 rowtab[64];
+  // one LDS block with the stage buffers at offset 0 (the row table and the
+  // per-row RoPE bases follow them): left to the compiler, the placement of
+  // the small arrays could move the stage buffers off offset 0, which costs
+  // up to half the throughput of the gated-residual kernels
+  constexpr int SMEM_BYTES = NS * STAGE * 2;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[SMEM_BYTES + 64 * 16 + SD_MAX_ROWS * 4];
+  bf16* const smem = (bf16*)lds;
+  int4* const rowtab = (int4*)(lds + SMEM_BYTES);
+  int* const t0s = (int*)(lds + SMEM_BYTES + 64 * 16);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
