@@ -21,7 +21,21 @@
 namespace sdk {
 
 // Launch-bound-checked helpers shared with the epilogue.
-SD_DEV float gelu_f(float v) { return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f)); }
+// GELU(v) = v * Phi(v) = 0.5 v (1 + erf(v / sqrt 2)), with erf from the
+// Abramowitz-Stegun rational approximation 7.1.26 (absolute error <= 1.5e-7,
+// far below the bf16 rounding of the stored result) and no branches:
+// erf(z) = 1 - e, e = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2),
+// t = 1 / (1 + p z), z = |v| / sqrt 2; for v < 0, 1 + erf = e exactly.
+SD_DEV float gelu_f(float v) {
+  const float z = fabsf(v) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+  float poly = fmaf(t, 1.061405429f, -1.453152027f);
+  poly = fmaf(t, poly, 1.421413741f);
+  poly = fmaf(t, poly, -0.284496736f);
+  poly = fmaf(t, poly, 0.254829592f);
+  const float e = poly * t * __builtin_amdgcn_exp2f(-z * z * 1.4426950408889634f);
+  return 0.5f * v * (v >= 0.f ? 2.0f - e : e);
+}
 
 SD_DEV void load8_bf16(const bf16* p, float* o) {
   const bf16x8 v = *(const bf16x8*)p;
