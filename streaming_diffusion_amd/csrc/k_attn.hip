@@ -453,42 +453,63 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Combine of split-KV partials: O = sum_s w_s O_s / sum_s w_s l_s with
-// w_s = 2^((m_s - max_s m_s) * scale * log2 e).  One thread per 4 head-dim
-// elements of one (token, head).
+// Combine of split partials: O = sum_s w_s O_s / sum_s w_s l_s with
+// w_s = 2^((m_s - max_s m_s) * scale * log2 e) (a split without keys has
+// m_s = -inf and weight 0).  One thread per 8 head-dim elements of one
+// (token, head); NS > 0 fixes the split count so every split's loads are in
+// flight together, NS = 0 loops over a.nsplit.  The host guarantees that
+// R * L * H * hd / 8 fits in 31 bits.
+template <int NS>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int hd4 = a.hd / 4;
-  const int64_t per_tok = (int64_t)a.H * hd4;
-  if (i >= (int64_t)a.R * a.L * per_tok) return;
-  const int64_t tok = i / per_tok;                // r_rel * L + t
-  const int h = (int)((i % per_tok) / hd4), e = (int)(i % hd4) * 4;
-  const int rr = (int)(tok / a.L), t = (int)(tok % a.L);
+  const int c8 = a.hd >> 3, per_tok = a.H * c8;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= a.R * a.L * per_tok) return;
+  const int tok = i / per_tok, rem = i - tok * per_tok;
+  const int h = rem / c8, e = (rem - h * c8) * 8;
+  const int rr = tok / a.L, t = tok - rr * a.L;
   const int r = a.r0 + rr;
   const float sl2 = a.scale * 1.4426950408889634f;
-  float mmax = -INFINITY;
-  for (int sp = 0; sp < a.nsplit; ++sp)
-    mmax = fmaxf(mmax, a.part_ml[sp * a.part_sml + ((int64_t)r * a.H + h) * a.L + t].x);
+  const float2* ml = a.part_ml + ((int64_t)r * a.H + h) * a.L + t;
+  const float* po = a.part_o + ((int64_t)r * a.L + t) * a.d + (int64_t)h * a.hd + e;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float l = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int sp = 0; sp < a.nsplit; ++sp) {
-    const float2 ml = a.part_ml[sp * a.part_sml + ((int64_t)r * a.H + h) * a.L + t];
-    if (ml.x == -INFINITY) continue;
-    const float w = exp2f((ml.x - mmax) * sl2);
-    l += w * ml.y;
-    const float4 v = *(const float4*)(a.part_o + sp * a.part_so + ((int64_t)r * a.L + t) * a.d + (int64_t)h * a.hd + e);
-    acc.x += w * v.x;
-    acc.y += w * v.y;
-    acc.z += w * v.z;
-    acc.w += w * v.w;
+  if constexpr (NS > 0) {
+    float2 m[NS];
+    float4 x0[NS], x1[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      m[s] = ml[s * a.part_sml];
+      x0[s] = *(const float4*)(po + s * a.part_so);
+      x1[s] = *(const float4*)(po + s * a.part_so + 4);
+    }
+    float mmax = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) mmax = fmaxf(mmax, m[s].x);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const float w = m[s].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m[s].x - mmax) * sl2);
+      l += w * m[s].y;
+      acc[0] += w * x0[s].x; acc[1] += w * x0[s].y; acc[2] += w * x0[s].z; acc[3] += w * x0[s].w;
+      acc[4] += w * x1[s].x; acc[5] += w * x1[s].y; acc[6] += w * x1[s].z; acc[7] += w * x1[s].w;
+    }
+  } else {
+    float mmax = -INFINITY;
+    for (int s = 0; s < a.nsplit; ++s) mmax = fmaxf(mmax, ml[s * a.part_sml].x);
+    for (int s = 0; s < a.nsplit; ++s) {
+      const float2 m = ml[s * a.part_sml];
+      if (m.x == -INFINITY) continue;
+      const float w = __builtin_amdgcn_exp2f((m.x - mmax) * sl2);
+      l += w * m.y;
+      const float4 x0 = *(const float4*)(po + s * a.part_so), x1 = *(const float4*)(po + s * a.part_so + 4);
+      acc[0] += w * x0.x; acc[1] += w * x0.y; acc[2] += w * x0.z; acc[3] += w * x0.w;
+      acc[4] += w * x1.x; acc[5] += w * x1.y; acc[6] += w * x1.z; acc[7] += w * x1.w;
+    }
   }
   const float inv = l > 0.f ? 1.0f / l : 0.f;
-  bf16x4 ov;
-  ov[0] = (bf16)(acc.x * inv);
-  ov[1] = (bf16)(acc.y * inv);
-  ov[2] = (bf16)(acc.z * inv);
-  ov[3] = (bf16)(acc.w * inv);
-  *(bf16x4*)((bf16*)a.o + ((int64_t)r * a.L + t) * a.d + (int64_t)h * a.hd + e) = ov;
+  bf16x8 ov;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ov[j] = (bf16)(acc[j] * inv);
+  *(bf16x8*)((bf16*)a.o + ((int64_t)r * a.L + t) * a.d + (int64_t)h * a.hd + e) = ov;
 }
 
 int attention_q_tile(bool bf, int hd) { return !bf ? 64 : 128; }
@@ -512,8 +533,19 @@ int attention_pick_split(int units, int tiles, int max_split, int concurrent) {
 
 hipError_t attention_combine(hipStream_t s, const AttnArgs& a) {
   if (a.nsplit <= 1 || a.R == 0 || a.L == 0) return hipSuccess;
-  const int64_t n = (int64_t)a.R * a.L * a.H * (a.hd / 4);
-  attn_combine_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a);
+  const int64_t n = (int64_t)a.R * a.L * a.H * (a.hd / 8);
+  if (a.hd % 8 || n > 0x7fffffff) return hipErrorInvalidValue;
+  const unsigned g = (unsigned)((n + 255) / 256);
+  switch (a.nsplit) {
+    case 2: attn_combine_kernel<2><<<g, 256, 0, s>>>(a); break;
+    case 3: attn_combine_kernel<3><<<g, 256, 0, s>>>(a); break;
+    case 4: attn_combine_kernel<4><<<g, 256, 0, s>>>(a); break;
+    case 5: attn_combine_kernel<5><<<g, 256, 0, s>>>(a); break;
+    case 6: attn_combine_kernel<6><<<g, 256, 0, s>>>(a); break;
+    case 7: attn_combine_kernel<7><<<g, 256, 0, s>>>(a); break;
+    case 8: attn_combine_kernel<8><<<g, 256, 0, s>>>(a); break;
+    default: attn_combine_kernel<0><<<g, 256, 0, s>>>(a); break;
+  }
   return hipGetLastError();
 }
 

@@ -312,9 +312,53 @@ __global__ void kv_append_kernel(const T* __restrict__ kown, const T* __restrict
   }
 }
 
+// bf16 with every token range a multiple of 8 and L <= W: 16-byte chunks (8
+// head-dim elements of one K row, or 8 consecutive tokens of one V^T row), one
+// conditional wrap per chunk.  Chunk i < H*L*hd/8 is a K chunk, the rest V^T.
+__global__ void kv_append_vec_kernel(const bf16* __restrict__ kown, const bf16* __restrict__ vtown,
+                                     bf16* __restrict__ ringK, bf16* __restrict__ ringVT, int H, int hd, int L, int W,
+                                     int ptr, bf16* __restrict__ sinkK, bf16* __restrict__ sinkVT, int S8,
+                                     int sink_off, int Se) {
+  const int64_t nk = (int64_t)H * L * (hd / 8);
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= 2 * nk) return;
+  if (i < nk) {
+    const int c = (int)(i % (hd / 8));
+    const int64_t ht = i / (hd / 8);
+    const int h = (int)(ht / L), t = (int)(ht % L);
+    const bf16x8 v = *(const bf16x8*)(kown + ht * hd + c * 8);
+    if (W > 0) {
+      int p = ptr + t;
+      if (p >= W) p -= W;
+      *(bf16x8*)(ringK + ((int64_t)h * W + p) * hd + c * 8) = v;
+    }
+    if (sinkK && t < Se) *(bf16x8*)(sinkK + ((int64_t)h * S8 + sink_off + t) * hd + c * 8) = v;
+  } else {
+    i -= nk;
+    const int tc = (int)(i % (L / 8));
+    const int64_t he = i / (L / 8);          // h * hd + e
+    const int t = tc * 8;
+    const bf16x8 v = *(const bf16x8*)(vtown + he * L + t);
+    if (W > 0) {
+      int p = ptr + t;
+      if (p >= W) p -= W;
+      *(bf16x8*)(ringVT + he * W + p) = v;
+    }
+    if (sinkVT && t < Se) *(bf16x8*)(sinkVT + he * S8 + sink_off + t) = v;
+  }
+}
+
 hipError_t kv_append(hipStream_t s, bool bf, const void* kown, const void* vtown, void* ringK, void* ringVT, int H,
                      int hd, int L, int W, int ptr, void* sinkK, void* sinkVT, int S8, int sink_off, int Se) {
   const int64_t n = (int64_t)H * L * hd;
+  if (bf && (hd % 8) == 0 && (L % 8) == 0 && (W % 8) == 0 && (ptr % 8) == 0 && ptr < (W > 0 ? W : 1) && (W == 0 || L <= W) &&
+      (!sinkK || ((S8 % 8) == 0 && (sink_off % 8) == 0 && (Se % 8) == 0))) {
+    const int64_t chunks = 2 * (n / 8);
+    kv_append_vec_kernel<<<grid1(chunks, 256), 256, 0, s>>>((const bf16*)kown, (const bf16*)vtown, (bf16*)ringK,
+                                                             (bf16*)ringVT, H, hd, L, W, ptr, (bf16*)sinkK,
+                                                             (bf16*)sinkVT, S8, sink_off, Se);
+    return hipGetLastError();
+  }
   if (bf)
     kv_append_kernel<bf16><<<grid1(n, 256), 256, 0, s>>>((const bf16*)kown, (const bf16*)vtown, (bf16*)ringK,
                                                          (bf16*)ringVT, H, hd, L, W, ptr, (bf16*)sinkK,
