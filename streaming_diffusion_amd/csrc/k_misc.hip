@@ -232,54 +232,104 @@ hipError_t temb_embed(hipStream_t s, const RowTable& rt, float* out, int d_freq)
 }
 
 // ---------------------------------------------------------------------------
-// Small-batch GEMV: the weight matrix is streamed once for all R rows.  One
-// wave per output feature, 8 weights (16 B bf16 / 32 B fp32) per lane per load.
+// Small-batch GEMV y[r][n] = act(x[r] . W[n] + b[n]) for all R rows, the
+// weight matrix streamed from HBM once.  Each wave owns GN consecutive
+// output features: per iteration every lane loads 8 weights (16 B bf16) of
+// each of the GN weight rows, so GN independent loads are in flight, and
+// applies them to the R input rows (read once per iteration, shared by the
+// GN features, cache resident).  RB >= R bounds the row loop at compile time.
 template <typename T>
+SD_DEV void load8(const T* p, float* w);
+template <>
+SD_DEV void load8<bf16>(const bf16* p, float* w) {
+  const bf16x8 v = *(const bf16x8*)p;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) w[q] = (float)v[q];
+}
+template <>
+SD_DEV void load8<float>(const float* p, float* w) {
+  const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+  w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+  w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+}
+
+constexpr int GEMV_GN = 4;
+
+template <typename T, int RB>
 __global__ __launch_bounds__(256) void gemv_kernel(const float* __restrict__ x, const T* __restrict__ W,
                                                    const T* __restrict__ bias, float* __restrict__ y, int R, int N,
                                                    int K, int act) {
+  constexpr int GN = GEMV_GN;
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nw = gridDim.x * 4;
   const int K8 = K >> 3;
-  for (int n = wave; n < N; n += nw) {
-    float acc[SD_MAX_ROWS];
+  for (int n0 = wave * GN; n0 < N; n0 += nw * GN) {
+    float acc[GN][RB];
 #pragma unroll
-    for (int r = 0; r < SD_MAX_ROWS; ++r) acc[r] = 0.f;
-    const T* wr = W + (int64_t)n * K;
+    for (int g = 0; g < GN; ++g)
+#pragma unroll
+      for (int r = 0; r < RB; ++r) acc[g][r] = 0.f;
+#pragma unroll 4
     for (int c = lane; c < K8; c += 64) {
-      float w[8];
+      float w[GN][8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) w[q] = to_f(wr[8 * c + q]);
+      for (int g = 0; g < GN; ++g) {
+        const int n = min(n0 + g, N - 1);      // a tail group repeats the last feature (not stored)
+        load8<T>(W + (int64_t)n * K + 8 * c, w[g]);
+      }
 #pragma unroll
-      for (int r = 0; r < SD_MAX_ROWS; ++r) {
+      for (int r = 0; r < RB; ++r) {
         if (r < R) {
           const float4* xr = (const float4*)(x + (int64_t)r * K + 8 * c);
           const float4 a = xr[0], b = xr[1];
-          acc[r] += w[0] * a.x + w[1] * a.y + w[2] * a.z + w[3] * a.w + w[4] * b.x + w[5] * b.y + w[6] * b.z +
-                    w[7] * b.w;
+#pragma unroll
+          for (int g = 0; g < GN; ++g)
+            acc[g][r] += w[g][0] * a.x + w[g][1] * a.y + w[g][2] * a.z + w[g][3] * a.w + w[g][4] * b.x +
+                         w[g][5] * b.y + w[g][6] * b.z + w[g][7] * b.w;
         }
       }
     }
-    const float bn = bias ? to_f(bias[n]) : 0.f;
 #pragma unroll
-    for (int r = 0; r < SD_MAX_ROWS; ++r) {
-      if (r < R) {
-        float v = wave_sum(acc[r]) + bn;
-        if (act == 1) v = v / (1.0f + expf(-v));
-        if (lane == 0) y[(int64_t)r * N + n] = v;
+    for (int g = 0; g < GN; ++g) {
+      const int n = n0 + g;
+      if (n >= N) break;
+      const float bn = bias ? to_f(bias[n]) : 0.f;
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        if (r < R) {
+          float v = wave_sum(acc[g][r]) + bn;
+          if (act == 1) v = v / (1.0f + expf(-v));
+          if (lane == 0) y[(int64_t)r * N + n] = v;
+        }
       }
     }
   }
 }
 
+template <typename T>
+static void launch_gemv(hipStream_t s, const float* x, const T* W, const T* b, float* y, int R, int N, int K, int act) {
+  const int groups = (N + GEMV_GN - 1) / GEMV_GN;
+  const int blocks = (groups + 3) / 4 < 2048 ? (groups + 3) / 4 : 2048;
+  if (R <= 2)
+    gemv_kernel<T, 2><<<blocks, 256, 0, s>>>(x, W, b, y, R, N, K, act);
+  else if (R <= 4)
+    gemv_kernel<T, 4><<<blocks, 256, 0, s>>>(x, W, b, y, R, N, K, act);
+  else if (R <= 8)
+    gemv_kernel<T, 8><<<blocks, 256, 0, s>>>(x, W, b, y, R, N, K, act);
+  else if (R <= 16)
+    gemv_kernel<T, 16><<<blocks, 256, 0, s>>>(x, W, b, y, R, N, K, act);
+  else
+    gemv_kernel<T, SD_MAX_ROWS><<<blocks, 256, 0, s>>>(x, W, b, y, R, N, K, act);
+}
+
 hipError_t gemv(hipStream_t s, bool bf, const float* x, const void* W, const void* b, float* y, int R, int N, int K,
                 int act) {
-  const int blocks = (N + 3) / 4 < 2048 ? (N + 3) / 4 : 2048;
+  if (R < 1 || R > SD_MAX_ROWS || N < 1 || K < 8 || (K & 7)) return hipErrorInvalidValue;
   if (bf)
-    gemv_kernel<bf16><<<blocks, 256, 0, s>>>(x, (const bf16*)W, (const bf16*)b, y, R, N, K, act);
+    launch_gemv<bf16>(s, x, (const bf16*)W, (const bf16*)b, y, R, N, K, act);
   else
-    gemv_kernel<float><<<blocks, 256, 0, s>>>(x, (const float*)W, (const float*)b, y, R, N, K, act);
+    launch_gemv<float>(s, x, (const float*)W, (const float*)b, y, R, N, K, act);
   return hipGetLastError();
 }
 
