@@ -76,6 +76,7 @@ class StepInfo:
     sink_entry: int
     sink_sim: float
     rope_next: int
+    n_out: int = 0            # frames emitted by the step (B when a slot group leaves)
 
 
 class OracleStream:
@@ -96,7 +97,7 @@ class OracleStream:
         if cfg.cfg_type == "onetime" and self.ctx_kv_neg is None and self.net is not None and cfg.ctx_len:
             raise ValueError("onetime-negative R-CFG needs a negative context")
         n = cfg.n_slots
-        self.slots: List[Optional[Frame]] = [None] * n
+        self.slots: List[Optional[List[Frame]]] = [None] * n      # slot groups of B frames
         self.pending: List[Frame] = []
         # SSF state
         self.ssf_ref = None
@@ -202,62 +203,72 @@ class OracleStream:
         return self.net.forward_row(fr.x, tau, fr.t0, snapshot, ctx_kv, collect=collect)
 
     def step(self):
+        """One Stream Batch step.  The B pending frames that entered together
+        form one slot group; all rows read the cache snapshot of the step
+        start; the group in the last slot leaves, in push order, each frame
+        appending its K/V and taking its sink decision in turn.  Returns
+        (out, info): out is None during warm-up, the emitted latent when
+        B = 1, else the [B][latent] stack in push order."""
         cfg = self.cfg
         n = cfg.n_slots
-        if len(self.pending) < cfg.chunks_per_step:
-            raise NotReady("no pending frame")
-        enter = self.pending.pop(0)
+        B = cfg.chunks_per_step
+        if len(self.pending) < B:
+            raise NotReady("fewer pending frames than chunks per step")
+        enter = [self.pending.pop(0) for _ in range(B)]
         self.slots = [enter] + self.slots[:n - 1]
         snapshot = None if self.identity else self.cache_snapshot()
-        rows = [(i, f) for i, f in enumerate(self.slots) if f is not None]
-        # onetime-negative: one extra row, the entering frame with the negative prompt
+        # forward rows: slot by slot, the frames of a slot in push order
+        rows = [(i, f) for i, grp in enumerate(self.slots) if grp is not None for f in grp]
+        # onetime-negative: one extra row per entering frame, with the negative prompt
+        neg_eps = []
         if cfg.cfg_type == "onetime":
-            tau0 = enter.taus[0]
-            a0, b0 = self.a[tau0], self.b[tau0]
-            if self.identity:
-                eps_neg = (enter.x - a0 * enter.x0) / b0
-            else:
-                eps_neg = self.net.forward_row(enter.x, tau0, enter.t0, snapshot, self.ctx_kv_neg)
-            enter.x0_star = guidance.predict_x0(enter.x, eps_neg, a0, b0)
-        results = {}
-        for i, f in rows:
-            results[i] = self._denoise(f, f.taus[i], snapshot, self.ctx_kv, collect=(i == n - 1))
+            for f in enter:
+                tau0 = f.taus[0]
+                a0, b0 = self.a[tau0], self.b[tau0]
+                if self.identity:
+                    eps_neg = (f.x - a0 * f.x0) / b0
+                else:
+                    eps_neg = self.net.forward_row(f.x, tau0, f.t0, snapshot, self.ctx_kv_neg)
+                f.x0_star = guidance.predict_x0(f.x, eps_neg, a0, b0)
+                neg_eps.append(eps_neg)
+        results = [self._denoise(f, f.taus[i], snapshot, self.ctx_kv, collect=(i == n - 1)) for i, f in rows]
         if not self.identity:
-            # denoiser outputs in forward row order (slots, then the negative row)
-            self.last_eps = [results[i][0] if i == n - 1 else results[i] for i, _ in rows]
-            if cfg.cfg_type == "onetime":
-                self.last_eps.append(eps_neg)
-        out = None
-        exiting = None
-        exit_kv = exit_hidden = None
-        for i, f in rows:
+            # denoiser outputs in forward row order (slots, then the negative rows)
+            self.last_eps = [res[0] if i == n - 1 else res for (i, _), res in zip(rows, results)]
+            self.last_eps.extend(neg_eps)
+        outs, exits = [], []
+        for (i, f), res in zip(rows, results):
             tau = f.taus[i]
             a, b = self.a[tau], self.b[tau]
             eps_p = guidance.virtual_residual(f.x, f.x0_star, a, b)
+            exit_kv = exit_hidden = None
             if self.identity:
                 eps_c = eps_p
             elif i == n - 1:
-                eps_c, exit_kv, exit_hidden = results[i]
+                eps_c, exit_kv, exit_hidden = res
             else:
-                eps_c = results[i]
+                eps_c = res
             eps_cfg = guidance.rcfg(eps_c, eps_p, cfg.gamma, cfg.delta)
             x0_hat = guidance.predict_x0(f.x, eps_cfg, a, b)
             if i < n - 1:
                 tn = f.taus[i + 1]
                 f.x = guidance.renoise(x0_hat, eps_cfg, self.a[tn], self.b[tn])
             else:
-                out = x0_hat
-                exiting = f
-        info = StepInfo(self.n_steps, exiting is not None, exiting.fid if exiting else -1, len(rows)
-                        + (1 if cfg.cfg_type == "onetime" else 0),
-                        0, 0, 0, False, -1, float("nan"), self.rope_p)
-        if exiting is not None:
+                outs.append(x0_hat)
+                exits.append((f, exit_kv, exit_hidden))
+        n_rows = len(rows) + len(neg_eps)
+        info = StepInfo(self.n_steps, bool(exits), exits[0][0].fid if exits else -1, n_rows,
+                        0, 0, 0, False, -1, float("nan"), self.rope_p, len(exits))
+        if exits:
             self.slots[n - 1] = None
             if not self.identity and not self.freeze:
-                self._append(exit_kv, exit_hidden, info)
+                for _, kv, hidden in exits:
+                    self._append(kv, hidden, info)
         info.kv_ptr, info.kv_valid, info.sink_count = self.kv_ptr, self.kv_valid, self.sink_count
         self.n_steps += 1
-        return out, info
+        if not outs:
+            return None, info
+        return (outs[0] if B == 1 else np.stack(outs)), info
 
     def _append(self, own_kv, hidden, info):
         cfg = self.cfg
@@ -272,9 +283,9 @@ class OracleStream:
                 j, sim, refresh = controls.sink_refresh_choice(h, self.sink_emb, cfg.sink_tau)
                 info.sink_sim = sim
                 info.sink_entry = j
+                info.sink_refreshed = bool(refresh)       # the last leaving chunk's decision
                 if refresh:
                     self._write_sink(j, own_kv, h)
-                    info.sink_refreshed = True
         if W > 0:
             for b in range(cfg.n_blocks):
                 k, v = own_kv[b]

@@ -191,3 +191,89 @@ def test_ssf_skip_cap_trace():
     h = np.zeros(cfg.ssf_shape, np.uint8); h[0, 0, 1] = 5
     r = [st3.push_frame(src.next(), nz.next(), f, 0.0).skipped for f in (g, h, g)]
     assert r == [False, False, False]           # cos = 0 -> p = 0, u = 0 is not < 0
+
+
+# ------------------------------------------------------------------ B > 1 chunks per step
+@pytest.mark.parametrize("B,t_index,cfg_type", [(2, (32, 45), "self"), (3, (0, 16, 32, 45), "self"),
+                                                (2, (0, 16, 32, 45), "onetime")])
+def test_identity_pipeline_emits_inputs_b_chunks(B, t_index, cfg_type):
+    """With B chunks per step the B frames of a group enter and leave
+    together: each leaves unchanged (identity denoiser, delta = 1), in push
+    order, n-1 steps after entering."""
+    cfg = get_config("tiny", t_index=t_index, cfg_type=cfg_type, gamma=2.1, delta=1.0, ssf_on=False,
+                     chunks_per_step=B)
+    st = OracleStream(cfg, None, identity_denoiser=True)
+    src, nz = gen.LatentSource(cfg), gen.NoiseSource(cfg)
+    n = cfg.n_slots
+    inputs, outs = [], []
+    for k in range(6):
+        for _ in range(B):
+            x0 = src.next()
+            inputs.append(x0)
+            st.push_frame(x0, nz.next())
+        out, info = st.step()
+        assert info.has_output == (k >= n - 1) and info.n_out == (B if k >= n - 1 else 0)
+        assert info.rows == B * min(k + 1, n) + (B if cfg_type == "onetime" else 0)
+        if out is not None:
+            assert out.shape == (B,) + inputs[0].shape
+            assert info.frame_id == (k - (n - 1)) * B
+            outs.extend(out)
+    assert len(outs) == (6 - (n - 1)) * B
+    for k, o in enumerate(outs):
+        assert np.allclose(o, inputs[k], atol=1e-11)
+
+
+def test_b_chunks_step_needs_b_pending_frames():
+    cfg = get_config("tiny", ssf_on=False, chunks_per_step=2)
+    st = OracleStream(cfg, None, identity_denoiser=True)
+    src, nz = gen.LatentSource(cfg), gen.NoiseSource(cfg)
+    st.push_frame(src.next(), nz.next())
+    with pytest.raises(NotReady):
+        st.step()
+
+
+def test_stream_batch_equals_sequential_b_chunks_live_cache():
+    """B = 2 with the cache live: each frame of a group, replayed alone
+    against the snapshots of the steps it spent in the pipeline, gives the
+    emitted latent bit for bit (frames of one group share their snapshots and
+    do not attend to each other)."""
+    cfg = small_cfg(t_index=(32, 45), chunks_per_step=2)
+    w = gen.make_weights(cfg)
+    st = OracleStream(cfg, w)
+    net = Denoiser(cfg, w)
+    a, b = schedule.sched_coeffs(cfg)
+    src, nz = gen.LatentSource(cfg), gen.NoiseSource(cfg)
+    frames, outs, snaps = [], [], []
+    for k in range(5):
+        for _ in range(2):
+            x0, e = src.next(), nz.next()
+            info = st.push_frame(x0, e)
+            frames.append((x0, e, info.t0, k))
+        snaps.append(st.cache_snapshot())
+        out, _ = st.step()
+        if out is not None:
+            outs.extend(out)
+    taus = schedule.taus_from_t_index(cfg)
+    n = cfg.n_slots
+    assert len(outs) == 8
+    for j, o in enumerate(outs):
+        x0, e, t0, k = frames[j]
+        ref = denoise_sequential(cfg, net, x0.astype(np.float64), e.astype(np.float64), taus, t0, a, b,
+                                 snapshots=[snaps[k + i] for i in range(n)])
+        assert np.array_equal(o, ref)
+
+
+def test_ring_pointer_and_sink_trace_b_chunks_overflowing_window():
+    """B = 2 chunks of L = 16 tokens leave per step into a 24-token window:
+    the two chunks append in order, so the window keeps the last 24 tokens
+    (ptr advances by 32 mod 24); the first leaving chunk captures the sink."""
+    cfg = small_cfg(t_index=(32, 45), window_tokens=24, chunks_per_step=2)
+    st = OracleStream(cfg, gen.make_weights(cfg))
+    src, nz = gen.LatentSource(cfg), gen.NoiseSource(cfg)
+    trace = []
+    for k in range(4):
+        for _ in range(2):
+            st.push_frame(src.next(), nz.next())
+        _, info = st.step()
+        trace.append((info.has_output, info.n_out, info.kv_ptr, info.kv_valid, info.sink_count))
+    assert trace == [(False, 0, 0, 0, 0), (True, 2, 8, 24, 1), (True, 2, 16, 24, 1), (True, 2, 0, 24, 1)]
