@@ -10,8 +10,11 @@ synthetic (seeded blob-motion latents, N(0,1) noise, N(0,0.02) weights) and
 resident in device memory before timing starts.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--workload NAME] [--n-slots n] [--chunks B]
+    python bench.py --workload video14b --sweep [--steps K]
 
-Prints one JSON line.
+Prints one JSON line (the sweep: one per (B, n) point, B chunks entering per
+step and n denoising slots, so B*n rows per forward).
 """
 from __future__ import annotations
 
@@ -36,6 +39,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=6)
     ap.add_argument("--workload", default="video13b")
     ap.add_argument("--n-slots", type=int, default=2)
+    ap.add_argument("--chunks", type=int, default=1, help="B: chunks entering (and leaving) per step")
+    ap.add_argument("--sweep", action="store_true",
+                    help="one JSON line per (B, n) in {1,2,4,8} x {1,2,4}, weights shared (no CPU baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-blocks", type=int, default=2, help="DiT blocks in the oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -111,45 +117,42 @@ def cpu_baseline(cfg, n_blocks_sample: int):
     }
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU sharding of this path is "
-              "described in DESIGN.md and not run.", file=sys.stderr)
-        sys.exit(2)
-
-    import numpy as np
+def measure(cfg, weights, steps: int, warmup: int, dev):
+    """Warm up (fills the slots, the window and the sink), time `steps` steps
+    with the inputs resident in device memory, then one untimed step with
+    every kernel kind timed.  Returns the bench record without the CPU leg."""
     import torch
 
-    from streaming_diffusion_amd.runner import StreamRunner, random_device_weights
-    from workloads import gen, get_config
+    from streaming_diffusion_amd.runner import StreamRunner
+    from workloads import gen
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    cfg = get_config(args.workload, t_index=slot_indices(args.n_slots))
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    weights = random_device_weights(cfg, seed=gen.SEED_WEIGHTS)
     run = StreamRunner(cfg, weights)
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     if cfg.ctx_len:
         ctx = torch.from_numpy(gen.make_context(cfg)).to(dev).to(tdt)
         ctx_neg = torch.from_numpy(gen.make_context(cfg, True)).to(dev).to(tdt) if cfg.cfg_type == "onetime" else None
         run.set_context(ctx, ctx_neg)
-    total = args.warmup + args.steps + 2
+    B = cfg.chunks_per_step
+    total = (warmup + steps + 2) * B
     src, nz = gen.LatentSource(cfg), gen.NoiseSource(cfg)
     xs = [torch.from_numpy(src.next()).to(dev) for _ in range(total)]
     ns = [torch.from_numpy(nz.next()).to(dev) for _ in range(total)]
-    out = torch.empty_like(xs[0])
+    out = run.out
     torch.cuda.synchronize()
-
-    # warm-up (fills the slots, the window and the sink); time to first frame
     k = 0
+
+    def push_group():
+        nonlocal k
+        for _ in range(B):
+            run.push(xs[k], ns[k])
+            k += 1
+
+    # warm-up; time to first frame
     ttff_ms = None
     t_first = time.perf_counter()
-    for _ in range(args.warmup):
-        run.push(xs[k], ns[k])
+    for _ in range(warmup):
+        push_group()
         info = run.step(out)
-        k += 1
         if info.has_output and ttff_ms is None:
             torch.cuda.synchronize()
             ttff_ms = (time.perf_counter() - t_first) * 1e3
@@ -161,32 +164,23 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     emitted = 0
-    for _ in range(args.steps):
-        run.push(xs[k], ns[k])
+    for _ in range(steps):
+        push_group()
         info = run.step(out)
-        emitted += info.has_output * cfg.latent_t
-        k += 1
+        emitted += info.n_out * cfg.latent_t
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     attn = run.profile_read().get("attn_self")
     elapsed = t1 - t0
-    ms_per_step = elapsed / args.steps * 1e3
+    ms_per_step = elapsed / steps * 1e3
 
     # untimed breakdown pass over every kernel kind (one step)
     run.profile(list(__import__("streaming_diffusion_amd._lib", fromlist=["PROF_KINDS"]).PROF_KINDS))
-    run.push(xs[k], ns[k])
+    push_group()
     run.step(out)
-    k += 1
     breakdown = run.profile_read()
     run.profile([])
-    if args.calibrate_copy:
-        n = args.calibrate_copy << 18          # float32 elements in MIB MiB
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    run.close()
 
     roofline = None
     if attn and attn["launches"]:
@@ -207,14 +201,14 @@ def main():
         bd[name] = {"ms": round(v["ms"], 3), "launches": v["launches"],
                     "tflops": round(v["flops"] / (v["ms"] * 1e-3) / 1e12, 1) if v["flops"] else None,
                     "gbs": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1)}
-
-    res = {
-        "metric": "denoised latent frames/s, one Stream Batch step per call (1.3B-shaped video DiT)",
+    return {
+        "metric": "denoised latent frames/s, one Stream Batch step per call (1.3B-shaped video DiT)"
+        if cfg.name == "video13b" else f"denoised latent frames/s, one Stream Batch step per call ({cfg.name})",
         "value": round(emitted / elapsed, 3),
         "unit": "frames/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 3),
         "higher_is_better": True,
         "scaling": "weak",
@@ -224,16 +218,55 @@ def main():
         "config": {"workload": f"{cfg.name}: {cfg.n_blocks} blocks d{cfg.d_model} h{cfg.n_heads} ffn{cfg.d_ffn}, "
                                f"chunk T={cfg.latent_t} {cfg.latent_c}x{cfg.latent_h}x{cfg.latent_w} "
                                f"({cfg.tokens} tokens), sink {cfg.sink_tokens} + window {cfg.window_tokens}, "
-                               f"n={cfg.n_slots} slots, R-CFG {cfg.cfg_type}, ctx {cfg.ctx_len}, motion on",
+                               f"n={cfg.n_slots} slots, B={B} chunks per step, R-CFG {cfg.cfg_type}, "
+                               f"ctx {cfg.ctx_len}, motion on",
                    "rows_per_step": cfg.rows_per_step, "tokens_per_row": cfg.tokens,
-                   "frames_per_step": cfg.latent_t, "parallelism": "single GPU"},
+                   "frames_per_step": B * cfg.latent_t, "parallelism": "single GPU"},
         "ttff_ms": round(ttff_ms, 2) if ttff_ms else None,
         "roofline": roofline,
         "breakdown_one_step": bd,
     }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU sharding of this path is "
+              "described in DESIGN.md and not run.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from streaming_diffusion_amd.runner import random_device_weights
+    from workloads import gen, get_config
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.sweep:
+        # weights do not depend on n or B
+        base = get_config(args.workload)
+        weights = random_device_weights(base, seed=gen.SEED_WEIGHTS)
+        for n in (1, 2, 4):
+            for B in (1, 2, 4, 8):
+                cfg = get_config(args.workload, t_index=slot_indices(n), chunks_per_step=B)
+                res = measure(cfg, weights, args.steps, max(args.warmup, n + 1), dev)
+                res["config"]["sweep"] = {"B": B, "n": n}
+                print(json.dumps(res), flush=True)
+        return
+    cfg = get_config(args.workload, t_index=slot_indices(args.n_slots), chunks_per_step=args.chunks)
+    weights = random_device_weights(cfg, seed=gen.SEED_WEIGHTS)
+    res = measure(cfg, weights, args.steps, args.warmup, dev)
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 18          # float32 elements in MIB MiB
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_blocks)
-    run.close()
     print(json.dumps(res))
 
 

@@ -50,6 +50,7 @@ extern "C" {
 #define SD_ABI_VERSION 1
 #define SD_MAX_SLOTS 8       /* n, denoising steps in flight */
 #define SD_MAX_ROWS 40       /* rows per forward: B*n (+B for onetime-negative) */
+#define SD_MAX_CHUNKS 8      /* chunks per step (B) */
 #define SD_MAX_SINK 8        /* sink entries M */
 
 typedef enum {
@@ -80,7 +81,8 @@ typedef struct {
   /* stream batch */
   int32_t n_slots;                 /* n = number of denoising steps in flight */
   int32_t t_index[SD_MAX_SLOTS];   /* 50-step grid index per slot: tau = 999 - 20 k */
-  int32_t chunks_per_step;         /* B; this version supports 1 */
+  int32_t chunks_per_step;         /* B in [1, SD_MAX_CHUNKS]: chunks that enter (and leave)
+                                      together; B*n rows (+B for onetime R-CFG) <= SD_MAX_ROWS */
   int32_t cfg_type;                /* sd_cfg_type */
   double gamma, delta;             /* R-CFG guidance scale and residual weight */
   /* KV cache, in tokens */
@@ -145,6 +147,8 @@ typedef struct {
   int32_t kv_ptr, kv_valid;    /* ring write position and valid tokens after the step */
   int32_t sink_count;          /* filled sink entries after the step */
   int32_t rope_next;           /* next temporal RoPE base */
+  int32_t n_out;               /* frames emitted: B when a slot group leaves, else 0;
+                                  frame_id is the first, the others follow in push order */
 } sd_step_info;
 
 /* Result of the last adaptive sink decision (read back on request). */
@@ -178,8 +182,12 @@ sd_status sd_stream_set_context(sd_stream* s, const void* ctx_pos, const void* c
 sd_status sd_stream_push_frame(sd_stream* s, const float* x0, const float* noise,
                                const void* ssf_frame, double u, sd_push_info* info);
 
-/* Advance the pipeline by one denoising step.  If a frame leaves, its clean
- * latent estimate is written to out_latent (device fp32 [T][C][H][W]). */
+/* Advance the pipeline by one denoising step (Stream Batch: the B oldest
+ * pending chunks enter slot 0, every slot advances one timestep, the slot
+ * group in the last slot leaves).  SD_ERR_NOT_READY while fewer than B chunks
+ * are pending.  When a group leaves, the clean latent estimates of its B
+ * chunks are written to out_latent (device fp32 [B][T][C][H][W], push order);
+ * out_latent may be NULL on steps that emit nothing. */
 sd_status sd_stream_step(sd_stream* s, float* out_latent, sd_step_info* info);
 
 /* Clear the ring, the sink and the RoPE counter (frames in flight continue). */

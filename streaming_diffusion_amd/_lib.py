@@ -62,7 +62,8 @@ class sd_push_info(C.Structure):
 
 class sd_step_info(C.Structure):
     _fields_ = [("step", C.c_int64), ("has_output", C.c_int32), ("rows", C.c_int32), ("frame_id", C.c_int64),
-                ("kv_ptr", C.c_int32), ("kv_valid", C.c_int32), ("sink_count", C.c_int32), ("rope_next", C.c_int32)]
+                ("kv_ptr", C.c_int32), ("kv_valid", C.c_int32), ("sink_count", C.c_int32), ("rope_next", C.c_int32),
+                ("n_out", C.c_int32)]
 
 
 class sd_sink_info(C.Structure):

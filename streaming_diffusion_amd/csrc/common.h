@@ -59,6 +59,8 @@ struct RowInfo {
   float a, b;         // sqrt(alpha_tau), sqrt(1 - alpha_tau)
   float an, bn;       // coefficients of the next slot's timestep
   float a0, b0;       // entry timestep coefficients (negative row)
+  int32_t oidx;       // last slot: position of the frame among the step's outputs
+  int32_t neg;        // entering frame with onetime R-CFG: its negative row, else -1
 };
 struct RowTable {
   int32_t R;

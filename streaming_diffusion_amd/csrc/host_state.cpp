@@ -29,7 +29,8 @@ int validate_config(const sd_stream_config& c, std::string* err) {
   if (c.d_freq < 2 || c.d_freq % 8) return fail(err, SD_ERR_SHAPE, "d_freq must be a positive multiple of 8");
   if (c.ctx_len < 0 || c.ctx_len > 4096) return fail(err, SD_ERR_SHAPE, "ctx_len out of range");
   if (c.n_slots < 1 || c.n_slots > SD_MAX_SLOTS) return fail(err, SD_ERR_ARG, "n_slots out of range");
-  if (c.chunks_per_step != 1) return fail(err, SD_ERR_ARG, "chunks_per_step must be 1 in this version");
+  if (c.chunks_per_step < 1 || c.chunks_per_step > SD_MAX_CHUNKS)
+    return fail(err, SD_ERR_ARG, "chunks_per_step must be in [1, 8]");
   if (c.cfg_type != SD_CFG_SELF && c.cfg_type != SD_CFG_ONETIME) return fail(err, SD_ERR_ARG, "unknown cfg_type");
   if (c.cfg_type == SD_CFG_ONETIME && c.ctx_len == 0)
     return fail(err, SD_ERR_ARG, "onetime-negative R-CFG needs a (negative) context");

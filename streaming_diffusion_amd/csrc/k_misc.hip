@@ -33,11 +33,12 @@ hipError_t entry_noise(hipStream_t s, const float* x0, const float* noise, float
 // Residual CFG (StreamDiffusion paper notes, section 2): virtual residual
 // noise eps' = (x - a x0*) / b, eps_cfg = delta eps' + gamma (eps_c - delta eps'),
 // then x0_hat = (x - b eps_cfg) / a and either re-noise to the next slot's
-// timestep or emit x0_hat.  For onetime-negative R-CFG the entering row first
-// turns the negative row's output into its x0* estimate.
+// timestep or emit x0_hat (to output position oidx of the step).  For
+// onetime-negative R-CFG an entering row first turns its negative row's output
+// into its x0* estimate.
 __global__ void rcfg_update_kernel(RowTable rt, float* __restrict__ store_x, float* __restrict__ store_x0s,
                                    const float* __restrict__ eps, float* __restrict__ out, int64_t lat, float gamma,
-                                   float delta, int neg_row) {
+                                   float delta) {
   const int r = blockIdx.y;
   const RowInfo ri = rt.r[r];
   if (ri.kind != 0) return;
@@ -46,8 +47,8 @@ __global__ void rcfg_update_kernel(RowTable rt, float* __restrict__ store_x, flo
   const int64_t off = (int64_t)ri.frame * lat + i;
   const float x = store_x[off];
   float x0s;
-  if (neg_row >= 0 && r == 0) {
-    const float en = eps[(int64_t)neg_row * lat + i];
+  if (ri.neg >= 0) {
+    const float en = eps[(int64_t)ri.neg * lat + i];
     x0s = (x - ri.b0 * en) / ri.a0;
     store_x0s[off] = x0s;
   } else {
@@ -58,16 +59,16 @@ __global__ void rcfg_update_kernel(RowTable rt, float* __restrict__ store_x, flo
   const float ecfg = delta * ep + gamma * (ec - delta * ep);
   const float x0h = (x - ri.b * ecfg) / ri.a;
   if (ri.last) {
-    out[i] = x0h;
+    out[(int64_t)ri.oidx * lat + i] = x0h;
   } else {
     store_x[off] = ri.an * x0h + ri.bn * ecfg;
   }
 }
 
 hipError_t rcfg_update(hipStream_t s, const RowTable& rt, float* store_x, float* store_x0s, const float* eps,
-                       float* out, int64_t lat, float gamma, float delta, int neg_row) {
+                       float* out, int64_t lat, float gamma, float delta) {
   dim3 g(grid1(lat, 256), rt.R);
-  rcfg_update_kernel<<<g, 256, 0, s>>>(rt, store_x, store_x0s, eps, out, lat, gamma, delta, neg_row);
+  rcfg_update_kernel<<<g, 256, 0, s>>>(rt, store_x, store_x0s, eps, out, lat, gamma, delta);
   return hipGetLastError();
 }
 

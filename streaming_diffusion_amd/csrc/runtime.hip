@@ -17,7 +17,8 @@ using sdk::KvSeg;
 
 namespace {
 
-constexpr int kPendingMax = 4;
+// pending chunks accepted before a step must run: at least 4, at least 2 B
+int pending_max(int B) { return B * 2 > 4 ? B * 2 : 4; }
 
 struct FrameRec {
   bool used = false;
@@ -39,6 +40,8 @@ struct sd_stream {
   int L = 0, d = 0, H = 0, hd = 0, F = 0, nb = 0, P = 0, Tn = 0, Hp = 0, Wp = 0;
   int64_t lat = 0, frame_elems = 0;
   int S = 0, S8 = 0, Se = 0, Ment = 0, Wt = 0, ctx8 = 0, Rmax = 0, n = 0, NF = 0;
+  int B = 1, pend_max = 4;        // chunks per step, pending-queue capacity
+  int Cc = 0;                     // sink-candidate tokens per (block, head) (B > 1 with a sink)
   int dt = 0, dh = 0, dw = 0, rope_pos = 0;
   std::vector<double> a, b;
   // device regions
@@ -51,6 +54,10 @@ struct sd_stream {
   void *xm = nullptr, *q = nullptr, *kown = nullptr, *vtown = nullptr, *ao = nullptr, *hid = nullptr;
   float* eps = nullptr;
   void *ringK = nullptr, *ringVT = nullptr, *sinkK = nullptr, *sinkVT = nullptr;
+  // B > 1: the first S_e tokens' K / V^T of each leaving chunk, staged at
+  // append time for its sink decision (the ring may already hold later
+  // chunks at those positions); [nb][H][Cc][hd] and [nb][H][hd][Cc]
+  void *candK = nullptr, *candVT = nullptr;
   void *ctxK = nullptr, *ctxVT = nullptr;
   float *sink_emb = nullptr, *sink_part = nullptr, *sink_sim = nullptr;
   int* sink_flag = nullptr;
@@ -64,7 +71,7 @@ struct sd_stream {
   // host state
   std::vector<FrameRec> frames;
   std::deque<int> pending;
-  int slots[SD_MAX_SLOTS];
+  int slots[SD_MAX_SLOTS * SD_MAX_CHUNKS];   // frame per (slot, lane), slot-major
   sd::Controls ctl;
   int64_t n_pushed = 0, n_steps = 0;
   int kv_ptr = 0, kv_valid = 0, sink_count = 0;
@@ -121,7 +128,10 @@ void dims(sd_stream* s) {
   s->ctx8 = (c.ctx_len + 7) & ~7;
   s->Rmax = sd::rows_max(c);
   s->n = c.n_slots;
-  s->NF = c.n_slots + kPendingMax + 1;
+  s->B = c.chunks_per_step;
+  s->pend_max = pending_max(s->B);
+  s->NF = c.n_slots * s->B + s->pend_max + 1;
+  s->Cc = (s->B > 1 && s->S > 0) ? ((s->B * s->Se + 7) & ~7) : 0;
   s->dh = 2 * (s->hd / 6);
   s->dw = s->dh;
   s->dt = s->hd - 2 * s->dh;
@@ -160,6 +170,10 @@ size_t carve(sd_stream* s, char* base) {
   s->ringVT = cv.take<void>((size_t)s->nb * s->H * s->Wt * s->hd * es);
   s->sinkK = cv.take<void>((size_t)s->nb * s->H * s->S8 * s->hd * es);
   s->sinkVT = cv.take<void>((size_t)s->nb * s->H * s->S8 * s->hd * es);
+  if (s->Cc > 0) {
+    s->candK = cv.take<void>((size_t)s->nb * s->H * s->Cc * s->hd * es);
+    s->candVT = cv.take<void>((size_t)s->nb * s->H * s->Cc * s->hd * es);
+  }
   if (c.ctx_len > 0) {
     s->ctxK = cv.take<void>((size_t)s->nb * nctx * s->H * s->ctx8 * s->hd * es);
     s->ctxVT = cv.take<void>((size_t)s->nb * nctx * s->H * s->ctx8 * s->hd * es);
@@ -318,7 +332,7 @@ sd_status sd_stream_create(const sd_stream_config* cfg, const sd_weights* w, voi
   s->ws_used = carve(s, (char*)workspace);
   sd::make_schedule(s->cfg, s->a, s->b);
   s->frames.assign(s->NF, FrameRec());
-  for (int i = 0; i < SD_MAX_SLOTS; ++i) s->slots[i] = -1;
+  for (int i = 0; i < SD_MAX_SLOTS * SD_MAX_CHUNKS; ++i) s->slots[i] = -1;
   s->ctl.s = s->cfg.s_max;
   std::memset(s->prof_acc, 0, sizeof(s->prof_acc));
   {
@@ -386,7 +400,7 @@ sd_status sd_stream_push_frame(sd_stream* s, const float* x0, const float* noise
   if (!x0 || !noise || !info) return set_err(s, SD_ERR_ARG, "null x0, noise or info");
   if (c.ssf_on && c.ssf_kind == SD_SSF_U8 && !ssf_frame) return set_err(s, SD_ERR_ARG, "ssf_frame is null");
   if (!(u >= 0.0 && u <= 1.0)) return set_err(s, SD_ERR_ARG, "u must be in [0, 1]");
-  if ((int)s->pending.size() >= kPendingMax) return set_err(s, SD_ERR_STATE, "pending queue full; call step()");
+  if ((int)s->pending.size() >= s->pend_max) return set_err(s, SD_ERR_STATE, "pending queue full; call step()");
   std::memset(info, 0, sizeof(*info));
   info->t0 = -1;
   info->frame_id = -1;
@@ -454,59 +468,77 @@ sd_status sd_stream_step(sd_stream* s, float* out_latent, sd_step_info* info) {
   if (!s) return SD_ERR_ARG;
   const sd_stream_config& c = s->cfg;
   if (!info) return set_err(s, SD_ERR_ARG, "info is null");
-  if (s->pending.empty()) return set_err(s, SD_ERR_NOT_READY, "no pending frame");
+  const int n = s->n, B = s->B;
+  if ((int)s->pending.size() < B) return set_err(s, SD_ERR_NOT_READY, "fewer pending chunks than chunks_per_step");
   if (!s->ctx_set) return set_err(s, SD_ERR_STATE, "set_context() must be called first");
-  const int n = s->n;
-  const bool will_exit = (n == 1) || (s->slots[n - 2] >= 0);
-  if (will_exit && !out_latent) return set_err(s, SD_ERR_ARG, "out_latent is null but a frame leaves this step");
+  const bool will_exit = (n == 1) || (s->slots[(n - 2) * B] >= 0);
+  if (will_exit && !out_latent) return set_err(s, SD_ERR_ARG, "out_latent is null but frames leave this step");
   std::memset(info, 0, sizeof(*info));
 
-  // ---- slot shift and row table
-  const int enter = s->pending.front();
-  s->pending.pop_front();
-  for (int i = n - 1; i >= 1; --i) s->slots[i] = s->slots[i - 1];
-  s->slots[0] = enter;
+  // ---- slot-group shift (the B oldest pending chunks enter slot 0) and row
+  // table: slot by slot, the chunks of a slot in push order
+  for (int i = n - 1; i >= 1; --i)
+    for (int k = 0; k < B; ++k) s->slots[i * B + k] = s->slots[(i - 1) * B + k];
+  for (int k = 0; k < B; ++k) {
+    s->slots[k] = s->pending.front();
+    s->pending.pop_front();
+  }
   RowTable rt;
   std::memset(&rt, 0, sizeof(rt));
-  int R = 0, r_exit = -1;
+  int R = 0, nexit = 0;
+  int exit_rows[SD_MAX_CHUNKS];
   for (int i = 0; i < n; ++i) {
-    const int f = s->slots[i];
-    if (f < 0) continue;
-    const FrameRec& fr = s->frames[f];
-    RowInfo& ri = rt.r[R];
-    ri.frame = f;
-    ri.tau = fr.taus[i];
-    ri.t0 = fr.t0;
-    ri.kind = 0;
-    ri.last = (i == n - 1);
-    ri.ctx = 0;
-    ri.a = (float)s->a[ri.tau];
-    ri.b = (float)s->b[ri.tau];
-    if (i + 1 < n) {
-      ri.an = (float)s->a[fr.taus[i + 1]];
-      ri.bn = (float)s->b[fr.taus[i + 1]];
+    for (int k = 0; k < B; ++k) {
+      const int f = s->slots[i * B + k];
+      if (f < 0) continue;
+      const FrameRec& fr = s->frames[f];
+      RowInfo& ri = rt.r[R];
+      ri.frame = f;
+      ri.tau = fr.taus[i];
+      ri.t0 = fr.t0;
+      ri.kind = 0;
+      ri.last = (i == n - 1);
+      ri.ctx = 0;
+      ri.a = (float)s->a[ri.tau];
+      ri.b = (float)s->b[ri.tau];
+      if (i + 1 < n) {
+        ri.an = (float)s->a[fr.taus[i + 1]];
+        ri.bn = (float)s->b[fr.taus[i + 1]];
+      }
+      ri.a0 = (float)s->a[fr.taus[0]];
+      ri.b0 = (float)s->b[fr.taus[0]];
+      ri.oidx = ri.last ? nexit : 0;
+      ri.neg = -1;
+      if (ri.last) exit_rows[nexit++] = R;
+      ++R;
     }
-    ri.a0 = (float)s->a[fr.taus[0]];
-    ri.b0 = (float)s->b[fr.taus[0]];
-    if (ri.last) r_exit = R;
-    ++R;
   }
   const int R_pos = R;
-  int neg_row = -1;
+  int nneg = 0;
   if (c.cfg_type == SD_CFG_ONETIME) {
-    rt.r[R] = rt.r[0];
-    rt.r[R].kind = 1;
-    rt.r[R].last = 0;
-    rt.r[R].ctx = 1;
-    neg_row = R;
-    ++R;
+    // one negative-prompt row per entering chunk (rows 0 .. B-1 are slot 0)
+    for (int k = 0; k < B; ++k) {
+      rt.r[R] = rt.r[k];
+      rt.r[R].kind = 1;
+      rt.r[R].last = 0;
+      rt.r[R].ctx = 1;
+      rt.r[R].neg = -1;
+      rt.r[k].neg = R;
+      ++R;
+      ++nneg;
+    }
   }
   rt.R = R;
   const int L = s->L, d = s->d, H = s->H, hd = s->hd, M = R * L;
   const size_t es = s->es;
   const bool bf = s->bf;
   hipStream_t st = s->st;
-  const bool capture = r_exit >= 0 && s->S > 0 && s->sink_count < s->Ment;
+  // sink plan of the leaving chunks, in push order: while entries are empty a
+  // chunk captures the next one; later chunks take a refresh decision
+  int cap_entry[SD_MAX_CHUNKS];
+  int sink_count_after = s->sink_count;
+  for (int k = 0; k < nexit; ++k)
+    cap_entry[k] = (s->S > 0 && sink_count_after < s->Ment) ? sink_count_after++ : -1;
   const int ptr_old = s->kv_ptr;
 
   // ---- conditioning: timestep embedding -> MLP -> SiLU(c) -> adaLN vectors
@@ -601,12 +633,30 @@ sd_status sd_stream_step(sd_stream* s, float* out_latent, sd_step_info* info) {
         PROF(SD_PROF_ATTN_COMBINE, 0.0, (double)A.nsplit * R * L * (d * 4.0 + H * 8.0) + (double)R * L * d * es,
              sdk::attention_combine(st, A));
     }
-    if (r_exit >= 0 && (s->Wt > 0 || capture)) {
-      const int64_t cb = (int64_t)b * H * s->S8 * hd;
-      PROF(SD_PROF_KV, 0.0, 4.0 * L * d * es, sdk::kv_append(st, bf, P(s->kown, r_exit * own_stride, es), P(s->vtown, r_exit * own_stride, es),
-                             Pm(s->ringK, (int64_t)b * H * s->Wt * hd, es), Pm(s->ringVT, (int64_t)b * H * s->Wt * hd, es),
-                             H, hd, L, s->Wt, s->kv_ptr, capture ? Pm(s->sinkK, cb, es) : nullptr,
-                             capture ? Pm(s->sinkVT, cb, es) : nullptr, s->S8, s->sink_count * s->Se, s->Se));
+    // the leaving chunks append their K / V^T in push order (ring positions
+    // ptr_old + k L); a capturing chunk also fills its sink entry, with B > 1
+    // a refresh candidate stages its first S_e tokens
+    for (int k = 0; k < nexit; ++k) {
+      void *dK = nullptr, *dVT = nullptr;
+      int dcap = s->S8, doff = 0;
+      if (cap_entry[k] >= 0) {
+        const int64_t cb = (int64_t)b * H * s->S8 * hd;
+        dK = Pm(s->sinkK, cb, es);
+        dVT = Pm(s->sinkVT, cb, es);
+        doff = cap_entry[k] * s->Se;
+      } else if (s->Cc > 0) {
+        const int64_t cb = (int64_t)b * H * s->Cc * hd;
+        dK = Pm(s->candK, cb, es);
+        dVT = Pm(s->candVT, cb, es);
+        dcap = s->Cc;
+        doff = k * s->Se;
+      }
+      if (s->Wt == 0 && !dK) continue;
+      const int pk = s->Wt > 0 ? (int)(((int64_t)ptr_old + (int64_t)k * L) % s->Wt) : 0;
+      PROF(SD_PROF_KV, 0.0, 4.0 * L * d * es,
+           sdk::kv_append(st, bf, P(s->kown, exit_rows[k] * own_stride, es), P(s->vtown, exit_rows[k] * own_stride, es),
+                          Pm(s->ringK, (int64_t)b * H * s->Wt * hd, es), Pm(s->ringVT, (int64_t)b * H * s->Wt * hd, es),
+                          H, hd, L, s->Wt, pk, dK, dVT, dcap, doff, s->Se));
     }
     {
       Epi E = epi_base(s, EPI_GATE_RESID);
@@ -631,15 +681,15 @@ sd_status sd_stream_step(sd_stream* s, float* out_latent, sd_step_info* info) {
              sdk::gemm(st, bf, s->xm, P(s->w.cq_w, (int64_t)b * d * d, es), M, d, d, E));
       }
       const size_t per = (size_t)H * s->ctx8 * hd;
-      for (int part = 0; part < (neg_row >= 0 ? 2 : 1); ++part) {
+      for (int part = 0; part < (nneg > 0 ? 2 : 1); ++part) {
         AttnArgs A;
         std::memset(&A, 0, sizeof(A));
         A.q = s->q;
         A.q_rs = own_stride;
         A.q_hs = (int64_t)L * hd;
         A.o = s->ao;
-        A.r0 = part == 0 ? 0 : neg_row;
-        A.R = part == 0 ? R_pos : 1;
+        A.r0 = part == 0 ? 0 : R_pos;
+        A.R = part == 0 ? R_pos : nneg;
         A.H = H;
         A.L = L;
         A.hd = hd;
@@ -687,13 +737,20 @@ sd_status sd_stream_step(sd_stream* s, float* out_latent, sd_step_info* info) {
   }
 
   // ---- adaptive sink: embedding of the exiting chunk, decision, predicated copy
-  if (r_exit >= 0 && s->S > 0) {
-    const int cap_entry = capture ? s->sink_count : -1;
-    PROF(SD_PROF_CONTROLS, 0.0, 4.0 * L * d, sdk::sink_score(st, s->resid + (int64_t)r_exit * L * d, s->sink_part, L, d, s->sink_emb, s->Ment, cap_entry,
-                            (float)c.sink_tau, s->sink_flag, s->sink_sim));
-    if (!capture)
-      PROF(SD_PROF_KV, 0.0, 4.0 * s->nb * s->Se * d * es, sdk::sink_copy(st, bf, s->sink_flag, s->ringK, s->ringVT, s->sinkK, s->sinkVT, s->nb, H, hd, s->Wt,
-                             s->S8, ptr_old, s->Se));
+  // one leaving chunk after the other, so that each decision sees the
+  // embeddings the previous one left; the K / V^T of a refresh come from the
+  // ring (B = 1: the chunk just appended at ptr_old) or from its staged copy
+  for (int k = 0; k < nexit && s->S > 0; ++k) {
+    PROF(SD_PROF_CONTROLS, 0.0, 4.0 * L * d,
+         sdk::sink_score(st, s->resid + (int64_t)exit_rows[k] * L * d, s->sink_part, L, d, s->sink_emb, s->Ment,
+                         cap_entry[k], (float)c.sink_tau, s->sink_flag, s->sink_sim));
+    if (cap_entry[k] < 0) {
+      const bool staged = s->Cc > 0;
+      PROF(SD_PROF_KV, 0.0, 4.0 * s->nb * s->Se * d * es,
+           sdk::sink_copy(st, bf, s->sink_flag, staged ? s->candK : s->ringK, staged ? s->candVT : s->ringVT,
+                          s->sinkK, s->sinkVT, s->nb, H, hd, staged ? s->Cc : s->Wt, s->S8,
+                          staged ? k * s->Se : ptr_old, s->Se));
+    }
   }
 
   // ---- final layer and unpatchify -> eps_c
@@ -705,24 +762,27 @@ sd_status sd_stream_step(sd_stream* s, float* out_latent, sd_step_info* info) {
     PROF(SD_PROF_OTHER, gflop(M, s->P, d), gbytes(M, s->P, d, es, 4), sdk::gemm(st, bf, s->xm, s->w.head_w, M, s->P, d, E));
   }
   // ---- R-CFG, x0 prediction, re-noise / emit
-  PROF(SD_PROF_EPILOGUE, 12.0 * R * s->lat, 16.0 * R * s->lat, sdk::rcfg_update(st, rt, s->fx, s->fx0s, s->eps, out_latent, s->lat, (float)c.gamma, (float)c.delta,
-                           neg_row));
+  PROF(SD_PROF_EPILOGUE, 12.0 * R * s->lat, 16.0 * R * s->lat,
+       sdk::rcfg_update(st, rt, s->fx, s->fx0s, s->eps, out_latent, s->lat, (float)c.gamma, (float)c.delta));
 
   // ---- host bookkeeping
   info->step = s->n_steps++;
   info->rows = R;
   info->frame_id = -1;
-  if (r_exit >= 0) {
-    const int f = s->slots[n - 1];
+  if (nexit > 0) {
     info->has_output = 1;
-    info->frame_id = s->frames[f].fid;
-    s->frames[f].used = false;
-    s->slots[n - 1] = -1;
-    if (s->Wt > 0) {
-      s->kv_ptr = (s->kv_ptr + L) % s->Wt;
-      s->kv_valid = std::min(s->Wt, s->kv_valid + L);
+    info->n_out = nexit;
+    info->frame_id = s->frames[s->slots[(n - 1) * B]].fid;
+    for (int k = 0; k < B; ++k) {
+      const int f = s->slots[(n - 1) * B + k];
+      if (f >= 0) s->frames[f].used = false;
+      s->slots[(n - 1) * B + k] = -1;
     }
-    if (capture) s->sink_count += 1;
+    if (s->Wt > 0) {
+      s->kv_ptr = (int)(((int64_t)s->kv_ptr + (int64_t)nexit * L) % s->Wt);
+      s->kv_valid = std::min(s->Wt, s->kv_valid + nexit * L);
+    }
+    s->sink_count = sink_count_after;
   }
   info->kv_ptr = s->kv_ptr;
   info->kv_valid = s->kv_valid;

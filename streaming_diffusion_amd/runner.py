@@ -96,7 +96,9 @@ class StreamRunner:
                                           C.c_void_p(self.stream.cuda_stream), C.byref(h)))
         self.h = h
         self.lat_shape = (cfg.latent_t, cfg.latent_c, cfg.latent_h, cfg.latent_w)
-        self.out = torch.empty(self.lat_shape, dtype=torch.float32, device=device)
+        # a step emits B latents ([B][T][C][H][W]); with B = 1 the leading axis is dropped
+        self.out_shape = self.lat_shape if cfg.chunks_per_step == 1 else (cfg.chunks_per_step,) + self.lat_shape
+        self.out = torch.empty(self.out_shape, dtype=torch.float32, device=device)
 
     def close(self):
         if getattr(self, "h", None):
@@ -120,8 +122,12 @@ class StreamRunner:
         return info
 
     def step(self, out=None) -> L.sd_step_info:
+        """Advance one step; the emitted latents (info.n_out of them) land in
+        out (default self.out), shaped [B][T][C][H][W] (no leading axis when B = 1)."""
         info = L.sd_step_info()
         o = self.out if out is None else out
+        if o.numel() < int(np.prod(self.out_shape)):
+            raise ValueError("out holds fewer elements than the B latents a step emits")
         L.check(self.lib.sd_stream_step(self.h, C.c_void_p(ptr(o)), C.byref(info)), self.h)
         return info
 

@@ -81,7 +81,9 @@ def test_workload_configs_validate(lib, state, name):
     (dict(t_index=(32, 51)), L.SD_ERR_ARG),
     (dict(window_tokens=32), L.SD_ERR_ARG),          # window smaller than a chunk
     (dict(ssf_eta=1.0), L.SD_ERR_ARG),
-    (dict(chunks_per_step=2), L.SD_ERR_ARG),
+    (dict(chunks_per_step=0), L.SD_ERR_ARG),
+    (dict(chunks_per_step=9), L.SD_ERR_ARG),         # beyond SD_MAX_CHUNKS
+    (dict(chunks_per_step=8, t_index=(0, 8, 16, 24, 32, 40)), L.SD_ERR_ARG),   # 48 rows > SD_MAX_ROWS
     (dict(cfg_type="onetime"), L.SD_ERR_ARG),        # tiny has no context
     (dict(latent_h=15), L.SD_ERR_SHAPE),
     (dict(d_model=5184, n_heads=81), L.SD_ERR_SHAPE),  # beyond the register-resident LayerNorm rows

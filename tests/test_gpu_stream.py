@@ -41,7 +41,8 @@ def run_parity(cfg, steps, check_ring=True):
     src, nz, us = gen.LatentSource(cfg), gen.NoiseSource(cfg), gen.UniformSource()
     ssf_src = gen.SSFFrameSource(cfg) if cfg.ssf_on and cfg.ssf_kind == "u8" else None
     lat = cfg.latent_elems
-    done = pushes = 0
+    B = cfg.chunks_per_step
+    done = pushes = queued = 0
     worst = 0.0
     while done < steps:
         x0, e, u = src.next(), nz.next(), us.next()
@@ -56,10 +57,15 @@ def run_parity(cfg, steps, check_ring=True):
         if po.skipped:
             continue
         assert list(pg.taus)[:cfg.n_slots] == po.taus and pg.t0 == po.t0 and pg.s == po.s
+        queued += 1
+        if queued < B:           # a step takes B pending chunks
+            continue
+        queued = 0
         out_o, so = orc.step()
         sg = run.step()
         torch.cuda.synchronize()
-        assert (sg.has_output, sg.rows, sg.frame_id) == (int(so.has_output), so.rows, so.frame_id)
+        assert (sg.has_output, sg.rows, sg.frame_id, sg.n_out) == (int(so.has_output), so.rows, so.frame_id,
+                                                                   so.n_out)
         assert (sg.kv_ptr, sg.kv_valid, sg.sink_count, sg.rope_next) == (so.kv_ptr, so.kv_valid, so.sink_count,
                                                                          so.rope_next)
         eps = run.buffer(L.SD_BUF_EPS, torch.float32, (sg.rows, lat)).cpu().numpy()
@@ -83,6 +89,17 @@ def run_parity(cfg, steps, check_ring=True):
                           stored_bf16=True)
             check_close(ringV[b].transpose(2, 0, 1)[valid], orc.ringV[b][valid], cfg.dtype, f"ring V block {b}",
                           stored_bf16=True)
+    if check_ring and cfg.sink_tokens and orc.sink_count:
+        H, hd, S = cfg.n_heads, cfg.head_dim, cfg.sink_tokens
+        S8 = (S + 7) // 8 * 8
+        used = orc.sink_count * (S // orc.M)
+        sinkK = run.buffer(L.SD_BUF_SINK_K, tdt, (cfg.n_blocks, H, S8, hd)).float().cpu().numpy()
+        sinkV = run.buffer(L.SD_BUF_SINK_V, tdt, (cfg.n_blocks, H, hd, S8)).float().cpu().numpy()
+        for b in range(cfg.n_blocks):
+            check_close(sinkK[b].transpose(1, 0, 2)[:used], orc.sinkK[b][:used], cfg.dtype, f"sink K block {b}",
+                        stored_bf16=True)
+            check_close(sinkV[b].transpose(2, 0, 1)[:used], orc.sinkV[b][:used], cfg.dtype, f"sink V block {b}",
+                        stored_bf16=True)
     print(f"{cfg.name}: {done} steps over {pushes} pushes, worst error {worst:.3e}", flush=True)
     run.close()
     return orc, run
@@ -130,6 +147,32 @@ def test_video_bf16_motion_sink_refresh():
     print("video bf16 reduced", flush=True)
     orc, _ = run_parity(cfg, 8)
     assert orc.kv_valid == cfg.window_tokens
+
+
+def test_tiny_fp32_two_chunks_per_step():
+    device()
+    cfg = reduced("tiny", ssf_on=False, chunks_per_step=2)
+    print("tiny fp32 B=2", flush=True)
+    orc, _ = run_parity(cfg, 8)
+    assert orc.sink_count == 1
+
+
+def test_video_bf16_three_chunks_overflowing_window_sink_refresh():
+    """B = 3 chunks of 192 tokens leave per step into a 384-token window: the
+    ring keeps the last two of them, and every sink decision after the first
+    capture reads its chunk's staged copy."""
+    device()
+    cfg = reduced("video13b", chunks_per_step=3, window_tokens=384)
+    print("video bf16 reduced B=3 W=384", flush=True)
+    orc, _ = run_parity(cfg, 5)
+    assert orc.kv_valid == cfg.window_tokens and orc.sink_count == 1
+
+
+def test_fourstep_bf16_onetime_negative_two_chunks_per_step():
+    device()
+    cfg = reduced("fourstep", chunks_per_step=2, ssf_on=False)
+    print("fourstep bf16 reduced B=2 onetime", flush=True)
+    run_parity(cfg, 6)
 
 
 def test_kv_reset_mid_stream_matches_oracle():
