@@ -103,13 +103,25 @@ def cpu_baseline(cfg, n_blocks_sample: int):
     rows = cfg.rows_per_step
     step_s = dt / n_blocks_sample * cfg.n_blocks * rows
     threads = 0
+    blas = "unknown"
     for p in threadpool_info():
         if p.get("user_api") == "blas":
             threads = max(threads, int(p.get("num_threads", 0)))
+            blas = f"{p.get('internal_api', '?')} {p.get('version', '')}".strip()
+    cpu_model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {
         "value": cfg.latent_t / step_s,
         "unit": "frames/s",
         "cores": threads or len(os.sched_getaffinity(0)),
+        "cpu_model": cpu_model,
+        "blas": blas,
         "kind": "oracle",
         "sample": (f"one row through {n_blocks_sample} of {cfg.n_blocks} DiT blocks at full shape (fp32 NumPy, "
                    f"{dt:.2f} s), scaled x{cfg.n_blocks // n_blocks_sample * rows} to one {rows}-row step "
