@@ -12,6 +12,7 @@ resident in device memory before timing starts.
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
                     [--workload NAME] [--n-slots n] [--chunks B]
     python bench.py --workload video14b --sweep [--steps K]
+    python bench.py --slo-fps F --chunks BMAX [--steps K]
 
 Prints one JSON line (the sweep: one per (B, n) point, B chunks entering per
 step and n denoising slots, so B*n rows per forward).
@@ -42,6 +43,9 @@ def parse():
     ap.add_argument("--chunks", type=int, default=1, help="B: chunks entering (and leaving) per step")
     ap.add_argument("--sweep", action="store_true",
                     help="one JSON line per (B, n) in {1,2,4,8} x {1,2,4}, weights shared (no CPU baseline)")
+    ap.add_argument("--slo-fps", type=float, default=0.0,
+                    help="run the SLO-aware batching loop for --steps steps with up to --chunks chunks per step "
+                         "and report the batch sizes it chose (one JSON line)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-blocks", type=int, default=2, help="DiT blocks in the oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -240,6 +244,56 @@ def measure(cfg, weights, steps: int, warmup: int, dev):
     }
 
 
+def slo_run(cfg, weights, target_fps: float, steps: int, dev):
+    """The SLO-aware batching loop on the real pipeline with a backlog of
+    input chunks: each step the scheduler picks how many enter; a step's
+    latency counts only once the last n groups all had the same size (the
+    latency depends on every group in flight)."""
+    import torch
+
+    from streaming_diffusion_amd.runner import StreamRunner
+    from streaming_diffusion_amd.slo import SLOBatchScheduler
+    from workloads import gen
+
+    run = StreamRunner(cfg, weights)
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    if cfg.ctx_len:
+        run.set_context(torch.from_numpy(gen.make_context(cfg)).to(dev).to(tdt))
+    src, nz = gen.LatentSource(cfg), gen.NoiseSource(cfg)
+    pool = [(torch.from_numpy(src.next()).to(dev), torch.from_numpy(nz.next()).to(dev)) for _ in range(16)]
+    sch = SLOBatchScheduler(cfg.latent_t, target_fps, cfg.chunks_per_step)
+    n = cfg.n_slots
+    sizes, trace = [], []
+    k = 0
+    for _ in range(steps):
+        b = sch.choose(pending=cfg.chunks_per_step)
+        for _ in range(b):
+            x, e = pool[k % len(pool)]
+            run.push(x, e)
+            k += 1
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run.step(chunks=b)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        sizes.append(b)
+        steady = len(sizes) >= n + 1 and all(v == b for v in sizes[-n:])
+        if steady:
+            sch.observe(b, dt)
+        trace.append((b, round(dt * 1e3, 2), steady))
+    run.close()
+    b_final = sizes[-1]
+    model = sch.model()
+    return {"metric": "SLO-aware batching: chunks per step chosen from observed latency",
+            "target_fps": target_fps, "b_max": cfg.chunks_per_step, "n_slots": n,
+            "chosen_b": b_final,
+            "predicted_fps_at_chosen_b": round(sch.rate(b_final, model), 2) if model else None,
+            "latency_model_ms": {"fixed": round(model[0] * 1e3, 3), "per_chunk": round(model[1] * 1e3, 3)}
+            if model else None,
+            "observed_ms": {str(b): round(v * 1e3, 2) for b, v in sorted(sch.lat.items())},
+            "trace": trace, "config": {"workload": cfg.name}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -255,6 +309,11 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.slo_fps > 0:
+        cfg = get_config(args.workload, t_index=slot_indices(args.n_slots), chunks_per_step=max(2, args.chunks))
+        weights = random_device_weights(cfg, seed=gen.SEED_WEIGHTS)
+        print(json.dumps(slo_run(cfg, weights, args.slo_fps, args.steps, dev)))
+        return
     if args.sweep:
         # weights do not depend on n or B
         base = get_config(args.workload)

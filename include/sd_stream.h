@@ -190,6 +190,15 @@ sd_status sd_stream_push_frame(sd_stream* s, const float* x0, const float* noise
  * out_latent may be NULL on steps that emit nothing. */
 sd_status sd_stream_step(sd_stream* s, float* out_latent, sd_step_info* info);
 
+/* sd_stream_step with a group of `chunks` (1 <= chunks <= chunks_per_step)
+ * entering instead of B: groups of different sizes travel through the slots
+ * and each leaves whole (n_out = its size), so a host scheduler can change
+ * the batch from step to step (StreamDiffusionV2 summary, SLO-aware batching
+ * scheduler).  SD_ERR_NOT_READY while fewer than `chunks` are pending;
+ * SD_ERR_ARG for chunks outside the range.  out_latent holds at least
+ * chunks_per_step latents. */
+sd_status sd_stream_step_chunks(sd_stream* s, int32_t chunks, float* out_latent, sd_step_info* info);
+
 /* Clear the ring, the sink and the RoPE counter (frames in flight continue). */
 sd_status sd_stream_kv_reset(sd_stream* s);
 

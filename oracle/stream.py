@@ -202,19 +202,23 @@ class OracleStream:
             return None
         return self.net.forward_row(fr.x, tau, fr.t0, snapshot, ctx_kv, collect=collect)
 
-    def step(self):
-        """One Stream Batch step.  The B pending frames that entered together
-        form one slot group; all rows read the cache snapshot of the step
-        start; the group in the last slot leaves, in push order, each frame
-        appending its K/V and taking its sink decision in turn.  Returns
-        (out, info): out is None during warm-up, the emitted latent when
-        B = 1, else the [B][latent] stack in push order."""
+    def step(self, chunks: Optional[int] = None):
+        """One Stream Batch step.  The `chunks` oldest pending frames (default
+        and at most B = chunks_per_step) enter together as one slot group; all
+        rows read the cache snapshot of the step start; the group in the last
+        slot leaves, in push order, each frame appending its K/V and taking its
+        sink decision in turn.  Returns (out, info): out is None when nothing
+        leaves, the emitted latent when B = 1, else the [group size][latent]
+        stack in push order."""
         cfg = self.cfg
         n = cfg.n_slots
         B = cfg.chunks_per_step
-        if len(self.pending) < B:
-            raise NotReady("fewer pending frames than chunks per step")
-        enter = [self.pending.pop(0) for _ in range(B)]
+        b = B if chunks is None else chunks
+        if not 1 <= b <= B:
+            raise ValueError("chunks must be in [1, chunks_per_step]")
+        if len(self.pending) < b:
+            raise NotReady("fewer pending frames than chunks for this step")
+        enter = [self.pending.pop(0) for _ in range(b)]
         self.slots = [enter] + self.slots[:n - 1]
         snapshot = None if self.identity else self.cache_snapshot()
         # forward rows: slot by slot, the frames of a slot in push order

@@ -466,10 +466,16 @@ sd_status sd_stream_push_frame(sd_stream* s, const float* x0, const float* noise
 
 sd_status sd_stream_step(sd_stream* s, float* out_latent, sd_step_info* info) {
   if (!s) return SD_ERR_ARG;
+  return sd_stream_step_chunks(s, s->B, out_latent, info);
+}
+
+sd_status sd_stream_step_chunks(sd_stream* s, int32_t chunks, float* out_latent, sd_step_info* info) {
+  if (!s) return SD_ERR_ARG;
   const sd_stream_config& c = s->cfg;
   if (!info) return set_err(s, SD_ERR_ARG, "info is null");
   const int n = s->n, B = s->B;
-  if ((int)s->pending.size() < B) return set_err(s, SD_ERR_NOT_READY, "fewer pending chunks than chunks_per_step");
+  if (chunks < 1 || chunks > B) return set_err(s, SD_ERR_ARG, "chunks must be in [1, chunks_per_step]");
+  if ((int)s->pending.size() < chunks) return set_err(s, SD_ERR_NOT_READY, "fewer pending chunks than requested");
   if (!s->ctx_set) return set_err(s, SD_ERR_STATE, "set_context() must be called first");
   const bool will_exit = (n == 1) || (s->slots[(n - 2) * B] >= 0);
   if (will_exit && !out_latent) return set_err(s, SD_ERR_ARG, "out_latent is null but frames leave this step");
@@ -480,8 +486,12 @@ sd_status sd_stream_step(sd_stream* s, float* out_latent, sd_step_info* info) {
   for (int i = n - 1; i >= 1; --i)
     for (int k = 0; k < B; ++k) s->slots[i * B + k] = s->slots[(i - 1) * B + k];
   for (int k = 0; k < B; ++k) {
-    s->slots[k] = s->pending.front();
-    s->pending.pop_front();
+    if (k < chunks) {
+      s->slots[k] = s->pending.front();
+      s->pending.pop_front();
+    } else {
+      s->slots[k] = -1;       // a smaller group leaves its upper lanes empty
+    }
   }
   RowTable rt;
   std::memset(&rt, 0, sizeof(rt));
@@ -516,8 +526,8 @@ sd_status sd_stream_step(sd_stream* s, float* out_latent, sd_step_info* info) {
   const int R_pos = R;
   int nneg = 0;
   if (c.cfg_type == SD_CFG_ONETIME) {
-    // one negative-prompt row per entering chunk (rows 0 .. B-1 are slot 0)
-    for (int k = 0; k < B; ++k) {
+    // one negative-prompt row per entering chunk (rows 0 .. chunks-1 are slot 0)
+    for (int k = 0; k < chunks; ++k) {
       rt.r[R] = rt.r[k];
       rt.r[R].kind = 1;
       rt.r[R].last = 0;

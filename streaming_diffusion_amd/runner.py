@@ -121,14 +121,18 @@ class StreamRunner:
                                               C.c_void_p(ptr(ssf_frame)), float(u), C.byref(info)), self.h)
         return info
 
-    def step(self, out=None) -> L.sd_step_info:
-        """Advance one step; the emitted latents (info.n_out of them) land in
-        out (default self.out), shaped [B][T][C][H][W] (no leading axis when B = 1)."""
+    def step(self, out=None, chunks=None) -> L.sd_step_info:
+        """Advance one step with a group of `chunks` entering (default B);
+        the emitted latents (info.n_out of them) land in out (default
+        self.out), shaped [B][T][C][H][W] (no leading axis when B = 1)."""
         info = L.sd_step_info()
         o = self.out if out is None else out
         if o.numel() < int(np.prod(self.out_shape)):
             raise ValueError("out holds fewer elements than the B latents a step emits")
-        L.check(self.lib.sd_stream_step(self.h, C.c_void_p(ptr(o)), C.byref(info)), self.h)
+        if chunks is None:
+            L.check(self.lib.sd_stream_step(self.h, C.c_void_p(ptr(o)), C.byref(info)), self.h)
+        else:
+            L.check(self.lib.sd_stream_step_chunks(self.h, int(chunks), C.c_void_p(ptr(o)), C.byref(info)), self.h)
         return info
 
     def kv_reset(self):

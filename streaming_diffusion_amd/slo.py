@@ -1,0 +1,78 @@
+"""SLO-aware batching: how many chunks enter each Stream Batch step.
+
+StreamDiffusionV2 summary, SLO-aware batching scheduler: a step that takes b
+chunks of T frames emits b*T frames after a latency L(b), so the achieved rate
+is f(b) = b*T / L(b).  In the memory-bound regime the pages describe, the
+latency is an affine function of the batch (activation traffic grows with b,
+the weight traffic does not), so f rises with b towards the roofline knee and
+flattens beyond it.  The scheduler adapts b from the latencies it observes:
+the smallest b whose predicted rate meets the target frame rate (least
+latency per frame), never more chunks than have been collected from the input
+stream, and -- when the target is out of reach -- no further along the curve
+than the knee, where a larger batch stops paying for its latency.
+
+Host logic only: it drives `StreamRunner.step(chunks=b)` (the library's
+sd_stream_step_chunks) and is exercised without a GPU by the tests.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional, Tuple
+
+
+class SLOBatchScheduler:
+    def __init__(self, frames_per_chunk: int, target_fps: float, b_max: int, knee_tol: float = 0.05,
+                 decay: float = 0.7):
+        if frames_per_chunk < 1 or b_max < 1 or target_fps <= 0:
+            raise ValueError("frames_per_chunk, b_max and target_fps must be positive")
+        self.T = frames_per_chunk
+        self.target = float(target_fps)
+        self.b_max = b_max
+        self.knee_tol = knee_tol
+        self.decay = decay
+        self.lat: Dict[int, float] = {}       # b -> smoothed step latency in seconds
+
+    def observe(self, b: int, seconds: float) -> None:
+        """Record the measured latency of a step that took b chunks."""
+        prev = self.lat.get(b)
+        self.lat[b] = seconds if prev is None else self.decay * prev + (1.0 - self.decay) * seconds
+
+    def model(self) -> Optional[Tuple[float, float]]:
+        """(alpha, beta) of L(b) = alpha + beta*b, least squares over the
+        smoothed latencies; with a single batch size observed the latency is
+        taken as proportional to b (no fixed part)."""
+        pts = sorted(self.lat.items())
+        if not pts:
+            return None
+        if len(pts) == 1:
+            b, l = pts[0]
+            return 0.0, l / b
+        n = len(pts)
+        mb = sum(b for b, _ in pts) / n
+        ml = sum(l for _, l in pts) / n
+        sbb = sum((b - mb) ** 2 for b, _ in pts)
+        beta = sum((b - mb) * (l - ml) for b, l in pts) / sbb
+        beta = max(beta, 1e-12)
+        alpha = max(ml - beta * mb, 0.0)
+        return alpha, beta
+
+    def rate(self, b: int, model: Optional[Tuple[float, float]] = None) -> float:
+        """Predicted frames per second of steps taking b chunks."""
+        alpha, beta = model if model is not None else self.model()
+        return b * self.T / (alpha + beta * b)
+
+    def choose(self, pending: int) -> int:
+        """Chunks for the next step, given `pending` collected chunks (>= 1)."""
+        cap = max(1, min(self.b_max, pending))
+        model = self.model()
+        if model is None:
+            return 1
+        if len(self.lat) == 1 and cap >= 2 and 2 not in self.lat:
+            return 2                          # a second batch size fixes the slope
+        for b in range(1, cap + 1):
+            if self.rate(b, model) >= self.target:
+                return b
+        best = max(self.rate(b, model) for b in range(1, cap + 1))
+        for b in range(1, cap + 1):
+            if self.rate(b, model) >= (1.0 - self.knee_tol) * best:
+                return b
+        return cap

@@ -29,7 +29,8 @@ def reduced(name, **kw):
     return get_config(name, **base)
 
 
-def run_parity(cfg, steps, check_ring=True):
+def run_parity(cfg, steps, check_ring=True, sizes=None):
+    """`sizes`: chunks entering at each step (cycled); default B every step."""
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     weights = gen.make_weights(cfg)
     ctx_pos = gen.make_context(cfg)
@@ -58,11 +59,12 @@ def run_parity(cfg, steps, check_ring=True):
             continue
         assert list(pg.taus)[:cfg.n_slots] == po.taus and pg.t0 == po.t0 and pg.s == po.s
         queued += 1
-        if queued < B:           # a step takes B pending chunks
+        want = sizes[done % len(sizes)] if sizes else B
+        if queued < want:        # a step takes `want` pending chunks
             continue
         queued = 0
-        out_o, so = orc.step()
-        sg = run.step()
+        out_o, so = orc.step(want)
+        sg = run.step(chunks=want)
         torch.cuda.synchronize()
         assert (sg.has_output, sg.rows, sg.frame_id, sg.n_out) == (int(so.has_output), so.rows, so.frame_id,
                                                                    so.n_out)
@@ -72,7 +74,10 @@ def run_parity(cfg, steps, check_ring=True):
         for r in range(sg.rows):
             worst = max(worst, check_close(eps[r], orc.last_eps[r].ravel(), cfg.dtype, f"step {done} eps row {r}"))
         if out_o is not None:
-            worst = max(worst, check_close(run.out.cpu().numpy(), out_o, cfg.dtype, f"step {done} output"))
+            got = run.out.cpu().numpy()
+            if B > 1:
+                got = got[:so.n_out]
+            worst = max(worst, check_close(got, out_o, cfg.dtype, f"step {done} output"))
         if not np.isnan(so.sink_sim):
             si = run.sink_info()
             assert si.evaluated == 1 and si.entry == so.sink_entry
@@ -173,6 +178,31 @@ def test_fourstep_bf16_onetime_negative_two_chunks_per_step():
     cfg = reduced("fourstep", chunks_per_step=2, ssf_on=False)
     print("fourstep bf16 reduced B=2 onetime", flush=True)
     run_parity(cfg, 6)
+
+
+def test_video_bf16_variable_group_sizes():
+    """Steps take 1 to 3 chunks (capacity B = 3): groups keep their size through
+    the slots, leave whole, and append / decide the sink in push order."""
+    device()
+    cfg = reduced("video13b", chunks_per_step=3, window_tokens=384)
+    print("video bf16 reduced, group sizes 1,3,2,2,1,3,2,1", flush=True)
+    run_parity(cfg, 8, sizes=[1, 3, 2, 2, 1, 3, 2, 1])
+
+
+def test_step_chunks_out_of_range():
+    device()
+    cfg = reduced("tiny", ssf_on=False, chunks_per_step=2)
+    run = StreamRunner(cfg, upload_weights(cfg, gen.make_weights(cfg)))
+    x = torch.zeros(run.lat_shape, device=device())
+    run.push(x, x)
+    for bad in (0, 3):
+        with pytest.raises(L.SDError) as ei:
+            run.step(chunks=bad)
+        assert ei.value.code == L.SD_ERR_ARG
+    with pytest.raises(L.SDError) as ei:
+        run.step(chunks=2)                     # one chunk pending
+    assert ei.value.code == L.SD_ERR_NOT_READY
+    run.close()
 
 
 def test_kv_reset_mid_stream_matches_oracle():

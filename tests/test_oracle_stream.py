@@ -277,3 +277,27 @@ def test_ring_pointer_and_sink_trace_b_chunks_overflowing_window():
         _, info = st.step()
         trace.append((info.has_output, info.n_out, info.kv_ptr, info.kv_valid, info.sink_count))
     assert trace == [(False, 0, 0, 0, 0), (True, 2, 8, 24, 1), (True, 2, 16, 24, 1), (True, 2, 0, 24, 1)]
+
+
+def test_identity_pipeline_variable_group_sizes():
+    """Steps may take fewer chunks than the capacity B: each group keeps its
+    size through the slots and leaves whole, frames in push order."""
+    cfg = get_config("tiny", t_index=(0, 16, 32, 45), gamma=1.7, delta=1.0, ssf_on=False, chunks_per_step=3)
+    st = OracleStream(cfg, None, identity_denoiser=True)
+    src, nz = gen.LatentSource(cfg), gen.NoiseSource(cfg)
+    sizes = [1, 3, 2, 2, 1, 3, 2, 1]
+    inputs, outs, emitted_sizes = [], [], []
+    for b in sizes:
+        for _ in range(b):
+            x0 = src.next()
+            inputs.append(x0)
+            st.push_frame(x0, nz.next())
+        out, info = st.step(b)
+        if out is not None:
+            emitted_sizes.append(info.n_out)
+            outs.extend(out)
+    assert emitted_sizes == sizes[:len(sizes) - 3]          # a group leaves n - 1 = 3 steps after entering
+    for k, o in enumerate(outs):
+        assert np.allclose(o, inputs[k], atol=1e-11)
+    with pytest.raises(ValueError):
+        st.step(4)
