@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--workload", default="video13b")
     ap.add_argument("--n-slots", type=int, default=2)
     ap.add_argument("--chunks", type=int, default=1, help="B: chunks entering (and leaving) per step")
+    ap.add_argument("--cfg", choices=["self", "onetime", "full"], default=None,
+                    help="guidance variant (default: the workload's own, self-negative R-CFG for the video DiT)")
     ap.add_argument("--sweep", action="store_true",
                     help="one JSON line per (B, n) in {1,2,4,8} x {1,2,4}, weights shared (no CPU baseline)")
     ap.add_argument("--slo-fps", type=float, default=0.0,
@@ -146,7 +148,7 @@ def measure(cfg, weights, steps: int, warmup: int, dev):
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     if cfg.ctx_len:
         ctx = torch.from_numpy(gen.make_context(cfg)).to(dev).to(tdt)
-        ctx_neg = torch.from_numpy(gen.make_context(cfg, True)).to(dev).to(tdt) if cfg.cfg_type == "onetime" else None
+        ctx_neg = torch.from_numpy(gen.make_context(cfg, True)).to(dev).to(tdt) if cfg.cfg_type != "self" else None
         run.set_context(ctx, ctx_neg)
     B = cfg.chunks_per_step
     total = (warmup + steps + 2) * B
@@ -234,8 +236,8 @@ def measure(cfg, weights, steps: int, warmup: int, dev):
         "config": {"workload": f"{cfg.name}: {cfg.n_blocks} blocks d{cfg.d_model} h{cfg.n_heads} ffn{cfg.d_ffn}, "
                                f"chunk T={cfg.latent_t} {cfg.latent_c}x{cfg.latent_h}x{cfg.latent_w} "
                                f"({cfg.tokens} tokens), sink {cfg.sink_tokens} + window {cfg.window_tokens}, "
-                               f"n={cfg.n_slots} slots, B={B} chunks per step, R-CFG {cfg.cfg_type}, "
-                               f"ctx {cfg.ctx_len}, motion on",
+                               f"n={cfg.n_slots} slots, B={B} chunks per step, guidance {cfg.cfg_type}, "
+                               f"ctx {cfg.ctx_len}, motion {'on' if cfg.motion_on else 'off'}",
                    "rows_per_step": cfg.rows_per_step, "tokens_per_row": cfg.tokens,
                    "frames_per_step": B * cfg.latent_t, "parallelism": "single GPU"},
         "ttff_ms": round(ttff_ms, 2) if ttff_ms else None,
@@ -258,7 +260,8 @@ def slo_run(cfg, weights, target_fps: float, steps: int, dev):
     run = StreamRunner(cfg, weights)
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     if cfg.ctx_len:
-        run.set_context(torch.from_numpy(gen.make_context(cfg)).to(dev).to(tdt))
+        neg = torch.from_numpy(gen.make_context(cfg, True)).to(dev).to(tdt) if cfg.cfg_type != "self" else None
+        run.set_context(torch.from_numpy(gen.make_context(cfg)).to(dev).to(tdt), neg)
     src, nz = gen.LatentSource(cfg), gen.NoiseSource(cfg)
     pool = [(torch.from_numpy(src.next()).to(dev), torch.from_numpy(nz.next()).to(dev)) for _ in range(16)]
     sch = SLOBatchScheduler(cfg.latent_t, target_fps, cfg.chunks_per_step)
@@ -309,8 +312,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    kw = {} if args.cfg is None else {"cfg_type": args.cfg}
     if args.slo_fps > 0:
-        cfg = get_config(args.workload, t_index=slot_indices(args.n_slots), chunks_per_step=max(2, args.chunks))
+        cfg = get_config(args.workload, t_index=slot_indices(args.n_slots), chunks_per_step=max(2, args.chunks), **kw)
         weights = random_device_weights(cfg, seed=gen.SEED_WEIGHTS)
         print(json.dumps(slo_run(cfg, weights, args.slo_fps, args.steps, dev)))
         return
@@ -320,12 +324,14 @@ def main():
         weights = random_device_weights(base, seed=gen.SEED_WEIGHTS)
         for n in (1, 2, 4):
             for B in (1, 2, 4, 8):
-                cfg = get_config(args.workload, t_index=slot_indices(n), chunks_per_step=B)
+                cfg = get_config(args.workload, t_index=slot_indices(n), chunks_per_step=B, **kw)
+                if cfg.rows_per_step > 40:          # beyond the rows one forward takes
+                    continue
                 res = measure(cfg, weights, args.steps, max(args.warmup, n + 1), dev)
                 res["config"]["sweep"] = {"B": B, "n": n}
                 print(json.dumps(res), flush=True)
         return
-    cfg = get_config(args.workload, t_index=slot_indices(args.n_slots), chunks_per_step=args.chunks)
+    cfg = get_config(args.workload, t_index=slot_indices(args.n_slots), chunks_per_step=args.chunks, **kw)
     weights = random_device_weights(cfg, seed=gen.SEED_WEIGHTS)
     res = measure(cfg, weights, args.steps, args.warmup, dev)
     if args.calibrate_copy:

@@ -23,6 +23,13 @@ extern "C" {
 sd_status sd_k_gemm(int32_t dtype, const void* A, const void* W, const void* bias, float* C, int32_t M, int32_t N,
                     int32_t K, void* stream);
 
+/* C[m][n] += sum_k A[m][k] W[n][k] + bias[n]: the update that closes the
+ * attention and FFN sub-layers of a denoiser block, adding the projected
+ * output to the fp32 residual stream.  Operand rules as sd_k_gemm; C is read
+ * and written in place; C must not alias A, W or bias. */
+sd_status sd_k_gemm_resid(int32_t dtype, const void* A, const void* W, const void* bias, float* C, int32_t M,
+                          int32_t N, int32_t K, void* stream);
+
 /* One key segment of an attention call.  K is [cap][hd] per (row, head), V is
  * stored transposed [hd][cap]; a head starts head_stride elements after the
  * previous one and a query row row_stride elements after the previous one

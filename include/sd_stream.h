@@ -49,7 +49,7 @@ extern "C" {
 
 #define SD_ABI_VERSION 1
 #define SD_MAX_SLOTS 8       /* n, denoising steps in flight */
-#define SD_MAX_ROWS 40       /* rows per forward: B*n (+B for onetime-negative) */
+#define SD_MAX_ROWS 40       /* rows per forward: B*n (+B onetime-negative, 2*B*n full CFG) */
 #define SD_MAX_CHUNKS 8      /* chunks per step (B) */
 #define SD_MAX_SINK 8        /* sink entries M */
 
@@ -64,10 +64,13 @@ typedef enum {
 } sd_status;
 
 typedef enum { SD_DTYPE_F32 = 0, SD_DTYPE_BF16 = 1 } sd_dtype;
-/* R-CFG variants (StreamDiffusion paper notes, section 2): self-negative uses
- * the frame's own input latent as x0*; onetime-negative adds one forward of
- * the entering frame under the negative prompt and uses its x0 estimate. */
-typedef enum { SD_CFG_SELF = 0, SD_CFG_ONETIME = 1 } sd_cfg_type;
+/* Guidance variants (StreamDiffusion paper notes, section 2): self-negative
+ * R-CFG uses the frame's own input latent as x0*; onetime-negative R-CFG adds
+ * one forward of the entering frame under the negative prompt and uses its x0
+ * estimate; full CFG, the standard guidance R-CFG replaces, gives every row a
+ * twin under the negative prompt (2n rows) whose prediction takes the place of
+ * the virtual residual (with delta = 1: eps_u + gamma (eps_c - eps_u)). */
+typedef enum { SD_CFG_SELF = 0, SD_CFG_ONETIME = 1, SD_CFG_FULL = 2 } sd_cfg_type;
 typedef enum { SD_SSF_U8 = 0, SD_SSF_LATENT = 1 } sd_ssf_kind;
 
 typedef struct {
@@ -82,7 +85,8 @@ typedef struct {
   int32_t n_slots;                 /* n = number of denoising steps in flight */
   int32_t t_index[SD_MAX_SLOTS];   /* 50-step grid index per slot: tau = 999 - 20 k */
   int32_t chunks_per_step;         /* B in [1, SD_MAX_CHUNKS]: chunks that enter (and leave)
-                                      together; B*n rows (+B for onetime R-CFG) <= SD_MAX_ROWS */
+                                      together; B*n rows (+B for onetime R-CFG, x2 for
+                                      full CFG) <= SD_MAX_ROWS */
   int32_t cfg_type;                /* sd_cfg_type */
   double gamma, delta;             /* R-CFG guidance scale and residual weight */
   /* KV cache, in tokens */

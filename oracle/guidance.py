@@ -5,6 +5,9 @@ StreamDiffusion paper notes, section 2 (R-CFG):
 * combine                  eps_cfg = delta eps' + gamma (eps_c - delta eps')
 * self-negative: x0* is the frame's own input latent (n forwards in total);
   onetime-negative: one negative forward (n+1 forwards in total).
+* full CFG, the standard guidance R-CFG replaces (2n forwards): eps' is the
+  denoiser's own prediction under the negative prompt for the same latent and
+  timestep; with delta = 1 the combine is eps_u + gamma (eps_c - eps_u).
 
 The pages name no sampler.  Reading: deterministic DDIM (eta = 0):
 x0_hat = (x_tau - b_tau eps_cfg) / a_tau, the next slot receives

@@ -94,8 +94,10 @@ class OracleStream:
         self.Se = cfg.sink_tokens // sink_entries
         self.ctx_kv = self._ctx(ctx_pos)
         self.ctx_kv_neg = self._ctx(ctx_neg)
-        if cfg.cfg_type == "onetime" and self.ctx_kv_neg is None and self.net is not None and cfg.ctx_len:
-            raise ValueError("onetime-negative R-CFG needs a negative context")
+        if cfg.cfg_type not in ("self", "onetime", "full"):
+            raise ValueError("cfg_type must be self, onetime or full")
+        if cfg.cfg_type != "self" and self.ctx_kv_neg is None and self.net is not None and cfg.ctx_len:
+            raise ValueError("onetime-negative R-CFG and full CFG need a negative context")
         n = cfg.n_slots
         self.slots: List[Optional[List[Frame]]] = [None] * n      # slot groups of B frames
         self.pending: List[Frame] = []
@@ -236,15 +238,27 @@ class OracleStream:
                 f.x0_star = guidance.predict_x0(f.x, eps_neg, a0, b0)
                 neg_eps.append(eps_neg)
         results = [self._denoise(f, f.taus[i], snapshot, self.ctx_kv, collect=(i == n - 1)) for i, f in rows]
+        # full CFG (StreamDiffusion paper notes, section 2: standard CFG costs
+        # 2n forwards): every row has a twin under the negative prompt, same
+        # latent, timestep and cache; its prediction replaces eps'
+        uncond = []
+        if cfg.cfg_type == "full":
+            for i, f in rows:
+                tau = f.taus[i]
+                if self.identity:
+                    uncond.append(guidance.virtual_residual(f.x, f.x0, self.a[tau], self.b[tau]))
+                else:
+                    uncond.append(self.net.forward_row(f.x, tau, f.t0, snapshot, self.ctx_kv_neg))
         if not self.identity:
             # denoiser outputs in forward row order (slots, then the negative rows)
             self.last_eps = [res[0] if i == n - 1 else res for (i, _), res in zip(rows, results)]
             self.last_eps.extend(neg_eps)
+            self.last_eps.extend(uncond)
         outs, exits = [], []
-        for (i, f), res in zip(rows, results):
+        for j, ((i, f), res) in enumerate(zip(rows, results)):
             tau = f.taus[i]
             a, b = self.a[tau], self.b[tau]
-            eps_p = guidance.virtual_residual(f.x, f.x0_star, a, b)
+            eps_p = uncond[j] if uncond else guidance.virtual_residual(f.x, f.x0_star, a, b)
             exit_kv = exit_hidden = None
             if self.identity:
                 eps_c = eps_p
@@ -260,7 +274,7 @@ class OracleStream:
             else:
                 outs.append(x0_hat)
                 exits.append((f, exit_kv, exit_hidden))
-        n_rows = len(rows) + len(neg_eps)
+        n_rows = len(rows) + len(neg_eps) + len(uncond)
         info = StepInfo(self.n_steps, bool(exits), exits[0][0].fid if exits else -1, n_rows,
                         0, 0, 0, False, -1, float("nan"), self.rope_p, len(exits))
         if exits:
@@ -310,10 +324,11 @@ class OracleStream:
 
 
 def denoise_sequential(cfg, net: Denoiser, x0, noise, taus, t0, a, b, snapshots=None, ctx_kv=None,
-                       x0_star=None):
+                       x0_star=None, ctx_kv_neg=None):
     """One frame denoised on its own, slot after slot, with no pipelining:
     the reference side of the Stream Batch invariant.  snapshots[i] is the
-    cache the frame reads at its i-th step (None: no cache)."""
+    cache the frame reads at its i-th step (None: no cache).  With
+    ctx_kv_neg (full CFG) eps' is the prediction under that context."""
     x = guidance.entry_noise(x0, noise, a[taus[0]], b[taus[0]])
     xs = x0 if x0_star is None else x0_star
     n = len(taus)
@@ -321,7 +336,10 @@ def denoise_sequential(cfg, net: Denoiser, x0, noise, taus, t0, a, b, snapshots=
         tau = taus[i]
         snap = None if snapshots is None else snapshots[i]
         eps_c = net.forward_row(x, tau, t0, snap, ctx_kv)
-        eps_p = guidance.virtual_residual(x, xs, a[tau], b[tau])
+        if ctx_kv_neg is not None:
+            eps_p = net.forward_row(x, tau, t0, snap, ctx_kv_neg)
+        else:
+            eps_p = guidance.virtual_residual(x, xs, a[tau], b[tau])
         eps_cfg = guidance.rcfg(eps_c, eps_p, cfg.gamma, cfg.delta)
         x0_hat = guidance.predict_x0(x, eps_cfg, a[tau], b[tau])
         if i == n - 1:

@@ -22,7 +22,7 @@ SD_OK, SD_ERR_ARG, SD_ERR_SHAPE, SD_ERR_STATE, SD_ERR_WORKSPACE, SD_ERR_HIP, SD_
 STATUS_NAMES = {0: "SD_OK", -1: "SD_ERR_ARG", -2: "SD_ERR_SHAPE", -3: "SD_ERR_STATE", -4: "SD_ERR_WORKSPACE",
                 -5: "SD_ERR_HIP", -6: "SD_ERR_NOT_READY"}
 SD_DTYPE_F32, SD_DTYPE_BF16 = 0, 1
-SD_CFG_SELF, SD_CFG_ONETIME = 0, 1
+SD_CFG_SELF, SD_CFG_ONETIME, SD_CFG_FULL = 0, 1, 2
 SD_SSF_U8, SD_SSF_LATENT = 0, 1
 SD_BUF_EPS, SD_BUF_RING_K, SD_BUF_RING_V, SD_BUF_SINK_K, SD_BUF_SINK_V, SD_BUF_RESID, SD_BUF_MOD = range(7)
 
@@ -104,6 +104,8 @@ SIGNATURES = {
     "sd_stream_last_error": (C.c_char_p, [C.c_void_p]),
     "sd_k_gemm": (C.c_int, [C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
                             C.c_int32, C.c_void_p]),
+    "sd_k_gemm_resid": (C.c_int, [C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
+                                  C.c_int32, C.c_void_p]),
     "sd_k_attention": (C.c_int, [C.c_int32, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int32, C.c_int32,
                                  C.c_int32, C.c_int32, C.c_int32, C.POINTER(sd_kv_segment), C.c_int32, C.c_void_p,
                                  C.c_size_t, C.c_void_p]),

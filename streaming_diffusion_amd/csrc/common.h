@@ -53,7 +53,7 @@ struct RowInfo {
   int32_t frame;      // frame-store record of the row's latent
   int32_t tau;        // timestep
   int32_t t0;         // temporal RoPE base
-  int32_t kind;       // 0 = denoise slot, 1 = negative-prompt row (onetime R-CFG)
+  int32_t kind;       // 0 = denoise slot, 1 = negative-prompt row (onetime R-CFG, full CFG)
   int32_t last;       // 1 if this slot is the last (the frame leaves)
   int32_t ctx;        // 0 = positive context, 1 = negative
   float a, b;         // sqrt(alpha_tau), sqrt(1 - alpha_tau)
@@ -61,6 +61,7 @@ struct RowInfo {
   float a0, b0;       // entry timestep coefficients (negative row)
   int32_t oidx;       // last slot: position of the frame among the step's outputs
   int32_t neg;        // entering frame with onetime R-CFG: its negative row, else -1
+  int32_t pair;       // full CFG: the row's twin under the negative prompt, else -1
 };
 struct RowTable {
   int32_t R;

@@ -31,9 +31,10 @@ int validate_config(const sd_stream_config& c, std::string* err) {
   if (c.n_slots < 1 || c.n_slots > SD_MAX_SLOTS) return fail(err, SD_ERR_ARG, "n_slots out of range");
   if (c.chunks_per_step < 1 || c.chunks_per_step > SD_MAX_CHUNKS)
     return fail(err, SD_ERR_ARG, "chunks_per_step must be in [1, 8]");
-  if (c.cfg_type != SD_CFG_SELF && c.cfg_type != SD_CFG_ONETIME) return fail(err, SD_ERR_ARG, "unknown cfg_type");
-  if (c.cfg_type == SD_CFG_ONETIME && c.ctx_len == 0)
-    return fail(err, SD_ERR_ARG, "onetime-negative R-CFG needs a (negative) context");
+  if (c.cfg_type != SD_CFG_SELF && c.cfg_type != SD_CFG_ONETIME && c.cfg_type != SD_CFG_FULL)
+    return fail(err, SD_ERR_ARG, "unknown cfg_type");
+  if (c.cfg_type != SD_CFG_SELF && c.ctx_len == 0)
+    return fail(err, SD_ERR_ARG, "onetime-negative R-CFG and full CFG need a (negative) context");
   if (!std::isfinite(c.gamma) || !std::isfinite(c.delta)) return fail(err, SD_ERR_ARG, "gamma/delta must be finite");
   if (c.n_train_steps < 50 || c.n_train_steps > 100000) return fail(err, SD_ERR_ARG, "n_train_steps out of range");
   if (!(c.beta_start > 0) || !(c.beta_end > 0) || !(c.beta_end < 1)) return fail(err, SD_ERR_ARG, "betas out of range");

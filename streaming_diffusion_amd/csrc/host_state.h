@@ -22,7 +22,9 @@ inline int64_t latent_elems(const sd_stream_config& c) {
   return (int64_t)c.latent_t * c.latent_c * c.latent_h * c.latent_w;
 }
 inline int rows_max(const sd_stream_config& c) {
-  return c.chunks_per_step * c.n_slots + (c.cfg_type == SD_CFG_ONETIME ? c.chunks_per_step : 0);
+  const int pos = c.chunks_per_step * c.n_slots;
+  if (c.cfg_type == SD_CFG_FULL) return 2 * pos;
+  return pos + (c.cfg_type == SD_CFG_ONETIME ? c.chunks_per_step : 0);
 }
 
 // Scaled-linear schedule: sqrt(beta_t) linear in t; alpha_t = prod(1 - beta).

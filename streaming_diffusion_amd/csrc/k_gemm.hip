@@ -13,39 +13,44 @@ namespace sdk {
 // ---------------------------------------------------------------------------
 // Epilogue.  acc is C[m][n] (fp32); partner is C[m][n ^ 1] (the other half of
 // a RoPE pair).  T is the element type of the GEMM.
+template <typename T>
+SD_DEV float bias_at(const Epi& E, int n) {
+  return E.bias ? to_f(((const T*)E.bias)[n]) : 0.f;
+}
+
 template <typename T, int MODE>
 SD_DEV void epi_apply(const Epi& E, int m, int n, int N, float acc, float partner) {
   switch (MODE) {
     case EPI_STORE: {
-      const float v = acc + (E.bias ? to_f(((const T*)E.bias)[n]) : 0.f);
+      const float v = acc + bias_at<T>(E, n);
       ((T*)E.out)[(int64_t)m * E.ldo + n] = from_f<T>(v);
       break;
     }
     case EPI_F32: {
-      const float v = acc + (E.bias ? to_f(((const T*)E.bias)[n]) : 0.f);
+      const float v = acc + bias_at<T>(E, n);
       ((float*)E.out)[(int64_t)m * E.ldo + n] = v;
       break;
     }
     case EPI_GELU: {
-      const float v = acc + (E.bias ? to_f(((const T*)E.bias)[n]) : 0.f);
+      const float v = acc + bias_at<T>(E, n);
       const float g = 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
       ((T*)E.out)[(int64_t)m * E.ldo + n] = from_f<T>(g);
       break;
     }
     case EPI_GATE_RESID: {
       const int r = m / E.L;
-      const float v = acc + to_f(((const T*)E.bias)[n]);
+      const float v = acc + bias_at<T>(E, n);
       const float g = E.mod[(int64_t)r * E.six_d + E.gate_off + n] + to_f(((const T*)E.blk)[E.gate_off + n]);
       E.resid[(int64_t)m * N + n] += g * v;
       break;
     }
     case EPI_RESID: {
-      const float v = acc + to_f(((const T*)E.bias)[n]);
+      const float v = acc + bias_at<T>(E, n);
       E.resid[(int64_t)m * N + n] += v;
       break;
     }
     case EPI_PATCH: {
-      E.resid[(int64_t)m * N + n] = acc + to_f(((const T*)E.bias)[n]);
+      E.resid[(int64_t)m * N + n] = acc + bias_at<T>(E, n);
       break;
     }
     case EPI_QKV:
@@ -53,11 +58,11 @@ SD_DEV void epi_apply(const Epi& E, int m, int n, int N, float acc, float partne
       const int which = n / E.d;
       const int nn = n - which * E.d;
       const int h = nn / E.hd, e = nn - h * E.hd;
-      float v = acc + to_f(((const T*)E.bias)[n]);
+      float v = acc + bias_at<T>(E, n);
       const int r = m / E.L, t = m - r * E.L;
       const int sec = (MODE == EPI_CTXKV) ? which + 1 : which;   // 0 q, 1 k, 2 v
       if (E.rope && sec < 2) {
-        const float pv = partner + to_f(((const T*)E.bias)[n ^ 1]);
+        const float pv = partner + bias_at<T>(E, n ^ 1);
         const int hw = E.Hp * E.Wp;
         const int f = t / hw, y = (t / E.Wp) % E.Hp, x = t % E.Wp;
         float2 cs;
@@ -84,7 +89,7 @@ SD_DEV void epi_apply(const Epi& E, int m, int n, int N, float acc, float partne
       const int f = t / hw, y = (t / E.Wp) % E.Hp, x = t % E.Wp;
       const int c = n % E.C, px = (n / E.C) % E.p, py = n / (E.C * E.p);
       const int64_t lat = (int64_t)E.T * E.C * E.Hl * E.Wl;
-      const float v = acc + to_f(((const T*)E.bias)[n]);
+      const float v = acc + bias_at<T>(E, n);
       E.eps[r * lat + (((int64_t)f * E.C + c) * E.Hl + y * E.p + py) * E.Wl + x * E.p + px] = v;
       break;
     }

@@ -35,7 +35,7 @@ hipError_t entry_noise(hipStream_t s, const float* x0, const float* noise, float
 // then x0_hat = (x - b eps_cfg) / a and either re-noise to the next slot's
 // timestep or emit x0_hat (to output position oidx of the step).  For
 // onetime-negative R-CFG an entering row first turns its negative row's output
-// into its x0* estimate.
+// into its x0* estimate; under full CFG eps' is the twin row's output.
 __global__ void rcfg_update_kernel(RowTable rt, float* __restrict__ store_x, float* __restrict__ store_x0s,
                                    const float* __restrict__ eps, float* __restrict__ out, int64_t lat, float gamma,
                                    float delta) {
@@ -46,15 +46,20 @@ __global__ void rcfg_update_kernel(RowTable rt, float* __restrict__ store_x, flo
   if (i >= lat) return;
   const int64_t off = (int64_t)ri.frame * lat + i;
   const float x = store_x[off];
-  float x0s;
-  if (ri.neg >= 0) {
-    const float en = eps[(int64_t)ri.neg * lat + i];
-    x0s = (x - ri.b0 * en) / ri.a0;
-    store_x0s[off] = x0s;
+  float ep;
+  if (ri.pair >= 0) {
+    ep = eps[(int64_t)ri.pair * lat + i];
   } else {
-    x0s = store_x0s[off];
+    float x0s;
+    if (ri.neg >= 0) {
+      const float en = eps[(int64_t)ri.neg * lat + i];
+      x0s = (x - ri.b0 * en) / ri.a0;
+      store_x0s[off] = x0s;
+    } else {
+      x0s = store_x0s[off];
+    }
+    ep = (x - ri.a * x0s) / ri.b;
   }
-  const float ep = (x - ri.a * x0s) / ri.b;
   const float ec = eps[(int64_t)r * lat + i];
   const float ecfg = delta * ep + gamma * (ec - delta * ep);
   const float x0h = (x - ri.b * ecfg) / ri.a;

@@ -7,20 +7,31 @@
 
 extern "C" {
 
-sd_status sd_k_gemm(int32_t dtype, const void* A, const void* W, const void* bias, float* C, int32_t M, int32_t N,
-                    int32_t K, void* stream) {
+static sd_status gemm_call(int32_t dtype, const void* A, const void* W, const void* bias, float* C, int32_t M,
+                           int32_t N, int32_t K, void* stream, int mode) {
   if (dtype != SD_DTYPE_F32 && dtype != SD_DTYPE_BF16) return SD_ERR_ARG;
   if (!A || !W || !C || M < 0 || N < 0 || K < 1) return SD_ERR_ARG;
   if (K % 8) return SD_ERR_SHAPE;
   Epi E;
   std::memset(&E, 0, sizeof(E));
-  E.mode = EPI_F32;
+  E.mode = mode;
   E.bias = bias;
   E.out = C;
+  E.resid = C;
   E.ldo = N;
   E.L = 1;
   return sdk::gemm((hipStream_t)stream, dtype == SD_DTYPE_BF16, A, W, M, N, K, E) == hipSuccess ? SD_OK
                                                                                              : SD_ERR_HIP;
+}
+
+sd_status sd_k_gemm(int32_t dtype, const void* A, const void* W, const void* bias, float* C, int32_t M, int32_t N,
+                    int32_t K, void* stream) {
+  return gemm_call(dtype, A, W, bias, C, M, N, K, stream, EPI_F32);
+}
+
+sd_status sd_k_gemm_resid(int32_t dtype, const void* A, const void* W, const void* bias, float* C, int32_t M,
+                          int32_t N, int32_t K, void* stream) {
+  return gemm_call(dtype, A, W, bias, C, M, N, K, stream, EPI_RESID);
 }
 
 static size_t part_o_bytes(int32_t R, int32_t H, int32_t L, int32_t hd, int32_t nsplit) {

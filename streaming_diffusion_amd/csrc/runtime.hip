@@ -144,7 +144,7 @@ size_t carve(sd_stream* s, char* base) {
   Carver cv{base};
   const size_t es = s->es;
   const int64_t M = (int64_t)s->Rmax * s->L;
-  const int nctx = c.cfg_type == SD_CFG_ONETIME ? 2 : 1;
+  const int nctx = c.cfg_type != SD_CFG_SELF ? 2 : 1;
   s->fx = cv.take<float>((size_t)s->NF * s->lat * 4);
   s->fx0s = cv.take<float>((size_t)s->NF * s->lat * 4);
   if (c.ssf_on) {
@@ -371,9 +371,9 @@ sd_status sd_stream_set_context(sd_stream* s, const void* ctx_pos, const void* c
   const sd_stream_config& c = s->cfg;
   if (c.ctx_len == 0) return set_err(s, SD_ERR_STATE, "no cross-attention configured (ctx_len == 0)");
   if (!ctx_pos) return set_err(s, SD_ERR_ARG, "ctx_pos is null");
-  if (c.cfg_type == SD_CFG_ONETIME && !ctx_neg)
-    return set_err(s, SD_ERR_ARG, "onetime-negative R-CFG needs ctx_neg");
-  const int nctx = c.cfg_type == SD_CFG_ONETIME ? 2 : 1;
+  if (c.cfg_type != SD_CFG_SELF && !ctx_neg)
+    return set_err(s, SD_ERR_ARG, "onetime-negative R-CFG and full CFG need ctx_neg");
+  const int nctx = c.cfg_type != SD_CFG_SELF ? 2 : 1;
   const size_t per = (size_t)s->H * s->ctx8 * s->hd;   // elements per (block, context)
   HIP_TRY(sdk::fill_zero(s->st, s->ctxK, (size_t)s->nb * nctx * per * s->es));
   HIP_TRY(sdk::fill_zero(s->st, s->ctxVT, (size_t)s->nb * nctx * per * s->es));
@@ -519,6 +519,7 @@ sd_status sd_stream_step_chunks(sd_stream* s, int32_t chunks, float* out_latent,
       ri.b0 = (float)s->b[fr.taus[0]];
       ri.oidx = ri.last ? nexit : 0;
       ri.neg = -1;
+      ri.pair = -1;
       if (ri.last) exit_rows[nexit++] = R;
       ++R;
     }
@@ -534,6 +535,17 @@ sd_status sd_stream_step_chunks(sd_stream* s, int32_t chunks, float* out_latent,
       rt.r[R].ctx = 1;
       rt.r[R].neg = -1;
       rt.r[k].neg = R;
+      ++R;
+      ++nneg;
+    }
+  } else if (c.cfg_type == SD_CFG_FULL) {
+    // full CFG: a twin of every row under the negative prompt, same order
+    for (int k = 0; k < R_pos; ++k) {
+      rt.r[R] = rt.r[k];
+      rt.r[R].kind = 1;
+      rt.r[R].last = 0;
+      rt.r[R].ctx = 1;
+      rt.r[k].pair = R;
       ++R;
       ++nneg;
     }
@@ -571,7 +583,7 @@ sd_status sd_stream_step_chunks(sd_stream* s, int32_t chunks, float* out_latent,
     PROF(SD_PROF_OTHER, gflop(M, d, s->P), gbytes(M, d, s->P, es, 4), sdk::gemm(st, bf, s->xm, s->w.pe_w, M, d, s->P, E));
   }
 
-  const int nctx = c.cfg_type == SD_CFG_ONETIME ? 2 : 1;
+  const int nctx = c.cfg_type != SD_CFG_SELF ? 2 : 1;
   const int64_t own_stride = (int64_t)H * L * hd;
   for (int b = 0; b < s->nb; ++b) {
     const void* blk = P(s->w.blk_mod, (int64_t)b * 6 * d, es);

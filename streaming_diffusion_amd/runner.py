@@ -24,7 +24,7 @@ def make_config(cfg) -> L.sd_stream_config:
     for i, k in enumerate(cfg.t_index):
         c.t_index[i] = int(k)
     c.chunks_per_step = cfg.chunks_per_step
-    c.cfg_type = L.SD_CFG_ONETIME if cfg.cfg_type == "onetime" else L.SD_CFG_SELF
+    c.cfg_type = {"self": L.SD_CFG_SELF, "onetime": L.SD_CFG_ONETIME, "full": L.SD_CFG_FULL}[cfg.cfg_type]
     c.gamma, c.delta = cfg.gamma, cfg.delta
     c.sink_tokens = cfg.sink_tokens
     c.sink_entries = getattr(cfg, "sink_entries", 1) if cfg.sink_tokens else 0

@@ -85,6 +85,8 @@ def test_workload_configs_validate(lib, state, name):
     (dict(chunks_per_step=9), L.SD_ERR_ARG),         # beyond SD_MAX_CHUNKS
     (dict(chunks_per_step=8, t_index=(0, 8, 16, 24, 32, 40)), L.SD_ERR_ARG),   # 48 rows > SD_MAX_ROWS
     (dict(cfg_type="onetime"), L.SD_ERR_ARG),        # tiny has no context
+    (dict(cfg_type="full"), L.SD_ERR_ARG),
+    (dict(cfg_type="full", ctx_len=8, chunks_per_step=3, t_index=(0, 8, 16, 24, 32, 40, 45)), L.SD_ERR_ARG),  # 42 rows
     (dict(latent_h=15), L.SD_ERR_SHAPE),
     (dict(d_model=5184, n_heads=81), L.SD_ERR_SHAPE),  # beyond the register-resident LayerNorm rows
 ])
@@ -110,6 +112,9 @@ def test_create_rejects_bad_arguments_before_any_device_call(lib):
     assert lib.sd_stream_kv_reset(None) == L.SD_ERR_ARG
     assert lib.sd_k_gemm(0, None, None, None, None, 1, 1, 8, None) == L.SD_ERR_ARG
     assert lib.sd_k_gemm(1, 8, 8, None, 8, 1, 1, 12, None) == L.SD_ERR_SHAPE
+    assert lib.sd_k_gemm_resid(2, 8, 8, None, 8, 1, 1, 8, None) == L.SD_ERR_ARG
+    assert lib.sd_k_gemm_resid(1, 8, None, None, 8, 1, 1, 8, None) == L.SD_ERR_ARG
+    assert lib.sd_k_gemm_resid(1, 8, 8, None, 8, 1, 1, 60, None) == L.SD_ERR_SHAPE
     seg = L.sd_kv_segment(k=8, vt=8, cap=64, start=0, count=100, wrap=0)
     assert lib.sd_k_attention(1, 8, 0, 0, 8, 1, 1, 8, 64, 1, C.byref(seg), 1, None, 0, None) == L.SD_ERR_SHAPE
     assert lib.sd_k_attention(1, 8, 0, 0, 8, 1, 1, 8, 48, 1, C.byref(seg), 1, None, 0, None) == L.SD_ERR_SHAPE

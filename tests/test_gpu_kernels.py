@@ -47,6 +47,43 @@ def test_gemm_bf16_exact_integers(lib, M, N, K):
     assert np.array_equal(out.cpu().numpy().astype(np.float64), ref)
 
 
+@pytest.mark.parametrize("M,N,K", [(400, 300, 128), (64, 64, 64), (1, 8, 64), (300, 200, 136), (300, 200, 4096),
+                                   (1000, 520, 2048), (1500, 700, 1600), (2048, 768, 3072), (6240, 1536, 1536),
+                                   (6240, 1536, 8960), (3120, 5120, 5120)])
+def test_gemm_resid_bf16_exact_integers(lib, M, N, K):
+    """Residual accumulation C += A W^T + b with integer-valued operands: every
+    product, partial sum and the final sum are exact in fp32, so the result is
+    the integer arithmetic bit for bit (ragged tiles, both DMA tile shapes, and
+    K not a multiple of 64 included)."""
+    print(f"gemm resid exact M={M} N={N} K={K}", flush=True)
+    rng = np.random.default_rng(M * 3 + N + K)
+    ai = rng.integers(-8, 9, size=(M, K))
+    wi = rng.integers(-8, 9, size=(N, K))
+    bi = rng.integers(-8, 9, size=N)
+    ci = rng.integers(-4096, 4097, size=(M, N))
+    A = to_dev(ai / 16.0, torch.bfloat16)
+    W = to_dev(wi / 16.0, torch.bfloat16)
+    b = to_dev(bi / 16.0, torch.bfloat16)
+    out = to_dev(ci / 256.0, torch.float32)
+    call(lib.sd_k_gemm_resid(1, A.data_ptr(), W.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, stream_ptr()))
+    torch.cuda.synchronize()
+    ref = (ai.astype(np.float64) @ wi.T.astype(np.float64) + ci) / 256.0 + bi / 16.0
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), ref)
+
+
+def test_gemm_resid_f32_matches_numpy(lib):
+    M, N, K = 130, 70, 24
+    rng = np.random.default_rng(9)
+    a = rng.standard_normal((M, K)).astype(np.float32)
+    w = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+    c = rng.standard_normal((M, N)).astype(np.float32)
+    A, W, out = to_dev(a, torch.float32), to_dev(w, torch.float32), to_dev(c, torch.float32)
+    call(lib.sd_k_gemm_resid(0, A.data_ptr(), W.data_ptr(), None, out.data_ptr(), M, N, K, stream_ptr()))
+    torch.cuda.synchronize()
+    ref = c.astype(np.float64) + a.astype(np.float64) @ w.T.astype(np.float64)
+    assert rel_inf(out.cpu().numpy(), ref) < 1e-5
+
+
 @pytest.mark.parametrize("M,N,K", [(130, 70, 24), (64, 384, 128), (128, 512, 512)])
 def test_gemm_f32_matches_oracle(lib, M, N, K):
     print(f"gemm f32 M={M} N={N} K={K}", flush=True)

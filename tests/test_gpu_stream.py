@@ -34,7 +34,7 @@ def run_parity(cfg, steps, check_ring=True, sizes=None):
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     weights = gen.make_weights(cfg)
     ctx_pos = gen.make_context(cfg)
-    ctx_neg = gen.make_context(cfg, negative=True) if cfg.cfg_type == "onetime" else None
+    ctx_neg = gen.make_context(cfg, negative=True) if cfg.cfg_type != "self" else None
     orc = OracleStream(cfg, weights, ctx_pos, ctx_neg)
     run = StreamRunner(cfg, upload_weights(cfg, weights))
     if cfg.ctx_len:
@@ -187,6 +187,28 @@ def test_video_bf16_variable_group_sizes():
     cfg = reduced("video13b", chunks_per_step=3, window_tokens=384)
     print("video bf16 reduced, group sizes 1,3,2,2,1,3,2,1", flush=True)
     run_parity(cfg, 8, sizes=[1, 3, 2, 2, 1, 3, 2, 1])
+
+
+def test_tiny_fp32_full_cfg_with_context():
+    device()
+    cfg = reduced("tiny", ssf_on=False, ctx_len=12, cfg_type="full", gamma=1.8, delta=1.0)
+    print("tiny fp32 full CFG", flush=True)
+    orc, _ = run_parity(cfg, 6)
+    assert orc.n_steps == 6
+
+
+def test_image_bf16_full_cfg_four_rows():
+    device()
+    cfg = reduced("image", cfg_type="full", delta=0.8)
+    print("image bf16 reduced full CFG", flush=True)
+    run_parity(cfg, 4)
+
+
+def test_video_bf16_full_cfg_two_chunks_per_step():
+    device()
+    cfg = reduced("video13b", cfg_type="full", chunks_per_step=2)
+    print("video bf16 reduced full CFG B=2", flush=True)
+    run_parity(cfg, 6)
 
 
 def test_step_chunks_out_of_range():

@@ -54,7 +54,8 @@ def test_true_noise_recovers_x0():
 
 # ------------------------------------------------------------------ identity pipeline
 @pytest.mark.parametrize("t_index,cfg_type", [((32,), "self"), ((32, 45), "self"),
-                                              ((0, 16, 32, 45), "self"), ((0, 16, 32, 45), "onetime")])
+                                              ((0, 16, 32, 45), "self"), ((0, 16, 32, 45), "onetime"),
+                                              ((0, 16, 32, 45), "full")])
 def test_identity_pipeline_emits_inputs(t_index, cfg_type):
     """Denoiser replaced by eps_c := eps'.  With delta = 1 every slot has
     eps_cfg = eps' and x0_hat = x0*, so each frame leaves as it came in, in
@@ -301,3 +302,74 @@ def test_identity_pipeline_variable_group_sizes():
         assert np.allclose(o, inputs[k], atol=1e-11)
     with pytest.raises(ValueError):
         st.step(4)
+
+
+# ------------------------------------------------------------------ full CFG (2n rows)
+def full_cfg_run(cfg, w, ctx_pos, ctx_neg, steps, B=1):
+    st = OracleStream(cfg, w, ctx_pos=ctx_pos, ctx_neg=ctx_neg)
+    src, nz = gen.LatentSource(cfg), gen.NoiseSource(cfg)
+    frames, outs, snaps, rows = [], [], [], []
+    for k in range(steps):
+        for _ in range(B):
+            x0, e = src.next(), nz.next()
+            info = st.push_frame(x0, e)
+            frames.append((x0, e, info.t0))
+        snaps.append(st.cache_snapshot())
+        out, info = st.step()
+        rows.append(info.rows)
+        if out is not None:
+            outs.extend([out] if B == 1 else list(out))
+    return st, frames, outs, snaps, rows
+
+
+def test_full_cfg_equals_textbook_guidance_replayed_per_frame():
+    """Full CFG with delta = 1: each frame, replayed alone against the cache
+    snapshots it read, with the standard guidance eps_u + gamma (eps_c - eps_u)
+    from one forward under each prompt and the deterministic DDIM update."""
+    cfg = small_cfg(t_index=(0, 16, 32, 45), ctx_len=6, cfg_type="full", gamma=1.7, delta=1.0)
+    w = gen.make_weights(cfg)
+    cp, cn = gen.make_context(cfg), gen.make_context(cfg, negative=True)
+    st, frames, outs, snaps, rows = full_cfg_run(cfg, w, cp, cn, 8)
+    n = cfg.n_slots
+    assert rows == [2 * min(k + 1, n) for k in range(8)]
+    net = Denoiser(cfg, w)
+    kv_pos = [net.cross_kv(cp, b) for b in range(cfg.n_blocks)]
+    kv_neg = [net.cross_kv(cn, b) for b in range(cfg.n_blocks)]
+    a, b = schedule.sched_coeffs(cfg)
+    taus = schedule.taus_from_t_index(cfg)
+    assert len(outs) == 8 - (n - 1)
+    for k, o in enumerate(outs):
+        x0, e, t0 = frames[k]
+        x = a[taus[0]] * x0.astype(np.float64) + b[taus[0]] * e.astype(np.float64)
+        for i, tau in enumerate(taus):
+            ec = net.forward_row(x, tau, t0, snaps[k + i], kv_pos)
+            eu = net.forward_row(x, tau, t0, snaps[k + i], kv_neg)
+            eps = eu + cfg.gamma * (ec - eu)
+            x0h = (x - b[tau] * eps) / a[tau]
+            if i + 1 < n:
+                x = a[taus[i + 1]] * x0h + b[taus[i + 1]] * eps
+        assert np.allclose(o, x0h, rtol=0, atol=1e-11 * max(1.0, np.abs(x0h).max()))
+
+
+@pytest.mark.parametrize("B", [1, 2])
+def test_full_cfg_with_the_same_prompt_twice_is_unguided(B):
+    """With the negative prompt equal to the positive one, eps_u = eps_c and
+    the guided prediction is eps_c for any gamma: the same stream as
+    self-negative R-CFG at gamma = 1, whose residual term cancels."""
+    base = dict(t_index=(32, 45), ctx_len=5, gamma=1.0, delta=1.0, chunks_per_step=B)
+    cfg_s = small_cfg(cfg_type="self", **base)
+    cfg_f = small_cfg(cfg_type="full", **{**base, "gamma": 2.9})
+    w = gen.make_weights(cfg_s)
+    cp = gen.make_context(cfg_s)
+    _, _, outs_s, _, _ = full_cfg_run(cfg_s, w, cp, None, 5, B)
+    _, _, outs_f, _, rows = full_cfg_run(cfg_f, w, cp, cp, 5, B)
+    assert rows[-1] == 2 * B * cfg_f.n_slots
+    assert len(outs_s) == len(outs_f) == 4 * B
+    for o_s, o_f in zip(outs_s, outs_f):
+        assert np.allclose(o_f, o_s, rtol=0, atol=1e-10)
+
+
+def test_full_cfg_needs_a_negative_context():
+    cfg = small_cfg(ctx_len=4, cfg_type="full")
+    with pytest.raises(ValueError):
+        OracleStream(cfg, gen.make_weights(cfg), ctx_pos=gen.make_context(cfg))

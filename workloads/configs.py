@@ -33,7 +33,7 @@ class Config:
     ctx_len: int                    # 0 = no cross-attention
     # stream batch
     t_index: Tuple[int, ...]        # one entry per slot; n = len(t_index)
-    cfg_type: str                   # "self" | "onetime" | "none"
+    cfg_type: str                   # "self" | "onetime" | "full"
     gamma: float = 1.4
     delta: float = 1.0
     chunks_per_step: int = 1        # B
@@ -86,8 +86,10 @@ class Config:
 
     @property
     def rows_per_step(self) -> int:
-        extra = self.chunks_per_step if self.cfg_type == "onetime" else 0
-        return self.chunks_per_step * self.n_slots + extra
+        pos = self.chunks_per_step * self.n_slots
+        if self.cfg_type == "full":
+            return 2 * pos
+        return pos + (self.chunks_per_step if self.cfg_type == "onetime" else 0)
 
     def replace(self, **kw) -> "Config":
         return dataclasses.replace(self, **kw)
