@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--workload", default="video13b")
     ap.add_argument("--n-slots", type=int, default=2)
     ap.add_argument("--chunks", type=int, default=1, help="B: chunks entering (and leaving) per step")
+    ap.add_argument("--batch-attn", action="store_true",
+                    help="cross-frame batch attention: every row attends to the own tokens of all rows")
     ap.add_argument("--cfg", choices=["self", "onetime", "full"], default=None,
                     help="guidance variant (default: the workload's own, self-negative R-CFG for the video DiT)")
     ap.add_argument("--sweep", action="store_true",
@@ -237,7 +239,8 @@ def measure(cfg, weights, steps: int, warmup: int, dev):
                                f"chunk T={cfg.latent_t} {cfg.latent_c}x{cfg.latent_h}x{cfg.latent_w} "
                                f"({cfg.tokens} tokens), sink {cfg.sink_tokens} + window {cfg.window_tokens}, "
                                f"n={cfg.n_slots} slots, B={B} chunks per step, guidance {cfg.cfg_type}, "
-                               f"ctx {cfg.ctx_len}, motion {'on' if cfg.motion_on else 'off'}",
+                               f"ctx {cfg.ctx_len}, motion {'on' if cfg.motion_on else 'off'}"
+                               + (", cross-frame batch attention" if cfg.batch_attn else ""),
                    "rows_per_step": cfg.rows_per_step, "tokens_per_row": cfg.tokens,
                    "frames_per_step": B * cfg.latent_t, "parallelism": "single GPU"},
         "ttff_ms": round(ttff_ms, 2) if ttff_ms else None,
@@ -313,6 +316,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     kw = {} if args.cfg is None else {"cfg_type": args.cfg}
+    if args.batch_attn:
+        kw["batch_attn"] = True
     if args.slo_fps > 0:
         cfg = get_config(args.workload, t_index=slot_indices(args.n_slots), chunks_per_step=max(2, args.chunks), **kw)
         weights = random_device_weights(cfg, seed=gen.SEED_WEIGHTS)

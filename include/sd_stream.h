@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SD_ABI_VERSION 1
+#define SD_ABI_VERSION 2
 #define SD_MAX_SLOTS 8       /* n, denoising steps in flight */
 #define SD_MAX_ROWS 40       /* rows per forward: B*n (+B onetime-negative, 2*B*n full CFG) */
 #define SD_MAX_CHUNKS 8      /* chunks per step (B) */
@@ -107,6 +107,11 @@ typedef struct {
   /* motion-aware noise rate */
   int32_t motion_on, motion_k;
   double motion_lambda, s_min, s_max, motion_sigma;
+  /* cross-frame batch attention (StreamDiffusion paper notes, section 1,
+   * temporal consistency): every row's queries attend to [sink | window |
+   * the own tokens of every row of the forward] instead of [sink | window |
+   * its own tokens].  Self-negative R-CFG only (the rows share one prompt). */
+  int32_t batch_attn;
 } sd_stream_config;
 
 /*

@@ -228,3 +228,63 @@ class Denoiser:
         if collect:
             return eps, own, hidden
         return eps
+
+    def forward_batch(self, rows, cache_kv=None, ctx_kv=None, collect=()):
+        """Denoise the rows of one forward together with cross-frame batch
+        attention (StreamDiffusion paper notes, section 1, temporal
+        consistency: a row's queries attend to the keys and values of the
+        whole batch).  Reading with the KV cache: each row attends to
+        [cache | every row's own tokens, rows in batch order].  Everything
+        else is forward_row's block, row by row.
+
+        rows    : list of (x_lat, tau, t0)
+        collect : indices of rows that return (eps, own, hidden) as
+                  forward_row(collect=True) does; the others return eps.
+        """
+        cfg, w = self.cfg, self.w
+        d, H, hd, p = cfg.d_model, cfg.n_heads, cfg.head_dim, cfg.patch
+        st = []
+        for x_lat, tau, t0 in rows:
+            T, C, Hl, Wl = x_lat.shape
+            sc = self.cond(tau)
+            st.append({"shape": (T, C, Hl, Wl), "L": T * (Hl // p) * (Wl // p),
+                       "pos": token_positions(T, Hl // p, Wl // p, t0), "sc": sc, "m": self.modulation(sc),
+                       "x": linear(patchify(np.asarray(x_lat, self.dtype), p), w["pe_w"], w["pe_b"]), "own": []})
+        for b in range(cfg.n_blocks):
+            qs = []
+            for r in st:
+                L = r["L"]
+                h1, s1, g1, h2, s2, g2 = self.block_mod(r["m"], b)
+                xm = modulate(layer_norm(r["x"]), h1, s1)
+                qkv = linear(xm, w["qkv_w"][b], w["qkv_b"][b])
+                qs.append(rope_apply(qkv[:, :d].reshape(L, H, hd), r["pos"], cfg.rope_base))
+                k = rope_apply(qkv[:, d:2 * d].reshape(L, H, hd), r["pos"], cfg.rope_base)
+                r["own"].append((k, qkv[:, 2 * d:].reshape(L, H, hd)))
+            kb = np.concatenate([r["own"][b][0] for r in st], axis=0)
+            vb = np.concatenate([r["own"][b][1] for r in st], axis=0)
+            if cache_kv is not None and cache_kv[b][0].shape[0] > 0:
+                kk = np.concatenate([cache_kv[b][0], kb], axis=0)
+                vv = np.concatenate([cache_kv[b][1], vb], axis=0)
+            else:
+                kk, vv = kb, vb
+            for r, q in zip(st, qs):
+                L = r["L"]
+                h1, s1, g1, h2, s2, g2 = self.block_mod(r["m"], b)
+                x = r["x"]
+                a = attention(q, kk, vv).reshape(L, d)
+                x = x + g1 * linear(a, w["o_w"][b], w["o_b"][b])
+                if ctx_kv is not None:
+                    qc = linear(layer_norm(x), w["cq_w"][b], w["cq_b"][b]).reshape(L, H, hd)
+                    ac = attention(qc, ctx_kv[b][0], ctx_kv[b][1]).reshape(L, d)
+                    x = x + linear(ac, w["co_w"][b], w["co_b"][b])
+                xm = modulate(layer_norm(x), h2, s2)
+                hdn = gelu(linear(xm, w["f1_w"][b], w["f1_b"][b]))
+                r["x"] = x + g2 * linear(hdn, w["f2_w"][b], w["f2_b"][b])
+        outs = []
+        for j, r in enumerate(st):
+            T, C, Hl, Wl = r["shape"]
+            fm = linear(r["sc"], w["fin_w"], w["fin_b"])
+            out = linear(modulate(layer_norm(r["x"]), fm[:d], fm[d:]), w["head_w"], w["head_b"])
+            eps = unpatchify(out, T, C, Hl, Wl, p)
+            outs.append((eps, r["own"], r["x"]) if j in collect else eps)
+        return outs

@@ -98,6 +98,8 @@ class OracleStream:
             raise ValueError("cfg_type must be self, onetime or full")
         if cfg.cfg_type != "self" and self.ctx_kv_neg is None and self.net is not None and cfg.ctx_len:
             raise ValueError("onetime-negative R-CFG and full CFG need a negative context")
+        if getattr(cfg, "batch_attn", False) and cfg.cfg_type != "self":
+            raise ValueError("batch attention is defined for self-negative R-CFG (rows of one prompt)")
         n = cfg.n_slots
         self.slots: List[Optional[List[Frame]]] = [None] * n      # slot groups of B frames
         self.pending: List[Frame] = []
@@ -237,7 +239,12 @@ class OracleStream:
                     eps_neg = self.net.forward_row(f.x, tau0, f.t0, snapshot, self.ctx_kv_neg)
                 f.x0_star = guidance.predict_x0(f.x, eps_neg, a0, b0)
                 neg_eps.append(eps_neg)
-        results = [self._denoise(f, f.taus[i], snapshot, self.ctx_kv, collect=(i == n - 1)) for i, f in rows]
+        if getattr(cfg, "batch_attn", False) and not self.identity:
+            # cross-frame batch attention: one joint forward over the rows
+            results = self.net.forward_batch([(f.x, f.taus[i], f.t0) for i, f in rows], snapshot, self.ctx_kv,
+                                             collect={j for j, (i, _) in enumerate(rows) if i == n - 1})
+        else:
+            results = [self._denoise(f, f.taus[i], snapshot, self.ctx_kv, collect=(i == n - 1)) for i, f in rows]
         # full CFG (StreamDiffusion paper notes, section 2: standard CFG costs
         # 2n forwards): every row has a twin under the negative prompt, same
         # latent, timestep and cache; its prediction replaces eps'

@@ -92,11 +92,13 @@ struct Epi {
   int gate_off;         // offset of the gate inside 6d
   int six_d;            // 6d
   int L;                // tokens per row
-  // EPI_QKV / EPI_CTXKV destinations (element type of the GEMM)
+  // EPI_QKV / EPI_CTXKV destinations (element type of the GEMM); k and vt
+  // are head-major so that one head's keys of all rows are contiguous
   void* q;              // [R][H][L][hd]
-  void* k;              // [R][H][kstride][hd]
-  void* vt;             // [R][H][hd][kstride]   (V stored transposed)
+  void* k;              // [H][krows][kstride][hd]
+  void* vt;             // [H][hd][krows][kstride]   (V stored transposed)
   int kstride;          // token capacity of the k/vt destination per (row, head)
+  int krows;            // rows of the k/vt destination (1 for a context)
   int H, hd, d;
   int rope;             // apply RoPE to q and k
   int Hp, Wp;           // token grid of one latent frame

@@ -74,13 +74,12 @@ SD_DEV void epi_apply(const Epi& E, int m, int n, int N, float acc, float partne
           cs = E.rope_w[x * ((E.hd - E.dt - E.dh) >> 1) + ((e - E.dt - E.dh) >> 1)];
         v = (e & 1) ? (pv * cs.y + v * cs.x) : (v * cs.x - pv * cs.y);
       }
-      const int64_t rh = (int64_t)r * E.H + h;
       if (sec == 0)
-        ((T*)E.q)[(rh * E.L + t) * E.hd + e] = from_f<T>(v);
+        ((T*)E.q)[(((int64_t)r * E.H + h) * E.L + t) * E.hd + e] = from_f<T>(v);
       else if (sec == 1)
-        ((T*)E.k)[(rh * E.kstride + t) * E.hd + e] = from_f<T>(v);
+        ((T*)E.k)[(((int64_t)h * E.krows + r) * E.kstride + t) * E.hd + e] = from_f<T>(v);
       else
-        ((T*)E.vt)[(rh * E.hd + e) * E.kstride + t] = from_f<T>(v);
+        ((T*)E.vt)[(((int64_t)h * E.hd + e) * E.krows + r) * E.kstride + t] = from_f<T>(v);
       break;
     }
     case EPI_HEAD: {

@@ -116,7 +116,6 @@ SD_DEV void epi_strip(const Epi& E, const float* stg, int LC, int m_base, int n0
           jp[p] = (tp[p] == 0 ? e : (tp[p] == 1 ? e - E.dt : e - E.dt - E.dh)) >> 1;
         }
         bf16* const dst = sec == 0 ? (bf16*)E.q : (bf16*)E.k;
-        const int dstride = sec == 0 ? E.L : E.kstride;
         constexpr int IT = 64 * G / NT;
         // phase 1: every (cos, sin) of the strip (table reads are not
         // ordered behind the stores of phase 2)
@@ -152,7 +151,8 @@ SD_DEV void epi_strip(const Epi& E, const float* stg, int LC, int m_base, int n0
               v[2 * p + 1] = x0 * cs[it][p].y + x1 * cs[it][p].x;
             }
           }
-          store8_bf16(dst + (((int64_t)r * E.H + h) * dstride + t) * E.hd + e0, v);
+          const int64_t tok = sec == 0 ? ((int64_t)r * E.H + h) * E.L + t : ((int64_t)h * E.krows + r) * E.kstride + t;
+          store8_bf16(dst + tok * E.hd + e0, v);
         }
       }
     }
@@ -176,11 +176,11 @@ SD_DEV void epi_strip(const Epi& E, const float* stg, int LC, int m_base, int n0
             float v[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) v[i] = stg[(rg * 8 + i) * LC + col] + bn;
-            store8_bf16((bf16*)E.vt + (((int64_t)r * E.H + h) * E.hd + e) * E.kstride + t, v);
+            store8_bf16((bf16*)E.vt + (((int64_t)h * E.hd + e) * E.krows + r) * E.kstride + t, v);
           } else {
             for (int i = 0; i < 8 && m + i < M; ++i) {
               const int rx = rowtab[rg * 8 + i].x;
-              bf16* di = (bf16*)E.vt + (((int64_t)(rx >> 20) * E.H + h) * E.hd + e) * E.kstride + (rx & 0xFFFFF);
+              bf16* di = (bf16*)E.vt + (((int64_t)h * E.hd + e) * E.krows + (rx >> 20)) * E.kstride + (rx & 0xFFFFF);
               *di = (bf16)(stg[(rg * 8 + i) * LC + col] + bn);
             }
           }

@@ -340,13 +340,13 @@ hipError_t gemv(hipStream_t s, bool bf, const float* x, const void* W, const voi
 }
 
 // ---------------------------------------------------------------------------
-// KV ring append: the exiting chunk's own K [H][L][hd] and V^T [H][hd][L]
-// go to ring positions (ptr + t) mod W; its first Se tokens optionally become
-// a sink entry.
+// KV ring append: the exiting chunk's own K (head h: [L][hd] at kown + h k_hs)
+// and V^T (row (h, e): [L] at vtown + (h hd + e) vt_ps) go to ring positions
+// (ptr + t) mod W; its first Se tokens optionally become a sink entry.
 template <typename T>
-__global__ void kv_append_kernel(const T* __restrict__ kown, const T* __restrict__ vtown, T* __restrict__ ringK,
-                                 T* __restrict__ ringVT, int H, int hd, int L, int W, int ptr, T* __restrict__ sinkK,
-                                 T* __restrict__ sinkVT, int S8, int sink_off, int Se) {
+__global__ void kv_append_kernel(const T* __restrict__ kown, const T* __restrict__ vtown, int64_t k_hs, int64_t vt_ps,
+                                 T* __restrict__ ringK, T* __restrict__ ringVT, int H, int hd, int L, int W, int ptr,
+                                 T* __restrict__ sinkK, T* __restrict__ sinkVT, int S8, int sink_off, int Se) {
   const int64_t per_head = (int64_t)L * hd;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= per_head * H) return;
@@ -355,14 +355,14 @@ __global__ void kv_append_kernel(const T* __restrict__ kown, const T* __restrict
   // K element (t, e)
   {
     const int t = (int)(j / hd), e = (int)(j % hd);
-    const T v = kown[i];
+    const T v = kown[h * k_hs + j];
     if (W > 0) ringK[((int64_t)h * W + (ptr + t) % W) * hd + e] = v;
     if (sinkK && t < Se) sinkK[((int64_t)h * S8 + sink_off + t) * hd + e] = v;
   }
   // V^T element (e, t)
   {
     const int e = (int)(j / L), t = (int)(j % L);
-    const T v = vtown[i];
+    const T v = vtown[((int64_t)h * hd + e) * vt_ps + t];
     if (W > 0) ringVT[((int64_t)h * hd + e) * W + (ptr + t) % W] = v;
     if (sinkVT && t < Se) sinkVT[((int64_t)h * hd + e) * S8 + sink_off + t] = v;
   }
@@ -371,9 +371,9 @@ __global__ void kv_append_kernel(const T* __restrict__ kown, const T* __restrict
 // bf16 with every token range a multiple of 8 and L <= W: 16-byte chunks (8
 // head-dim elements of one K row, or 8 consecutive tokens of one V^T row), one
 // conditional wrap per chunk.  Chunk i < H*L*hd/8 is a K chunk, the rest V^T.
-__global__ void kv_append_vec_kernel(const bf16* __restrict__ kown, const bf16* __restrict__ vtown,
-                                     bf16* __restrict__ ringK, bf16* __restrict__ ringVT, int H, int hd, int L, int W,
-                                     int ptr, bf16* __restrict__ sinkK, bf16* __restrict__ sinkVT, int S8,
+__global__ void kv_append_vec_kernel(const bf16* __restrict__ kown, const bf16* __restrict__ vtown, int64_t k_hs,
+                                     int64_t vt_ps, bf16* __restrict__ ringK, bf16* __restrict__ ringVT, int H, int hd,
+                                     int L, int W, int ptr, bf16* __restrict__ sinkK, bf16* __restrict__ sinkVT, int S8,
                                      int sink_off, int Se) {
   const int64_t nk = (int64_t)H * L * (hd / 8);
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -382,7 +382,7 @@ __global__ void kv_append_vec_kernel(const bf16* __restrict__ kown, const bf16* 
     const int c = (int)(i % (hd / 8));
     const int64_t ht = i / (hd / 8);
     const int h = (int)(ht / L), t = (int)(ht % L);
-    const bf16x8 v = *(const bf16x8*)(kown + ht * hd + c * 8);
+    const bf16x8 v = *(const bf16x8*)(kown + h * k_hs + (int64_t)t * hd + c * 8);
     if (W > 0) {
       int p = ptr + t;
       if (p >= W) p -= W;
@@ -394,7 +394,7 @@ __global__ void kv_append_vec_kernel(const bf16* __restrict__ kown, const bf16* 
     const int tc = (int)(i % (L / 8));
     const int64_t he = i / (L / 8);          // h * hd + e
     const int t = tc * 8;
-    const bf16x8 v = *(const bf16x8*)(vtown + he * L + t);
+    const bf16x8 v = *(const bf16x8*)(vtown + he * vt_ps + t);
     if (W > 0) {
       int p = ptr + t;
       if (p >= W) p -= W;
@@ -404,25 +404,28 @@ __global__ void kv_append_vec_kernel(const bf16* __restrict__ kown, const bf16* 
   }
 }
 
-hipError_t kv_append(hipStream_t s, bool bf, const void* kown, const void* vtown, void* ringK, void* ringVT, int H,
-                     int hd, int L, int W, int ptr, void* sinkK, void* sinkVT, int S8, int sink_off, int Se) {
+hipError_t kv_append(hipStream_t s, bool bf, const void* kown, const void* vtown, int64_t k_hs, int64_t vt_ps,
+                     void* ringK, void* ringVT, int H, int hd, int L, int W, int ptr, void* sinkK, void* sinkVT, int S8,
+                     int sink_off, int Se) {
   const int64_t n = (int64_t)H * L * hd;
+  if (k_hs < (int64_t)L * hd || vt_ps < L) return hipErrorInvalidValue;
   if (bf && (hd % 8) == 0 && (L % 8) == 0 && (W % 8) == 0 && (ptr % 8) == 0 && ptr < (W > 0 ? W : 1) && (W == 0 || L <= W) &&
+      (k_hs % 8) == 0 && (vt_ps % 8) == 0 &&
       (!sinkK || ((S8 % 8) == 0 && (sink_off % 8) == 0 && (Se % 8) == 0))) {
     const int64_t chunks = 2 * (n / 8);
-    kv_append_vec_kernel<<<grid1(chunks, 256), 256, 0, s>>>((const bf16*)kown, (const bf16*)vtown, (bf16*)ringK,
-                                                             (bf16*)ringVT, H, hd, L, W, ptr, (bf16*)sinkK,
-                                                             (bf16*)sinkVT, S8, sink_off, Se);
+    kv_append_vec_kernel<<<grid1(chunks, 256), 256, 0, s>>>((const bf16*)kown, (const bf16*)vtown, k_hs, vt_ps,
+                                                             (bf16*)ringK, (bf16*)ringVT, H, hd, L, W, ptr,
+                                                             (bf16*)sinkK, (bf16*)sinkVT, S8, sink_off, Se);
     return hipGetLastError();
   }
   if (bf)
-    kv_append_kernel<bf16><<<grid1(n, 256), 256, 0, s>>>((const bf16*)kown, (const bf16*)vtown, (bf16*)ringK,
-                                                         (bf16*)ringVT, H, hd, L, W, ptr, (bf16*)sinkK,
+    kv_append_kernel<bf16><<<grid1(n, 256), 256, 0, s>>>((const bf16*)kown, (const bf16*)vtown, k_hs, vt_ps,
+                                                         (bf16*)ringK, (bf16*)ringVT, H, hd, L, W, ptr, (bf16*)sinkK,
                                                          (bf16*)sinkVT, S8, sink_off, Se);
   else
-    kv_append_kernel<float><<<grid1(n, 256), 256, 0, s>>>((const float*)kown, (const float*)vtown, (float*)ringK,
-                                                          (float*)ringVT, H, hd, L, W, ptr, (float*)sinkK,
-                                                          (float*)sinkVT, S8, sink_off, Se);
+    kv_append_kernel<float><<<grid1(n, 256), 256, 0, s>>>((const float*)kown, (const float*)vtown, k_hs, vt_ps,
+                                                          (float*)ringK, (float*)ringVT, H, hd, L, W, ptr,
+                                                          (float*)sinkK, (float*)sinkVT, S8, sink_off, Se);
   return hipGetLastError();
 }
 

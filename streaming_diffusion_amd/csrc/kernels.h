@@ -26,8 +26,11 @@ hipError_t gemv(hipStream_t s, bool bf, const float* x, const void* W, const voi
                 int act);
 // Append the exiting row's own K / V^T to the ring; optionally capture its
 // first Se tokens as sink entry (sink_off .. sink_off+Se).
-hipError_t kv_append(hipStream_t s, bool bf, const void* kown, const void* vtown, void* ringK, void* ringVT, int H,
-                     int hd, int L, int W, int ptr, void* sinkK, void* sinkVT, int S8, int sink_off, int Se);
+// kown: head h's [L][hd] keys start at kown + h * k_hs; vtown: the V^T row of
+// (h, e) starts at vtown + (h * hd + e) * vt_ps.
+hipError_t kv_append(hipStream_t s, bool bf, const void* kown, const void* vtown, int64_t k_hs, int64_t vt_ps,
+                     void* ringK, void* ringVT, int H, int hd, int L, int W, int ptr, void* sinkK, void* sinkVT, int S8,
+                     int sink_off, int Se);
 // Predicated sink refresh copy over all blocks (flag[0] != 0 -> entry flag[1]).
 hipError_t sink_copy(hipStream_t s, bool bf, const int* flag, const void* ringK, const void* ringVT, void* sinkK,
                      void* sinkVT, int nb, int H, int hd, int W, int S8, int ptr_old, int Se);

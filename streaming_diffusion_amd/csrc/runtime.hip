@@ -256,6 +256,7 @@ Epi epi_base(const sd_stream* s, int mode) {
   E.Wl = s->cfg.latent_w;
   E.p = s->cfg.patch;
   E.T = s->Tn;
+  E.krows = 1;
   return E;
 }
 
@@ -584,7 +585,11 @@ sd_status sd_stream_step_chunks(sd_stream* s, int32_t chunks, float* out_latent,
   }
 
   const int nctx = c.cfg_type != SD_CFG_SELF ? 2 : 1;
+  // q is [R][H][L][hd]; the own K / V^T are head-major, [H][R][L][hd] and
+  // [H][hd][R][L], so that one head's keys of every row are contiguous (the
+  // key range of cross-frame batch attention)
   const int64_t own_stride = (int64_t)H * L * hd;
+  const int64_t kv_hs = (int64_t)R * L * hd;
   for (int b = 0; b < s->nb; ++b) {
     const void* blk = P(s->w.blk_mod, (int64_t)b * 6 * d, es);
     // self-attention
@@ -596,6 +601,7 @@ sd_status sd_stream_step_chunks(sd_stream* s, int32_t chunks, float* out_latent,
       E.k = s->kown;
       E.vt = s->vtown;
       E.kstride = L;
+      E.krows = R;
       E.rope = 1;
       for (int r = 0; r < R; ++r) E.t0[r] = rt.r[r].t0;
       PROF(SD_PROF_GEMM_QKV, gflop(M, 3 * d, d), gbytes(M, 3 * d, d, es, es),
@@ -630,16 +636,19 @@ sd_status sd_stream_step_chunks(sd_stream* s, int32_t chunks, float* out_latent,
       sw.count = s->kv_valid;
       sw.start = s->Wt > 0 ? (s->kv_ptr - s->kv_valid + s->Wt) % s->Wt : 0;
       sw.wrap = 1;
+      // own tokens: this row's (row stride L tokens), or with batch attention
+      // every row's (row stride 0, R L tokens)
       KvSeg& so = A.seg[ns++];
       so.k = s->kown;
       so.vt = s->vtown;
-      so.k_rs = so.vt_rs = own_stride;
-      so.k_hs = so.vt_hs = (int64_t)L * hd;
-      so.cap = L;
-      so.count = L;
+      so.k_rs = c.batch_attn ? 0 : (int64_t)L * hd;
+      so.vt_rs = c.batch_attn ? 0 : L;
+      so.k_hs = so.vt_hs = kv_hs;
+      so.cap = R * L;
+      so.count = c.batch_attn ? R * L : L;
       A.nseg = ns;
       if (s->attn_split_max > 1) {
-        const int nk = ((sk.count + 7) & ~7) + sw.count + L;
+        const int nk = ((sk.count + 7) & ~7) + sw.count + so.count;
         const int qt = sdk::attention_q_tile(bf, hd);
         A.nsplit = sdk::attention_pick_split(R * H * ((L + qt - 1) / qt), (nk + 63) / 64, s->attn_split_max,
                                              s->cus * sdk::attention_wg_per_cu(bf, hd));
@@ -649,7 +658,7 @@ sd_status sd_stream_step_chunks(sd_stream* s, int32_t chunks, float* out_latent,
         A.part_sml = (long long)s->Rmax * H * L;
       }
       const double shared = (double)sk.count + sw.count;
-      PROF(SD_PROF_ATTN_SELF, 4.0 * R * L * (shared + L) * d,
+      PROF(SD_PROF_ATTN_SELF, 4.0 * R * L * (shared + so.count) * d,
            (double)es * d * (2.0 * R * L + 2.0 * shared + 2.0 * R * L), sdk::attention(st, bf, A, false));
       if (A.nsplit > 1)
         PROF(SD_PROF_ATTN_COMBINE, 0.0, (double)A.nsplit * R * L * (d * 4.0 + H * 8.0) + (double)R * L * d * es,
@@ -676,7 +685,8 @@ sd_status sd_stream_step_chunks(sd_stream* s, int32_t chunks, float* out_latent,
       if (s->Wt == 0 && !dK) continue;
       const int pk = s->Wt > 0 ? (int)(((int64_t)ptr_old + (int64_t)k * L) % s->Wt) : 0;
       PROF(SD_PROF_KV, 0.0, 4.0 * L * d * es,
-           sdk::kv_append(st, bf, P(s->kown, exit_rows[k] * own_stride, es), P(s->vtown, exit_rows[k] * own_stride, es),
+           sdk::kv_append(st, bf, P(s->kown, (int64_t)exit_rows[k] * L * hd, es), P(s->vtown, (int64_t)exit_rows[k] * L, es),
+                          kv_hs, (int64_t)R * L,
                           Pm(s->ringK, (int64_t)b * H * s->Wt * hd, es), Pm(s->ringVT, (int64_t)b * H * s->Wt * hd, es),
                           H, hd, L, s->Wt, pk, dK, dVT, dcap, doff, s->Se));
     }

@@ -39,6 +39,7 @@ def make_config(cfg) -> L.sd_stream_config:
     c.ssf_eta, c.max_skip_frame = cfg.ssf_eta, cfg.max_skip_frame
     c.motion_on, c.motion_k = int(cfg.motion_on), cfg.motion_k
     c.motion_lambda, c.s_min, c.s_max, c.motion_sigma = cfg.motion_lambda, cfg.s_min, cfg.s_max, cfg.motion_sigma
+    c.batch_attn = int(cfg.batch_attn)
     return c
 
 

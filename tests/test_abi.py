@@ -86,6 +86,7 @@ def test_workload_configs_validate(lib, state, name):
     (dict(chunks_per_step=8, t_index=(0, 8, 16, 24, 32, 40)), L.SD_ERR_ARG),   # 48 rows > SD_MAX_ROWS
     (dict(cfg_type="onetime"), L.SD_ERR_ARG),        # tiny has no context
     (dict(cfg_type="full"), L.SD_ERR_ARG),
+    (dict(cfg_type="onetime", ctx_len=8, batch_attn=True), L.SD_ERR_ARG),   # batch attention mixes prompts
     (dict(cfg_type="full", ctx_len=8, chunks_per_step=3, t_index=(0, 8, 16, 24, 32, 40, 45)), L.SD_ERR_ARG),  # 42 rows
     (dict(latent_h=15), L.SD_ERR_SHAPE),
     (dict(d_model=5184, n_heads=81), L.SD_ERR_SHAPE),  # beyond the register-resident LayerNorm rows

@@ -211,6 +211,28 @@ def test_video_bf16_full_cfg_two_chunks_per_step():
     run_parity(cfg, 6)
 
 
+def test_tiny_fp32_batch_attention():
+    device()
+    cfg = reduced("tiny", ssf_on=False, batch_attn=True, t_index=(10, 32, 45))
+    print("tiny fp32 batch attention n=3", flush=True)
+    run_parity(cfg, 7)
+
+
+def test_image_bf16_batch_attention():
+    device()
+    cfg = reduced("image", batch_attn=True)
+    print("image bf16 reduced batch attention", flush=True)
+    run_parity(cfg, 4)
+
+
+def test_video_bf16_batch_attention_two_chunks_per_step():
+    device()
+    cfg = reduced("video13b", batch_attn=True, chunks_per_step=2)
+    print("video bf16 reduced batch attention B=2", flush=True)
+    orc, _ = run_parity(cfg, 8)
+    assert orc.kv_valid == cfg.window_tokens
+
+
 def test_step_chunks_out_of_range():
     device()
     cfg = reduced("tiny", ssf_on=False, chunks_per_step=2)

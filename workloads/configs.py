@@ -37,6 +37,7 @@ class Config:
     gamma: float = 1.4
     delta: float = 1.0
     chunks_per_step: int = 1        # B
+    batch_attn: bool = False        # cross-frame batch attention (rows attend to every row's tokens)
     # KV cache (tokens)
     sink_tokens: int = 0
     window_tokens: int = 0
