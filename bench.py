@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--chunks", type=int, default=1, help="B: chunks entering (and leaving) per step")
     ap.add_argument("--batch-attn", action="store_true",
                     help="cross-frame batch attention: every row attends to the own tokens of all rows")
+    ap.add_argument("--sampler", choices=["ddim", "lcm"], default="ddim",
+                    help="per-slot update: DDIM (re-noise with the guided prediction) or LCM-style fresh noise")
     ap.add_argument("--cfg", choices=["self", "onetime", "full"], default=None,
                     help="guidance variant (default: the workload's own, self-negative R-CFG for the video DiT)")
     ap.add_argument("--sweep", action="store_true",
@@ -156,7 +158,7 @@ def measure(cfg, weights, steps: int, warmup: int, dev):
     total = (warmup + steps + 2) * B
     src, nz = gen.LatentSource(cfg), gen.NoiseSource(cfg)
     xs = [torch.from_numpy(src.next()).to(dev) for _ in range(total)]
-    ns = [torch.from_numpy(nz.next()).to(dev) for _ in range(total)]
+    ns = [torch.from_numpy(gen.frame_noise(cfg, nz)).to(dev) for _ in range(total)]
     out = run.out
     torch.cuda.synchronize()
     k = 0
@@ -240,7 +242,8 @@ def measure(cfg, weights, steps: int, warmup: int, dev):
                                f"({cfg.tokens} tokens), sink {cfg.sink_tokens} + window {cfg.window_tokens}, "
                                f"n={cfg.n_slots} slots, B={B} chunks per step, guidance {cfg.cfg_type}, "
                                f"ctx {cfg.ctx_len}, motion {'on' if cfg.motion_on else 'off'}"
-                               + (", cross-frame batch attention" if cfg.batch_attn else ""),
+                               + (", cross-frame batch attention" if cfg.batch_attn else "")
+                               + (f", {cfg.sampler} sampler" if cfg.sampler != "ddim" else ""),
                    "rows_per_step": cfg.rows_per_step, "tokens_per_row": cfg.tokens,
                    "frames_per_step": B * cfg.latent_t, "parallelism": "single GPU"},
         "ttff_ms": round(ttff_ms, 2) if ttff_ms else None,
@@ -266,7 +269,8 @@ def slo_run(cfg, weights, target_fps: float, steps: int, dev):
         neg = torch.from_numpy(gen.make_context(cfg, True)).to(dev).to(tdt) if cfg.cfg_type != "self" else None
         run.set_context(torch.from_numpy(gen.make_context(cfg)).to(dev).to(tdt), neg)
     src, nz = gen.LatentSource(cfg), gen.NoiseSource(cfg)
-    pool = [(torch.from_numpy(src.next()).to(dev), torch.from_numpy(nz.next()).to(dev)) for _ in range(16)]
+    pool = [(torch.from_numpy(src.next()).to(dev), torch.from_numpy(gen.frame_noise(cfg, nz)).to(dev))
+            for _ in range(16)]
     sch = SLOBatchScheduler(cfg.latent_t, target_fps, cfg.chunks_per_step)
     n = cfg.n_slots
     sizes, trace = [], []
@@ -318,6 +322,8 @@ def main():
     kw = {} if args.cfg is None else {"cfg_type": args.cfg}
     if args.batch_attn:
         kw["batch_attn"] = True
+    if args.sampler != "ddim":
+        kw["sampler"] = args.sampler
     if args.slo_fps > 0:
         cfg = get_config(args.workload, t_index=slot_indices(args.n_slots), chunks_per_step=max(2, args.chunks), **kw)
         weights = random_device_weights(cfg, seed=gen.SEED_WEIGHTS)

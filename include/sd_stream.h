@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SD_ABI_VERSION 2
+#define SD_ABI_VERSION 3
 #define SD_MAX_SLOTS 8       /* n, denoising steps in flight */
 #define SD_MAX_ROWS 40       /* rows per forward: B*n (+B onetime-negative, 2*B*n full CFG) */
 #define SD_MAX_CHUNKS 8      /* chunks per step (B) */
@@ -72,6 +72,11 @@ typedef enum { SD_DTYPE_F32 = 0, SD_DTYPE_BF16 = 1 } sd_dtype;
  * the virtual residual (with delta = 1: eps_u + gamma (eps_c - eps_u)). */
 typedef enum { SD_CFG_SELF = 0, SD_CFG_ONETIME = 1, SD_CFG_FULL = 2 } sd_cfg_type;
 typedef enum { SD_SSF_U8 = 0, SD_SSF_LATENT = 1 } sd_ssf_kind;
+/* Per-slot latent update.  The pages name no sampler.  DDIM (eta = 0) hands
+ * the next slot a_next x0_hat + b_next eps_cfg; the LCM-style update (the
+ * pages pair the pipeline with LCM models) re-noises with fresh noise,
+ * a_next x0_hat + b_next z, z given with the frame for each later slot. */
+typedef enum { SD_SAMPLER_DDIM = 0, SD_SAMPLER_LCM = 1 } sd_sampler;
 
 typedef struct {
   uint32_t abi_version;            /* must be SD_ABI_VERSION */
@@ -112,6 +117,7 @@ typedef struct {
    * the own tokens of every row of the forward] instead of [sink | window |
    * its own tokens].  Self-negative R-CFG only (the rows share one prompt). */
   int32_t batch_attn;
+  int32_t sampler;                 /* sd_sampler */
 } sd_stream_config;
 
 /*
@@ -185,7 +191,9 @@ sd_status sd_stream_create(const sd_stream_config* cfg, const sd_weights* w, voi
 sd_status sd_stream_set_context(sd_stream* s, const void* ctx_pos, const void* ctx_neg);
 
 /* Offer one chunk.  x0 and noise are device fp32 [T][C][H][W] (noise ~ N(0,1),
- * the entry noise of this frame); ssf_frame is a device uint8 [h][w][c] image
+ * the entry noise of this frame; with SD_SAMPLER_LCM noise is [n][T][C][H][W]:
+ * the entry noise, then the noise slots 1 .. n-1 re-noise with, copied into
+ * the frame store); ssf_frame is a device uint8 [h][w][c] image
  * for SD_SSF_U8 (ignored otherwise); u is the host uniform in [0,1) for the
  * SSF draw.  A skipped frame changes nothing but the skip counter. */
 sd_status sd_stream_push_frame(sd_stream* s, const float* x0, const float* noise,

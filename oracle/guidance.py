@@ -11,7 +11,10 @@ StreamDiffusion paper notes, section 2 (R-CFG):
 
 The pages name no sampler.  Reading: deterministic DDIM (eta = 0):
 x0_hat = (x_tau - b_tau eps_cfg) / a_tau, the next slot receives
-a_next x0_hat + b_next eps_cfg, the last slot emits x0_hat.
+a_next x0_hat + b_next eps_cfg, the last slot emits x0_hat.  The LCM-style
+variant (the pages pair the pipeline with LCM models) re-noises x0_hat with
+fresh noise z instead: a_next x0_hat + b_next z, z drawn per frame and slot and
+passed in with the frame.
 
 Pins (tests/test_oracle_guidance.py): gamma = 1 gives eps_c; delta = 0 gives
 gamma eps_c; at the entry slot the virtual residual equals the entry noise;

@@ -50,6 +50,7 @@ class Frame:
     taus: List[int]
     t0: int                   # temporal RoPE base
     x0_star: Optional[np.ndarray] = None
+    renoise: Optional[List[np.ndarray]] = None   # LCM sampler: noise of slots 1 .. n-1
 
 
 @dataclass
@@ -179,8 +180,14 @@ class OracleStream:
         t0 = self.rope_p
         self.rope_p += T
         a0, b0 = self.a[taus[0]], self.b[taus[0]]
-        x = guidance.entry_noise(x0.astype(self.dtype), np.asarray(noise, self.dtype), a0, b0)
+        lcm = getattr(cfg, "sampler", "ddim") == "lcm"
+        noise = np.asarray(noise, self.dtype)
+        if lcm and noise.shape != (cfg.n_slots,) + x0.shape:
+            raise ValueError("the LCM sampler takes n noise latents per frame (entry, then one per later slot)")
+        x = guidance.entry_noise(x0.astype(self.dtype), noise[0] if lcm else noise, a0, b0)
         fr = Frame(self.n_pushed, x0.astype(self.dtype), x, taus, t0)
+        if lcm:
+            fr.renoise = [noise[i] for i in range(1, cfg.n_slots)]
         if cfg.cfg_type != "onetime":
             fr.x0_star = fr.x0
         self.pending.append(fr)
@@ -277,7 +284,9 @@ class OracleStream:
             x0_hat = guidance.predict_x0(f.x, eps_cfg, a, b)
             if i < n - 1:
                 tn = f.taus[i + 1]
-                f.x = guidance.renoise(x0_hat, eps_cfg, self.a[tn], self.b[tn])
+                # DDIM re-noises with the guided prediction, LCM with fresh noise
+                z = eps_cfg if f.renoise is None else f.renoise[i]
+                f.x = guidance.renoise(x0_hat, z, self.a[tn], self.b[tn])
             else:
                 outs.append(x0_hat)
                 exits.append((f, exit_kv, exit_hidden))

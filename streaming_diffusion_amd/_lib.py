@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libsdstream.so")
 STATE_LIB_PATH = os.path.join(PKG, "libsdstate.so")
 
-SD_ABI_VERSION = 2
+SD_ABI_VERSION = 3
 SD_MAX_SLOTS = 8
 SD_MAX_ROWS = 40
 SD_MAX_SINK = 8
@@ -24,6 +24,7 @@ STATUS_NAMES = {0: "SD_OK", -1: "SD_ERR_ARG", -2: "SD_ERR_SHAPE", -3: "SD_ERR_ST
 SD_DTYPE_F32, SD_DTYPE_BF16 = 0, 1
 SD_CFG_SELF, SD_CFG_ONETIME, SD_CFG_FULL = 0, 1, 2
 SD_SSF_U8, SD_SSF_LATENT = 0, 1
+SD_SAMPLER_DDIM, SD_SAMPLER_LCM = 0, 1
 SD_BUF_EPS, SD_BUF_RING_K, SD_BUF_RING_V, SD_BUF_SINK_K, SD_BUF_SINK_V, SD_BUF_RESID, SD_BUF_MOD = range(7)
 
 
@@ -43,6 +44,7 @@ class sd_stream_config(C.Structure):
         ("ssf_c", C.c_int32), ("ssf_eta", C.c_double), ("max_skip_frame", C.c_int32),
         ("motion_on", C.c_int32), ("motion_k", C.c_int32), ("motion_lambda", C.c_double), ("s_min", C.c_double),
         ("s_max", C.c_double), ("motion_sigma", C.c_double), ("batch_attn", C.c_int32),
+        ("sampler", C.c_int32),
     ]
 
 

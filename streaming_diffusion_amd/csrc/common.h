@@ -62,6 +62,7 @@ struct RowInfo {
   int32_t oidx;       // last slot: position of the frame among the step's outputs
   int32_t neg;        // entering frame with onetime R-CFG: its negative row, else -1
   int32_t pair;       // full CFG: the row's twin under the negative prompt, else -1
+  int32_t zrow;       // LCM sampler, not the last slot: record of the re-noise latent, else -1
 };
 struct RowTable {
   int32_t R;

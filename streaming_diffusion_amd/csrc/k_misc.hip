@@ -33,12 +33,13 @@ hipError_t entry_noise(hipStream_t s, const float* x0, const float* noise, float
 // Residual CFG (StreamDiffusion paper notes, section 2): virtual residual
 // noise eps' = (x - a x0*) / b, eps_cfg = delta eps' + gamma (eps_c - delta eps'),
 // then x0_hat = (x - b eps_cfg) / a and either re-noise to the next slot's
-// timestep or emit x0_hat (to output position oidx of the step).  For
+// timestep (DDIM: with eps_cfg; LCM sampler: with the frame's noise record
+// zrow) or emit x0_hat (to output position oidx of the step).  For
 // onetime-negative R-CFG an entering row first turns its negative row's output
 // into its x0* estimate; under full CFG eps' is the twin row's output.
 __global__ void rcfg_update_kernel(RowTable rt, float* __restrict__ store_x, float* __restrict__ store_x0s,
-                                   const float* __restrict__ eps, float* __restrict__ out, int64_t lat, float gamma,
-                                   float delta) {
+                                   const float* __restrict__ eps, const float* __restrict__ store_z,
+                                   float* __restrict__ out, int64_t lat, float gamma, float delta) {
   const int r = blockIdx.y;
   const RowInfo ri = rt.r[r];
   if (ri.kind != 0) return;
@@ -66,14 +67,17 @@ __global__ void rcfg_update_kernel(RowTable rt, float* __restrict__ store_x, flo
   if (ri.last) {
     out[(int64_t)ri.oidx * lat + i] = x0h;
   } else {
-    store_x[off] = ri.an * x0h + ri.bn * ecfg;
+    // DDIM re-noises with the guided prediction, the LCM sampler with the
+    // frame's fresh noise for the next slot
+    const float z = ri.zrow >= 0 ? store_z[(int64_t)ri.zrow * lat + i] : ecfg;
+    store_x[off] = ri.an * x0h + ri.bn * z;
   }
 }
 
 hipError_t rcfg_update(hipStream_t s, const RowTable& rt, float* store_x, float* store_x0s, const float* eps,
-                       float* out, int64_t lat, float gamma, float delta) {
+                       const float* store_z, float* out, int64_t lat, float gamma, float delta) {
   dim3 g(grid1(lat, 256), rt.R);
-  rcfg_update_kernel<<<g, 256, 0, s>>>(rt, store_x, store_x0s, eps, out, lat, gamma, delta);
+  rcfg_update_kernel<<<g, 256, 0, s>>>(rt, store_x, store_x0s, eps, store_z, out, lat, gamma, delta);
   return hipGetLastError();
 }
 

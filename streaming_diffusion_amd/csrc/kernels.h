@@ -11,7 +11,7 @@ hipError_t entry_noise(hipStream_t s, const float* x0, const float* noise, float
                        float a, float b);
 // R-CFG, x0 prediction and re-noise for every denoise row of rt.
 hipError_t rcfg_update(hipStream_t s, const RowTable& rt, float* store_x, float* store_x0s, const float* eps,
-                       float* out, int64_t lat, float gamma, float delta);
+                       const float* store_z, float* out, int64_t lat, float gamma, float delta);
 // Gather patches of each row's latent into [R*L][p*p*C] (element type by bf).
 hipError_t patchify(hipStream_t s, bool bf, const RowTable& rt, const float* store_x, void* out, int64_t lat,
                     int T, int C, int Hl, int Wl, int p);

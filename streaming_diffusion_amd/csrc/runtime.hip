@@ -46,6 +46,7 @@ struct sd_stream {
   std::vector<double> a, b;
   // device regions
   float *fx = nullptr, *fx0s = nullptr;
+  float* fz = nullptr;          // LCM sampler: per frame record, the n-1 re-noise latents
   void* ssf_ref = nullptr;
   long long* sums = nullptr;      // [0..2] ssf, [4..4+T) motion
   float* mprev = nullptr;
@@ -147,6 +148,7 @@ size_t carve(sd_stream* s, char* base) {
   const int nctx = c.cfg_type != SD_CFG_SELF ? 2 : 1;
   s->fx = cv.take<float>((size_t)s->NF * s->lat * 4);
   s->fx0s = cv.take<float>((size_t)s->NF * s->lat * 4);
+  if (c.sampler == SD_SAMPLER_LCM && s->n > 1) s->fz = cv.take<float>((size_t)s->NF * (s->n - 1) * s->lat * 4);
   if (c.ssf_on) {
     const size_t rb = c.ssf_kind == SD_SSF_U8 ? (size_t)c.ssf_h * c.ssf_w * c.ssf_c : (size_t)s->lat * 4;
     s->ssf_ref = cv.take<void>(rb);
@@ -458,6 +460,9 @@ sd_status sd_stream_push_frame(sd_stream* s, const float* x0, const float* noise
   PROF(SD_PROF_EPILOGUE, 2.0 * s->lat, 16.0 * s->lat,
        sdk::entry_noise(s->st, x0, noise, s->fx + (int64_t)f * s->lat, s->fx0s + (int64_t)f * s->lat, s->lat,
                         (float)s->a[tau0], (float)s->b[tau0]));
+  if (s->fz)
+    HIP_TRY(hipMemcpyAsync(s->fz + (int64_t)f * (s->n - 1) * s->lat, noise + s->lat,
+                           (size_t)(s->n - 1) * s->lat * 4, hipMemcpyDeviceToDevice, s->st));
   s->pending.push_back(f);
   info->t0 = fr.t0;
   info->frame_id = fr.fid;
@@ -521,6 +526,7 @@ sd_status sd_stream_step_chunks(sd_stream* s, int32_t chunks, float* out_latent,
       ri.oidx = ri.last ? nexit : 0;
       ri.neg = -1;
       ri.pair = -1;
+      ri.zrow = (s->fz && i + 1 < n) ? f * (n - 1) + i : -1;
       if (ri.last) exit_rows[nexit++] = R;
       ++R;
     }
@@ -795,7 +801,7 @@ sd_status sd_stream_step_chunks(sd_stream* s, int32_t chunks, float* out_latent,
   }
   // ---- R-CFG, x0 prediction, re-noise / emit
   PROF(SD_PROF_EPILOGUE, 12.0 * R * s->lat, 16.0 * R * s->lat,
-       sdk::rcfg_update(st, rt, s->fx, s->fx0s, s->eps, out_latent, s->lat, (float)c.gamma, (float)c.delta));
+       sdk::rcfg_update(st, rt, s->fx, s->fx0s, s->eps, s->fz, out_latent, s->lat, (float)c.gamma, (float)c.delta));
 
   // ---- host bookkeeping
   info->step = s->n_steps++;

@@ -179,3 +179,13 @@ def test_motion_bit_exact(state):
         s_o = controls.motion_update(s, win, cfg)
         assert s_c == s_o
         s = s_o
+
+
+def test_unknown_sampler_and_batch_flag_are_rejected(lib, state):
+    for field, value in (("sampler", 7), ("batch_attn", 2)):
+        c = cfg_struct("tiny")
+        setattr(c, field, value)
+        assert state.sdstate_validate(C.byref(c), None, 0) == L.SD_ERR_ARG
+        assert lib.sd_stream_workspace_bytes(C.byref(c)) == 0
+    c = cfg_struct("tiny", sampler="lcm")
+    assert state.sdstate_validate(C.byref(c), None, 0) == L.SD_OK

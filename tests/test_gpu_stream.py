@@ -46,7 +46,7 @@ def run_parity(cfg, steps, check_ring=True, sizes=None):
     done = pushes = queued = 0
     worst = 0.0
     while done < steps:
-        x0, e, u = src.next(), nz.next(), us.next()
+        x0, e, u = src.next(), gen.frame_noise(cfg, nz), us.next()
         frame = ssf_src.next() if ssf_src else None
         po = orc.push_frame(x0, e, frame, u)
         pg = run.push(to_dev(x0, torch.float32), to_dev(e, torch.float32),
@@ -231,6 +231,20 @@ def test_video_bf16_batch_attention_two_chunks_per_step():
     print("video bf16 reduced batch attention B=2", flush=True)
     orc, _ = run_parity(cfg, 8)
     assert orc.kv_valid == cfg.window_tokens
+
+
+def test_tiny_fp32_lcm_sampler_three_slots():
+    device()
+    cfg = reduced("tiny", ssf_on=False, sampler="lcm", t_index=(10, 32, 45))
+    print("tiny fp32 LCM sampler n=3", flush=True)
+    run_parity(cfg, 7)
+
+
+def test_video_bf16_lcm_sampler_two_chunks_per_step():
+    device()
+    cfg = reduced("video13b", sampler="lcm", chunks_per_step=2)
+    print("video bf16 reduced LCM sampler B=2", flush=True)
+    run_parity(cfg, 6)
 
 
 def test_step_chunks_out_of_range():

@@ -373,3 +373,60 @@ def test_full_cfg_needs_a_negative_context():
     cfg = small_cfg(ctx_len=4, cfg_type="full")
     with pytest.raises(ValueError):
         OracleStream(cfg, gen.make_weights(cfg), ctx_pos=gen.make_context(cfg))
+
+
+# ------------------------------------------------------------------ LCM-style re-noise
+def lcm_noise(nz, n):
+    return np.stack([nz.next() for _ in range(n)])
+
+
+@pytest.mark.parametrize("t_index", [(32, 45), (0, 16, 32, 45)])
+def test_lcm_identity_pipeline_emits_inputs(t_index):
+    """With eps_c := eps' and delta = 1, x0_hat = x0 at every slot whatever
+    noise the previous slot re-noised with."""
+    cfg = get_config("tiny", t_index=t_index, sampler="lcm", gamma=2.3, delta=1.0, ssf_on=False)
+    st = OracleStream(cfg, None, identity_denoiser=True)
+    src, nz = gen.LatentSource(cfg), gen.NoiseSource(cfg)
+    n, ins, outs = cfg.n_slots, [], []
+    for _ in range(8):
+        x0 = src.next()
+        ins.append(x0)
+        st.push_frame(x0, lcm_noise(nz, n))
+        out, _ = st.step()
+        if out is not None:
+            outs.append(out)
+    for k, o in enumerate(outs):
+        assert np.allclose(o, ins[k], atol=1e-11)
+
+
+def test_lcm_slots_hold_the_fresh_noise_closed_form():
+    """After the first step the frame's slot-1 latent is exactly
+    a1 x0_hat + b1 z1 (z1 the frame's second noise latent), not the DDIM
+    a1 x0_hat + b1 eps_cfg."""
+    cfg = small_cfg(t_index=(16, 45), sampler="lcm", window_tokens=0, sink_tokens=0)
+    w = gen.make_weights(cfg)
+    st = OracleStream(cfg, w)
+    net = Denoiser(cfg, w)
+    a, b = schedule.sched_coeffs(cfg)
+    src, nz = gen.LatentSource(cfg), gen.NoiseSource(cfg)
+    x0 = src.next()
+    z = lcm_noise(nz, 2)
+    info = st.push_frame(x0, z)
+    st.step()
+    t0, t1 = info.taus
+    x = a[t0] * x0.astype(np.float64) + b[t0] * z[0].astype(np.float64)
+    ec = net.forward_row(x, t0, info.t0)
+    ep = (x - a[t0] * x0) / b[t0]
+    eps = cfg.delta * ep + cfg.gamma * (ec - cfg.delta * ep)
+    x0h = (x - b[t0] * eps) / a[t0]
+    want = a[t1] * x0h + b[t1] * z[1].astype(np.float64)
+    assert np.allclose(st.slots[0][0].x, want, rtol=0, atol=1e-12)
+    assert not np.allclose(st.slots[0][0].x, a[t1] * x0h + b[t1] * eps, rtol=0, atol=1e-6)
+
+
+def test_lcm_needs_n_noise_latents():
+    cfg = get_config("tiny", sampler="lcm", ssf_on=False)
+    st = OracleStream(cfg, None, identity_denoiser=True)
+    src, nz = gen.LatentSource(cfg), gen.NoiseSource(cfg)
+    with pytest.raises(ValueError):
+        st.push_frame(src.next(), nz.next())

@@ -38,6 +38,7 @@ class Config:
     delta: float = 1.0
     chunks_per_step: int = 1        # B
     batch_attn: bool = False        # cross-frame batch attention (rows attend to every row's tokens)
+    sampler: str = "ddim"           # "ddim" (re-noise with eps_cfg) | "lcm" (re-noise with fresh noise)
     # KV cache (tokens)
     sink_tokens: int = 0
     window_tokens: int = 0

@@ -89,6 +89,14 @@ def make_weights(cfg: Config, seed: int = SEED_WEIGHTS, std: float = WEIGHT_STD)
     return out
 
 
+def frame_noise(cfg: Config, nz: "NoiseSource"):
+    """The noise one push takes: the entry noise, or for the LCM sampler the
+    entry noise and then one latent per later slot ([n][T][C][H][W])."""
+    if getattr(cfg, "sampler", "ddim") == "lcm":
+        return np.stack([nz.next() for _ in range(cfg.n_slots)])
+    return nz.next()
+
+
 def make_context(cfg: Config, negative: bool = False):
     if cfg.ctx_len == 0:
         return None
