@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--chunks", type=int, default=1, help="B: chunks entering (and leaving) per step")
     ap.add_argument("--batch-attn", action="store_true",
                     help="cross-frame batch attention: every row attends to the own tokens of all rows")
+    ap.add_argument("--kv-recompute", action="store_true",
+                    help="leaving chunks' cache entries from a clean-latent forward at timestep 0 (+B rows per step)")
     ap.add_argument("--sampler", choices=["ddim", "lcm"], default="ddim",
                     help="per-slot update: DDIM (re-noise with the guided prediction) or LCM-style fresh noise")
     ap.add_argument("--cfg", choices=["self", "onetime", "full"], default=None,
@@ -243,7 +245,8 @@ def measure(cfg, weights, steps: int, warmup: int, dev):
                                f"n={cfg.n_slots} slots, B={B} chunks per step, guidance {cfg.cfg_type}, "
                                f"ctx {cfg.ctx_len}, motion {'on' if cfg.motion_on else 'off'}"
                                + (", cross-frame batch attention" if cfg.batch_attn else "")
-                               + (f", {cfg.sampler} sampler" if cfg.sampler != "ddim" else ""),
+                               + (f", {cfg.sampler} sampler" if cfg.sampler != "ddim" else "")
+                               + (", clean-latent KV recompute" if cfg.kv_recompute else ""),
                    "rows_per_step": cfg.rows_per_step, "tokens_per_row": cfg.tokens,
                    "frames_per_step": B * cfg.latent_t, "parallelism": "single GPU"},
         "ttff_ms": round(ttff_ms, 2) if ttff_ms else None,
@@ -324,6 +327,8 @@ def main():
         kw["batch_attn"] = True
     if args.sampler != "ddim":
         kw["sampler"] = args.sampler
+    if args.kv_recompute:
+        kw["kv_recompute"] = True
     if args.slo_fps > 0:
         cfg = get_config(args.workload, t_index=slot_indices(args.n_slots), chunks_per_step=max(2, args.chunks), **kw)
         weights = random_device_weights(cfg, seed=gen.SEED_WEIGHTS)

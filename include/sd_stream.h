@@ -47,9 +47,9 @@
 extern "C" {
 #endif
 
-#define SD_ABI_VERSION 3
+#define SD_ABI_VERSION 4
 #define SD_MAX_SLOTS 8       /* n, denoising steps in flight */
-#define SD_MAX_ROWS 40       /* rows per forward: B*n (+B onetime-negative, 2*B*n full CFG) */
+#define SD_MAX_ROWS 40       /* rows per step: B*n (+B onetime-negative, 2*B*n full CFG; +B kv_recompute) */
 #define SD_MAX_CHUNKS 8      /* chunks per step (B) */
 #define SD_MAX_SINK 8        /* sink entries M */
 
@@ -118,6 +118,11 @@ typedef struct {
    * its own tokens].  Self-negative R-CFG only (the rows share one prompt). */
   int32_t batch_attn;
   int32_t sampler;                 /* sd_sampler */
+  /* clean-latent KV recompute: the K/V a leaving chunk appends to the cache
+   * (and the hidden state of its sink decision) come from one more forward of
+   * its emitted latent at timestep 0 against the same cache, instead of from
+   * its last denoising forward; + B rows per step */
+  int32_t kv_recompute;
 } sd_stream_config;
 
 /*

@@ -19,7 +19,10 @@ Readings:
   the least similar entry;
 * RoPE refresh: a host counter p gives a chunk of T frames temporal positions
   p..p+T-1; if p+T-1 would exceed the threshold, p restarts at 0 first.
-* kv_reset clears ring, sink and the RoPE counter; frames in flight continue.
+* kv_reset clears ring, sink and the RoPE counter; frames in flight continue;
+* with kv_recompute the K/V a leaving chunk appends (and the hidden state its
+  sink decision uses) come instead from one more forward of its emitted
+  x0_hat at timestep 0, against the same snapshot.
 
 Pins (tests/test_oracle_stream.py): the identity pipeline returns every input
 frame; with the cache frozen the pipelined output equals the same frame
@@ -291,6 +294,20 @@ class OracleStream:
                 outs.append(x0_hat)
                 exits.append((f, exit_kv, exit_hidden))
         n_rows = len(rows) + len(neg_eps) + len(uncond)
+        if getattr(cfg, "kv_recompute", False) and exits and not self.identity:
+            # clean-latent recompute: the leaving chunks' cache entries and sink
+            # embeddings come from a forward of their emitted x0_hat at tau = 0
+            # over the same snapshot; its eps is not used
+            frames = [f for f, _, _ in exits]
+            if getattr(cfg, "batch_attn", False):
+                clean = self.net.forward_batch([(x, 0, f.t0) for f, x in zip(frames, outs)], snapshot,
+                                               self.ctx_kv, collect=set(range(len(frames))))
+            else:
+                clean = [self.net.forward_row(x, 0, f.t0, snapshot, self.ctx_kv, collect=True)
+                         for f, x in zip(frames, outs)]
+            exits = [(f, kv, hidden) for f, (_, kv, hidden) in zip(frames, clean)]
+            self.last_eps.extend(e for e, _, _ in clean)
+            n_rows += len(clean)
         info = StepInfo(self.n_steps, bool(exits), exits[0][0].fid if exits else -1, n_rows,
                         0, 0, 0, False, -1, float("nan"), self.rope_p, len(exits))
         if exits:

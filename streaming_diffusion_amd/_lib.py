@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libsdstream.so")
 STATE_LIB_PATH = os.path.join(PKG, "libsdstate.so")
 
-SD_ABI_VERSION = 3
+SD_ABI_VERSION = 4
 SD_MAX_SLOTS = 8
 SD_MAX_ROWS = 40
 SD_MAX_SINK = 8
@@ -44,7 +44,7 @@ class sd_stream_config(C.Structure):
         ("ssf_c", C.c_int32), ("ssf_eta", C.c_double), ("max_skip_frame", C.c_int32),
         ("motion_on", C.c_int32), ("motion_k", C.c_int32), ("motion_lambda", C.c_double), ("s_min", C.c_double),
         ("s_max", C.c_double), ("motion_sigma", C.c_double), ("batch_attn", C.c_int32),
-        ("sampler", C.c_int32),
+        ("sampler", C.c_int32), ("kv_recompute", C.c_int32),
     ]
 
 

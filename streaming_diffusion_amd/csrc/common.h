@@ -63,6 +63,7 @@ struct RowInfo {
   int32_t neg;        // entering frame with onetime R-CFG: its negative row, else -1
   int32_t pair;       // full CFG: the row's twin under the negative prompt, else -1
   int32_t zrow;       // LCM sampler, not the last slot: record of the re-noise latent, else -1
+  int32_t keep;       // last slot with clean-latent recompute: x0_hat also stays in the frame record
 };
 struct RowTable {
   int32_t R;

@@ -38,6 +38,7 @@ int validate_config(const sd_stream_config& c, std::string* err) {
   if (!std::isfinite(c.gamma) || !std::isfinite(c.delta)) return fail(err, SD_ERR_ARG, "gamma/delta must be finite");
   if (c.batch_attn != 0 && c.batch_attn != 1) return fail(err, SD_ERR_ARG, "batch_attn must be 0 or 1");
   if (c.sampler != SD_SAMPLER_DDIM && c.sampler != SD_SAMPLER_LCM) return fail(err, SD_ERR_ARG, "unknown sampler");
+  if (c.kv_recompute != 0 && c.kv_recompute != 1) return fail(err, SD_ERR_ARG, "kv_recompute must be 0 or 1");
   if (c.batch_attn && c.cfg_type != SD_CFG_SELF)
     return fail(err, SD_ERR_ARG, "batch attention needs self-negative R-CFG (all rows under one prompt)");
   if (c.n_train_steps < 50 || c.n_train_steps > 100000) return fail(err, SD_ERR_ARG, "n_train_steps out of range");

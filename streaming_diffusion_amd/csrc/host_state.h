@@ -23,8 +23,9 @@ inline int64_t latent_elems(const sd_stream_config& c) {
 }
 inline int rows_max(const sd_stream_config& c) {
   const int pos = c.chunks_per_step * c.n_slots;
-  if (c.cfg_type == SD_CFG_FULL) return 2 * pos;
-  return pos + (c.cfg_type == SD_CFG_ONETIME ? c.chunks_per_step : 0);
+  const int clean = c.kv_recompute ? c.chunks_per_step : 0;
+  if (c.cfg_type == SD_CFG_FULL) return 2 * pos + clean;
+  return pos + (c.cfg_type == SD_CFG_ONETIME ? c.chunks_per_step : 0) + clean;
 }
 
 // Scaled-linear schedule: sqrt(beta_t) linear in t; alpha_t = prod(1 - beta).

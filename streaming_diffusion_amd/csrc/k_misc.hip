@@ -66,6 +66,7 @@ __global__ void rcfg_update_kernel(RowTable rt, float* __restrict__ store_x, flo
   const float x0h = (x - ri.b * ecfg) / ri.a;
   if (ri.last) {
     out[(int64_t)ri.oidx * lat + i] = x0h;
+    if (ri.keep) store_x[off] = x0h;
   } else {
     // DDIM re-noises with the guided prediction, the LCM sampler with the
     // frame's fresh noise for the next slot

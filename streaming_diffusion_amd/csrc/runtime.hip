@@ -470,105 +470,34 @@ sd_status sd_stream_push_frame(sd_stream* s, const float* x0, const float* noise
   return SD_OK;
 }
 
-sd_status sd_stream_step(sd_stream* s, float* out_latent, sd_step_info* info) {
-  if (!s) return SD_ERR_ARG;
-  return sd_stream_step_chunks(s, s->B, out_latent, info);
-}
+// Which rows of a forward leave the pipeline and take the cache updates: in
+// push order, row rows[k] appends its K / V^T at ring position ptr_old + k L
+// (and fills sink entry cap_entry[k], or stages a refresh candidate), then
+// takes its sink decision after the last block.
+struct ExitPlan {
+  int n;
+  const int* rows;
+  const int* cap_entry;
+  int ptr_old;
+};
 
-sd_status sd_stream_step_chunks(sd_stream* s, int32_t chunks, float* out_latent, sd_step_info* info) {
-  if (!s) return SD_ERR_ARG;
+// One denoiser forward over the rows of rt (rows [0, R_pos) under the
+// positive prompt, the nneg after them under the negative one): conditioning,
+// patch embedding, the blocks, the final layer; eps_out receives eps of row r
+// at eps_out + r * lat.  With xp the leaving rows update the KV cache and the
+// sink; without it the cache is only read.
+static sd_status run_forward(sd_stream* s, const RowTable& rt, int R_pos, int nneg, const ExitPlan* xp,
+                             float* eps_out) {
   const sd_stream_config& c = s->cfg;
-  if (!info) return set_err(s, SD_ERR_ARG, "info is null");
-  const int n = s->n, B = s->B;
-  if (chunks < 1 || chunks > B) return set_err(s, SD_ERR_ARG, "chunks must be in [1, chunks_per_step]");
-  if ((int)s->pending.size() < chunks) return set_err(s, SD_ERR_NOT_READY, "fewer pending chunks than requested");
-  if (!s->ctx_set) return set_err(s, SD_ERR_STATE, "set_context() must be called first");
-  const bool will_exit = (n == 1) || (s->slots[(n - 2) * B] >= 0);
-  if (will_exit && !out_latent) return set_err(s, SD_ERR_ARG, "out_latent is null but frames leave this step");
-  std::memset(info, 0, sizeof(*info));
-
-  // ---- slot-group shift (the B oldest pending chunks enter slot 0) and row
-  // table: slot by slot, the chunks of a slot in push order
-  for (int i = n - 1; i >= 1; --i)
-    for (int k = 0; k < B; ++k) s->slots[i * B + k] = s->slots[(i - 1) * B + k];
-  for (int k = 0; k < B; ++k) {
-    if (k < chunks) {
-      s->slots[k] = s->pending.front();
-      s->pending.pop_front();
-    } else {
-      s->slots[k] = -1;       // a smaller group leaves its upper lanes empty
-    }
-  }
-  RowTable rt;
-  std::memset(&rt, 0, sizeof(rt));
-  int R = 0, nexit = 0;
-  int exit_rows[SD_MAX_CHUNKS];
-  for (int i = 0; i < n; ++i) {
-    for (int k = 0; k < B; ++k) {
-      const int f = s->slots[i * B + k];
-      if (f < 0) continue;
-      const FrameRec& fr = s->frames[f];
-      RowInfo& ri = rt.r[R];
-      ri.frame = f;
-      ri.tau = fr.taus[i];
-      ri.t0 = fr.t0;
-      ri.kind = 0;
-      ri.last = (i == n - 1);
-      ri.ctx = 0;
-      ri.a = (float)s->a[ri.tau];
-      ri.b = (float)s->b[ri.tau];
-      if (i + 1 < n) {
-        ri.an = (float)s->a[fr.taus[i + 1]];
-        ri.bn = (float)s->b[fr.taus[i + 1]];
-      }
-      ri.a0 = (float)s->a[fr.taus[0]];
-      ri.b0 = (float)s->b[fr.taus[0]];
-      ri.oidx = ri.last ? nexit : 0;
-      ri.neg = -1;
-      ri.pair = -1;
-      ri.zrow = (s->fz && i + 1 < n) ? f * (n - 1) + i : -1;
-      if (ri.last) exit_rows[nexit++] = R;
-      ++R;
-    }
-  }
-  const int R_pos = R;
-  int nneg = 0;
-  if (c.cfg_type == SD_CFG_ONETIME) {
-    // one negative-prompt row per entering chunk (rows 0 .. chunks-1 are slot 0)
-    for (int k = 0; k < chunks; ++k) {
-      rt.r[R] = rt.r[k];
-      rt.r[R].kind = 1;
-      rt.r[R].last = 0;
-      rt.r[R].ctx = 1;
-      rt.r[R].neg = -1;
-      rt.r[k].neg = R;
-      ++R;
-      ++nneg;
-    }
-  } else if (c.cfg_type == SD_CFG_FULL) {
-    // full CFG: a twin of every row under the negative prompt, same order
-    for (int k = 0; k < R_pos; ++k) {
-      rt.r[R] = rt.r[k];
-      rt.r[R].kind = 1;
-      rt.r[R].last = 0;
-      rt.r[R].ctx = 1;
-      rt.r[k].pair = R;
-      ++R;
-      ++nneg;
-    }
-  }
-  rt.R = R;
+  const int R = rt.R;
   const int L = s->L, d = s->d, H = s->H, hd = s->hd, M = R * L;
   const size_t es = s->es;
   const bool bf = s->bf;
   hipStream_t st = s->st;
-  // sink plan of the leaving chunks, in push order: while entries are empty a
-  // chunk captures the next one; later chunks take a refresh decision
-  int cap_entry[SD_MAX_CHUNKS];
-  int sink_count_after = s->sink_count;
-  for (int k = 0; k < nexit; ++k)
-    cap_entry[k] = (s->S > 0 && sink_count_after < s->Ment) ? sink_count_after++ : -1;
-  const int ptr_old = s->kv_ptr;
+  const int nexit = xp ? xp->n : 0;
+  const int* exit_rows = xp ? xp->rows : nullptr;
+  const int* cap_entry = xp ? xp->cap_entry : nullptr;
+  const int ptr_old = xp ? xp->ptr_old : 0;
 
   // ---- conditioning: timestep embedding -> MLP -> SiLU(c) -> adaLN vectors
   PROF(SD_PROF_GEMV, 0.0, 4.0 * R * c.d_freq, sdk::temb_embed(st, rt, s->emb, c.d_freq));
@@ -796,16 +725,151 @@ sd_status sd_stream_step_chunks(sd_stream* s, int32_t chunks, float* out_latent,
   {
     Epi E = epi_base(s, EPI_HEAD);
     E.bias = s->w.head_b;
-    E.eps = s->eps;
+    E.eps = eps_out;
     PROF(SD_PROF_OTHER, gflop(M, s->P, d), gbytes(M, s->P, d, es, 4), sdk::gemm(st, bf, s->xm, s->w.head_w, M, s->P, d, E));
   }
+  return SD_OK;
+}
+
+sd_status sd_stream_step(sd_stream* s, float* out_latent, sd_step_info* info) {
+  if (!s) return SD_ERR_ARG;
+  return sd_stream_step_chunks(s, s->B, out_latent, info);
+}
+
+sd_status sd_stream_step_chunks(sd_stream* s, int32_t chunks, float* out_latent, sd_step_info* info) {
+  if (!s) return SD_ERR_ARG;
+  const sd_stream_config& c = s->cfg;
+  if (!info) return set_err(s, SD_ERR_ARG, "info is null");
+  const int n = s->n, B = s->B;
+  if (chunks < 1 || chunks > B) return set_err(s, SD_ERR_ARG, "chunks must be in [1, chunks_per_step]");
+  if ((int)s->pending.size() < chunks) return set_err(s, SD_ERR_NOT_READY, "fewer pending chunks than requested");
+  if (!s->ctx_set) return set_err(s, SD_ERR_STATE, "set_context() must be called first");
+  const bool will_exit = (n == 1) || (s->slots[(n - 2) * B] >= 0);
+  if (will_exit && !out_latent) return set_err(s, SD_ERR_ARG, "out_latent is null but frames leave this step");
+  std::memset(info, 0, sizeof(*info));
+
+  // ---- slot-group shift (the B oldest pending chunks enter slot 0) and row
+  // table: slot by slot, the chunks of a slot in push order
+  for (int i = n - 1; i >= 1; --i)
+    for (int k = 0; k < B; ++k) s->slots[i * B + k] = s->slots[(i - 1) * B + k];
+  for (int k = 0; k < B; ++k) {
+    if (k < chunks) {
+      s->slots[k] = s->pending.front();
+      s->pending.pop_front();
+    } else {
+      s->slots[k] = -1;       // a smaller group leaves its upper lanes empty
+    }
+  }
+  RowTable rt;
+  std::memset(&rt, 0, sizeof(rt));
+  int R = 0, nexit = 0;
+  int exit_rows[SD_MAX_CHUNKS];
+  for (int i = 0; i < n; ++i) {
+    for (int k = 0; k < B; ++k) {
+      const int f = s->slots[i * B + k];
+      if (f < 0) continue;
+      const FrameRec& fr = s->frames[f];
+      RowInfo& ri = rt.r[R];
+      ri.frame = f;
+      ri.tau = fr.taus[i];
+      ri.t0 = fr.t0;
+      ri.kind = 0;
+      ri.last = (i == n - 1);
+      ri.ctx = 0;
+      ri.a = (float)s->a[ri.tau];
+      ri.b = (float)s->b[ri.tau];
+      if (i + 1 < n) {
+        ri.an = (float)s->a[fr.taus[i + 1]];
+        ri.bn = (float)s->b[fr.taus[i + 1]];
+      }
+      ri.a0 = (float)s->a[fr.taus[0]];
+      ri.b0 = (float)s->b[fr.taus[0]];
+      ri.oidx = ri.last ? nexit : 0;
+      ri.neg = -1;
+      ri.pair = -1;
+      ri.zrow = (s->fz && i + 1 < n) ? f * (n - 1) + i : -1;
+      ri.keep = (i == n - 1 && c.kv_recompute) ? 1 : 0;
+      if (ri.last) exit_rows[nexit++] = R;
+      ++R;
+    }
+  }
+  const int R_pos = R;
+  int nneg = 0;
+  if (c.cfg_type == SD_CFG_ONETIME) {
+    // one negative-prompt row per entering chunk (rows 0 .. chunks-1 are slot 0)
+    for (int k = 0; k < chunks; ++k) {
+      rt.r[R] = rt.r[k];
+      rt.r[R].kind = 1;
+      rt.r[R].last = 0;
+      rt.r[R].ctx = 1;
+      rt.r[R].neg = -1;
+      rt.r[k].neg = R;
+      ++R;
+      ++nneg;
+    }
+  } else if (c.cfg_type == SD_CFG_FULL) {
+    // full CFG: a twin of every row under the negative prompt, same order
+    for (int k = 0; k < R_pos; ++k) {
+      rt.r[R] = rt.r[k];
+      rt.r[R].kind = 1;
+      rt.r[R].last = 0;
+      rt.r[R].ctx = 1;
+      rt.r[k].pair = R;
+      ++R;
+      ++nneg;
+    }
+  }
+  rt.R = R;
+  const int L = s->L;
+  hipStream_t st = s->st;
+  // sink plan of the leaving chunks, in push order: while entries are empty a
+  // chunk captures the next one; later chunks take a refresh decision
+  int cap_entry[SD_MAX_CHUNKS];
+  int sink_count_after = s->sink_count;
+  for (int k = 0; k < nexit; ++k)
+    cap_entry[k] = (s->S > 0 && sink_count_after < s->Ment) ? sink_count_after++ : -1;
+  const int ptr_old = s->kv_ptr;
+
+  const ExitPlan plan{nexit, exit_rows, cap_entry, ptr_old};
+  {
+    // with clean-latent recompute this forward only reads the cache
+    const sd_status fs = run_forward(s, rt, R_pos, nneg, c.kv_recompute ? nullptr : &plan, s->eps);
+    if (fs != SD_OK) return fs;
+  }
+
   // ---- R-CFG, x0 prediction, re-noise / emit
   PROF(SD_PROF_EPILOGUE, 12.0 * R * s->lat, 16.0 * R * s->lat,
        sdk::rcfg_update(st, rt, s->fx, s->fx0s, s->eps, s->fz, out_latent, s->lat, (float)c.gamma, (float)c.delta));
 
+  // ---- clean-latent recompute: the leaving chunks' emitted latents (kept in
+  // their frame records) go through one more forward at timestep 0 against
+  // the same cache; its leaving rows take the cache and sink updates and its
+  // eps lands after the main forward's rows
+  int clean_rows = 0;
+  if (c.kv_recompute && nexit > 0) {
+    RowTable rc;
+    std::memset(&rc, 0, sizeof(rc));
+    int rows_c[SD_MAX_CHUNKS];
+    for (int k = 0; k < nexit; ++k) {
+      RowInfo& ri = rc.r[k];
+      ri = rt.r[exit_rows[k]];
+      ri.tau = 0;
+      ri.a = (float)s->a[0];
+      ri.b = (float)s->b[0];
+      ri.neg = ri.pair = ri.zrow = -1;
+      ri.keep = 0;
+      rows_c[k] = k;
+    }
+    rc.R = nexit;
+    const ExitPlan cplan{nexit, rows_c, cap_entry, ptr_old};
+    const sd_status fs = run_forward(s, rc, nexit, 0, &cplan, s->eps + (int64_t)R * s->lat);
+    if (fs != SD_OK) return fs;
+    clean_rows = nexit;
+  }
+
   // ---- host bookkeeping
   info->step = s->n_steps++;
-  info->rows = R;
+  info->rows = R + clean_rows;
   info->frame_id = -1;
   if (nexit > 0) {
     info->has_output = 1;

@@ -41,6 +41,7 @@ def make_config(cfg) -> L.sd_stream_config:
     c.motion_lambda, c.s_min, c.s_max, c.motion_sigma = cfg.motion_lambda, cfg.s_min, cfg.s_max, cfg.motion_sigma
     c.batch_attn = int(cfg.batch_attn)
     c.sampler = {"ddim": L.SD_SAMPLER_DDIM, "lcm": L.SD_SAMPLER_LCM}[cfg.sampler]
+    c.kv_recompute = int(cfg.kv_recompute)
     return c
 
 

@@ -247,6 +247,22 @@ def test_video_bf16_lcm_sampler_two_chunks_per_step():
     run_parity(cfg, 6)
 
 
+def test_tiny_fp32_clean_latent_kv_recompute():
+    device()
+    cfg = reduced("tiny", ssf_on=False, kv_recompute=True, t_index=(10, 32, 45))
+    print("tiny fp32 clean-latent KV recompute n=3", flush=True)
+    orc, _ = run_parity(cfg, 9)
+    assert orc.sink_count == 1
+
+
+def test_video_bf16_clean_latent_kv_recompute_two_chunks_per_step():
+    device()
+    cfg = reduced("video13b", kv_recompute=True, chunks_per_step=2)
+    print("video bf16 reduced clean-latent KV recompute B=2", flush=True)
+    orc, _ = run_parity(cfg, 8)
+    assert orc.kv_valid == cfg.window_tokens
+
+
 def test_step_chunks_out_of_range():
     device()
     cfg = reduced("tiny", ssf_on=False, chunks_per_step=2)

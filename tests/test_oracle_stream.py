@@ -430,3 +430,55 @@ def test_lcm_needs_n_noise_latents():
     src, nz = gen.LatentSource(cfg), gen.NoiseSource(cfg)
     with pytest.raises(ValueError):
         st.push_frame(src.next(), nz.next())
+
+
+# ------------------------------------------------------------------ clean-latent KV recompute
+def test_kv_recompute_appends_the_clean_forward():
+    """The ring entries a leaving chunk appends are the per-block K/V of a
+    forward of its emitted latent at tau = 0 against the step's snapshot,
+    and the emitted frames are those of the stream without recompute up to
+    the first step that reads a recomputed entry."""
+    cfg = small_cfg(t_index=(16, 45), kv_recompute=True)
+    w = gen.make_weights(cfg)
+    net = Denoiser(cfg, w)
+    st = OracleStream(cfg, w)
+    ref = OracleStream(cfg.replace(kv_recompute=False), w)
+    src, nz = gen.LatentSource(cfg), gen.NoiseSource(cfg)
+    L, W = cfg.tokens, cfg.window_tokens
+    for k in range(5):
+        x0, e = src.next(), nz.next()
+        info = st.push_frame(x0, e)
+        ref.push_frame(x0, e)
+        snap = st.cache_snapshot()
+        ptr = st.kv_ptr
+        out, si = st.step()
+        out_r, _ = ref.step()
+        if k < 2:                        # the first append is read from step 2 on
+            assert (out is None and out_r is None) or np.array_equal(out, out_r)
+        if out is not None:
+            assert si.rows == cfg.n_slots + 1
+            f0 = k - (cfg.n_slots - 1)
+            t0 = f0 * cfg.latent_t       # RoPE base of the leaving frame (no wrap here)
+            _, own, _ = net.forward_row(out, 0, t0, snap, None, collect=True)
+            pos = [(ptr + j) % W for j in range(L)]
+            for b in range(cfg.n_blocks):
+                assert np.array_equal(st.ringK[b][pos], own[b][0])
+                assert np.array_equal(st.ringV[b][pos], own[b][1])
+    assert any(not np.array_equal(a, b) for a, b in [(st.ringK, ref.ringK)])
+
+
+def test_kv_recompute_frozen_cache_changes_nothing_emitted():
+    cfg = small_cfg(t_index=(0, 16, 32, 45), kv_recompute=True)
+    w = gen.make_weights(cfg)
+    a = OracleStream(cfg, w, freeze_cache=True)
+    b = OracleStream(cfg.replace(kv_recompute=False), w, freeze_cache=True)
+    src, nz = gen.LatentSource(cfg), gen.NoiseSource(cfg)
+    for _ in range(6):
+        x0, e = src.next(), nz.next()
+        a.push_frame(x0, e)
+        b.push_frame(x0, e)
+        oa, ia = a.step()
+        ob, ib = b.step()
+        assert (oa is None) == (ob is None)
+        if oa is not None:
+            assert np.array_equal(oa, ob) and ia.rows == ib.rows + 1

@@ -39,6 +39,7 @@ class Config:
     chunks_per_step: int = 1        # B
     batch_attn: bool = False        # cross-frame batch attention (rows attend to every row's tokens)
     sampler: str = "ddim"           # "ddim" (re-noise with eps_cfg) | "lcm" (re-noise with fresh noise)
+    kv_recompute: bool = False      # leaving chunks' cache entries from a clean-latent forward at tau = 0
     # KV cache (tokens)
     sink_tokens: int = 0
     window_tokens: int = 0
@@ -89,9 +90,10 @@ class Config:
     @property
     def rows_per_step(self) -> int:
         pos = self.chunks_per_step * self.n_slots
+        clean = self.chunks_per_step if self.kv_recompute else 0
         if self.cfg_type == "full":
-            return 2 * pos
-        return pos + (self.chunks_per_step if self.cfg_type == "onetime" else 0)
+            return 2 * pos + clean
+        return pos + (self.chunks_per_step if self.cfg_type == "onetime" else 0) + clean
 
     def replace(self, **kw) -> "Config":
         return dataclasses.replace(self, **kw)
