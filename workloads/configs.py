@@ -157,3 +157,47 @@ CONFIGS = {
 def get_config(name: str, **overrides) -> Config:
     cfg = CONFIGS[name]
     return cfg.replace(**overrides) if overrides else cfg
+
+
+# ---------------------------------------------------------------------------
+# Stream-VAE shapes.  A chunk is latent_t latent frames (2 x latent_t pixel
+# frames) of latent_h x latent_w latents (8x larger in pixels); c1..c3 are the
+# channel widths from the pixel side inward.
+@dataclass(frozen=True)
+class VAEConfig:
+    name: str
+    latent_t: int = 2
+    latent_c: int = 16
+    latent_h: int = 60
+    latent_w: int = 104
+    c1: int = 64
+    c2: int = 128
+    c3: int = 256
+    chunks: int = 3                 # chunks a test or bench streams
+
+    @property
+    def frames(self) -> int:
+        return 2 * self.latent_t
+
+    @property
+    def height(self) -> int:
+        return 8 * self.latent_h
+
+    @property
+    def width(self) -> int:
+        return 8 * self.latent_w
+
+    def replace(self, **kw) -> "VAEConfig":
+        return dataclasses.replace(self, **kw)
+
+
+VAE_CONFIGS = {
+    # the 1.3B-shaped video workload's latent chunk: 4 frames of 480 x 832
+    "video13b": VAEConfig(name="video13b"),
+    # small enough for the oracle in seconds; every layer kind, ragged tiles
+    "small": VAEConfig(name="small", latent_h=3, latent_w=5, c1=16, c2=32, c3=64),
+}
+
+
+def get_vae_config(name: str, **overrides) -> VAEConfig:
+    return VAE_CONFIGS[name].replace(**overrides)

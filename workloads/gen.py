@@ -22,6 +22,8 @@ SEED_UNIFORM = 3
 SEED_CTX_POS = 4
 SEED_CTX_NEG = 5
 SEED_SSF = 6
+SEED_VAE_WEIGHTS = 7
+SEED_VAE_PIXELS = 8
 
 WEIGHT_STD = 0.02
 
@@ -226,3 +228,80 @@ class SSFFrameSource:
     def next(self) -> np.ndarray:
         f = self.base + self.std * self.rng.standard_normal(size=self.base.shape)
         return np.clip(np.rint(f), 0, 255).astype(np.uint8)
+
+
+# --------------------------------------------------------------------------
+# Stream-VAE
+# --------------------------------------------------------------------------
+def vae_param_specs(vcfg):
+    """(name, shape) of every Stream-VAE parameter: conv weights
+    [Cout][3][3][3][Cin], biases [Cout], norm gains [Cout]."""
+    enc = [("e0", 8, vcfg.c1, True), ("e1", vcfg.c1, vcfg.c2, True), ("e2", vcfg.c2, vcfg.c3, True),
+           ("e3", vcfg.c3, vcfg.c3, True), ("e_out", vcfg.c3, vcfg.latent_c, False)]
+    dec = [("d0", vcfg.latent_c, vcfg.c3, True), ("d1", vcfg.c3, vcfg.c3, True), ("d2", vcfg.c3, vcfg.c2, True),
+           ("d3", vcfg.c2, vcfg.c1, True), ("d_out", vcfg.c1, 3, False)]
+    out = []
+    for name, cin, cout, norm in enc + dec:
+        out.append((name + ".w", (cout, 3, 3, 3, cin)))
+        out.append((name + ".b", (cout,)))
+        if norm:
+            out.append((name + ".g", (cout,)))
+    return out
+
+
+def make_vae_weights(vcfg, seed: int = SEED_VAE_WEIGHTS):
+    """bf16-representable float32 weights: conv weights N(0, 1/fan_in) (unit
+    gain through a layer), biases N(0, 0.02^2), norm gains 1 + N(0, 0.1^2).
+    The encoder's first layer sees zeros on input channels 3..7; its weights
+    there are zero too."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = {}
+    for name, shape in vae_param_specs(vcfg):
+        if name.endswith(".w"):
+            fan_in = int(np.prod(shape[1:]))
+            w = rng.standard_normal(size=shape, dtype=np.float32) / np.float32(np.sqrt(fan_in))
+            if name == "e0.w":
+                w[..., 3:] = 0
+        elif name.endswith(".b"):
+            w = rng.standard_normal(size=shape, dtype=np.float32) * np.float32(0.02)
+        else:
+            w = 1.0 + rng.standard_normal(size=shape, dtype=np.float32) * np.float32(0.1)
+        out[name] = round_bf16(w.astype(np.float32))
+    return out
+
+
+class PixelSource:
+    """Pixel chunks [2 latent_t][3][H][W] in [-1, 1]: a smooth moving pattern
+    plus noise (bf16-representable), so consecutive chunks are correlated as
+    video frames are."""
+
+    def __init__(self, vcfg, seed: int = SEED_VAE_PIXELS):
+        self.v = vcfg
+        self.rng = np.random.Generator(np.random.PCG64(seed))
+        self.t = 0
+
+    def next(self):
+        v = self.v
+        T, H, W = v.frames, v.height, v.width
+        yy, xx = np.meshgrid(np.linspace(0, 1, H), np.linspace(0, 1, W), indexing="ij")
+        out = np.empty((T, 3, H, W), np.float32)
+        for f in range(T):
+            ph = 0.15 * (self.t + f)
+            for c in range(3):
+                out[f, c] = 0.6 * np.sin(6.0 * xx + 4.0 * yy + ph + 2.1 * c)
+        self.t += T
+        out += 0.2 * self.rng.standard_normal(size=out.shape, dtype=np.float32)
+        return round_bf16(np.clip(out, -1.0, 1.0))
+
+
+class VAELatentSource:
+    """Latent chunks [latent_t][16][h][w], N(0, 1), bf16-representable."""
+
+    def __init__(self, vcfg, seed: int = SEED_LATENT):
+        self.v = vcfg
+        self.rng = np.random.Generator(np.random.PCG64(seed))
+
+    def next(self):
+        v = self.v
+        return round_bf16(self.rng.standard_normal(size=(v.latent_t, v.latent_c, v.latent_h, v.latent_w),
+                                                   dtype=np.float32))
