@@ -30,6 +30,17 @@ sd_status sd_k_gemm(int32_t dtype, const void* A, const void* W, const void* bia
 sd_status sd_k_gemm_resid(int32_t dtype, const void* A, const void* W, const void* bias, float* C, int32_t M,
                           int32_t N, int32_t K, void* stream);
 
+/* One causal 3x3x3 convolution of the Stream-VAE (StreamDiffusionV2 summary,
+ * Stream-VAE: features cached inside every 3D convolution), bf16 channels-last:
+ * x [T][H][W][Cin], cache [2][H][W][Cin] (the two input frames before the
+ * chunk; NULL = zeros), w [Cout][3][3][3][Cin], bias [Cout] (NULL = 0);
+ * y[t][i][j][o] = bias[o] + sum w[o][dt][dy][dx][c] x'[t+dt-2][i+dy-1][j+dx-1][c]
+ * with x' = [cache | x] in time and zero outside the frame.  Cin a multiple of
+ * 8, Cout a multiple of 4 (y bf16 [T][H][W][Cout]) or, with y_f32_cf != NULL
+ * and Cout <= 16, fp32 channels-first [T][Cout][H][W] to y_f32_cf instead. */
+sd_status sd_k_conv3d(const void* x, const void* cache, const void* w, const void* bias, void* y, float* y_f32_cf,
+                      int32_t T, int32_t H, int32_t W, int32_t Cin, int32_t Cout, void* stream);
+
 /* One key segment of an attention call.  K is [cap][hd] per (row, head), V is
  * stored transposed [hd][cap]; a head starts head_stride elements after the
  * previous one and a query row row_stride elements after the previous one

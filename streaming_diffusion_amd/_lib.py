@@ -87,6 +87,22 @@ class sd_kv_segment(C.Structure):
                 ("count", C.c_int32), ("wrap", C.c_int32)]
 
 
+SD_VAE_ABI_VERSION = 1
+SD_VAE_LAYERS = 10
+VAE_LAYER_NAMES = ["e0", "e1", "e2", "e3", "e_out", "d0", "d1", "d2", "d3", "d_out"]
+
+
+class sd_vae_config(C.Structure):
+    _fields_ = [("abi_version", C.c_uint32), ("latent_t", C.c_int32), ("latent_c", C.c_int32),
+                ("latent_h", C.c_int32), ("latent_w", C.c_int32), ("c1", C.c_int32), ("c2", C.c_int32),
+                ("c3", C.c_int32)]
+
+
+class sd_vae_weights(C.Structure):
+    _fields_ = [("w", C.c_void_p * SD_VAE_LAYERS), ("b", C.c_void_p * SD_VAE_LAYERS),
+                ("g", C.c_void_p * SD_VAE_LAYERS)]
+
+
 # name -> (restype, argtypes)
 SIGNATURES = {
     "sd_stream_workspace_bytes": (C.c_size_t, [C.POINTER(sd_stream_config)]),
@@ -114,6 +130,16 @@ SIGNATURES = {
     "sd_k_attention_workspace_bytes": (C.c_size_t, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32]),
     "sd_k_ssf_sums": (C.c_int, [C.c_int32, C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]),
     "sd_k_motion_sums": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_int64, C.c_void_p, C.c_void_p]),
+    "sd_k_conv3d": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
+                              C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p]),
+    "sd_vae_workspace_bytes": (C.c_size_t, [C.POINTER(sd_vae_config)]),
+    "sd_vae_create": (C.c_int, [C.POINTER(sd_vae_config), C.POINTER(sd_vae_weights), C.c_void_p, C.c_size_t,
+                                C.c_void_p, C.POINTER(C.c_void_p)]),
+    "sd_vae_encode": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p]),
+    "sd_vae_decode": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p]),
+    "sd_vae_reset": (C.c_int, [C.c_void_p]),
+    "sd_vae_destroy": (None, [C.c_void_p]),
+    "sd_vae_last_error": (C.c_char_p, [C.c_void_p]),
 }
 
 STATE_SIGNATURES = {

@@ -19,7 +19,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsdstream.so")
 STATE_LIB = os.path.join(PKG, "libsdstate.so")
 
-HIP_SOURCES = ["k_misc.hip", "k_gemm.hip", "k_gemm_mfma.hip", "k_attn.hip", "runtime.hip", "kernels_abi.hip"]
+HIP_SOURCES = ["k_misc.hip", "k_gemm.hip", "k_gemm_mfma.hip", "k_attn.hip", "k_vae.hip", "runtime.hip", "vae.hip",
+               "kernels_abi.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 HIP_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

@@ -182,3 +182,76 @@ def _wrap_device(addr, dtype, shape, device, owner):
     if off < 0 or off + count * esz > owner.numel() * owner.element_size():
         raise ValueError("address outside the workspace")
     return owner[off:off + count * esz].view(dtype).view(*shape)
+
+
+# --------------------------------------------------------------------------
+# Stream-VAE
+# --------------------------------------------------------------------------
+def make_vae_config(vcfg) -> "L.sd_vae_config":
+    c = L.sd_vae_config()
+    c.abi_version = L.SD_VAE_ABI_VERSION
+    c.latent_t, c.latent_c, c.latent_h, c.latent_w = vcfg.latent_t, vcfg.latent_c, vcfg.latent_h, vcfg.latent_w
+    c.c1, c.c2, c.c3 = vcfg.c1, vcfg.c2, vcfg.c3
+    return c
+
+
+def upload_vae_weights(vcfg, weights: dict, device="cuda") -> dict:
+    """Host float32 arrays (bf16-representable) -> contiguous bf16 device tensors."""
+    return {k: torch.from_numpy(np.ascontiguousarray(v)).to(device=device).to(torch.bfloat16).contiguous()
+            for k, v in weights.items()}
+
+
+class VAERunner:
+    """Owns the workspace and weight table of one sd_vae; encode / decode take
+    and return fp32 device tensors in the channels-first layouts."""
+
+    def __init__(self, vcfg, dev_weights: dict, device="cuda", stream=None):
+        self.lib = L.load()
+        self.v = vcfg
+        self.cfg = make_vae_config(vcfg)
+        self.weights = dev_weights
+        self.wt = L.sd_vae_weights()
+        for i, name in enumerate(L.VAE_LAYER_NAMES):
+            self.wt.w[i] = dev_weights[name + ".w"].data_ptr()
+            self.wt.b[i] = dev_weights[name + ".b"].data_ptr()
+            g = dev_weights.get(name + ".g")
+            self.wt.g[i] = g.data_ptr() if g is not None else None
+        nbytes = self.lib.sd_vae_workspace_bytes(C.byref(self.cfg))
+        if nbytes == 0:
+            raise ValueError("invalid Stream-VAE configuration")
+        self.ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        base = self.ws.data_ptr()
+        off = (-base) % 256
+        self.h = C.c_void_p()
+        s = stream.cuda_stream if stream is not None else torch.cuda.current_stream().cuda_stream
+        L.check(self.lib.sd_vae_create(C.byref(self.cfg), C.byref(self.wt), C.c_void_p(base + off),
+                                       C.c_size_t(nbytes), C.c_void_p(s), C.byref(self.h)))
+        self.lat_shape = (vcfg.latent_t, vcfg.latent_c, vcfg.latent_h, vcfg.latent_w)
+        self.pix_shape = (vcfg.frames, 3, vcfg.height, vcfg.width)
+
+    def _check(self, code):
+        if code != L.SD_OK:
+            m = self.lib.sd_vae_last_error(self.h)
+            raise L.SDError(code, m.decode() if m else "")
+
+    def encode(self, pixels, out=None):
+        if tuple(pixels.shape) != self.pix_shape or pixels.dtype != torch.float32 or not pixels.is_contiguous():
+            raise ValueError(f"pixels must be contiguous fp32 {self.pix_shape}")
+        out = torch.empty(self.lat_shape, dtype=torch.float32, device=pixels.device) if out is None else out
+        self._check(self.lib.sd_vae_encode(self.h, C.c_void_p(pixels.data_ptr()), C.c_void_p(out.data_ptr())))
+        return out
+
+    def decode(self, latent, out=None):
+        if tuple(latent.shape) != self.lat_shape or latent.dtype != torch.float32 or not latent.is_contiguous():
+            raise ValueError(f"latent must be contiguous fp32 {self.lat_shape}")
+        out = torch.empty(self.pix_shape, dtype=torch.float32, device=latent.device) if out is None else out
+        self._check(self.lib.sd_vae_decode(self.h, C.c_void_p(latent.data_ptr()), C.c_void_p(out.data_ptr())))
+        return out
+
+    def reset(self):
+        self._check(self.lib.sd_vae_reset(self.h))
+
+    def close(self):
+        if self.h:
+            self.lib.sd_vae_destroy(self.h)
+            self.h = C.c_void_p()

@@ -17,10 +17,10 @@ L = pytest.importorskip("streaming_diffusion_amd._lib")
 
 def header_symbols():
     syms = set()
-    for h in ("sd_stream.h", "sd_kernels.h"):
+    for h in ("sd_stream.h", "sd_kernels.h", "sd_vae.h"):
         src = open(os.path.join(ROOT, "include", h)).read()
         src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-        syms |= set(re.findall(r"\b(sd_(?:stream|k)_\w+)\s*\(", src))
+        syms |= set(re.findall(r"\b(sd_(?:stream|k|vae)_\w+)\s*\(", src))
     return sorted(syms)
 
 
@@ -189,3 +189,44 @@ def test_unknown_sampler_and_batch_flag_are_rejected(lib, state):
         assert lib.sd_stream_workspace_bytes(C.byref(c)) == 0
     c = cfg_struct("tiny", sampler="lcm")
     assert state.sdstate_validate(C.byref(c), None, 0) == L.SD_OK
+
+
+def test_vae_struct_sizes_match_a_c_compiler(tmp_path):
+    probe = tmp_path / "probe.c"
+    fields = [f for f, _ in L.sd_vae_config._fields_]
+    lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{ROOT}/include/sd_vae.h"', "int main(void){",
+             'printf("%zu %zu\\n", sizeof(sd_vae_config), sizeof(sd_vae_weights));']
+    lines += [f'printf("%zu\\n", offsetof(sd_vae_config, {f}));' for f in fields]
+    lines.append('printf("%d\\n", (int)SD_VAE_LAYERS); return 0;}')
+    probe.write_text("\n".join(lines))
+    exe = tmp_path / "probe"
+    assert os.system(f"gcc -o {exe} {probe}") == 0
+    out = [int(v) for v in os.popen(str(exe)).read().split()]
+    assert out[:2] == [C.sizeof(L.sd_vae_config), C.sizeof(L.sd_vae_weights)]
+    assert out[2:-1] == [getattr(L.sd_vae_config, f).offset for f in fields]
+    assert out[-1] == L.SD_VAE_LAYERS
+
+
+def vae_cfg(**kw):
+    from streaming_diffusion_amd.runner import make_vae_config
+    from workloads import get_vae_config
+    return make_vae_config(get_vae_config("small", **kw))
+
+
+@pytest.mark.parametrize("kw,ok", [({}, True), (dict(latent_t=1), False), (dict(latent_c=12), False),
+                                   (dict(c2=48), False), (dict(latent_h=0), False)])
+def test_vae_config_validation(lib, kw, ok):
+    c = vae_cfg(**kw)
+    assert (lib.sd_vae_workspace_bytes(C.byref(c)) > 0) == ok
+
+
+def test_vae_and_conv_argument_errors(lib):
+    c = vae_cfg()
+    w = L.sd_vae_weights()
+    h = C.c_void_p()
+    assert lib.sd_vae_create(C.byref(c), C.byref(w), 256, 1 << 30, None, C.byref(h)) == L.SD_ERR_ARG   # null weights
+    assert lib.sd_vae_encode(None, 8, 8) == L.SD_ERR_ARG
+    assert lib.sd_k_conv3d(8, None, 8, None, 8, None, 1, 4, 4, 12, 8, None) == L.SD_ERR_SHAPE       # Cin % 8
+    assert lib.sd_k_conv3d(8, None, 8, None, 8, None, 1, 4, 4, 8, 6, None) == L.SD_ERR_SHAPE        # Cout % 4
+    assert lib.sd_k_conv3d(8, None, 8, None, None, 8, 1, 4, 4, 8, 17, None) == L.SD_ERR_SHAPE       # narrow > 16
+    assert lib.sd_k_conv3d(None, None, 8, None, 8, None, 1, 4, 4, 8, 8, None) == L.SD_ERR_ARG
