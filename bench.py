@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--slo-fps", type=float, default=0.0,
                     help="run the SLO-aware batching loop for --steps steps with up to --chunks chunks per step "
                          "and report the batch sizes it chose (one JSON line)")
+    ap.add_argument("--vae", action="store_true",
+                    help="measure the Stream-VAE instead: encode + decode of 4-frame chunks at the video shape")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-blocks", type=int, default=2, help="DiT blocks in the oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -255,6 +257,127 @@ def measure(cfg, weights, steps: int, warmup: int, dev):
     }
 
 
+def vae_conv_flops(L):
+    """Algorithmic FLOP of one convolution layer: 2 x 27 Cin x Cout per output position."""
+    return 2.0 * 27 * L["cin"] * L["cout"] * L["T"] * L["H"] * L["W"]
+
+
+def vae_layers(v):
+    T, h, w = v.latent_t, v.latent_h, v.latent_w
+    Tp, H, W = 2 * T, 8 * h, 8 * w
+    rows = [("e0", 8, v.c1, Tp, H, W), ("e1", v.c1, v.c2, Tp, H // 2, W // 2), ("e2", v.c2, v.c3, Tp, H // 4, W // 4),
+            ("e3", v.c3, v.c3, T, h, w), ("e_out", v.c3, v.latent_c, T, h, w), ("d0", v.latent_c, v.c3, T, h, w),
+            ("d1", v.c3, v.c3, Tp, H // 4, W // 4), ("d2", v.c3, v.c2, Tp, H // 2, W // 2),
+            ("d3", v.c2, v.c1, Tp, H, W), ("d_out", v.c1, 3, Tp, H, W)]
+    return [dict(name=n, cin=ci, cout=co, T=t, H=hh, W=ww) for n, ci, co, t, hh, ww in rows]
+
+
+def vae_run(steps: int, warmup: int, dev, cpu: bool):
+    """Stream-VAE at the video shape: `steps` chunks encoded and decoded back
+    to back (pixels and latents resident), then every matrix-core layer timed
+    alone at its real shape with HIP events on the library's stream."""
+    import ctypes as C
+
+    import numpy as np
+    import torch
+
+    import streaming_diffusion_amd._lib as L
+    from streaming_diffusion_amd.runner import VAERunner, upload_vae_weights
+    from workloads import gen, get_vae_config
+
+    v = get_vae_config("video13b")
+    w = gen.make_vae_weights(v)
+    run = VAERunner(v, upload_vae_weights(v, w))
+    src = gen.PixelSource(v)
+    pix = [torch.from_numpy(np.ascontiguousarray(src.next())).to(dev) for _ in range(4)]
+    lat = torch.empty(run.lat_shape, dtype=torch.float32, device=dev)
+    out = torch.empty(run.pix_shape, dtype=torch.float32, device=dev)
+    for k in range(warmup):
+        run.encode(pix[k % 4], lat)
+        run.decode(lat, out)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    enc_ms = dec_ms = 0.0
+    t0 = time.perf_counter()
+    for k in range(steps):
+        ev[0].record()
+        run.encode(pix[k % 4], lat)
+        ev[1].record()
+        run.decode(lat, out)
+        ev[2].record()
+        torch.cuda.synchronize()
+        enc_ms += ev[0].elapsed_time(ev[1])
+        dec_ms += ev[1].elapsed_time(ev[2])
+    elapsed = time.perf_counter() - t0
+    run.close()
+    # each matrix-core convolution alone, random operands of its shape
+    lib = L.load()
+    stream = torch.cuda.current_stream()
+    layers = []
+    for Ly in vae_layers(v):
+        if Ly["cout"] < 32:
+            continue
+        T, H, W, ci, co = Ly["T"], Ly["H"], Ly["W"], Ly["cin"], Ly["cout"]
+        x = torch.randn((T, H, W, ci), device=dev).to(torch.bfloat16)
+        cache = torch.randn((2, H, W, ci), device=dev).to(torch.bfloat16)
+        wt = (torch.randn((co, 27 * ci), device=dev) / np.sqrt(27 * ci)).to(torch.bfloat16)
+        y = torch.empty((T, H, W, co), dtype=torch.bfloat16, device=dev)
+        call = lambda: lib.sd_k_conv3d(x.data_ptr(), cache.data_ptr(), wt.data_ptr(), None, y.data_ptr(), None,
+                                       T, H, W, ci, co, C.c_void_p(stream.cuda_stream))
+        for _ in range(2):
+            call()
+        ev[0].record(stream)
+        reps = 10
+        for _ in range(reps):
+            call()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / reps
+        fl = vae_conv_flops(Ly)
+        layers.append({"layer": Ly["name"], "cin": ci, "cout": co, "positions": T * H * W, "ms": round(ms, 4),
+                       "tflops": round(fl / (ms * 1e-3) / 1e12, 1)})
+        del x, cache, wt, y
+    dom = max(layers, key=lambda r: r["ms"])
+    Ldom = next(r for r in vae_layers(v) if r["name"] == dom["layer"])
+    per_chunk_ms = (enc_ms + dec_ms) / steps
+    res = {
+        "metric": "Stream-VAE frames/s, encode + decode of one chunk per call (4 frames 480x832 <-> 2 x 16 x 60 x 104)",
+        "value": round(steps * v.frames / ((enc_ms + dec_ms) * 1e-3), 2),
+        "unit": "frames/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(per_chunk_ms, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"Stream-VAE video13b: chunk {v.frames} x 3 x {v.height} x {v.width} pixels, "
+                               f"latent {v.latent_t} x {v.latent_c} x {v.latent_h} x {v.latent_w}, widths "
+                               f"{v.c1}/{v.c2}/{v.c3}, causal 3x3x3 convolutions with 2-frame caches",
+                   "parallelism": "single GPU"},
+        "encode_ms_per_chunk": round(enc_ms / steps, 3), "decode_ms_per_chunk": round(dec_ms / steps, 3),
+        "wall_ms_per_chunk": round(elapsed / steps * 1e3, 3),
+        "roofline": {"kernel": f"conv3d_mfma_kernel (layer {dom['layer']}, timed alone at its shape)",
+                     "bound": "mfma", "achieved": dom["tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(dom["tflops"] / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "avg_launch_ms": dom["ms"], "flop_per_launch": vae_conv_flops(Ldom)},
+        "layers": layers,
+    }
+    if cpu:
+        from threadpoolctl import threadpool_info
+
+        from oracle import vae as ovae
+        sv = ovae.StreamVAE(v, w)
+        pix0 = src.next()
+        t1 = time.perf_counter()
+        sv.encode_chunk(pix0)
+        dt = time.perf_counter() - t1
+        fl_enc = sum(vae_conv_flops(r) for r in vae_layers(v) if r["name"].startswith("e"))
+        fl_all = sum(vae_conv_flops(r) for r in vae_layers(v))
+        chunk_s = dt * fl_all / fl_enc
+        threads = max([int(p.get("num_threads", 0)) for p in threadpool_info() if p.get("user_api") == "blas"] or [0])
+        res["cpu_baseline"] = {"value": round(v.frames / chunk_s, 4), "unit": "frames/s",
+                               "cores": threads or len(os.sched_getaffinity(0)), "kind": "oracle",
+                               "sample": f"one chunk through the encoder (fp64 NumPy, {dt:.1f} s), scaled by the "
+                                         f"encode + decode / encode FLOP ratio {fl_all / fl_enc:.2f}"}
+    return res
+
+
 def slo_run(cfg, weights, target_fps: float, steps: int, dev):
     """The SLO-aware batching loop on the real pipeline with a backlog of
     input chunks: each step the scheduler picks how many enter; a step's
@@ -322,6 +445,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.vae:
+        print(json.dumps(vae_run(args.steps, args.warmup, dev, not args.no_cpu_baseline)))
+        return
     kw = {} if args.cfg is None else {"cfg_type": args.cfg}
     if args.batch_attn:
         kw["batch_attn"] = True

@@ -24,40 +24,55 @@ SD_DEV const bf16* conv_src(const ConvArgs& a, int t, int y, int x, int k, int H
 // Implicit-GEMM convolution on the matrix cores: C^T[n][m] = sum_k W[n][k]
 // A[m][k], m an output position, n an output channel, A the gathered input
 // (im2col on the fly).  Workgroup tile 128 positions x BN channels, k-tiles
-// of 32, 4 waves in 2 x 2 (each 64 positions x BN/2 channels), operands
+// of 32, 4 waves: 2 x 2 (each 64 positions x BN/2 channels) for BN >= 64,
+// 4 x 1 (each 32 positions x 32 channels) for the narrow BN = 32, operands
 // staged global -> registers -> LDS (double buffered, one barrier per
 // k-tile); LDS rows are 64 bytes with their four 16-byte chunks XOR-swizzled
 // by row.  The weights are the A operand, so a lane holds one position and
-// four runs of 4 consecutive channels: 8-byte bf16 stores.
-constexpr int CV_BM = 128, CV_BK = 32;
+// four runs of 4 consecutive channels: 8-byte bf16 stores channels-last, or
+// fp32 stores channels-first (the pixel / latent outputs, where consecutive
+// lanes write consecutive positions of one channel).
+constexpr int CV_BM = 128;
+constexpr int CV_BK = 32;     // k-tile width used by the dispatch
 
-SD_DEV int cv_swz(int row) { return (row >> 2) & 3; }
+// 16-byte chunk swizzle of a row of BK elements: the 16 lanes of one
+// ds_read_b128 pass (16 consecutive rows, one logical chunk) land on 16
+// distinct 16-byte bank groups
+template <int BK>
+SD_DEV int cv_swz(int row) {
+  return (row / (128 / BK)) & (BK / 8 - 1);
+}
 
-template <int BN>
+template <int BN, int BK>
 __global__ __launch_bounds__(256) void conv3d_mfma_kernel(ConvArgs a) {
-  constexpr int NB = BN / 64;                  // 32-channel blocks per wave
-  constexpr int RB = BN / 64;                  // weight chunks per thread per k-tile
-  __shared__ __attribute__((aligned(16))) bf16 As[2][CV_BM * CV_BK];
-  __shared__ __attribute__((aligned(16))) bf16 Bs[2][BN * CV_BK];
+  constexpr int WMW = BN >= 64 ? 2 : 4, WNW = 4 / WMW;   // waves along positions / channels
+  constexpr int TMP = CV_BM / WMW, TNC = BN / WNW;      // wave tile: positions x channels
+  constexpr int MB = TMP / 32, NB = TNC / 32;           // 32 x 32 blocks per wave
+  constexpr int CPR = BK / 8, RPP = 256 / CPR;          // chunks per row, rows per pass of 256 threads
+  constexpr int RA = CV_BM / RPP;                       // input chunks per thread per k-tile
+  constexpr int RB = (BN + RPP - 1) / RPP;              // weight chunks per thread per k-tile
+  static_assert(MB >= 1 && NB >= 1 && RA >= 1, "wave tile");
+  __shared__ __attribute__((aligned(16))) bf16 As[2][CV_BM * BK];
+  __shared__ __attribute__((aligned(16))) bf16 Bs[2][BN * BK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wn = wave >> 1, wm = wave & 1;
+  const int wn = wave / WMW, wm = wave % WMW;
   const int HW = a.H * a.W;
   const int M = a.T * HW;
   const int K = 27 * a.Cin;
-  const int KT = (K + CV_BK - 1) / CV_BK;
+  const int KT = (K + BK - 1) / BK;
   const int tiles_m = (M + CV_BM - 1) / CV_BM;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
   const int tm = lid % tiles_m, tn = lid / tiles_m;
   const int m0 = tm * CV_BM, n0 = tn * BN;
 
-  // staged chunks of this thread: A rows tid/4 and tid/4 + 64, weight rows
-  // tid/4 (+64), all at chunk tid%4 of the k-tile
-  const int ck = tid & 3, r0 = tid >> 2;
-  int pt[2], py[2], px[2];
-  bool pv[2];
+  // staged chunks of this thread: input rows r0 + RPP i, weight rows
+  // r0 + RPP i, all at chunk ck of the k-tile
+  const int ck = tid % CPR, r0 = tid / CPR;
+  int pt[RA], py[RA], px[RA];
+  bool pv[RA];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int p = m0 + r0 + 64 * i;
+  for (int i = 0; i < RA; ++i) {
+    const int p = m0 + r0 + RPP * i;
     pv[i] = p < M;
     const int pp = pv[i] ? p : 0;
     pt[i] = pp / HW;
@@ -66,39 +81,39 @@ __global__ __launch_bounds__(256) void conv3d_mfma_kernel(ConvArgs a) {
     px[i] = rem - py[i] * a.W;
   }
   const bf16x8 zero8 = {};
-  bf16x8 ra[2], rb[RB];
+  bf16x8 ra[RA], rb[RB];
   auto load = [&](int kt) {
-    const int k = kt * CV_BK + ck * 8;
+    const int k = kt * BK + ck * 8;
     const bool kv = k < K;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < RA; ++i) {
       const bf16* src = (kv && pv[i]) ? conv_src(a, pt[i], py[i], px[i], k, HW) : nullptr;
       ra[i] = src ? *(const bf16x8*)src : zero8;
     }
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
-      const int n = n0 + r0 + 64 * i;
-      rb[i] = (kv && n < a.Cout) ? *(const bf16x8*)(a.w + (int64_t)n * K + k) : zero8;
+      const int n = n0 + r0 + RPP * i;
+      rb[i] = (kv && r0 + RPP * i < BN && n < a.Cout) ? *(const bf16x8*)(a.w + (int64_t)n * K + k) : zero8;
     }
   };
   auto store = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = r0 + 64 * i;
-      *(bf16x8*)&As[buf][r * CV_BK + ((ck ^ cv_swz(r)) * 8)] = ra[i];
+    for (int i = 0; i < RA; ++i) {
+      const int r = r0 + RPP * i;
+      *(bf16x8*)&As[buf][r * BK + ((ck ^ cv_swz<BK>(r)) * 8)] = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
-      const int r = r0 + 64 * i;
-      *(bf16x8*)&Bs[buf][r * CV_BK + ((ck ^ cv_swz(r)) * 8)] = rb[i];
+      const int r = r0 + RPP * i;
+      if (r < BN) *(bf16x8*)&Bs[buf][r * BK + ((ck ^ cv_swz<BK>(r)) * 8)] = rb[i];
     }
   };
 
-  f32x16 acc[NB][2];
+  f32x16 acc[NB][MB];
 #pragma unroll
   for (int i = 0; i < NB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < MB; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
@@ -110,23 +125,23 @@ __global__ __launch_bounds__(256) void conv3d_mfma_kernel(ConvArgs a) {
     const int buf = kt & 1;
     if (kt + 1 < KT) load(kt + 1);            // in flight during this k-tile's MFMAs
 #pragma unroll
-    for (int s = 0; s < CV_BK / 16; ++s) {
+    for (int s = 0; s < BK / 16; ++s) {
       const int c = s * 2 + lh;
-      bf16x8 fw[NB], fp[2];
+      bf16x8 fw[NB], fp[MB];
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
-        const int row = wn * (BN / 2) + i * 32 + lr;
-        fw[i] = *(const bf16x8*)&Bs[buf][row * CV_BK + ((c ^ cv_swz(row)) * 8)];
+        const int row = wn * TNC + i * 32 + lr;
+        fw[i] = *(const bf16x8*)&Bs[buf][row * BK + ((c ^ cv_swz<BK>(row)) * 8)];
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int row = wm * 64 + j * 32 + lr;
-        fp[j] = *(const bf16x8*)&As[buf][row * CV_BK + ((c ^ cv_swz(row)) * 8)];
+      for (int j = 0; j < MB; ++j) {
+        const int row = wm * TMP + j * 32 + lr;
+        fp[j] = *(const bf16x8*)&As[buf][row * BK + ((c ^ cv_swz<BK>(row)) * 8)];
       }
 #pragma unroll
       for (int i = 0; i < NB; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i], fp[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < MB; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i], fp[j], acc[i][j], 0, 0, 0);
     }
     if (kt + 1 < KT) store(buf ^ 1);
     __syncthreads();
@@ -135,87 +150,45 @@ __global__ __launch_bounds__(256) void conv3d_mfma_kernel(ConvArgs a) {
   // lane: position column lr of each 32-position block; channel rows
   // 8 (q / 4) + 4 lh + (q % 4) of each 32-channel block
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int p = m0 + wm * 64 + j * 32 + lr;
+  for (int j = 0; j < MB; ++j) {
+    const int p = m0 + wm * TMP + j * 32 + lr;
     if (p >= M) continue;
 #pragma unroll
     for (int i = 0; i < NB; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * (BN / 2) + i * 32 + 8 * g + 4 * lh;
+        const int n = n0 + wn * TNC + i * 32 + 8 * g + 4 * lh;
         if (n >= a.Cout) continue;
-        bf16x4 o;
+        if (a.ycf) {
+          const int t = p / HW, hw = p - t * HW;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = (bf16)(acc[i][j][4 * g + e] + (a.b ? (float)a.b[n + e] : 0.f));
-        *(bf16x4*)(a.y + (int64_t)p * a.Cout + n) = o;
+          for (int e = 0; e < 4; ++e)
+            if (n + e < a.Cout)
+              a.ycf[((int64_t)t * a.Cout + n + e) * HW + hw] = acc[i][j][4 * g + e] + (a.b ? (float)a.b[n + e] : 0.f);
+        } else {
+          bf16x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = (bf16)(acc[i][j][4 * g + e] + (a.b ? (float)a.b[n + e] : 0.f));
+          *(bf16x4*)(a.y + (int64_t)p * a.Cout + n) = o;
+        }
       }
   }
 }
 
 hipError_t conv3d(hipStream_t s, const ConvArgs& a) {
-  if (a.Cin < 8 || (a.Cin & 7) || a.Cout < 4 || (a.Cout & 3) || a.T < 1 || a.H < 1 || a.W < 1)
-    return hipErrorInvalidValue;
+  if (a.Cin < 8 || (a.Cin & 7) || a.Cout < 1 || a.T < 1 || a.H < 1 || a.W < 1) return hipErrorInvalidValue;
+  if (a.ycf ? false : (!a.y || (a.Cout & 3))) return hipErrorInvalidValue;
   const int64_t M = (int64_t)a.T * a.H * a.W;
   if (M * a.Cout >= (1ll << 31) || M * a.Cin >= (1ll << 31) || 27ll * a.Cin * a.Cout >= (1ll << 31))
     return hipErrorInvalidValue;
   const int tiles_m = (int)((M + CV_BM - 1) / CV_BM);
-  if (a.Cout <= 64) {
-    conv3d_mfma_kernel<64><<<tiles_m * ((a.Cout + 63) / 64), 256, 0, s>>>(a);
+  if (a.Cout <= 32) {
+    conv3d_mfma_kernel<32, CV_BK><<<tiles_m * ((a.Cout + 31) / 32), 256, 0, s>>>(a);
+  } else if (a.Cout <= 64) {
+    conv3d_mfma_kernel<64, CV_BK><<<tiles_m * ((a.Cout + 63) / 64), 256, 0, s>>>(a);
   } else {
-    conv3d_mfma_kernel<128><<<tiles_m * ((a.Cout + 127) / 128), 256, 0, s>>>(a);
+    conv3d_mfma_kernel<128, CV_BK><<<tiles_m * ((a.Cout + 127) / 128), 256, 0, s>>>(a);
   }
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// Narrow convolution (Cout <= CO, the 3 pixel or 16 latent channels): one
-// thread per output position on the vector ALUs; weight reads are uniform
-// over the workgroup.  Writes fp32 channels-first [T][Cout][H][W], the
-// external layout of pixels and latents.
-template <int CO>
-__global__ __launch_bounds__(256) void conv3d_narrow_kernel(ConvArgs a, float* __restrict__ out) {
-  const int HW = a.H * a.W;
-  const int M = a.T * HW;
-  const int p = blockIdx.x * 256 + threadIdx.x;
-  if (p >= M) return;
-  const int K = 27 * a.Cin;
-  const int t = p / HW, rem = p - t * HW, y = rem / a.W, x = rem - (rem / a.W) * a.W;
-  float acc[CO];
-#pragma unroll
-  for (int o = 0; o < CO; ++o) acc[o] = (o < a.Cout && a.b) ? (float)a.b[o] : 0.f;
-  for (int tap = 0; tap < 27; ++tap) {
-    const bf16* src = conv_src(a, t, y, x, tap * a.Cin, HW);
-    if (!src) continue;
-    for (int c = 0; c < a.Cin; c += 8) {
-      const bf16x8 v = *(const bf16x8*)(src + c);
-      float vf[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vf[e] = (float)v[e];
-#pragma unroll
-      for (int o = 0; o < CO; ++o) {
-        if (o < a.Cout) {
-          const bf16x8 wv = *(const bf16x8*)(a.w + (int64_t)o * K + tap * a.Cin + c);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[o] = fmaf(vf[e], (float)wv[e], acc[o]);
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int o = 0; o < CO; ++o)
-    if (o < a.Cout) out[((int64_t)t * a.Cout + o) * HW + rem] = acc[o];
-}
-
-hipError_t conv3d_narrow(hipStream_t s, const ConvArgs& a, float* out) {
-  if (a.Cin < 8 || (a.Cin & 7) || a.Cout < 1 || a.Cout > 16 || a.T < 1 || a.H < 1 || a.W < 1)
-    return hipErrorInvalidValue;
-  const int64_t M = (int64_t)a.T * a.H * a.W;
-  if (M * a.Cin >= (1ll << 31)) return hipErrorInvalidValue;
-  const unsigned g = (unsigned)((M + 255) / 256);
-  if (a.Cout <= 4)
-    conv3d_narrow_kernel<4><<<g, 256, 0, s>>>(a, out);
-  else
-    conv3d_narrow_kernel<16><<<g, 256, 0, s>>>(a, out);
   return hipGetLastError();
 }
 

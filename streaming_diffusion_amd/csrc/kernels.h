@@ -99,19 +99,19 @@ int attention_pick_split(int units, int tiles, int max_split, int concurrent);
 // ---------------------------------------------------------------- Stream-VAE
 // Causal 3x3x3 convolution: x bf16 [T][H][W][Cin], cache bf16 [2][H][W][Cin]
 // (input frames -2, -1; null = zeros), w bf16 [Cout][27 Cin], b bf16 [Cout]
-// (null = 0), y bf16 [T][H][W][Cout].  Cin a multiple of 8, Cout of 4.
+// (null = 0); output bf16 channels-last y [T][H][W][Cout] (Cout a multiple of
+// 4) or, when ycf is set, fp32 channels-first ycf [T][Cout][H][W] (any Cout).
+// Cin a multiple of 8.
 struct ConvArgs {
   const bf16* x;
   const bf16* cache;
   const bf16* w;
   const bf16* b;
   bf16* y;
+  float* ycf;
   int T, H, W, Cin, Cout;
 };
 hipError_t conv3d(hipStream_t s, const ConvArgs& a);
-// The same for Cout <= 16 on the vector ALUs, fp32 channels-first output
-// [T][Cout][H][W] (a.y unused).
-hipError_t conv3d_narrow(hipStream_t s, const ConvArgs& a, float* out);
 // In place on bf16 [P][C]: RMS norm over C (gain g bf16 [C]) then SiLU.
 hipError_t norm_silu(hipStream_t s, void* x, const void* g, int64_t P, int C, float eps);
 // bf16 channels-last resampling: mode 0 pool 2x2, 1 pool 2x2x2, 2 nearest

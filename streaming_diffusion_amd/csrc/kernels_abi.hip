@@ -112,6 +112,7 @@ sd_status sd_k_conv3d(const void* x, const void* cache, const void* w, const voi
   a.w = (const bf16*)w;
   a.b = (const bf16*)bias;
   a.y = (bf16*)y;
+  a.ycf = y_f32_cf;
   a.T = T;
   a.H = H;
   a.W = W;
@@ -119,7 +120,8 @@ sd_status sd_k_conv3d(const void* x, const void* cache, const void* w, const voi
   a.Cout = Cout;
   if (y_f32_cf) {
     if (Cout > 16) return SD_ERR_SHAPE;
-    return sdk::conv3d_narrow((hipStream_t)stream, a, y_f32_cf) == hipSuccess ? SD_OK : SD_ERR_HIP;
+    a.y = nullptr;
+    return sdk::conv3d((hipStream_t)stream, a) == hipSuccess ? SD_OK : SD_ERR_HIP;
   }
   if (!y) return SD_ERR_ARG;
   if (Cout % 4) return SD_ERR_SHAPE;

@@ -104,16 +104,14 @@ sd_status run_layers(sd_vae* v, int first, int last, int cur, int T, int H, int 
     a.cache = (const bf16*)l.cache;
     a.w = (const bf16*)v->w.w[li];
     a.b = (const bf16*)v->w.b[li];
-    a.y = (bf16*)v->act[in ^ 1];
+    a.y = li == last ? nullptr : (bf16*)v->act[in ^ 1];
+    a.ycf = li == last ? out : nullptr;
     a.T = l.T;
     a.H = l.H;
     a.W = l.W;
     a.Cin = l.cin;
     a.Cout = l.cout;
-    if (li == last)
-      VHIP(sdk::conv3d_narrow(v->st, a, out));
-    else
-      VHIP(sdk::conv3d(v->st, a));
+    VHIP(sdk::conv3d(v->st, a));
     // this chunk's last two input frames become the layer's cache
     const size_t frame = (size_t)l.H * l.W * l.cin;
     VHIP(hipMemcpyAsync(l.cache, (const char*)v->act[in] + (size_t)(l.T - 2) * frame * 2, 2 * frame * 2,

@@ -40,7 +40,8 @@ def bf16_of(a):
 
 
 @pytest.mark.parametrize("T,H,W,Ci,Co", [(4, 5, 7, 8, 16), (4, 9, 13, 24, 64), (2, 6, 10, 64, 132),
-                                         (3, 16, 17, 128, 256), (4, 1, 1, 8, 4)])
+                                         (3, 16, 17, 128, 256), (4, 1, 1, 8, 4), (3, 7, 11, 16, 32),
+                                         (2, 5, 6, 8, 20), (2, 8, 9, 40, 96)])
 def test_conv3d_bit_exact_on_integers(lib, T, H, W, Ci, Co):
     print(f"conv3d exact T={T} H={H} W={W} Cin={Ci} Cout={Co}", flush=True)
     x, cache, w, b = int_operands(T * 1000 + Co, T, H, W, Ci, Co)
@@ -104,7 +105,7 @@ def conv_at(x, cache, w, b, t, i, j):
 @pytest.mark.parametrize("layer", ["d3", "d_out"])
 def test_conv3d_full_video_shape_sampled(lib, layer):
     """The video decoder's two full-resolution layers (4 x 480 x 832): d3
-    (128 -> 64 channels, matrix cores) and d_out (64 -> 3, vector ALUs),
+    (128 -> 64 channels, bf16 out) and d_out (64 -> 3, fp32 channels-first out),
     random bf16 operands, outputs sampled at borders, cache frames and random
     positions against the definition in fp64."""
     v = get_vae_config("video13b")
