@@ -343,13 +343,16 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   if (a.nsplit > 1) {
     // partial result of this key range: unnormalised O and (reference max, sum)
     if (myq < a.L) {
-      float* po = a.part_o + sp * a.part_so + ((int64_t)r * a.L + myq) * a.d + (int64_t)h * HD;
+      bf16* po = a.part_o + sp * a.part_so + ((int64_t)r * a.L + myq) * a.d + (int64_t)h * HD;
 #pragma unroll
       for (int t = 0; t < HD / 32; ++t)
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          *(float4*)(po + t * 32 + 8 * g + 4 * half) =
-              make_float4(o[t][4 * g], o[t][4 * g + 1], o[t][4 * g + 2], o[t][4 * g + 3]);
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (bf16)o[t][4 * g + e];
+          *(bf16x4*)(po + t * 32 + 8 * g + 4 * half) = v;
+        }
       if (half == 0) a.part_ml[sp * a.part_sml + ((int64_t)r * a.H + h) * a.L + myq] = make_float2(m_run, l_tot);
     }
     return;
@@ -470,17 +473,16 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int r = a.r0 + rr;
   const float sl2 = a.scale * 1.4426950408889634f;
   const float2* ml = a.part_ml + ((int64_t)r * a.H + h) * a.L + t;
-  const float* po = a.part_o + ((int64_t)r * a.L + t) * a.d + (int64_t)h * a.hd + e;
+  const bf16* po = a.part_o + ((int64_t)r * a.L + t) * a.d + (int64_t)h * a.hd + e;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float l = 0.f;
   if constexpr (NS > 0) {
     float2 m[NS];
-    float4 x0[NS], x1[NS];
+    bf16x8 x[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       m[s] = ml[s * a.part_sml];
-      x0[s] = *(const float4*)(po + s * a.part_so);
-      x1[s] = *(const float4*)(po + s * a.part_so + 4);
+      x[s] = *(const bf16x8*)(po + s * a.part_so);
     }
     float mmax = -INFINITY;
 #pragma unroll
@@ -489,8 +491,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     for (int s = 0; s < NS; ++s) {
       const float w = m[s].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m[s].x - mmax) * sl2);
       l += w * m[s].y;
-      acc[0] += w * x0[s].x; acc[1] += w * x0[s].y; acc[2] += w * x0[s].z; acc[3] += w * x0[s].w;
-      acc[4] += w * x1[s].x; acc[5] += w * x1[s].y; acc[6] += w * x1[s].z; acc[7] += w * x1[s].w;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] += w * (float)x[s][j];
     }
   } else {
     float mmax = -INFINITY;
@@ -500,9 +502,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
       if (m.x == -INFINITY) continue;
       const float w = __builtin_amdgcn_exp2f((m.x - mmax) * sl2);
       l += w * m.y;
-      const float4 x0 = *(const float4*)(po + s * a.part_so), x1 = *(const float4*)(po + s * a.part_so + 4);
-      acc[0] += w * x0.x; acc[1] += w * x0.y; acc[2] += w * x0.z; acc[3] += w * x0.w;
-      acc[4] += w * x1.x; acc[5] += w * x1.y; acc[6] += w * x1.z; acc[7] += w * x1.w;
+      const bf16x8 x = *(const bf16x8*)(po + s * a.part_so);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] += w * (float)x[j];
     }
   }
   const float inv = l > 0.f ? 1.0f / l : 0.f;

@@ -81,7 +81,7 @@ struct AttnArgs {
   // absolute, strides part_so / part_sml elements), then a combine pass
   // normalises.  nsplit = 1 writes O directly.
   int nsplit;
-  float* part_o;
+  bf16* part_o;
   float2* part_ml;
   long long part_so, part_sml;
 };

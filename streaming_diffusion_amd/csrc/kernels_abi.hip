@@ -35,7 +35,7 @@ sd_status sd_k_gemm_resid(int32_t dtype, const void* A, const void* W, const voi
 }
 
 static size_t part_o_bytes(int32_t R, int32_t H, int32_t L, int32_t hd, int32_t nsplit) {
-  return (((size_t)nsplit * R * L * H * hd * 4) + 255) & ~(size_t)255;
+  return (((size_t)nsplit * R * L * H * hd * 2) + 255) & ~(size_t)255;
 }
 
 size_t sd_k_attention_workspace_bytes(int32_t R, int32_t H, int32_t L, int32_t hd, int32_t nsplit) {
@@ -93,7 +93,7 @@ sd_status sd_k_attention(int32_t dtype, const void* q, int64_t q_row_stride, int
   }
   a.nsplit = nsplit;
   if (nsplit > 1) {
-    a.part_o = (float*)workspace;
+    a.part_o = (bf16*)workspace;
     a.part_ml = (float2*)((char*)workspace + part_o_bytes(R, H, L, hd, nsplit));
     a.part_so = (long long)R * L * H * hd;
     a.part_sml = (long long)R * H * L;

@@ -65,7 +65,7 @@ struct sd_stream {
   float2 *rope_t = nullptr, *rope_h = nullptr, *rope_w = nullptr;
   // split-KV partials of the self-attention
   int attn_split_max = 1;
-  float* part_o = nullptr;
+  bf16* part_o = nullptr;         // split-KV partial outputs (unnormalised, bf16)
   float2* part_ml = nullptr;
   int cus = 256;                // compute units of the device
   size_t ws_used = 0;
@@ -192,7 +192,7 @@ size_t carve(sd_stream* s, char* base) {
     const size_t per = (size_t)M * s->d * 4 + (size_t)M * s->H * sizeof(float2);
     s->attn_split_max = (int)std::max<size_t>(1, std::min<size_t>(8, ((size_t)1 << 30) / per));
     if (s->attn_split_max > 1) {
-      s->part_o = cv.take<float>((size_t)s->attn_split_max * M * s->d * 4);
+      s->part_o = cv.take<bf16>((size_t)s->attn_split_max * M * s->d * 2);
       s->part_ml = cv.take<float2>((size_t)s->attn_split_max * M * s->H * sizeof(float2));
     }
   }

@@ -122,7 +122,7 @@ def test_create_rejects_bad_arguments_before_any_device_call(lib):
     assert lib.sd_k_attention(1, 8, 0, 0, 8, 1, 1, 8, 64, 1, C.byref(seg), 2, None, 0, None) == L.SD_ERR_ARG
     assert lib.sd_k_attention(1, 8, 0, 0, 8, 1, 1, 8, 64, 1, C.byref(seg), 2, 256, 16, None) == L.SD_ERR_WORKSPACE
     assert lib.sd_k_attention_workspace_bytes(2, 3, 40, 64, 1) == 0
-    assert lib.sd_k_attention_workspace_bytes(2, 3, 40, 64, 3) == ((3 * 2 * 40 * 3 * 64 * 4 + 255) // 256 * 256
+    assert lib.sd_k_attention_workspace_bytes(2, 3, 40, 64, 3) == ((3 * 2 * 40 * 3 * 64 * 2 + 255) // 256 * 256
                                                                   + 3 * 2 * 3 * 40 * 8)
 
 
