@@ -596,7 +596,7 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, int R_pos, int nn
       PROF(SD_PROF_ATTN_SELF, 4.0 * R * L * (shared + so.count) * d,
            (double)es * d * (2.0 * R * L + 2.0 * shared + 2.0 * R * L), sdk::attention(st, bf, A, false));
       if (A.nsplit > 1)
-        PROF(SD_PROF_ATTN_COMBINE, 0.0, (double)A.nsplit * R * L * (d * 4.0 + H * 8.0) + (double)R * L * d * es,
+        PROF(SD_PROF_ATTN_COMBINE, 0.0, (double)A.nsplit * R * L * (d * 2.0 + H * 8.0) + (double)R * L * d * es,
              sdk::attention_combine(st, A));
     }
     // the leaving chunks append their K / V^T in push order (ring positions
