@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--chunks", type=int, default=1, help="B: chunks entering (and leaving) per step")
     ap.add_argument("--batch-attn", action="store_true",
                     help="cross-frame batch attention: every row attends to the own tokens of all rows")
+    ap.add_argument("--io-stream", action="store_true",
+                    help="pushes on a second stream (the IO queue), overlapped with the previous step's forward")
     ap.add_argument("--kv-recompute", action="store_true",
                     help="leaving chunks' cache entries from a clean-latent forward at timestep 0 (+B rows per step)")
     ap.add_argument("--sampler", choices=["ddim", "lcm"], default="ddim",
@@ -143,7 +145,7 @@ def cpu_baseline(cfg, n_blocks_sample: int):
     }
 
 
-def measure(cfg, weights, steps: int, warmup: int, dev):
+def measure(cfg, weights, steps: int, warmup: int, dev, io_stream: bool = False):
     """Warm up (fills the slots, the window and the sink), time `steps` steps
     with the inputs resident in device memory, then one untimed step with
     every kernel kind timed.  Returns the bench record without the CPU leg."""
@@ -153,6 +155,8 @@ def measure(cfg, weights, steps: int, warmup: int, dev):
     from workloads import gen
 
     run = StreamRunner(cfg, weights)
+    if io_stream:
+        run.set_io_stream(torch.cuda.Stream())        # inputs below are resident before the timed region
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     if cfg.ctx_len:
         ctx = torch.from_numpy(gen.make_context(cfg)).to(dev).to(tdt)
@@ -250,7 +254,8 @@ def measure(cfg, weights, steps: int, warmup: int, dev):
                                + (f", {cfg.sampler} sampler" if cfg.sampler != "ddim" else "")
                                + (", clean-latent KV recompute" if cfg.kv_recompute else ""),
                    "rows_per_step": cfg.rows_per_step, "tokens_per_row": cfg.tokens,
-                   "frames_per_step": B * cfg.latent_t, "parallelism": "single GPU"},
+                   "frames_per_step": B * cfg.latent_t, "parallelism": "single GPU",
+                   "io_stream": bool(io_stream)},
         "ttff_ms": round(ttff_ms, 2) if ttff_ms else None,
         "roofline": roofline,
         "breakdown_one_step": bd,
@@ -475,7 +480,7 @@ def main():
         return
     cfg = get_config(args.workload, t_index=slot_indices(args.n_slots), chunks_per_step=args.chunks, **kw)
     weights = random_device_weights(cfg, seed=gen.SEED_WEIGHTS)
-    res = measure(cfg, weights, args.steps, args.warmup, dev)
+    res = measure(cfg, weights, args.steps, args.warmup, dev, args.io_stream)
     if args.calibrate_copy:
         n = args.calibrate_copy << 18          # float32 elements in MIB MiB
         a = torch.ones(n, dtype=torch.float32, device=dev)

@@ -204,6 +204,18 @@ sd_status sd_stream_set_context(sd_stream* s, const void* ctx_pos, const void* c
 sd_status sd_stream_push_frame(sd_stream* s, const float* x0, const float* noise,
                                const void* ssf_frame, double u, sd_push_info* info);
 
+/* IO queue (StreamDiffusion project intro: input and output queues that decouple
+ * frame arrival from the denoising loop).  With io_stream set (a hipStream_t of
+ * default priority), push_frame reads its inputs and runs all of its work there:
+ * the SSF / motion reductions (the only part the host waits for), the reference
+ * copies and the entry noise into a frame record.  The write of a frame record
+ * first waits, on the device, for the step that last read that record, and the
+ * next step waits for the push, so the pushes of the next chunk overlap the
+ * forward of the current step on one GPU.  The caller produces x0, noise and
+ * ssf_frame on io_stream (or before the call).  NULL (the default) runs pushes
+ * on the stream given at create. */
+sd_status sd_stream_set_io_stream(sd_stream* s, void* io_stream);
+
 /* Advance the pipeline by one denoising step (Stream Batch: the B oldest
  * pending chunks enter slot 0, every slot advances one timestep, the slot
  * group in the last slot leaves).  SD_ERR_NOT_READY while fewer than B chunks

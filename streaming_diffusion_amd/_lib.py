@@ -111,6 +111,7 @@ SIGNATURES = {
     "sd_stream_set_context": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p]),
     "sd_stream_push_frame": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_double,
                                        C.POINTER(sd_push_info)]),
+    "sd_stream_set_io_stream": (C.c_int, [C.c_void_p, C.c_void_p]),
     "sd_stream_step": (C.c_int, [C.c_void_p, C.c_void_p, C.POINTER(sd_step_info)]),
     "sd_stream_step_chunks": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.POINTER(sd_step_info)]),
     "sd_stream_kv_reset": (C.c_int, [C.c_void_p]),

@@ -85,8 +85,20 @@ struct sd_stream {
   int ev_used = 0;
   std::vector<ProfRec> prof_pending;
   sd_kernel_stat prof_acc[SD_PROF_KINDS];
+  hipStream_t pst = nullptr;            // stream the profiling events go to (st, or io during a push)
+  // IO queue: pushes on io; ev_push marks the last push, rec_ev[f] the end of
+  // the step that last read frame record f
+  hipStream_t io = nullptr;
+  hipEvent_t ev_push = nullptr;
+  bool push_pending = false;
+  std::vector<hipEvent_t> rec_ev;
+  std::vector<char> rec_ev_set;
   ~sd_stream() {
+    if (io) (void)hipStreamSynchronize(io);
+    if (st) (void)hipStreamSynchronize(st);
     for (hipEvent_t e : ev_pool) (void)hipEventDestroy(e);
+    for (hipEvent_t e : rec_ev) (void)hipEventDestroy(e);
+    if (ev_push) (void)hipEventDestroy(ev_push);
   }
 };
 
@@ -272,13 +284,13 @@ int prof_begin(sd_stream* s, int kind) {
   }
   const int ev = s->ev_used;
   s->ev_used += 2;
-  if (hipEventRecord(s->ev_pool[ev], s->st) != hipSuccess) return -1;
+  if (hipEventRecord(s->ev_pool[ev], s->pst) != hipSuccess) return -1;
   return ev;
 }
 
 void prof_end(sd_stream* s, int kind, int ev, double flops, double bytes) {
   if (ev < 0) return;
-  if (hipEventRecord(s->ev_pool[ev + 1], s->st) != hipSuccess) return;
+  if (hipEventRecord(s->ev_pool[ev + 1], s->pst) != hipSuccess) return;
   s->prof_pending.push_back({kind, ev, flops, bytes});
 }
 
@@ -326,6 +338,7 @@ sd_status sd_stream_create(const sd_stream_config* cfg, const sd_weights* w, voi
   s->cfg = *cfg;
   s->w = *w;
   s->st = (hipStream_t)hip_stream;
+  s->pst = s->st;
   dims(s);
   const size_t need_ws = carve(s, nullptr);
   if (ws_bytes < need_ws) {
@@ -335,6 +348,17 @@ sd_status sd_stream_create(const sd_stream_config* cfg, const sd_weights* w, voi
   s->ws_used = carve(s, (char*)workspace);
   sd::make_schedule(s->cfg, s->a, s->b);
   s->frames.assign(s->NF, FrameRec());
+  s->rec_ev.assign(s->NF, nullptr);
+  s->rec_ev_set.assign(s->NF, 0);
+  for (int i = 0; i < s->NF; ++i)
+    if (hipEventCreateWithFlags(&s->rec_ev[i], hipEventDisableTiming) != hipSuccess) {
+      delete s;
+      return SD_ERR_HIP;
+    }
+  if (hipEventCreateWithFlags(&s->ev_push, hipEventDisableTiming) != hipSuccess) {
+    delete s;
+    return SD_ERR_HIP;
+  }
   for (int i = 0; i < SD_MAX_SLOTS * SD_MAX_CHUNKS; ++i) s->slots[i] = -1;
   s->ctl.s = s->cfg.s_max;
   std::memset(s->prof_acc, 0, sizeof(s->prof_acc));
@@ -409,6 +433,13 @@ sd_status sd_stream_push_frame(sd_stream* s, const float* x0, const float* noise
   info->frame_id = -1;
   info->sim = 1.0;
   info->s = s->ctl.s;
+  // all of the push runs on the IO stream when one is set
+  const hipStream_t ps = s->io ? s->io : s->st;
+  s->pst = ps;
+  struct RestorePst {
+    sd_stream* s;
+    ~RestorePst() { s->pst = s->st; }
+  } restore_pst{s};
   // device reductions for the SSF and motion decisions, one read-back
   const void* ssf_cur = c.ssf_kind == SD_SSF_U8 ? ssf_frame : (const void*)x0;
   const int64_t ssf_n = c.ssf_kind == SD_SSF_U8 ? (int64_t)c.ssf_h * c.ssf_w * c.ssf_c : s->lat;
@@ -416,13 +447,13 @@ sd_status sd_stream_push_frame(sd_stream* s, const float* x0, const float* noise
   long long hs[4 + 64] = {};
   if (do_ssf)
     PROF(SD_PROF_CONTROLS, 0.0, 2.0 * ssf_n * (c.ssf_kind == SD_SSF_U8 ? 1 : 4),
-         sdk::ssf_sums(s->st, c.ssf_kind, ssf_cur, s->ssf_ref, ssf_n, s->sums));
+         sdk::ssf_sums(ps, c.ssf_kind, ssf_cur, s->ssf_ref, ssf_n, s->sums));
   if (c.motion_on)
     PROF(SD_PROF_CONTROLS, 0.0, 4.0 * (s->Tn + 1) * s->frame_elems,
-         sdk::motion_sums(s->st, x0, s->ctl.has_prev ? s->mprev : nullptr, s->Tn, s->frame_elems, s->sums + 4));
+         sdk::motion_sums(ps, x0, s->ctl.has_prev ? s->mprev : nullptr, s->Tn, s->frame_elems, s->sums + 4));
   if (do_ssf || c.motion_on) {
-    HIP_TRY(hipMemcpyAsync(hs, s->sums, sizeof(long long) * (4 + s->Tn), hipMemcpyDeviceToHost, s->st));
-    HIP_TRY(hipStreamSynchronize(s->st));
+    HIP_TRY(hipMemcpyAsync(hs, s->sums, sizeof(long long) * (4 + s->Tn), hipMemcpyDeviceToHost, ps));
+    HIP_TRY(hipStreamSynchronize(ps));
   }
   if (c.ssf_on) {
     double sim = 1.0, p = 0.0;
@@ -434,7 +465,7 @@ sd_status sd_stream_push_frame(sd_stream* s, const float* x0, const float* noise
       return SD_OK;
     }
     const size_t rb = c.ssf_kind == SD_SSF_U8 ? (size_t)ssf_n : (size_t)ssf_n * 4;
-    HIP_TRY(hipMemcpyAsync(s->ssf_ref, ssf_cur, rb, hipMemcpyDeviceToDevice, s->st));
+    HIP_TRY(hipMemcpyAsync(s->ssf_ref, ssf_cur, rb, hipMemcpyDeviceToDevice, ps));
   }
   const int f = free_frame(s);
   if (f < 0) return set_err(s, SD_ERR_STATE, "frame store full");
@@ -446,7 +477,7 @@ sd_status sd_stream_push_frame(sd_stream* s, const float* x0, const float* noise
     sd::motion_push(s->ctl, c, dist, nd);
     if (nd > 0) info->d = dist[nd - 1];
     HIP_TRY(hipMemcpyAsync(s->mprev, x0 + (int64_t)(s->Tn - 1) * s->frame_elems, s->frame_elems * 4,
-                           hipMemcpyDeviceToDevice, s->st));
+                           hipMemcpyDeviceToDevice, ps));
     s->ctl.has_prev = true;
     sd::taus_from_noise_rate(s->ctl.s, s->n, c.n_train_steps, fr.taus);
   } else {
@@ -457,12 +488,18 @@ sd_status sd_stream_push_frame(sd_stream* s, const float* x0, const float* noise
   fr.fid = s->n_pushed++;
   fr.used = true;
   const int tau0 = fr.taus[0];
+  // the record's previous reader (a step on the main stream) must be done
+  if (s->io && s->rec_ev_set[f]) HIP_TRY(hipStreamWaitEvent(ps, s->rec_ev[f], 0));
   PROF(SD_PROF_EPILOGUE, 2.0 * s->lat, 16.0 * s->lat,
-       sdk::entry_noise(s->st, x0, noise, s->fx + (int64_t)f * s->lat, s->fx0s + (int64_t)f * s->lat, s->lat,
+       sdk::entry_noise(ps, x0, noise, s->fx + (int64_t)f * s->lat, s->fx0s + (int64_t)f * s->lat, s->lat,
                         (float)s->a[tau0], (float)s->b[tau0]));
   if (s->fz)
     HIP_TRY(hipMemcpyAsync(s->fz + (int64_t)f * (s->n - 1) * s->lat, noise + s->lat,
-                           (size_t)(s->n - 1) * s->lat * 4, hipMemcpyDeviceToDevice, s->st));
+                           (size_t)(s->n - 1) * s->lat * 4, hipMemcpyDeviceToDevice, ps));
+  if (s->io) {
+    HIP_TRY(hipEventRecord(s->ev_push, ps));
+    s->push_pending = true;
+  }
   s->pending.push_back(f);
   info->t0 = fr.t0;
   info->frame_id = fr.fid;
@@ -747,6 +784,10 @@ sd_status sd_stream_step_chunks(sd_stream* s, int32_t chunks, float* out_latent,
   const bool will_exit = (n == 1) || (s->slots[(n - 2) * B] >= 0);
   if (will_exit && !out_latent) return set_err(s, SD_ERR_ARG, "out_latent is null but frames leave this step");
   std::memset(info, 0, sizeof(*info));
+  if (s->push_pending) {
+    HIP_TRY(hipStreamWaitEvent(s->st, s->ev_push, 0));   // the entering chunks' records are written
+    s->push_pending = false;
+  }
 
   // ---- slot-group shift (the B oldest pending chunks enter slot 0) and row
   // table: slot by slot, the chunks of a slot in push order
@@ -877,7 +918,12 @@ sd_status sd_stream_step_chunks(sd_stream* s, int32_t chunks, float* out_latent,
     info->frame_id = s->frames[s->slots[(n - 1) * B]].fid;
     for (int k = 0; k < B; ++k) {
       const int f = s->slots[(n - 1) * B + k];
-      if (f >= 0) s->frames[f].used = false;
+      if (f >= 0) {
+        s->frames[f].used = false;
+        // a later push on the IO stream rewrites the record only after this step
+        HIP_TRY(hipEventRecord(s->rec_ev[f], st));
+        s->rec_ev_set[f] = 1;
+      }
       s->slots[(n - 1) * B + k] = -1;
     }
     if (s->Wt > 0) {
@@ -940,6 +986,7 @@ sd_status sd_stream_profile(sd_stream* s, uint32_t kind_mask) {
 
 sd_status sd_stream_profile_read(sd_stream* s, sd_kernel_stat* out, int32_t n_max, int32_t* n_out) {
   if (!s || !out || !n_out || n_max < 1) return SD_ERR_ARG;
+  if (s->io) HIP_TRY(hipStreamSynchronize(s->io));
   HIP_TRY(hipStreamSynchronize(s->st));
   for (int k = 0; k < SD_PROF_KINDS; ++k) s->prof_acc[k].kind = k;
   for (const auto& r : s->prof_pending) {
@@ -958,6 +1005,16 @@ sd_status sd_stream_profile_read(sd_stream* s, sd_kernel_stat* out, int32_t n_ma
     if (s->prof_acc[k].launches > 0) out[n++] = s->prof_acc[k];
   *n_out = n;
   std::memset(s->prof_acc, 0, sizeof(s->prof_acc));
+  return SD_OK;
+}
+
+sd_status sd_stream_set_io_stream(sd_stream* s, void* io_stream) {
+  if (!s) return SD_ERR_ARG;
+  if (s->io && (hipStream_t)io_stream != s->io) {
+    // later steps no longer wait on ev_push: let the switch wait for the old queue
+    HIP_TRY(hipStreamSynchronize(s->io));
+  }
+  s->io = (hipStream_t)io_stream;
   return SD_OK;
 }
 

@@ -141,6 +141,12 @@ class StreamRunner:
     def kv_reset(self):
         L.check(self.lib.sd_stream_kv_reset(self.h), self.h)
 
+    def set_io_stream(self, stream=None):
+        """Run pushes on `stream` (a torch.cuda.Stream on which the caller also
+        produces the inputs), overlapped with the steps; None: the main stream."""
+        self.io_stream = stream
+        L.check(self.lib.sd_stream_set_io_stream(self.h, C.c_void_p(stream.cuda_stream if stream else None)), self.h)
+
     def sink_info(self) -> L.sd_sink_info:
         info = L.sd_sink_info()
         L.check(self.lib.sd_stream_sink_info(self.h, C.byref(info)), self.h)

@@ -29,8 +29,10 @@ def reduced(name, **kw):
     return get_config(name, **base)
 
 
-def run_parity(cfg, steps, check_ring=True, sizes=None):
-    """`sizes`: chunks entering at each step (cycled); default B every step."""
+def run_parity(cfg, steps, check_ring=True, sizes=None, io_stream=False):
+    """`sizes`: chunks entering at each step (cycled); default B every step.
+    `io_stream`: inputs are produced and pushed on a second stream (the IO
+    queue), overlapped with the steps on the main stream."""
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     weights = gen.make_weights(cfg)
     ctx_pos = gen.make_context(cfg)
@@ -39,6 +41,9 @@ def run_parity(cfg, steps, check_ring=True, sizes=None):
     run = StreamRunner(cfg, upload_weights(cfg, weights))
     if cfg.ctx_len:
         run.set_context(to_dev(ctx_pos, tdt), to_dev(ctx_neg, tdt) if ctx_neg is not None else None)
+    io = torch.cuda.Stream() if io_stream else None
+    if io is not None:
+        run.set_io_stream(io)
     src, nz, us = gen.LatentSource(cfg), gen.NoiseSource(cfg), gen.UniformSource()
     ssf_src = gen.SSFFrameSource(cfg) if cfg.ssf_on and cfg.ssf_kind == "u8" else None
     lat = cfg.latent_elems
@@ -49,8 +54,9 @@ def run_parity(cfg, steps, check_ring=True, sizes=None):
         x0, e, u = src.next(), gen.frame_noise(cfg, nz), us.next()
         frame = ssf_src.next() if ssf_src else None
         po = orc.push_frame(x0, e, frame, u)
-        pg = run.push(to_dev(x0, torch.float32), to_dev(e, torch.float32),
-                      to_dev(frame, torch.uint8) if frame is not None else None, u)
+        with torch.cuda.stream(io if io is not None else torch.cuda.current_stream()):
+            pg = run.push(to_dev(x0, torch.float32), to_dev(e, torch.float32),
+                          to_dev(frame, torch.uint8) if frame is not None else None, u)
         pushes += 1
         # SSF decision, probability and similarity: bit-exact
         assert bool(pg.skipped) == po.skipped, f"push {pushes}"
@@ -261,6 +267,24 @@ def test_video_bf16_clean_latent_kv_recompute_two_chunks_per_step():
     print("video bf16 reduced clean-latent KV recompute B=2", flush=True)
     orc, _ = run_parity(cfg, 8)
     assert orc.kv_valid == cfg.window_tokens
+
+
+def test_video_bf16_pushes_on_an_io_stream_two_chunks_per_step():
+    """Inputs produced and pushed on a second stream (motion reductions,
+    entry noise into recycled frame records) overlapped with the steps: the
+    same outputs, ring and sink as the oracle."""
+    device()
+    cfg = reduced("video13b", chunks_per_step=2)
+    print("video bf16 reduced B=2, pushes on an IO stream", flush=True)
+    orc, _ = run_parity(cfg, 10, io_stream=True)
+    assert orc.kv_valid == cfg.window_tokens
+
+
+def test_tiny_fp32_ssf_pushes_on_an_io_stream():
+    device()
+    cfg = reduced("tiny")
+    print("tiny fp32 SSF, pushes on an IO stream", flush=True)
+    run_parity(cfg, 12, io_stream=True)
 
 
 def test_step_chunks_out_of_range():
