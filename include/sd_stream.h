@@ -212,8 +212,9 @@ sd_status sd_stream_push_frame(sd_stream* s, const float* x0, const float* noise
  * first waits, on the device, for the step that last read that record, and the
  * next step waits for the push, so the pushes of the next chunk overlap the
  * forward of the current step on one GPU.  The caller produces x0, noise and
- * ssf_frame on io_stream (or before the call).  NULL (the default) runs pushes
- * on the stream given at create. */
+ * ssf_frame on io_stream (or before the call) and keeps io_stream alive while
+ * it is set.  NULL (the default) runs pushes on the stream given at create;
+ * switching queues first waits for the old one. */
 sd_status sd_stream_set_io_stream(sd_stream* s, void* io_stream);
 
 /* Advance the pipeline by one denoising step (Stream Batch: the B oldest
