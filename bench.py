@@ -167,6 +167,13 @@ def measure(cfg, weights, steps: int, warmup: int, dev, io_stream: bool = False)
     src, nz = gen.LatentSource(cfg), gen.NoiseSource(cfg)
     xs = [torch.from_numpy(src.next()).to(dev) for _ in range(total)]
     ns = [torch.from_numpy(gen.frame_noise(cfg, nz)).to(dev) for _ in range(total)]
+    # SSF on images needs the frames; the uniform 1.0 never skips (u < p is
+    # false for p <= 1), so the filter's reductions and decision run on every
+    # push and every timed step has its chunks
+    fs = None
+    if cfg.ssf_on and cfg.ssf_kind == "u8":
+        fsrc = gen.SSFFrameSource(cfg)
+        fs = [torch.from_numpy(fsrc.next()).to(dev) for _ in range(total)]
     out = run.out
     torch.cuda.synchronize()
     k = 0
@@ -174,7 +181,7 @@ def measure(cfg, weights, steps: int, warmup: int, dev, io_stream: bool = False)
     def push_group():
         nonlocal k
         for _ in range(B):
-            run.push(xs[k], ns[k])
+            run.push(xs[k], ns[k], fs[k] if fs is not None else None, 1.0)
             k += 1
 
     # warm-up; time to first frame
