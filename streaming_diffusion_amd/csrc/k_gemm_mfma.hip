@@ -688,6 +688,11 @@ hipError_t gemm_mfma_mode(hipStream_t s, const bf16* A, const bf16* W, int M, in
     const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
     const int64_t t192 = (int64_t)((M + 191) / 192) * ((N + 255) / 256);
     const int64_t c256 = (t256 + cus - 1) / cus * 256, c192 = (t192 + cus - 1) / cus * 192;
+    // small problems: when even the 192-row tiles would occupy fewer than 60 %
+    // of the CUs, 128 x 128 tiles (4 waves, two workgroups per CU) spread the
+    // work over more of them (measured faster on every GEMM of the 12- and
+    // 24-block image DiTs, slower on the video DiT's 198-tile N = 1536 GEMMs)
+    if (t192 * 10 < cus * 6) return launch_dma<128, 128, 4, 64, 2, true, MODE>(s, A, W, M, N, K, E);
     if (c192 < c256) return launch_dma<192, 256, 8, 64, 2, true, MODE>(s, A, W, M, N, K, E);
     return launch_dma<256, 256, 8, 64, 2, true, MODE>(s, A, W, M, N, K, E);
   }
