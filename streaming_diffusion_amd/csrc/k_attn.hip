@@ -260,21 +260,40 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     if (tile + 1 < NT) issue(tile + 1, buf ^ 1);
     const bf16* ks = smem + buf * STAGE;
     const bf16* vs = ks + KT_EL;
-    // S^T for two 32-key halves of the tile
-    f32x16 s[2];
+    // S^T for two 32-key halves of the tile.  Every K fragment read is
+    // issued before the first product: while the next tile's DMA is in
+    // flight each LDS wait drains all outstanding reads, so reads issued one
+    // product ahead would put an LDS round trip in front of every MFMA.
+    bf16x8 ka[2][HD / 16];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const int row = kt * 32 + krow;
       const bf16* kp = ks + row * HD;
       const int sw = chunk_swz<HD>(row);
-      bf16x8 ka[HD / 16];
 #pragma unroll
-      for (int kk = 0; kk < HD / 16; ++kk) ka[kk] = *(const bf16x8*)(kp + (((kk * 2 + half) ^ sw) * 8));
+      for (int kk = 0; kk < HD / 16; ++kk) ka[kt][kk] = *(const bf16x8*)(kp + (((kk * 2 + half) ^ sw) * 8));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 s[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int q = 0; q < 16; ++q) s[kt][q] = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < HD / 16; ++kk) s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qf[kk], s[kt], 0, 0, 0);
-    }
+    for (int kk = 0; kk < HD / 16; ++kk)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kt][kk], qf[kk], s[kt], 0, 0, 0);
+    // the V^T fragments of the PV product, read while the softmax runs
+    bf16x8 va[4][HD / 32];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int t = 0; t < HD / 32; ++t) {
+        const int row = t * 32 + vrow;
+        va[kb][t] = *(const bf16x8*)(vs + row * KB + (((kb * 2 + half) ^ chunk_swz<KB>(row)) * 8));
+      }
+    __builtin_amdgcn_sched_barrier(0);
     // accumulator q of half kt holds tile key kt*32 + 16*(q/8) + 8*half + (q%8)
     const int nvalid = tile_ref(tile).nvalid;
     if (__builtin_expect(nvalid < KB, 0)) {
@@ -326,17 +345,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
       l_run += ps0 + ps1;
     }
     // O^T += V^T P^T over 4 key blocks of 16
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      bf16x8 va[HD / 32];
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int t = 0; t < HD / 32; ++t) {
-        const int row = t * 32 + vrow;
-        va[t] = *(const bf16x8*)(vs + row * KB + (((kb * 2 + half) ^ chunk_swz<KB>(row)) * 8));
-      }
-#pragma unroll
-      for (int t = 0; t < HD / 32; ++t) o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t], pb[kb], o[t], 0, 0, 0);
-    }
+      for (int t = 0; t < HD / 32; ++t) o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kb][t], pb[kb], o[t], 0, 0, 0);
   }
 
   const float l_tot = halves_sum(l_run);

@@ -76,7 +76,7 @@ struct AttnArgs {
   KvSeg seg[3];
   float scale;            // 1/sqrt(hd)
   // split over the key sequence (bf16 path): nsplit workgroups share one
-  // query tile, each writes unnormalised O (fp32) and its (max, sum) to
+  // query tile, each writes unnormalised O (bf16) and its (max, sum) to
   // part_o [nsplit][rows*L][d] / part_ml [nsplit][rows][H][L] (row index
   // absolute, strides part_so / part_sml elements), then a combine pass
   // normalises.  nsplit = 1 writes O directly.

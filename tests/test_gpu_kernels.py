@@ -142,6 +142,9 @@ def make_segments(rng, H, hd, R, L, sink_count, sink_cap, W, ring_start, ring_co
     ("bf16", 64, 72, 4, 64, 40, 48, 2),        # split over the keys, partial combine
     ("bf16", 128, 200, 12, 512, 136, 504, 3),
     ("bf16", 128, 136, 8, 256, 0, 256, 5),     # more splits than some key ranges fill
+    ("bf16", 128, 296, 4, 640, 600, 600, 1),   # 256-query tiles, the second partial; 16 key tiles, every LDS stage reused
+    ("bf16", 128, 8, 0, 64, 0, 0, 1),          # a single (partial) key tile
+    ("bf16", 128, 520, 0, 448, 104, 448, 2),   # three query tiles, two key splits of odd tile counts
     ("bf16", 64, 72, 0, 64, 0, 0, 1),          # full key tile then a partial one (masked keys hold real data)
     ("bf16", 64, 72, 0, 64, 0, 64, 1),         # full ring tile, full own tile, partial own tile
     ("bf16", 64, 64, 8, 64, 0, 0, 1),          # partial sink tile (8 of 64), then the own tile
