@@ -27,7 +27,7 @@ def lib():
 
 # ------------------------------------------------------------------ GEMM
 @pytest.mark.parametrize("M,N,K", [(300, 200, 136), (64, 64, 16), (1, 8, 8), (257, 129, 1040), (400, 300, 128),
-                                   (6240, 4608, 1536), (6240, 1536, 8960)])
+                                   (6240, 4608, 1536), (6240, 1536, 8960), (6240, 960, 1536)])
 def test_gemm_bf16_exact_integers(lib, M, N, K):
     """Inputs k/16 with |k| <= 8 are exact in bf16 and every product and
     partial sum is exact in fp32, so the MFMA result must equal the integer
@@ -49,7 +49,7 @@ def test_gemm_bf16_exact_integers(lib, M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [(400, 300, 128), (64, 64, 64), (1, 8, 64), (300, 200, 136), (300, 200, 4096),
                                    (1000, 520, 2048), (1500, 700, 1600), (2048, 768, 3072), (6240, 1536, 1536),
-                                   (6240, 1536, 8960), (3120, 5120, 5120)])
+                                   (6240, 1536, 8960), (3120, 5120, 5120), (6240, 1536, 960)])
 def test_gemm_resid_bf16_exact_integers(lib, M, N, K):
     """Residual accumulation C += A W^T + b with integer-valued operands: every
     product, partial sum and the final sum are exact in fp32, so the result is
