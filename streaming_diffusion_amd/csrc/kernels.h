@@ -35,6 +35,11 @@ hipError_t kv_append(hipStream_t s, bool bf, const void* kown, const void* vtown
 hipError_t sink_copy(hipStream_t s, bool bf, const int* flag, const void* ringK, const void* ringVT, void* sinkK,
                      void* sinkVT, int nb, int H, int hd, int W, int S8, int ptr_old, int Se);
 hipError_t fill_zero(hipStream_t s, void* p, size_t bytes);
+// cross-attention with folded prompt projections (k_attn.hip): the folded
+// score / output matrices of one block and context, and the grouped softmax
+hipError_t cross_fold(hipStream_t s, const bf16* K, const bf16* VT, const bf16* Wq, const bf16* bq, const bf16* Wo,
+                      bf16* wq_f, float* cq, bf16* wo_f, int d, int H, int hd, int C, int Cp);
+hipError_t ctx_softmax(hipStream_t s, const float* S, const float* c, bf16* P, int64_t M, int H, int Cp);
 
 // ---------------------------------------------------------------- reductions
 // Exact int64 (sum a*b, sum a*a, sum b*b); kind 0 = uint8, 1 = fp32 latents

@@ -60,6 +60,11 @@ struct sd_stream {
   // chunks at those positions); [nb][H][Cc][hd] and [nb][H][hd][Cc]
   void *candK = nullptr, *candVT = nullptr;
   void *ctxK = nullptr, *ctxVT = nullptr;
+  // one bf16 context: cross-attention runs on folded projections (k_attn.hip):
+  // per block wq_f [H Cp][d], wo_f [d][H Cp] bf16 and the score bias [H Cp]
+  bool fold = false;
+  void *fold_q = nullptr, *fold_o = nullptr;
+  float* fold_c = nullptr;
   float *sink_emb = nullptr, *sink_part = nullptr, *sink_sim = nullptr;
   int* sink_flag = nullptr;
   float2 *rope_t = nullptr, *rope_h = nullptr, *rope_w = nullptr;
@@ -191,6 +196,14 @@ size_t carve(sd_stream* s, char* base) {
   if (c.ctx_len > 0) {
     s->ctxK = cv.take<void>((size_t)s->nb * nctx * s->H * s->ctx8 * s->hd * es);
     s->ctxVT = cv.take<void>((size_t)s->nb * nctx * s->H * s->ctx8 * s->hd * es);
+    // the step's scores (fp32) and probabilities (bf16) live in the FFN buffer
+    const size_t ncol = (size_t)s->H * s->ctx8;
+    s->fold = s->bf && nctx == 1 && s->ctx8 <= 128 && ncol * 3 <= (size_t)s->F;
+    if (s->fold) {
+      s->fold_q = cv.take<void>((size_t)s->nb * ncol * s->d * es);
+      s->fold_o = cv.take<void>((size_t)s->nb * s->d * ncol * es);
+      s->fold_c = cv.take<float>((size_t)s->nb * ncol * 4);
+    }
   }
   s->sink_emb = cv.take<float>((size_t)std::max(1, s->Ment) * s->d * 4);
   s->sink_part = cv.take<float>((size_t)64 * s->d * 4);
@@ -416,6 +429,18 @@ sd_status sd_stream_set_context(sd_stream* s, const void* ctx_pos, const void* c
       HIP_TRY(sdk::gemm(s->st, s->bf, ci == 0 ? ctx_pos : ctx_neg, P(s->w.ckv_w, (int64_t)b * 2 * s->d * s->d, s->es),
                         c.ctx_len, 2 * s->d, s->d, E));
     }
+  if (s->fold) {
+    const int64_t ncol = (int64_t)s->H * s->ctx8, d = s->d;
+    for (int b = 0; b < s->nb; ++b)
+      HIP_TRY(sdk::cross_fold(s->st, (const bf16*)P(s->ctxK, (int64_t)b * per, s->es),
+                              (const bf16*)P(s->ctxVT, (int64_t)b * per, s->es),
+                              (const bf16*)P(s->w.cq_w, (int64_t)b * d * d, s->es),
+                              (const bf16*)P(s->w.cq_b, (int64_t)b * d, s->es),
+                              (const bf16*)P(s->w.co_w, (int64_t)b * d * d, s->es),
+                              (bf16*)Pm(s->fold_q, (int64_t)b * ncol * d, s->es), s->fold_c + b * ncol,
+                              (bf16*)Pm(s->fold_o, (int64_t)b * d * ncol, s->es), s->d, s->H, s->hd, c.ctx_len,
+                              s->ctx8));
+  }
   s->ctx_set = true;
   return SD_OK;
 }
@@ -673,7 +698,29 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, int R_pos, int nn
            sdk::gemm(st, bf, s->ao, P(s->w.o_w, (int64_t)b * d * d, es), M, d, d, E));
     }
     // cross-attention to the pre-computed prompt K/V
-    if (c.ctx_len > 0) {
+    if (c.ctx_len > 0 && s->fold) {
+      PROF(SD_PROF_LN, 0.0, (4.0 + es) * M * d,
+           sdk::ln_mod(st, bf, s->resid, s->xm, M, d, L, nullptr, nullptr, 0, 0, 6 * d, 1e-6f));
+      const int ncol = H * s->ctx8;
+      float* sc = (float*)s->hid;
+      bf16* pc = (bf16*)((char*)s->hid + (size_t)M * ncol * 4);
+      {
+        Epi E = epi_base(s, EPI_F32);
+        E.out = sc;
+        E.ldo = ncol;
+        PROF(SD_PROF_GEMM_CROSS, gflop(M, ncol, d), gbytes(M, ncol, d, es, 4),
+             sdk::gemm(st, bf, s->xm, P(s->fold_q, (int64_t)b * ncol * d, es), M, ncol, d, E));
+      }
+      PROF(SD_PROF_ATTN_CROSS, 4.0 * M * ncol, 6.0 * M * ncol,
+           sdk::ctx_softmax(st, sc, s->fold_c + (size_t)b * ncol, pc, M, H, s->ctx8));
+      {
+        Epi E = epi_base(s, EPI_RESID);
+        E.bias = P(s->w.co_b, (int64_t)b * d, es);
+        E.resid = s->resid;
+        PROF(SD_PROF_GEMM_CROSS, gflop(M, d, ncol), gbytes(M, d, ncol, es, 8),
+             sdk::gemm(st, bf, pc, P(s->fold_o, (int64_t)b * d * ncol, es), M, d, ncol, E));
+      }
+    } else if (c.ctx_len > 0) {
       PROF(SD_PROF_LN, 0.0, (4.0 + es) * M * d,
            sdk::ln_mod(st, bf, s->resid, s->xm, M, d, L, nullptr, nullptr, 0, 0, 6 * d, 1e-6f));
       {
