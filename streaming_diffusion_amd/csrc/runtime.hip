@@ -60,8 +60,8 @@ struct sd_stream {
   // chunks at those positions); [nb][H][Cc][hd] and [nb][H][hd][Cc]
   void *candK = nullptr, *candVT = nullptr;
   void *ctxK = nullptr, *ctxVT = nullptr;
-  // one bf16 context: cross-attention runs on folded projections (k_attn.hip):
-  // per block wq_f [H Cp][d], wo_f [d][H Cp] bf16 and the score bias [H Cp]
+  // bf16: cross-attention runs on folded projections (k_attn.hip): per block
+  // and context wq_f [H Cp][d], wo_f [d][H Cp] bf16 and the score bias [H Cp]
   bool fold = false;
   void *fold_q = nullptr, *fold_o = nullptr;
   float* fold_c = nullptr;
@@ -196,13 +196,15 @@ size_t carve(sd_stream* s, char* base) {
   if (c.ctx_len > 0) {
     s->ctxK = cv.take<void>((size_t)s->nb * nctx * s->H * s->ctx8 * s->hd * es);
     s->ctxVT = cv.take<void>((size_t)s->nb * nctx * s->H * s->ctx8 * s->hd * es);
-    // the step's scores (fp32) and probabilities (bf16) live in the FFN buffer
+    // folding trades the d x d Q and O projections for two d x H Cp GEMMs: it
+    // pays only when H Cp <= d.  The step's scores (fp32) and probabilities
+    // (bf16) live in the FFN buffer.
     const size_t ncol = (size_t)s->H * s->ctx8;
-    s->fold = s->bf && nctx == 1 && s->ctx8 <= 128 && ncol * 3 <= (size_t)s->F;
+    s->fold = s->bf && s->ctx8 <= 128 && ncol <= (size_t)s->d && ncol * 3 <= (size_t)s->F;
     if (s->fold) {
-      s->fold_q = cv.take<void>((size_t)s->nb * ncol * s->d * es);
-      s->fold_o = cv.take<void>((size_t)s->nb * s->d * ncol * es);
-      s->fold_c = cv.take<float>((size_t)s->nb * ncol * 4);
+      s->fold_q = cv.take<void>((size_t)s->nb * nctx * ncol * s->d * es);
+      s->fold_o = cv.take<void>((size_t)s->nb * nctx * s->d * ncol * es);
+      s->fold_c = cv.take<float>((size_t)s->nb * nctx * ncol * 4);
     }
   }
   s->sink_emb = cv.take<float>((size_t)std::max(1, s->Ment) * s->d * 4);
@@ -432,14 +434,15 @@ sd_status sd_stream_set_context(sd_stream* s, const void* ctx_pos, const void* c
   if (s->fold) {
     const int64_t ncol = (int64_t)s->H * s->ctx8, d = s->d;
     for (int b = 0; b < s->nb; ++b)
-      HIP_TRY(sdk::cross_fold(s->st, (const bf16*)P(s->ctxK, (int64_t)b * per, s->es),
-                              (const bf16*)P(s->ctxVT, (int64_t)b * per, s->es),
-                              (const bf16*)P(s->w.cq_w, (int64_t)b * d * d, s->es),
-                              (const bf16*)P(s->w.cq_b, (int64_t)b * d, s->es),
-                              (const bf16*)P(s->w.co_w, (int64_t)b * d * d, s->es),
-                              (bf16*)Pm(s->fold_q, (int64_t)b * ncol * d, s->es), s->fold_c + b * ncol,
-                              (bf16*)Pm(s->fold_o, (int64_t)b * d * ncol, s->es), s->d, s->H, s->hd, c.ctx_len,
-                              s->ctx8));
+      for (int ci = 0; ci < nctx; ++ci) {
+        const int64_t bc = (int64_t)b * nctx + ci;
+        HIP_TRY(sdk::cross_fold(s->st, (const bf16*)P(s->ctxK, bc * per, s->es), (const bf16*)P(s->ctxVT, bc * per, s->es),
+                                (const bf16*)P(s->w.cq_w, (int64_t)b * d * d, s->es),
+                                (const bf16*)P(s->w.cq_b, (int64_t)b * d, s->es),
+                                (const bf16*)P(s->w.co_w, (int64_t)b * d * d, s->es),
+                                (bf16*)Pm(s->fold_q, bc * ncol * d, s->es), s->fold_c + bc * ncol,
+                                (bf16*)Pm(s->fold_o, bc * d * ncol, s->es), s->d, s->H, s->hd, c.ctx_len, s->ctx8));
+      }
   }
   s->ctx_set = true;
   return SD_OK;
@@ -704,21 +707,26 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, int R_pos, int nn
       const int ncol = H * s->ctx8;
       float* sc = (float*)s->hid;
       bf16* pc = (bf16*)((char*)s->hid + (size_t)M * ncol * 4);
-      {
-        Epi E = epi_base(s, EPI_F32);
-        E.out = sc;
-        E.ldo = ncol;
-        PROF(SD_PROF_GEMM_CROSS, gflop(M, ncol, d), gbytes(M, ncol, d, es, 4),
-             sdk::gemm(st, bf, s->xm, P(s->fold_q, (int64_t)b * ncol * d, es), M, ncol, d, E));
-      }
-      PROF(SD_PROF_ATTN_CROSS, 4.0 * M * ncol, 6.0 * M * ncol,
-           sdk::ctx_softmax(st, sc, s->fold_c + (size_t)b * ncol, pc, M, H, s->ctx8));
-      {
-        Epi E = epi_base(s, EPI_RESID);
-        E.bias = P(s->w.co_b, (int64_t)b * d, es);
-        E.resid = s->resid;
-        PROF(SD_PROF_GEMM_CROSS, gflop(M, d, ncol), gbytes(M, d, ncol, es, 8),
-             sdk::gemm(st, bf, pc, P(s->fold_o, (int64_t)b * d * ncol, es), M, d, ncol, E));
+      // rows [0, R_pos) read the positive context, [R_pos, R_pos + nneg) the negative one
+      for (int part = 0; part < (nneg > 0 ? 2 : 1); ++part) {
+        const int64_t t0 = (int64_t)(part == 0 ? 0 : R_pos) * L, Mp = (int64_t)(part == 0 ? R_pos : nneg) * L;
+        const int64_t bc = (int64_t)b * nctx + part;
+        {
+          Epi E = epi_base(s, EPI_F32);
+          E.out = sc + t0 * ncol;
+          E.ldo = ncol;
+          PROF(SD_PROF_GEMM_CROSS, gflop(Mp, ncol, d), gbytes(Mp, ncol, d, es, 4),
+               sdk::gemm(st, bf, P(s->xm, t0 * d, es), P(s->fold_q, bc * ncol * d, es), (int)Mp, ncol, d, E));
+        }
+        PROF(SD_PROF_ATTN_CROSS, 4.0 * Mp * ncol, 6.0 * Mp * ncol,
+             sdk::ctx_softmax(st, sc + t0 * ncol, s->fold_c + bc * ncol, pc + t0 * ncol, Mp, H, s->ctx8));
+        {
+          Epi E = epi_base(s, EPI_RESID);
+          E.bias = P(s->w.co_b, (int64_t)b * d, es);
+          E.resid = s->resid + t0 * d;
+          PROF(SD_PROF_GEMM_CROSS, gflop(Mp, d, ncol), gbytes(Mp, d, ncol, es, 8),
+               sdk::gemm(st, bf, pc + t0 * ncol, P(s->fold_o, bc * d * ncol, es), (int)Mp, d, ncol, E));
+        }
       }
     } else if (c.ctx_len > 0) {
       PROF(SD_PROF_LN, 0.0, (4.0 + es) * M * d,
