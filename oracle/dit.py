@@ -30,7 +30,10 @@ definitions, linear against integer brute force, RoPE norm preservation,
 relative-position property and the rotation of a unit pair, attention
 against a pure-Python softmax loop and its special cases, modulation with
 zero scale/shift reducing to LayerNorm, a block whose gates are zero being
-the identity.  The composed forward is "parity unpinned" beyond its parts.
+the identity, the six modulation slots read off a one-token block in closed
+form (shift, scale, gate for attention, then for the MLP), the final layer's
+(shift, scale) order, and the cross-attention branch adding its projected
+output without gate or modulation.  The composed forward is "parity unpinned" beyond its parts.
 """
 from __future__ import annotations
 

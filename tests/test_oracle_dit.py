@@ -195,3 +195,109 @@ def test_modulation_with_zero_scale_shift_is_layernorm():
     x = rng(6).standard_normal((4, 16))
     z = np.zeros(16)
     assert np.array_equal(dit.modulate(dit.layer_norm(x), z, z), dit.layer_norm(x))
+
+
+# ------------------------------------------------------------------ modulation slots, final layer, cross branch
+# One latent patch (4 x 2 x 2 with p = 2) is one token, so self-attention over
+# the row's own chunk with no cache sees a single key and returns its value
+# exactly; the block can then be read off in closed form.
+def _one_token_net(n_blocks=1, ctx_len=0):
+    cfg = get_config("tiny", n_blocks=n_blocks, ctx_len=ctx_len)
+    w = {k: np.asarray(v, np.float64) for k, v in gen.make_weights(cfg).items()}
+    return cfg, w
+
+
+def _set_modulation(w, slots):
+    """Make the shared modulation vector equal concat(slots) for every tau:
+    zero projection, bias = the slots, zero per-block table."""
+    w["mod_w"] = np.zeros_like(w["mod_w"])
+    w["mod_b"] = np.concatenate(slots)
+    w["blk_mod"] = np.zeros_like(w["blk_mod"])
+
+
+def _patch_embed(w, x):
+    # the single token of a 4 x 2 x 2 latent, vector order (py, px, c)
+    tok = np.array([[x[0, c, py, px] for py in range(2) for px in range(2) for c in range(4)]])
+    return tok @ w["pe_w"].T + w["pe_b"]
+
+
+def test_block_modulation_slots_are_shift_scale_gate():
+    """block_mod's split: slots 0..5 are (shift, scale, gate) for attention,
+    then for the MLP.  With V and the output projection the identity, one
+    token and the MLP gate zero, the block output is
+    x + g1 * (LN(x) * (1 + s1) + h1) exactly; any other assignment of the six
+    distinct random slot vectors changes it."""
+    cfg, w = _one_token_net()
+    d = cfg.d_model
+    r = rng(11)
+    h1, s1, g1, h2, s2 = (r.standard_normal(d) for _ in range(5))
+    _set_modulation(w, [h1, s1, g1, h2, s2, np.zeros(d)])
+    w["qkv_w"][0, 2 * d:] = np.eye(d)
+    w["qkv_b"][0] = 0.0
+    w["o_w"][0] = np.eye(d)
+    w["o_b"][0] = 0.0
+    x = r.standard_normal((1, 4, 2, 2))
+    _, _, hidden = dit.Denoiser(cfg, w).forward_row(x, 359, 0, collect=True)
+    x_pe = _patch_embed(w, x)
+    mu = x_pe.mean()
+    ln = (x_pe - mu) / math.sqrt(((x_pe - mu) ** 2).mean() + 1e-6)
+    expect = x_pe + g1 * (ln * (1 + s1) + h1)
+    assert np.allclose(hidden, expect, rtol=0, atol=1e-12)
+    # a swapped split (shift <-> scale) would give a different hidden state
+    assert not np.allclose(x_pe + g1 * (ln * (1 + h1) + s1), expect, atol=1e-3)
+
+
+def test_final_layer_split_is_shift_then_scale():
+    """The final layer's 2d vector is (shift, scale): with no blocks, the head
+    picking the first p*p*C features and zero bias, eps is
+    (LN(x) * (1 + s_f) + h_f)[:16] unpatchified."""
+    cfg, w = _one_token_net()
+    d = cfg.d_model
+    r = rng(12)
+    hf, sf = r.standard_normal(d), r.standard_normal(d)
+    w["fin_w"] = np.zeros_like(w["fin_w"])
+    w["fin_b"] = np.concatenate([hf, sf])
+    w["head_w"] = np.eye(16, d)
+    w["head_b"] = np.zeros(16)
+    # zero both gates so the block passes x through
+    m = np.zeros(6 * d)
+    _set_modulation(w, [m[:d]] * 6)
+    x = r.standard_normal((1, 4, 2, 2))
+    eps = dit.Denoiser(cfg, w).forward_row(x, 99, 0)
+    x_pe = _patch_embed(w, x)[0]
+    mu = x_pe.mean()
+    out = ((x_pe - mu) / math.sqrt(((x_pe - mu) ** 2).mean() + 1e-6) * (1 + sf) + hf)[:16]
+    for py in range(2):
+        for px in range(2):
+            for c in range(4):
+                assert abs(eps[0, c, py, px] - out[(py * 2 + px) * 4 + c]) < 1e-12
+
+
+def test_cross_branch_is_ungated_and_adds_its_output():
+    """Cross-attention adds its projected output to x with no gate and no
+    modulation.  With zero query / key / value weights and biases the
+    attention output is zero, so the block adds exactly co_b; with the value
+    projection the identity and zero keys every prompt token gets weight
+    1/77, so it adds mean(ctx) W_o^T + co_b.  Both gates are zero, so
+    self-attention and the MLP add nothing."""
+    cfg, w = _one_token_net(ctx_len=77)
+    d, H, hd = cfg.d_model, cfg.n_heads, cfg.head_dim
+    r = rng(13)
+    _set_modulation(w, [np.zeros(d)] * 6)
+    ctx = r.standard_normal((77, d))
+    x = r.standard_normal((1, 4, 2, 2))
+    x_pe = _patch_embed(w, x)
+    co_b = r.standard_normal(d)
+    for name in ("cq_w", "cq_b", "ckv_w", "ckv_b", "co_w"):
+        w[name] = np.zeros_like(w[name])
+    w["co_b"][0] = co_b
+    net = dit.Denoiser(cfg, w)
+    _, _, hidden = net.forward_row(x, 359, 0, ctx_kv=[net.cross_kv(ctx, 0)], collect=True)
+    assert np.allclose(hidden, x_pe + co_b, rtol=0, atol=1e-12)
+    # value projection = identity, zero keys (uniform weights), output = identity
+    w["ckv_w"][0, d:] = np.eye(d)
+    w["co_w"][0] = np.eye(d)
+    w["cq_w"][0] = r.standard_normal((d, d))
+    net = dit.Denoiser(cfg, w)
+    _, _, hidden = net.forward_row(x, 359, 0, ctx_kv=[net.cross_kv(ctx, 0)], collect=True)
+    assert np.allclose(hidden, x_pe + ctx.mean(0) + co_b, rtol=0, atol=1e-12)
