@@ -30,6 +30,74 @@ sd_status sd_k_gemm(int32_t dtype, const void* A, const void* W, const void* bia
 sd_status sd_k_gemm_resid(int32_t dtype, const void* A, const void* W, const void* bias, float* C, int32_t M,
                           int32_t N, int32_t K, void* stream);
 
+/* Epilogue modes of the denoiser's bf16 GEMMs: each fuses the step that
+ * follows a linear layer of a DiT block (StreamDiffusionV2 notes, 实现细节:
+ * the Wan-shaped video DiT; the block layout is the reading written in the
+ * oracle's denoiser).  C[m][n] = sum_k A[m][k] W[n][k] + bias[n], then
+ *   SD_EPI_STORE      out[m][n] = bf16(C)
+ *   SD_EPI_GELU       out[m][n] = bf16(GELU(C))            (FFN first layer)
+ *   SD_EPI_GATE_RESID resid[m][n] += gate[m/L][n] * C      (attention out / FFN out)
+ *                     with gate[r][n] = mod[r*six_d + gate_off + n] + blk[gate_off + n]
+ *   SD_EPI_RESID      resid[m][n] += C                     (cross-attention out)
+ *   SD_EPI_PATCH      resid[m][n] = C                      (patch embedding)
+ *   SD_EPI_QKV        N = 3*H*hd: q | k | v per token, RoPE on q and k when
+ *                     rope != 0, q to [rows][H][L][hd], k to
+ *                     [H][krows][kstride][hd], v transposed to
+ *                     [H][hd][krows][kstride] (row r = m / L, token t = m % L)
+ *   SD_EPI_HEAD       eps[r] (fp32 [T][C][Hl][Wl]) = unpatchify(C) of row r
+ *   SD_EPI_F32        out[m][n] = C in fp32 */
+enum { SD_EPI_STORE = 0, SD_EPI_GELU = 1, SD_EPI_GATE_RESID = 2, SD_EPI_RESID = 3, SD_EPI_PATCH = 4,
+       SD_EPI_QKV = 5, SD_EPI_HEAD = 6, SD_EPI_F32 = 8 };
+
+typedef struct {
+  int32_t mode;                /* SD_EPI_* */
+  const void* bias;            /* bf16 [N]; NULL = 0 (row-major modes only) */
+  void* out;                   /* STORE / GELU: bf16 [M][ldo]; F32: fp32 [M][ldo] */
+  int32_t ldo;
+  float* resid;                /* GATE_RESID / RESID / PATCH: fp32 [M][N] */
+  const float* mod;            /* GATE_RESID: fp32 [M/L][six_d] */
+  const void* blk;             /* GATE_RESID: bf16 [six_d] */
+  int32_t gate_off, six_d;
+  int32_t L;                   /* tokens per row; M must be a multiple of L for QKV and HEAD */
+  void* q;                     /* QKV destinations (bf16) */
+  void* k;
+  void* vt;
+  int32_t kstride, krows;      /* k / vt token capacity per (head, row) and rows (krows >= M/L) */
+  int32_t H, hd;               /* heads and head dim (QKV) */
+  int32_t rope;                /* QKV: rotate q and k by 3D RoPE */
+  int32_t Hp, Wp;              /* token grid of one latent frame (QKV with RoPE, HEAD) */
+  const void* rope_table;      /* device copy of the sd_k_rope_tables() table */
+  int32_t rope_positions;      /* temporal positions the table holds */
+  int32_t t0[SD_MAX_ROWS];     /* temporal RoPE base of each row */
+  float* eps;                  /* HEAD: fp32 [M/L][T][C][Hl][Wl] */
+  int32_t C, Hl, Wl, p, T;     /* HEAD: latent geometry and patch (Hl = Hp*p, Wl = Wp*p, L = T*Hp*Wp) */
+} sd_gemm_epi;
+
+/* One bf16 GEMM with the epilogue e->mode, on the kernels and launch
+ * configuration sd_stream_step() uses for the same (M, N, K).  A [M][K],
+ * W [N][K] bf16, K a multiple of 8.  Destinations must not alias operands. */
+sd_status sd_k_gemm_epi(const void* A, const void* W, int32_t M, int32_t N, int32_t K, const sd_gemm_epi* e,
+                        void* stream);
+
+/* Elements (float pairs) of the 3D RoPE table for head dim hd: the temporal
+ * section (positions x dt/2), then height (Hp x dh/2), then width (Wp x dw/2),
+ * with dh = dw = 2*floor(hd/6) and dt = hd - 2*dh (StreamDiffusionV2 summary,
+ * adaptive sink and RoPE refresh: positions restart below a threshold, so the
+ * temporal section has a fixed length). */
+size_t sd_k_rope_table_pairs(int32_t hd, int32_t positions, int32_t Hp, int32_t Wp);
+/* Fill host memory `out` (2 * sd_k_rope_table_pairs() floats) with
+ * (cos, sin) of pos * base^(-2j/width) for every section; the same table
+ * sd_stream_create() builds.  Host only, no HIP call. */
+sd_status sd_k_rope_tables(int32_t hd, int32_t positions, int32_t Hp, int32_t Wp, double base, float* out);
+
+/* LayerNorm over d (no affine, population variance, eps) of fp32 x [M][d],
+ * then x * (1 + scale) + shift with scale / shift = mod[r*six_d + off + c] +
+ * blk[off + c], r = m / L (mod NULL: no modulation; blk NULL: 0); out in
+ * dtype (bf16 or fp32) [M][d].  d a multiple of 4, at most 5120.  The
+ * adaLN-modulated normalisation in front of a block's attention and MLP. */
+sd_status sd_k_ln_mod(int32_t dtype, const float* x, void* out, int32_t M, int32_t d, int32_t L, const float* mod,
+                      const void* blk, int32_t shift_off, int32_t scale_off, int32_t six_d, void* stream);
+
 /* One causal 3x3x3 convolution of the Stream-VAE (StreamDiffusionV2 summary,
  * Stream-VAE: features cached inside every 3D convolution), bf16 channels-last:
  * x [T][H][W][Cin], cache [2][H][W][Cin] (the two input frames before the

@@ -85,13 +85,15 @@ class StepInfo:
 
 class OracleStream:
     def __init__(self, cfg, weights, ctx_pos=None, ctx_neg=None, dtype=np.float64,
-                 identity_denoiser=False, freeze_cache=False, sink_entries: int = 1):
+                 identity_denoiser=False, freeze_cache=False, sink_entries: Optional[int] = None):
         self.cfg = cfg
         self.dtype = dtype
         self.net = Denoiser(cfg, weights, dtype) if weights is not None else None
         self.a, self.b = schedule.sched_coeffs(cfg)
         self.identity = identity_denoiser
         self.freeze = freeze_cache
+        if sink_entries is None:
+            sink_entries = getattr(cfg, "sink_entries", 1)
         self.M = sink_entries
         if cfg.sink_tokens % sink_entries:
             raise ValueError("sink tokens must split evenly into entries")

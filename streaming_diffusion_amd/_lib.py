@@ -87,6 +87,20 @@ class sd_kv_segment(C.Structure):
                 ("count", C.c_int32), ("wrap", C.c_int32)]
 
 
+SD_EPI_STORE, SD_EPI_GELU, SD_EPI_GATE_RESID, SD_EPI_RESID, SD_EPI_PATCH, SD_EPI_QKV, SD_EPI_HEAD = range(7)
+SD_EPI_F32 = 8
+
+
+class sd_gemm_epi(C.Structure):
+    _fields_ = [("mode", C.c_int32), ("bias", C.c_void_p), ("out", C.c_void_p), ("ldo", C.c_int32),
+                ("resid", C.c_void_p), ("mod", C.c_void_p), ("blk", C.c_void_p), ("gate_off", C.c_int32),
+                ("six_d", C.c_int32), ("L", C.c_int32), ("q", C.c_void_p), ("k", C.c_void_p), ("vt", C.c_void_p),
+                ("kstride", C.c_int32), ("krows", C.c_int32), ("H", C.c_int32), ("hd", C.c_int32),
+                ("rope", C.c_int32), ("Hp", C.c_int32), ("Wp", C.c_int32), ("rope_table", C.c_void_p),
+                ("rope_positions", C.c_int32), ("t0", C.c_int32 * SD_MAX_ROWS), ("eps", C.c_void_p),
+                ("C", C.c_int32), ("Hl", C.c_int32), ("Wl", C.c_int32), ("p", C.c_int32), ("T", C.c_int32)]
+
+
 SD_VAE_ABI_VERSION = 1
 SD_VAE_LAYERS = 10
 VAE_LAYER_NAMES = ["e0", "e1", "e2", "e3", "e_out", "d0", "d1", "d2", "d3", "d_out"]
@@ -125,6 +139,12 @@ SIGNATURES = {
                             C.c_int32, C.c_void_p]),
     "sd_k_gemm_resid": (C.c_int, [C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
                                   C.c_int32, C.c_void_p]),
+    "sd_k_gemm_epi": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.POINTER(sd_gemm_epi),
+                                C.c_void_p]),
+    "sd_k_rope_table_pairs": (C.c_size_t, [C.c_int32, C.c_int32, C.c_int32, C.c_int32]),
+    "sd_k_rope_tables": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_double, C.c_void_p]),
+    "sd_k_ln_mod": (C.c_int, [C.c_int32, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
+                              C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p]),
     "sd_k_attention": (C.c_int, [C.c_int32, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int32, C.c_int32,
                                  C.c_int32, C.c_int32, C.c_int32, C.POINTER(sd_kv_segment), C.c_int32, C.c_void_p,
                                  C.c_size_t, C.c_void_p]),

@@ -199,6 +199,17 @@ __global__ __launch_bounds__(256) void ln_mod_kernel(const float* __restrict__ x
   }
 }
 
+void rope_table_fill(float2* out, int npos, int width, double base) {
+  const int np = width / 2;
+  for (int p = 0; p < npos; ++p) {
+    if (np == 0) out[p] = float2{1.f, 0.f};
+    for (int j = 0; j < np; ++j) {
+      const double th = (double)p * std::pow(base, -2.0 * j / (double)width);
+      out[(size_t)p * np + j] = float2{(float)std::cos(th), (float)std::sin(th)};
+    }
+  }
+}
+
 hipError_t ln_mod(hipStream_t s, bool bf, const float* x, void* out, int M, int d, int L, const float* mod,
                   const void* blk, int shift_off, int scale_off, int six_d, float eps) {
   if (M == 0) return hipSuccess;
@@ -561,29 +572,31 @@ hipError_t motion_sums(hipStream_t s, const float* cur, const float* prev_last, 
 // mean of the last block's output; cosine against each sink embedding; the
 // least similar entry is refreshed when its cosine is below tau.
 #define SINK_PARTS 64
-__global__ __launch_bounds__(256) void sink_partial_kernel(const float* __restrict__ x, float* __restrict__ part,
+// The token mean, the embeddings and the cosines are kept in fp64, and the
+// decision compares against tau in fp64, as the rule is stated.
+__global__ __launch_bounds__(256) void sink_partial_kernel(const float* __restrict__ x, double* __restrict__ part,
                                                            int L, int d) {
   const int g = blockIdx.y;
   const int c = blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= d) return;
   const int per = (L + SINK_PARTS - 1) / SINK_PARTS;
   const int t0 = g * per, t1 = min(L, t0 + per);
-  float s = 0.f;
-  for (int t = t0; t < t1; ++t) s += x[(int64_t)t * d + c];
+  double s = 0.0;
+  for (int t = t0; t < t1; ++t) s += (double)x[(int64_t)t * d + c];
   part[(int64_t)g * d + c] = s;
 }
 
-__global__ __launch_bounds__(1024) void sink_decide_kernel(const float* __restrict__ part, int L, int d,
-                                                           float* __restrict__ emb, int M, int capture_entry,
-                                                           float tau, int* __restrict__ flag,
-                                                           float* __restrict__ sim_out) {
-  extern __shared__ float h[];
+__global__ __launch_bounds__(1024) void sink_decide_kernel(const double* __restrict__ part, int L, int d,
+                                                           double* __restrict__ emb, int M, int capture_entry,
+                                                           double tau, int* __restrict__ flag,
+                                                           double* __restrict__ sim_out) {
+  extern __shared__ double h[];
   __shared__ double red[3][16];
   __shared__ double sims[SD_MAX_SINK];
   for (int c = threadIdx.x; c < d; c += blockDim.x) {
-    float s = 0.f;
+    double s = 0.0;
     for (int g = 0; g < SINK_PARTS; ++g) s += part[(int64_t)g * d + c];
-    h[c] = s / (float)L;
+    h[c] = s / (double)L;
   }
   __syncthreads();
   if (capture_entry >= 0) {
@@ -592,7 +605,7 @@ __global__ __launch_bounds__(1024) void sink_decide_kernel(const float* __restri
       flag[0] = 0;
       flag[1] = capture_entry;
       flag[2] = 0;
-      sim_out[0] = 1.0f;
+      sim_out[0] = 1.0;
     }
     return;
   }
@@ -631,24 +644,24 @@ __global__ __launch_bounds__(1024) void sink_decide_kernel(const float* __restri
     for (int j = 1; j < M; ++j)
       if (sims[j] < sims[js]) js = j;
     jstar = js;
-    const int refresh = sims[js] < (double)tau ? 1 : 0;
+    const int refresh = sims[js] < tau ? 1 : 0;
     flag[0] = refresh;
     flag[1] = js;
     flag[2] = 1;
-    sim_out[0] = (float)sims[js];
+    sim_out[0] = sims[js];
   }
   __syncthreads();
-  if (sims[jstar] < (double)tau)
+  if (sims[jstar] < tau)
     for (int c = threadIdx.x; c < d; c += blockDim.x) emb[(int64_t)jstar * d + c] = h[c];
 }
 
-hipError_t sink_score(hipStream_t s, const float* x, float* partial, int L, int d, float* emb, int M,
-                      int capture_entry, float tau, int* flag, float* sim) {
+hipError_t sink_score(hipStream_t s, const float* x, double* partial, int L, int d, double* emb, int M,
+                      int capture_entry, double tau, int* flag, double* sim) {
   dim3 g1((d + 255) / 256, SINK_PARTS);
   sink_partial_kernel<<<g1, 256, 0, s>>>(x, partial, L, d);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  sink_decide_kernel<<<1, 1024, d * sizeof(float), s>>>(partial, L, d, emb, M, capture_entry, tau, flag, sim);
+  sink_decide_kernel<<<1, 1024, d * sizeof(double), s>>>(partial, L, d, emb, M, capture_entry, tau, flag, sim);
   return hipGetLastError();
 }
 

@@ -35,6 +35,10 @@ hipError_t kv_append(hipStream_t s, bool bf, const void* kown, const void* vtown
 hipError_t sink_copy(hipStream_t s, bool bf, const int* flag, const void* ringK, const void* ringVT, void* sinkK,
                      void* sinkVT, int nb, int H, int hd, int W, int S8, int ptr_old, int Se);
 hipError_t fill_zero(hipStream_t s, void* p, size_t bytes);
+// Host: one section of the 3D RoPE table, (cos, sin) of pos * base^(-2j/width)
+// for pos < npos, j < width/2, written as npos * max(1, width/2) pairs
+// (width 0: a single identity pair per position).
+void rope_table_fill(float2* out, int npos, int width, double base);
 // cross-attention with folded prompt projections (k_attn.hip): the folded
 // score / output matrices of one block and context, and the grouped softmax
 hipError_t cross_fold(hipStream_t s, const bf16* K, const bf16* VT, const bf16* Wq, const bf16* bq, const bf16* Wo,
@@ -51,8 +55,8 @@ hipError_t ssf_sums(hipStream_t s, int kind, const void* a, const void* b, int64
 hipError_t motion_sums(hipStream_t s, const float* cur, const float* prev_last, int T, int64_t n, long long* out);
 // Chunk embedding (token mean of x [L][d]) and cosine decision against the
 // sink embeddings.  capture_entry >= 0 stores h as that entry instead.
-hipError_t sink_score(hipStream_t s, const float* x, float* partial, int L, int d, float* emb, int M,
-                      int capture_entry, float tau, int* flag, float* sim);
+hipError_t sink_score(hipStream_t s, const float* x, double* partial, int L, int d, double* emb, int M,
+                      int capture_entry, double tau, int* flag, double* sim);
 
 // ---------------------------------------------------------------- GEMM
 // C = A[M][K] * W[N][K]^T with epilogue E; element type by bf (bf16 on MFMA,

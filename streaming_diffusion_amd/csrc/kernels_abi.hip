@@ -34,6 +34,135 @@ sd_status sd_k_gemm_resid(int32_t dtype, const void* A, const void* W, const voi
   return gemm_call(dtype, A, W, bias, C, M, N, K, stream, EPI_RESID);
 }
 
+static void rope_split(int hd, int* dt, int* dh, int* dw) {
+  *dh = 2 * (hd / 6);
+  *dw = *dh;
+  *dt = hd - 2 * *dh;
+}
+
+static size_t pairs_of(int npos, int width) { return (size_t)npos * (size_t)(width / 2 > 1 ? width / 2 : 1); }
+
+size_t sd_k_rope_table_pairs(int32_t hd, int32_t positions, int32_t Hp, int32_t Wp) {
+  if (hd < 2 || positions < 1 || Hp < 1 || Wp < 1) return 0;
+  int dt, dh, dw;
+  rope_split(hd, &dt, &dh, &dw);
+  return pairs_of(positions, dt) + pairs_of(Hp, dh) + pairs_of(Wp, dw);
+}
+
+sd_status sd_k_rope_tables(int32_t hd, int32_t positions, int32_t Hp, int32_t Wp, double base, float* out) {
+  if (!out || hd < 2 || (hd & 1) || positions < 1 || Hp < 1 || Wp < 1 || !(base > 1.0)) return SD_ERR_ARG;
+  int dt, dh, dw;
+  rope_split(hd, &dt, &dh, &dw);
+  float2* o = (float2*)out;
+  sdk::rope_table_fill(o, positions, dt, base);
+  o += pairs_of(positions, dt);
+  sdk::rope_table_fill(o, Hp, dh, base);
+  o += pairs_of(Hp, dh);
+  sdk::rope_table_fill(o, Wp, dw, base);
+  return SD_OK;
+}
+
+sd_status sd_k_gemm_epi(const void* A, const void* W, int32_t M, int32_t N, int32_t K, const sd_gemm_epi* e,
+                        void* stream) {
+  if (!A || !W || !e || M < 0 || N < 1 || K < 8) return SD_ERR_ARG;
+  if (K % 8) return SD_ERR_SHAPE;
+  Epi E;
+  std::memset(&E, 0, sizeof(E));
+  E.mode = e->mode;
+  E.bias = e->bias;
+  E.L = e->L > 0 ? e->L : 1;
+  E.ldo = N;
+  switch (e->mode) {
+    case SD_EPI_STORE:
+    case SD_EPI_GELU:
+    case SD_EPI_F32:
+      if (!e->out || e->ldo < N) return SD_ERR_ARG;
+      E.out = e->out;
+      E.ldo = e->ldo;
+      break;
+    case SD_EPI_GATE_RESID:
+      if (!e->resid || !e->mod || !e->blk || e->L < 1) return SD_ERR_ARG;
+      if (e->gate_off < 0 || e->gate_off % 8 || e->six_d % 8 || e->gate_off + N > e->six_d) return SD_ERR_SHAPE;
+      E.resid = e->resid;
+      E.mod = e->mod;
+      E.blk = e->blk;
+      E.gate_off = e->gate_off;
+      E.six_d = e->six_d;
+      break;
+    case SD_EPI_RESID:
+    case SD_EPI_PATCH:
+      if (!e->resid) return SD_ERR_ARG;
+      E.resid = e->resid;
+      break;
+    case SD_EPI_QKV: {
+      if (!e->q || !e->k || !e->vt || !e->bias || e->L < 1 || e->H < 1 || e->hd < 8) return SD_ERR_ARG;
+      const int rows = M / e->L;
+      if (e->hd % 8 || N != 3 * e->H * e->hd || M % e->L || e->L % 8 || rows > SD_MAX_ROWS) return SD_ERR_SHAPE;
+      if (e->krows < rows || e->kstride < e->L || e->kstride % 8) return SD_ERR_SHAPE;
+      E.q = e->q;
+      E.k = e->k;
+      E.vt = e->vt;
+      E.kstride = e->kstride;
+      E.krows = e->krows;
+      E.H = e->H;
+      E.hd = e->hd;
+      E.d = e->H * e->hd;
+      E.rope = e->rope ? 1 : 0;
+      if (E.rope) {
+        if (!e->rope_table || e->Hp < 1 || e->Wp < 1 || e->rope_positions < 1) return SD_ERR_ARG;
+        const int hw = e->Hp * e->Wp;
+        if (e->L % hw) return SD_ERR_SHAPE;
+        for (int r = 0; r < rows; ++r)
+          if (e->t0[r] < 0 || e->t0[r] + e->L / hw > e->rope_positions) return SD_ERR_SHAPE;
+        int dt, dh, dw;
+        rope_split(e->hd, &dt, &dh, &dw);
+        E.Hp = e->Hp;
+        E.Wp = e->Wp;
+        E.dt = dt;
+        E.dh = dh;
+        E.rope_t = (const float2*)e->rope_table;
+        E.rope_h = E.rope_t + pairs_of(e->rope_positions, dt);
+        E.rope_w = E.rope_h + pairs_of(e->Hp, dh);
+        for (int r = 0; r < rows; ++r) E.t0[r] = e->t0[r];
+      }
+      break;
+    }
+    case SD_EPI_HEAD: {
+      if (!e->eps || !e->bias || e->L < 1 || e->C < 1 || e->p < 1 || e->T < 1 || e->Hp < 1 || e->Wp < 1)
+        return SD_ERR_ARG;
+      if (N != e->p * e->p * e->C || e->Hl != e->Hp * e->p || e->Wl != e->Wp * e->p ||
+          e->L != e->T * e->Hp * e->Wp || M % e->L)
+        return SD_ERR_SHAPE;
+      E.eps = e->eps;
+      E.C = e->C;
+      E.Hl = e->Hl;
+      E.Wl = e->Wl;
+      E.p = e->p;
+      E.T = e->T;
+      E.Hp = e->Hp;
+      E.Wp = e->Wp;
+      break;
+    }
+    default:
+      return SD_ERR_ARG;
+  }
+  return sdk::gemm_mfma((hipStream_t)stream, A, W, M, N, K, E) == hipSuccess ? SD_OK : SD_ERR_HIP;
+}
+
+sd_status sd_k_ln_mod(int32_t dtype, const float* x, void* out, int32_t M, int32_t d, int32_t L, const float* mod,
+                      const void* blk, int32_t shift_off, int32_t scale_off, int32_t six_d, void* stream) {
+  if (dtype != SD_DTYPE_F32 && dtype != SD_DTYPE_BF16) return SD_ERR_ARG;
+  if (!x || !out || M < 0 || d < 4 || L < 1) return SD_ERR_ARG;
+  if (d % 4 || d > 5120) return SD_ERR_SHAPE;
+  if (mod && (shift_off < 0 || scale_off < 0 || shift_off % 4 || scale_off % 4 || six_d % 4 ||
+              shift_off + d > six_d || scale_off + d > six_d))
+    return SD_ERR_SHAPE;
+  return sdk::ln_mod((hipStream_t)stream, dtype == SD_DTYPE_BF16, x, out, M, d, L, mod, mod ? blk : nullptr,
+                     shift_off, scale_off, mod ? six_d : 4, 1e-6f) == hipSuccess
+             ? SD_OK
+             : SD_ERR_HIP;
+}
+
 static size_t part_o_bytes(int32_t R, int32_t H, int32_t L, int32_t hd, int32_t nsplit) {
   return (((size_t)nsplit * R * L * H * hd * 2) + 255) & ~(size_t)255;
 }

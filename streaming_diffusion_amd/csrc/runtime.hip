@@ -65,7 +65,7 @@ struct sd_stream {
   bool fold = false;
   void *fold_q = nullptr, *fold_o = nullptr;
   float* fold_c = nullptr;
-  float *sink_emb = nullptr, *sink_part = nullptr, *sink_sim = nullptr;
+  double *sink_emb = nullptr, *sink_part = nullptr, *sink_sim = nullptr;
   int* sink_flag = nullptr;
   float2 *rope_t = nullptr, *rope_h = nullptr, *rope_w = nullptr;
   // split-KV partials of the self-attention
@@ -207,10 +207,10 @@ size_t carve(sd_stream* s, char* base) {
       s->fold_c = cv.take<float>((size_t)s->nb * nctx * ncol * 4);
     }
   }
-  s->sink_emb = cv.take<float>((size_t)std::max(1, s->Ment) * s->d * 4);
-  s->sink_part = cv.take<float>((size_t)64 * s->d * 4);
+  s->sink_emb = cv.take<double>((size_t)std::max(1, s->Ment) * s->d * 8);
+  s->sink_part = cv.take<double>((size_t)64 * s->d * 8);
   s->sink_flag = cv.take<int>(16);
-  s->sink_sim = cv.take<float>(16);
+  s->sink_sim = cv.take<double>(16);
   s->rope_t = cv.take<float2>((size_t)s->rope_pos * std::max(1, s->dt / 2) * sizeof(float2));
   s->rope_h = cv.take<float2>((size_t)s->Hp * std::max(1, s->dh / 2) * sizeof(float2));
   s->rope_w = cv.take<float2>((size_t)s->Wp * std::max(1, s->dw / 2) * sizeof(float2));
@@ -251,13 +251,8 @@ char* Pm(void* base, int64_t elem_off, size_t es) { return (char*)base + elem_of
 void rope_tables(const sd_stream* s, std::vector<float2>& t, std::vector<float2>& h, std::vector<float2>& w) {
   const double base = s->cfg.rope_base;
   auto fill = [&](std::vector<float2>& out, int npos, int width) {
-    const int np = width / 2;
-    out.assign((size_t)npos * std::max(1, np), float2{1.f, 0.f});
-    for (int p = 0; p < npos; ++p)
-      for (int j = 0; j < np; ++j) {
-        const double th = (double)p * std::pow(base, -2.0 * j / (double)width);
-        out[(size_t)p * np + j] = float2{(float)std::cos(th), (float)std::sin(th)};
-      }
+    out.assign((size_t)npos * std::max(1, width / 2), float2{1.f, 0.f});
+    sdk::rope_table_fill(out.data(), npos, width, base);
   };
   fill(t, s->rope_pos, s->dt);
   fill(h, s->Hp, s->dh);
@@ -393,7 +388,7 @@ sd_status sd_stream_create(const sd_stream_config* cfg, const sd_weights* w, voi
   if (e == hipSuccess) e = sdk::fill_zero(s->st, s->ringVT, cache_bytes[0]);
   if (e == hipSuccess) e = sdk::fill_zero(s->st, s->sinkK, cache_bytes[1]);
   if (e == hipSuccess) e = sdk::fill_zero(s->st, s->sinkVT, cache_bytes[1]);
-  if (e == hipSuccess) e = sdk::fill_zero(s->st, s->sink_emb, (size_t)std::max(1, s->Ment) * s->d * 4);
+  if (e == hipSuccess) e = sdk::fill_zero(s->st, s->sink_emb, (size_t)std::max(1, s->Ment) * s->d * 8);
   if (e == hipSuccess) e = sdk::fill_zero(s->st, s->sink_flag, 16);
   if (e == hipSuccess) e = hipMemcpyAsync(s->rope_t, rt.data(), rt.size() * sizeof(float2), hipMemcpyHostToDevice, s->st);
   if (e == hipSuccess) e = hipMemcpyAsync(s->rope_h, rh.data(), rh.size() * sizeof(float2), hipMemcpyHostToDevice, s->st);
@@ -802,7 +797,7 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, int R_pos, int nn
   for (int k = 0; k < nexit && s->S > 0; ++k) {
     PROF(SD_PROF_CONTROLS, 0.0, 4.0 * L * d,
          sdk::sink_score(st, s->resid + (int64_t)exit_rows[k] * L * d, s->sink_part, L, d, s->sink_emb, s->Ment,
-                         cap_entry[k], (float)c.sink_tau, s->sink_flag, s->sink_sim));
+                         cap_entry[k], c.sink_tau, s->sink_flag, s->sink_sim));
     if (cap_entry[k] < 0) {
       const bool staged = s->Cc > 0;
       PROF(SD_PROF_KV, 0.0, 4.0 * s->nb * s->Se * d * es,
@@ -1006,14 +1001,14 @@ sd_status sd_stream_kv_reset(sd_stream* s) {
 sd_status sd_stream_sink_info(sd_stream* s, sd_sink_info* info) {
   if (!s || !info) return SD_ERR_ARG;
   int fl[4] = {};
-  float sim = 0.f;
+  double sim = 0.0;
   HIP_TRY(hipMemcpyAsync(fl, s->sink_flag, sizeof(int) * 3, hipMemcpyDeviceToHost, s->st));
-  HIP_TRY(hipMemcpyAsync(&sim, s->sink_sim, sizeof(float), hipMemcpyDeviceToHost, s->st));
+  HIP_TRY(hipMemcpyAsync(&sim, s->sink_sim, sizeof(double), hipMemcpyDeviceToHost, s->st));
   HIP_TRY(hipStreamSynchronize(s->st));
   info->refreshed = fl[0];
   info->entry = fl[1];
   info->evaluated = fl[2];
-  info->sim = sim;
+  info->sim = (float)sim;
   return SD_OK;
 }
 

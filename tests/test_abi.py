@@ -230,3 +230,67 @@ def test_vae_and_conv_argument_errors(lib):
     assert lib.sd_k_conv3d(8, None, 8, None, 8, None, 1, 4, 4, 8, 6, None) == L.SD_ERR_SHAPE        # Cout % 4
     assert lib.sd_k_conv3d(8, None, 8, None, None, 8, 1, 4, 4, 8, 17, None) == L.SD_ERR_SHAPE       # narrow > 16
     assert lib.sd_k_conv3d(None, None, 8, None, 8, None, 1, 4, 4, 8, 8, None) == L.SD_ERR_ARG
+
+
+# ------------------------------------------------------------------ GEMM-epilogue and LN test entries
+def test_gemm_epi_struct_matches_a_c_compiler(tmp_path):
+    probe = tmp_path / "probe_epi.c"
+    fields = [f for f, _ in L.sd_gemm_epi._fields_]
+    lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{ROOT}/include/sd_kernels.h"', "int main(void){",
+             'printf("%zu\\n", sizeof(sd_gemm_epi));']
+    lines += [f'printf("%zu\\n", offsetof(sd_gemm_epi, {f}));' for f in fields]
+    lines.append("return 0;}")
+    probe.write_text("\n".join(lines))
+    exe = tmp_path / "probe_epi"
+    assert os.system(f"gcc -o {exe} {probe}") == 0
+    out = [int(v) for v in os.popen(str(exe)).read().split()]
+    assert out[0] == C.sizeof(L.sd_gemm_epi)
+    assert out[1:] == [getattr(L.sd_gemm_epi, f).offset for f in fields]
+
+
+def test_gemm_epi_and_ln_mod_reject_bad_arguments_before_any_device_call(lib):
+    e = L.sd_gemm_epi(mode=L.SD_EPI_STORE, out=None, ldo=64)
+    assert lib.sd_k_gemm_epi(8, 8, 64, 64, 64, C.byref(e), None) == L.SD_ERR_ARG        # no output
+    e = L.sd_gemm_epi(mode=L.SD_EPI_STORE, out=8, ldo=32)
+    assert lib.sd_k_gemm_epi(8, 8, 64, 64, 64, C.byref(e), None) == L.SD_ERR_ARG        # ldo < N
+    assert lib.sd_k_gemm_epi(8, 8, 64, 64, 60, C.byref(e), None) == L.SD_ERR_SHAPE      # K % 8
+    e = L.sd_gemm_epi(mode=99)
+    assert lib.sd_k_gemm_epi(8, 8, 64, 64, 64, C.byref(e), None) == L.SD_ERR_ARG
+    e = L.sd_gemm_epi(mode=L.SD_EPI_GATE_RESID, resid=8, mod=8, blk=8, L=16, gate_off=4, six_d=384)
+    assert lib.sd_k_gemm_epi(8, 8, 64, 64, 64, C.byref(e), None) == L.SD_ERR_SHAPE      # unaligned gate offset
+    e.gate_off = 336
+    assert lib.sd_k_gemm_epi(8, 8, 64, 64, 64, C.byref(e), None) == L.SD_ERR_SHAPE      # gate beyond 6d
+    # q | k | v widths must match the heads; rows must fit the k / v^T destination; RoPE positions in the table
+    e = L.sd_gemm_epi(mode=L.SD_EPI_QKV, bias=8, q=8, k=8, vt=8, L=64, H=2, hd=32, kstride=64, krows=2)
+    assert lib.sd_k_gemm_epi(8, 8, 128, 190, 64, C.byref(e), None) == L.SD_ERR_SHAPE
+    assert lib.sd_k_gemm_epi(8, 8, 192, 192, 64, C.byref(e), None) == L.SD_ERR_SHAPE    # 3 rows > krows
+    e.rope, e.rope_table, e.Hp, e.Wp, e.rope_positions = 1, 8, 8, 8, 4
+    e.t0[0], e.t0[1] = 0, 4
+    assert lib.sd_k_gemm_epi(8, 8, 128, 192, 64, C.byref(e), None) == L.SD_ERR_SHAPE    # position 4 not in table
+    e = L.sd_gemm_epi(mode=L.SD_EPI_HEAD, bias=8, eps=8, L=64, C=4, p=2, T=1, Hp=8, Wp=8, Hl=16, Wl=15)
+    assert lib.sd_k_gemm_epi(8, 8, 64, 16, 128, C.byref(e), None) == L.SD_ERR_SHAPE
+    assert lib.sd_k_ln_mod(1, 8, 8, 4, 5124, 1, None, None, 0, 0, 0, None) == L.SD_ERR_SHAPE
+    assert lib.sd_k_ln_mod(1, 8, 8, 4, 128, 1, 8, 8, 0, 700, 768, None) == L.SD_ERR_SHAPE
+    assert lib.sd_k_ln_mod(3, 8, 8, 4, 128, 1, None, None, 0, 0, 0, None) == L.SD_ERR_ARG
+
+
+def test_rope_tables_are_cos_sin_of_the_section_angles(lib):
+    """Host table of the RoPE epilogue: (cos, sin) of pos * base^(-2j/width)
+    per section (t: hd - 2*dh, h = w: 2*floor(hd/6)), each value the fp64
+    angle's cosine / sine rounded to fp32 (within one fp32 ulp of numpy's)."""
+    hd, npos, Hp, Wp, base = 128, 7, 5, 6, 10000.0
+    n = lib.sd_k_rope_table_pairs(hd, npos, Hp, Wp)
+    dh = 2 * (hd // 6)
+    dt = hd - 2 * dh
+    assert n == npos * dt // 2 + Hp * dh // 2 + Wp * dh // 2
+    buf = np.zeros(2 * n, np.float32)
+    assert lib.sd_k_rope_tables(hd, npos, Hp, Wp, base, buf.ctypes.data) == L.SD_OK
+    got = buf.reshape(-1, 2)
+    ref = []
+    for npos_a, width in ((npos, dt), (Hp, dh), (Wp, dh)):
+        for p in range(npos_a):
+            for j in range(width // 2):
+                th = p * base ** (-2.0 * j / width)
+                ref.append((np.cos(th), np.sin(th)))
+    ref = np.array(ref, np.float32)
+    assert np.all(np.abs(got - ref) <= np.spacing(np.abs(ref)))

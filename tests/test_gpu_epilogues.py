@@ -1,0 +1,213 @@
+"""GPU parity of the fused GEMM epilogues at the shapes and launch
+configurations the 1.3B-shaped video step runs (two rows of 3120 tokens,
+d 1536, 12 heads of 128, FFN 8960, 64-wide patches), through sd_k_gemm_epi
+and sd_k_ln_mod.
+
+Operands are k/16 with |k| <= 8, exact in bf16, so every accumulator is exact
+in fp32.  Epilogues that only add, scatter or multiply exact values are then
+compared bit for bit (with the oracle's own layouts: patchify / unpatchify,
+per-head q / k, transposed v); RoPE and GELU are compared with the oracle's
+fp64 rope_apply / gelu on the exact accumulators, within the bf16 rounding of
+the stored result plus a bound on the fp32 arithmetic written in each test."""
+import ctypes as C
+
+import numpy as np
+import pytest
+import torch
+
+import streaming_diffusion_amd._lib as sdlib
+from oracle import dit
+
+from gpu_helpers import bf16_round, call, device, stream_ptr, to_dev
+
+pytestmark = pytest.mark.gpu
+
+# the 1.3B-shaped video DiT, two rows (n = 2) of one T = 2 chunk
+R, T, Hp, Wp = 2, 2, 30, 52
+L = T * Hp * Wp                     # 3120 tokens
+D, H, HD, F = 1536, 12, 128, 8960
+PC, P, CH = 64, 2, 16               # patch vector 2*2*16
+ROPE_POS = 1025                     # temporal positions of the table (reset threshold 1024)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    device()
+    return sdlib.load()
+
+
+def int_operands(M, N, K, seed):
+    rng = np.random.default_rng(seed)
+    ai = rng.integers(-8, 9, size=(M, K))
+    wi = rng.integers(-8, 9, size=(N, K))
+    bi = rng.integers(-8, 9, size=N)
+    acc = (ai.astype(np.float64) @ wi.T.astype(np.float64)) / 256.0 + bi / 16.0     # exact
+    A, W, b = to_dev(ai / 16.0, torch.bfloat16), to_dev(wi / 16.0, torch.bfloat16), to_dev(bi / 16.0, torch.bfloat16)
+    return A, W, b, acc
+
+
+def run(lib, A, W, M, N, K, e):
+    call(lib.sd_k_gemm_epi(A.data_ptr(), W.data_ptr(), M, N, K, C.byref(e), stream_ptr()))
+    torch.cuda.synchronize()
+
+
+def rope_table(lib, hd, positions, hp, wp):
+    n = lib.sd_k_rope_table_pairs(hd, positions, hp, wp)
+    buf = np.zeros(2 * n, np.float32)
+    call(lib.sd_k_rope_tables(hd, positions, hp, wp, 10000.0, buf.ctypes.data))
+    return to_dev(buf, torch.float32)
+
+
+# ------------------------------------------------------------------ q / k / v scatter with RoPE
+def qkv_case(lib, rows, t, hp, wp, d, h, rope, t0s, kextra=0, seed=1):
+    hd = d // h
+    Lr = t * hp * wp
+    M, N, K = rows * Lr, 3 * d, d
+    print(f"qkv M={M} N={N} K={K} rope={rope} t0={t0s}", flush=True)
+    A, W, b, acc = int_operands(M, N, K, seed)
+    kstride, krows = Lr + kextra, rows + (1 if kextra else 0)
+    q = torch.zeros((rows, h, Lr, hd), dtype=torch.bfloat16, device=device())
+    k = torch.zeros((h, krows, kstride, hd), dtype=torch.bfloat16, device=device())
+    vt = torch.zeros((h, hd, krows, kstride), dtype=torch.bfloat16, device=device())
+    e = sdlib.sd_gemm_epi(mode=sdlib.SD_EPI_QKV, bias=b.data_ptr(), L=Lr, q=q.data_ptr(), k=k.data_ptr(),
+                          vt=vt.data_ptr(), kstride=kstride, krows=krows, H=h, hd=hd, rope=int(rope), Hp=hp, Wp=wp)
+    tab = None
+    if rope:
+        tab = rope_table(lib, hd, ROPE_POS, hp, wp)
+        e.rope_table, e.rope_positions = tab.data_ptr(), ROPE_POS
+        for r, v in enumerate(t0s):
+            e.t0[r] = v
+    run(lib, A, W, M, N, K, e)
+    qg, kg, vg = q.float().cpu().numpy(), k.float().cpu().numpy(), vt.float().cpu().numpy()
+    for r in range(rows):
+        c = acc[r * Lr:(r + 1) * Lr].reshape(Lr, 3, h, hd)
+        v_ref = c[:, 2]
+        # v is stored unrotated: bit for bit the bf16 rounding of the exact value
+        assert np.array_equal(vg[:, :, r, :Lr].transpose(2, 0, 1), bf16_round(v_ref)), f"v row {r}"
+        for sec, got in ((0, qg[r].transpose(1, 0, 2)), (1, kg[:, r, :Lr].transpose(1, 0, 2))):
+            x = c[:, sec]
+            if not rope:
+                assert np.array_equal(got, bf16_round(x)), f"section {sec} row {r}"
+                continue
+            ref = dit.rope_apply(x, dit.token_positions(t, hp, wp, t0s[r]))
+            # pair magnitude |x0| + |x1| bounds the fp32 table and arithmetic error
+            pair = np.abs(x[..., 0::2]) + np.abs(x[..., 1::2])
+            pair = np.repeat(pair, 2, axis=-1)
+            err = np.abs(got - ref) - 2.0 ** -8 * np.abs(ref) - 1e-6 * pair
+            assert err.max() <= 0.0, f"section {sec} row {r}: excess {err.max():.3e}"
+    if kextra:   # capacity beyond the rows / tokens written stays untouched
+        assert not k[:, rows:].any() and not k[:, :, Lr:].any() and not vt[:, :, rows:].any()
+
+
+def test_qkv_scatter_video13b_exact(lib):
+    qkv_case(lib, R, T, Hp, Wp, D, H, rope=False, t0s=[0, 0])
+
+
+def test_qkv_rope_video13b(lib):
+    # second row's chunk ends on the last temporal position before the reset
+    qkv_case(lib, R, T, Hp, Wp, D, H, rope=True, t0s=[6, 1023])
+
+
+def test_qkv_rope_small_head_dims_and_strided_destination(lib):
+    # hd 64 and 32 (RoPE sections 24/20/20 and 12/10/10), ragged tiles, a k / v^T capacity beyond the rows
+    qkv_case(lib, 3, 1, 8, 10, 256, 4, rope=True, t0s=[0, 5, 17], kextra=16, seed=2)
+    qkv_case(lib, 2, 2, 4, 6, 128, 4, rope=True, t0s=[1, 1000], kextra=8, seed=3)
+
+
+def test_qkv_scatter_video14b_width_exact(lib):
+    # d 5120, 40 heads, one row
+    qkv_case(lib, 1, T, Hp, Wp, 5120, 40, rope=False, t0s=[0], seed=4)
+
+
+# ------------------------------------------------------------------ FFN first layer with GELU
+@pytest.mark.parametrize("M,N,K", [(R * L, F, D), (1000, 520, 256)])
+def test_gelu_epilogue(lib, M, N, K):
+    print(f"gelu M={M} N={N} K={K}", flush=True)
+    A, W, b, acc = int_operands(M, N, K, 5)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=device())
+    e = sdlib.sd_gemm_epi(mode=sdlib.SD_EPI_GELU, bias=b.data_ptr(), out=out.data_ptr(), ldo=N)
+    run(lib, A, W, M, N, K, e)
+    got = out.float().cpu().numpy()
+    ref = dit.gelu(acc)
+    # bf16 rounding of the stored value; the erf approximation (|error| <=
+    # 1.5e-7) and the fp32 reciprocal / exponential add at most 2e-6 |v|
+    err = np.abs(got - ref) - 2.0 ** -8 * np.abs(ref) - 2e-6 * np.abs(acc) - 1e-7
+    assert err.max() <= 0.0, f"excess {err.max():.3e}"
+
+
+# ------------------------------------------------------------------ gated residual (attention out, FFN out)
+@pytest.mark.parametrize("M,N,K", [(R * L, D, D), (R * L, D, F), (700, 136, 320)])
+def test_gate_resid_epilogue_exact(lib, M, N, K):
+    """resid += (mod[r][5d + n] + blk[5d + n]) * (A W^T + b)[m][n], r = m / L.
+    Gates are multiples of 1/2 and the residual a multiple of 1/256: every
+    product and sum is exact in fp32."""
+    print(f"gate resid M={M} N={N} K={K}", flush=True)
+    Lr = L if M % L == 0 else 100
+    rows = M // Lr + (M % Lr > 0)
+    A, W, b, acc = int_operands(M, N, K, 6)
+    rng = np.random.default_rng(7)
+    six_d = 6 * N
+    off = 5 * N
+    mod = rng.integers(-2, 3, size=(rows, six_d)) / 2.0
+    blk = rng.integers(-1, 2, size=six_d) / 2.0
+    c0 = rng.integers(-4096, 4097, size=(M, N)) / 256.0
+    resid = to_dev(c0, torch.float32)
+    mod_d, blk_d = to_dev(mod, torch.float32), to_dev(blk, torch.bfloat16)
+    e = sdlib.sd_gemm_epi(mode=sdlib.SD_EPI_GATE_RESID, bias=b.data_ptr(), resid=resid.data_ptr(),
+                          mod=mod_d.data_ptr(), blk=blk_d.data_ptr(), gate_off=off, six_d=six_d, L=Lr)
+    run(lib, A, W, M, N, K, e)
+    gate = mod[np.arange(M) // Lr, off:off + N] + blk[off:off + N]
+    assert np.array_equal(resid.cpu().numpy().astype(np.float64), c0 + gate * acc)
+
+
+# ------------------------------------------------------------------ patch embedding and head
+def test_patch_embedding_epilogue_exact(lib):
+    """The patch embedding of the video rows: K = 64 (a single 64-deep k-tile)
+    writes the fp32 residual stream."""
+    M, N, K = R * L, D, PC
+    A, W, b, acc = int_operands(M, N, K, 8)
+    resid = torch.full((M, N), 7.0, dtype=torch.float32, device=device())
+    e = sdlib.sd_gemm_epi(mode=sdlib.SD_EPI_PATCH, bias=b.data_ptr(), resid=resid.data_ptr())
+    run(lib, A, W, M, N, K, e)
+    assert np.array_equal(resid.cpu().numpy().astype(np.float64), acc)
+
+
+@pytest.mark.parametrize("rows,t,hp,wp,ch", [(R, T, Hp, Wp, CH), (3, 1, 8, 8, 4)])
+def test_head_epilogue_unpatchifies_exactly(lib, rows, t, hp, wp, ch):
+    Lr = t * hp * wp
+    M, N, K = rows * Lr, P * P * ch, 256
+    A, W, b, acc = int_operands(M, N, K, 9)
+    eps = torch.zeros((rows, t, ch, hp * P, wp * P), dtype=torch.float32, device=device())
+    e = sdlib.sd_gemm_epi(mode=sdlib.SD_EPI_HEAD, bias=b.data_ptr(), eps=eps.data_ptr(), L=Lr, C=ch, Hl=hp * P,
+                          Wl=wp * P, p=P, T=t, Hp=hp, Wp=wp)
+    run(lib, A, W, M, N, K, e)
+    got = eps.cpu().numpy().astype(np.float64)
+    for r in range(rows):
+        ref = dit.unpatchify(acc[r * Lr:(r + 1) * Lr], t, ch, hp * P, wp * P, P)
+        assert np.array_equal(got[r], ref), f"row {r}"
+
+
+# ------------------------------------------------------------------ LayerNorm + adaLN modulation
+@pytest.mark.parametrize("M,d,Lr", [(R * L, D, L), (L, 5120, L), (2048, 1024, 1024), (37, 128, 10)])
+def test_ln_mod_against_oracle(lib, M, d, Lr):
+    """bf16 output of LN(x) * (1 + scale) + shift, scale / shift = the row's
+    modulation slots plus the block table (the attention slots 0 and 1 of
+    6d); register-resident rows of 4 (d <= 1024), 8 (1536) and 20 (5120)
+    vectors per lane.  Bound: the stored bf16 rounding plus 1e-4 of the RMS."""
+    print(f"ln_mod M={M} d={d}", flush=True)
+    rng = np.random.default_rng(d + M)
+    rows = (M + Lr - 1) // Lr
+    x = rng.standard_normal((M, d)).astype(np.float32) * 3 + 0.5
+    mod = (0.3 * rng.standard_normal((rows, 6 * d))).astype(np.float32)
+    blk = bf16_round(0.02 * rng.standard_normal(6 * d))
+    out = torch.empty((M, d), dtype=torch.bfloat16, device=device())
+    xd, md, bd = to_dev(x, torch.float32), to_dev(mod, torch.float32), to_dev(blk, torch.bfloat16)
+    call(lib.sd_k_ln_mod(sdlib.SD_DTYPE_BF16, xd.data_ptr(), out.data_ptr(), M, d, Lr, md.data_ptr(), bd.data_ptr(),
+                         0, d, 6 * d, stream_ptr()))
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    m = mod.astype(np.float64)[np.arange(M) // Lr] + blk.astype(np.float64)
+    ref = dit.modulate(dit.layer_norm(x.astype(np.float64)), m[:, :d], m[:, d:2 * d])
+    rms = np.sqrt(np.mean(ref * ref))
+    excess = np.max(np.abs(got - ref) - 2.0 ** -8 * np.abs(ref)) / rms
+    assert excess <= 1e-4, f"excess {excess:.3e}"

@@ -29,15 +29,27 @@ def reduced(name, **kw):
     return get_config(name, **base)
 
 
-def run_parity(cfg, steps, check_ring=True, sizes=None, io_stream=False):
+def scene_cut(pushes, scale=-4.0):
+    """Input transform of a crafted scene cut: the latents of the given
+    pushes (0-based) are scaled by `scale`, which turns the chunk embedding
+    away from the sink's (cosine about -0.9 instead of 0.93-0.99)."""
+    return lambda k, x: x * np.float32(scale) if k in pushes else x
+
+
+def run_parity(cfg, steps, check_ring=True, sizes=None, io_stream=False, transform=None, oracle_dtype=np.float64,
+               progress=False):
     """`sizes`: chunks entering at each step (cycled); default B every step.
     `io_stream`: inputs are produced and pushed on a second stream (the IO
-    queue), overlapped with the steps on the main stream."""
+    queue), overlapped with the steps on the main stream.  `transform(k, x0)`
+    changes push k's clean latent on both sides.  The oracle's sink decisions
+    that the GPU matched are kept in orc.sink_events as (sim, refreshed)."""
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     weights = gen.make_weights(cfg)
     ctx_pos = gen.make_context(cfg)
     ctx_neg = gen.make_context(cfg, negative=True) if cfg.cfg_type != "self" else None
-    orc = OracleStream(cfg, weights, ctx_pos, ctx_neg)
+    orc = OracleStream(cfg, weights, ctx_pos, ctx_neg, dtype=oracle_dtype)
+    orc.sink_events = []
+    orc.t0_trace = []
     run = StreamRunner(cfg, upload_weights(cfg, weights))
     if cfg.ctx_len:
         run.set_context(to_dev(ctx_pos, tdt), to_dev(ctx_neg, tdt) if ctx_neg is not None else None)
@@ -52,6 +64,8 @@ def run_parity(cfg, steps, check_ring=True, sizes=None, io_stream=False):
     worst = 0.0
     while done < steps:
         x0, e, u = src.next(), gen.frame_noise(cfg, nz), us.next()
+        if transform is not None:
+            x0 = transform(pushes, x0)
         frame = ssf_src.next() if ssf_src else None
         po = orc.push_frame(x0, e, frame, u)
         with torch.cuda.stream(io if io is not None else torch.cuda.current_stream()):
@@ -64,6 +78,7 @@ def run_parity(cfg, steps, check_ring=True, sizes=None, io_stream=False):
         if po.skipped:
             continue
         assert list(pg.taus)[:cfg.n_slots] == po.taus and pg.t0 == po.t0 and pg.s == po.s
+        orc.t0_trace.append(po.t0)
         queued += 1
         want = sizes[done % len(sizes)] if sizes else B
         if queued < want:        # a step takes `want` pending chunks
@@ -89,7 +104,10 @@ def run_parity(cfg, steps, check_ring=True, sizes=None, io_stream=False):
             assert si.evaluated == 1 and si.entry == so.sink_entry
             if abs(so.sink_sim - cfg.sink_tau) > 1e-2:
                 assert bool(si.refreshed) == so.sink_refreshed, (done, si.sim, so.sink_sim)
+                orc.sink_events.append((so.sink_sim, so.sink_refreshed))
         done += 1
+        if progress:
+            print(f"  step {done}: {sg.rows} rows, kv_valid {sg.kv_valid}, worst error {worst:.3e}", flush=True)
     if check_ring and cfg.window_tokens:
         H, hd, W = cfg.n_heads, cfg.head_dim, cfg.window_tokens
         ringK = run.buffer(L.SD_BUF_RING_K, tdt, (cfg.n_blocks, H, W, hd)).float().cpu().numpy()
@@ -124,7 +142,7 @@ def test_tiny_fp32_sixteen_steps_with_ssf():
     assert orc.sink_count == 1
 
 
-def test_tiny_fp32_without_ssf_three_slots_and_kv_reset():
+def test_tiny_fp32_without_ssf_three_slots_wide_window():
     device()
     cfg = reduced("tiny", ssf_on=False, t_index=(10, 32, 45), window_tokens=128)
     print("tiny fp32 n=3 W=128", flush=True)
@@ -152,12 +170,73 @@ def test_fourstep_bf16_onetime_negative_with_latent_ssf():
     run_parity(cfg, 6)
 
 
-def test_video_bf16_motion_sink_refresh():
+def test_video_bf16_motion_full_window():
     device()
     cfg = reduced("video13b")
     print("video bf16 reduced", flush=True)
     orc, _ = run_parity(cfg, 8)
     assert orc.kv_valid == cfg.window_tokens
+
+
+def refresh_and_keep(orc, margin=1e-2):
+    """Both sink outcomes occurred, each decided more than `margin` from tau
+    (the GPU's decision was compared with the oracle's for each)."""
+    tau = orc.cfg.sink_tau
+    ref = [s for s, r in orc.sink_events if r and tau - s > margin]
+    keep = [s for s, r in orc.sink_events if not r and s - tau > margin]
+    assert ref and keep, orc.sink_events
+    return len(ref), len(keep)
+
+
+def test_video_bf16_sink_refresh_fires_after_a_scene_cut():
+    """StreamDiffusionV2 summary, adaptive sink refresh: chunks 5 and 6 are a
+    scene cut; their embeddings point away from the sink's, the entry is
+    refreshed, and the following ordinary chunks are kept."""
+    device()
+    cfg = reduced("video13b")
+    print("video bf16 reduced, scene cut at pushes 5-6", flush=True)
+    orc, _ = run_parity(cfg, 10, transform=scene_cut({5, 6}))
+    print("refresh / keep events:", refresh_and_keep(orc), flush=True)
+
+
+def test_video_bf16_two_sink_entries_scene_cut():
+    """M = 2 sink entries of 48 tokens: both fill from the first two leaving
+    chunks, the least similar one is replaced after the cut."""
+    device()
+    cfg = reduced("video13b", sink_entries=2)
+    print("video bf16 reduced, M = 2, scene cut", flush=True)
+    orc, _ = run_parity(cfg, 10, transform=scene_cut({5, 6}))
+    assert orc.sink_count == 2
+    print("refresh / keep events:", refresh_and_keep(orc), flush=True)
+
+
+def test_video_bf16_three_chunks_staged_sink_refresh():
+    """B = 3: the cut chunk is the third of its group, so its refresh copies
+    from its staged candidate slot (the ring already holds the later chunks)."""
+    device()
+    cfg = reduced("video13b", chunks_per_step=3, window_tokens=384)
+    print("video bf16 reduced B=3, scene cut at push 5", flush=True)
+    orc, _ = run_parity(cfg, 6, transform=scene_cut({5}))
+    print("refresh / keep events:", refresh_and_keep(orc), flush=True)
+
+
+def test_video_bf16_rope_reset_wraps_temporal_positions():
+    """StreamDiffusionV2 summary, RoPE refresh: with the threshold at 3 and
+    T = 2 frames per chunk the temporal base runs 0, 2, 0, 2, ...; keys cached
+    before a wrap keep their old rotation."""
+    device()
+    cfg = reduced("video13b", rope_reset=3)
+    print("video bf16 reduced, rope_reset 3", flush=True)
+    orc, _ = run_parity(cfg, 8)
+    assert orc.t0_trace == [0, 2] * 4
+
+
+def test_tiny_fp32_rope_reset_wraps_temporal_positions():
+    device()
+    cfg = reduced("tiny", ssf_on=False, rope_reset=3)
+    print("tiny fp32, rope_reset 3", flush=True)
+    orc, _ = run_parity(cfg, 9)
+    assert orc.t0_trace == [0, 1, 2, 3, 0, 1, 2, 3, 0]
 
 
 def test_tiny_fp32_two_chunks_per_step():
@@ -168,7 +247,7 @@ def test_tiny_fp32_two_chunks_per_step():
     assert orc.sink_count == 1
 
 
-def test_video_bf16_three_chunks_overflowing_window_sink_refresh():
+def test_video_bf16_three_chunks_overflowing_window():
     """B = 3 chunks of 192 tokens leave per step into a 384-token window: the
     ring keeps the last two of them, and every sink decision after the first
     capture reads its chunk's staged copy."""

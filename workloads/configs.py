@@ -43,6 +43,7 @@ class Config:
     # KV cache (tokens)
     sink_tokens: int = 0
     window_tokens: int = 0
+    sink_entries: int = 1           # M entries of sink_tokens / M tokens each
     sink_tau: float = 0.9           # reading: "tau should be large"
     rope_reset: int = 1024
     rope_base: float = 10000.0
