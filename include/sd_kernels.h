@@ -71,6 +71,7 @@ typedef struct {
   int32_t t0[SD_MAX_ROWS];     /* temporal RoPE base of each row */
   float* eps;                  /* HEAD: fp32 [M/L][T][C][Hl][Wl] */
   int32_t C, Hl, Wl, p, T;     /* HEAD: latent geometry and patch (Hl = Hp*p, Wl = Wp*p, L = T*Hp*Wp) */
+  int32_t f16;                 /* A and W are IEEE fp16 (F32 and RESID only; bias stays bf16) */
 } sd_gemm_epi;
 
 /* One bf16 GEMM with the epilogue e->mode, on the kernels and launch
@@ -92,11 +93,17 @@ sd_status sd_k_rope_tables(int32_t hd, int32_t positions, int32_t Hp, int32_t Wp
 
 /* LayerNorm over d (no affine, population variance, eps) of fp32 x [M][d],
  * then x * (1 + scale) + shift with scale / shift = mod[r*six_d + off + c] +
- * blk[off + c], r = m / L (mod NULL: no modulation; blk NULL: 0); out in
- * dtype (bf16 or fp32) [M][d].  d a multiple of 4, at most 5120.  The
- * adaLN-modulated normalisation in front of a block's attention and MLP. */
+ * blk[off + c], r = m / L (mod NULL: no modulation; blk NULL: 0).  d a
+ * multiple of 4, at most 5120.  The adaLN-modulated normalisation in front of
+ * a block's attention and MLP.  Output by form:
+ *   SD_LN_PLAIN  dtype (bf16 or fp32) [M][d]
+ *   SD_LN_F16    fp16 [M][d], no modulation (the cross-attention input)
+ *   SD_LN_SPLIT  bf16 [M][2d]: hi = bf16(y) in [0, d), lo = bf16(y - hi) in
+ *                [d, 2d) (the head's input, read against doubled weights) */
+enum { SD_LN_PLAIN = 0, SD_LN_F16 = 1, SD_LN_SPLIT = 2 };
 sd_status sd_k_ln_mod(int32_t dtype, const float* x, void* out, int32_t M, int32_t d, int32_t L, const float* mod,
-                      const void* blk, int32_t shift_off, int32_t scale_off, int32_t six_d, void* stream);
+                      const void* blk, int32_t shift_off, int32_t scale_off, int32_t six_d, int32_t form,
+                      void* stream);
 
 /* One causal 3x3x3 convolution of the Stream-VAE (StreamDiffusionV2 summary,
  * Stream-VAE: features cached inside every 3D convolution), bf16 channels-last:

@@ -98,7 +98,11 @@ class sd_gemm_epi(C.Structure):
                 ("kstride", C.c_int32), ("krows", C.c_int32), ("H", C.c_int32), ("hd", C.c_int32),
                 ("rope", C.c_int32), ("Hp", C.c_int32), ("Wp", C.c_int32), ("rope_table", C.c_void_p),
                 ("rope_positions", C.c_int32), ("t0", C.c_int32 * SD_MAX_ROWS), ("eps", C.c_void_p),
-                ("C", C.c_int32), ("Hl", C.c_int32), ("Wl", C.c_int32), ("p", C.c_int32), ("T", C.c_int32)]
+                ("C", C.c_int32), ("Hl", C.c_int32), ("Wl", C.c_int32), ("p", C.c_int32), ("T", C.c_int32),
+                ("f16", C.c_int32)]
+
+
+SD_LN_PLAIN, SD_LN_F16, SD_LN_SPLIT = 0, 1, 2
 
 
 SD_VAE_ABI_VERSION = 1
@@ -144,7 +148,7 @@ SIGNATURES = {
     "sd_k_rope_table_pairs": (C.c_size_t, [C.c_int32, C.c_int32, C.c_int32, C.c_int32]),
     "sd_k_rope_tables": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_double, C.c_void_p]),
     "sd_k_ln_mod": (C.c_int, [C.c_int32, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
-                              C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p]),
+                              C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p]),
     "sd_k_attention": (C.c_int, [C.c_int32, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int32, C.c_int32,
                                  C.c_int32, C.c_int32, C.c_int32, C.POINTER(sd_kv_segment), C.c_int32, C.c_void_p,
                                  C.c_size_t, C.c_void_p]),

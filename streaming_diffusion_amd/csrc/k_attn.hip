@@ -406,46 +406,53 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 // Cp columns and a GEMM back to the residual (K = H Cp), in place of the Q
 // projection, the attention over the prompt keys and the O projection.
 // Context slots C .. Cp - 1 get zero weight rows and a score bias of -inf.
-// Layouts: K [H][Cp][hd], V^T [H][hd][Cp]; W_q, W_oc [d][d] (out x in).
+// The folds read the prompt K / V in fp32 ([C][2d], token-major, before any
+// rounding) and store the folded matrices, the step's normalised input and
+// its probabilities in fp16: every value there is bounded (LayerNorm output,
+// probabilities, products of weights with the prompt projections), and fp16
+// carries three more mantissa bits than bf16 at the same matrix-core rate.
+// W_q, W_oc [d][d] (out x in).
 
-// wq_f[h Cp + j][k] = s sum_e K[h][j][e] W_q[h hd + e][k];  cq[h Cp + j] = s K[h][j] . b_q[h hd ..]
-__global__ __launch_bounds__(256) void fold_q_kernel(const bf16* __restrict__ K, const bf16* __restrict__ Wq,
-                                                     const bf16* __restrict__ bq, bf16* __restrict__ wq_f,
+// wq_f[h Cp + j][k] = s sum_e K[j][h hd + e] W_q[h hd + e][k];  cq[h Cp + j] = s K[j][h hd ..] . b_q[h hd ..]
+// (K, V: the fp32 prompt projections, token-major [C][2d], K in [0, d), V in [d, 2d))
+__global__ __launch_bounds__(256) void fold_q_kernel(const float* __restrict__ kv, const bf16* __restrict__ Wq,
+                                                     const bf16* __restrict__ bq, f16* __restrict__ wq_f,
                                                      float* __restrict__ cq, int d, int hd, int C, int Cp, float scale) {
   const int row = blockIdx.y, h = row / Cp, j = row - h * Cp;
   const int k = blockIdx.x * 256 + threadIdx.x;
-  const bf16* kr = K + ((int64_t)h * Cp + j) * hd;
+  const float* kr = kv + (int64_t)min(j, C - 1) * 2 * d + h * hd;
   if (k < d) {
     float acc = 0.f;
     if (j < C)
-      for (int e = 0; e < hd; ++e) acc += (float)kr[e] * (float)Wq[(int64_t)(h * hd + e) * d + k];
-    wq_f[(int64_t)row * d + k] = (bf16)(acc * scale);
+      for (int e = 0; e < hd; ++e) acc += kr[e] * (float)Wq[(int64_t)(h * hd + e) * d + k];
+    wq_f[(int64_t)row * d + k] = (f16)(acc * scale);
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     float acc = 0.f;
-    for (int e = 0; e < hd; ++e) acc += (float)kr[e] * (float)bq[h * hd + e];
+    for (int e = 0; e < hd; ++e) acc += kr[e] * (float)bq[h * hd + e];
     cq[row] = j < C ? acc * scale : -INFINITY;
   }
 }
 
-// wo_f[n][h Cp + j] = sum_e V^T[h][e][j] W_oc[n][h hd + e]
-__global__ __launch_bounds__(256) void fold_o_kernel(const bf16* __restrict__ VT, const bf16* __restrict__ Wo,
-                                                     bf16* __restrict__ wo_f, int d, int H, int hd, int C, int Cp) {
+// wo_f[n][h Cp + j] = sum_e V[j][h hd + e] W_oc[n][h hd + e]
+__global__ __launch_bounds__(256) void fold_o_kernel(const float* __restrict__ kv, const bf16* __restrict__ Wo,
+                                                     f16* __restrict__ wo_f, int d, int H, int hd, int C, int Cp) {
   const int n = blockIdx.x, ncol = H * Cp;
   for (int col = threadIdx.x; col < ncol; col += 256) {
     const int h = col / Cp, j = col - h * Cp;
     float acc = 0.f;
-    if (j < C)
-      for (int e = 0; e < hd; ++e)
-        acc += (float)VT[((int64_t)h * hd + e) * Cp + j] * (float)Wo[(int64_t)n * d + h * hd + e];
-    wo_f[(int64_t)n * ncol + col] = (bf16)acc;
+    if (j < C) {
+      const float* vr = kv + (int64_t)j * 2 * d + d + h * hd;
+      for (int e = 0; e < hd; ++e) acc += vr[e] * (float)Wo[(int64_t)n * d + h * hd + e];
+    }
+    wo_f[(int64_t)n * ncol + col] = (f16)acc;
   }
 }
 
 // P[m][h Cp + j] = softmax over j of (S[m][h Cp + j] + c[h Cp + j]); 16 lanes
 // per (row, head), Cp <= 128
 __global__ __launch_bounds__(256) void ctx_softmax_kernel(const float* __restrict__ S, const float* __restrict__ c,
-                                                          bf16* __restrict__ P, int64_t M, int H, int Cp) {
+                                                          f16* __restrict__ P, int64_t M, int H, int Cp) {
   const int64_t g = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int l = threadIdx.x & 15;
   if (g >= M * H) return;           // whole 16-lane groups leave together
@@ -474,20 +481,20 @@ __global__ __launch_bounds__(256) void ctx_softmax_kernel(const float* __restric
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int j = l + 16 * i;
-    if (j < Cp) P[base + j] = (bf16)(v[i] * inv);
+    if (j < Cp) P[base + j] = (f16)(v[i] * inv);
   }
 }
 
-hipError_t cross_fold(hipStream_t s, const bf16* K, const bf16* VT, const bf16* Wq, const bf16* bq, const bf16* Wo,
-                      bf16* wq_f, float* cq, bf16* wo_f, int d, int H, int hd, int C, int Cp) {
+hipError_t cross_fold(hipStream_t s, const float* kv, const bf16* Wq, const bf16* bq, const bf16* Wo, f16* wq_f,
+                      float* cq, f16* wo_f, int d, int H, int hd, int C, int Cp) {
   if (C < 1 || C > Cp || Cp > 128 || H * Cp > 65535) return hipErrorInvalidValue;
-  fold_q_kernel<<<dim3((d + 255) / 256, H * Cp), 256, 0, s>>>(K, Wq, bq, wq_f, cq, d, hd, C, Cp,
+  fold_q_kernel<<<dim3((d + 255) / 256, H * Cp), 256, 0, s>>>(kv, Wq, bq, wq_f, cq, d, hd, C, Cp,
                                                               1.0f / std::sqrt((float)hd));
-  fold_o_kernel<<<d, 256, 0, s>>>(VT, Wo, wo_f, d, H, hd, C, Cp);
+  fold_o_kernel<<<d, 256, 0, s>>>(kv, Wo, wo_f, d, H, hd, C, Cp);
   return hipGetLastError();
 }
 
-hipError_t ctx_softmax(hipStream_t s, const float* S, const float* c, bf16* P, int64_t M, int H, int Cp) {
+hipError_t ctx_softmax(hipStream_t s, const float* S, const float* c, f16* P, int64_t M, int H, int Cp) {
   if (Cp < 1 || Cp > 128) return hipErrorInvalidValue;
   const int64_t groups = M * H;
   if (groups == 0) return hipSuccess;

@@ -37,6 +37,17 @@ SD_DEV float gelu_f(float v) {
   return 0.5f * v * (v >= 0.f ? 2.0f - e : e);
 }
 
+// One 32x32x16 matrix-core product; with H16 the 16-bit operands are
+// IEEE half precision (same layout and rate as bf16, 3 more mantissa bits).
+template <bool H16>
+SD_DEV f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  if constexpr (H16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
+                                                  0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 SD_DEV void load8_bf16(const bf16* p, float* o) {
   const bf16x8 v = *(const bf16x8*)p;
 #pragma unroll
@@ -287,7 +298,7 @@ SD_DEV void epi_strip(const Epi& E, const float* stg, int LC, int m_base, int n0
   }
 }
 
-template <int BM, int BN, int NW, int MODE>
+template <int BM, int BN, int NW, int MODE, bool H16 = false>
 __global__ __launch_bounds__(64 * NW) void gemm_mfma_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
                                                         int M, int N, int K, Epi E) {
   constexpr int BK = 64, PAD = 8, LDK = BK + PAD;
@@ -398,7 +409,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_kernel(const bf16* __restri
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = mfma32<H16>(fa[cur][i], fb[cur][j], acc[i][j]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -474,7 +485,7 @@ SD_DEV void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(n) : "memory");
 }
 
-template <int BM, int BN, int NW, int BK, int NS, bool SPREAD, int MODE>
+template <int BM, int BN, int NW, int BK, int NS, bool SPREAD, int MODE, bool H16 = false>
 __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
                                                           int M, int N, int K, Epi E) {
   constexpr int NT = 64 * NW, WN = NW / 2;
@@ -575,7 +586,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restric
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = mfma32<H16>(fa[i], fb[j], acc[i][j]);
     }
   };
 
@@ -653,14 +664,14 @@ static int device_cus() {
   return cus;
 }
 
-template <int BM, int BN, int NW, int BK, int NS, bool SPREAD, int MODE>
+template <int BM, int BN, int NW, int BK, int NS, bool SPREAD, int MODE, bool H16 = false>
 hipError_t launch_dma(hipStream_t s, const bf16* A, const bf16* W, int M, int N, int K, const Epi& E) {
   const unsigned grid = (unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
-  gemm_dma_kernel<BM, BN, NW, BK, NS, SPREAD, MODE><<<grid, 64 * NW, 0, s>>>(A, W, M, N, K, E);
+  gemm_dma_kernel<BM, BN, NW, BK, NS, SPREAD, MODE, H16><<<grid, 64 * NW, 0, s>>>(A, W, M, N, K, E);
   return hipGetLastError();
 }
 
-template <int MODE>
+template <int MODE, bool H16 = false>
 hipError_t gemm_mfma_mode(hipStream_t s, const bf16* A, const bf16* W, int M, int N, int K, const Epi& E) {
   // pick the tile that minimises (rounds of resident workgroups) x (cost per
   // tile); larger tiles cost less per flop.  256 x 256 with 8 waves keeps two
@@ -692,18 +703,18 @@ hipError_t gemm_mfma_mode(hipStream_t s, const bf16* A, const bf16* W, int M, in
     // of the CUs, 128 x 128 tiles (4 waves, two workgroups per CU) spread the
     // work over more of them (measured faster on every GEMM of the 12- and
     // 24-block image DiTs, slower on the video DiT's 198-tile N = 1536 GEMMs)
-    if (t192 * 10 < cus * 6) return launch_dma<128, 128, 4, 64, 2, true, MODE>(s, A, W, M, N, K, E);
-    if (c192 < c256) return launch_dma<192, 256, 8, 64, 2, true, MODE>(s, A, W, M, N, K, E);
-    return launch_dma<256, 256, 8, 64, 2, true, MODE>(s, A, W, M, N, K, E);
+    if (t192 * 10 < cus * 6) return launch_dma<128, 128, 4, 64, 2, true, MODE, H16>(s, A, W, M, N, K, E);
+    if (c192 < c256) return launch_dma<192, 256, 8, 64, 2, true, MODE, H16>(s, A, W, M, N, K, E);
+    return launch_dma<256, 256, 8, 64, 2, true, MODE, H16>(s, A, W, M, N, K, E);
   }
   const int bm = opts[best].bm, bn = opts[best].bn;
   const unsigned grid = (unsigned)(((M + bm - 1) / bm) * ((N + bn - 1) / bn));
   if (best == 0)
-    gemm_mfma_kernel<256, 256, 8, MODE><<<grid, 512, 0, s>>>(A, W, M, N, K, E);
+    gemm_mfma_kernel<256, 256, 8, MODE, H16><<<grid, 512, 0, s>>>(A, W, M, N, K, E);
   else if (best == 1)
-    gemm_mfma_kernel<256, 128, 4, MODE><<<grid, 256, 0, s>>>(A, W, M, N, K, E);
+    gemm_mfma_kernel<256, 128, 4, MODE, H16><<<grid, 256, 0, s>>>(A, W, M, N, K, E);
   else
-    gemm_mfma_kernel<128, 128, 4, MODE><<<grid, 256, 0, s>>>(A, W, M, N, K, E);
+    gemm_mfma_kernel<128, 128, 4, MODE, H16><<<grid, 256, 0, s>>>(A, W, M, N, K, E);
   return hipGetLastError();
 }
 
@@ -722,6 +733,18 @@ hipError_t gemm_mfma(hipStream_t s, const void* A, const void* W, int M, int N, 
     case EPI_HEAD: return gemm_mfma_mode<EPI_HEAD>(s, a, w, M, N, K, E);
     case EPI_CTXKV: return gemm_mfma_mode<EPI_CTXKV>(s, a, w, M, N, K, E);
     case EPI_F32: return gemm_mfma_mode<EPI_F32>(s, a, w, M, N, K, E);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t gemm_mfma_f16(hipStream_t s, const void* A, const void* W, int M, int N, int K, const Epi& E) {
+  if ((uint64_t)M * K >= (1ull << 32) || (uint64_t)N * K >= (1ull << 32)) return hipErrorInvalidValue;
+  if (M == 0 || N == 0) return hipSuccess;
+  const bf16* a = (const bf16*)A;
+  const bf16* w = (const bf16*)W;
+  switch (E.mode) {
+    case EPI_RESID: return gemm_mfma_mode<EPI_RESID, true>(s, a, w, M, N, K, E);
+    case EPI_F32: return gemm_mfma_mode<EPI_F32, true>(s, a, w, M, N, K, E);
     default: return hipErrorInvalidValue;
   }
 }

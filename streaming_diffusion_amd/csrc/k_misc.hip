@@ -84,8 +84,10 @@ hipError_t rcfg_update(hipStream_t s, const RowTable& rt, float* store_x, float*
 
 // ---------------------------------------------------------------------------
 // Patch gather: token (t, y, x) of row r gets the p x p x C patch in
-// (py, px, c) order.
-template <typename T>
+// (py, px, c) order.  SPLIT (bf16): a token's row holds the P values as
+// hi = bf16(v), then lo = bf16(v - hi) (row pitch 2P), for a patch embedding
+// over K = 2P against [W | W] that sees the fp32 latent to about 16 bits.
+template <typename T, bool SPLIT = false>
 __global__ void patchify_kernel(RowTable rt, const float* __restrict__ store_x, T* __restrict__ out, int64_t lat,
                                 int Tn, int C, int Hl, int Wl, int p) {
   const int r = blockIdx.y;
@@ -100,14 +102,24 @@ __global__ void patchify_kernel(RowTable rt, const float* __restrict__ store_x, 
   const int c = v % C, px = (v / C) % p, py = v / (C * p);
   const float* src = store_x + (int64_t)rt.r[r].frame * lat;
   const float val = src[(((int64_t)f * C + c) * Hl + (yq * p + py)) * Wl + (xq * p + px)];
-  out[(int64_t)r * per_row + i] = from_f<T>(val);
+  if constexpr (SPLIT) {
+    const T hi = from_f<T>(val);
+    T* o = out + ((int64_t)r * Tn * Hp * Wp + tok) * 2 * P + v;
+    o[0] = hi;
+    o[P] = from_f<T>(val - (float)hi);
+  } else {
+    out[(int64_t)r * per_row + i] = from_f<T>(val);
+  }
 }
 
 hipError_t patchify(hipStream_t s, bool bf, const RowTable& rt, const float* store_x, void* out, int64_t lat,
-                    int T, int C, int Hl, int Wl, int p) {
+                    int T, int C, int Hl, int Wl, int p, bool split) {
   const int64_t per_row = (int64_t)T * (Hl / p) * (Wl / p) * p * p * C;
   dim3 g(grid1(per_row, 256), rt.R);
-  if (bf)
+  if (split && !bf) return hipErrorInvalidValue;
+  if (split)
+    patchify_kernel<bf16, true><<<g, 256, 0, s>>>(rt, store_x, (bf16*)out, lat, T, C, Hl, Wl, p);
+  else if (bf)
     patchify_kernel<bf16><<<g, 256, 0, s>>>(rt, store_x, (bf16*)out, lat, T, C, Hl, Wl, p);
   else
     patchify_kernel<float><<<g, 256, 0, s>>>(rt, store_x, (float*)out, lat, T, C, Hl, Wl, p);
@@ -133,6 +145,14 @@ SD_DEV void store4<bf16>(bf16* p, const float* o) {
   for (int q = 0; q < 4; ++q) v[q] = (bf16)o[q];
   *(bf16x4*)p = v;
 }
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+template <>
+SD_DEV void store4<f16>(f16* p, const float* o) {
+  f16x4 v;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = (f16)o[q];
+  *(f16x4*)p = v;
+}
 SD_DEV void load4(const float* p, float* o) {
   const float4 v = *(const float4*)p;
   o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
@@ -142,8 +162,16 @@ SD_DEV void load4(const bf16* p, float* o) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) o[q] = (float)v[q];
 }
+SD_DEV void load4(const f16* p, float* o) {
+  const f16x4 v = *(const f16x4*)p;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) o[q] = (float)v[q];
+}
 
-template <typename T, int NV>
+// SPLIT (bf16): the row of 2d outputs holds hi = bf16(y) in [0, d) and
+// lo = bf16(y - hi) in [d, 2d), so hi + lo carries y to about 16 bits; a GEMM
+// over K = 2d against the weights stored twice ([W | W]) then sees y itself.
+template <typename T, int NV, bool SPLIT = false>
 __global__ __launch_bounds__(256) void ln_mod_kernel(const float* __restrict__ x, T* __restrict__ out, int M, int d,
                                                      int L, const float* __restrict__ mod, const T* __restrict__ blk,
                                                      int shift_off, int scale_off, int six_d, float eps) {
@@ -172,7 +200,7 @@ __global__ __launch_bounds__(256) void ln_mod_kernel(const float* __restrict__ x
   const float rstd = 1.0f / sqrtf(wave_sum(sq) / (float)d + eps);
   const int r = row / L;
   const float* mr = mod ? mod + (int64_t)r * six_d : nullptr;
-  T* orow = out + (int64_t)row * d;
+  T* orow = out + (int64_t)row * (SPLIT ? 2 * d : d);
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int j = lane + 64 * i;
@@ -196,6 +224,12 @@ __global__ __launch_bounds__(256) void ln_mod_kernel(const float* __restrict__ x
       for (int q = 0; q < 4; ++q) o[q] = o[q] * (1.0f + sc[q]) + sh[q];
     }
     store4<T>(orow + 4 * j, o);
+    if constexpr (SPLIT) {
+      float lo[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) lo[q] = o[q] - (float)(T)o[q];
+      store4<T>(orow + d + 4 * j, lo);
+    }
   }
 }
 
@@ -211,13 +245,20 @@ void rope_table_fill(float2* out, int npos, int width, double base) {
 }
 
 hipError_t ln_mod(hipStream_t s, bool bf, const float* x, void* out, int M, int d, int L, const float* mod,
-                  const void* blk, int shift_off, int scale_off, int six_d, float eps) {
+                  const void* blk, int shift_off, int scale_off, int six_d, float eps, int form) {
   if (M == 0) return hipSuccess;
   if ((d & 3) || d > 4 * 64 * LN_MAXV || (shift_off & 3) || (scale_off & 3) || (six_d & 3)) return hipErrorInvalidValue;
+  if (form != LN_PLAIN && !bf) return hipErrorInvalidValue;
+  if (form == LN_F16 && mod) return hipErrorInvalidValue;
   const unsigned g = (unsigned)((M + 3) / 4);
 #define SD_LN_LAUNCH(NV)                                                                                           \
   do {                                                                                                             \
-    if (bf)                                                                                                        \
+    if (form == LN_F16)                                                                                            \
+      ln_mod_kernel<f16, NV><<<g, 256, 0, s>>>(x, (f16*)out, M, d, L, nullptr, nullptr, 0, 0, six_d, eps);         \
+    else if (form == LN_SPLIT)                                                                                     \
+      ln_mod_kernel<bf16, NV, true><<<g, 256, 0, s>>>(x, (bf16*)out, M, d, L, mod, (const bf16*)blk, shift_off,    \
+                                                      scale_off, six_d, eps);                                      \
+    else if (bf)                                                                                                   \
       ln_mod_kernel<bf16, NV><<<g, 256, 0, s>>>(x, (bf16*)out, M, d, L, mod, (const bf16*)blk, shift_off, scale_off, \
                                                 six_d, eps);                                                       \
     else                                                                                                           \

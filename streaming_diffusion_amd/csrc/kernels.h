@@ -12,13 +12,17 @@ hipError_t entry_noise(hipStream_t s, const float* x0, const float* noise, float
 // R-CFG, x0 prediction and re-noise for every denoise row of rt.
 hipError_t rcfg_update(hipStream_t s, const RowTable& rt, float* store_x, float* store_x0s, const float* eps,
                        const float* store_z, float* out, int64_t lat, float gamma, float delta);
-// Gather patches of each row's latent into [R*L][p*p*C] (element type by bf).
+// Gather patches of each row's latent into [R*L][p*p*C] (element type by bf);
+// split (bf16): [R*L][2*p*p*C], each token's values as hi then lo parts.
 hipError_t patchify(hipStream_t s, bool bf, const RowTable& rt, const float* store_x, void* out, int64_t lat,
-                    int T, int C, int Hl, int Wl, int p);
+                    int T, int C, int Hl, int Wl, int p, bool split = false);
 // LayerNorm (no affine, population variance) then optional modulation
-// x*(1+scale)+shift with scale/shift = mod[r][off] + blk[off]; output element type by bf.
+// x*(1+scale)+shift with scale/shift = mod[r][off] + blk[off]; output element
+// type by bf (form LN_PLAIN), fp16 without modulation (LN_F16), or bf16 as a
+// hi / lo pair per element, row pitch 2d (LN_SPLIT).
+enum { LN_PLAIN = 0, LN_F16 = 1, LN_SPLIT = 2 };
 hipError_t ln_mod(hipStream_t s, bool bf, const float* x, void* out, int M, int d, int L, const float* mod,
-                  const void* blk, int shift_off, int scale_off, int six_d, float eps);
+                  const void* blk, int shift_off, int scale_off, int six_d, float eps, int form = LN_PLAIN);
 // Sinusoidal timestep embedding per row: [cos(tau w_j), sin(tau w_j)], fp64 math.
 hipError_t temb_embed(hipStream_t s, const RowTable& rt, float* out, int d_freq);
 // y[r][n] = act(sum_k x[r][k] W[n][k] + b[n]); act 0 = none, 1 = SiLU.
@@ -41,9 +45,11 @@ hipError_t fill_zero(hipStream_t s, void* p, size_t bytes);
 void rope_table_fill(float2* out, int npos, int width, double base);
 // cross-attention with folded prompt projections (k_attn.hip): the folded
 // score / output matrices of one block and context, and the grouped softmax
-hipError_t cross_fold(hipStream_t s, const bf16* K, const bf16* VT, const bf16* Wq, const bf16* bq, const bf16* Wo,
-                      bf16* wq_f, float* cq, bf16* wo_f, int d, int H, int hd, int C, int Cp);
-hipError_t ctx_softmax(hipStream_t s, const float* S, const float* c, bf16* P, int64_t M, int H, int Cp);
+// kv: the context's fp32 K | V projections, token-major [C][2d]; the folded
+// matrices are fp16 (score and output GEMMs run on fp16 operands)
+hipError_t cross_fold(hipStream_t s, const float* kv, const bf16* Wq, const bf16* bq, const bf16* Wo, f16* wq_f,
+                      float* cq, f16* wo_f, int d, int H, int hd, int C, int Cp);
+hipError_t ctx_softmax(hipStream_t s, const float* S, const float* c, f16* P, int64_t M, int H, int Cp);
 
 // ---------------------------------------------------------------- reductions
 // Exact int64 (sum a*b, sum a*a, sum b*b); kind 0 = uint8, 1 = fp32 latents
@@ -64,6 +70,8 @@ hipError_t sink_score(hipStream_t s, const float* x, double* partial, int L, int
 hipError_t gemm(hipStream_t s, bool bf, const void* A, const void* W, int M, int N, int K, const Epi& E);
 // bf16 matrix-core path of gemm() (K a multiple of 8).
 hipError_t gemm_mfma(hipStream_t s, const void* A, const void* W, int M, int N, int K, const Epi& E);
+// The same with fp16 operands A and W (bias stays bf16); EPI_F32 and EPI_RESID.
+hipError_t gemm_mfma_f16(hipStream_t s, const void* A, const void* W, int M, int N, int K, const Epi& E);
 
 // ---------------------------------------------------------------- attention
 struct KvSeg {

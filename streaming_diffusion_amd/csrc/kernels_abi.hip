@@ -72,6 +72,7 @@ sd_status sd_k_gemm_epi(const void* A, const void* W, int32_t M, int32_t N, int3
   E.bias = e->bias;
   E.L = e->L > 0 ? e->L : 1;
   E.ldo = N;
+  if (e->f16 && e->mode != SD_EPI_F32 && e->mode != SD_EPI_RESID) return SD_ERR_ARG;
   switch (e->mode) {
     case SD_EPI_STORE:
     case SD_EPI_GELU:
@@ -146,19 +147,25 @@ sd_status sd_k_gemm_epi(const void* A, const void* W, int32_t M, int32_t N, int3
     default:
       return SD_ERR_ARG;
   }
-  return sdk::gemm_mfma((hipStream_t)stream, A, W, M, N, K, E) == hipSuccess ? SD_OK : SD_ERR_HIP;
+  const hipError_t r = e->f16 ? sdk::gemm_mfma_f16((hipStream_t)stream, A, W, M, N, K, E)
+                             : sdk::gemm_mfma((hipStream_t)stream, A, W, M, N, K, E);
+  return r == hipSuccess ? SD_OK : SD_ERR_HIP;
 }
 
 sd_status sd_k_ln_mod(int32_t dtype, const float* x, void* out, int32_t M, int32_t d, int32_t L, const float* mod,
-                      const void* blk, int32_t shift_off, int32_t scale_off, int32_t six_d, void* stream) {
+                      const void* blk, int32_t shift_off, int32_t scale_off, int32_t six_d, int32_t form,
+                      void* stream) {
   if (dtype != SD_DTYPE_F32 && dtype != SD_DTYPE_BF16) return SD_ERR_ARG;
+  if (form != SD_LN_PLAIN && form != SD_LN_F16 && form != SD_LN_SPLIT) return SD_ERR_ARG;
+  if (form != SD_LN_PLAIN && dtype != SD_DTYPE_BF16) return SD_ERR_ARG;
+  if (form == SD_LN_F16 && mod) return SD_ERR_ARG;
   if (!x || !out || M < 0 || d < 4 || L < 1) return SD_ERR_ARG;
   if (d % 4 || d > 5120) return SD_ERR_SHAPE;
   if (mod && (shift_off < 0 || scale_off < 0 || shift_off % 4 || scale_off % 4 || six_d % 4 ||
               shift_off + d > six_d || scale_off + d > six_d))
     return SD_ERR_SHAPE;
   return sdk::ln_mod((hipStream_t)stream, dtype == SD_DTYPE_BF16, x, out, M, d, L, mod, mod ? blk : nullptr,
-                     shift_off, scale_off, mod ? six_d : 4, 1e-6f) == hipSuccess
+                     shift_off, scale_off, mod ? six_d : 4, 1e-6f, form) == hipSuccess
              ? SD_OK
              : SD_ERR_HIP;
 }

@@ -61,8 +61,13 @@ struct sd_stream {
   void *candK = nullptr, *candVT = nullptr;
   void *ctxK = nullptr, *ctxVT = nullptr;
   // bf16: cross-attention runs on folded projections (k_attn.hip): per block
-  // and context wq_f [H Cp][d], wo_f [d][H Cp] bf16 and the score bias [H Cp]
+  // and context wq_f [H Cp][d], wo_f [d][H Cp] fp16 and the score bias [H Cp]
   bool fold = false;
+  // bf16: the patch embedding and the head see their fp32 inputs as hi + lo
+  // bf16 pairs (K doubled); their weights are kept twice side by side,
+  // pe2 [d][2P] = [pe_w | pe_w], head2 [P][2d] = [head_w | head_w], copied
+  // from the caller's weights at create
+  void *pe2 = nullptr, *head2 = nullptr;
   void *fold_q = nullptr, *fold_o = nullptr;
   float* fold_c = nullptr;
   double *sink_emb = nullptr, *sink_part = nullptr, *sink_sim = nullptr;
@@ -178,7 +183,7 @@ size_t carve(sd_stream* s, char* base) {
   s->mod = cv.take<float>((size_t)s->Rmax * 6 * s->d * 4);
   s->fmod = cv.take<float>((size_t)s->Rmax * 2 * s->d * 4);
   s->resid = cv.take<float>((size_t)M * s->d * 4);
-  s->xm = cv.take<void>((size_t)M * std::max(s->d, s->P) * es);
+  s->xm = cv.take<void>((size_t)M * std::max(s->d, s->P) * (s->bf ? 2 : 1) * es);
   s->q = cv.take<void>((size_t)M * s->d * es);
   s->kown = cv.take<void>((size_t)M * s->d * es);
   s->vtown = cv.take<void>((size_t)M * s->d * es);
@@ -200,12 +205,17 @@ size_t carve(sd_stream* s, char* base) {
     // pays only when H Cp <= d.  The step's scores (fp32) and probabilities
     // (bf16) live in the FFN buffer.
     const size_t ncol = (size_t)s->H * s->ctx8;
-    s->fold = s->bf && s->ctx8 <= 128 && ncol <= (size_t)s->d && ncol * 3 <= (size_t)s->F;
+    s->fold = s->bf && s->ctx8 <= 128 && ncol <= (size_t)s->d && ncol * 3 <= (size_t)s->F &&
+              (size_t)c.ctx_len * 2 * s->d * 4 <= (size_t)M * s->F * es;
     if (s->fold) {
       s->fold_q = cv.take<void>((size_t)s->nb * nctx * ncol * s->d * es);
       s->fold_o = cv.take<void>((size_t)s->nb * nctx * s->d * ncol * es);
       s->fold_c = cv.take<float>((size_t)s->nb * nctx * ncol * 4);
     }
+  }
+  if (s->bf) {
+    s->pe2 = cv.take<void>((size_t)s->d * 2 * s->P * es);
+    s->head2 = cv.take<void>((size_t)s->P * 2 * s->d * es);
   }
   s->sink_emb = cv.take<double>((size_t)std::max(1, s->Ment) * s->d * 8);
   s->sink_part = cv.take<double>((size_t)64 * s->d * 8);
@@ -390,6 +400,14 @@ sd_status sd_stream_create(const sd_stream_config* cfg, const sd_weights* w, voi
   if (e == hipSuccess) e = sdk::fill_zero(s->st, s->sinkVT, cache_bytes[1]);
   if (e == hipSuccess) e = sdk::fill_zero(s->st, s->sink_emb, (size_t)std::max(1, s->Ment) * s->d * 8);
   if (e == hipSuccess) e = sdk::fill_zero(s->st, s->sink_flag, 16);
+  if (s->bf)
+    for (int half = 0; half < 2 && e == hipSuccess; ++half) {
+      e = hipMemcpy2DAsync(Pm(s->pe2, (int64_t)half * s->P, s->es), 2 * s->P * s->es, w->pe_w, s->P * s->es,
+                           s->P * s->es, s->d, hipMemcpyDeviceToDevice, s->st);
+      if (e == hipSuccess)
+        e = hipMemcpy2DAsync(Pm(s->head2, (int64_t)half * s->d, s->es), 2 * s->d * s->es, w->head_w, s->d * s->es,
+                             s->d * s->es, s->P, hipMemcpyDeviceToDevice, s->st);
+    }
   if (e == hipSuccess) e = hipMemcpyAsync(s->rope_t, rt.data(), rt.size() * sizeof(float2), hipMemcpyHostToDevice, s->st);
   if (e == hipSuccess) e = hipMemcpyAsync(s->rope_h, rh.data(), rh.size() * sizeof(float2), hipMemcpyHostToDevice, s->st);
   if (e == hipSuccess) e = hipMemcpyAsync(s->rope_w, rw.data(), rw.size() * sizeof(float2), hipMemcpyHostToDevice, s->st);
@@ -427,16 +445,24 @@ sd_status sd_stream_set_context(sd_stream* s, const void* ctx_pos, const void* c
                         c.ctx_len, 2 * s->d, s->d, E));
     }
   if (s->fold) {
+    // the prompt K | V in fp32 (scratch: the FFN buffer, free between steps),
+    // folded into fp16 score / output matrices
     const int64_t ncol = (int64_t)s->H * s->ctx8, d = s->d;
+    float* kv = (float*)s->hid;
     for (int b = 0; b < s->nb; ++b)
       for (int ci = 0; ci < nctx; ++ci) {
         const int64_t bc = (int64_t)b * nctx + ci;
-        HIP_TRY(sdk::cross_fold(s->st, (const bf16*)P(s->ctxK, bc * per, s->es), (const bf16*)P(s->ctxVT, bc * per, s->es),
-                                (const bf16*)P(s->w.cq_w, (int64_t)b * d * d, s->es),
+        Epi E = epi_base(s, EPI_F32);
+        E.bias = P(s->w.ckv_b, (int64_t)b * 2 * d, s->es);
+        E.out = kv;
+        E.ldo = 2 * s->d;
+        HIP_TRY(sdk::gemm(s->st, s->bf, ci == 0 ? ctx_pos : ctx_neg, P(s->w.ckv_w, (int64_t)b * 2 * d * d, s->es),
+                          c.ctx_len, 2 * s->d, s->d, E));
+        HIP_TRY(sdk::cross_fold(s->st, kv, (const bf16*)P(s->w.cq_w, (int64_t)b * d * d, s->es),
                                 (const bf16*)P(s->w.cq_b, (int64_t)b * d, s->es),
                                 (const bf16*)P(s->w.co_w, (int64_t)b * d * d, s->es),
-                                (bf16*)Pm(s->fold_q, bc * ncol * d, s->es), s->fold_c + bc * ncol,
-                                (bf16*)Pm(s->fold_o, bc * d * ncol, s->es), s->d, s->H, s->hd, c.ctx_len, s->ctx8));
+                                (f16*)Pm(s->fold_q, bc * ncol * d, s->es), s->fold_c + bc * ncol,
+                                (f16*)Pm(s->fold_o, bc * d * ncol, s->es), s->d, s->H, s->hd, c.ctx_len, s->ctx8));
       }
   }
   s->ctx_set = true;
@@ -570,13 +596,16 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, int R_pos, int nn
        sdk::gemv(st, bf, s->sc, s->w.fin_w, s->w.fin_b, s->fmod, R, 2 * d, d, 0));
 
   // ---- patch embedding into the fp32 residual stream
-  PROF(SD_PROF_OTHER, 0.0, (4.0 + es) * R * s->lat,
-       sdk::patchify(st, bf, rt, s->fx, s->xm, s->lat, s->Tn, c.latent_c, c.latent_h, c.latent_w, c.patch));
+  // (bf16: hi + lo input pairs against the doubled weights, K = 2P)
+  const int KP = bf ? 2 * s->P : s->P;
+  PROF(SD_PROF_OTHER, 0.0, (4.0 + es * KP / s->P) * R * s->lat,
+       sdk::patchify(st, bf, rt, s->fx, s->xm, s->lat, s->Tn, c.latent_c, c.latent_h, c.latent_w, c.patch, bf));
   {
     Epi E = epi_base(s, EPI_PATCH);
     E.bias = s->w.pe_b;
     E.resid = s->resid;
-    PROF(SD_PROF_OTHER, gflop(M, d, s->P), gbytes(M, d, s->P, es, 4), sdk::gemm(st, bf, s->xm, s->w.pe_w, M, d, s->P, E));
+    PROF(SD_PROF_OTHER, gflop(M, d, KP), gbytes(M, d, KP, es, 4),
+         sdk::gemm(st, bf, s->xm, bf ? s->pe2 : s->w.pe_w, M, d, KP, E));
   }
 
   const int nctx = c.cfg_type != SD_CFG_SELF ? 2 : 1;
@@ -698,10 +727,10 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, int R_pos, int nn
     // cross-attention to the pre-computed prompt K/V
     if (c.ctx_len > 0 && s->fold) {
       PROF(SD_PROF_LN, 0.0, (4.0 + es) * M * d,
-           sdk::ln_mod(st, bf, s->resid, s->xm, M, d, L, nullptr, nullptr, 0, 0, 6 * d, 1e-6f));
+           sdk::ln_mod(st, bf, s->resid, s->xm, M, d, L, nullptr, nullptr, 0, 0, 6 * d, 1e-6f, sdk::LN_F16));
       const int ncol = H * s->ctx8;
       float* sc = (float*)s->hid;
-      bf16* pc = (bf16*)((char*)s->hid + (size_t)M * ncol * 4);
+      f16* pc = (f16*)((char*)s->hid + (size_t)M * ncol * 4);
       // rows [0, R_pos) read the positive context, [R_pos, R_pos + nneg) the negative one
       for (int part = 0; part < (nneg > 0 ? 2 : 1); ++part) {
         const int64_t t0 = (int64_t)(part == 0 ? 0 : R_pos) * L, Mp = (int64_t)(part == 0 ? R_pos : nneg) * L;
@@ -711,7 +740,7 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, int R_pos, int nn
           E.out = sc + t0 * ncol;
           E.ldo = ncol;
           PROF(SD_PROF_GEMM_CROSS, gflop(Mp, ncol, d), gbytes(Mp, ncol, d, es, 4),
-               sdk::gemm(st, bf, P(s->xm, t0 * d, es), P(s->fold_q, bc * ncol * d, es), (int)Mp, ncol, d, E));
+               sdk::gemm_mfma_f16(st, P(s->xm, t0 * d, es), P(s->fold_q, bc * ncol * d, es), (int)Mp, ncol, d, E));
         }
         PROF(SD_PROF_ATTN_CROSS, 4.0 * Mp * ncol, 6.0 * Mp * ncol,
              sdk::ctx_softmax(st, sc + t0 * ncol, s->fold_c + bc * ncol, pc + t0 * ncol, Mp, H, s->ctx8));
@@ -720,7 +749,7 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, int R_pos, int nn
           E.bias = P(s->w.co_b, (int64_t)b * d, es);
           E.resid = s->resid + t0 * d;
           PROF(SD_PROF_GEMM_CROSS, gflop(Mp, d, ncol), gbytes(Mp, d, ncol, es, 8),
-               sdk::gemm(st, bf, pc + t0 * ncol, P(s->fold_o, bc * d * ncol, es), (int)Mp, d, ncol, E));
+               sdk::gemm_mfma_f16(st, pc + t0 * ncol, P(s->fold_o, bc * d * ncol, es), (int)Mp, d, ncol, E));
         }
       }
     } else if (c.ctx_len > 0) {
@@ -808,12 +837,17 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, int R_pos, int nn
   }
 
   // ---- final layer and unpatchify -> eps_c
-  PROF(SD_PROF_LN, 0.0, (4.0 + es) * M * d, sdk::ln_mod(st, bf, s->resid, s->xm, M, d, L, s->fmod, nullptr, 0, d, 2 * d, 1e-6f));
+  // (bf16: the normalised rows as hi + lo pairs against the doubled head, K = 2d)
+  const int KH = bf ? 2 * d : d;
+  PROF(SD_PROF_LN, 0.0, (4.0 + es * KH / d) * M * d,
+       sdk::ln_mod(st, bf, s->resid, s->xm, M, d, L, s->fmod, nullptr, 0, d, 2 * d, 1e-6f,
+                   bf ? sdk::LN_SPLIT : sdk::LN_PLAIN));
   {
     Epi E = epi_base(s, EPI_HEAD);
     E.bias = s->w.head_b;
     E.eps = eps_out;
-    PROF(SD_PROF_OTHER, gflop(M, s->P, d), gbytes(M, s->P, d, es, 4), sdk::gemm(st, bf, s->xm, s->w.head_w, M, s->P, d, E));
+    PROF(SD_PROF_OTHER, gflop(M, s->P, KH), gbytes(M, s->P, KH, es, 4),
+         sdk::gemm(st, bf, s->xm, bf ? s->head2 : s->w.head_w, M, s->P, KH, E));
   }
   return SD_OK;
 }

@@ -269,9 +269,13 @@ def test_gemm_epi_and_ln_mod_reject_bad_arguments_before_any_device_call(lib):
     assert lib.sd_k_gemm_epi(8, 8, 128, 192, 64, C.byref(e), None) == L.SD_ERR_SHAPE    # position 4 not in table
     e = L.sd_gemm_epi(mode=L.SD_EPI_HEAD, bias=8, eps=8, L=64, C=4, p=2, T=1, Hp=8, Wp=8, Hl=16, Wl=15)
     assert lib.sd_k_gemm_epi(8, 8, 64, 16, 128, C.byref(e), None) == L.SD_ERR_SHAPE
-    assert lib.sd_k_ln_mod(1, 8, 8, 4, 5124, 1, None, None, 0, 0, 0, None) == L.SD_ERR_SHAPE
-    assert lib.sd_k_ln_mod(1, 8, 8, 4, 128, 1, 8, 8, 0, 700, 768, None) == L.SD_ERR_SHAPE
-    assert lib.sd_k_ln_mod(3, 8, 8, 4, 128, 1, None, None, 0, 0, 0, None) == L.SD_ERR_ARG
+    assert lib.sd_k_ln_mod(1, 8, 8, 4, 5124, 1, None, None, 0, 0, 0, 0, None) == L.SD_ERR_SHAPE
+    assert lib.sd_k_ln_mod(1, 8, 8, 4, 128, 1, 8, 8, 0, 700, 768, 0, None) == L.SD_ERR_SHAPE
+    assert lib.sd_k_ln_mod(3, 8, 8, 4, 128, 1, None, None, 0, 0, 0, 0, None) == L.SD_ERR_ARG
+    assert lib.sd_k_ln_mod(0, 8, 8, 4, 128, 1, None, None, 0, 0, 0, L.SD_LN_SPLIT, None) == L.SD_ERR_ARG
+    assert lib.sd_k_ln_mod(1, 8, 8, 4, 128, 1, 8, 8, 0, 128, 768, L.SD_LN_F16, None) == L.SD_ERR_ARG
+    e = L.sd_gemm_epi(mode=L.SD_EPI_GELU, out=8, ldo=64, f16=1)
+    assert lib.sd_k_gemm_epi(8, 8, 64, 64, 64, C.byref(e), None) == L.SD_ERR_ARG     # fp16: F32 / RESID only
 
 
 def test_rope_tables_are_cos_sin_of_the_section_angles(lib):

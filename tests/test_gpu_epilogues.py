@@ -203,7 +203,7 @@ def test_ln_mod_against_oracle(lib, M, d, Lr):
     out = torch.empty((M, d), dtype=torch.bfloat16, device=device())
     xd, md, bd = to_dev(x, torch.float32), to_dev(mod, torch.float32), to_dev(blk, torch.bfloat16)
     call(lib.sd_k_ln_mod(sdlib.SD_DTYPE_BF16, xd.data_ptr(), out.data_ptr(), M, d, Lr, md.data_ptr(), bd.data_ptr(),
-                         0, d, 6 * d, stream_ptr()))
+                         0, d, 6 * d, sdlib.SD_LN_PLAIN, stream_ptr()))
     torch.cuda.synchronize()
     got = out.float().cpu().numpy()
     m = mod.astype(np.float64)[np.arange(M) // Lr] + blk.astype(np.float64)
@@ -211,3 +211,62 @@ def test_ln_mod_against_oracle(lib, M, d, Lr):
     rms = np.sqrt(np.mean(ref * ref))
     excess = np.max(np.abs(got - ref) - 2.0 ** -8 * np.abs(ref)) / rms
     assert excess <= 1e-4, f"excess {excess:.3e}"
+
+
+@pytest.mark.parametrize("M,d", [(R * L, D), (L, 5120)])
+def test_ln_split_and_fp16_forms(lib, M, d):
+    """The head's input as hi + lo bf16 pairs (SD_LN_SPLIT, with the final
+    layer's (shift, scale) slots of a 2d vector) reconstructs the modulated
+    LayerNorm to fp32 accuracy; the cross-attention's fp16 input (SD_LN_F16,
+    no modulation) is within fp16 rounding (2^-11 relative)."""
+    print(f"ln split / f16 M={M} d={d}", flush=True)
+    rng = np.random.default_rng(d + 3 * M)
+    x = rng.standard_normal((M, d)).astype(np.float32) * 2 - 0.3
+    mod = (0.3 * rng.standard_normal((M // L, 2 * d))).astype(np.float32)
+    xd, md = to_dev(x, torch.float32), to_dev(mod, torch.float32)
+    ln = dit.layer_norm(x.astype(np.float64))
+    split = torch.empty((M, 2 * d), dtype=torch.bfloat16, device=device())
+    call(lib.sd_k_ln_mod(sdlib.SD_DTYPE_BF16, xd.data_ptr(), split.data_ptr(), M, d, L, md.data_ptr(), None, 0, d,
+                         2 * d, sdlib.SD_LN_SPLIT, stream_ptr()))
+    half = torch.empty((M, d), dtype=torch.float16, device=device())
+    call(lib.sd_k_ln_mod(sdlib.SD_DTYPE_BF16, xd.data_ptr(), half.data_ptr(), M, d, L, None, None, 0, 0, 0,
+                         sdlib.SD_LN_F16, stream_ptr()))
+    torch.cuda.synchronize()
+    m = mod.astype(np.float64)[np.arange(M) // L]
+    ref = dit.modulate(ln, m[:, :d], m[:, d:])
+    sp = split.float().cpu().numpy()
+    hi, lo = sp[:, :d].astype(np.float64), sp[:, d:].astype(np.float64)
+    # hi alone is the bf16 value (within its rounding of the reference)
+    assert np.all(np.abs(hi - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5 * np.sqrt(np.mean(ref * ref)))
+    rms = np.sqrt(np.mean(ref * ref))
+    e_split = np.max(np.abs(hi + lo - ref) - 2.0 ** -16 * np.abs(ref)) / rms
+    assert e_split <= 1e-5, f"split excess {e_split:.3e}"
+    h = half.float().cpu().numpy()
+    e_half = np.max(np.abs(h - ln) - 2.0 ** -11 * np.abs(ln)) / np.sqrt(np.mean(ln * ln))
+    assert e_half <= 1e-5, f"fp16 excess {e_half:.3e}"
+
+
+@pytest.mark.parametrize("M,N,K,mode", [(R * L, 960, D, "f32"), (R * L, D, 960, "resid"), (L, 3200, 5120, "f32"),
+                                        (L, 5120, 3200, "resid"), (300, 200, 136, "resid")])
+def test_fp16_gemm_exact_integers(lib, M, N, K, mode):
+    """The folded cross-attention's fp16 GEMMs (scores: N = heads x 80
+    prompt slots; output: K = heads x 80): k/16 operands are exact in fp16 as
+    in bf16, so the result is the integer arithmetic bit for bit."""
+    print(f"fp16 gemm {mode} M={M} N={N} K={K}", flush=True)
+    rng = np.random.default_rng(M + N + K)
+    ai = rng.integers(-8, 9, size=(M, K))
+    wi = rng.integers(-8, 9, size=(N, K))
+    bi = rng.integers(-8, 9, size=N)
+    A, W = to_dev(ai / 16.0, torch.float16), to_dev(wi / 16.0, torch.float16)
+    b = to_dev(bi / 16.0, torch.bfloat16)
+    ref = (ai.astype(np.float64) @ wi.T.astype(np.float64)) / 256.0 + bi / 16.0
+    if mode == "f32":
+        out = torch.empty((M, N), dtype=torch.float32, device=device())
+        e = sdlib.sd_gemm_epi(mode=sdlib.SD_EPI_F32, bias=b.data_ptr(), out=out.data_ptr(), ldo=N, f16=1)
+    else:
+        c0 = rng.integers(-4096, 4097, size=(M, N)) / 256.0
+        out = to_dev(c0, torch.float32)
+        e = sdlib.sd_gemm_epi(mode=sdlib.SD_EPI_RESID, bias=b.data_ptr(), resid=out.data_ptr(), f16=1)
+        ref = ref + c0
+    run(lib, A, W, M, N, K, e)
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), ref)
