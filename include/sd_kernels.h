@@ -143,6 +143,21 @@ sd_status sd_k_attention(int32_t dtype, const void* q, int64_t q_row_stride, int
                          int32_t nsplit, void* workspace, size_t workspace_bytes, void* stream);
 size_t sd_k_attention_workspace_bytes(int32_t R, int32_t H, int32_t L, int32_t hd, int32_t nsplit);
 
+/* sd_k_attention without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The split partials use a fixed array of
+ * SD_ATTENTION_NOALLOC_SCRATCH_BYTES (128 MiB) in the library's code object,
+ * one per device, held until the process ends; the call allocates nothing.
+ * A split whose sd_k_attention_workspace_bytes() exceeds that size returns
+ * SD_ERR_WORKSPACE before any HIP call.  Results equal sd_k_attention's with
+ * the same arguments.  Calls that overlap on one device (different streams,
+ * threads or processes' kernels in flight together) share the array and
+ * race; calls ordered on one stream do not. */
+#define SD_ATTENTION_NOALLOC_SCRATCH_BYTES (128u << 20)
+sd_status sd_k_attention_noalloc(int32_t dtype, const void* q, int64_t q_row_stride, int64_t q_head_stride, void* o,
+                                 int32_t R, int32_t H, int32_t L, int32_t hd, int32_t nseg,
+                                 const sd_kv_segment* segs, int32_t nsplit, void* stream);
+
 /* Exact int64 sums (sum a*b, sum a*a, sum b*b) of two frames: kind SD_SSF_U8
  * (uint8) or SD_SSF_LATENT (fp32 quantised to rint(x*2^12) clamped to +-2^20).
  * out_dev is a device int64[3].  StreamDiffusion paper notes, section 3 (SSF). */

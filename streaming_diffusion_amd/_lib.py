@@ -17,6 +17,7 @@ SD_ABI_VERSION = 4
 SD_MAX_SLOTS = 8
 SD_MAX_ROWS = 40
 SD_MAX_SINK = 8
+SD_ATTENTION_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 SD_OK, SD_ERR_ARG, SD_ERR_SHAPE, SD_ERR_STATE, SD_ERR_WORKSPACE, SD_ERR_HIP, SD_ERR_NOT_READY = 0, -1, -2, -3, -4, -5, -6
 STATUS_NAMES = {0: "SD_OK", -1: "SD_ERR_ARG", -2: "SD_ERR_SHAPE", -3: "SD_ERR_STATE", -4: "SD_ERR_WORKSPACE",
@@ -153,6 +154,9 @@ SIGNATURES = {
                                  C.c_int32, C.c_int32, C.c_int32, C.POINTER(sd_kv_segment), C.c_int32, C.c_void_p,
                                  C.c_size_t, C.c_void_p]),
     "sd_k_attention_workspace_bytes": (C.c_size_t, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32]),
+    "sd_k_attention_noalloc": (C.c_int, [C.c_int32, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int32,
+                                         C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.POINTER(sd_kv_segment),
+                                         C.c_int32, C.c_void_p]),
     "sd_k_ssf_sums": (C.c_int, [C.c_int32, C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]),
     "sd_k_motion_sums": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_int64, C.c_void_p, C.c_void_p]),
     "sd_k_conv3d": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,

@@ -1,6 +1,7 @@
 // sd_k_* : single-kernel entry points (see include/sd_kernels.h).
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/sd_kernels.h"
 #include "kernels.h"
@@ -180,20 +181,19 @@ size_t sd_k_attention_workspace_bytes(int32_t R, int32_t H, int32_t L, int32_t h
   return part_o_bytes(R, H, L, hd, nsplit) + (size_t)nsplit * R * H * L * 8;
 }
 
-sd_status sd_k_attention(int32_t dtype, const void* q, int64_t q_row_stride, int64_t q_head_stride, void* o,
-                         int32_t R, int32_t H, int32_t L, int32_t hd, int32_t nseg, const sd_kv_segment* segs,
-                         int32_t nsplit, void* workspace, size_t workspace_bytes, void* stream) {
+// Validation and argument packing shared by the attention entry points; no
+// HIP call.  The split partials are attached by the caller.
+static sd_status attention_prepare(int32_t dtype, const void* q, int64_t q_row_stride, int64_t q_head_stride,
+                                   void* o, int32_t R, int32_t H, int32_t L, int32_t hd, int32_t nseg,
+                                   const sd_kv_segment* segs, int32_t nsplit, sdk::AttnArgs* out, bool* bf_out) {
   if (nsplit < 1 || nsplit > 64) return SD_ERR_ARG;
-  if (nsplit > 1) {
-    if (dtype != SD_DTYPE_BF16 || !workspace || ((uintptr_t)workspace & 255)) return SD_ERR_ARG;
-    if (workspace_bytes < sd_k_attention_workspace_bytes(R, H, L, hd, nsplit)) return SD_ERR_WORKSPACE;
-  }
+  if (nsplit > 1 && dtype != SD_DTYPE_BF16) return SD_ERR_ARG;
   if (dtype != SD_DTYPE_F32 && dtype != SD_DTYPE_BF16) return SD_ERR_ARG;
   if (!q || !o || !segs || nseg < 1 || nseg > 3 || R < 0 || H < 1 || L < 0) return SD_ERR_ARG;
   const bool bf = dtype == SD_DTYPE_BF16;
   if (bf && hd != 32 && hd != 64 && hd != 128) return SD_ERR_SHAPE;
   if (!bf && hd != 16 && hd != 32 && hd != 64 && hd != 128) return SD_ERR_SHAPE;
-  sdk::AttnArgs a;
+  sdk::AttnArgs& a = *out;
   std::memset(&a, 0, sizeof(a));
   a.q = q;
   a.q_rs = q_row_stride;
@@ -215,24 +215,91 @@ sd_status sd_k_attention(int32_t dtype, const void* q, int64_t q_row_stride, int
     if (g.wrap && g.count > g.cap) return SD_ERR_SHAPE;
     if (bf && (g.cap % 8 || g.start % 8 || (g.wrap && g.count % 8))) return SD_ERR_SHAPE;
     if (bf && !g.wrap && g.start + ((g.count + 7) & ~7) > g.cap) return SD_ERR_SHAPE;
-    sdk::KvSeg& s = a.seg[i];
-    s.k = g.k;
-    s.vt = g.vt;
-    s.k_hs = g.k_head_stride;
-    s.vt_hs = g.vt_head_stride;
-    s.k_rs = g.k_row_stride;
-    s.vt_rs = g.vt_row_stride;
-    s.cap = g.cap;
-    s.start = g.start;
-    s.count = g.count;
-    s.wrap = g.wrap;
+    sdk::KvSeg& sg = a.seg[i];
+    sg.k = g.k;
+    sg.vt = g.vt;
+    sg.k_hs = g.k_head_stride;
+    sg.vt_hs = g.vt_head_stride;
+    sg.k_rs = g.k_row_stride;
+    sg.vt_rs = g.vt_row_stride;
+    sg.cap = g.cap;
+    sg.start = g.start;
+    sg.count = g.count;
+    sg.wrap = g.wrap;
   }
   a.nsplit = nsplit;
+  *bf_out = bf;
+  return SD_OK;
+}
+
+static void attach_partials(sdk::AttnArgs& a, void* workspace) {
+  if (a.nsplit < 2) return;
+  a.part_o = (bf16*)workspace;
+  a.part_ml = (float2*)((char*)workspace + part_o_bytes(a.R, a.H, a.L, a.hd, a.nsplit));
+  a.part_so = (long long)a.R * a.L * a.H * a.hd;
+  a.part_sml = (long long)a.R * a.H * a.L;
+}
+
+sd_status sd_k_attention(int32_t dtype, const void* q, int64_t q_row_stride, int64_t q_head_stride, void* o,
+                         int32_t R, int32_t H, int32_t L, int32_t hd, int32_t nseg, const sd_kv_segment* segs,
+                         int32_t nsplit, void* workspace, size_t workspace_bytes, void* stream) {
+  if (nsplit < 1 || nsplit > 64) return SD_ERR_ARG;
   if (nsplit > 1) {
-    a.part_o = (bf16*)workspace;
-    a.part_ml = (float2*)((char*)workspace + part_o_bytes(R, H, L, hd, nsplit));
-    a.part_so = (long long)R * L * H * hd;
-    a.part_sml = (long long)R * H * L;
+    if (dtype != SD_DTYPE_BF16 || !workspace || ((uintptr_t)workspace & 255)) return SD_ERR_ARG;
+    if (workspace_bytes < sd_k_attention_workspace_bytes(R, H, L, hd, nsplit)) return SD_ERR_WORKSPACE;
+  }
+  sdk::AttnArgs a;
+  bool bf = false;
+  const sd_status st = attention_prepare(dtype, q, q_row_stride, q_head_stride, o, R, H, L, hd, nseg, segs, nsplit,
+                                         &a, &bf);
+  if (st != SD_OK) return st;
+  attach_partials(a, workspace);
+  return sdk::attention((hipStream_t)stream, bf, a) == hipSuccess ? SD_OK : SD_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free attention.  The split partials live in `scratch`, a
+// fixed-size array in the code object (each device that loads the library
+// holds its own copy until the process ends).  Host code never passes the
+// array's name to a kernel: that is a host-side stand-in.  The device address
+// of each device's copy is looked up once, with that device current, and
+// kept per device.  Every split partial is written before the combine reads
+// it, so nothing needs clearing between calls.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[SD_ATTENTION_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// device address of this device's scratch copy (nullptr on failure)
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+sd_status sd_k_attention_noalloc(int32_t dtype, const void* q, int64_t q_row_stride, int64_t q_head_stride, void* o,
+                                 int32_t R, int32_t H, int32_t L, int32_t hd, int32_t nseg,
+                                 const sd_kv_segment* segs, int32_t nsplit, void* stream) {
+  sdk::AttnArgs a;
+  bool bf = false;
+  const sd_status st = attention_prepare(dtype, q, q_row_stride, q_head_stride, o, R, H, L, hd, nseg, segs, nsplit,
+                                         &a, &bf);
+  if (st != SD_OK) return st;
+  if (nsplit > 1) {
+    if (sd_k_attention_workspace_bytes(R, H, L, hd, nsplit) > (size_t)SD_ATTENTION_NOALLOC_SCRATCH_BYTES)
+      return SD_ERR_WORKSPACE;
+    void* ws = device_scratch();
+    if (!ws) return SD_ERR_HIP;
+    attach_partials(a, ws);
   }
   return sdk::attention((hipStream_t)stream, bf, a) == hipSuccess ? SD_OK : SD_ERR_HIP;
 }

@@ -298,3 +298,16 @@ def test_rope_tables_are_cos_sin_of_the_section_angles(lib):
                 ref.append((np.cos(th), np.sin(th)))
     ref = np.array(ref, np.float32)
     assert np.all(np.abs(got - ref) <= np.spacing(np.abs(ref)))
+
+
+def test_attention_noalloc_rejects_before_any_device_call(lib):
+    seg = L.sd_kv_segment(k=8, vt=8, cap=64, start=0, count=64, wrap=0)
+    # 8 splits of 2 rows x 12 heads x 3120 queries x hd 128 need more than the fixed scratch
+    need = lib.sd_k_attention_workspace_bytes(2, 12, 3120, 128, 8)
+    assert need > L.SD_ATTENTION_NOALLOC_SCRATCH_BYTES
+    assert lib.sd_k_attention_noalloc(1, 8, 0, 0, 8, 2, 12, 3120, 128, 1, C.byref(seg), 8, None) == L.SD_ERR_WORKSPACE
+    assert lib.sd_k_attention_noalloc(0, 8, 0, 0, 8, 1, 1, 8, 64, 1, C.byref(seg), 2, None) == L.SD_ERR_ARG   # fp32 split
+    assert lib.sd_k_attention_noalloc(1, 8, 0, 0, 8, 1, 1, 8, 48, 1, C.byref(seg), 1, None) == L.SD_ERR_SHAPE
+    assert lib.sd_k_attention_noalloc(1, None, 0, 0, 8, 1, 1, 8, 64, 1, C.byref(seg), 1, None) == L.SD_ERR_ARG
+    # the video step's own split (5 splits, 2 rows) fits
+    assert lib.sd_k_attention_workspace_bytes(2, 12, 3120, 128, 5) <= L.SD_ATTENTION_NOALLOC_SCRATCH_BYTES
