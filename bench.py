@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--chunks", type=int, default=1, help="B: chunks entering (and leaving) per step")
     ap.add_argument("--batch-attn", action="store_true",
                     help="cross-frame batch attention: every row attends to the own tokens of all rows")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step as a captured HIP graph (the library runs on its own stream)")
     ap.add_argument("--io-stream", action="store_true",
                     help="pushes on a second stream (the IO queue), overlapped with the previous step's forward")
     ap.add_argument("--kv-recompute", action="store_true",
@@ -145,7 +147,14 @@ def cpu_baseline(cfg, n_blocks_sample: int):
     }
 
 
-def measure(cfg, weights, steps: int, warmup: int, dev, io_stream: bool = False):
+def dominant_kind(cfg):
+    """The kernel kind that bounds the step: self-attention at the video
+    chunk sizes (MFMA-bound); below the roofline knee the FFN's second GEMM,
+    which streams the largest weight matrix per launch (HBM-bound)."""
+    return "gemm_ffn2" if cfg.tokens * cfg.rows_per_step <= 256 else "attn_self"
+
+
+def measure(cfg, weights, steps: int, warmup: int, dev, io_stream: bool = False, graph: bool = False):
     """Warm up (fills the slots, the window and the sink), time `steps` steps
     with the inputs resident in device memory, then one untimed step with
     every kernel kind timed.  Returns the bench record without the CPU leg."""
@@ -154,7 +163,10 @@ def measure(cfg, weights, steps: int, warmup: int, dev, io_stream: bool = False)
     from streaming_diffusion_amd.runner import StreamRunner
     from workloads import gen
 
-    run = StreamRunner(cfg, weights)
+    run = StreamRunner(cfg, weights, stream=torch.cuda.Stream() if graph else None)
+    if graph:
+        torch.cuda.synchronize()
+        run.set_graph(True)
     if io_stream:
         run.set_io_stream(torch.cuda.Stream())        # inputs below are resident before the timed region
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
@@ -163,7 +175,7 @@ def measure(cfg, weights, steps: int, warmup: int, dev, io_stream: bool = False)
         ctx_neg = torch.from_numpy(gen.make_context(cfg, True)).to(dev).to(tdt) if cfg.cfg_type != "self" else None
         run.set_context(ctx, ctx_neg)
     B = cfg.chunks_per_step
-    total = (warmup + steps + 2) * B
+    total = (warmup + (2 if graph else 1) * steps + 2) * B
     src, nz = gen.LatentSource(cfg), gen.NoiseSource(cfg)
     xs = [torch.from_numpy(src.next()).to(dev) for _ in range(total)]
     ns = [torch.from_numpy(gen.frame_noise(cfg, nz)).to(dev) for _ in range(total)]
@@ -195,9 +207,13 @@ def measure(cfg, weights, steps: int, warmup: int, dev, io_stream: bool = False)
             ttff_ms = (time.perf_counter() - t_first) * 1e3
     torch.cuda.synchronize()
 
-    # timed region: the dominant kernel (self-attention) is timed live with events
-    run.profile(["attn_self"])
-    run.profile_read()
+    # timed region: the dominant kernel is timed live with events (with graph
+    # replay, live events would turn replay off: it is timed over as many
+    # extra launched steps right after)
+    dom_kind = dominant_kind(cfg)
+    if not graph:
+        run.profile([dom_kind])
+        run.profile_read()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     emitted = 0
@@ -207,7 +223,15 @@ def measure(cfg, weights, steps: int, warmup: int, dev, io_stream: bool = False)
         emitted += info.n_out * cfg.latent_t
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    attn = run.profile_read().get("attn_self")
+    if graph:
+        graph_stats = run.graph_stats()
+        run.profile([dom_kind])
+        run.profile_read()
+        for _ in range(steps):
+            push_group()
+            run.step(out)
+        torch.cuda.synchronize()
+    attn = run.profile_read().get(dom_kind)
     elapsed = t1 - t0
     ms_per_step = elapsed / steps * 1e3
 
@@ -220,7 +244,7 @@ def measure(cfg, weights, steps: int, warmup: int, dev, io_stream: bool = False)
     run.close()
 
     roofline = None
-    if attn and attn["launches"]:
+    if attn and attn["launches"] and dom_kind == "attn_self":
         per_launch_ms = attn["ms"] / attn["launches"]
         per_launch_flop = attn["flops"] / attn["launches"]
         achieved = per_launch_flop / (per_launch_ms * 1e-3) / 1e12
@@ -230,6 +254,18 @@ def measure(cfg, weights, steps: int, warmup: int, dev, io_stream: bool = False)
                     "traffic": measured_traffic(),
                     "avg_launch_ms": round(per_launch_ms, 4), "flop_per_launch": per_launch_flop,
                     "algorithmic_bytes_per_launch": attn["bytes"] / attn["launches"],
+                    "launches": attn["launches"]}
+    elif attn and attn["launches"]:
+        # below the knee: the FFN GEMMs stream the largest weights; bytes per
+        # launch = W + A + the output pass (algorithmic), over the launch time
+        per_launch_ms = attn["ms"] / attn["launches"]
+        per_launch_bytes = attn["bytes"] / attn["launches"]
+        achieved = per_launch_bytes / (per_launch_ms * 1e-3) / 1e9
+        roofline = {"kernel": f"{dom_kind}: gemm_wstream_kernel + gemm_reduce_kernel (weight-streaming GEMM, "
+                              f"K split over the CUs)",
+                    "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "avg_launch_ms": round(per_launch_ms, 4), "algorithmic_bytes_per_launch": per_launch_bytes,
                     "launches": attn["launches"]}
     bd = {}
     for name, v in breakdown.items():
@@ -262,8 +298,9 @@ def measure(cfg, weights, steps: int, warmup: int, dev, io_stream: bool = False)
                                + (", clean-latent KV recompute" if cfg.kv_recompute else ""),
                    "rows_per_step": cfg.rows_per_step, "tokens_per_row": cfg.tokens,
                    "frames_per_step": B * cfg.latent_t, "parallelism": "single GPU",
-                   "io_stream": bool(io_stream)},
+                   "io_stream": bool(io_stream), "graph": bool(graph)},
         "ttff_ms": round(ttff_ms, 2) if ttff_ms else None,
+        "graph": {"captures": graph_stats[0], "replays": graph_stats[1]} if graph else None,
         "roofline": roofline,
         "breakdown_one_step": bd,
     }
@@ -487,7 +524,7 @@ def main():
         return
     cfg = get_config(args.workload, t_index=slot_indices(args.n_slots), chunks_per_step=args.chunks, **kw)
     weights = random_device_weights(cfg, seed=gen.SEED_WEIGHTS)
-    res = measure(cfg, weights, args.steps, args.warmup, dev, args.io_stream)
+    res = measure(cfg, weights, args.steps, args.warmup, dev, args.io_stream, args.graph)
     if args.calibrate_copy:
         n = args.calibrate_copy << 18          # float32 elements in MIB MiB
         a = torch.ones(n, dtype=torch.float32, device=dev)

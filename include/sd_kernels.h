@@ -72,6 +72,9 @@ typedef struct {
   float* eps;                  /* HEAD: fp32 [M/L][T][C][Hl][Wl] */
   int32_t C, Hl, Wl, p, T;     /* HEAD: latent geometry and patch (Hl = Hp*p, Wl = Wp*p, L = T*Hp*Wp) */
   int32_t f16;                 /* A and W are IEEE fp16 (F32 and RESID only; bias stays bf16) */
+  void* workspace;             /* optional device scratch (256-byte aligned): with M <= 256 the
+                                  product is split over K into fp32 partials held here */
+  size_t workspace_bytes;
 } sd_gemm_epi;
 
 /* One bf16 GEMM with the epilogue e->mode, on the kernels and launch

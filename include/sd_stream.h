@@ -217,6 +217,24 @@ sd_status sd_stream_push_frame(sd_stream* s, const float* x0, const float* noise
  * switching queues first waits for the old one. */
 sd_status sd_stream_set_io_stream(sd_stream* s, void* io_stream);
 
+/* Graph replay of the step (StreamDiffusion project intro and StreamDiffusionV2
+ * summary, system-level co-design: the denoising loop runs as one launch
+ * sequence that the host re-issues every step).  With enable != 0, the forward
+ * and the latent update of a step are captured once as a HIP graph and then
+ * replayed: the values that change from step to step (the rows, their RoPE
+ * bases, the window range, the ring positions of the appends) are written to
+ * device memory by one small kernel first and read there by the kernels, so
+ * a replay launches the whole step at once.  A graph is recorded per launch
+ * sequence (rows, exits, sink state, window fill, output buffer); up to four
+ * are kept.  Applies to bf16 configurations without kv_recompute, with no IO
+ * queue set and no live profiling (otherwise the step is launched as usual);
+ * needs a created stream (SD_ERR_STATE on the null stream).  Results equal
+ * those of the launched step.  enable == 0 (the default) waits for the stream
+ * and frees the graphs. */
+sd_status sd_stream_set_graph(sd_stream* s, int32_t enable);
+/* Steps that recorded a new graph and steps that replayed one. */
+sd_status sd_stream_graph_stats(sd_stream* s, int64_t* captures, int64_t* replays);
+
 /* Advance the pipeline by one denoising step (Stream Batch: the B oldest
  * pending chunks enter slot 0, every slot advances one timestep, the slot
  * group in the last slot leaves).  SD_ERR_NOT_READY while fewer than B chunks

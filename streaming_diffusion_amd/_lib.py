@@ -100,7 +100,7 @@ class sd_gemm_epi(C.Structure):
                 ("rope", C.c_int32), ("Hp", C.c_int32), ("Wp", C.c_int32), ("rope_table", C.c_void_p),
                 ("rope_positions", C.c_int32), ("t0", C.c_int32 * SD_MAX_ROWS), ("eps", C.c_void_p),
                 ("C", C.c_int32), ("Hl", C.c_int32), ("Wl", C.c_int32), ("p", C.c_int32), ("T", C.c_int32),
-                ("f16", C.c_int32)]
+                ("f16", C.c_int32), ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t)]
 
 
 SD_LN_PLAIN, SD_LN_F16, SD_LN_SPLIT = 0, 1, 2
@@ -131,6 +131,8 @@ SIGNATURES = {
     "sd_stream_push_frame": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_double,
                                        C.POINTER(sd_push_info)]),
     "sd_stream_set_io_stream": (C.c_int, [C.c_void_p, C.c_void_p]),
+    "sd_stream_set_graph": (C.c_int, [C.c_void_p, C.c_int32]),
+    "sd_stream_graph_stats": (C.c_int, [C.c_void_p, C.POINTER(C.c_int64), C.POINTER(C.c_int64)]),
     "sd_stream_step": (C.c_int, [C.c_void_p, C.c_void_p, C.POINTER(sd_step_info)]),
     "sd_stream_step_chunks": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.POINTER(sd_step_info)]),
     "sd_stream_kv_reset": (C.c_int, [C.c_void_p]),

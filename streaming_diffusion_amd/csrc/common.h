@@ -72,6 +72,19 @@ struct RowTable {
   RowInfo r[SD_MAX_ROWS];
 };
 
+// Everything of a forward that changes from step to step while the launch
+// sequence stays the same: the rows, their RoPE bases, the self-attention's
+// sink / window ranges and the ring positions of the leaving chunks' appends.
+// Written to device memory by one small kernel before the forward, so that a
+// captured graph of the forward can be replayed with new values.
+struct StepDyn {
+  RowTable rt;
+  int32_t t0[SD_MAX_ROWS];
+  int32_t seg[4];                 // sink start, sink count, window start, window count
+  int32_t kv_pos[SD_MAX_CHUNKS];  // ring position of leaving chunk k's append
+  int32_t ptr_old;                // ring position of the first leaving chunk
+};
+
 // GEMM epilogue modes: C[m][n] = sum_k A[m][k] * W[n][k], then:
 enum EpiMode {
   EPI_STORE = 0,      // out[m][n] = T(acc + bias[n])
@@ -111,7 +124,13 @@ struct Epi {
   const float2* rope_h; // [Hp][dh/2]
   const float2* rope_w; // [Wp][dw/2]
   int t0[SD_MAX_ROWS];
+  const int* t0_dev;    // when set, the RoPE bases are read from device memory instead of t0
   // EPI_HEAD
   float* eps;           // [R][T][C][Hl][Wl]
   int C, Hl, Wl, p, T;
+  // split over K for few rows: fp32 partials [ksplit][M][N] (capacity
+  // part_cap floats; null: no split); ksplit is set by the dispatch
+  float* part;
+  int64_t part_cap;
+  int ksplit;
 };

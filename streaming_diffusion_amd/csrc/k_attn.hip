@@ -133,8 +133,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 
   // segments of this (row, head) as plain scalars, uniform over the
   // workgroup (unused segments have no keys)
-  const int c0 = a.nseg > 0 ? a.seg[0].count : 0;
-  const int c1 = a.nseg > 1 ? a.seg[1].count : 0;
+  const int* const dyn = a.dyn_seg;
+  const int c0 = a.nseg > 0 ? (dyn ? dyn[1] : a.seg[0].count) : 0;
+  const int c1 = a.nseg > 1 ? (dyn ? dyn[3] : a.seg[1].count) : 0;
   const int c2 = a.nseg > 2 ? a.seg[2].count : 0;
   const int nt0 = (c0 + KB - 1) / KB, nt1 = (c1 + KB - 1) / KB, nt2 = (c2 + KB - 1) / KB;
   const int NT_all = nt0 + nt1 + nt2;
@@ -147,7 +148,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   const bf16* const vbase1 = (const bf16*)a.seg[1].vt + (int64_t)r * a.seg[1].vt_rs + (int64_t)h * a.seg[1].vt_hs;
   const bf16* const vbase2 = (const bf16*)a.seg[2].vt + (int64_t)r * a.seg[2].vt_rs + (int64_t)h * a.seg[2].vt_hs;
   const int cap0 = a.seg[0].cap, cap1 = a.seg[1].cap, cap2 = a.seg[2].cap;
-  const int st0 = a.seg[0].start, st1 = a.seg[1].start, st2 = a.seg[2].start;
+  const int st0 = dyn ? dyn[0] : a.seg[0].start, st1 = dyn ? dyn[2] : a.seg[1].start, st2 = a.seg[2].start;
   const int wr0 = a.seg[0].wrap, wr1 = a.seg[1].wrap, wr2 = a.seg[2].wrap;
 
   // tile t -> its segment's bases, the position of its first key, the

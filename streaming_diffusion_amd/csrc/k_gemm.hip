@@ -67,7 +67,7 @@ SD_DEV void epi_apply(const Epi& E, int m, int n, int N, float acc, float partne
         const int f = t / hw, y = (t / E.Wp) % E.Hp, x = t % E.Wp;
         float2 cs;
         if (e < E.dt)
-          cs = E.rope_t[(E.t0[r] + f) * (E.dt >> 1) + (e >> 1)];
+          cs = E.rope_t[((E.t0_dev ? E.t0_dev[r] : E.t0[r]) + f) * (E.dt >> 1) + (e >> 1)];
         else if (e < E.dt + E.dh)
           cs = E.rope_h[y * (E.dh >> 1) + ((e - E.dt) >> 1)];
         else

@@ -12,6 +12,7 @@
 // layouts (8 consecutive head-dim elements of one token, RoPE applied to the
 // pairs in registers) and the transposed V layout (8 consecutive tokens of one
 // head-dim element).
+#include <algorithm>
 #include <cmath>
 
 #include <type_traits>
@@ -417,7 +418,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_kernel(const bf16* __restri
   if constexpr (MODE == EPI_QKV) {
     if (tid == 0) {
 #pragma unroll
-      for (int i = 0; i < SD_MAX_ROWS; ++i) t0s[i] = E.t0[i];
+      for (int i = 0; i < SD_MAX_ROWS; ++i) t0s[i] = E.t0_dev ? E.t0_dev[i] : E.t0[i];
     }
   }
   // One register stage, two LDS stages: the loads of k-tile t+1 are issued
@@ -593,7 +594,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restric
   if constexpr (MODE == EPI_QKV) {
     if (tid == 0) {
 #pragma unroll
-      for (int i = 0; i < SD_MAX_ROWS; ++i) t0s[i] = E.t0[i];
+      for (int i = 0; i < SD_MAX_ROWS; ++i) t0s[i] = E.t0_dev ? E.t0_dev[i] : E.t0[i];
     }
   }
   const int KT = K / BK;
@@ -650,6 +651,60 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restric
   }
 }
 
+// Second pass of a split over K: a 64-row x 32-column strip sums the slices'
+// partials in slice order (fixed, so results do not depend on scheduling)
+// and runs the epilogue of MODE on the sum.
+template <int MODE>
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(int M, int N, Epi E) {
+  constexpr int BN = 32, NT = 256, LC = BN + 4;
+  __shared__ __attribute__((aligned(16))) float stg[64 * LC];
+  __shared__ int4 rowtab[64];
+  __shared__ int t0s[SD_MAX_ROWS];
+  const int tid = threadIdx.x;
+  const int tiles_n = (N + BN - 1) / BN;
+  const int m_base = (blockIdx.x / tiles_n) * 64, n0 = (blockIdx.x % tiles_n) * BN;
+  if constexpr (MODE == EPI_QKV) {
+    if (tid < SD_MAX_ROWS) t0s[tid] = E.t0_dev ? E.t0_dev[tid] : E.t0[tid];
+  }
+  // 64 x 32 floats = 512 float4: two per thread
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int idx = tid + h * NT;
+    const int row = idx / (BN / 4), c4 = idx % (BN / 4);
+    const int m = m_base + row, n = n0 + c4 * 4;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (m < M && n < N) {
+      const float* src = E.part + (int64_t)m * N + n;
+      const int64_t st = (int64_t)M * N;
+      int sl = 0;
+      for (; sl + 4 <= E.ksplit; sl += 4) {
+        float4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = *(const float4*)(src + (sl + u) * st);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          acc.x += v[u].x;
+          acc.y += v[u].y;
+          acc.z += v[u].z;
+          acc.w += v[u].w;
+        }
+      }
+      for (; sl < E.ksplit; ++sl) {
+        const float4 v = *(const float4*)(src + sl * st);
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+      }
+    }
+    *(float4*)(stg + row * LC + c4 * 4) = acc;
+  }
+  __syncthreads();
+  epi_rows<MODE>(E, rowtab, m_base, M, tid, t0s);
+  __syncthreads();
+  epi_strip<BN, NT, MODE>(E, stg, LC, m_base, n0, M, N, tid, rowtab);
+}
+
 // compute units of the current device (queried once; 256 on MI355X)
 static int device_cus() {
   static int cus = 0;
@@ -671,6 +726,171 @@ hipError_t launch_dma(hipStream_t s, const bf16* A, const bf16* W, int M, int N,
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Weight-streaming product for few rows (one tile of up to 128 rows), the
+// regime below the knee where reading W from HBM bounds the GEMM.  C^T = W A^T
+// per workgroup tile of 128 output features x 128 rows over one K slice of
+// KT k-tiles of 64: at kernel start every wave issues its share of the W slice
+// (global -> LDS DMA, KT stages of [128][64] in the swizzled layout of the
+// DMA GEMM) and its own 32 rows of A straight into registers (the MFMA B
+// operand), so the whole slice is in flight at once -- one memory round trip
+// per workgroup instead of one per k-tile.  After one wait the 4 x 4 KT
+// products of each wave run from registers and LDS.  A split over K
+// (E.ksplit > 1) leaves fp32 partials for gemm_reduce_kernel; otherwise the
+// epilogue of MODE runs on 64-row strips as in the DMA GEMM.
+template <int KT, int MODE, bool H16>
+__global__ __launch_bounds__(256) void gemm_wstream_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
+                                                           int M, int N, int K, Epi E) {
+  constexpr int BN = 128, BK = 64, NT = 256, LC = BN + 4;
+  constexpr int STAGE = BN * BK;                          // bf16 elements per k-tile of W
+  constexpr int SMEM_BYTES = (KT * STAGE * 2 > 64 * LC * 4) ? KT * STAGE * 2 : 64 * LC * 4;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[SMEM_BYTES + 64 * 16 + SD_MAX_ROWS * 4];
+  bf16* const ws = (bf16*)lds;
+  int4* const rowtab = (int4*)(lds + SMEM_BYTES);
+  int* const t0s = (int*)(lds + SMEM_BYTES + 64 * 16);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ks = E.ksplit > 1 ? E.ksplit : 1;
+  const int tiles_n = (N + BN - 1) / BN;
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int slice = lid % ks, tile = lid / ks;
+  const int n0 = (tile % tiles_n) * BN, m0 = (tile / tiles_n) * 128;
+  const int kbase = slice * KT * BK;                      // dispatch: K = ks * KT * 64
+  // W slice: per k-tile 16 DMA blocks of 8 rows x 128 bytes, 4 per wave
+  {
+    const int lrow = lane >> 3, lpos = lane & 7;
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = (wave * 4 + q) * 8 + lrow;
+        const uint32_t src = (uint32_t)min(n0 + r, N - 1) * (uint32_t)K + (uint32_t)(kbase + t * BK + (lpos ^ swz<BK>(r)) * 8);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(W + src),
+                                         (__attribute__((address_space(3))) void*)(ws + t * STAGE + (wave * 4 + q) * 8 * BK),
+                                         16, 0, 0);
+      }
+  }
+  // A rows of this wave: B-operand fragments, lane (token l % 32, half l / 32)
+  const int lr = lane & 31, lh = lane >> 5;
+  bf16x8 af[4 * KT];
+  {
+    const bf16* arow = A + (int64_t)min(m0 + wave * 32 + lr, M - 1) * K + kbase + lh * 8;
+#pragma unroll
+    for (int j = 0; j < 4 * KT; ++j) af[j] = *(const bf16x8*)(arow + j * 16);
+  }
+  if constexpr (MODE == EPI_QKV) {
+    if (tid < SD_MAX_ROWS) t0s[tid] = E.t0_dev ? E.t0_dev[tid] : E.t0[tid];
+  }
+  f32x16 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[i][q] = 0.f;
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+  for (int t = 0; t < KT; ++t) {
+    const bf16* st = ws + t * STAGE;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int c = kk * 2 + lh;
+      bf16x8 wf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = i * 32 + lr;
+        wf[i] = *(const bf16x8*)(st + row * BK + ((c ^ swz<BK>(row)) * 8));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = mfma32<H16>(wf[i], af[t * 4 + kk], acc[i]);
+    }
+  }
+  __syncthreads();
+  // C^T fragments -> [token][feature] strips of 64 tokens in LDS: lane l of
+  // wave w holds token 32 w + l % 32, features 32 i + 8 (q / 4) + 4 (l / 32) + q % 4
+  float* stg = (float*)lds;
+#pragma unroll
+  for (int sidx = 0; sidx < 2; ++sidx) {
+    if ((wave >> 1) == sidx) {
+      const int row = (wave & 1) * 32 + lr;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) stg[row * LC + i * 32 + 8 * (q >> 2) + 4 * lh + (q & 3)] = acc[i][q];
+    }
+    __syncthreads();
+    const int mb = m0 + sidx * 64;
+    if (ks > 1) {
+      float* dst = E.part + (int64_t)slice * M * N;
+      for (int idx = tid; idx < 64 * (BN / 4); idx += NT) {
+        const int row = idx / (BN / 4), c4 = idx % (BN / 4);
+        const int m = mb + row, n = n0 + c4 * 4;
+        if (m < M && n < N) *(float4*)(dst + (int64_t)m * N + n) = *(const float4*)(stg + row * LC + c4 * 4);
+      }
+    } else {
+      epi_rows<MODE>(E, rowtab, mb, M, tid, t0s);
+      __syncthreads();
+      epi_strip<BN, NT, MODE>(E, stg, LC, mb, n0, M, N, tid, rowtab);
+    }
+    __syncthreads();
+  }
+}
+
+template <int KT, int MODE, bool H16>
+hipError_t launch_wstream(hipStream_t s, const bf16* A, const bf16* W, int M, int N, int K, const Epi& E) {
+  const unsigned grid = (unsigned)(((M + 127) / 128) * ((N + 127) / 128)) * (E.ksplit > 1 ? E.ksplit : 1);
+  gemm_wstream_kernel<KT, MODE, H16><<<grid, 256, 0, s>>>(A, W, M, N, K, E);
+  return hipGetLastError();
+}
+
+// Few rows (M <= 256, below the knee where streaming W from HBM bounds the
+// product): gemm_wstream_kernel over 128 x 128 tiles with K split into ks
+// slices of KT k-tiles (K = 64 ks KT), then gemm_reduce_kernel.  KT is chosen
+// by a small cost model: one memory round trip per workgroup plus the bytes
+// of W and A over the bandwidth the workgroups can draw, plus the partials'
+// write and read-back when ks > 1.  Returns false when the shape does not
+// take this path (M > 256, K % 64, no partial buffer, N % 4).
+template <int MODE, bool H16>
+bool launch_stream(hipStream_t s, const bf16* A, const bf16* W, int M, int N, int K, const Epi& E0, hipError_t* err) {
+  if (M > 256 || K % 64 || (N & 3) || M < 1) return false;
+  const int KT64 = K / 64;
+  const int64_t tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+  const double w_bytes = 2.0 * N * K, a_bytes = 2.0 * M * K * ((N + 127) / 128);
+  int best_kt = 0;
+  double best_t = 1e30;
+  for (int kt = 8; kt >= 1; --kt) {
+    if (KT64 % kt) continue;
+    const int64_t ks = KT64 / kt;
+    if (ks > 64) continue;
+    if (ks > 1 && (!E0.part || ks * (int64_t)M * N > E0.part_cap)) continue;
+    const int64_t wgs = tiles * ks;
+    const double rounds = (double)((wgs + 255) / 256);
+    const double bw = std::min(8.0e12 * 0.8, (double)std::min<int64_t>(wgs, 256) * 40.0e9);   // bytes/s
+    double t = rounds * 2.0e-6 + (w_bytes + a_bytes) / bw;
+    if (ks > 1) t += 3.0e-6 + 2.0 * ks * M * N * 4.0 / 10.0e12;
+    if (t < best_t * 0.999) {
+      best_t = t;
+      best_kt = kt;
+    }
+  }
+  if (!best_kt) return false;
+  Epi E = E0;
+  E.ksplit = KT64 / best_kt;
+  switch (best_kt) {
+    case 1: *err = launch_wstream<1, MODE, H16>(s, A, W, M, N, K, E); break;
+    case 2: *err = launch_wstream<2, MODE, H16>(s, A, W, M, N, K, E); break;
+    case 3: *err = launch_wstream<3, MODE, H16>(s, A, W, M, N, K, E); break;
+    case 4: *err = launch_wstream<4, MODE, H16>(s, A, W, M, N, K, E); break;
+    case 5: *err = launch_wstream<5, MODE, H16>(s, A, W, M, N, K, E); break;
+    case 6: *err = launch_wstream<6, MODE, H16>(s, A, W, M, N, K, E); break;
+    case 7: *err = launch_wstream<7, MODE, H16>(s, A, W, M, N, K, E); break;
+    default: *err = launch_wstream<8, MODE, H16>(s, A, W, M, N, K, E); break;
+  }
+  if (*err == hipSuccess && E.ksplit > 1) {
+    const unsigned grid = (unsigned)(((M + 63) / 64) * ((N + 31) / 32));
+    gemm_reduce_kernel<MODE><<<grid, 256, 0, s>>>(M, N, E);
+    *err = hipGetLastError();
+  }
+  return true;
+}
+
 template <int MODE, bool H16 = false>
 hipError_t gemm_mfma_mode(hipStream_t s, const bf16* A, const bf16* W, int M, int N, int K, const Epi& E) {
   // pick the tile that minimises (rounds of resident workgroups) x (cost per
@@ -689,6 +909,10 @@ hipError_t gemm_mfma_mode(hipStream_t s, const bf16* A, const bf16* W, int M, in
       best_t = t;
       best = i;
     }
+  }
+  {
+    hipError_t err = hipSuccess;
+    if (launch_stream<MODE, H16>(s, A, W, M, N, K, E, &err)) return err;
   }
   if (K % 64 == 0) {
     // direct-to-LDS, DMA spread over the MFMAs, one workgroup per CU: 256 x 256

@@ -37,11 +37,12 @@ hipError_t entry_noise(hipStream_t s, const float* x0, const float* noise, float
 // zrow) or emit x0_hat (to output position oidx of the step).  For
 // onetime-negative R-CFG an entering row first turns its negative row's output
 // into its x0* estimate; under full CFG eps' is the twin row's output.
-__global__ void rcfg_update_kernel(RowTable rt, float* __restrict__ store_x, float* __restrict__ store_x0s,
-                                   const float* __restrict__ eps, const float* __restrict__ store_z,
-                                   float* __restrict__ out, int64_t lat, float gamma, float delta) {
+__global__ void rcfg_update_kernel(const RowTable* __restrict__ rt, float* __restrict__ store_x,
+                                   float* __restrict__ store_x0s, const float* __restrict__ eps,
+                                   const float* __restrict__ store_z, float* __restrict__ out, int64_t lat, float gamma,
+                                   float delta) {
   const int r = blockIdx.y;
-  const RowInfo ri = rt.r[r];
+  const RowInfo ri = rt->r[r];
   if (ri.kind != 0) return;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= lat) return;
@@ -75,9 +76,10 @@ __global__ void rcfg_update_kernel(RowTable rt, float* __restrict__ store_x, flo
   }
 }
 
-hipError_t rcfg_update(hipStream_t s, const RowTable& rt, float* store_x, float* store_x0s, const float* eps,
+hipError_t rcfg_update(hipStream_t s, const RowTable* rt, int R, float* store_x, float* store_x0s, const float* eps,
                        const float* store_z, float* out, int64_t lat, float gamma, float delta) {
-  dim3 g(grid1(lat, 256), rt.R);
+  if (R == 0) return hipSuccess;
+  dim3 g(grid1(lat, 256), R);
   rcfg_update_kernel<<<g, 256, 0, s>>>(rt, store_x, store_x0s, eps, store_z, out, lat, gamma, delta);
   return hipGetLastError();
 }
@@ -88,8 +90,8 @@ hipError_t rcfg_update(hipStream_t s, const RowTable& rt, float* store_x, float*
 // hi = bf16(v), then lo = bf16(v - hi) (row pitch 2P), for a patch embedding
 // over K = 2P against [W | W] that sees the fp32 latent to about 16 bits.
 template <typename T, bool SPLIT = false>
-__global__ void patchify_kernel(RowTable rt, const float* __restrict__ store_x, T* __restrict__ out, int64_t lat,
-                                int Tn, int C, int Hl, int Wl, int p) {
+__global__ void patchify_kernel(const RowTable* __restrict__ rt, const float* __restrict__ store_x, T* __restrict__ out,
+                                int64_t lat, int Tn, int C, int Hl, int Wl, int p) {
   const int r = blockIdx.y;
   const int Hp = Hl / p, Wp = Wl / p;
   const int P = p * p * C;
@@ -100,7 +102,7 @@ __global__ void patchify_kernel(RowTable rt, const float* __restrict__ store_x, 
   const int64_t tok = i / P;
   const int xq = (int)(tok % Wp), yq = (int)((tok / Wp) % Hp), f = (int)(tok / ((int64_t)Wp * Hp));
   const int c = v % C, px = (v / C) % p, py = v / (C * p);
-  const float* src = store_x + (int64_t)rt.r[r].frame * lat;
+  const float* src = store_x + (int64_t)rt->r[r].frame * lat;
   const float val = src[(((int64_t)f * C + c) * Hl + (yq * p + py)) * Wl + (xq * p + px)];
   if constexpr (SPLIT) {
     const T hi = from_f<T>(val);
@@ -112,10 +114,11 @@ __global__ void patchify_kernel(RowTable rt, const float* __restrict__ store_x, 
   }
 }
 
-hipError_t patchify(hipStream_t s, bool bf, const RowTable& rt, const float* store_x, void* out, int64_t lat,
+hipError_t patchify(hipStream_t s, bool bf, const RowTable* rt, int R, const float* store_x, void* out, int64_t lat,
                     int T, int C, int Hl, int Wl, int p, bool split) {
   const int64_t per_row = (int64_t)T * (Hl / p) * (Wl / p) * p * p * C;
-  dim3 g(grid1(per_row, 256), rt.R);
+  if (R == 0) return hipSuccess;
+  dim3 g(grid1(per_row, 256), R);
   if (split && !bf) return hipErrorInvalidValue;
   if (split)
     patchify_kernel<bf16, true><<<g, 256, 0, s>>>(rt, store_x, (bf16*)out, lat, T, C, Hl, Wl, p);
@@ -278,19 +281,20 @@ hipError_t ln_mod(hipStream_t s, bool bf, const float* x, void* out, int M, int 
 // ---------------------------------------------------------------------------
 // Sinusoidal timestep embedding in fp64: e = [cos(tau w_j), sin(tau w_j)],
 // w_j = 10000^(-j / (D/2)).
-__global__ void temb_embed_kernel(RowTable rt, float* __restrict__ out, int d_freq) {
+__global__ void temb_embed_kernel(const RowTable* __restrict__ rt, float* __restrict__ out, int d_freq) {
   const int r = blockIdx.x;
   const int half = d_freq / 2;
   for (int j = threadIdx.x; j < half; j += blockDim.x) {
     const double w = pow(10000.0, -(double)j / (double)half);
-    const double arg = (double)rt.r[r].tau * w;
+    const double arg = (double)rt->r[r].tau * w;
     out[(int64_t)r * d_freq + j] = (float)cos(arg);
     out[(int64_t)r * d_freq + half + j] = (float)sin(arg);
   }
 }
 
-hipError_t temb_embed(hipStream_t s, const RowTable& rt, float* out, int d_freq) {
-  temb_embed_kernel<<<rt.R, 128, 0, s>>>(rt, out, d_freq);
+hipError_t temb_embed(hipStream_t s, const RowTable* rt, int R, float* out, int d_freq) {
+  if (R == 0) return hipSuccess;
+  temb_embed_kernel<<<R, 128, 0, s>>>(rt, out, d_freq);
   return hipGetLastError();
 }
 
@@ -403,7 +407,9 @@ hipError_t gemv(hipStream_t s, bool bf, const float* x, const void* W, const voi
 template <typename T>
 __global__ void kv_append_kernel(const T* __restrict__ kown, const T* __restrict__ vtown, int64_t k_hs, int64_t vt_ps,
                                  T* __restrict__ ringK, T* __restrict__ ringVT, int H, int hd, int L, int W, int ptr,
-                                 T* __restrict__ sinkK, T* __restrict__ sinkVT, int S8, int sink_off, int Se) {
+                                 T* __restrict__ sinkK, T* __restrict__ sinkVT, int S8, int sink_off, int Se,
+                                 const int* __restrict__ ptr_dev) {
+  if (ptr_dev) ptr = *ptr_dev;
   const int64_t per_head = (int64_t)L * hd;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= per_head * H) return;
@@ -431,7 +437,8 @@ __global__ void kv_append_kernel(const T* __restrict__ kown, const T* __restrict
 __global__ void kv_append_vec_kernel(const bf16* __restrict__ kown, const bf16* __restrict__ vtown, int64_t k_hs,
                                      int64_t vt_ps, bf16* __restrict__ ringK, bf16* __restrict__ ringVT, int H, int hd,
                                      int L, int W, int ptr, bf16* __restrict__ sinkK, bf16* __restrict__ sinkVT, int S8,
-                                     int sink_off, int Se) {
+                                     int sink_off, int Se, const int* __restrict__ ptr_dev) {
+  if (ptr_dev) ptr = *ptr_dev;
   const int64_t nk = (int64_t)H * L * (hd / 8);
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= 2 * nk) return;
@@ -463,7 +470,7 @@ __global__ void kv_append_vec_kernel(const bf16* __restrict__ kown, const bf16* 
 
 hipError_t kv_append(hipStream_t s, bool bf, const void* kown, const void* vtown, int64_t k_hs, int64_t vt_ps,
                      void* ringK, void* ringVT, int H, int hd, int L, int W, int ptr, void* sinkK, void* sinkVT, int S8,
-                     int sink_off, int Se) {
+                     int sink_off, int Se, const int* ptr_dev) {
   const int64_t n = (int64_t)H * L * hd;
   if (k_hs < (int64_t)L * hd || vt_ps < L) return hipErrorInvalidValue;
   if (bf && (hd % 8) == 0 && (L % 8) == 0 && (W % 8) == 0 && (ptr % 8) == 0 && ptr < (W > 0 ? W : 1) && (W == 0 || L <= W) &&
@@ -472,17 +479,17 @@ hipError_t kv_append(hipStream_t s, bool bf, const void* kown, const void* vtown
     const int64_t chunks = 2 * (n / 8);
     kv_append_vec_kernel<<<grid1(chunks, 256), 256, 0, s>>>((const bf16*)kown, (const bf16*)vtown, k_hs, vt_ps,
                                                              (bf16*)ringK, (bf16*)ringVT, H, hd, L, W, ptr,
-                                                             (bf16*)sinkK, (bf16*)sinkVT, S8, sink_off, Se);
+                                                             (bf16*)sinkK, (bf16*)sinkVT, S8, sink_off, Se, ptr_dev);
     return hipGetLastError();
   }
   if (bf)
     kv_append_kernel<bf16><<<grid1(n, 256), 256, 0, s>>>((const bf16*)kown, (const bf16*)vtown, k_hs, vt_ps,
                                                          (bf16*)ringK, (bf16*)ringVT, H, hd, L, W, ptr, (bf16*)sinkK,
-                                                         (bf16*)sinkVT, S8, sink_off, Se);
+                                                         (bf16*)sinkVT, S8, sink_off, Se, ptr_dev);
   else
     kv_append_kernel<float><<<grid1(n, 256), 256, 0, s>>>((const float*)kown, (const float*)vtown, k_hs, vt_ps,
                                                           (float*)ringK, (float*)ringVT, H, hd, L, W, ptr,
-                                                          (float*)sinkK, (float*)sinkVT, S8, sink_off, Se);
+                                                          (float*)sinkK, (float*)sinkVT, S8, sink_off, Se, ptr_dev);
   return hipGetLastError();
 }
 
@@ -491,8 +498,9 @@ hipError_t kv_append(hipStream_t s, bool bf, const void* kown, const void* vtown
 template <typename T>
 __global__ void sink_copy_kernel(const int* __restrict__ flag, const T* __restrict__ ringK,
                                  const T* __restrict__ ringVT, T* __restrict__ sinkK, T* __restrict__ sinkVT, int nb,
-                                 int H, int hd, int W, int S8, int ptr_old, int Se) {
+                                 int H, int hd, int W, int S8, int ptr_old, int Se, const int* __restrict__ ptr_dev) {
   if (flag[0] == 0) return;
+  if (ptr_dev) ptr_old = *ptr_dev;
   const int j = flag[1];
   const int64_t per = (int64_t)Se * hd;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -510,16 +518,31 @@ __global__ void sink_copy_kernel(const int* __restrict__ flag, const T* __restri
 }
 
 hipError_t sink_copy(hipStream_t s, bool bf, const int* flag, const void* ringK, const void* ringVT, void* sinkK,
-                     void* sinkVT, int nb, int H, int hd, int W, int S8, int ptr_old, int Se) {
+                     void* sinkVT, int nb, int H, int hd, int W, int S8, int ptr_old, int Se, const int* ptr_dev) {
   const int64_t n = (int64_t)nb * H * Se * hd;
   if (n == 0) return hipSuccess;
   if (bf)
     sink_copy_kernel<bf16><<<grid1(n, 256), 256, 0, s>>>(flag, (const bf16*)ringK, (const bf16*)ringVT,
-                                                         (bf16*)sinkK, (bf16*)sinkVT, nb, H, hd, W, S8, ptr_old, Se);
+                                                         (bf16*)sinkK, (bf16*)sinkVT, nb, H, hd, W, S8, ptr_old, Se,
+                                                         ptr_dev);
   else
     sink_copy_kernel<float><<<grid1(n, 256), 256, 0, s>>>(flag, (const float*)ringK, (const float*)ringVT,
                                                           (float*)sinkK, (float*)sinkVT, nb, H, hd, W, S8, ptr_old,
-                                                          Se);
+                                                          Se, ptr_dev);
+  return hipGetLastError();
+}
+
+// The step's dynamic values, by value in the kernel arguments, to device memory.
+__global__ __launch_bounds__(256) void dyn_write_kernel(StepDyn d, StepDyn* __restrict__ dst) {
+  constexpr int NW = (int)(sizeof(StepDyn) / 4);
+  const uint32_t* src = (const uint32_t*)&d;
+  uint32_t* out = (uint32_t*)dst;
+  for (int i = threadIdx.x; i < NW; i += blockDim.x) out[i] = src[i];
+}
+
+hipError_t dyn_write(hipStream_t s, const StepDyn& d, StepDyn* dst) {
+  static_assert(sizeof(StepDyn) % 4 == 0 && sizeof(StepDyn) <= 4000, "step values must fit the kernel arguments");
+  dyn_write_kernel<<<1, 256, 0, s>>>(d, dst);
   return hipGetLastError();
 }
 

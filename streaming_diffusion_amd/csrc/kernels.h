@@ -9,12 +9,13 @@ namespace sdk {
 // xs = a*x0 + b*noise; x0s = x0 (when x0s != nullptr).
 hipError_t entry_noise(hipStream_t s, const float* x0, const float* noise, float* xs, float* x0s, int64_t n,
                        float a, float b);
-// R-CFG, x0 prediction and re-noise for every denoise row of rt.
-hipError_t rcfg_update(hipStream_t s, const RowTable& rt, float* store_x, float* store_x0s, const float* eps,
+// R-CFG, x0 prediction and re-noise for every denoise row of the device row
+// table rt (R rows).
+hipError_t rcfg_update(hipStream_t s, const RowTable* rt, int R, float* store_x, float* store_x0s, const float* eps,
                        const float* store_z, float* out, int64_t lat, float gamma, float delta);
 // Gather patches of each row's latent into [R*L][p*p*C] (element type by bf);
 // split (bf16): [R*L][2*p*p*C], each token's values as hi then lo parts.
-hipError_t patchify(hipStream_t s, bool bf, const RowTable& rt, const float* store_x, void* out, int64_t lat,
+hipError_t patchify(hipStream_t s, bool bf, const RowTable* rt, int R, const float* store_x, void* out, int64_t lat,
                     int T, int C, int Hl, int Wl, int p, bool split = false);
 // LayerNorm (no affine, population variance) then optional modulation
 // x*(1+scale)+shift with scale/shift = mod[r][off] + blk[off]; output element
@@ -24,7 +25,9 @@ enum { LN_PLAIN = 0, LN_F16 = 1, LN_SPLIT = 2 };
 hipError_t ln_mod(hipStream_t s, bool bf, const float* x, void* out, int M, int d, int L, const float* mod,
                   const void* blk, int shift_off, int scale_off, int six_d, float eps, int form = LN_PLAIN);
 // Sinusoidal timestep embedding per row: [cos(tau w_j), sin(tau w_j)], fp64 math.
-hipError_t temb_embed(hipStream_t s, const RowTable& rt, float* out, int d_freq);
+hipError_t temb_embed(hipStream_t s, const RowTable* rt, int R, float* out, int d_freq);
+// Copy the step's dynamic values to device memory (one small launch).
+hipError_t dyn_write(hipStream_t s, const StepDyn& d, StepDyn* dst);
 // y[r][n] = act(sum_k x[r][k] W[n][k] + b[n]); act 0 = none, 1 = SiLU.
 hipError_t gemv(hipStream_t s, bool bf, const float* x, const void* W, const void* b, float* y, int R, int N, int K,
                 int act);
@@ -32,12 +35,15 @@ hipError_t gemv(hipStream_t s, bool bf, const float* x, const void* W, const voi
 // first Se tokens as sink entry (sink_off .. sink_off+Se).
 // kown: head h's [L][hd] keys start at kown + h * k_hs; vtown: the V^T row of
 // (h, e) starts at vtown + (h * hd + e) * vt_ps.
+// ptr_dev (nullable): the ring position is read from device memory instead
+// of ptr (then ptr only selects the kernel: any multiple of 8 below W).
 hipError_t kv_append(hipStream_t s, bool bf, const void* kown, const void* vtown, int64_t k_hs, int64_t vt_ps,
                      void* ringK, void* ringVT, int H, int hd, int L, int W, int ptr, void* sinkK, void* sinkVT, int S8,
-                     int sink_off, int Se);
+                     int sink_off, int Se, const int* ptr_dev = nullptr);
 // Predicated sink refresh copy over all blocks (flag[0] != 0 -> entry flag[1]).
 hipError_t sink_copy(hipStream_t s, bool bf, const int* flag, const void* ringK, const void* ringVT, void* sinkK,
-                     void* sinkVT, int nb, int H, int hd, int W, int S8, int ptr_old, int Se);
+                     void* sinkVT, int nb, int H, int hd, int W, int S8, int ptr_old, int Se,
+                     const int* ptr_old_dev = nullptr);
 hipError_t fill_zero(hipStream_t s, void* p, size_t bytes);
 // Host: one section of the 3D RoPE table, (cos, sin) of pos * base^(-2j/width)
 // for pos < npos, j < width/2, written as npos * max(1, width/2) pairs
@@ -101,6 +107,9 @@ struct AttnArgs {
   bf16* part_o;
   float2* part_ml;
   long long part_so, part_sml;
+  // bf16 path: when set, (start, count) of segments 0 and 1 are read from
+  // dyn_seg[0..3] in device memory instead of seg[0], seg[1]
+  const int* dyn_seg;
 };
 // With combine = false a split launch leaves its partials for a separate
 // attention_combine() call (so the two passes can be timed apart).

@@ -74,6 +74,7 @@ sd_status sd_k_gemm_epi(const void* A, const void* W, int32_t M, int32_t N, int3
   E.L = e->L > 0 ? e->L : 1;
   E.ldo = N;
   if (e->f16 && e->mode != SD_EPI_F32 && e->mode != SD_EPI_RESID) return SD_ERR_ARG;
+  if (e->workspace && ((uintptr_t)e->workspace & 255)) return SD_ERR_ARG;
   switch (e->mode) {
     case SD_EPI_STORE:
     case SD_EPI_GELU:
@@ -147,6 +148,10 @@ sd_status sd_k_gemm_epi(const void* A, const void* W, int32_t M, int32_t N, int3
     }
     default:
       return SD_ERR_ARG;
+  }
+  if (e->workspace && e->workspace_bytes >= 4) {
+    E.part = (float*)e->workspace;
+    E.part_cap = (int64_t)(e->workspace_bytes / 4);
   }
   const hipError_t r = e->f16 ? sdk::gemm_mfma_f16((hipStream_t)stream, A, W, M, N, K, E)
                              : sdk::gemm_mfma((hipStream_t)stream, A, W, M, N, K, E);

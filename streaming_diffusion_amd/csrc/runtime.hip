@@ -68,6 +68,24 @@ struct sd_stream {
   // pe2 [d][2P] = [pe_w | pe_w], head2 [P][2d] = [head_w | head_w], copied
   // from the caller's weights at create
   void *pe2 = nullptr, *head2 = nullptr;
+  // bf16 with short chunks (L <= 256): fp32 partials of GEMMs split over K
+  // when a forward has few rows (kernels.h, Epi::part)
+  float* gpart = nullptr;
+  int64_t gpart_cap = 0;
+  // the step's dynamic values in device memory: [0] the forward, [1] the
+  // clean-latent forward of kv_recompute
+  StepDyn* dyn = nullptr;
+  // graph replay of the step's forward and update (sd_stream_set_graph): a
+  // few instantiated graphs keyed by the launch sequence's static arguments
+  struct GraphEntry {
+    std::vector<int64_t> key;
+    hipGraphExec_t exec = nullptr;
+    uint64_t used = 0;
+  };
+  bool graph_on = false;
+  std::vector<GraphEntry> graphs;
+  uint64_t graph_clock = 0;
+  int64_t graph_captures = 0, graph_replays = 0;
   void *fold_q = nullptr, *fold_o = nullptr;
   float* fold_c = nullptr;
   double *sink_emb = nullptr, *sink_part = nullptr, *sink_sim = nullptr;
@@ -106,6 +124,8 @@ struct sd_stream {
   ~sd_stream() {
     if (io) (void)hipStreamSynchronize(io);
     if (st) (void)hipStreamSynchronize(st);
+    for (GraphEntry& g : graphs)
+      if (g.exec) (void)hipGraphExecDestroy(g.exec);
     for (hipEvent_t e : ev_pool) (void)hipEventDestroy(e);
     for (hipEvent_t e : rec_ev) (void)hipEventDestroy(e);
     if (ev_push) (void)hipEventDestroy(ev_push);
@@ -213,10 +233,15 @@ size_t carve(sd_stream* s, char* base) {
       s->fold_c = cv.take<float>((size_t)s->nb * nctx * ncol * 4);
     }
   }
+  if (s->bf && s->L <= 256) {
+    s->gpart_cap = (int64_t)16 << 20;          // 64 MiB of fp32 partials
+    s->gpart = cv.take<float>((size_t)s->gpart_cap * 4);
+  }
   if (s->bf) {
     s->pe2 = cv.take<void>((size_t)s->d * 2 * s->P * es);
     s->head2 = cv.take<void>((size_t)s->P * 2 * s->d * es);
   }
+  s->dyn = cv.take<StepDyn>(2 * sizeof(StepDyn));
   s->sink_emb = cv.take<double>((size_t)std::max(1, s->Ment) * s->d * 8);
   s->sink_part = cv.take<double>((size_t)64 * s->d * 8);
   s->sink_flag = cv.take<int>(16);
@@ -291,6 +316,8 @@ Epi epi_base(const sd_stream* s, int mode) {
   E.p = s->cfg.patch;
   E.T = s->Tn;
   E.krows = 1;
+  E.part = s->gpart;
+  E.part_cap = s->gpart_cap;
   return E;
 }
 
@@ -572,8 +599,75 @@ struct ExitPlan {
 // patch embedding, the blocks, the final layer; eps_out receives eps of row r
 // at eps_out + r * lat.  With xp the leaving rows update the KV cache and the
 // sink; without it the cache is only read.
-static sd_status run_forward(sd_stream* s, const RowTable& rt, int R_pos, int nneg, const ExitPlan* xp,
-                             float* eps_out) {
+extern "C++" {
+// Per-step device values of a forward over rt (see StepDyn), from the cache
+// state as it stands at the start of the step.
+static StepDyn make_dyn(const sd_stream* s, const RowTable& rt, int nexit, int ptr_old) {
+  StepDyn d;
+  std::memset(&d, 0, sizeof(d));
+  d.rt = rt;
+  for (int r = 0; r < rt.R; ++r) d.t0[r] = rt.r[r].t0;
+  d.seg[0] = 0;
+  d.seg[1] = s->sink_count * s->Se;
+  d.seg[2] = s->Wt > 0 ? (s->kv_ptr - s->kv_valid + s->Wt) % s->Wt : 0;
+  d.seg[3] = s->kv_valid;
+  for (int k = 0; k < nexit; ++k)
+    d.kv_pos[k] = s->Wt > 0 ? (int)(((int64_t)ptr_old + (int64_t)k * s->L) % s->Wt) : 0;
+  d.ptr_old = ptr_old;
+  return d;
+}
+
+// Graph replay applies to bf16 steps on a created stream with no IO queue,
+// no live profiling and no clean-latent recompute (its second forward's rows
+// depend on the exits).
+static bool graph_eligible(const sd_stream* s) {
+  return s->graph_on && s->bf && s->st != nullptr && s->io == nullptr && s->prof_mask == 0 && !s->cfg.kv_recompute;
+}
+
+// Launch the graph recorded for `key`, capturing it from `body` the first
+// time; at most four are kept (least recently used evicted).
+template <typename F>
+static sd_status graph_run(sd_stream* s, const std::vector<int64_t>& key, F&& body) {
+  sd_stream::GraphEntry* ge = nullptr;
+  for (auto& g : s->graphs)
+    if (g.key == key) ge = &g;
+  if (!ge) {
+    HIP_TRY(hipStreamBeginCapture(s->st, hipStreamCaptureModeThreadLocal));
+    const sd_status fs = body();
+    hipGraph_t graph = nullptr;
+    const hipError_t ce = hipStreamEndCapture(s->st, &graph);
+    if (fs != SD_OK) {
+      if (graph) (void)hipGraphDestroy(graph);
+      return fs;
+    }
+    if (ce != hipSuccess || !graph) return set_err(s, SD_ERR_HIP, std::string("graph capture: ") + hipGetErrorString(ce));
+    hipGraphExec_t exec = nullptr;
+    const hipError_t ie = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (ie != hipSuccess) return set_err(s, SD_ERR_HIP, std::string("graph instantiate: ") + hipGetErrorString(ie));
+    if (s->graphs.size() >= 4) {
+      auto lru = s->graphs.begin();
+      for (auto it = s->graphs.begin(); it != s->graphs.end(); ++it)
+        if (it->used < lru->used) lru = it;
+      (void)hipGraphExecDestroy(lru->exec);
+      s->graphs.erase(lru);
+    }
+    s->graphs.push_back({key, exec, 0});
+    ge = &s->graphs.back();
+    ++s->graph_captures;
+  } else {
+    ++s->graph_replays;
+  }
+  ge->used = ++s->graph_clock;
+  HIP_TRY(hipGraphLaunch(ge->exec, s->st));
+  return SD_OK;
+}
+}  // extern "C++"
+
+// The forward over rows rt (host copy, for shapes and launch decisions); the
+// kernels read the per-step values from dd, the device copy written before.
+static sd_status run_forward(sd_stream* s, const RowTable& rt, const StepDyn* dd, int R_pos, int nneg,
+                             const ExitPlan* xp, float* eps_out) {
   const sd_stream_config& c = s->cfg;
   const int R = rt.R;
   const int L = s->L, d = s->d, H = s->H, hd = s->hd, M = R * L;
@@ -586,7 +680,7 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, int R_pos, int nn
   const int ptr_old = xp ? xp->ptr_old : 0;
 
   // ---- conditioning: timestep embedding -> MLP -> SiLU(c) -> adaLN vectors
-  PROF(SD_PROF_GEMV, 0.0, 4.0 * R * c.d_freq, sdk::temb_embed(st, rt, s->emb, c.d_freq));
+  PROF(SD_PROF_GEMV, 0.0, 4.0 * R * c.d_freq, sdk::temb_embed(st, &dd->rt, R, s->emb, c.d_freq));
   PROF(SD_PROF_GEMV, 2.0 * R * d * c.d_freq, (double)d * c.d_freq * es,
        sdk::gemv(st, bf, s->emb, s->w.t_w1, s->w.t_b1, s->h1, R, d, c.d_freq, 1));
   PROF(SD_PROF_GEMV, 2.0 * R * d * d, (double)d * d * es, sdk::gemv(st, bf, s->h1, s->w.t_w2, s->w.t_b2, s->sc, R, d, d, 1));
@@ -599,7 +693,8 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, int R_pos, int nn
   // (bf16: hi + lo input pairs against the doubled weights, K = 2P)
   const int KP = bf ? 2 * s->P : s->P;
   PROF(SD_PROF_OTHER, 0.0, (4.0 + es * KP / s->P) * R * s->lat,
-       sdk::patchify(st, bf, rt, s->fx, s->xm, s->lat, s->Tn, c.latent_c, c.latent_h, c.latent_w, c.patch, bf));
+       sdk::patchify(st, bf, &dd->rt, R, s->fx, s->xm, s->lat, s->Tn, c.latent_c, c.latent_h, c.latent_w, c.patch,
+                     bf));
   {
     Epi E = epi_base(s, EPI_PATCH);
     E.bias = s->w.pe_b;
@@ -628,6 +723,7 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, int R_pos, int nn
       E.krows = R;
       E.rope = 1;
       for (int r = 0; r < R; ++r) E.t0[r] = rt.r[r].t0;
+      E.t0_dev = dd->t0;
       PROF(SD_PROF_GEMM_QKV, gflop(M, 3 * d, d), gbytes(M, 3 * d, d, es, es),
            sdk::gemm(st, bf, s->xm, P(s->w.qkv_w, (int64_t)b * 3 * d * d, es), M, 3 * d, d, E));
     }
@@ -671,6 +767,7 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, int R_pos, int nn
       so.cap = R * L;
       so.count = c.batch_attn ? R * L : L;
       A.nseg = ns;
+      if (bf) A.dyn_seg = dd->seg;
       if (s->attn_split_max > 1) {
         const int nk = ((sk.count + 7) & ~7) + sw.count + so.count;
         const int qt = sdk::attention_q_tile(bf, hd);
@@ -712,7 +809,7 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, int R_pos, int nn
            sdk::kv_append(st, bf, P(s->kown, (int64_t)exit_rows[k] * L * hd, es), P(s->vtown, (int64_t)exit_rows[k] * L, es),
                           kv_hs, (int64_t)R * L,
                           Pm(s->ringK, (int64_t)b * H * s->Wt * hd, es), Pm(s->ringVT, (int64_t)b * H * s->Wt * hd, es),
-                          H, hd, L, s->Wt, pk, dK, dVT, dcap, doff, s->Se));
+                          H, hd, L, s->Wt, pk, dK, dVT, dcap, doff, s->Se, &dd->kv_pos[k]));
     }
     {
       Epi E = epi_base(s, EPI_GATE_RESID);
@@ -832,7 +929,7 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, int R_pos, int nn
       PROF(SD_PROF_KV, 0.0, 4.0 * s->nb * s->Se * d * es,
            sdk::sink_copy(st, bf, s->sink_flag, staged ? s->candK : s->ringK, staged ? s->candVT : s->ringVT,
                           s->sinkK, s->sinkVT, s->nb, H, hd, staged ? s->Cc : s->Wt, s->S8,
-                          staged ? k * s->Se : ptr_old, s->Se));
+                          staged ? k * s->Se : ptr_old, s->Se, staged ? nullptr : &dd->ptr_old));
     }
   }
 
@@ -956,15 +1053,31 @@ sd_status sd_stream_step_chunks(sd_stream* s, int32_t chunks, float* out_latent,
   const int ptr_old = s->kv_ptr;
 
   const ExitPlan plan{nexit, exit_rows, cap_entry, ptr_old};
-  {
-    // with clean-latent recompute this forward only reads the cache
-    const sd_status fs = run_forward(s, rt, R_pos, nneg, c.kv_recompute ? nullptr : &plan, s->eps);
+  HIP_TRY(sdk::dyn_write(st, make_dyn(s, rt, nexit, ptr_old), s->dyn));
+  // the forward (with clean-latent recompute it only reads the cache), then
+  // R-CFG, x0 prediction, re-noise / emit
+  auto forward_update = [&]() -> sd_status {
+    const sd_status fs = run_forward(s, rt, s->dyn, R_pos, nneg, c.kv_recompute ? nullptr : &plan, s->eps);
+    if (fs != SD_OK) return fs;
+    PROF(SD_PROF_EPILOGUE, 12.0 * R * s->lat, 16.0 * R * s->lat,
+         sdk::rcfg_update(st, &s->dyn->rt, R, s->fx, s->fx0s, s->eps, s->fz, out_latent, s->lat, (float)c.gamma,
+                          (float)c.delta));
+    return SD_OK;
+  };
+  if (graph_eligible(s)) {
+    // everything the launch sequence depends on besides the device values
+    std::vector<int64_t> key = {R, R_pos, nneg, nexit, chunks, s->sink_count, s->kv_valid,
+                                (int64_t)(uintptr_t)out_latent};
+    for (int k = 0; k < nexit; ++k) {
+      key.push_back(exit_rows[k]);
+      key.push_back(cap_entry[k]);
+    }
+    const sd_status gs = graph_run(s, key, forward_update);
+    if (gs != SD_OK) return gs;
+  } else {
+    const sd_status fs = forward_update();
     if (fs != SD_OK) return fs;
   }
-
-  // ---- R-CFG, x0 prediction, re-noise / emit
-  PROF(SD_PROF_EPILOGUE, 12.0 * R * s->lat, 16.0 * R * s->lat,
-       sdk::rcfg_update(st, rt, s->fx, s->fx0s, s->eps, s->fz, out_latent, s->lat, (float)c.gamma, (float)c.delta));
 
   // ---- clean-latent recompute: the leaving chunks' emitted latents (kept in
   // their frame records) go through one more forward at timestep 0 against
@@ -987,7 +1100,8 @@ sd_status sd_stream_step_chunks(sd_stream* s, int32_t chunks, float* out_latent,
     }
     rc.R = nexit;
     const ExitPlan cplan{nexit, rows_c, cap_entry, ptr_old};
-    const sd_status fs = run_forward(s, rc, nexit, 0, &cplan, s->eps + (int64_t)R * s->lat);
+    HIP_TRY(sdk::dyn_write(st, make_dyn(s, rc, nexit, ptr_old), s->dyn + 1));
+    const sd_status fs = run_forward(s, rc, s->dyn + 1, nexit, 0, &cplan, s->eps + (int64_t)R * s->lat);
     if (fs != SD_OK) return fs;
     clean_rows = nexit;
   }
@@ -1020,6 +1134,25 @@ sd_status sd_stream_step_chunks(sd_stream* s, int32_t chunks, float* out_latent,
   info->kv_valid = s->kv_valid;
   info->sink_count = s->sink_count;
   info->rope_next = s->ctl.rope_p;
+  return SD_OK;
+}
+
+sd_status sd_stream_set_graph(sd_stream* s, int32_t enable) {
+  if (!s) return SD_ERR_ARG;
+  if (enable && !s->st) return set_err(s, SD_ERR_STATE, "graph replay needs a created stream (not the null stream)");
+  if (!enable) {
+    HIP_TRY(hipStreamSynchronize(s->st));
+    for (auto& g : s->graphs) (void)hipGraphExecDestroy(g.exec);
+    s->graphs.clear();
+  }
+  s->graph_on = enable != 0;
+  return SD_OK;
+}
+
+sd_status sd_stream_graph_stats(sd_stream* s, int64_t* captures, int64_t* replays) {
+  if (!s || !captures || !replays) return SD_ERR_ARG;
+  *captures = s->graph_captures;
+  *replays = s->graph_replays;
   return SD_OK;
 }
 

@@ -147,6 +147,16 @@ class StreamRunner:
         self.io_stream = stream
         L.check(self.lib.sd_stream_set_io_stream(self.h, C.c_void_p(stream.cuda_stream if stream else None)), self.h)
 
+    def set_graph(self, enable: bool = True):
+        """Replay each step as a captured HIP graph (the runner's stream must
+        be a created stream, not the default one)."""
+        L.check(self.lib.sd_stream_set_graph(self.h, int(enable)), self.h)
+
+    def graph_stats(self):
+        cap, rep = C.c_int64(), C.c_int64()
+        L.check(self.lib.sd_stream_graph_stats(self.h, C.byref(cap), C.byref(rep)), self.h)
+        return cap.value, rep.value
+
     def sink_info(self) -> L.sd_sink_info:
         info = L.sd_sink_info()
         L.check(self.lib.sd_stream_sink_info(self.h, C.byref(info)), self.h)

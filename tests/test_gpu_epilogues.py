@@ -270,3 +270,85 @@ def test_fp16_gemm_exact_integers(lib, M, N, K, mode):
         ref = ref + c0
     run(lib, A, W, M, N, K, e)
     assert np.array_equal(out.cpu().numpy().astype(np.float64), ref)
+
+
+# ------------------------------------------------------------------ few rows: the product split over K
+def split_ws(nbytes=64 << 20):
+    ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=device())
+    return ws, (ws.data_ptr() + 255) // 256 * 256, nbytes
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 4608, 1536), (256, 8960, 1536), (128, 1536, 8960), (256, 1536, 1536),
+                                   (96, 200, 640)])
+def test_split_k_epilogues_exact(lib, M, N, K):
+    """Below the knee (M <= 256 rows: the sub-knee video diagnostic's 128 or
+    256 tokens per forward) the product is split over K into fp32 partials
+    that a second pass sums in slice order before the epilogue; on exact
+    operands the sums are exact, so F32, RESID and the gated residual are
+    bit for bit the integer arithmetic, and STORE the bf16 rounding of it."""
+    print(f"split-K M={M} N={N} K={K}", flush=True)
+    A, W, b, acc = int_operands(M, N, K, 21)
+    ws, wsp, wsb = split_ws()
+    out = torch.empty((M, N), dtype=torch.float32, device=device())
+    e = sdlib.sd_gemm_epi(mode=sdlib.SD_EPI_F32, bias=b.data_ptr(), out=out.data_ptr(), ldo=N, workspace=wsp,
+                          workspace_bytes=wsb)
+    run(lib, A, W, M, N, K, e)
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), acc)
+    rng = np.random.default_rng(22)
+    c0 = rng.integers(-4096, 4097, size=(M, N)) / 256.0
+    Lr = M // 2 if M % 2 == 0 else M
+    rows = M // Lr
+    mod = rng.integers(-2, 3, size=(rows, 6 * N)) / 2.0
+    blk = rng.integers(-1, 2, size=6 * N) / 2.0
+    resid = to_dev(c0, torch.float32)
+    mod_d, blk_d = to_dev(mod, torch.float32), to_dev(blk, torch.bfloat16)
+    e = sdlib.sd_gemm_epi(mode=sdlib.SD_EPI_GATE_RESID, bias=b.data_ptr(), resid=resid.data_ptr(),
+                          mod=mod_d.data_ptr(), blk=blk_d.data_ptr(), gate_off=2 * N, six_d=6 * N, L=Lr,
+                          workspace=wsp, workspace_bytes=wsb)
+    run(lib, A, W, M, N, K, e)
+    gate = mod[np.arange(M) // Lr, 2 * N:3 * N] + blk[2 * N:3 * N]
+    assert np.array_equal(resid.cpu().numpy().astype(np.float64), c0 + gate * acc)
+    st = torch.empty((M, N), dtype=torch.bfloat16, device=device())
+    e = sdlib.sd_gemm_epi(mode=sdlib.SD_EPI_STORE, bias=b.data_ptr(), out=st.data_ptr(), ldo=N, workspace=wsp,
+                          workspace_bytes=wsb)
+    run(lib, A, W, M, N, K, e)
+    assert np.array_equal(st.float().cpu().numpy(), bf16_round(acc.astype(np.float32)))
+
+
+def test_split_k_qkv_rope_and_fp16(lib):
+    """The q / k / v scatter with RoPE and the fp16 cross-attention products on
+    the split path (one latent frame of 8 x 16 tokens per row, two rows)."""
+    ws, wsp, wsb = split_ws()
+    rows, t, hp, wp, d, h = 2, 1, 8, 16, 1536, 12
+    hd, Lr = d // h, t * hp * wp
+    M, N, K = rows * Lr, 3 * d, d
+    A, W, b, acc = int_operands(M, N, K, 23)
+    q = torch.zeros((rows, h, Lr, hd), dtype=torch.bfloat16, device=device())
+    k = torch.zeros((h, rows, Lr, hd), dtype=torch.bfloat16, device=device())
+    vt = torch.zeros((h, hd, rows, Lr), dtype=torch.bfloat16, device=device())
+    tab = rope_table(lib, hd, ROPE_POS, hp, wp)
+    e = sdlib.sd_gemm_epi(mode=sdlib.SD_EPI_QKV, bias=b.data_ptr(), L=Lr, q=q.data_ptr(), k=k.data_ptr(),
+                          vt=vt.data_ptr(), kstride=Lr, krows=rows, H=h, hd=hd, rope=1, Hp=hp, Wp=wp,
+                          rope_table=tab.data_ptr(), rope_positions=ROPE_POS, workspace=wsp, workspace_bytes=wsb)
+    e.t0[0], e.t0[1] = 3, 1020
+    run(lib, A, W, M, N, K, e)
+    qg, kg, vg = q.float().cpu().numpy(), k.float().cpu().numpy(), vt.float().cpu().numpy()
+    for r, t0 in enumerate((3, 1020)):
+        c = acc[r * Lr:(r + 1) * Lr].reshape(Lr, 3, h, hd)
+        assert np.array_equal(vg[:, :, r].transpose(2, 0, 1), bf16_round(c[:, 2]))
+        for sec, got in ((0, qg[r].transpose(1, 0, 2)), (1, kg[:, r].transpose(1, 0, 2))):
+            x = c[:, sec]
+            ref = dit.rope_apply(x, dit.token_positions(t, hp, wp, t0))
+            pair = np.repeat(np.abs(x[..., 0::2]) + np.abs(x[..., 1::2]), 2, axis=-1)
+            assert (np.abs(got - ref) - 2.0 ** -8 * np.abs(ref) - 1e-6 * pair).max() <= 0.0
+    # fp16 operands (the folded cross-attention) on the split path
+    rng = np.random.default_rng(24)
+    M2, N2, K2 = 128, 960, 1536
+    ai, wi = rng.integers(-8, 9, size=(M2, K2)), rng.integers(-8, 9, size=(N2, K2))
+    out = torch.empty((M2, N2), dtype=torch.float32, device=device())
+    e = sdlib.sd_gemm_epi(mode=sdlib.SD_EPI_F32, out=out.data_ptr(), ldo=N2, f16=1, workspace=wsp,
+                          workspace_bytes=wsb)
+    call(lib.sd_k_gemm_epi(to_dev(ai / 16.0, torch.float16).data_ptr(), to_dev(wi / 16.0, torch.float16).data_ptr(),
+                           M2, N2, K2, C.byref(e), stream_ptr()))
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), (ai.astype(np.float64) @ wi.T) / 256.0)

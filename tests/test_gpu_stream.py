@@ -37,7 +37,7 @@ def scene_cut(pushes, scale=-4.0):
 
 
 def run_parity(cfg, steps, check_ring=True, sizes=None, io_stream=False, transform=None, oracle_dtype=np.float64,
-               progress=False):
+               progress=False, graph=False):
     """`sizes`: chunks entering at each step (cycled); default B every step.
     `io_stream`: inputs are produced and pushed on a second stream (the IO
     queue), overlapped with the steps on the main stream.  `transform(k, x0)`
@@ -48,9 +48,14 @@ def run_parity(cfg, steps, check_ring=True, sizes=None, io_stream=False, transfo
     ctx_pos = gen.make_context(cfg)
     ctx_neg = gen.make_context(cfg, negative=True) if cfg.cfg_type != "self" else None
     orc = OracleStream(cfg, weights, ctx_pos, ctx_neg, dtype=oracle_dtype)
+    # graph replay needs a created stream: inputs are then produced on it too
+    side = torch.cuda.Stream() if graph else None
     orc.sink_events = []
     orc.t0_trace = []
-    run = StreamRunner(cfg, upload_weights(cfg, weights))
+    run = StreamRunner(cfg, upload_weights(cfg, weights), stream=side)
+    if graph:
+        torch.cuda.synchronize()
+        run.set_graph(True)
     if cfg.ctx_len:
         run.set_context(to_dev(ctx_pos, tdt), to_dev(ctx_neg, tdt) if ctx_neg is not None else None)
     io = torch.cuda.Stream() if io_stream else None
@@ -68,7 +73,7 @@ def run_parity(cfg, steps, check_ring=True, sizes=None, io_stream=False, transfo
             x0 = transform(pushes, x0)
         frame = ssf_src.next() if ssf_src else None
         po = orc.push_frame(x0, e, frame, u)
-        with torch.cuda.stream(io if io is not None else torch.cuda.current_stream()):
+        with torch.cuda.stream(io if io is not None else (side if side is not None else torch.cuda.current_stream())):
             pg = run.push(to_dev(x0, torch.float32), to_dev(e, torch.float32),
                           to_dev(frame, torch.uint8) if frame is not None else None, u)
         pushes += 1
@@ -129,6 +134,8 @@ def run_parity(cfg, steps, check_ring=True, sizes=None, io_stream=False, transfo
                         stored_bf16=True)
             check_close(sinkV[b].transpose(2, 0, 1)[:used], orc.sinkV[b][:used], cfg.dtype, f"sink V block {b}",
                         stored_bf16=True)
+    if graph:
+        orc.graph_stats = run.graph_stats()
     print(f"{cfg.name}: {done} steps over {pushes} pushes, worst error {worst:.3e}", flush=True)
     run.close()
     return orc, run
@@ -420,3 +427,34 @@ def test_step_errors():
         run.push(x, x)
     assert ei.value.code == L.SD_ERR_STATE
     run.close()
+
+
+# ------------------------------------------------------------------ graph replay of the step
+def test_video_bf16_graph_replay_matches_oracle():
+    """The step recorded once as a HIP graph and replayed with new rows, RoPE
+    bases, window ranges and ring positions each step: the same outputs, ring
+    and sink as the oracle; the steady state replays one graph."""
+    device()
+    cfg = reduced("video13b")
+    print("video bf16 reduced, graph replay", flush=True)
+    orc, _ = run_parity(cfg, 12, graph=True, transform=scene_cut({7}))
+    cap, rep = orc.graph_stats
+    print("graph captures / replays:", cap, rep, flush=True)
+    assert rep >= 6 and cap <= 6
+
+
+def test_fourstep_bf16_graph_replay_onetime_negative():
+    device()
+    cfg = reduced("fourstep", ssf_on=False)
+    print("fourstep bf16 reduced, graph replay", flush=True)
+    orc, _ = run_parity(cfg, 10, graph=True)
+    cap, rep = orc.graph_stats
+    assert rep >= 4
+
+
+def test_video_bf16_graph_replay_variable_group_sizes():
+    device()
+    cfg = reduced("video13b", chunks_per_step=3, window_tokens=384)
+    print("video bf16 reduced B=3, variable groups, graph replay", flush=True)
+    orc, _ = run_parity(cfg, 12, graph=True, sizes=[1, 3, 2, 2, 1, 3, 2, 1])
+    assert sum(orc.graph_stats) == 12

@@ -54,3 +54,25 @@ def test_video14b_full_width_one_block():
     print("video14b full width, 1 block, 4 steps", flush=True)
     orc, _ = run_parity(cfg, 4, oracle_dtype=np.float32, progress=True)
     assert orc.kv_valid == cfg.window_tokens
+
+
+@pytest.mark.parametrize("n", [1, 2])
+def test_video13b_subknee_full_width_two_blocks(n):
+    """The sub-knee diagnostic (the 1.3B-shaped widths with 128-token chunks):
+    every GEMM of the forward has M = 128 or 256 rows and runs split over K;
+    6 steps fill and wrap the 384-token window."""
+    device()
+    cfg = get_config("video13b_subknee", n_blocks=2, t_index=(32,) if n == 1 else (32, 45))
+    print(f"video13b sub-knee, n = {n}, 2 blocks", flush=True)
+    orc, _ = run_parity(cfg, 6, oracle_dtype=np.float32, progress=True)
+    assert orc.kv_valid == cfg.window_tokens
+
+
+def test_video13b_subknee_graph_replay():
+    """The sub-knee diagnostic's step replayed as a graph (split-K GEMMs,
+    reductions and all), 8 steps against the oracle."""
+    device()
+    cfg = get_config("video13b_subknee", n_blocks=2)
+    print("video13b sub-knee, 2 blocks, graph replay", flush=True)
+    orc, _ = run_parity(cfg, 8, oracle_dtype=np.float32, progress=True, graph=True)
+    assert orc.graph_stats[1] >= 3

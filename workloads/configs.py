@@ -141,6 +141,22 @@ CONFIGS = {
         motion_sigma=0.05,
         frames=300,
     ),
+    # Diagnostic below the roofline knee (not one of the pages' workloads):
+    # the 1.3B-shaped video DiT's weights with one small latent frame of
+    # 16 x 32 latents (8 x 16 = 128 tokens) per chunk, so one forward holds
+    # 128 tokens per slot -- far below the ~312 tokens per forward at which
+    # streaming the weights from HBM stops being the bound.  Cache: one sink
+    # frame and a window of three chunks, as in the video workload.
+    "video13b_subknee": Config(
+        name="video13b_subknee", dtype="bf16",
+        latent_c=16, latent_t=1, latent_h=16, latent_w=32, patch=2,
+        n_blocks=30, d_model=1536, n_heads=12, d_ffn=8960, d_freq=256, ctx_len=77,
+        t_index=(32,), cfg_type="self",
+        sink_tokens=128, window_tokens=384,
+        motion_on=True, motion_k=8, motion_lambda=0.3, s_min=0.3, s_max=0.9,
+        motion_sigma=0.05,
+        frames=300,
+    ),
     # Video-DiT chunk, 14B-shaped.
     "video14b": Config(
         name="video14b", dtype="bf16",
