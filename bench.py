@@ -58,10 +58,17 @@ def parse():
     ap.add_argument("--slo-fps", type=float, default=0.0,
                     help="run the SLO-aware batching loop for --steps steps with up to --chunks chunks per step "
                          "and report the batch sizes it chose (one JSON line)")
+    ap.add_argument("--slo-plan", type=float, default=0.0, metavar="FPS",
+                    help="measure steps at B in {1,2,4} x n in {1,2,4}, fit the latency per row and choose the "
+                         "denoising steps n and chunks per step B for the target frame rate (one JSON line)")
     ap.add_argument("--vae", action="store_true",
                     help="measure the Stream-VAE instead: encode + decode of 4-frame chunks at the video shape")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-blocks", type=int, default=2, help="DiT blocks in the oracle sample")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="time the CPU oracle alone, unsampled: the tiny workload's 16 steps (all threads and one "
+                         "thread), one image-DiT step (one thread) and two full steps of the video DiT's pipeline "
+                         "(n = 2, all 30 blocks, fp32); one JSON line, no GPU work (takes about ten minutes)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after the run, copy MIB MiB device-to-device once (reference dispatch for HBM counters)")
     return ap.parse_args()
@@ -427,6 +434,50 @@ def vae_run(steps: int, warmup: int, dev, cpu: bool):
     return res
 
 
+def cpu_full():
+    """The oracle itself on whole steps of the workloads, no sampling."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle.stream import OracleStream
+    from workloads import gen, get_config
+
+    def run_steps(cfg, steps, dtype, threads=None):
+        w = gen.make_weights(cfg)
+        ctx = gen.make_context(cfg)
+        neg = gen.make_context(cfg, True) if cfg.cfg_type != "self" else None
+        orc = OracleStream(cfg, w, ctx, neg, dtype=dtype)
+        src, nz, us = gen.LatentSource(cfg), gen.NoiseSource(cfg), gen.UniformSource()
+        ssf = gen.SSFFrameSource(cfg) if cfg.ssf_on and cfg.ssf_kind == "u8" else None
+        times = []
+        with threadpool_limits(limits=threads):
+            while len(times) < steps:
+                t0 = time.perf_counter()
+                po = orc.push_frame(src.next(), gen.frame_noise(cfg, nz), ssf.next() if ssf else None, us.next())
+                if po.skipped:
+                    continue
+                orc.step()
+                times.append(time.perf_counter() - t0)
+        return times
+
+    threads = max([int(p.get("num_threads", 0)) for p in threadpool_info() if p.get("user_api") == "blas"] or [0])
+    res = {"metric": "CPU oracle, whole steps (no sampling)", "kind": "oracle", "cores": threads}
+    t = run_steps(get_config("tiny"), 16, np.float64)
+    res["tiny_fp64_16_steps"] = {"s_total": round(sum(t), 3), "ms_per_step": round(1e3 * sum(t) / 16, 2)}
+    t = run_steps(get_config("tiny"), 16, np.float64, threads=1)
+    res["tiny_fp64_16_steps_1_thread"] = {"s_total": round(sum(t), 3), "ms_per_step": round(1e3 * sum(t) / 16, 2)}
+    t = run_steps(get_config("image", t_index=(32,)), 1, np.float64, threads=1)
+    res["image_fp64_n1_one_step_1_thread"] = {"s": round(t[0], 2), "frames_per_s": round(1.0 / t[0], 4)}
+    print(json.dumps(res), flush=True)
+    cfg = get_config("video13b")
+    t = run_steps(cfg, 2, np.float32)
+    res["video13b_fp32_n2_two_steps"] = {
+        "s_per_step": [round(x, 1) for x in t],
+        "note": "step 1: one row (the entering chunk); step 2: two rows, the first chunk leaves (cache still empty, "
+                "3120 keys per row); a steady-state step attends over 14040 keys"}
+    return res
+
+
 def slo_run(cfg, weights, target_fps: float, steps: int, dev):
     """The SLO-aware batching loop on the real pipeline with a backlog of
     input chunks: each step the scheduler picks how many enter; a step's
@@ -486,6 +537,10 @@ def main():
               "described in DESIGN.md and not run.", file=sys.stderr)
         sys.exit(2)
 
+    if args.cpu_full:
+        print(json.dumps(cpu_full()))
+        return
+
     import torch
 
     from streaming_diffusion_amd.runner import random_device_weights
@@ -508,6 +563,26 @@ def main():
         cfg = get_config(args.workload, t_index=slot_indices(args.n_slots), chunks_per_step=max(2, args.chunks), **kw)
         weights = random_device_weights(cfg, seed=gen.SEED_WEIGHTS)
         print(json.dumps(slo_run(cfg, weights, args.slo_fps, args.steps, dev)))
+        return
+    if args.slo_plan > 0:
+        from streaming_diffusion_amd.slo import fit_rows_model, plan_steps_and_batch
+        base = get_config(args.workload)
+        weights = random_device_weights(base, seed=gen.SEED_WEIGHTS)
+        table = {}
+        for n in (1, 2, 4):
+            for B in (1, 2, 4):
+                cfg = get_config(args.workload, t_index=slot_indices(n), chunks_per_step=B, **kw)
+                r = measure(cfg, weights, args.steps, max(args.warmup, n + 1), dev, graph=args.graph)
+                table[(B, n)] = r["ms_per_step"] * 1e-3
+        alpha, beta = fit_rows_model([(B * n, t) for (B, n), t in table.items()])
+        plan = plan_steps_and_batch(lambda B, n: alpha + beta * B * n, base.latent_t, args.slo_plan, 4, (1, 2, 4))
+        print(json.dumps({"metric": "SLO plan: denoising steps and chunks per step for a frame-rate target",
+                          "target_fps": args.slo_plan, "workload": args.workload,
+                          "measured_ms": {f"B{B}_n{n}": round(t * 1e3, 3) for (B, n), t in sorted(table.items())},
+                          "latency_model_ms": {"fixed": round(alpha * 1e3, 3), "per_row": round(beta * 1e3, 3)},
+                          "plan": {"n": plan[0], "B": plan[1],
+                                   "predicted_fps": round(plan[1] * base.latent_t / (alpha + beta * plan[0] * plan[1]), 2)},
+                          "graph": bool(args.graph)}))
         return
     if args.sweep:
         # weights do not depend on n or B

@@ -76,3 +76,52 @@ class SLOBatchScheduler:
             if self.rate(b, model) >= (1.0 - self.knee_tol) * best:
                 return b
         return cap
+
+
+def fit_rows_model(samples) -> Tuple[float, float]:
+    """(alpha, beta) of L = alpha + beta * rows by least squares over measured
+    (rows, seconds) pairs, rows = B * n per forward.  Every row of a Stream
+    Batch forward costs the same (each is one chunk at one denoising slot), so
+    a sweep over B and n collapses onto one line in rows; the intercept is the
+    per-step cost that does not grow with the batch (in the pages' model, the
+    weight traffic)."""
+    pts = [(float(r), float(t)) for r, t in samples]
+    if len(pts) < 2 or len({r for r, _ in pts}) < 2:
+        raise ValueError("need latencies at two different row counts")
+    n = len(pts)
+    mr = sum(r for r, _ in pts) / n
+    mt = sum(t for _, t in pts) / n
+    beta = sum((r - mr) * (t - mt) for r, t in pts) / sum((r - mr) ** 2 for r, _ in pts)
+    beta = max(beta, 1e-12)
+    return max(mt - beta * mr, 0.0), beta
+
+
+def plan_steps_and_batch(latency, frames_per_chunk: int, target_fps: float, b_max: int, n_options,
+                         knee_tol: float = 0.05) -> Tuple[int, int]:
+    """Denoising steps n and chunks per step B for a frame-rate target.
+
+    StreamDiffusionV2 summary, SLO-aware batching: the scheduler sizes the
+    stream batch from the target rate, and the denoising steps multiply the
+    rows of every forward (B chunks at n slots each), so n trades image
+    quality against rate.  Quality first: the largest n in n_options for
+    which some B <= b_max reaches f(B, n) = B * T / L(B, n) >= target, with
+    the smallest such B (least latency per frame).  When no pair reaches the
+    target: the fewest steps, and on that curve the smallest B within
+    knee_tol of its best rate.  `latency(B, n)` returns seconds per step."""
+    if frames_per_chunk < 1 or b_max < 1 or target_fps <= 0 or not n_options:
+        raise ValueError("frames_per_chunk, b_max, target_fps and n_options must be positive / non-empty")
+    T = frames_per_chunk
+
+    def rate(b, n):
+        return b * T / latency(b, n)
+
+    for n in sorted(n_options, reverse=True):
+        for b in range(1, b_max + 1):
+            if rate(b, n) >= target_fps:
+                return n, b
+    n = min(n_options)
+    best = max(rate(b, n) for b in range(1, b_max + 1))
+    for b in range(1, b_max + 1):
+        if rate(b, n) >= (1.0 - knee_tol) * best:
+            return n, b
+    return n, b_max

@@ -82,3 +82,55 @@ def test_invalid_arguments():
         SLOBatchScheduler(0, 30.0, 4)
     with pytest.raises(ValueError):
         SLOBatchScheduler(2, 0.0, 4)
+
+
+# ------------------------------------------------------------------ denoising steps and batch together
+from streaming_diffusion_amd.slo import fit_rows_model, plan_steps_and_batch
+
+
+def brute_plan(lat, T, target, cap, ns, tol=0.05):
+    ok = [(n, b) for n in ns for b in range(1, cap + 1) if b * T / lat(b, n) >= target]
+    if ok:
+        n = max(n for n, _ in ok)
+        return n, min(b for m, b in ok if m == n)
+    n = min(ns)
+    rates = {b: b * T / lat(b, n) for b in range(1, cap + 1)}
+    best = max(rates.values())
+    return n, min(b for b in rates if rates[b] >= (1 - tol) * best)
+
+
+REGIMES = {
+    # below the knee: a fixed weight-streaming cost per step plus a cost per row
+    "memory": lambda b, n: 0.012 + 0.0015 * b * n,
+    # above the knee: every row costs the same (the video DiTs on one MI355X)
+    "compute": lambda b, n: 0.020 * b * n,
+    # in between
+    "mixed": lambda b, n: 0.005 + 0.006 * b * n,
+}
+
+
+@pytest.mark.parametrize("regime", list(REGIMES))
+@pytest.mark.parametrize("target", [10.0, 30.0, 60.0, 120.0, 400.0])
+def test_plan_matches_brute_force(regime, target):
+    lat = REGIMES[regime]
+    got = plan_steps_and_batch(lat, 2, target, 8, (1, 2, 4))
+    assert got == brute_plan(lat, 2, target, 8, (1, 2, 4))
+
+
+def test_plan_prefers_more_steps_when_the_target_allows():
+    lat = REGIMES["memory"]
+    # 4 steps reach 30 frames/s with one chunk: 2 / (0.012 + 0.006) = 111 frames/s
+    assert plan_steps_and_batch(lat, 2, 30.0, 8, (1, 2, 4)) == (4, 1)
+    # compute-bound: frames/s = 2 / (0.02 n) does not depend on B; 60 frames/s needs n = 1
+    assert plan_steps_and_batch(REGIMES["compute"], 2, 60.0, 8, (1, 2, 4)) == (1, 1)
+    # unreachable: fewest steps, and B = 1 since batching never pays
+    assert plan_steps_and_batch(REGIMES["compute"], 2, 500.0, 8, (1, 2, 4)) == (1, 1)
+
+
+def test_rows_model_recovers_the_line_from_a_sweep():
+    lat = REGIMES["mixed"]
+    samples = [(b * n, lat(b, n)) for b in (1, 2, 4) for n in (1, 2, 4)]
+    alpha, beta = fit_rows_model(samples)
+    assert alpha == pytest.approx(0.005) and beta == pytest.approx(0.006)
+    with pytest.raises(ValueError):
+        fit_rows_model([(2, 0.1), (2, 0.11)])
