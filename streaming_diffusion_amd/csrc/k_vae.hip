@@ -9,6 +9,21 @@
 
 namespace sdk {
 
+// 16-bit activation element: bf16, or fp16 (H16) for the Stream-VAE's own
+// chain, whose values are bounded (normalised activations, unit-gain
+// convolutions) and gain three mantissa bits in fp16 at the same matrix-core
+// rate.  Data movement treats both as raw 16-bit words.
+template <bool H16>
+SD_DEV bf16 to16(float v) {
+  if constexpr (H16) return __builtin_bit_cast(bf16, (f16)v);
+  else return (bf16)v;
+}
+template <bool H16>
+SD_DEV float from16(bf16 v) {
+  if constexpr (H16) return (float)__builtin_bit_cast(f16, v);
+  else return (float)v;
+}
+
 // k index -> (tap, channel): 16-byte chunks of 8 channels never straddle a
 // tap because Cin is a multiple of 8.
 SD_DEV const bf16* conv_src(const ConvArgs& a, int t, int y, int x, int k, int HW) {
@@ -43,7 +58,7 @@ SD_DEV int cv_swz(int row) {
   return (row / (128 / BK)) & (BK / 8 - 1);
 }
 
-template <int BN, int BK>
+template <int BN, int BK, bool H16>
 __global__ __launch_bounds__(256) void conv3d_mfma_kernel(ConvArgs a) {
   constexpr int WMW = BN >= 64 ? 2 : 4, WNW = 4 / WMW;   // waves along positions / channels
   constexpr int TMP = CV_BM / WMW, TNC = BN / WNW;      // wave tile: positions x channels
@@ -141,7 +156,13 @@ __global__ __launch_bounds__(256) void conv3d_mfma_kernel(ConvArgs a) {
 #pragma unroll
       for (int i = 0; i < NB; ++i)
 #pragma unroll
-        for (int j = 0; j < MB; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i], fp[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < MB; ++j) {
+          if constexpr (H16)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, fw[i]),
+                                                               __builtin_bit_cast(f16x8, fp[j]), acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i], fp[j], acc[i][j], 0, 0, 0);
+        }
     }
     if (kt + 1 < KT) store(buf ^ 1);
     __syncthreads();
@@ -168,7 +189,7 @@ __global__ __launch_bounds__(256) void conv3d_mfma_kernel(ConvArgs a) {
         } else {
           bf16x4 o;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = (bf16)(acc[i][j][4 * g + e] + (a.b ? (float)a.b[n + e] : 0.f));
+          for (int e = 0; e < 4; ++e) o[e] = to16<H16>(acc[i][j][4 * g + e] + (a.b ? (float)a.b[n + e] : 0.f));
           *(bf16x4*)(a.y + (int64_t)p * a.Cout + n) = o;
         }
       }
@@ -182,13 +203,16 @@ hipError_t conv3d(hipStream_t s, const ConvArgs& a) {
   if (M * a.Cout >= (1ll << 31) || M * a.Cin >= (1ll << 31) || 27ll * a.Cin * a.Cout >= (1ll << 31))
     return hipErrorInvalidValue;
   const int tiles_m = (int)((M + CV_BM - 1) / CV_BM);
-  if (a.Cout <= 32) {
-    conv3d_mfma_kernel<32, CV_BK><<<tiles_m * ((a.Cout + 31) / 32), 256, 0, s>>>(a);
-  } else if (a.Cout <= 64) {
-    conv3d_mfma_kernel<64, CV_BK><<<tiles_m * ((a.Cout + 63) / 64), 256, 0, s>>>(a);
-  } else {
-    conv3d_mfma_kernel<128, CV_BK><<<tiles_m * ((a.Cout + 127) / 128), 256, 0, s>>>(a);
-  }
+#define SD_CONV_LAUNCH(BN)                                                                  \
+  do {                                                                                      \
+    const unsigned g = (unsigned)(tiles_m * ((a.Cout + BN - 1) / BN));                      \
+    if (a.h16) conv3d_mfma_kernel<BN, CV_BK, true><<<g, 256, 0, s>>>(a);                    \
+    else conv3d_mfma_kernel<BN, CV_BK, false><<<g, 256, 0, s>>>(a);                         \
+  } while (0)
+  if (a.Cout <= 32) SD_CONV_LAUNCH(32);
+  else if (a.Cout <= 64) SD_CONV_LAUNCH(64);
+  else SD_CONV_LAUNCH(128);
+#undef SD_CONV_LAUNCH
   return hipGetLastError();
 }
 
@@ -196,7 +220,7 @@ hipError_t conv3d(hipStream_t s, const ConvArgs& a) {
 // RMS norm over the C channels of a position, gain g, then SiLU, in place.
 // C / 8 lanes per position, 8 channels each; the sum of squares is reduced
 // with butterfly shuffles inside the lane group (every lane takes part).
-template <int C>
+template <int C, bool H16>
 __global__ __launch_bounds__(256) void norm_silu_kernel(bf16* __restrict__ x, const bf16* __restrict__ g, int64_t P,
                                                         float eps) {
   constexpr int LP = C / 8;
@@ -209,7 +233,7 @@ __global__ __launch_bounds__(256) void norm_silu_kernel(bf16* __restrict__ x, co
   float f[8], ss = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    f[e] = (float)v[e];
+    f[e] = from16<H16>(v[e]);
     ss = fmaf(f[e], f[e], ss);
   }
 #pragma unroll
@@ -221,28 +245,35 @@ __global__ __launch_bounds__(256) void norm_silu_kernel(bf16* __restrict__ x, co
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float n = f[e] * r * (float)gv[e];
-    o[e] = (bf16)(n / (1.0f + __expf(-n)));
+    o[e] = to16<H16>(n / (1.0f + __expf(-n)));
   }
   *(bf16x8*)(x + p * C + c0) = o;
 }
 
-hipError_t norm_silu(hipStream_t s, void* x, const void* g, int64_t P, int C, float eps) {
+hipError_t norm_silu(hipStream_t s, void* x, const void* g, int64_t P, int C, float eps, bool h16) {
   const int64_t n = P * (C / 8);
   const unsigned grid = (unsigned)((n + 255) / 256);
+#define SD_NS(CC)                                                                                 \
+  case CC:                                                                                        \
+    if (h16) norm_silu_kernel<CC, true><<<grid, 256, 0, s>>>((bf16*)x, (const bf16*)g, P, eps);   \
+    else norm_silu_kernel<CC, false><<<grid, 256, 0, s>>>((bf16*)x, (const bf16*)g, P, eps);      \
+    break;
   switch (C) {
-    case 16: norm_silu_kernel<16><<<grid, 256, 0, s>>>((bf16*)x, (const bf16*)g, P, eps); break;
-    case 32: norm_silu_kernel<32><<<grid, 256, 0, s>>>((bf16*)x, (const bf16*)g, P, eps); break;
-    case 64: norm_silu_kernel<64><<<grid, 256, 0, s>>>((bf16*)x, (const bf16*)g, P, eps); break;
-    case 128: norm_silu_kernel<128><<<grid, 256, 0, s>>>((bf16*)x, (const bf16*)g, P, eps); break;
-    case 256: norm_silu_kernel<256><<<grid, 256, 0, s>>>((bf16*)x, (const bf16*)g, P, eps); break;
+    SD_NS(16)
+    SD_NS(32)
+    SD_NS(64)
+    SD_NS(128)
+    SD_NS(256)
     default: return hipErrorInvalidValue;
   }
+#undef SD_NS
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
 // 2 x 2 (x 2 in time) average pooling and nearest 2x upsampling, one thread
 // per 8-channel chunk of an output position.
+template <bool H16>
 __global__ void pool_kernel(const bf16* __restrict__ x, bf16* __restrict__ y, int T, int H, int W, int C,
                             int temporal) {
   const int To = temporal ? T / 2 : T, Ho = H / 2, Wo = W / 2, C8 = C / 8;
@@ -262,12 +293,12 @@ __global__ void pool_kernel(const bf16* __restrict__ x, bf16* __restrict__ y, in
         const int t = temporal ? 2 * to + dt : to;
         const bf16x8 v = *(const bf16x8*)(x + (((int64_t)t * H + 2 * yo + dy) * W + 2 * xo + dx) * C + c);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += (float)v[e];
+        for (int e = 0; e < 8; ++e) acc[e] += from16<H16>(v[e]);
       }
   const float sc = temporal ? 0.125f : 0.25f;
   bf16x8 o;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = (bf16)(acc[e] * sc);
+  for (int e = 0; e < 8; ++e) o[e] = to16<H16>(acc[e] * sc);
   *(bf16x8*)(y + i * 8) = o;
 }
 
@@ -286,7 +317,7 @@ __global__ void upsample_kernel(const bf16* __restrict__ x, bf16* __restrict__ y
   *(bf16x8*)(y + i * 8) = *(const bf16x8*)(x + (((int64_t)t * H + yo / 2) * W + xo / 2) * C + c);
 }
 
-hipError_t resample(hipStream_t s, const void* x, void* y, int T, int H, int W, int C, int mode) {
+hipError_t resample(hipStream_t s, const void* x, void* y, int T, int H, int W, int C, int mode, bool h16) {
   // mode 0 pool 2x2, 1 pool 2x2x2, 2 upsample 2x2, 3 upsample 2x2x2
   if ((C & 7) || T < 1 || H < 1 || W < 1 || mode < 0 || mode > 3) return hipErrorInvalidValue;
   const bool pool = mode < 2, temporal = mode & 1;
@@ -298,8 +329,10 @@ hipError_t resample(hipStream_t s, const void* x, void* y, int T, int H, int W, 
     n = (int64_t)(temporal ? 2 * T : T) * (2 * H) * (2 * W) * (C / 8);
   }
   const unsigned g = (unsigned)((n + 255) / 256);
-  if (pool)
-    pool_kernel<<<g, 256, 0, s>>>((const bf16*)x, (bf16*)y, T, H, W, C, temporal);
+  if (pool && h16)
+    pool_kernel<true><<<g, 256, 0, s>>>((const bf16*)x, (bf16*)y, T, H, W, C, temporal);
+  else if (pool)
+    pool_kernel<false><<<g, 256, 0, s>>>((const bf16*)x, (bf16*)y, T, H, W, C, temporal);
   else
     upsample_kernel<<<g, 256, 0, s>>>((const bf16*)x, (bf16*)y, T, H, W, C, temporal);
   return hipGetLastError();
@@ -307,6 +340,7 @@ hipError_t resample(hipStream_t s, const void* x, void* y, int T, int H, int W, 
 
 // fp32 channels-first [T][C][H][W] -> bf16 channels-last [T][H][W][Cp],
 // channels C .. Cp-1 zero; one thread per (position, 8-channel chunk).
+template <bool H16>
 __global__ void to_channels_last_kernel(const float* __restrict__ x, bf16* __restrict__ y, int T, int C, int HW,
                                         int Cp) {
   const int C8 = Cp / 8;
@@ -319,15 +353,30 @@ __global__ void to_channels_last_kernel(const float* __restrict__ x, bf16* __res
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int c = c0 + e;
-    o[e] = (bf16)(c < C ? x[((int64_t)t * C + c) * HW + hw] : 0.f);
+    o[e] = to16<H16>(c < C ? x[((int64_t)t * C + c) * HW + hw] : 0.f);
   }
   *(bf16x8*)(y + i * 8) = o;
 }
 
-hipError_t to_channels_last(hipStream_t s, const float* x, void* y, int T, int C, int HW, int Cp) {
+hipError_t to_channels_last(hipStream_t s, const float* x, void* y, int T, int C, int HW, int Cp, bool h16) {
   if (Cp < C || (Cp & 7) || T < 1 || HW < 1) return hipErrorInvalidValue;
   const int64_t n = (int64_t)T * HW * (Cp / 8);
-  to_channels_last_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(x, (bf16*)y, T, C, HW, Cp);
+  if (h16)
+    to_channels_last_kernel<true><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(x, (bf16*)y, T, C, HW, Cp);
+  else
+    to_channels_last_kernel<false><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(x, (bf16*)y, T, C, HW, Cp);
+  return hipGetLastError();
+}
+
+// bf16 -> fp16, n elements (the Stream-VAE's weights, once at create)
+__global__ void cast_h16_kernel(const bf16* __restrict__ x, f16* __restrict__ y, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) y[i] = (f16)(float)x[i];
+}
+
+hipError_t cast_to_h16(hipStream_t s, const void* x, void* y, int64_t n) {
+  if (n <= 0) return hipSuccess;
+  cast_h16_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>((const bf16*)x, (f16*)y, n);
   return hipGetLastError();
 }
 

@@ -136,14 +136,18 @@ struct ConvArgs {
   bf16* y;
   float* ycf;
   int T, H, W, Cin, Cout;
+  bool h16;             // x, cache, w and y hold fp16 words (b stays bf16)
 };
 hipError_t conv3d(hipStream_t s, const ConvArgs& a);
-// In place on bf16 [P][C]: RMS norm over C (gain g bf16 [C]) then SiLU.
-hipError_t norm_silu(hipStream_t s, void* x, const void* g, int64_t P, int C, float eps);
+// In place on [P][C] (bf16, or fp16 with h16): RMS norm over C (gain g bf16
+// [C]) then SiLU.
+hipError_t norm_silu(hipStream_t s, void* x, const void* g, int64_t P, int C, float eps, bool h16 = false);
 // bf16 channels-last resampling: mode 0 pool 2x2, 1 pool 2x2x2, 2 nearest
 // upsample 2x2, 3 nearest upsample 2x2x2; (T, H, W) is the input's shape.
-hipError_t resample(hipStream_t s, const void* x, void* y, int T, int H, int W, int C, int mode);
-// fp32 [T][C][H*W] -> bf16 [T][H*W][Cp], channels C .. Cp-1 zero.
-hipError_t to_channels_last(hipStream_t s, const float* x, void* y, int T, int C, int HW, int Cp);
+hipError_t resample(hipStream_t s, const void* x, void* y, int T, int H, int W, int C, int mode, bool h16 = false);
+// fp32 [T][C][H*W] -> bf16 (fp16 with h16) [T][H*W][Cp], channels C .. Cp-1 zero.
+hipError_t to_channels_last(hipStream_t s, const float* x, void* y, int T, int C, int HW, int Cp, bool h16 = false);
+// bf16 -> fp16 elementwise
+hipError_t cast_to_h16(hipStream_t s, const void* x, void* y, int64_t n);
 
 }  // namespace sdk

@@ -315,6 +315,7 @@ sd_status sd_k_conv3d(const void* x, const void* cache, const void* w, const voi
   if (Cin % 8) return SD_ERR_SHAPE;
   if ((int64_t)T * H * W * (Cin > Cout ? Cin : Cout) >= (1ll << 31)) return SD_ERR_SHAPE;
   sdk::ConvArgs a;
+  a.h16 = false;
   a.x = (const bf16*)x;
   a.cache = (const bf16*)cache;
   a.w = (const bf16*)w;

@@ -1,7 +1,12 @@
 // sd_vae_*: the Stream-VAE runtime (see include/sd_vae.h).  Per chunk the
 // layers run in order on the caller's stream; each convolution reads its
 // cache (the previous chunk's last two input frames) and then replaces it
-// with the last two frames of its own input.
+// with the last two frames of its own input.  Activations, caches and the
+// convolution weights (copied at create from the caller's bf16) are fp16:
+// the chain stores its activations nine times on the decoder path, and
+// fp16's three extra mantissa bits keep the accumulated rounding an order
+// below bf16's at the same matrix-core rate (all values are bounded: inputs
+// of unit scale, RMS-normalised activations, unit-gain convolutions).
 #include <algorithm>
 #include <cstring>
 #include <string>
@@ -16,7 +21,8 @@ struct VaeLayer {
   int mode;          // resampling of the layer's input: -1 none, else sdk::resample's mode
   bool norm;
   int T, H, W;       // shape of the convolution's input (after resampling)
-  void* cache;       // bf16 [2][H][W][cin]
+  void* cache;       // fp16 [2][H][W][cin]
+  void* w16;         // fp16 copy of the weights [cout][27 cin]
 };
 
 bool width_ok(int c) { return c == 16 || c == 32 || c == 64 || c == 128 || c == 256; }
@@ -37,16 +43,16 @@ int validate(const sd_vae_config& c, std::string* err) {
 void layers_of(const sd_vae_config& c, VaeLayer* L) {
   const int T = c.latent_t, h = c.latent_h, w = c.latent_w, z = c.latent_c;
   const int Tp = 2 * T, H = 8 * h, W = 8 * w;
-  L[SD_VAE_E0] = {8, c.c1, -1, true, Tp, H, W, nullptr};
-  L[SD_VAE_E1] = {c.c1, c.c2, 0, true, Tp, H / 2, W / 2, nullptr};
-  L[SD_VAE_E2] = {c.c2, c.c3, 0, true, Tp, H / 4, W / 4, nullptr};
-  L[SD_VAE_E3] = {c.c3, c.c3, 1, true, T, h, w, nullptr};
-  L[SD_VAE_E_OUT] = {c.c3, z, -1, false, T, h, w, nullptr};
-  L[SD_VAE_D0] = {z, c.c3, -1, true, T, h, w, nullptr};
-  L[SD_VAE_D1] = {c.c3, c.c3, 3, true, Tp, H / 4, W / 4, nullptr};
-  L[SD_VAE_D2] = {c.c3, c.c2, 2, true, Tp, H / 2, W / 2, nullptr};
-  L[SD_VAE_D3] = {c.c2, c.c1, 2, true, Tp, H, W, nullptr};
-  L[SD_VAE_D_OUT] = {c.c1, 3, -1, false, Tp, H, W, nullptr};
+  L[SD_VAE_E0] = {8, c.c1, -1, true, Tp, H, W, nullptr, nullptr};
+  L[SD_VAE_E1] = {c.c1, c.c2, 0, true, Tp, H / 2, W / 2, nullptr, nullptr};
+  L[SD_VAE_E2] = {c.c2, c.c3, 0, true, Tp, H / 4, W / 4, nullptr, nullptr};
+  L[SD_VAE_E3] = {c.c3, c.c3, 1, true, T, h, w, nullptr, nullptr};
+  L[SD_VAE_E_OUT] = {c.c3, z, -1, false, T, h, w, nullptr, nullptr};
+  L[SD_VAE_D0] = {z, c.c3, -1, true, T, h, w, nullptr, nullptr};
+  L[SD_VAE_D1] = {c.c3, c.c3, 3, true, Tp, H / 4, W / 4, nullptr, nullptr};
+  L[SD_VAE_D2] = {c.c3, c.c2, 2, true, Tp, H / 2, W / 2, nullptr, nullptr};
+  L[SD_VAE_D3] = {c.c2, c.c1, 2, true, Tp, H, W, nullptr, nullptr};
+  L[SD_VAE_D_OUT] = {c.c1, 3, -1, false, Tp, H, W, nullptr, nullptr};
 }
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -62,6 +68,7 @@ size_t act_bytes(const VaeLayer* L) {
 }
 
 size_t cache_bytes(const VaeLayer& l) { return align256((size_t)2 * l.H * l.W * l.cin * 2); }
+size_t weight_bytes(const VaeLayer& l) { return align256((size_t)27 * l.cin * l.cout * 2); }
 
 }  // namespace
 
@@ -96,13 +103,14 @@ sd_status run_layers(sd_vae* v, int first, int last, int cur, int T, int H, int 
     VaeLayer& l = v->L[li];
     int in = cur;
     if (l.mode >= 0) {
-      VHIP(sdk::resample(v->st, v->act[cur], v->act[cur ^ 1], T, H, W, C, l.mode));
+      VHIP(sdk::resample(v->st, v->act[cur], v->act[cur ^ 1], T, H, W, C, l.mode, true));
       in = cur ^ 1;
     }
     sdk::ConvArgs a;
     a.x = (const bf16*)v->act[in];
     a.cache = (const bf16*)l.cache;
-    a.w = (const bf16*)v->w.w[li];
+    a.w = (const bf16*)l.w16;
+    a.h16 = true;
     a.b = (const bf16*)v->w.b[li];
     a.y = li == last ? nullptr : (bf16*)v->act[in ^ 1];
     a.ycf = li == last ? out : nullptr;
@@ -117,7 +125,8 @@ sd_status run_layers(sd_vae* v, int first, int last, int cur, int T, int H, int 
     VHIP(hipMemcpyAsync(l.cache, (const char*)v->act[in] + (size_t)(l.T - 2) * frame * 2, 2 * frame * 2,
                         hipMemcpyDeviceToDevice, v->st));
     if (li == last) break;
-    if (l.norm) VHIP(sdk::norm_silu(v->st, v->act[in ^ 1], v->w.g[li], (int64_t)l.T * l.H * l.W, l.cout, 1e-6f));
+    if (l.norm)
+      VHIP(sdk::norm_silu(v->st, v->act[in ^ 1], v->w.g[li], (int64_t)l.T * l.H * l.W, l.cout, 1e-6f, true));
     cur = in ^ 1;
     T = l.T;
     H = l.H;
@@ -136,7 +145,7 @@ size_t sd_vae_workspace_bytes(const sd_vae_config* cfg) {
   VaeLayer L[SD_VAE_LAYERS];
   layers_of(*cfg, L);
   size_t n = 2 * act_bytes(L);
-  for (int i = 0; i < SD_VAE_LAYERS; ++i) n += cache_bytes(L[i]);
+  for (int i = 0; i < SD_VAE_LAYERS; ++i) n += cache_bytes(L[i]) + weight_bytes(L[i]);
   return n;
 }
 
@@ -169,6 +178,14 @@ sd_status sd_vae_create(const sd_vae_config* cfg, const sd_vae_weights* w, void*
     p += cache_bytes(v->L[i]);
   }
   v->cache_total = (size_t)(p - (char*)v->cache_base);
+  for (int i = 0; i < SD_VAE_LAYERS; ++i) {
+    v->L[i].w16 = p;
+    p += weight_bytes(v->L[i]);
+    if (sdk::cast_to_h16(v->st, w->w[i], v->L[i].w16, (int64_t)27 * v->L[i].cin * v->L[i].cout) != hipSuccess) {
+      delete v;
+      return SD_ERR_HIP;
+    }
+  }
   const sd_status r = sd_vae_reset(v);
   if (r != SD_OK) {
     delete v;
@@ -189,7 +206,7 @@ sd_status sd_vae_encode(sd_vae* v, const float* pixels, float* latent) {
   if (!pixels || !latent) return set_err(v, SD_ERR_ARG, "null pixels or latent");
   const sd_vae_config& c = v->cfg;
   const int Tp = 2 * c.latent_t, H = 8 * c.latent_h, W = 8 * c.latent_w;
-  VHIP(sdk::to_channels_last(v->st, pixels, v->act[0], Tp, 3, H * W, 8));
+  VHIP(sdk::to_channels_last(v->st, pixels, v->act[0], Tp, 3, H * W, 8, true));
   return run_layers(v, SD_VAE_E0, SD_VAE_E_OUT, 0, Tp, H, W, 8, latent);
 }
 
@@ -197,7 +214,8 @@ sd_status sd_vae_decode(sd_vae* v, const float* latent, float* pixels) {
   if (!v) return SD_ERR_ARG;
   if (!pixels || !latent) return set_err(v, SD_ERR_ARG, "null pixels or latent");
   const sd_vae_config& c = v->cfg;
-  VHIP(sdk::to_channels_last(v->st, latent, v->act[0], c.latent_t, c.latent_c, c.latent_h * c.latent_w, c.latent_c));
+  VHIP(sdk::to_channels_last(v->st, latent, v->act[0], c.latent_t, c.latent_c, c.latent_h * c.latent_w, c.latent_c,
+                             true));
   return run_layers(v, SD_VAE_D0, SD_VAE_D_OUT, 0, c.latent_t, c.latent_h, c.latent_w, c.latent_c, pixels);
 }
 

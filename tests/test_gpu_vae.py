@@ -135,13 +135,12 @@ def test_conv3d_full_video_shape_sampled(lib, layer):
     check_close(got, ref, "bf16", f"{layer} sampled", stored_bf16=(layer == "d3"))
 
 
-# Whole encoder / decoder chains store every activation in bf16: the decoder
-# path rounds 9 times (its input, then each of 4 convolution outputs and 4
-# norm outputs) through layers of unit gain, each rounding at most 2^-8
-# relative, so the worst element can drift by about 9 * 2^-8 = 3.5 % of the
-# RMS; the aggregate (RMS of the error) stays near one rounding.
-VAE_MAX_TOL = 6e-2
-VAE_RMS_TOL = 1.5e-2
+# Whole encoder / decoder chains: the bf16 bar of the path (2e-2 max-abs over
+# RMS).  The chains store their activations in fp16 (2^-11 relative per
+# rounding, 9 roundings on the decoder path through layers of unit gain), so
+# the bar holds with margin; the RMS of the error stays near one rounding.
+VAE_MAX_TOL = 2e-2
+VAE_RMS_TOL = 5e-3
 
 
 def check_vae(got, ref, what):
@@ -150,6 +149,7 @@ def check_vae(got, ref, what):
     rms = np.sqrt(np.mean(ref * ref))
     e_max = np.max(np.abs(got - ref)) / rms
     e_rms = np.sqrt(np.mean((got - ref) ** 2)) / rms
+    print(f"  {what}: max-abs/RMS {e_max:.3e}, RMS {e_rms:.3e}", flush=True)
     assert e_max <= VAE_MAX_TOL and e_rms <= VAE_RMS_TOL, f"{what}: max-abs/RMS {e_max:.3e}, RMS {e_rms:.3e}"
 
 
