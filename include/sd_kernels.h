@@ -75,6 +75,8 @@ typedef struct {
   void* workspace;             /* optional device scratch (256-byte aligned): with M <= 256 the
                                   product is split over K into fp32 partials held here */
   size_t workspace_bytes;
+  const void* wpack;           /* optional: W rearranged by sd_k_pack_weight(); with M <= 256 and a
+                                  workspace the product reads W from here (NULL: from W) */
 } sd_gemm_epi;
 
 /* One bf16 GEMM with the epilogue e->mode, on the kernels and launch
@@ -82,6 +84,19 @@ typedef struct {
  * W [N][K] bf16, K a multiple of 8.  Destinations must not alias operands. */
 sd_status sd_k_gemm_epi(const void* A, const void* W, int32_t M, int32_t N, int32_t K, const sd_gemm_epi* e,
                         void* stream);
+
+/* W [N][K] (bf16 or fp16, K a multiple of 64) rearranged for the few-row
+ * product of sd_k_gemm_epi (sd_gemm_epi.wpack): 16-byte chunk
+ * (nb, kt, kk, lane), nb = 0 .. ceil(N/32)-1, kt = 0 .. K/64-1, kk = 0 .. 3,
+ * lane = 0 .. 63, holds W[32 nb + lane % 32][64 kt + 16 kk + 8 (lane / 32) .. + 7],
+ * rows past N zero, so that each 32 x 16 matrix-core operand of a wave is one
+ * contiguous 1 KB load.  Below the batch knee the product is bound by reading
+ * W (StreamDiffusionV2 summary, SLO-aware batching scheduler: latency model);
+ * sd_stream_create() keeps such a copy of the block weights when every forward
+ * has at most 256 tokens.  out: device, sd_k_pack_weight_bytes() bytes,
+ * 16-byte aligned, not overlapping W.  Enqueued on stream. */
+size_t sd_k_pack_weight_bytes(int32_t N, int32_t K);
+sd_status sd_k_pack_weight(const void* W, int32_t N, int32_t K, void* out, void* stream);
 
 /* Elements (float pairs) of the 3D RoPE table for head dim hd: the temporal
  * section (positions x dt/2), then height (Hp x dh/2), then width (Wp x dw/2),

@@ -186,7 +186,12 @@ typedef struct sd_stream sd_stream;
 size_t sd_stream_workspace_bytes(const sd_stream_config* cfg);
 
 /* Validate cfg, carve the workspace, build the schedule and RoPE tables and
- * zero the state.  hip_stream is a hipStream_t (NULL = default stream). */
+ * zero the state.  hip_stream is a hipStream_t (NULL = default stream).
+ * In bf16 the workspace also receives copies of some weights made here: the
+ * patch-embedding and head weights side by side twice (their fp32 inputs are
+ * read as hi + lo bf16 pairs), and, when a chunk has at most 256 tokens, the
+ * block weights rearranged for the few-row product (sd_k_pack_weight).  A
+ * caller that changes the weights afterwards creates the stream again. */
 sd_status sd_stream_create(const sd_stream_config* cfg, const sd_weights* w, void* workspace,
                            size_t workspace_bytes, void* hip_stream, sd_stream** out);
 

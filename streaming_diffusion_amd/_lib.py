@@ -100,7 +100,8 @@ class sd_gemm_epi(C.Structure):
                 ("rope", C.c_int32), ("Hp", C.c_int32), ("Wp", C.c_int32), ("rope_table", C.c_void_p),
                 ("rope_positions", C.c_int32), ("t0", C.c_int32 * SD_MAX_ROWS), ("eps", C.c_void_p),
                 ("C", C.c_int32), ("Hl", C.c_int32), ("Wl", C.c_int32), ("p", C.c_int32), ("T", C.c_int32),
-                ("f16", C.c_int32), ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t)]
+                ("f16", C.c_int32), ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
+                ("wpack", C.c_void_p)]
 
 
 SD_LN_PLAIN, SD_LN_F16, SD_LN_SPLIT = 0, 1, 2
@@ -148,6 +149,8 @@ SIGNATURES = {
                                   C.c_int32, C.c_void_p]),
     "sd_k_gemm_epi": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.POINTER(sd_gemm_epi),
                                 C.c_void_p]),
+    "sd_k_pack_weight_bytes": (C.c_size_t, [C.c_int32, C.c_int32]),
+    "sd_k_pack_weight": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]),
     "sd_k_rope_table_pairs": (C.c_size_t, [C.c_int32, C.c_int32, C.c_int32, C.c_int32]),
     "sd_k_rope_tables": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_double, C.c_void_p]),
     "sd_k_ln_mod": (C.c_int, [C.c_int32, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,

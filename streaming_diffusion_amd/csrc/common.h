@@ -128,9 +128,13 @@ struct Epi {
   // EPI_HEAD
   float* eps;           // [R][T][C][Hl][Wl]
   int C, Hl, Wl, p, T;
-  // split over K for few rows: fp32 partials [ksplit][M][N] (capacity
+  // split over K for few rows: fp32 partials of ksplit slices, each
+  // ceil(M/128) ceil(N/128) tiles of 128 x 128 in accumulator order (capacity
   // part_cap floats; null: no split); ksplit is set by the dispatch
   float* part;
   int64_t part_cap;
   int ksplit;
+  // the same W in fragment order (pack_weight), read by the few-row product
+  // when set (null: W is read as [N][K])
+  const void* wpack;
 };

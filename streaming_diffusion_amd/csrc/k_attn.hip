@@ -640,12 +640,14 @@ int attention_q_tile(bool bf, int hd) { return !bf ? 64 : 128; }
 int attention_wg_per_cu(bool bf, int hd) { return !bf ? 1 : 2; }
 
 int attention_pick_split(int units, int tiles, int max_split, int concurrent) {
+  // cost ~ rounds of resident workgroups x key tiles per workgroup, plus 4%
+  // per split launch for the partial traffic and the combine pass; ties go
+  // to fewer splits
   int best = 1;
-  double best_cost = (double)((units + concurrent - 1) / concurrent);
-  for (int sp = 2; sp <= max_split; ++sp) {
-    if (tiles / sp < 4) break;
+  double best_cost = (double)((units + concurrent - 1) / concurrent) * tiles;
+  for (int sp = 2; sp <= max_split && sp <= tiles; ++sp) {
     const double rounds = (double)(((int64_t)units * sp + concurrent - 1) / concurrent);
-    const double cost = rounds / sp * 1.04;     // 4% for the partial traffic and the combine pass
+    const double cost = rounds * ((tiles + sp - 1) / sp) * 1.04;
     if (cost < best_cost * 0.98) {
       best_cost = cost;
       best = sp;

@@ -651,9 +651,14 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restric
   }
 }
 
-// Second pass of a split over K: a 64-row x 32-column strip sums the slices'
-// partials in slice order (fixed, so results do not depend on scheduling)
-// and runs the epilogue of MODE on the sum.
+// Second pass of the weight-streaming product.  Its partials are stored in
+// accumulator order, float4 granules [slice][tile][feature block][row block]
+// [g][lane] (tile = 128 features x 128 rows, blocks of 32; lane l of
+// feature block i, row block j holds row 32 j + l % 32, features
+// 32 i + 8 g + 4 (l / 32) + 0..3), so both passes move whole 1 KB wave rows.
+// One workgroup takes one tile, one 64-row strip and one feature block: it
+// sums the K slices in slice order (fixed, so results do not depend on
+// scheduling) and runs the epilogue of MODE on the 64 x 32 strip.
 template <int MODE>
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(int M, int N, Epi E) {
   constexpr int BN = 32, NT = 256, LC = BN + 4;
@@ -661,43 +666,40 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(int M, int N, Epi E) {
   __shared__ int4 rowtab[64];
   __shared__ int t0s[SD_MAX_ROWS];
   const int tid = threadIdx.x;
-  const int tiles_n = (N + BN - 1) / BN;
-  const int m_base = (blockIdx.x / tiles_n) * 64, n0 = (blockIdx.x % tiles_n) * BN;
+  const int tiles_n = (N + 127) / 128, tiles = tiles_n * ((M + 127) / 128);
+  const int tile = blockIdx.x / 8, sp = (blockIdx.x / 4) % 2, i = blockIdx.x % 4;
+  const int m_base = (tile / tiles_n) * 128 + sp * 64, n0 = (tile % tiles_n) * 128 + i * 32;
+  if (m_base >= M || n0 >= N) return;                     // uniform over the workgroup
   if constexpr (MODE == EPI_QKV) {
     if (tid < SD_MAX_ROWS) t0s[tid] = E.t0_dev ? E.t0_dev[tid] : E.t0[tid];
   }
-  // 64 x 32 floats = 512 float4: two per thread
+  const int g = tid / 64, ln = tid % 64;
+  const int64_t slice_st = (int64_t)tiles * 4 * 16 * 64;  // float4 granules per slice
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int idx = tid + h * NT;
-    const int row = idx / (BN / 4), c4 = idx % (BN / 4);
-    const int m = m_base + row, n = n0 + c4 * 4;
+    const float4* src = (const float4*)E.part + (((int64_t)tile * 4 + i) * 16 + (2 * sp + h) * 4 + g) * 64 + ln;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (m < M && n < N) {
-      const float* src = E.part + (int64_t)m * N + n;
-      const int64_t st = (int64_t)M * N;
-      int sl = 0;
-      for (; sl + 4 <= E.ksplit; sl += 4) {
-        float4 v[4];
+    int sl = 0;
+    for (; sl + 4 <= E.ksplit; sl += 4) {
+      float4 v[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = *(const float4*)(src + (sl + u) * st);
+      for (int u = 0; u < 4; ++u) v[u] = src[(sl + u) * slice_st];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          acc.x += v[u].x;
-          acc.y += v[u].y;
-          acc.z += v[u].z;
-          acc.w += v[u].w;
-        }
-      }
-      for (; sl < E.ksplit; ++sl) {
-        const float4 v = *(const float4*)(src + sl * st);
-        acc.x += v.x;
-        acc.y += v.y;
-        acc.z += v.z;
-        acc.w += v.w;
+      for (int u = 0; u < 4; ++u) {
+        acc.x += v[u].x;
+        acc.y += v[u].y;
+        acc.z += v[u].z;
+        acc.w += v[u].w;
       }
     }
-    *(float4*)(stg + row * LC + c4 * 4) = acc;
+    for (; sl < E.ksplit; ++sl) {
+      const float4 v = src[sl * slice_st];
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    *(float4*)(stg + (h * 32 + ln % 32) * LC + 8 * g + 4 * (ln / 32)) = acc;
   }
   __syncthreads();
   epi_rows<MODE>(E, rowtab, m_base, M, tid, t0s);
@@ -727,116 +729,130 @@ hipError_t launch_dma(hipStream_t s, const bf16* A, const bf16* W, int M, int N,
 }
 
 // ---------------------------------------------------------------------------
-// Weight-streaming product for few rows (one tile of up to 128 rows), the
-// regime below the knee where reading W from HBM bounds the GEMM.  C^T = W A^T
-// per workgroup tile of 128 output features x 128 rows over one K slice of
-// KT k-tiles of 64: at kernel start every wave issues its share of the W slice
-// (global -> LDS DMA, KT stages of [128][64] in the swizzled layout of the
-// DMA GEMM) and its own 32 rows of A straight into registers (the MFMA B
-// operand), so the whole slice is in flight at once -- one memory round trip
-// per workgroup instead of one per k-tile.  After one wait the 4 x 4 KT
-// products of each wave run from registers and LDS.  A split over K
-// (E.ksplit > 1) leaves fp32 partials for gemm_reduce_kernel; otherwise the
-// epilogue of MODE runs on 64-row strips as in the DMA GEMM.
-template <int KT, int MODE, bool H16>
+// Weight-streaming product for few rows (tiles of up to 128 rows), the regime
+// below the knee where reading W from HBM bounds the GEMM.  C^T = W A^T per
+// workgroup tile of 128 output features x 128 rows over one K slice of KT
+// k-tiles of 64.  Wave w owns features 32 w .. 32 w + 31 of the tile and all
+// 128 rows.  At kernel start every lane issues its share of the A slice (rows
+// shared by the four waves, staged through registers into swizzled LDS rows)
+// and then its wave's W fragments for the whole slice straight into registers
+// (the MFMA A operand: W never passes through LDS), so the slice is in flight
+// at once -- one memory round trip per workgroup.  The products of k-tile t
+// wait only for that k-tile's W fragments (register loads, which the
+// compiler's counters track exactly), so they start while later k-tiles are
+// still arriving from HBM.  The fp32 accumulators leave as they are, in
+// fragment order, for gemm_reduce_kernel (which sums the K slices and runs
+// the epilogue).  Workgroups are ordered slice-major, so the tiles that read
+// one A slice share an XCD and its L2.
+template <int KT, bool H16, bool PACKED>
 __global__ __launch_bounds__(256) void gemm_wstream_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
                                                            int M, int N, int K, Epi E) {
-  constexpr int BN = 128, BK = 64, NT = 256, LC = BN + 4;
-  constexpr int STAGE = BN * BK;                          // bf16 elements per k-tile of W
-  constexpr int SMEM_BYTES = (KT * STAGE * 2 > 64 * LC * 4) ? KT * STAGE * 2 : 64 * LC * 4;
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[SMEM_BYTES + 64 * 16 + SD_MAX_ROWS * 4];
-  bf16* const ws = (bf16*)lds;
-  int4* const rowtab = (int4*)(lds + SMEM_BYTES);
-  int* const t0s = (int*)(lds + SMEM_BYTES + 64 * 16);
+  constexpr int BN = 128, BK = 64;
+  constexpr int ATILE = 128 * BK;                         // bf16 elements of one k-tile of A
+  __shared__ __attribute__((aligned(1024))) bf16 as[KT * ATILE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ks = E.ksplit > 1 ? E.ksplit : 1;
-  const int tiles_n = (N + BN - 1) / BN;
+  const int tiles_n = (N + BN - 1) / BN, tiles = tiles_n * ((M + 127) / 128);
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int slice = lid % ks, tile = lid / ks;
+  const int slice = lid / tiles, tile = lid % tiles;
   const int n0 = (tile % tiles_n) * BN, m0 = (tile / tiles_n) * 128;
-  const int kbase = slice * KT * BK;                      // dispatch: K = ks * KT * 64
-  // W slice: per k-tile 16 DMA blocks of 8 rows x 128 bytes, 4 per wave
-  {
-    const int lrow = lane >> 3, lpos = lane & 7;
+  const int kbase = slice * KT * BK;                      // dispatch: K = ksplit * KT * 64
+  // A slice: 16-byte chunks, 8 lanes per 128-byte row piece (rows past M
+  // read row M - 1: finite values in accumulators the reduction drops)
+  const int crow = tid >> 3, cc = tid & 7;
+  bf16x8 ast[4 * KT];
 #pragma unroll
-    for (int t = 0; t < KT; ++t)
+  for (int t = 0; t < KT; ++t)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = (wave * 4 + q) * 8 + lrow;
-        const uint32_t src = (uint32_t)min(n0 + r, N - 1) * (uint32_t)K + (uint32_t)(kbase + t * BK + (lpos ^ swz<BK>(r)) * 8);
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(W + src),
-                                         (__attribute__((address_space(3))) void*)(ws + t * STAGE + (wave * 4 + q) * 8 * BK),
-                                         16, 0, 0);
-      }
-  }
-  // A rows of this wave: B-operand fragments, lane (token l % 32, half l / 32)
+    for (int u = 0; u < 4; ++u)
+      ast[t * 4 + u] = *(const bf16x8*)(A + (int64_t)min(m0 + u * 32 + crow, M - 1) * K + kbase + t * BK + cc * 8);
+  // W fragments: lane l holds feature n0 + 32 w + l % 32, k offsets 16 j + 8 (l / 32) .. + 7;
+  // from the fragment-ordered copy (PACKED) each fragment is one contiguous
+  // 1 KB wave load, from [N][K] it is 32 rows x 32 bytes
   const int lr = lane & 31, lh = lane >> 5;
-  bf16x8 af[4 * KT];
-  {
-    const bf16* arow = A + (int64_t)min(m0 + wave * 32 + lr, M - 1) * K + kbase + lh * 8;
+  bf16x8 wf[4 * KT];
+  if constexpr (PACKED) {
+    const int nblk = min((n0 >> 5) + wave, ((N + 31) >> 5) - 1);
+    const bf16* const wp = (const bf16*)E.wpack + (((int64_t)nblk * (K >> 6) + (kbase >> 6)) * 4) * 512 + lane * 8;
 #pragma unroll
-    for (int j = 0; j < 4 * KT; ++j) af[j] = *(const bf16x8*)(arow + j * 16);
+    for (int j = 0; j < 4 * KT; ++j) wf[j] = *(const bf16x8*)(wp + j * 512);
+  } else {
+    const bf16* const wrow = W + (int64_t)min(n0 + wave * 32 + lr, N - 1) * K + kbase + lh * 8;
+#pragma unroll
+    for (int j = 0; j < 4 * KT; ++j) wf[j] = *(const bf16x8*)(wrow + j * 16);
   }
-  if constexpr (MODE == EPI_QKV) {
-    if (tid < SD_MAX_ROWS) t0s[tid] = E.t0_dev ? E.t0_dev[tid] : E.t0[tid];
-  }
+#pragma unroll
+  for (int t = 0; t < KT; ++t)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int row = u * 32 + crow;
+      *(bf16x8*)(as + t * ATILE + row * BK + ((cc ^ swz<BK>(row)) * 8)) = ast[t * 4 + u];
+    }
+  __syncthreads();
   f32x16 acc[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int q = 0; q < 16; ++q) acc[i][q] = 0.f;
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    for (int q = 0; q < 16; ++q) acc[j][q] = 0.f;
 #pragma unroll
-  for (int t = 0; t < KT; ++t) {
-    const bf16* st = ws + t * STAGE;
+  for (int t = 0; t < KT; ++t)
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int c = kk * 2 + lh;
-      bf16x8 wf[4];
+      bf16x8 bfr[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = i * 32 + lr;
-        wf[i] = *(const bf16x8*)(st + row * BK + ((c ^ swz<BK>(row)) * 8));
+      for (int j = 0; j < 4; ++j) {
+        const int row = j * 32 + lr;
+        bfr[j] = *(const bf16x8*)(as + t * ATILE + row * BK + ((c ^ swz<BK>(row)) * 8));
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = mfma32<H16>(wf[i], af[t * 4 + kk], acc[i]);
+      for (int j = 0; j < 4; ++j) acc[j] = mfma32<H16>(wf[t * 4 + kk], bfr[j], acc[j]);
     }
-  }
-  __syncthreads();
-  // C^T fragments -> [token][feature] strips of 64 tokens in LDS: lane l of
-  // wave w holds token 32 w + l % 32, features 32 i + 8 (q / 4) + 4 (l / 32) + q % 4
-  float* stg = (float*)lds;
+  // granules [slice][tile][feature block = wave][row block j][g][lane]: lane l
+  // holds row 32 j + l % 32, features 32 w + 8 g + 4 (l / 32) + 0..3
+  float4* dst = (float4*)E.part + ((((int64_t)slice * tiles + tile) * 4 + wave) * 16) * 64 + lane;
 #pragma unroll
-  for (int sidx = 0; sidx < 2; ++sidx) {
-    if ((wave >> 1) == sidx) {
-      const int row = (wave & 1) * 32 + lr;
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) stg[row * LC + i * 32 + 8 * (q >> 2) + 4 * lh + (q & 3)] = acc[i][q];
-    }
-    __syncthreads();
-    const int mb = m0 + sidx * 64;
-    if (ks > 1) {
-      float* dst = E.part + (int64_t)slice * M * N;
-      for (int idx = tid; idx < 64 * (BN / 4); idx += NT) {
-        const int row = idx / (BN / 4), c4 = idx % (BN / 4);
-        const int m = mb + row, n = n0 + c4 * 4;
-        if (m < M && n < N) *(float4*)(dst + (int64_t)m * N + n) = *(const float4*)(stg + row * LC + c4 * 4);
-      }
-    } else {
-      epi_rows<MODE>(E, rowtab, mb, M, tid, t0s);
-      __syncthreads();
-      epi_strip<BN, NT, MODE>(E, stg, LC, mb, n0, M, N, tid, rowtab);
-    }
-    __syncthreads();
-  }
+    for (int g = 0; g < 4; ++g)
+      dst[(j * 4 + g) * 64] = make_float4(acc[j][4 * g], acc[j][4 * g + 1], acc[j][4 * g + 2], acc[j][4 * g + 3]);
 }
 
-template <int KT, int MODE, bool H16>
+template <int KT, bool H16>
 hipError_t launch_wstream(hipStream_t s, const bf16* A, const bf16* W, int M, int N, int K, const Epi& E) {
-  const unsigned grid = (unsigned)(((M + 127) / 128) * ((N + 127) / 128)) * (E.ksplit > 1 ? E.ksplit : 1);
-  gemm_wstream_kernel<KT, MODE, H16><<<grid, 256, 0, s>>>(A, W, M, N, K, E);
+  const unsigned grid = (unsigned)(((M + 127) / 128) * ((N + 127) / 128)) * E.ksplit;
+  if (E.wpack)
+    gemm_wstream_kernel<KT, H16, true><<<grid, 256, 0, s>>>(A, W, M, N, K, E);
+  else
+    gemm_wstream_kernel<KT, H16, false><<<grid, 256, 0, s>>>(A, W, M, N, K, E);
+  return hipGetLastError();
+}
+
+// W [N][K] -> fragment order: 16-byte chunk (nb, kt, kk, lane) holds
+// W[32 nb + lane % 32][64 kt + 16 kk + 8 (lane / 32) .. + 7], rows past N zero.
+__global__ __launch_bounds__(256) void pack_weight_kernel(const bf16* __restrict__ W, int N, int K,
+                                                          bf16* __restrict__ out, int64_t chunks) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= chunks) return;
+  const int lane = (int)(c & 63), kk = (int)((c >> 6) & 3);
+  const int64_t rest = c >> 8;
+  const int kt = (int)(rest % (K >> 6)), nb = (int)(rest / (K >> 6));
+  const int n = nb * 32 + (lane & 31), k = kt * 64 + kk * 16 + (lane >> 5) * 8;
+  bf16x8 v;
+  if (n < N) {
+    v = *(const bf16x8*)(W + (int64_t)n * K + k);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (bf16)0.f;
+  }
+  *(bf16x8*)(out + c * 8) = v;
+}
+
+size_t pack_weight_bytes(int N, int K) { return (size_t)((N + 31) / 32) * 32 * (size_t)K * 2; }
+
+hipError_t pack_weight(hipStream_t s, const void* W, int N, int K, void* out) {
+  if (N < 1 || K < 64 || K % 64) return hipErrorInvalidValue;
+  const int64_t chunks = (int64_t)pack_weight_bytes(N, K) / 16;
+  pack_weight_kernel<<<(unsigned)((chunks + 255) / 256), 256, 0, s>>>((const bf16*)W, N, K, (bf16*)out, chunks);
   return hipGetLastError();
 }
 
@@ -859,7 +875,7 @@ bool launch_stream(hipStream_t s, const bf16* A, const bf16* W, int M, int N, in
     if (KT64 % kt) continue;
     const int64_t ks = KT64 / kt;
     if (ks > 64) continue;
-    if (ks > 1 && (!E0.part || ks * (int64_t)M * N > E0.part_cap)) continue;
+    if (!E0.part || ks * tiles * 128 * 128 > E0.part_cap) continue;
     const int64_t wgs = tiles * ks;
     const double rounds = (double)((wgs + 255) / 256);
     const double bw = std::min(8.0e12 * 0.8, (double)std::min<int64_t>(wgs, 256) * 40.0e9);   // bytes/s
@@ -874,18 +890,17 @@ bool launch_stream(hipStream_t s, const bf16* A, const bf16* W, int M, int N, in
   Epi E = E0;
   E.ksplit = KT64 / best_kt;
   switch (best_kt) {
-    case 1: *err = launch_wstream<1, MODE, H16>(s, A, W, M, N, K, E); break;
-    case 2: *err = launch_wstream<2, MODE, H16>(s, A, W, M, N, K, E); break;
-    case 3: *err = launch_wstream<3, MODE, H16>(s, A, W, M, N, K, E); break;
-    case 4: *err = launch_wstream<4, MODE, H16>(s, A, W, M, N, K, E); break;
-    case 5: *err = launch_wstream<5, MODE, H16>(s, A, W, M, N, K, E); break;
-    case 6: *err = launch_wstream<6, MODE, H16>(s, A, W, M, N, K, E); break;
-    case 7: *err = launch_wstream<7, MODE, H16>(s, A, W, M, N, K, E); break;
-    default: *err = launch_wstream<8, MODE, H16>(s, A, W, M, N, K, E); break;
+    case 1: *err = launch_wstream<1, H16>(s, A, W, M, N, K, E); break;
+    case 2: *err = launch_wstream<2, H16>(s, A, W, M, N, K, E); break;
+    case 3: *err = launch_wstream<3, H16>(s, A, W, M, N, K, E); break;
+    case 4: *err = launch_wstream<4, H16>(s, A, W, M, N, K, E); break;
+    case 5: *err = launch_wstream<5, H16>(s, A, W, M, N, K, E); break;
+    case 6: *err = launch_wstream<6, H16>(s, A, W, M, N, K, E); break;
+    case 7: *err = launch_wstream<7, H16>(s, A, W, M, N, K, E); break;
+    default: *err = launch_wstream<8, H16>(s, A, W, M, N, K, E); break;
   }
-  if (*err == hipSuccess && E.ksplit > 1) {
-    const unsigned grid = (unsigned)(((M + 63) / 64) * ((N + 31) / 32));
-    gemm_reduce_kernel<MODE><<<grid, 256, 0, s>>>(M, N, E);
+  if (*err == hipSuccess) {
+    gemm_reduce_kernel<MODE><<<(unsigned)(tiles * 8), 256, 0, s>>>(M, N, E);
     *err = hipGetLastError();
   }
   return true;

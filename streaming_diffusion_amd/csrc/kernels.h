@@ -78,6 +78,11 @@ hipError_t gemm(hipStream_t s, bool bf, const void* A, const void* W, int M, int
 hipError_t gemm_mfma(hipStream_t s, const void* A, const void* W, int M, int N, int K, const Epi& E);
 // The same with fp16 operands A and W (bias stays bf16); EPI_F32 and EPI_RESID.
 hipError_t gemm_mfma_f16(hipStream_t s, const void* A, const void* W, int M, int N, int K, const Epi& E);
+// A weight W [N][K] (16-bit elements, K a multiple of 64) rearranged for the
+// few-row product (Epi::wpack): 16-byte chunk (nb, kt, kk, lane) holds
+// W[32 nb + lane % 32][64 kt + 16 kk + 8 (lane / 32) .. + 7], rows past N zero.
+size_t pack_weight_bytes(int N, int K);
+hipError_t pack_weight(hipStream_t s, const void* W, int N, int K, void* out);
 
 // ---------------------------------------------------------------- attention
 struct KvSeg {

@@ -153,9 +153,26 @@ sd_status sd_k_gemm_epi(const void* A, const void* W, int32_t M, int32_t N, int3
     E.part = (float*)e->workspace;
     E.part_cap = (int64_t)(e->workspace_bytes / 4);
   }
+  if (e->wpack) {
+    if ((uintptr_t)e->wpack & 15) return SD_ERR_ARG;
+    if (K % 64) return SD_ERR_SHAPE;
+    E.wpack = e->wpack;
+  }
   const hipError_t r = e->f16 ? sdk::gemm_mfma_f16((hipStream_t)stream, A, W, M, N, K, E)
                              : sdk::gemm_mfma((hipStream_t)stream, A, W, M, N, K, E);
   return r == hipSuccess ? SD_OK : SD_ERR_HIP;
+}
+
+size_t sd_k_pack_weight_bytes(int32_t N, int32_t K) {
+  if (N < 1 || K < 64 || K % 64) return 0;
+  return sdk::pack_weight_bytes(N, K);
+}
+
+sd_status sd_k_pack_weight(const void* W, int32_t N, int32_t K, void* out, void* stream) {
+  if (!W || !out || N < 1 || K < 1) return SD_ERR_ARG;
+  if (K % 64) return SD_ERR_SHAPE;
+  if ((uintptr_t)out & 15) return SD_ERR_ARG;
+  return sdk::pack_weight((hipStream_t)stream, W, N, K, out) == hipSuccess ? SD_OK : SD_ERR_HIP;
 }
 
 sd_status sd_k_ln_mod(int32_t dtype, const float* x, void* out, int32_t M, int32_t d, int32_t L, const float* mod,

@@ -72,6 +72,12 @@ struct sd_stream {
   // when a forward has few rows (kernels.h, Epi::part)
   float* gpart = nullptr;
   int64_t gpart_cap = 0;
+  // with short chunks, fragment-ordered copies of the block weights for the
+  // few-row product (kernels.h, pack_weight; null where K % 64 != 0): made
+  // at create from the caller's weights, the folded cross-attention ones at
+  // set_context
+  void *wp_qkv = nullptr, *wp_o = nullptr, *wp_f1 = nullptr, *wp_f2 = nullptr, *wp_cq = nullptr, *wp_co = nullptr;
+  void *wp_fq = nullptr, *wp_fo = nullptr;
   // the step's dynamic values in device memory: [0] the forward, [1] the
   // clean-latent forward of kv_recompute
   StepDyn* dyn = nullptr;
@@ -181,6 +187,9 @@ void dims(sd_stream* s) {
   s->rope_pos = std::max(c.rope_reset, s->Tn - 1) + 1;
 }
 
+// bytes of one fragment-ordered weight copy [N][K] (K % 64 == 0)
+size_t packed_bytes(int N, int K) { return sdk::pack_weight_bytes(N, K); }
+
 // Lay out (or, with base == nullptr, measure) the workspace.
 size_t carve(sd_stream* s, char* base) {
   const sd_stream_config& c = s->cfg;
@@ -236,6 +245,23 @@ size_t carve(sd_stream* s, char* base) {
   if (s->bf && s->L <= 256) {
     s->gpart_cap = (int64_t)16 << 20;          // 64 MiB of fp32 partials
     s->gpart = cv.take<float>((size_t)s->gpart_cap * 4);
+    const int d = s->d, F = s->F, nb = s->nb;
+    auto take_packed = [&](int N, int K, int count) -> void* {
+      return K % 64 ? nullptr : cv.take<void>(packed_bytes(N, K) * count);
+    };
+    s->wp_qkv = take_packed(3 * d, d, nb);
+    s->wp_o = take_packed(d, d, nb);
+    s->wp_f1 = take_packed(F, d, nb);
+    s->wp_f2 = take_packed(d, F, nb);
+    if (c.ctx_len > 0 && !s->fold) {
+      s->wp_cq = take_packed(d, d, nb);
+      s->wp_co = take_packed(d, d, nb);
+    }
+    if (s->fold) {
+      const int ncol = s->H * s->ctx8;
+      s->wp_fq = take_packed(ncol, d, nb * nctx);
+      s->wp_fo = take_packed(d, ncol, nb * nctx);
+    }
   }
   if (s->bf) {
     s->pe2 = cv.take<void>((size_t)s->d * 2 * s->P * es);
@@ -292,6 +318,11 @@ void rope_tables(const sd_stream* s, std::vector<float2>& t, std::vector<float2>
   fill(t, s->rope_pos, s->dt);
   fill(h, s->Hp, s->dh);
   fill(w, s->Wp, s->dw);
+}
+
+// block (or block-and-context) b of a fragment-ordered copy, null if none
+const void* packed_at(const void* base, int b, int N, int K) {
+  return base ? (const char*)base + (int64_t)b * (int64_t)packed_bytes(N, K) : nullptr;
 }
 
 Epi epi_base(const sd_stream* s, int mode) {
@@ -435,6 +466,20 @@ sd_status sd_stream_create(const sd_stream_config* cfg, const sd_weights* w, voi
         e = hipMemcpy2DAsync(Pm(s->head2, (int64_t)half * s->d, s->es), 2 * s->d * s->es, w->head_w, s->d * s->es,
                              s->d * s->es, s->P, hipMemcpyDeviceToDevice, s->st);
     }
+  {
+    const int d = s->d, F = s->F;
+    auto pack = [&](void* dst, const void* src, int N, int K) {
+      if (!dst) return;
+      for (int b = 0; b < s->nb && e == hipSuccess; ++b)
+        e = sdk::pack_weight(s->st, P(src, (int64_t)b * N * K, s->es), N, K, Pm(dst, (int64_t)b * packed_bytes(N, K), 1));
+    };
+    pack(s->wp_qkv, w->qkv_w, 3 * d, d);
+    pack(s->wp_o, w->o_w, d, d);
+    pack(s->wp_f1, w->f1_w, F, d);
+    pack(s->wp_f2, w->f2_w, d, F);
+    pack(s->wp_cq, w->cq_w, d, d);
+    pack(s->wp_co, w->co_w, d, d);
+  }
   if (e == hipSuccess) e = hipMemcpyAsync(s->rope_t, rt.data(), rt.size() * sizeof(float2), hipMemcpyHostToDevice, s->st);
   if (e == hipSuccess) e = hipMemcpyAsync(s->rope_h, rh.data(), rh.size() * sizeof(float2), hipMemcpyHostToDevice, s->st);
   if (e == hipSuccess) e = hipMemcpyAsync(s->rope_w, rw.data(), rw.size() * sizeof(float2), hipMemcpyHostToDevice, s->st);
@@ -490,6 +535,12 @@ sd_status sd_stream_set_context(sd_stream* s, const void* ctx_pos, const void* c
                                 (const bf16*)P(s->w.co_w, (int64_t)b * d * d, s->es),
                                 (f16*)Pm(s->fold_q, bc * ncol * d, s->es), s->fold_c + bc * ncol,
                                 (f16*)Pm(s->fold_o, bc * d * ncol, s->es), s->d, s->H, s->hd, c.ctx_len, s->ctx8));
+        if (s->wp_fq)
+          HIP_TRY(sdk::pack_weight(s->st, P(s->fold_q, bc * ncol * d, s->es), (int)ncol, (int)d,
+                                   Pm(s->wp_fq, bc * (int64_t)packed_bytes((int)ncol, (int)d), 1)));
+        if (s->wp_fo)
+          HIP_TRY(sdk::pack_weight(s->st, P(s->fold_o, bc * d * ncol, s->es), (int)d, (int)ncol,
+                                   Pm(s->wp_fo, bc * (int64_t)packed_bytes((int)d, (int)ncol), 1)));
       }
   }
   s->ctx_set = true;
@@ -724,6 +775,7 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, const StepDyn* dd
       E.rope = 1;
       for (int r = 0; r < R; ++r) E.t0[r] = rt.r[r].t0;
       E.t0_dev = dd->t0;
+      E.wpack = packed_at(s->wp_qkv, b, 3 * d, d);
       PROF(SD_PROF_GEMM_QKV, gflop(M, 3 * d, d), gbytes(M, 3 * d, d, es, es),
            sdk::gemm(st, bf, s->xm, P(s->w.qkv_w, (int64_t)b * 3 * d * d, es), M, 3 * d, d, E));
     }
@@ -818,6 +870,7 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, const StepDyn* dd
       E.mod = s->mod;
       E.blk = blk;
       E.gate_off = 2 * d;
+      E.wpack = packed_at(s->wp_o, b, d, d);
       PROF(SD_PROF_GEMM_O, gflop(M, d, d), gbytes(M, d, d, es, 8),
            sdk::gemm(st, bf, s->ao, P(s->w.o_w, (int64_t)b * d * d, es), M, d, d, E));
     }
@@ -836,6 +889,7 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, const StepDyn* dd
           Epi E = epi_base(s, EPI_F32);
           E.out = sc + t0 * ncol;
           E.ldo = ncol;
+          E.wpack = packed_at(s->wp_fq, (int)bc, ncol, d);
           PROF(SD_PROF_GEMM_CROSS, gflop(Mp, ncol, d), gbytes(Mp, ncol, d, es, 4),
                sdk::gemm_mfma_f16(st, P(s->xm, t0 * d, es), P(s->fold_q, bc * ncol * d, es), (int)Mp, ncol, d, E));
         }
@@ -845,6 +899,7 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, const StepDyn* dd
           Epi E = epi_base(s, EPI_RESID);
           E.bias = P(s->w.co_b, (int64_t)b * d, es);
           E.resid = s->resid + t0 * d;
+          E.wpack = packed_at(s->wp_fo, (int)bc, d, ncol);
           PROF(SD_PROF_GEMM_CROSS, gflop(Mp, d, ncol), gbytes(Mp, d, ncol, es, 8),
                sdk::gemm_mfma_f16(st, pc + t0 * ncol, P(s->fold_o, bc * d * ncol, es), (int)Mp, d, ncol, E));
         }
@@ -857,6 +912,7 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, const StepDyn* dd
         E.bias = P(s->w.cq_b, (int64_t)b * d, es);
         E.q = s->q;
         E.rope = 0;
+        E.wpack = packed_at(s->wp_cq, b, d, d);
         PROF(SD_PROF_GEMM_CROSS, gflop(M, d, d), gbytes(M, d, d, es, es),
              sdk::gemm(st, bf, s->xm, P(s->w.cq_w, (int64_t)b * d * d, es), M, d, d, E));
       }
@@ -889,6 +945,7 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, const StepDyn* dd
         Epi E = epi_base(s, EPI_RESID);
         E.bias = P(s->w.co_b, (int64_t)b * d, es);
         E.resid = s->resid;
+        E.wpack = packed_at(s->wp_co, b, d, d);
         PROF(SD_PROF_GEMM_CROSS, gflop(M, d, d), gbytes(M, d, d, es, 8),
              sdk::gemm(st, bf, s->ao, P(s->w.co_w, (int64_t)b * d * d, es), M, d, d, E));
       }
@@ -901,6 +958,7 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, const StepDyn* dd
       E.bias = P(s->w.f1_b, (int64_t)b * s->F, es);
       E.out = s->hid;
       E.ldo = s->F;
+      E.wpack = packed_at(s->wp_f1, b, s->F, d);
       PROF(SD_PROF_GEMM_FFN1, gflop(M, s->F, d), gbytes(M, s->F, d, es, es),
            sdk::gemm(st, bf, s->xm, P(s->w.f1_w, (int64_t)b * s->F * d, es), M, s->F, d, E));
     }
@@ -911,6 +969,7 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, const StepDyn* dd
       E.mod = s->mod;
       E.blk = blk;
       E.gate_off = 5 * d;
+      E.wpack = packed_at(s->wp_f2, b, d, s->F);
       PROF(SD_PROF_GEMM_FFN2, gflop(M, d, s->F), gbytes(M, d, s->F, es, 8),
            sdk::gemm(st, bf, s->hid, P(s->w.f2_w, (int64_t)b * d * s->F, es), M, d, s->F, E));
     }

@@ -276,6 +276,22 @@ def test_gemm_epi_and_ln_mod_reject_bad_arguments_before_any_device_call(lib):
     assert lib.sd_k_ln_mod(1, 8, 8, 4, 128, 1, 8, 8, 0, 128, 768, L.SD_LN_F16, None) == L.SD_ERR_ARG
     e = L.sd_gemm_epi(mode=L.SD_EPI_GELU, out=8, ldo=64, f16=1)
     assert lib.sd_k_gemm_epi(8, 8, 64, 64, 64, C.byref(e), None) == L.SD_ERR_ARG     # fp16: F32 / RESID only
+    e = L.sd_gemm_epi(mode=L.SD_EPI_F32, out=8, ldo=64, wpack=24)
+    assert lib.sd_k_gemm_epi(8, 8, 64, 64, 64, C.byref(e), None) == L.SD_ERR_ARG     # packed copy misaligned
+    e.wpack = 32
+    assert lib.sd_k_gemm_epi(8, 8, 64, 64, 96, C.byref(e), None) == L.SD_ERR_SHAPE   # packed: K % 64
+
+
+def test_pack_weight_size_and_validation(lib):
+    """The fragment-ordered weight copy: whole 32-row blocks of K/64 tiles of
+    4 x 64 chunks of 16 bytes; rejected shapes and pointers never reach the
+    device."""
+    assert lib.sd_k_pack_weight_bytes(1536, 8960) == 1536 * 8960 * 2
+    assert lib.sd_k_pack_weight_bytes(200, 640) == 224 * 640 * 2          # rows padded to 32
+    assert lib.sd_k_pack_weight_bytes(64, 96) == 0
+    assert lib.sd_k_pack_weight(None, 64, 64, 32, None) == L.SD_ERR_ARG
+    assert lib.sd_k_pack_weight(32, 64, 96, 32, None) == L.SD_ERR_SHAPE
+    assert lib.sd_k_pack_weight(32, 64, 64, 40, None) == L.SD_ERR_ARG       # output not 16-byte aligned
 
 
 def test_rope_tables_are_cos_sin_of_the_section_angles(lib):

@@ -315,20 +315,74 @@ def test_split_k_epilogues_exact(lib, M, N, K):
     assert np.array_equal(st.float().cpu().numpy(), bf16_round(acc.astype(np.float32)))
 
 
+def packed_copy(lib, W, N, K):
+    n = lib.sd_k_pack_weight_bytes(N, K)
+    assert n > 0
+    buf = torch.empty(n // 2, dtype=W.dtype, device=device())
+    call(lib.sd_k_pack_weight(W.data_ptr(), N, K, buf.data_ptr(), stream_ptr()))
+    torch.cuda.synchronize()
+    return buf
+
+
+def test_pack_weight_layout(lib):
+    """sd_k_pack_weight against its definition: chunk (nb, kt, kk, lane) is
+    W[32 nb + lane % 32][64 kt + 16 kk + 8 (lane / 32) .. + 7], rows past N
+    zero (N = 200 pads to 224)."""
+    N, K = 200, 192
+    rng = np.random.default_rng(31)
+    wi = rng.integers(-200, 201, size=(N, K)).astype(np.float64)     # exact in bf16
+    got = packed_copy(lib, to_dev(wi, torch.bfloat16), N, K).float().cpu().numpy().astype(np.float64)
+    NB, KT = (N + 31) // 32, K // 64
+    wp = np.zeros((NB * 32, K))
+    wp[:N] = wi
+    ref = wp.reshape(NB, 32, KT, 4, 2, 8).transpose(0, 2, 3, 4, 1, 5).reshape(-1)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 4608, 1536), (128, 8960, 1536), (128, 1536, 8960), (256, 1536, 1536),
+                                   (96, 200, 640)])
+def test_split_k_packed_weights_exact(lib, M, N, K):
+    """The few-row product reading W from its fragment-ordered copy (what the
+    stream uses when every forward has at most 256 tokens): bit for bit the
+    integer arithmetic, as with W read in place."""
+    print(f"split-K packed M={M} N={N} K={K}", flush=True)
+    A, W, b, acc = int_operands(M, N, K, 23)
+    wp = packed_copy(lib, W, N, K)
+    ws, wsp, wsb = split_ws()
+    out = torch.empty((M, N), dtype=torch.float32, device=device())
+    e = sdlib.sd_gemm_epi(mode=sdlib.SD_EPI_F32, bias=b.data_ptr(), out=out.data_ptr(), ldo=N, workspace=wsp,
+                          workspace_bytes=wsb, wpack=wp.data_ptr())
+    run(lib, A, W, M, N, K, e)
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), acc)
+    rng = np.random.default_rng(24)
+    c0 = rng.integers(-4096, 4097, size=(M, N)) / 256.0
+    Lr = M // 2 if M % 2 == 0 else M
+    mod = rng.integers(-2, 3, size=(M // Lr, 6 * N)) / 2.0
+    blk = rng.integers(-1, 2, size=6 * N) / 2.0
+    resid = to_dev(c0, torch.float32)
+    mod_d, blk_d = to_dev(mod, torch.float32), to_dev(blk, torch.bfloat16)
+    e = sdlib.sd_gemm_epi(mode=sdlib.SD_EPI_GATE_RESID, bias=b.data_ptr(), resid=resid.data_ptr(),
+                          mod=mod_d.data_ptr(), blk=blk_d.data_ptr(), gate_off=5 * N, six_d=6 * N, L=Lr,
+                          workspace=wsp, workspace_bytes=wsb, wpack=wp.data_ptr())
+    run(lib, A, W, M, N, K, e)
+    gate = mod[np.arange(M) // Lr, 5 * N:6 * N] + blk[5 * N:6 * N]
+    assert np.array_equal(resid.cpu().numpy().astype(np.float64), c0 + gate * acc)
+
+
 def test_split_k_qkv_rope_and_fp16(lib):
     """The q / k / v scatter with RoPE and the fp16 cross-attention products on
     the split path (one latent frame of 8 x 16 tokens per row, two rows)."""
     ws, wsp, wsb = split_ws()
-    rows, t, hp, wp, d, h = 2, 1, 8, 16, 1536, 12
-    hd, Lr = d // h, t * hp * wp
+    rows, t, hp, wp_, d, h = 2, 1, 8, 16, 1536, 12
+    hd, Lr = d // h, t * hp * wp_
     M, N, K = rows * Lr, 3 * d, d
     A, W, b, acc = int_operands(M, N, K, 23)
     q = torch.zeros((rows, h, Lr, hd), dtype=torch.bfloat16, device=device())
     k = torch.zeros((h, rows, Lr, hd), dtype=torch.bfloat16, device=device())
     vt = torch.zeros((h, hd, rows, Lr), dtype=torch.bfloat16, device=device())
-    tab = rope_table(lib, hd, ROPE_POS, hp, wp)
+    tab = rope_table(lib, hd, ROPE_POS, hp, wp_)
     e = sdlib.sd_gemm_epi(mode=sdlib.SD_EPI_QKV, bias=b.data_ptr(), L=Lr, q=q.data_ptr(), k=k.data_ptr(),
-                          vt=vt.data_ptr(), kstride=Lr, krows=rows, H=h, hd=hd, rope=1, Hp=hp, Wp=wp,
+                          vt=vt.data_ptr(), kstride=Lr, krows=rows, H=h, hd=hd, rope=1, Hp=hp, Wp=wp_,
                           rope_table=tab.data_ptr(), rope_positions=ROPE_POS, workspace=wsp, workspace_bytes=wsb)
     e.t0[0], e.t0[1] = 3, 1020
     run(lib, A, W, M, N, K, e)
@@ -338,7 +392,7 @@ def test_split_k_qkv_rope_and_fp16(lib):
         assert np.array_equal(vg[:, :, r].transpose(2, 0, 1), bf16_round(c[:, 2]))
         for sec, got in ((0, qg[r].transpose(1, 0, 2)), (1, kg[:, r].transpose(1, 0, 2))):
             x = c[:, sec]
-            ref = dit.rope_apply(x, dit.token_positions(t, hp, wp, t0))
+            ref = dit.rope_apply(x, dit.token_positions(t, hp, wp_, t0))
             pair = np.repeat(np.abs(x[..., 0::2]) + np.abs(x[..., 1::2]), 2, axis=-1)
             assert (np.abs(got - ref) - 2.0 ** -8 * np.abs(ref) - 1e-6 * pair).max() <= 0.0
     # fp16 operands (the folded cross-attention) on the split path
@@ -348,7 +402,24 @@ def test_split_k_qkv_rope_and_fp16(lib):
     out = torch.empty((M2, N2), dtype=torch.float32, device=device())
     e = sdlib.sd_gemm_epi(mode=sdlib.SD_EPI_F32, out=out.data_ptr(), ldo=N2, f16=1, workspace=wsp,
                           workspace_bytes=wsb)
-    call(lib.sd_k_gemm_epi(to_dev(ai / 16.0, torch.float16).data_ptr(), to_dev(wi / 16.0, torch.float16).data_ptr(),
-                           M2, N2, K2, C.byref(e), stream_ptr()))
+    A2, W2 = to_dev(ai / 16.0, torch.float16), to_dev(wi / 16.0, torch.float16)
+    call(lib.sd_k_gemm_epi(A2.data_ptr(), W2.data_ptr(), M2, N2, K2, C.byref(e), stream_ptr()))
     torch.cuda.synchronize()
-    assert np.array_equal(out.cpu().numpy().astype(np.float64), (ai.astype(np.float64) @ wi.T) / 256.0)
+    ref2 = (ai.astype(np.float64) @ wi.T) / 256.0
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), ref2)
+    # the same from fragment-ordered copies of W (fp16, and the q / k / v product)
+    out.zero_()
+    wp2 = packed_copy(lib, W2, N2, K2)
+    e.wpack = wp2.data_ptr()
+    call(lib.sd_k_gemm_epi(A2.data_ptr(), W2.data_ptr(), M2, N2, K2, C.byref(e), stream_ptr()))
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), ref2)
+    q2, k2, vt2 = torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(vt)
+    wp = packed_copy(lib, W, N, K)
+    e = sdlib.sd_gemm_epi(mode=sdlib.SD_EPI_QKV, bias=b.data_ptr(), L=Lr, q=q2.data_ptr(), k=k2.data_ptr(),
+                          vt=vt2.data_ptr(), kstride=Lr, krows=rows, H=h, hd=hd, rope=1, Hp=hp, Wp=wp_,
+                          rope_table=tab.data_ptr(), rope_positions=ROPE_POS, workspace=wsp, workspace_bytes=wsb,
+                          wpack=wp.data_ptr())
+    e.t0[0], e.t0[1] = 3, 1020
+    run(lib, A, W, M, N, K, e)
+    assert torch.equal(q2, q) and torch.equal(k2, k) and torch.equal(vt2, vt)
