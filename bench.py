@@ -64,6 +64,8 @@ def parse():
     ap.add_argument("--vae", action="store_true",
                     help="measure the Stream-VAE instead: encode + decode of 4-frame chunks at the video shape")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-knee", action="store_true",
+                    help="skip the below-the-knee leg (1.3B widths, 128-token chunks) of the default run")
     ap.add_argument("--cpu-blocks", type=int, default=2, help="DiT blocks in the oracle sample")
     ap.add_argument("--cpu-full", action="store_true",
                     help="time the CPU oracle alone, unsampled: the tiny workload's 16 steps (all threads and one "
@@ -80,16 +82,19 @@ def slot_indices(n):
 
 PMC_FILE = os.path.join(ROOT, "profiles", "attn_self_video13b_pmc.json")
 ATTN_SOURCE = os.path.join(ROOT, "streaming_diffusion_amd", "csrc", "k_attn.hip")
+PMC_FILE_KNEE = os.path.join(ROOT, "profiles", "gemm_ffn2_video13b_subknee_pmc.json")
+GEMM_SOURCE = os.path.join(ROOT, "streaming_diffusion_amd", "csrc", "k_gemm_mfma.hip")
 
 
-def measured_traffic():
-    """HBM bytes per self-attention launch from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE runs, each scaled by what the counter read for a
-    device copy of known size.  None when the kernel source changed since."""
+def measured_traffic(pmc_file=PMC_FILE, source=ATTN_SOURCE):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE runs, each scaled by what the counter
+    read for a device copy of known size.  None when the kernel source
+    changed since."""
     import hashlib
     try:
-        rec = json.load(open(PMC_FILE))
-        sha = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
+        rec = json.load(open(pmc_file))
+        sha = hashlib.sha256(open(source, "rb").read()).hexdigest()
     except (OSError, ValueError):
         return None
     if rec.get("source_sha256") != sha:
@@ -271,7 +276,8 @@ def measure(cfg, weights, steps: int, warmup: int, dev, io_stream: bool = False,
         roofline = {"kernel": f"{dom_kind}: gemm_wstream_kernel + gemm_reduce_kernel (weight-streaming GEMM, "
                               f"K split over the CUs)",
                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic(PMC_FILE_KNEE, GEMM_SOURCE) if dom_kind == "gemm_ffn2" else None,
                     "avg_launch_ms": round(per_launch_ms, 4), "algorithmic_bytes_per_launch": per_launch_bytes,
                     "launches": attn["launches"]}
     bd = {}
@@ -600,6 +606,16 @@ def main():
     cfg = get_config(args.workload, t_index=slot_indices(args.n_slots), chunks_per_step=args.chunks, **kw)
     weights = random_device_weights(cfg, seed=gen.SEED_WEIGHTS)
     res = measure(cfg, weights, args.steps, args.warmup, dev, args.io_stream, args.graph)
+    plain = not (args.batch_attn or args.kv_recompute or args.io_stream or args.graph or args.cfg or
+                 args.sampler != "ddim" or args.chunks != 1 or args.n_slots != 2)
+    if cfg.name == "video13b" and plain and not args.no_knee:
+        # the memory-bound side of the roofline: the same weights with one
+        # latent frame of 8 x 16 tokens per chunk and one slot (128 tokens per
+        # forward, below the knee), step replayed as a captured graph
+        knee_cfg = get_config("video13b_subknee", t_index=slot_indices(1))
+        knee = measure(knee_cfg, weights, max(args.steps, 20), args.warmup, dev, graph=True)
+        res["roofline_below_knee"] = dict(knee["roofline"] or {}, workload=knee["config"]["workload"],
+                                          ms_per_step=knee["ms_per_step"], frames_per_s=knee["value"])
     if args.calibrate_copy:
         n = args.calibrate_copy << 18          # float32 elements in MIB MiB
         a = torch.ones(n, dtype=torch.float32, device=dev)
