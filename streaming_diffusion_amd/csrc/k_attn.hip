@@ -125,10 +125,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nqt = (a.L + BQ - 1) / BQ;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  // order (row, head, split, q-tile): the workgroups resident on one XCD at
-  // a time are q-tiles of the same key range, which then streams through L2
-  const int qt = lid % nqt, sp = (lid / nqt) % a.nsplit;
-  const int h = (lid / (nqt * a.nsplit)) % a.H, r = a.r0 + lid / (nqt * a.nsplit * a.H);
+  // order (head, split, row, q-tile): the workgroups resident on one XCD at
+  // a time are the q-tiles of every row for the same key range -- the rows
+  // share the sink and the window, which then stream through that XCD's L2
+  // once for all of them
+  const int qt = lid % nqt, r = a.r0 + (lid / nqt) % a.R;
+  const int sp = (lid / (nqt * a.R)) % a.nsplit, h = lid / (nqt * a.R * a.nsplit);
   const int q0 = qt * BQ;
 
   // segments of this (row, head) as plain scalars, uniform over the
