@@ -464,6 +464,7 @@ def cpu_full():
                     continue
                 orc.step()
                 times.append(time.perf_counter() - t0)
+                print(f"cpu-full: {cfg.name} step {len(times)}/{steps} {times[-1]:.2f} s", file=sys.stderr, flush=True)
         return times
 
     threads = max([int(p.get("num_threads", 0)) for p in threadpool_info() if p.get("user_api") == "blas"] or [0])
