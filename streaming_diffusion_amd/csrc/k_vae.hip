@@ -196,6 +196,172 @@ __global__ __launch_bounds__(256) void conv3d_mfma_kernel(ConvArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// The same implicit GEMM for the wide layers (Cin and Cout multiples of 64,
+// enough positions to fill the chip): workgroup tile BM positions x BN
+// channels, 8 waves (WMW along positions x 8 / WMW along channels, each a
+// 64 x 64 block of outputs), k-tiles of 64 that lie inside one tap
+// (Cin % 64 == 0), so the tap's (dt, dy, dx) shift is uniform per k-tile.
+// Both operands go global -> LDS by DMA (global_load_lds, 16 bytes per lane,
+// no register staging) into NS stages: the DMA of k-tile t + NS - 1 leaves
+// while tile t is multiplied.  A gathered input row whose tap falls outside
+// the frame (or before the chunk without a cache) reads a 16-byte zero row in
+// device memory instead.  256 x 128 tiles with 3 stages for 128-channel
+// outputs, 512 x 64 with 2 stages for 64-channel outputs.
+static __device__ __attribute__((aligned(64))) bf16 conv_zero_row[8];
+
+template <int n>
+SD_DEV void conv_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(n) : "memory");
+}
+
+template <int BM, int BN, int WMW, int NS, bool H16>
+__global__ __launch_bounds__(512) void conv3d_dma_kernel(ConvArgs a) {
+  constexpr int BK = 64;
+  constexpr int WNW = 8 / WMW;                          // waves along positions / channels
+  constexpr int TMP = BM / WMW, TNC = BN / WNW;         // wave tile: positions x channels
+  constexpr int MB = TMP / 32, NB = TNC / 32;           // 32 x 32 blocks per wave
+  constexpr int AQ = BM / 64, BQ = BN / 64;             // DMA instructions per wave per k-tile (8 rows each)
+  constexpr int DQ = AQ + BQ;
+  constexpr int STAGE = (BM + BN) * BK;
+  static_assert(NB >= 1 && MB >= 1 && BQ >= 1 && (NS == 2 || NS == 3), "tile shape");
+  __shared__ __attribute__((aligned(1024))) bf16 smem[NS * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave / WMW, wm = wave % WMW;
+  const int HW = a.H * a.W;
+  const int M = a.T * HW;
+  const int K = 27 * a.Cin;
+  const int KT = K / BK;
+  const int tiles_m = (M + BM - 1) / BM;
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int tm = lid % tiles_m, tn = lid / tiles_m;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const bf16* const zero = conv_zero_row;
+
+  // this lane's DMA rows: row (wave * Q + q) * 8 + lane / 8 of the tile, its
+  // 16-byte LDS slot lane % 8 holds logical chunk (lane % 8) ^ swz(row)
+  const int lrow = lane >> 3, lpos = lane & 7;
+  int pt[AQ], py[AQ], px[AQ], ach[AQ];
+  bool pv[AQ];
+#pragma unroll
+  for (int q = 0; q < AQ; ++q) {
+    const int row = (wave * AQ + q) * 8 + lrow;
+    const int p = m0 + row;
+    pv[q] = p < M;
+    const int pp = pv[q] ? p : 0;
+    pt[q] = pp / HW;
+    const int rem = pp - pt[q] * HW;
+    py[q] = rem / a.W;
+    px[q] = rem - py[q] * a.W;
+    ach[q] = (lpos ^ cv_swz<BK>(row)) * 8;
+  }
+  const bf16* wsrc[BQ];
+#pragma unroll
+  for (int q = 0; q < BQ; ++q) {
+    const int row = (wave * BQ + q) * 8 + lrow;
+    const int n = n0 + row;
+    wsrc[q] = n < a.Cout ? a.w + (int64_t)n * K + (lpos ^ cv_swz<BK>(row)) * 8 : nullptr;
+  }
+  auto dma = [](const bf16* src, bf16* lds) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+  };
+  auto issue = [&](int kt, int buf) {
+    const int k0 = kt * BK;
+    const int tap = k0 / a.Cin, ci0 = k0 - tap * a.Cin;
+    const int dt = tap / 9, dy = (tap / 3) % 3, dx = tap % 3;
+    bf16* as = smem + buf * STAGE;
+    bf16* bs = as + BM * BK;
+#pragma unroll
+    for (int q = 0; q < AQ; ++q) {
+      const int t2 = pt[q] + dt - 2, y2 = py[q] + dy - 1, x2 = px[q] + dx - 1;
+      const bf16* src = zero;
+      if (pv[q] && (unsigned)y2 < (unsigned)a.H && (unsigned)x2 < (unsigned)a.W) {
+        if (t2 >= 0)
+          src = a.x + ((int64_t)t2 * HW + (int64_t)y2 * a.W + x2) * a.Cin + ci0 + ach[q];
+        else if (a.cache)
+          src = a.cache + ((int64_t)(t2 + 2) * HW + (int64_t)y2 * a.W + x2) * a.Cin + ci0 + ach[q];
+      }
+      dma(src, as + (wave * AQ + q) * 8 * BK);
+    }
+#pragma unroll
+    for (int q = 0; q < BQ; ++q) dma(wsrc[q] ? wsrc[q] + k0 : zero, bs + (wave * BQ + q) * 8 * BK);
+  };
+
+  f32x16 acc[NB][MB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int j = 0; j < MB; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  const int lr = lane & 31, lh = lane >> 5;
+  issue(0, 0);
+  if (NS == 3 && KT > 1) issue(1, 1);
+  for (int kt = 0; kt < KT; ++kt) {
+    // k-tile kt has landed in every wave (with 3 stages kt + 1 may stay in
+    // flight) and every wave is done with the stage the next DMA overwrites
+    if (NS == 3 && kt + 1 < KT) conv_wait_barrier<DQ>();
+    else conv_wait_barrier<0>();
+    if (kt + NS - 1 < KT) issue(kt + NS - 1, (kt + NS - 1) % NS);
+    const bf16* as = smem + (kt % NS) * STAGE;
+    const bf16* bs = as + BM * BK;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int c = ks * 2 + lh;
+      bf16x8 fw[NB], fp[MB];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int row = wn * TNC + i * 32 + lr;
+        fw[i] = *(const bf16x8*)&bs[row * BK + ((c ^ cv_swz<BK>(row)) * 8)];
+      }
+#pragma unroll
+      for (int j = 0; j < MB; ++j) {
+        const int row = wm * TMP + j * 32 + lr;
+        fp[j] = *(const bf16x8*)&as[row * BK + ((c ^ cv_swz<BK>(row)) * 8)];
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < MB; ++j) {
+          if constexpr (H16)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, fw[i]),
+                                                               __builtin_bit_cast(f16x8, fp[j]), acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i], fp[j], acc[i][j], 0, 0, 0);
+        }
+    }
+  }
+
+  // lane: position column lr of each 32-position block; channel rows
+  // 8 (q / 4) + 4 lh + (q % 4) of each 32-channel block
+#pragma unroll
+  for (int j = 0; j < MB; ++j) {
+    const int p = m0 + wm * TMP + j * 32 + lr;
+    if (p >= M) continue;
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * TNC + i * 32 + 8 * g + 4 * lh;
+        if (n >= a.Cout) continue;
+        if (a.ycf) {
+          const int t = p / HW, hw = p - t * HW;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < a.Cout)
+              a.ycf[((int64_t)t * a.Cout + n + e) * HW + hw] = acc[i][j][4 * g + e] + (a.b ? (float)a.b[n + e] : 0.f);
+        } else {
+          bf16x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = to16<H16>(acc[i][j][4 * g + e] + (a.b ? (float)a.b[n + e] : 0.f));
+          *(bf16x4*)(a.y + (int64_t)p * a.Cout + n) = o;
+        }
+      }
+  }
+}
+
 hipError_t conv3d(hipStream_t s, const ConvArgs& a) {
   if (a.Cin < 8 || (a.Cin & 7) || a.Cout < 1 || a.T < 1 || a.H < 1 || a.W < 1) return hipErrorInvalidValue;
   if (a.ycf ? false : (!a.y || (a.Cout & 3))) return hipErrorInvalidValue;
@@ -209,6 +375,24 @@ hipError_t conv3d(hipStream_t s, const ConvArgs& a) {
     if (a.h16) conv3d_mfma_kernel<BN, CV_BK, true><<<g, 256, 0, s>>>(a);                    \
     else conv3d_mfma_kernel<BN, CV_BK, false><<<g, 256, 0, s>>>(a);                         \
   } while (0)
+  // wide layers with enough tiles to fill the chip twice take the DMA
+  // kernel: 256 x 128 tiles when the output channels are a multiple of 128,
+  // else 512 x 64
+  if (a.Cin % 64 == 0 && a.Cout % 64 == 0) {
+    const bool wide = a.Cout % 128 == 0;
+    const int64_t tiles = wide ? ((M + 255) / 256) * (a.Cout / 128) : ((M + 511) / 512) * (a.Cout / 64);
+    if (tiles >= 512) {
+      const unsigned g = (unsigned)tiles;
+      if (wide) {
+        if (a.h16) conv3d_dma_kernel<256, 128, 4, 3, true><<<g, 512, 0, s>>>(a);
+        else conv3d_dma_kernel<256, 128, 4, 3, false><<<g, 512, 0, s>>>(a);
+      } else {
+        if (a.h16) conv3d_dma_kernel<512, 64, 8, 2, true><<<g, 512, 0, s>>>(a);
+        else conv3d_dma_kernel<512, 64, 8, 2, false><<<g, 512, 0, s>>>(a);
+      }
+      return hipGetLastError();
+    }
+  }
   if (a.Cout <= 32) SD_CONV_LAUNCH(32);
   else if (a.Cout <= 64) SD_CONV_LAUNCH(64);
   else SD_CONV_LAUNCH(128);

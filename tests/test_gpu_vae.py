@@ -102,6 +102,27 @@ def conv_at(x, cache, w, b, t, i, j):
     return acc
 
 
+@pytest.mark.parametrize("T,H,W,Ci,Co", [(4, 128, 160, 64, 256), (4, 128, 256, 128, 128), (4, 256, 256, 128, 64)])
+def test_conv3d_dma_path_bit_exact_sampled(lib, T, H, W, Ci, Co):
+    """Wide layers with at least 512 tiles take the DMA-fed kernel (256 x 128
+    tiles for output channels a multiple of 128, else 512 x 64; 64-deep
+    k-tiles inside one tap, out-of-frame taps read a zero row): integer
+    operands, outputs at borders, cache frames and random positions equal the
+    exact sum rounded once to bf16."""
+    print(f"conv3d DMA path T={T} H={H} W={W} Cin={Ci} Cout={Co}", flush=True)
+    x, cache, w, b = int_operands(T * 7 + Co, T, H, W, Ci, Co)
+    dx, dc, dw, db = (to_dev(a, torch.bfloat16) for a in (x, cache, w, b))
+    y = torch.empty((T, H, W, Co), dtype=torch.bfloat16, device=device())
+    call(lib.sd_k_conv3d(dx.data_ptr(), dc.data_ptr(), dw.data_ptr(), db.data_ptr(), y.data_ptr(), None,
+                         T, H, W, Ci, Co, stream_ptr()))
+    torch.cuda.synchronize()
+    yc = y.float().cpu().numpy().astype(np.float64)
+    pts = sampled_positions(np.random.default_rng(5), T, H, W, n=64)
+    got = np.stack([yc[t, i, j] for t, i, j in pts])
+    ref = np.stack([conv_at(x, cache, w, b, t, i, j) for t, i, j in pts])
+    assert np.array_equal(got, bf16_of(ref))
+
+
 @pytest.mark.parametrize("layer", ["d3", "d_out"])
 def test_conv3d_full_video_shape_sampled(lib, layer):
     """The video decoder's two full-resolution layers (4 x 480 x 832): d3
@@ -192,4 +213,26 @@ def test_vae_stream_three_latent_frames_wider_grid():
     v = get_vae_config("small", latent_h=6, latent_w=7, c1=32, c2=64, c3=128, latent_t=3)
     print("Stream-VAE medium, latent_t=3", flush=True)
     _, run, _, _ = run_vae_stream(v, chunks=2)
+    run.close()
+
+
+def test_vae_stream_full_resolution_layer_on_the_dma_path():
+    """192 x 256 pixels, widths 128 / 128 / 256: the decoder's full-resolution
+    128 -> 128 convolution (4 x 192 x 256 positions) runs on the DMA-fed kernel
+    with fp16 operands; two chunks against the oracle."""
+    device()
+    v = get_vae_config("small", latent_h=24, latent_w=32, c1=128, c2=128, c3=256)
+    print("Stream-VAE 192 x 256, widths 128 / 128 / 256, 2 chunks", flush=True)
+    _, run, _, _ = run_vae_stream(v, chunks=2)
+    run.close()
+
+
+def test_vae_stream_64_channel_full_resolution_layer_on_the_dma_path():
+    """256 x 256 pixels, widths 64 / 128 / 256: the decoder's full-resolution
+    128 -> 64 convolution (4 x 256 x 256 positions) runs on the DMA-fed kernel
+    with 512 x 64 tiles and fp16 operands; one chunk against the oracle."""
+    device()
+    v = get_vae_config("small", latent_h=32, latent_w=32, c1=64, c2=128, c3=256)
+    print("Stream-VAE 256 x 256, widths 64 / 128 / 256, 1 chunk", flush=True)
+    _, run, _, _ = run_vae_stream(v, chunks=1)
     run.close()
