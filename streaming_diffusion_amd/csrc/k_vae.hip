@@ -362,6 +362,181 @@ __global__ __launch_bounds__(512) void conv3d_dma_kernel(ConvArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Direct convolution for the layers of a whole 4-frame chunk: a workgroup
+// computes all 4 output frames x 8 rows x 16 columns (512 positions) x BN
+// output channels.  The input it reads -- frames t-2 .. t+3 (the two before
+// the chunk from the cache), one row and one column beyond the tile on each
+// side -- is a halo of 6 x 10 x 18 positions.  Per chunk of 32 input channels
+// the halo is DMA'd into LDS once (64-byte rows, 16-byte chunks XOR-swizzled
+// by row; positions outside the frame read a zero row), and all 27 taps read
+// their operand rows from it at their (dt, dy, dx) offsets: each input
+// element crosses from L2 once per output tile instead of once per tap.  The
+// next chunk's halo loads into the second buffer while this chunk's 27 x 2
+// products run.  Weight fragments (the first matrix-core operand) come from
+// device memory straight into registers, one tap ahead.  8 waves: WMW along
+// positions x 8 / WMW along channels.
+template <int BN, int WMW, bool H16>
+__global__ __launch_bounds__(512) void conv3d_halo_kernel(ConvArgs a) {
+  constexpr int TT = 4, TY = 8, TX = 16;                // output tile: frames x rows x columns
+  constexpr int HY = TY + 2, HX = TX + 2, HT = TT + 2;  // halo
+  constexpr int HROWS = HT * HY * HX;                   // 1080
+  constexpr int CK = 32;                                // input channels per chunk: 64-byte rows
+  constexpr int HINS = (HROWS + 15) / 16;               // DMA instructions per halo (16 rows each)
+  constexpr int HQ = (HINS + 7) / 8;                    // per wave
+  constexpr int HBUF = HINS * 16 * CK;                  // elements per halo buffer
+  constexpr int WNW = 8 / WMW;
+  constexpr int TMP = TT * TY * TX / WMW, TNC = BN / WNW;
+  constexpr int MB = TMP / 32, NB = TNC / 32;
+  static_assert(MB >= 1 && NB >= 1 && WMW * WNW == 8, "wave layout");
+  // two halo buffers as separate arrays: the compiler can then tell that the
+  // DMA into one does not write what the products read from the other
+  __shared__ __attribute__((aligned(1024))) bf16 halo0[HBUF];
+  __shared__ __attribute__((aligned(1024))) bf16 halo1[HBUF];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WMW, wn = wave / WMW;
+  const int HW = a.H * a.W;
+  const int K = 27 * a.Cin;
+  const int tiles_x = (a.W + TX - 1) / TX, tiles_y = (a.H + TY - 1) / TY, tiles_n = a.Cout / BN;
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  // channel tiles of one spatial tile are neighbours: they read the same halo
+  const int tn = lid % tiles_n, txy = lid / tiles_n;
+  const int y0 = (txy / tiles_x) * TY, x0 = (txy % tiles_x) * TX, n0 = tn * BN;
+  const bf16* const zero = conv_zero_row;
+
+  // this lane's halo rows: row (wave * HQ + q) * 16 + lane / 4; its 16-byte
+  // LDS slot lane % 4 holds logical chunk (lane % 4) ^ swz(row)
+  const bf16* hsrc[HQ];
+#pragma unroll
+  for (int q = 0; q < HQ; ++q) {
+    const int ins = wave * HQ + q;
+    const int row = ins * 16 + (lane >> 2);
+    const bf16* src = nullptr;
+    if (ins < HINS && row < HROWS) {
+      const int ft = row / (HY * HX), hy = (row / HX) % HY, hx = row % HX;
+      const int ti = ft - 2, y = y0 + hy - 1, x = x0 + hx - 1;
+      if ((unsigned)y < (unsigned)a.H && (unsigned)x < (unsigned)a.W) {
+        if (ti >= 0)
+          src = a.x + ((int64_t)ti * HW + (int64_t)y * a.W + x) * a.Cin;
+        else if (a.cache)
+          src = a.cache + ((int64_t)(ti + 2) * HW + (int64_t)y * a.W + x) * a.Cin;
+      }
+      if (src) src += ((lane & 3) ^ cv_swz<CK>(row)) * 8;
+    }
+    hsrc[q] = src;
+  }
+  auto issue_halo = [&](int cc, bf16* buf) {
+#pragma unroll
+    for (int q = 0; q < HQ; ++q) {
+      const int ins = wave * HQ + q;
+      if (ins < HINS)
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(hsrc[q] ? hsrc[q] + cc * CK : zero),
+            (__attribute__((address_space(3))) void*)(buf + ins * 16 * CK), 16, 0, 0);
+    }
+  };
+  // halo row of tap (0, 0, 0) for each of this lane's position blocks
+  const int lr = lane & 31, lh = lane >> 5;
+  int hbase[MB];
+#pragma unroll
+  for (int j = 0; j < MB; ++j) {
+    const int pw = wm * TMP + j * 32 + lr;
+    const int tf = pw / (TY * TX), r = (pw / TX) % TY, c = pw % TX;
+    hbase[j] = (tf * HY + r) * HX + c;
+  }
+  // weight fragments of (chunk cc, tap): rows n0 + wn TNC + 32 i + l % 32
+  const bf16* wrow[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) wrow[i] = a.w + (int64_t)(n0 + wn * TNC + i * 32 + lr) * K + lh * 8;
+  auto load_w = [&](int cc, int tap, bf16x8 (&wf)[2][NB]) {
+    const int k = tap * a.Cin + cc * CK;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < NB; ++i) wf[ks][i] = *(const bf16x8*)(wrow[i] + k + ks * 16);
+  };
+
+  f32x16 acc[NB][MB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int j = 0; j < MB; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  const int NC = a.Cin / CK;
+  bf16x8 wcur[2][NB], wnxt[2][NB];
+  // one chunk: products from the halo in rd while the next chunk's halo
+  // streams into wr
+  auto chunk = [&](int cc, const bf16* rd, bf16* wr) {
+    // the halo of chunk cc and the weights of (cc, tap 0) have landed in
+    // every wave; every wave is done with the buffer the next halo
+    // overwrites.  (A wait the compiler sees: otherwise the first products
+    // after the next halo's DMA would wait for that DMA too.)
+    __builtin_amdgcn_s_waitcnt(0x0070);               // vmcnt(0) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    if (cc + 1 < NC) issue_halo(cc + 1, wr);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int tap = 0; tap < 27; ++tap) {
+      if (tap < 26) load_w(cc, tap + 1, wnxt);
+      else if (cc + 1 < NC) load_w(cc + 1, 0, wnxt);
+      const int dt = tap / 9, dy = (tap / 3) % 3, dx = tap % 3;
+      const int toff = (dt * HY + dy) * HX + dx;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int c = ks * 2 + lh;
+        bf16x8 fp[MB];
+#pragma unroll
+        for (int j = 0; j < MB; ++j) {
+          const int row = hbase[j] + toff;
+          fp[j] = *(const bf16x8*)(rd + row * CK + ((c ^ cv_swz<CK>(row)) * 8));
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+          for (int j = 0; j < MB; ++j) {
+            if constexpr (H16)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, wcur[ks][i]),
+                                                                 __builtin_bit_cast(f16x8, fp[j]), acc[i][j], 0, 0, 0);
+            else
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wcur[ks][i], fp[j], acc[i][j], 0, 0, 0);
+          }
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < NB; ++i) wcur[ks][i] = wnxt[ks][i];
+    }
+  };
+  issue_halo(0, halo0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_w(0, 0, wcur);
+  for (int cc = 0; cc < NC; cc += 2) {
+    chunk(cc, halo0, halo1);
+    if (cc + 1 < NC) chunk(cc + 1, halo1, halo0);
+  }
+
+  // lane: position column lr of each 32-position block; channel rows
+  // 8 (q / 4) + 4 lh + (q % 4) of each 32-channel block
+#pragma unroll
+  for (int j = 0; j < MB; ++j) {
+    const int pw = wm * TMP + j * 32 + lr;
+    const int tf = pw / (TY * TX), y = y0 + (pw / TX) % TY, x = x0 + pw % TX;
+    if (y >= a.H || x >= a.W) continue;
+    const int64_t p = (int64_t)tf * HW + (int64_t)y * a.W + x;
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * TNC + i * 32 + 8 * g + 4 * lh;
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = to16<H16>(acc[i][j][4 * g + e] + (a.b ? (float)a.b[n + e] : 0.f));
+        *(bf16x4*)(a.y + p * a.Cout + n) = o;
+      }
+  }
+}
+
 hipError_t conv3d(hipStream_t s, const ConvArgs& a) {
   if (a.Cin < 8 || (a.Cin & 7) || a.Cout < 1 || a.T < 1 || a.H < 1 || a.W < 1) return hipErrorInvalidValue;
   if (a.ycf ? false : (!a.y || (a.Cout & 3))) return hipErrorInvalidValue;
@@ -375,6 +550,23 @@ hipError_t conv3d(hipStream_t s, const ConvArgs& a) {
     if (a.h16) conv3d_mfma_kernel<BN, CV_BK, true><<<g, 256, 0, s>>>(a);                    \
     else conv3d_mfma_kernel<BN, CV_BK, false><<<g, 256, 0, s>>>(a);                         \
   } while (0)
+  // 4-frame layers with 32-channel input chunks and 64- or 128-channel
+  // output tiles: the halo kernel, when its tiles fill the chip
+  if (a.T == 4 && !a.ycf && a.Cin % 32 == 0 && a.Cout % 64 == 0) {
+    const bool wide = a.Cout % 128 == 0;
+    const int64_t tiles = (int64_t)((a.H + 7) / 8) * ((a.W + 15) / 16) * (a.Cout / (wide ? 128 : 64));
+    if (tiles >= 256) {
+      const unsigned g = (unsigned)tiles;
+      if (wide) {
+        if (a.h16) conv3d_halo_kernel<128, 4, true><<<g, 512, 0, s>>>(a);
+        else conv3d_halo_kernel<128, 4, false><<<g, 512, 0, s>>>(a);
+      } else {
+        if (a.h16) conv3d_halo_kernel<64, 4, true><<<g, 512, 0, s>>>(a);
+        else conv3d_halo_kernel<64, 4, false><<<g, 512, 0, s>>>(a);
+      }
+      return hipGetLastError();
+    }
+  }
   // wide layers with enough tiles to fill the chip twice take the DMA
   // kernel: 256 x 128 tiles when the output channels are a multiple of 128,
   // else 512 x 64

@@ -102,12 +102,15 @@ def conv_at(x, cache, w, b, t, i, j):
     return acc
 
 
-@pytest.mark.parametrize("T,H,W,Ci,Co", [(4, 128, 160, 64, 256), (4, 128, 256, 128, 128), (4, 256, 256, 128, 64)])
-def test_conv3d_dma_path_bit_exact_sampled(lib, T, H, W, Ci, Co):
-    """Wide layers with at least 512 tiles take the DMA-fed kernel (256 x 128
-    tiles for output channels a multiple of 128, else 512 x 64; 64-deep
-    k-tiles inside one tap, out-of-frame taps read a zero row): integer
-    operands, outputs at borders, cache frames and random positions equal the
+@pytest.mark.parametrize("T,H,W,Ci,Co", [(4, 128, 160, 64, 256), (4, 128, 256, 128, 128), (4, 256, 256, 128, 64),
+                                         (4, 124, 200, 96, 192), (2, 256, 256, 64, 128), (3, 256, 352, 64, 64)])
+def test_conv3d_wide_paths_bit_exact_sampled(lib, T, H, W, Ci, Co):
+    """The wide-layer kernels: 4-frame layers take the halo kernel (4 x 8 x 16
+    output tiles, the 6 x 10 x 18 input halo per 32-channel chunk in LDS, all
+    27 taps read from it; ragged 124 x 200 frame and 96 / 192 channels
+    included), other layers with at least 512 tiles the DMA-fed implicit GEMM
+    (256 x 128 and 512 x 64 tiles, 64-deep k-tiles inside one tap).  Integer
+    operands: outputs at borders, cache frames and random positions equal the
     exact sum rounded once to bf16."""
     print(f"conv3d DMA path T={T} H={H} W={W} Cin={Ci} Cout={Co}", flush=True)
     x, cache, w, b = int_operands(T * 7 + Co, T, H, W, Ci, Co)
@@ -216,10 +219,10 @@ def test_vae_stream_three_latent_frames_wider_grid():
     run.close()
 
 
-def test_vae_stream_full_resolution_layer_on_the_dma_path():
+def test_vae_stream_full_resolution_layer_on_the_halo_path():
     """192 x 256 pixels, widths 128 / 128 / 256: the decoder's full-resolution
-    128 -> 128 convolution (4 x 192 x 256 positions) runs on the DMA-fed kernel
-    with fp16 operands; two chunks against the oracle."""
+    128 -> 128 convolution (4 x 192 x 256 positions) runs on the halo kernel
+    with 128-channel tiles and fp16 operands; two chunks against the oracle."""
     device()
     v = get_vae_config("small", latent_h=24, latent_w=32, c1=128, c2=128, c3=256)
     print("Stream-VAE 192 x 256, widths 128 / 128 / 256, 2 chunks", flush=True)
@@ -227,10 +230,10 @@ def test_vae_stream_full_resolution_layer_on_the_dma_path():
     run.close()
 
 
-def test_vae_stream_64_channel_full_resolution_layer_on_the_dma_path():
+def test_vae_stream_64_channel_full_resolution_layer_on_the_halo_path():
     """256 x 256 pixels, widths 64 / 128 / 256: the decoder's full-resolution
-    128 -> 64 convolution (4 x 256 x 256 positions) runs on the DMA-fed kernel
-    with 512 x 64 tiles and fp16 operands; one chunk against the oracle."""
+    128 -> 64 convolution (4 x 256 x 256 positions) runs on the halo kernel
+    with 64-channel tiles and fp16 operands; one chunk against the oracle."""
     device()
     v = get_vae_config("small", latent_h=32, latent_w=32, c1=64, c2=128, c3=256)
     print("Stream-VAE 256 x 256, widths 64 / 128 / 256, 1 chunk", flush=True)
