@@ -475,6 +475,12 @@ def cpu_full():
     res["tiny_fp64_16_steps_1_thread"] = {"s_total": round(sum(t), 3), "ms_per_step": round(1e3 * sum(t) / 16, 2)}
     t = run_steps(get_config("image", t_index=(32,)), 1, np.float64, threads=1)
     res["image_fp64_n1_one_step_1_thread"] = {"s": round(t[0], 2), "frames_per_s": round(1.0 / t[0], 4)}
+    t = run_steps(get_config("image"), 8, np.float64)
+    res["image_fp64_n2_8_steps"] = {"s_total": round(sum(t), 2), "ms_per_step": round(1e3 * sum(t) / 8, 1),
+                                    "frames_per_s": round(8 / sum(t), 3)}
+    t = run_steps(get_config("fourstep"), 4, np.float64)
+    res["fourstep_fp64_n4_onetime_4_steps"] = {"s_total": round(sum(t), 2), "ms_per_step": round(1e3 * sum(t) / 4, 1),
+                                               "frames_per_s": round(4 / sum(t), 4)}
     print(json.dumps(res), flush=True)
     cfg = get_config("video13b")
     t = run_steps(cfg, 2, np.float32)
