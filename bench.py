@@ -414,7 +414,8 @@ def vae_run(steps: int, warmup: int, dev, cpu: bool):
                    "parallelism": "single GPU"},
         "encode_ms_per_chunk": round(enc_ms / steps, 3), "decode_ms_per_chunk": round(dec_ms / steps, 3),
         "wall_ms_per_chunk": round(elapsed / steps * 1e3, 3),
-        "roofline": {"kernel": f"conv3d_mfma_kernel (layer {dom['layer']}, timed alone at its shape)",
+        "roofline": {"kernel": f"sd_k_conv3d (layer {dom['layer']}, timed alone at its shape; halo-tiled "
+                                "direct convolution for 4-frame layers)",
                      "bound": "mfma", "achieved": dom["tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(dom["tflops"] / BF16_PEAK_TFLOPS, 4), "traffic": None,
                      "avg_launch_ms": dom["ms"], "flop_per_launch": vae_conv_flops(Ldom)},

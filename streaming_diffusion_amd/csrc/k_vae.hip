@@ -397,7 +397,7 @@ __global__ __launch_bounds__(512) void conv3d_halo_kernel(ConvArgs a) {
   const int wm = wave % WMW, wn = wave / WMW;
   const int HW = a.H * a.W;
   const int K = 27 * a.Cin;
-  const int tiles_x = (a.W + TX - 1) / TX, tiles_y = (a.H + TY - 1) / TY, tiles_n = a.Cout / BN;
+  const int tiles_x = (a.W + TX - 1) / TX, tiles_n = a.Cout / BN;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
   // channel tiles of one spatial tile are neighbours: they read the same halo
   const int tn = lid % tiles_n, txy = lid / tiles_n;
