@@ -486,17 +486,28 @@ SD_DEV void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(n) : "memory");
 }
 
-template <int BM, int BN, int NW, int BK, int NS, bool SPREAD, int MODE, bool H16 = false>
+//
+// TM0 < BM / 2 splits the tile rows unevenly between the two wave rows (TM0
+// and BM - TM0 rows, both multiples of 32): a 160-row tile as 96 + 64.  Wave
+// w then takes wave row w / WN, so each SIMD (waves w and w + 4) holds one
+// wave of each row and gets the same number of products per k-step as the
+// others; the A rows of a k-tile need not divide evenly over the waves
+// (DMA block b goes to wave b % NW).
+template <int BM, int BN, int NW, int BK, int NS, bool SPREAD, int MODE, bool H16 = false, int TM0 = BM / 2>
 __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restrict__ A, const bf16* __restrict__ W,
                                                           int M, int N, int K, Epi E) {
+  constexpr bool EVEN = TM0 * 2 == BM;
   constexpr int NT = 64 * NW, WN = NW / 2;
-  constexpr int TM = BM / 2, TN = BN / WN, FM = TM / 32, FN = TN / 32;
+  constexpr int TN = BN / WN, FM = TM0 / 32, FM1 = (BM - TM0) / 32, FN = TN / 32;
   constexpr int CPR = BK / 8, RPB = 64 / CPR;             // chunks per row, rows per DMA block
-  constexpr int AQ = BM / RPB / NW, BQ = BN / RPB / NW;   // DMA blocks per wave per k-tile
+  constexpr int ABLK = BM / RPB;                          // A DMA blocks per k-tile
+  constexpr int AQ = (ABLK + NW - 1) / NW, BQ = BN / RPB / NW;   // DMA blocks per wave per k-tile (A: at most)
   constexpr int DQ = AQ + BQ;
   constexpr int STAGE = (BM + BN) * BK;                   // bf16 elements per stage
   constexpr int LC = BN + 4;
-  static_assert(AQ >= 1 && BQ >= 1 && AQ * RPB * NW == BM && BQ * RPB * NW == BN, "tile shape");
+  static_assert(TM0 % 32 == 0 && TM0 * 2 >= BM && FM1 >= 1, "wave rows");
+  static_assert(BQ >= 1 && ABLK * RPB == BM && BQ * RPB * NW == BN, "tile shape");
+  static_assert(EVEN ? AQ * NW == ABLK : NS == 2, "uneven A blocks need the full wait of two stages");
   static_assert(NS >= 2 && NS <= 4 && DQ * (NS - 2) < 64, "stages");
   static_assert(64 * LC * 4 <= NS * STAGE * 2, "epilogue strip must fit in the stage buffers");
   // one LDS block with the stage buffers at offset 0 (the row table and the
@@ -510,7 +521,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restric
   int* const t0s = (int*)(lds + SMEM_BYTES + 64 * 16);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = EVEN ? (wave & 1) : wave / WN, wn = EVEN ? (wave >> 1) : wave % WN;
+  const int row0 = wm * TM0;                               // first tile row of this wave row
   constexpr int GM = 4;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
@@ -530,11 +542,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restric
 
   // per-lane source offsets (elements) of this wave's DMA blocks, k-tile 0;
   // rows beyond M / N are clamped (they feed outputs that are never stored)
+  auto ablk = [&](int q) { return EVEN ? wave * AQ + q : q * NW + wave; };
   uint32_t a_src[AQ], b_src[BQ];
   const int lrow = lane / CPR, lpos = lane % CPR;
 #pragma unroll
   for (int q = 0; q < AQ; ++q) {
-    const int r = (wave * AQ + q) * RPB + lrow;
+    const int r = min(ablk(q), ABLK - 1) * RPB + lrow;
     a_src[q] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)K + (uint32_t)((lpos ^ swz<BK>(r)) * 8);
   }
 #pragma unroll
@@ -550,9 +563,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restric
     bf16* bs = as + BM * BK;
 #pragma unroll
     for (int q = 0; q < AQ; ++q)
-      if (part < 0 || q * (BK / 16) / DQ == part)
+      if ((EVEN || ablk(q) < ABLK) && (part < 0 || q * (BK / 16) / DQ == part))
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(A + a_src[q] + k0),
-                                         (__attribute__((address_space(3))) void*)(as + (wave * AQ + q) * RPB * BK),
+                                         (__attribute__((address_space(3))) void*)(as + ablk(q) * RPB * BK),
                                          16, 0, 0);
 #pragma unroll
     for (int q = 0; q < BQ; ++q)
@@ -563,19 +576,21 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restric
   };
   // fragment rows of this lane and their swizzle
   const int lr = lane & 31, lh = lane >> 5;
-  // MFMAs over stage buf; with SPREAD and WI the DMA of k-tile nkt into stage
-  // nbuf is issued a part per 16-wide k step
-  auto compute = [&](int buf, int nkt, int nbuf, auto wi) {
+  // MFMAs over stage buf for a wave row of FR fragment rows; with SPREAD and
+  // WI the DMA of k-tile nkt into stage nbuf is issued a part per 16-wide k
+  // step
+  auto compute_rows = [&](int buf, int nkt, int nbuf, auto wi, auto fr) {
+    constexpr int FR = decltype(fr)::value;
     const bf16* as = smem + buf * STAGE;
     const bf16* bs = as + BM * BK;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       if constexpr (SPREAD && decltype(wi)::value) issue(nkt, nbuf, ks);
       const int c = ks * 2 + lh;           // logical 16-byte chunk of this lane
-      bf16x8 fa[FM], fb[FN];
+      bf16x8 fa[FR], fb[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int row = wm * TM + i * 32 + lr;
+      for (int i = 0; i < FR; ++i) {
+        const int row = row0 + i * 32 + lr;
         fa[i] = *(const bf16x8*)(as + row * BK + ((c ^ swz<BK>(row)) * 8));
       }
 #pragma unroll
@@ -584,10 +599,18 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restric
         fb[j] = *(const bf16x8*)(bs + row * BK + ((c ^ swz<BK>(row)) * 8));
       }
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FR; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           acc[i][j] = mfma32<H16>(fa[i], fb[j], acc[i][j]);
+    }
+  };
+  auto compute = [&](int buf, int nkt, int nbuf, auto wi) {
+    if constexpr (EVEN) {
+      compute_rows(buf, nkt, nbuf, wi, std::integral_constant<int, FM>{});
+    } else {
+      if (wm == 0) compute_rows(buf, nkt, nbuf, wi, std::integral_constant<int, FM>{});
+      else compute_rows(buf, nkt, nbuf, wi, std::integral_constant<int, FM1>{});
     }
   };
 
@@ -626,14 +649,18 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restric
   __syncthreads();
 
   // epilogue in 64-row strips staged through LDS; a strip gathers the
-  // 32-row fragment rows of whichever waves hold them (TM may be 96)
+  // 32-row fragment rows of whichever waves hold them (a wave row may hold
+  // 96 or 64 rows); the last strip of a 160-row tile is half full, and rows
+  // past the tile (mt) are not stored
   float* stg = (float*)smem;
+  const int mt = min(M, m0 + BM);
+  const int fm = (EVEN || wm == 0) ? FM : FM1;
 #pragma unroll
-  for (int s = 0; s < BM / 64; ++s) {
+  for (int s = 0; s < (BM + 63) / 64; ++s) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const int rb = wm * TM + i * 32;
-      if (rb / 64 == s) {
+      const int rb = row0 + i * 32;
+      if (i < fm && rb / 64 == s) {
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -644,9 +671,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restric
           }
       }
     }
-    epi_rows<MODE>(E, rowtab, m0 + s * 64, M, tid, t0s);
+    epi_rows<MODE>(E, rowtab, m0 + s * 64, mt, tid, t0s);
     __syncthreads();
-    epi_strip<BN, NT, MODE>(E, stg, LC, m0 + s * 64, n0, M, N, tid, rowtab);
+    epi_strip<BN, NT, MODE>(E, stg, LC, m0 + s * 64, n0, mt, N, tid, rowtab);
     __syncthreads();
   }
 }
@@ -721,10 +748,10 @@ static int device_cus() {
   return cus;
 }
 
-template <int BM, int BN, int NW, int BK, int NS, bool SPREAD, int MODE, bool H16 = false>
+template <int BM, int BN, int NW, int BK, int NS, bool SPREAD, int MODE, bool H16 = false, int TM0 = BM / 2>
 hipError_t launch_dma(hipStream_t s, const bf16* A, const bf16* W, int M, int N, int K, const Epi& E) {
   const unsigned grid = (unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
-  gemm_dma_kernel<BM, BN, NW, BK, NS, SPREAD, MODE, H16><<<grid, 64 * NW, 0, s>>>(A, W, M, N, K, E);
+  gemm_dma_kernel<BM, BN, NW, BK, NS, SPREAD, MODE, H16, TM0><<<grid, 64 * NW, 0, s>>>(A, W, M, N, K, E);
   return hipGetLastError();
 }
 
@@ -930,21 +957,32 @@ hipError_t gemm_mfma_mode(hipStream_t s, const bf16* A, const bf16* W, int M, in
     if (launch_stream<MODE, H16>(s, A, W, M, N, K, E, &err)) return err;
   }
   if (K % 64 == 0) {
-    // direct-to-LDS, DMA spread over the MFMAs, one workgroup per CU: 256 x 256
-    // or 192 x 256 tiles, whichever needs the smaller (rounds of resident
-    // tiles) x (tile area); 192-row tiles fill more CUs when the 256-row
-    // grid leaves many idle (N = 1536: 150 vs 198 tiles on 256 CUs)
+    // direct-to-LDS, DMA spread over the MFMAs, one workgroup per CU, tiles of
+    // 256 columns and 256, 224, 192 or 160 rows (224 and 160 split unevenly
+    // over the two wave rows: 128 + 96 and 96 + 64), whichever needs the
+    // fewest (rounds of resident tiles) x (tile rows), ties to the larger
+    // tile; the 160-row tile is charged 8 % (more operand traffic per flop,
+    // a half-empty last epilogue strip: the video QKV measured 5 % slower on
+    // 3 rounds of 160 rows than on 2 of 256).  Measured at the video shapes
+    // (6240 rows, normal operands, one box): QKV 130.5 us on 256-row tiles
+    // (450 tiles, 1.76 rounds) vs 104.3 on 224 (504, 1.97); FFN1 221.8 on
+    // 192 vs 204.9 on 224; N = 1536 (FFN2) 179.0 on 192 (198 tiles) vs 165.9
+    // on 160 (234).
     const int64_t cus = device_cus();
-    const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-    const int64_t t192 = (int64_t)((M + 191) / 192) * ((N + 255) / 256);
-    const int64_t c256 = (t256 + cus - 1) / cus * 256, c192 = (t192 + cus - 1) / cus * 192;
+    const int64_t tn = (N + 255) / 256;
+    auto cost = [&](int bm) { return ((M + bm - 1) / bm * tn + cus - 1) / cus * bm; };
+    const int64_t t192 = (int64_t)((M + 191) / 192) * tn;
     // small problems: when even the 192-row tiles would occupy fewer than 60 %
     // of the CUs, 128 x 128 tiles (4 waves, two workgroups per CU) spread the
     // work over more of them (measured faster on every GEMM of the 12- and
     // 24-block image DiTs, slower on the video DiT's 198-tile N = 1536 GEMMs)
     if (t192 * 10 < cus * 6) return launch_dma<128, 128, 4, 64, 2, true, MODE, H16>(s, A, W, M, N, K, E);
-    if (c192 < c256) return launch_dma<192, 256, 8, 64, 2, true, MODE, H16>(s, A, W, M, N, K, E);
-    return launch_dma<256, 256, 8, 64, 2, true, MODE, H16>(s, A, W, M, N, K, E);
+    const int64_t c256 = cost(256), c224 = cost(224), c192 = cost(192), c160 = cost(160) * 108 / 100;
+    const int64_t best = std::min(std::min(c256, c224), std::min(c192, c160));
+    if (c256 == best) return launch_dma<256, 256, 8, 64, 2, true, MODE, H16>(s, A, W, M, N, K, E);
+    if (c224 == best) return launch_dma<224, 256, 8, 64, 2, true, MODE, H16, 128>(s, A, W, M, N, K, E);
+    if (c192 == best) return launch_dma<192, 256, 8, 64, 2, true, MODE, H16>(s, A, W, M, N, K, E);
+    return launch_dma<160, 256, 8, 64, 2, true, MODE, H16, 96>(s, A, W, M, N, K, E);
   }
   const int bm = opts[best].bm, bn = opts[best].bn;
   const unsigned grid = (unsigned)(((M + bm - 1) / bm) * ((N + bn - 1) / bn));

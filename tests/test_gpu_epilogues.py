@@ -114,14 +114,22 @@ def test_qkv_rope_small_head_dims_and_strided_destination(lib):
     qkv_case(lib, 2, 2, 4, 6, 128, 4, rope=True, t0s=[1, 1000], kextra=8, seed=3)
 
 
+def test_qkv_rope_ragged_160_row_tiles(lib):
+    """1872-token rows: 3744 rows take 160-row tiles (2 rounds of 24 x 18
+    tiles against 2 of 15 x 18 256-row tiles) and end in a tile of 64 rows."""
+    qkv_case(lib, R, T, 24, 39, D, H, True, [0, 7])
+
+
 def test_qkv_scatter_video14b_width_exact(lib):
     # d 5120, 40 heads, one row
     qkv_case(lib, 1, T, Hp, Wp, 5120, 40, rope=False, t0s=[0], seed=4)
 
 
 # ------------------------------------------------------------------ FFN first layer with GELU
-@pytest.mark.parametrize("M,N,K", [(R * L, F, D), (1000, 520, 256)])
+@pytest.mark.parametrize("M,N,K", [(R * L, F, D), (6100, F, D), (1000, 520, 256)])
 def test_gelu_epilogue(lib, M, N, K):
+    """224-row tiles (128 + 96 rows per wave row) at 6240 and 6100 rows (the
+    latter ends in a tile of 52 rows); 128 x 128 tiles for the small case."""
     print(f"gelu M={M} N={N} K={K}", flush=True)
     A, W, b, acc = int_operands(M, N, K, 5)
     out = torch.empty((M, N), dtype=torch.bfloat16, device=device())
@@ -136,11 +144,12 @@ def test_gelu_epilogue(lib, M, N, K):
 
 
 # ------------------------------------------------------------------ gated residual (attention out, FFN out)
-@pytest.mark.parametrize("M,N,K", [(R * L, D, D), (R * L, D, F), (700, 136, 320)])
+@pytest.mark.parametrize("M,N,K", [(R * L, D, D), (R * L, D, F), (6100, D, D), (6020, D, 960), (700, 136, 320)])
 def test_gate_resid_epilogue_exact(lib, M, N, K):
     """resid += (mod[r][5d + n] + blk[5d + n]) * (A W^T + b)[m][n], r = m / L.
     Gates are multiples of 1/2 and the residual a multiple of 1/256: every
-    product and sum is exact in fp32."""
+    product and sum is exact in fp32.  N = 1536 takes 160-row tiles (96 + 64
+    rows per wave row); 6100 and 6020 rows end in a tile of 20 and 100 rows."""
     print(f"gate resid M={M} N={N} K={K}", flush=True)
     Lr = L if M % L == 0 else 100
     rows = M // Lr + (M % Lr > 0)
