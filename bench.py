@@ -377,14 +377,16 @@ def vae_run(steps: int, warmup: int, dev, cpu: bool):
     stream = torch.cuda.current_stream()
     layers = []
     for Ly in vae_layers(v):
-        if Ly["cout"] < 32:
-            continue
         T, H, W, ci, co = Ly["T"], Ly["H"], Ly["W"], Ly["cin"], Ly["cout"]
         x = torch.randn((T, H, W, ci), device=dev).to(torch.bfloat16)
         cache = torch.randn((2, H, W, ci), device=dev).to(torch.bfloat16)
         wt = (torch.randn((co, 27 * ci), device=dev) / np.sqrt(27 * ci)).to(torch.bfloat16)
-        y = torch.empty((T, H, W, co), dtype=torch.bfloat16, device=dev)
-        call = lambda: lib.sd_k_conv3d(x.data_ptr(), cache.data_ptr(), wt.data_ptr(), None, y.data_ptr(), None,
+        # the narrow last layers (latent and pixel projections) write fp32 channels-first
+        narrow = co < 32
+        y = torch.empty((T, co, H, W) if narrow else (T, H, W, co), dtype=torch.float32 if narrow else torch.bfloat16,
+                        device=dev)
+        call = lambda: lib.sd_k_conv3d(x.data_ptr(), cache.data_ptr(), wt.data_ptr(), None,
+                                       None if narrow else y.data_ptr(), y.data_ptr() if narrow else None,
                                        T, H, W, ci, co, C.c_void_p(stream.cuda_stream))
         for _ in range(2):
             call()

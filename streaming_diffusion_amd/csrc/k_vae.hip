@@ -537,6 +537,173 @@ __global__ __launch_bounds__(512) void conv3d_halo_kernel(ConvArgs a) {
   }
 }
 
+// The same halo scheme for layers with at most 16 output channels (the
+// encoder's latent projection, 16 channels, and the decoder's pixel
+// projection, 3): 16 x 16 x 32 matrix-core products, the weights (zero rows
+// past Cout) as the first operand -- one 16-byte fragment per lane covers a
+// whole 32-channel chunk of one tap, so all 27 taps of a chunk sit in
+// registers, loaded while the previous chunk runs -- and 16 output positions
+// along x as the second, read from the halo.  NW waves, each 1 / NW of the
+// TT x TY x 16 positions.  A product reads as many halo bytes as it does
+// work, so these layers are bound by the LDS reads, which is still far less
+// traffic than gathering every tap's input from memory.  Output: fp32
+// channels-first (ycf) or 16-bit channels-last (Cout a multiple of 4).
+template <int TT, int TY, int NW, bool H16>
+__global__ __launch_bounds__(64 * NW) void conv3d_halo16_kernel(ConvArgs a) {
+  constexpr int TX = 16;
+  constexpr int HY = TY + 2, HX = TX + 2, HT = TT + 2;
+  constexpr int HROWS = HT * HY * HX;
+  constexpr int CK = 32;
+  constexpr int HINS = (HROWS + 15) / 16;               // DMA instructions per halo (16 rows each)
+  constexpr int HQ = (HINS + NW - 1) / NW;              // per wave
+  constexpr int HBUF = HINS * 16 * CK;
+  constexpr int PW = TT * TY * TX / NW, MB = PW / 16;   // positions per wave, blocks of 16
+  static_assert(MB >= 1 && PW % 16 == 0, "wave tile");
+  __shared__ __attribute__((aligned(1024))) bf16 halo0[HBUF];
+  __shared__ __attribute__((aligned(1024))) bf16 halo1[HBUF];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int HW = a.H * a.W;
+  const int K = 27 * a.Cin;
+  const int tiles_x = (a.W + TX - 1) / TX;
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int y0 = (lid / tiles_x) * TY, x0 = (lid % tiles_x) * TX;
+  const bf16* const zero = conv_zero_row;
+
+  const bf16* hsrc[HQ];
+#pragma unroll
+  for (int q = 0; q < HQ; ++q) {
+    const int ins = wave * HQ + q;
+    const int row = ins * 16 + (lane >> 2);
+    const bf16* src = nullptr;
+    if (ins < HINS && row < HROWS) {
+      const int ft = row / (HY * HX), hy = (row / HX) % HY, hx = row % HX;
+      const int ti = ft - 2, y = y0 + hy - 1, x = x0 + hx - 1;
+      if ((unsigned)y < (unsigned)a.H && (unsigned)x < (unsigned)a.W) {
+        if (ti >= 0)
+          src = a.x + ((int64_t)ti * HW + (int64_t)y * a.W + x) * a.Cin;
+        else if (a.cache)
+          src = a.cache + ((int64_t)(ti + 2) * HW + (int64_t)y * a.W + x) * a.Cin;
+      }
+      if (src) src += ((lane & 3) ^ cv_swz<CK>(row)) * 8;
+    }
+    hsrc[q] = src;
+  }
+  auto issue_halo = [&](int cc, bf16* buf) {
+#pragma unroll
+    for (int q = 0; q < HQ; ++q) {
+      const int ins = wave * HQ + q;
+      if (ins < HINS)
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(hsrc[q] ? hsrc[q] + cc * CK : zero),
+            (__attribute__((address_space(3))) void*)(buf + ins * 16 * CK), 16, 0, 0);
+    }
+  };
+  // second operand: lane -> position (block base + lane % 16), channels
+  // 8 (lane / 16) .. + 7 of the chunk; halo row of tap (0, 0, 0) per block
+  const int l16 = lane & 15, lq = lane >> 4;
+  int hbase[MB];
+#pragma unroll
+  for (int j = 0; j < MB; ++j) {
+    const int pw = wave * PW + j * 16 + l16;
+    const int tf = pw / (TY * TX), r = (pw / TX) % TY, c = pw % TX;
+    hbase[j] = (tf * HY + r) * HX + c;
+  }
+  // first operand: lane -> output channel lane % 16 (zero past Cout), the
+  // same 8 channels of the chunk, every tap
+  const bool wlive = l16 < a.Cout;
+  const bf16* const wrow = a.w + (int64_t)(wlive ? l16 : 0) * K + lq * 8;
+  bf16x8 wt[27];
+  auto load_w = [&](int cc) {
+#pragma unroll
+    for (int tap = 0; tap < 27; ++tap) {
+      bf16x8 v = {};
+      if (wlive) v = *(const bf16x8*)(wrow + tap * a.Cin + cc * CK);
+      wt[tap] = v;
+    }
+  };
+
+  f32x4 acc[MB];
+#pragma unroll
+  for (int j = 0; j < MB; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[j][q] = 0.f;
+
+  const int NC = a.Cin / CK;
+  auto chunk = [&](int cc, const bf16* rd, bf16* wr) {
+    // halo and weights of chunk cc landed in every wave; every wave is done
+    // with the buffer the next halo overwrites
+    __builtin_amdgcn_s_waitcnt(0x0070);               // vmcnt(0) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    if (cc + 1 < NC) issue_halo(cc + 1, wr);
+    __builtin_amdgcn_sched_barrier(0);
+    // halo fragments one tap ahead of the products (two register sets); a
+    // scheduling fence per tap keeps the compiler from hoisting every tap's
+    // reads, which would not fit in registers
+    auto read_tap = [&](int tap, bf16x8 (&fp)[MB]) {
+      const int dt = tap / 9, dy = (tap / 3) % 3, dx = tap % 3;
+      const int toff = (dt * HY + dy) * HX + dx;
+#pragma unroll
+      for (int j = 0; j < MB; ++j) {
+        const int row = hbase[j] + toff;
+        fp[j] = *(const bf16x8*)(rd + row * CK + ((lq ^ cv_swz<CK>(row)) * 8));
+      }
+    };
+    // the 27 x MB swizzled read addresses do not change between chunks; left
+    // to itself the compiler keeps them all in registers across the chunk
+    // loop and spills, so they are recomputed per tap
+#pragma unroll
+    for (int j = 0; j < MB; ++j) asm volatile("" : "+v"(hbase[j]));
+    bf16x8 fa[MB], fb[MB];
+    read_tap(0, fa);
+#pragma unroll
+    for (int tap = 0; tap < 27; ++tap) {
+      bf16x8 (&cur)[MB] = (tap & 1) ? fb : fa;
+      bf16x8 (&nxt)[MB] = (tap & 1) ? fa : fb;
+      if (tap < 26) read_tap(tap + 1, nxt);
+#pragma unroll
+      for (int j = 0; j < MB; ++j) {
+        if constexpr (H16)
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, wt[tap]),
+                                                          __builtin_bit_cast(f16x8, cur[j]), acc[j], 0, 0, 0);
+        else
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wt[tap], cur[j], acc[j], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the next chunk's weights, in flight across the next barrier
+    __builtin_amdgcn_sched_barrier(0);
+    if (cc + 1 < NC) load_w(cc + 1);
+  };
+  issue_halo(0, halo0);
+  load_w(0);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int cc = 0; cc < NC; cc += 2) {
+    chunk(cc, halo0, halo1);
+    if (cc + 1 < NC) chunk(cc + 1, halo1, halo0);
+  }
+
+  // lane: position l % 16 of each block, output channels 4 (l / 16) + 0..3
+#pragma unroll
+  for (int j = 0; j < MB; ++j) {
+    const int pw = wave * PW + j * 16 + l16;
+    const int tf = pw / (TY * TX), y = y0 + (pw / TX) % TY, x = x0 + pw % TX;
+    if (y >= a.H || x >= a.W) continue;
+    const int n = 4 * lq;
+    if (n >= a.Cout) continue;
+    if (a.ycf) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (n + e < a.Cout)
+          a.ycf[(((int64_t)tf * a.Cout + n + e) * a.H + y) * a.W + x] = acc[j][e] + (a.b ? (float)a.b[n + e] : 0.f);
+    } else {
+      bf16x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = to16<H16>(acc[j][e] + (a.b ? (float)a.b[n + e] : 0.f));
+      *(bf16x4*)(a.y + ((int64_t)tf * HW + (int64_t)y * a.W + x) * a.Cout + n) = o;
+    }
+  }
+}
+
 hipError_t conv3d(hipStream_t s, const ConvArgs& a) {
   if (a.Cin < 8 || (a.Cin & 7) || a.Cout < 1 || a.T < 1 || a.H < 1 || a.W < 1) return hipErrorInvalidValue;
   if (a.ycf ? false : (!a.y || (a.Cout & 3))) return hipErrorInvalidValue;
@@ -566,6 +733,20 @@ hipError_t conv3d(hipStream_t s, const ConvArgs& a) {
       }
       return hipGetLastError();
     }
+  }
+  // layers with at most 16 output channels (latent and pixel projections):
+  // the narrow halo kernel, 4 x 8 x 16 tiles for 4 frames, 2 x 2 x 16 for 2
+  if (a.Cout <= 16 && a.Cin % 32 == 0 && (a.T == 4 || a.T == 2)) {
+    if (a.T == 4) {
+      const unsigned g = (unsigned)(((a.H + 7) / 8) * ((a.W + 15) / 16));
+      if (a.h16) conv3d_halo16_kernel<4, 8, 8, true><<<g, 512, 0, s>>>(a);
+      else conv3d_halo16_kernel<4, 8, 8, false><<<g, 512, 0, s>>>(a);
+    } else {
+      const unsigned g = (unsigned)(((a.H + 1) / 2) * ((a.W + 15) / 16));
+      if (a.h16) conv3d_halo16_kernel<2, 2, 4, true><<<g, 256, 0, s>>>(a);
+      else conv3d_halo16_kernel<2, 2, 4, false><<<g, 256, 0, s>>>(a);
+    }
+    return hipGetLastError();
   }
   // wide layers with enough tiles to fill the chip twice take the DMA
   // kernel: 256 x 128 tiles when the output channels are a multiple of 128,

@@ -68,6 +68,31 @@ def test_conv3d_narrow_bit_exact_on_integers(lib, Co):
     assert np.array_equal(y.cpu().numpy().astype(np.float64), np.transpose(ref, (0, 3, 1, 2)))
 
 
+@pytest.mark.parametrize("T,H,W,Ci,Co,cf", [(4, 13, 37, 64, 3, True), (4, 9, 20, 32, 16, False),
+                                            (2, 10, 40, 96, 16, True), (2, 7, 19, 32, 8, False)])
+def test_conv3d_narrow_halo_bit_exact_on_integers(lib, T, H, W, Ci, Co, cf):
+    """At most 16 output channels with 32-channel input chunks: the narrow halo
+    kernel (16 x 16 x 32 products, weights zero past Cout; 4 x 8 x 16 tiles for
+    4 frames, 2 x 2 x 16 for 2), ragged frames, an odd number of chunks (96
+    channels), fp32 channels-first or bf16 channels-last out."""
+    print(f"conv3d narrow halo T={T} H={H} W={W} Cin={Ci} Cout={Co} cf={cf}", flush=True)
+    x, cache, w, b = int_operands(T * 31 + Co + Ci, T, H, W, Ci, Co)
+    ref, _ = ovae.causal_conv3d(x, w, b, cache)
+    dx, dc, dw, db = (to_dev(a, torch.bfloat16) for a in (x, cache, w, b))
+    if cf:
+        y = torch.empty((T, Co, H, W), dtype=torch.float32, device=device())
+        call(lib.sd_k_conv3d(dx.data_ptr(), dc.data_ptr(), dw.data_ptr(), db.data_ptr(), None, y.data_ptr(),
+                             T, H, W, Ci, Co, stream_ptr()))
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy().astype(np.float64), np.transpose(ref, (0, 3, 1, 2)))
+    else:
+        y = torch.empty((T, H, W, Co), dtype=torch.bfloat16, device=device())
+        call(lib.sd_k_conv3d(dx.data_ptr(), dc.data_ptr(), dw.data_ptr(), db.data_ptr(), y.data_ptr(), None,
+                             T, H, W, Ci, Co, stream_ptr()))
+        torch.cuda.synchronize()
+        assert np.array_equal(y.float().cpu().numpy().astype(np.float64), bf16_of(ref))
+
+
 def test_conv3d_without_cache_is_zero_history(lib):
     T, H, W, Ci, Co = 3, 4, 5, 16, 8
     x, _, w, b = int_operands(7, T, H, W, Ci, Co)
@@ -103,13 +128,16 @@ def conv_at(x, cache, w, b, t, i, j):
 
 
 @pytest.mark.parametrize("T,H,W,Ci,Co", [(4, 128, 160, 64, 256), (4, 128, 256, 128, 128), (4, 256, 256, 128, 64),
-                                         (4, 124, 200, 96, 192), (2, 256, 256, 64, 128), (3, 256, 352, 64, 64)])
+                                         (4, 124, 200, 96, 192), (2, 256, 256, 64, 128), (3, 256, 352, 64, 64),
+                                         (2, 60, 104, 256, 256)])
 def test_conv3d_wide_paths_bit_exact_sampled(lib, T, H, W, Ci, Co):
     """The wide-layer kernels: 4-frame layers take the halo kernel (4 x 8 x 16
     output tiles, the 6 x 10 x 18 input halo per 32-channel chunk in LDS, all
     27 taps read from it; ragged 124 x 200 frame and 96 / 192 channels
     included), other layers with at least 512 tiles the DMA-fed implicit GEMM
-    (256 x 128 and 512 x 64 tiles, 64-deep k-tiles inside one tap).  Integer
+    (256 x 128 and 512 x 64 tiles, 64-deep k-tiles inside one tap), the
+    encoder's latent-resolution layer (2 x 60 x 104, 256 channels, too few
+    tiles for both) the register-staged kernel.  Integer
     operands: outputs at borders, cache frames and random positions equal the
     exact sum rounded once to bf16."""
     print(f"conv3d DMA path T={T} H={H} W={W} Cin={Ci} Cout={Co}", flush=True)
@@ -129,7 +157,8 @@ def test_conv3d_wide_paths_bit_exact_sampled(lib, T, H, W, Ci, Co):
 @pytest.mark.parametrize("layer", ["d3", "d_out"])
 def test_conv3d_full_video_shape_sampled(lib, layer):
     """The video decoder's two full-resolution layers (4 x 480 x 832): d3
-    (128 -> 64 channels, bf16 out) and d_out (64 -> 3, fp32 channels-first out),
+    (128 -> 64 channels, bf16 out) and d_out (64 -> 3, fp32 channels-first out,
+    the narrow halo kernel),
     random bf16 operands, outputs sampled at borders, cache frames and random
     positions against the definition in fp64."""
     v = get_vae_config("video13b")
