@@ -765,6 +765,15 @@ hipError_t conv3d(hipStream_t s, const ConvArgs& a) {
       }
       return hipGetLastError();
     }
+    // the latent-resolution layers (12 480 positions): 128 x 64 tiles, two
+    // workgroups per CU, so the grid still covers the chip
+    const int64_t t64 = ((M + 127) / 128) * (a.Cout / 64);
+    if (t64 >= 256) {
+      const unsigned g = (unsigned)t64;
+      if (a.h16) conv3d_dma_kernel<128, 64, 4, 3, true><<<g, 512, 0, s>>>(a);
+      else conv3d_dma_kernel<128, 64, 4, 3, false><<<g, 512, 0, s>>>(a);
+      return hipGetLastError();
+    }
   }
   if (a.Cout <= 32) SD_CONV_LAUNCH(32);
   else if (a.Cout <= 64) SD_CONV_LAUNCH(64);

@@ -41,8 +41,10 @@ def bf16_of(a):
 
 @pytest.mark.parametrize("T,H,W,Ci,Co", [(4, 5, 7, 8, 16), (4, 9, 13, 24, 64), (2, 6, 10, 64, 132),
                                          (3, 16, 17, 128, 256), (4, 1, 1, 8, 4), (3, 7, 11, 16, 32),
-                                         (2, 5, 6, 8, 20), (2, 8, 9, 40, 96)])
+                                         (2, 5, 6, 8, 20), (2, 8, 9, 40, 96), (2, 47, 97, 64, 256)])
 def test_conv3d_bit_exact_on_integers(lib, T, H, W, Ci, Co):
+    """Register-staged implicit GEMM at ragged small shapes; the last case
+    (9118 positions, 256 channels) takes the DMA kernel's 128 x 64 tiles."""
     print(f"conv3d exact T={T} H={H} W={W} Cin={Ci} Cout={Co}", flush=True)
     x, cache, w, b = int_operands(T * 1000 + Co, T, H, W, Ci, Co)
     ref, _ = ovae.causal_conv3d(x, w, b, cache)
@@ -137,7 +139,7 @@ def test_conv3d_wide_paths_bit_exact_sampled(lib, T, H, W, Ci, Co):
     included), other layers with at least 512 tiles the DMA-fed implicit GEMM
     (256 x 128 and 512 x 64 tiles, 64-deep k-tiles inside one tap), the
     encoder's latent-resolution layer (2 x 60 x 104, 256 channels, too few
-    tiles for both) the register-staged kernel.  Integer
+    tiles for both) its 128 x 64 tiles.  Integer
     operands: outputs at borders, cache frames and random positions equal the
     exact sum rounded once to bf16."""
     print(f"conv3d DMA path T={T} H={H} W={W} Cin={Ci} Cout={Co}", flush=True)
