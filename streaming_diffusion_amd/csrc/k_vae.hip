@@ -548,8 +548,12 @@ __global__ __launch_bounds__(512) void conv3d_halo_kernel(ConvArgs a) {
 // work, so these layers are bound by the LDS reads, which is still far less
 // traffic than gathering every tap's input from memory.  Output: fp32
 // channels-first (ycf) or 16-bit channels-last (Cout a multiple of 4).
-template <int TT, int TY, int NW, bool H16>
-__global__ __launch_bounds__(64 * NW) void conv3d_halo16_kernel(ConvArgs a) {
+//
+// NBUF = 1 keeps a single halo buffer (the next chunk's halo is DMA'd after
+// every wave is done with this one), so two workgroups fit on a CU and one
+// computes while the other waits for its halo.
+template <int TT, int TY, int NW, int NBUF, bool H16>
+__global__ __launch_bounds__(64 * NW, NBUF == 1 ? 2 : 1) void conv3d_halo16_kernel(ConvArgs a) {
   constexpr int TX = 16;
   constexpr int HY = TY + 2, HX = TX + 2, HT = TT + 2;
   constexpr int HROWS = HT * HY * HX;
@@ -558,9 +562,9 @@ __global__ __launch_bounds__(64 * NW) void conv3d_halo16_kernel(ConvArgs a) {
   constexpr int HQ = (HINS + NW - 1) / NW;              // per wave
   constexpr int HBUF = HINS * 16 * CK;
   constexpr int PW = TT * TY * TX / NW, MB = PW / 16;   // positions per wave, blocks of 16
-  static_assert(MB >= 1 && PW % 16 == 0, "wave tile");
+  static_assert(MB >= 1 && PW % 16 == 0 && (NBUF == 1 || NBUF == 2), "wave tile");
   __shared__ __attribute__((aligned(1024))) bf16 halo0[HBUF];
-  __shared__ __attribute__((aligned(1024))) bf16 halo1[HBUF];
+  __shared__ __attribute__((aligned(1024))) bf16 halo1[NBUF == 2 ? HBUF : 8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int HW = a.H * a.W;
   const int K = 27 * a.Cin;
@@ -569,33 +573,36 @@ __global__ __launch_bounds__(64 * NW) void conv3d_halo16_kernel(ConvArgs a) {
   const int y0 = (lid / tiles_x) * TY, x0 = (lid % tiles_x) * TX;
   const bf16* const zero = conv_zero_row;
 
-  const bf16* hsrc[HQ];
+  // this lane's halo rows as 32-bit element offsets (registers are tight):
+  // >= 0 into x, <= -2 into the cache (-2 - offset), -1 the zero row
+  int hoff[HQ];
 #pragma unroll
   for (int q = 0; q < HQ; ++q) {
     const int ins = wave * HQ + q;
     const int row = ins * 16 + (lane >> 2);
-    const bf16* src = nullptr;
+    int off = -1;
     if (ins < HINS && row < HROWS) {
       const int ft = row / (HY * HX), hy = (row / HX) % HY, hx = row % HX;
       const int ti = ft - 2, y = y0 + hy - 1, x = x0 + hx - 1;
+      const int sw = ((lane & 3) ^ cv_swz<CK>(row)) * 8;
       if ((unsigned)y < (unsigned)a.H && (unsigned)x < (unsigned)a.W) {
         if (ti >= 0)
-          src = a.x + ((int64_t)ti * HW + (int64_t)y * a.W + x) * a.Cin;
+          off = (ti * HW + y * a.W + x) * a.Cin + sw;
         else if (a.cache)
-          src = a.cache + ((int64_t)(ti + 2) * HW + (int64_t)y * a.W + x) * a.Cin;
+          off = -2 - (((ti + 2) * HW + y * a.W + x) * a.Cin + sw);
       }
-      if (src) src += ((lane & 3) ^ cv_swz<CK>(row)) * 8;
     }
-    hsrc[q] = src;
+    hoff[q] = off;
   }
   auto issue_halo = [&](int cc, bf16* buf) {
 #pragma unroll
     for (int q = 0; q < HQ; ++q) {
       const int ins = wave * HQ + q;
+      const int off = hoff[q];
+      const bf16* src = off >= 0 ? a.x + off + cc * CK : (off == -1 ? zero : a.cache + (-2 - off) + cc * CK);
       if (ins < HINS)
-        __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void*)(hsrc[q] ? hsrc[q] + cc * CK : zero),
-            (__attribute__((address_space(3))) void*)(buf + ins * 16 * CK), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                         (__attribute__((address_space(3))) void*)(buf + ins * 16 * CK), 16, 0, 0);
     }
   };
   // second operand: lane -> position (block base + lane % 16), channels
@@ -634,12 +641,12 @@ __global__ __launch_bounds__(64 * NW) void conv3d_halo16_kernel(ConvArgs a) {
     // with the buffer the next halo overwrites
     __builtin_amdgcn_s_waitcnt(0x0070);               // vmcnt(0) lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
-    if (cc + 1 < NC) issue_halo(cc + 1, wr);
+    if (NBUF == 2 && cc + 1 < NC) issue_halo(cc + 1, wr);
     __builtin_amdgcn_sched_barrier(0);
     // halo fragments one tap ahead of the products (two register sets); a
     // scheduling fence per tap keeps the compiler from hoisting every tap's
     // reads, which would not fit in registers
-    auto read_tap = [&](int tap, bf16x8 (&fp)[MB]) {
+    auto read_tap = [&](int tap, bf16x8* fp) {
       const int dt = tap / 9, dy = (tap / 3) % 3, dx = tap % 3;
       const int toff = (dt * HY + dy) * HX + dx;
 #pragma unroll
@@ -653,13 +660,20 @@ __global__ __launch_bounds__(64 * NW) void conv3d_halo16_kernel(ConvArgs a) {
     // loop and spills, so they are recomputed per tap
 #pragma unroll
     for (int j = 0; j < MB; ++j) asm volatile("" : "+v"(hbase[j]));
-    bf16x8 fa[MB], fb[MB];
+    // (with one halo buffer two workgroups share the CU and hide each
+    // other's read latency: a single register set)
+    constexpr int NF = NBUF == 2 ? MB : 1;
+    bf16x8 fa[MB], fb[NF];
     read_tap(0, fa);
 #pragma unroll
     for (int tap = 0; tap < 27; ++tap) {
-      bf16x8 (&cur)[MB] = (tap & 1) ? fb : fa;
-      bf16x8 (&nxt)[MB] = (tap & 1) ? fa : fb;
-      if (tap < 26) read_tap(tap + 1, nxt);
+      bf16x8* cur = fa;
+      if constexpr (NBUF == 2) {
+        cur = (tap & 1) ? fb : fa;
+        if (tap < 26) read_tap(tap + 1, (tap & 1) ? fa : fb);
+      } else if (tap > 0) {
+        read_tap(tap, fa);
+      }
 #pragma unroll
       for (int j = 0; j < MB; ++j) {
         if constexpr (H16)
@@ -670,16 +684,28 @@ __global__ __launch_bounds__(64 * NW) void conv3d_halo16_kernel(ConvArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // the next chunk's weights, in flight across the next barrier
+    // the next chunk's weights (and with one buffer its halo, once every
+    // wave is done reading this one), in flight across the next barrier
     __builtin_amdgcn_sched_barrier(0);
-    if (cc + 1 < NC) load_w(cc + 1);
+    if (cc + 1 < NC) {
+      if constexpr (NBUF == 1) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0): this wave's halo reads are done
+        __builtin_amdgcn_s_barrier();
+        issue_halo(cc + 1, wr);
+      }
+      load_w(cc + 1);
+    }
   };
   issue_halo(0, halo0);
   load_w(0);
   __builtin_amdgcn_sched_barrier(0);
-  for (int cc = 0; cc < NC; cc += 2) {
-    chunk(cc, halo0, halo1);
-    if (cc + 1 < NC) chunk(cc + 1, halo1, halo0);
+  if constexpr (NBUF == 1) {
+    for (int cc = 0; cc < NC; ++cc) chunk(cc, halo0, halo0);
+  } else {
+    for (int cc = 0; cc < NC; cc += 2) {
+      chunk(cc, halo0, halo1);
+      if (cc + 1 < NC) chunk(cc + 1, halo1, halo0);
+    }
   }
 
   // lane: position l % 16 of each block, output channels 4 (l / 16) + 0..3
@@ -738,13 +764,13 @@ hipError_t conv3d(hipStream_t s, const ConvArgs& a) {
   // the narrow halo kernel, 4 x 8 x 16 tiles for 4 frames, 2 x 2 x 16 for 2
   if (a.Cout <= 16 && a.Cin % 32 == 0 && (a.T == 4 || a.T == 2)) {
     if (a.T == 4) {
-      const unsigned g = (unsigned)(((a.H + 7) / 8) * ((a.W + 15) / 16));
-      if (a.h16) conv3d_halo16_kernel<4, 8, 8, true><<<g, 512, 0, s>>>(a);
-      else conv3d_halo16_kernel<4, 8, 8, false><<<g, 512, 0, s>>>(a);
+      const unsigned g = (unsigned)(((a.H + 3) / 4) * ((a.W + 15) / 16));
+      if (a.h16) conv3d_halo16_kernel<4, 4, 4, 1, true><<<g, 256, 0, s>>>(a);
+      else conv3d_halo16_kernel<4, 4, 4, 1, false><<<g, 256, 0, s>>>(a);
     } else {
       const unsigned g = (unsigned)(((a.H + 1) / 2) * ((a.W + 15) / 16));
-      if (a.h16) conv3d_halo16_kernel<2, 2, 4, true><<<g, 256, 0, s>>>(a);
-      else conv3d_halo16_kernel<2, 2, 4, false><<<g, 256, 0, s>>>(a);
+      if (a.h16) conv3d_halo16_kernel<2, 2, 4, 2, true><<<g, 256, 0, s>>>(a);
+      else conv3d_halo16_kernel<2, 2, 4, 2, false><<<g, 256, 0, s>>>(a);
     }
     return hipGetLastError();
   }
@@ -810,8 +836,10 @@ __global__ __launch_bounds__(256) void norm_silu_kernel(bf16* __restrict__ x, co
   bf16x8 o;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
+    // SiLU n sigmoid(n) with the hardware reciprocal (1 ulp, far below the
+    // 16-bit rounding of the stored value): n -> -inf gives -0, n -> +inf n
     const float n = f[e] * r * (float)gv[e];
-    o[e] = to16<H16>(n / (1.0f + __expf(-n)));
+    o[e] = to16<H16>(n * __builtin_amdgcn_rcpf(1.0f + __expf(-n)));
   }
   *(bf16x8*)(x + p * C + c0) = o;
 }
