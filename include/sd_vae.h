@@ -17,9 +17,11 @@
  *
  * Memory: the library allocates nothing; the caller provides weights (device,
  * bf16) and a workspace of sd_vae_workspace_bytes() (device, 256-byte
- * aligned), which holds activations, the per-layer caches and an fp16 copy of
- * the convolution weights made at create (activations and caches are stored
- * in fp16; the weights must not change while the handle lives).  Calls are
+ * aligned), which holds two input buffers per layer (used on alternate
+ * chunks: the other one still holds the previous chunk's frames, which are
+ * the layer's cache), a staging buffer and an fp16 copy of the convolution
+ * weights made at create (activations and caches are stored in fp16; the
+ * weights must not change while the handle lives).  Calls are
  * asynchronous on the stream given at create; encode and decode keep separate
  * caches and must each be fed the chunks of one stream in order.
  */

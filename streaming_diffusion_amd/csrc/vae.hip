@@ -1,7 +1,10 @@
 // sd_vae_*: the Stream-VAE runtime (see include/sd_vae.h).  Per chunk the
-// layers run in order on the caller's stream; each convolution reads its
-// cache (the previous chunk's last two input frames) and then replaces it
-// with the last two frames of its own input.  Activations, caches and the
+// layers run in order on the caller's stream.  Every layer owns two input
+// buffers and uses them on alternate chunks: its convolution reads the
+// chunk's frames from one and the previous chunk's last two input frames --
+// the layer's cache -- straight from the other, so no frames are copied.
+// The layer before writes (or resamples) into the buffer of this chunk's
+// parity.  Activations, caches and the
 // convolution weights (copied at create from the caller's bf16) are fp16:
 // the chain stores its activations nine times on the decoder path, and
 // fp16's three extra mantissa bits keep the accumulated rounding an order
@@ -21,7 +24,8 @@ struct VaeLayer {
   int mode;          // resampling of the layer's input: -1 none, else sdk::resample's mode
   bool norm;
   int T, H, W;       // shape of the convolution's input (after resampling)
-  void* cache;       // fp16 [2][H][W][cin]
+  void* in[2];       // fp16 [T][H][W][cin]: this chunk's input / the previous chunk's
+  int par;           // which of in[] the next chunk uses
   void* w16;         // fp16 copy of the weights [cout][27 cin]
 };
 
@@ -43,31 +47,30 @@ int validate(const sd_vae_config& c, std::string* err) {
 void layers_of(const sd_vae_config& c, VaeLayer* L) {
   const int T = c.latent_t, h = c.latent_h, w = c.latent_w, z = c.latent_c;
   const int Tp = 2 * T, H = 8 * h, W = 8 * w;
-  L[SD_VAE_E0] = {8, c.c1, -1, true, Tp, H, W, nullptr, nullptr};
-  L[SD_VAE_E1] = {c.c1, c.c2, 0, true, Tp, H / 2, W / 2, nullptr, nullptr};
-  L[SD_VAE_E2] = {c.c2, c.c3, 0, true, Tp, H / 4, W / 4, nullptr, nullptr};
-  L[SD_VAE_E3] = {c.c3, c.c3, 1, true, T, h, w, nullptr, nullptr};
-  L[SD_VAE_E_OUT] = {c.c3, z, -1, false, T, h, w, nullptr, nullptr};
-  L[SD_VAE_D0] = {z, c.c3, -1, true, T, h, w, nullptr, nullptr};
-  L[SD_VAE_D1] = {c.c3, c.c3, 3, true, Tp, H / 4, W / 4, nullptr, nullptr};
-  L[SD_VAE_D2] = {c.c3, c.c2, 2, true, Tp, H / 2, W / 2, nullptr, nullptr};
-  L[SD_VAE_D3] = {c.c2, c.c1, 2, true, Tp, H, W, nullptr, nullptr};
-  L[SD_VAE_D_OUT] = {c.c1, 3, -1, false, Tp, H, W, nullptr, nullptr};
+  L[SD_VAE_E0] = {8, c.c1, -1, true, Tp, H, W, {nullptr, nullptr}, 0, nullptr};
+  L[SD_VAE_E1] = {c.c1, c.c2, 0, true, Tp, H / 2, W / 2, {nullptr, nullptr}, 0, nullptr};
+  L[SD_VAE_E2] = {c.c2, c.c3, 0, true, Tp, H / 4, W / 4, {nullptr, nullptr}, 0, nullptr};
+  L[SD_VAE_E3] = {c.c3, c.c3, 1, true, T, h, w, {nullptr, nullptr}, 0, nullptr};
+  L[SD_VAE_E_OUT] = {c.c3, z, -1, false, T, h, w, {nullptr, nullptr}, 0, nullptr};
+  L[SD_VAE_D0] = {z, c.c3, -1, true, T, h, w, {nullptr, nullptr}, 0, nullptr};
+  L[SD_VAE_D1] = {c.c3, c.c3, 3, true, Tp, H / 4, W / 4, {nullptr, nullptr}, 0, nullptr};
+  L[SD_VAE_D2] = {c.c3, c.c2, 2, true, Tp, H / 2, W / 2, {nullptr, nullptr}, 0, nullptr};
+  L[SD_VAE_D3] = {c.c2, c.c1, 2, true, Tp, H, W, {nullptr, nullptr}, 0, nullptr};
+  L[SD_VAE_D_OUT] = {c.c1, 3, -1, false, Tp, H, W, {nullptr, nullptr}, 0, nullptr};
 }
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-// bytes of one activation buffer: the largest convolution input or output
+// bytes of the staging buffer: the largest convolution output that is
+// resampled before the next layer
 size_t act_bytes(const VaeLayer* L) {
   size_t m = 0;
-  for (int i = 0; i < SD_VAE_LAYERS; ++i) {
-    const size_t pos = (size_t)L[i].T * L[i].H * L[i].W;
-    m = std::max(m, pos * (size_t)std::max(L[i].cin, L[i].cout));
-  }
+  for (int i = 0; i + 1 < SD_VAE_LAYERS; ++i)
+    if (L[i + 1].mode >= 0) m = std::max(m, (size_t)L[i].T * L[i].H * L[i].W * L[i].cout);
   return align256(m * 2);
 }
 
-size_t cache_bytes(const VaeLayer& l) { return align256((size_t)2 * l.H * l.W * l.cin * 2); }
+size_t input_bytes(const VaeLayer& l) { return align256((size_t)l.T * l.H * l.W * l.cin * 2); }
 size_t weight_bytes(const VaeLayer& l) { return align256((size_t)27 * l.cin * l.cout * 2); }
 
 }  // namespace
@@ -77,8 +80,8 @@ struct sd_vae {
   sd_vae_weights w;
   VaeLayer L[SD_VAE_LAYERS];
   hipStream_t st = nullptr;
-  void* act[2] = {nullptr, nullptr};
-  void* cache_base = nullptr;
+  void* act = nullptr;             // staging of a convolution output that is resampled
+  void* cache_base = nullptr;      // the layers' input buffers
   size_t cache_total = 0;
   std::string err;
 };
@@ -96,42 +99,38 @@ sd_status set_err(sd_vae* v, sd_status code, const std::string& m) {
     if (_e != hipSuccess) return set_err(v, SD_ERR_HIP, std::string(#expr) + ": " + hipGetErrorString(_e)); \
   } while (0)
 
-// layers [first, last] on the channels-last chunk in act[cur] (shape T, H, W,
-// C); the last layer is narrow and writes fp32 channels-first to out
-sd_status run_layers(sd_vae* v, int first, int last, int cur, int T, int H, int W, int C, float* out) {
+// layers [first, last] on the chunk already in L[first].in[par] (16-bit
+// channels-last); the last layer is narrow and writes fp32 channels-first to
+// out
+sd_status run_layers(sd_vae* v, int first, int last, float* out) {
   for (int li = first; li <= last; ++li) {
     VaeLayer& l = v->L[li];
-    int in = cur;
-    if (l.mode >= 0) {
-      VHIP(sdk::resample(v->st, v->act[cur], v->act[cur ^ 1], T, H, W, C, l.mode, true));
-      in = cur ^ 1;
-    }
+    VaeLayer* nx = li < last ? &v->L[li + 1] : nullptr;
+    // this layer's output: the next layer's input buffer of this chunk, or
+    // the staging buffer when the next layer resamples it first
+    void* dst = nx ? (nx->mode >= 0 ? v->act : nx->in[nx->par]) : nullptr;
+    const size_t frame = (size_t)l.H * l.W * l.cin;
     sdk::ConvArgs a;
-    a.x = (const bf16*)v->act[in];
-    a.cache = (const bf16*)l.cache;
+    a.x = (const bf16*)l.in[l.par];
+    a.cache = (const bf16*)((const char*)l.in[l.par ^ 1] + (size_t)(l.T - 2) * frame * 2);
     a.w = (const bf16*)l.w16;
     a.h16 = true;
     a.b = (const bf16*)v->w.b[li];
-    a.y = li == last ? nullptr : (bf16*)v->act[in ^ 1];
-    a.ycf = li == last ? out : nullptr;
+    a.y = (bf16*)dst;
+    a.ycf = nx ? nullptr : out;
     a.T = l.T;
     a.H = l.H;
     a.W = l.W;
     a.Cin = l.cin;
     a.Cout = l.cout;
     VHIP(sdk::conv3d(v->st, a));
-    // this chunk's last two input frames become the layer's cache
-    const size_t frame = (size_t)l.H * l.W * l.cin;
-    VHIP(hipMemcpyAsync(l.cache, (const char*)v->act[in] + (size_t)(l.T - 2) * frame * 2, 2 * frame * 2,
-                        hipMemcpyDeviceToDevice, v->st));
-    if (li == last) break;
+    // the input just read is the next chunk's cache
+    l.par ^= 1;
+    if (!nx) break;
     if (l.norm)
-      VHIP(sdk::norm_silu(v->st, v->act[in ^ 1], v->w.g[li], (int64_t)l.T * l.H * l.W, l.cout, 1e-6f, true));
-    cur = in ^ 1;
-    T = l.T;
-    H = l.H;
-    W = l.W;
-    C = l.cout;
+      VHIP(sdk::norm_silu(v->st, dst, v->w.g[li], (int64_t)l.T * l.H * l.W, l.cout, 1e-6f, true));
+    if (nx->mode >= 0)
+      VHIP(sdk::resample(v->st, v->act, nx->in[nx->par], l.T, l.H, l.W, l.cout, nx->mode, true));
   }
   return SD_OK;
 }
@@ -144,8 +143,8 @@ size_t sd_vae_workspace_bytes(const sd_vae_config* cfg) {
   if (!cfg || validate(*cfg, nullptr) != SD_OK) return 0;
   VaeLayer L[SD_VAE_LAYERS];
   layers_of(*cfg, L);
-  size_t n = 2 * act_bytes(L);
-  for (int i = 0; i < SD_VAE_LAYERS; ++i) n += cache_bytes(L[i]) + weight_bytes(L[i]);
+  size_t n = act_bytes(L);
+  for (int i = 0; i < SD_VAE_LAYERS; ++i) n += 2 * input_bytes(L[i]) + weight_bytes(L[i]);
   return n;
 }
 
@@ -168,15 +167,14 @@ sd_status sd_vae_create(const sd_vae_config* cfg, const sd_vae_weights* w, void*
   v->st = (hipStream_t)hip_stream;
   layers_of(*cfg, v->L);
   char* p = (char*)workspace;
-  const size_t ab = act_bytes(v->L);
-  v->act[0] = p;
-  v->act[1] = p + ab;
-  p += 2 * ab;
+  v->act = p;
+  p += act_bytes(v->L);
   v->cache_base = p;
-  for (int i = 0; i < SD_VAE_LAYERS; ++i) {
-    v->L[i].cache = p;
-    p += cache_bytes(v->L[i]);
-  }
+  for (int i = 0; i < SD_VAE_LAYERS; ++i)
+    for (int k = 0; k < 2; ++k) {
+      v->L[i].in[k] = p;
+      p += input_bytes(v->L[i]);
+    }
   v->cache_total = (size_t)(p - (char*)v->cache_base);
   for (int i = 0; i < SD_VAE_LAYERS; ++i) {
     v->L[i].w16 = p;
@@ -197,7 +195,9 @@ sd_status sd_vae_create(const sd_vae_config* cfg, const sd_vae_weights* w, void*
 
 sd_status sd_vae_reset(sd_vae* v) {
   if (!v) return SD_ERR_ARG;
+  // both input buffers of every layer: the first chunk's caches read zeros
   VHIP(sdk::fill_zero(v->st, v->cache_base, v->cache_total));
+  for (int i = 0; i < SD_VAE_LAYERS; ++i) v->L[i].par = 0;
   return SD_OK;
 }
 
@@ -206,17 +206,19 @@ sd_status sd_vae_encode(sd_vae* v, const float* pixels, float* latent) {
   if (!pixels || !latent) return set_err(v, SD_ERR_ARG, "null pixels or latent");
   const sd_vae_config& c = v->cfg;
   const int Tp = 2 * c.latent_t, H = 8 * c.latent_h, W = 8 * c.latent_w;
-  VHIP(sdk::to_channels_last(v->st, pixels, v->act[0], Tp, 3, H * W, 8, true));
-  return run_layers(v, SD_VAE_E0, SD_VAE_E_OUT, 0, Tp, H, W, 8, latent);
+  VaeLayer& l0 = v->L[SD_VAE_E0];
+  VHIP(sdk::to_channels_last(v->st, pixels, l0.in[l0.par], Tp, 3, H * W, 8, true));
+  return run_layers(v, SD_VAE_E0, SD_VAE_E_OUT, latent);
 }
 
 sd_status sd_vae_decode(sd_vae* v, const float* latent, float* pixels) {
   if (!v) return SD_ERR_ARG;
   if (!pixels || !latent) return set_err(v, SD_ERR_ARG, "null pixels or latent");
   const sd_vae_config& c = v->cfg;
-  VHIP(sdk::to_channels_last(v->st, latent, v->act[0], c.latent_t, c.latent_c, c.latent_h * c.latent_w, c.latent_c,
-                             true));
-  return run_layers(v, SD_VAE_D0, SD_VAE_D_OUT, 0, c.latent_t, c.latent_h, c.latent_w, c.latent_c, pixels);
+  VaeLayer& l0 = v->L[SD_VAE_D0];
+  VHIP(sdk::to_channels_last(v->st, latent, l0.in[l0.par], c.latent_t, c.latent_c, c.latent_h * c.latent_w,
+                             c.latent_c, true));
+  return run_layers(v, SD_VAE_D0, SD_VAE_D_OUT, pixels);
 }
 
 void sd_vae_destroy(sd_vae* v) { delete v; }
