@@ -134,6 +134,17 @@ sd_status sd_k_ln_mod(int32_t dtype, const float* x, void* out, int32_t M, int32
 sd_status sd_k_conv3d(const void* x, const void* cache, const void* w, const void* bias, void* y, float* y_f32_cf,
                       int32_t T, int32_t H, int32_t W, int32_t Cin, int32_t Cout, void* stream);
 
+/* The same convolution reading its input upsampled 2x2 (nearest): x bf16
+ * [T][H/2][W/2][Cin] and cache [2][H/2][W/2][Cin] stand for
+ * x'[t][i][j] = x[t][i/2][j/2] at the output size H x W, as the Stream-VAE
+ * decoder's upsampling layers use it (the upsampled tensor is never
+ * written).  y bf16 [T][H][W][Cout].  Only the shapes of the halo kernel:
+ * T = 4, H and W even, Cin a multiple of 32, Cout of 64, at least 256
+ * output tiles of 4 x 8 x 16 positions x 64 or 128 channels; else
+ * SD_ERR_SHAPE. */
+sd_status sd_k_conv3d_up2(const void* x, const void* cache, const void* w, const void* bias, void* y, int32_t T,
+                          int32_t H, int32_t W, int32_t Cin, int32_t Cout, void* stream);
+
 /* One key segment of an attention call.  K is [cap][hd] per (row, head), V is
  * stored transposed [hd][cap]; a head starts head_stride elements after the
  * previous one and a query row row_stride elements after the previous one

@@ -166,6 +166,8 @@ SIGNATURES = {
     "sd_k_motion_sums": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_int64, C.c_void_p, C.c_void_p]),
     "sd_k_conv3d": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
                               C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p]),
+    "sd_k_conv3d_up2": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
+                                  C.c_int32, C.c_int32, C.c_int32, C.c_void_p]),
     "sd_vae_workspace_bytes": (C.c_size_t, [C.POINTER(sd_vae_config)]),
     "sd_vae_create": (C.c_int, [C.POINTER(sd_vae_config), C.POINTER(sd_vae_weights), C.c_void_p, C.c_size_t,
                                 C.c_void_p, C.POINTER(C.c_void_p)]),

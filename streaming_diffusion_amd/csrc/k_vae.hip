@@ -405,7 +405,11 @@ __global__ __launch_bounds__(512) void conv3d_halo_kernel(ConvArgs a) {
   const bf16* const zero = conv_zero_row;
 
   // this lane's halo rows: row (wave * HQ + q) * 16 + lane / 4; its 16-byte
-  // LDS slot lane % 4 holds logical chunk (lane % 4) ^ swz(row)
+  // LDS slot lane % 4 holds logical chunk (lane % 4) ^ swz(row).  With an
+  // upsampled input the row (y, x) is read from (y / 2, x / 2) of the
+  // half-size frames.
+  const int us = a.up ? 1 : 0;
+  const int Ws = a.W >> us, HWs = (a.H >> us) * Ws;
   const bf16* hsrc[HQ];
 #pragma unroll
   for (int q = 0; q < HQ; ++q) {
@@ -416,10 +420,11 @@ __global__ __launch_bounds__(512) void conv3d_halo_kernel(ConvArgs a) {
       const int ft = row / (HY * HX), hy = (row / HX) % HY, hx = row % HX;
       const int ti = ft - 2, y = y0 + hy - 1, x = x0 + hx - 1;
       if ((unsigned)y < (unsigned)a.H && (unsigned)x < (unsigned)a.W) {
+        const int64_t sp = (int64_t)(y >> us) * Ws + (x >> us);
         if (ti >= 0)
-          src = a.x + ((int64_t)ti * HW + (int64_t)y * a.W + x) * a.Cin;
+          src = a.x + ((int64_t)ti * HWs + sp) * a.Cin;
         else if (a.cache)
-          src = a.cache + ((int64_t)(ti + 2) * HW + (int64_t)y * a.W + x) * a.Cin;
+          src = a.cache + ((int64_t)(ti + 2) * HWs + sp) * a.Cin;
       }
       if (src) src += ((lane & 3) ^ cv_swz<CK>(row)) * 8;
     }
@@ -730,8 +735,15 @@ __global__ __launch_bounds__(64 * NW, NBUF == 1 ? 2 : 1) void conv3d_halo16_kern
   }
 }
 
+bool conv3d_upsample_ok(int T, int H, int W, int Cin, int Cout) {
+  if (T != 4 || Cin % 32 || Cout % 64 || (H & 1) || (W & 1)) return false;
+  const int64_t tiles = (int64_t)((H + 7) / 8) * ((W + 15) / 16) * (Cout / (Cout % 128 == 0 ? 128 : 64));
+  return tiles >= 256;
+}
+
 hipError_t conv3d(hipStream_t s, const ConvArgs& a) {
   if (a.Cin < 8 || (a.Cin & 7) || a.Cout < 1 || a.T < 1 || a.H < 1 || a.W < 1) return hipErrorInvalidValue;
+  if (a.up && (a.ycf || !conv3d_upsample_ok(a.T, a.H, a.W, a.Cin, a.Cout))) return hipErrorInvalidValue;
   if (a.ycf ? false : (!a.y || (a.Cout & 3))) return hipErrorInvalidValue;
   const int64_t M = (int64_t)a.T * a.H * a.W;
   if (M * a.Cout >= (1ll << 31) || M * a.Cin >= (1ll << 31) || 27ll * a.Cin * a.Cout >= (1ll << 31))

@@ -142,8 +142,14 @@ struct ConvArgs {
   float* ycf;
   int T, H, W, Cin, Cout;
   bool h16;             // x, cache, w and y hold fp16 words (b stays bf16)
+  // x and cache hold the input at half the height and width ([.][H/2][W/2]
+  // [Cin]); the convolution reads it upsampled 2x2 (nearest).  Only where
+  // conv3d_upsample_ok() holds.
+  bool up = false;
 };
 hipError_t conv3d(hipStream_t s, const ConvArgs& a);
+// whether conv3d can read its input upsampled (the halo kernel's shapes)
+bool conv3d_upsample_ok(int T, int H, int W, int Cin, int Cout);
 // In place on [P][C] (bf16, or fp16 with h16): RMS norm over C (gain g bf16
 // [C]) then SiLU.
 hipError_t norm_silu(hipStream_t s, void* x, const void* g, int64_t P, int C, float eps, bool h16 = false);

@@ -354,6 +354,28 @@ sd_status sd_k_conv3d(const void* x, const void* cache, const void* w, const voi
   return sdk::conv3d((hipStream_t)stream, a) == hipSuccess ? SD_OK : SD_ERR_HIP;
 }
 
+sd_status sd_k_conv3d_up2(const void* x, const void* cache, const void* w, const void* bias, void* y, int32_t T,
+                          int32_t H, int32_t W, int32_t Cin, int32_t Cout, void* stream) {
+  if (!x || !w || !y || T < 1 || H < 1 || W < 1 || Cin < 8 || Cout < 1) return SD_ERR_ARG;
+  if ((int64_t)T * H * W * (Cin > Cout ? Cin : Cout) >= (1ll << 31)) return SD_ERR_SHAPE;
+  if (!sdk::conv3d_upsample_ok(T, H, W, Cin, Cout)) return SD_ERR_SHAPE;
+  sdk::ConvArgs a;
+  a.h16 = false;
+  a.up = true;
+  a.x = (const bf16*)x;
+  a.cache = (const bf16*)cache;
+  a.w = (const bf16*)w;
+  a.b = (const bf16*)bias;
+  a.y = (bf16*)y;
+  a.ycf = nullptr;
+  a.T = T;
+  a.H = H;
+  a.W = W;
+  a.Cin = Cin;
+  a.Cout = Cout;
+  return sdk::conv3d((hipStream_t)stream, a) == hipSuccess ? SD_OK : SD_ERR_HIP;
+}
+
 sd_status sd_k_ssf_sums(int32_t kind, const void* a, const void* b, int64_t n, int64_t* out_dev, void* stream) {
   if ((kind != SD_SSF_U8 && kind != SD_SSF_LATENT) || !a || !b || !out_dev || n < 0) return SD_ERR_ARG;
   return sdk::ssf_sums((hipStream_t)stream, kind, a, b, n, (long long*)out_dev) == hipSuccess ? SD_OK : SD_ERR_HIP;

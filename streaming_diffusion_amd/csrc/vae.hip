@@ -24,7 +24,8 @@ struct VaeLayer {
   int mode;          // resampling of the layer's input: -1 none, else sdk::resample's mode
   bool norm;
   int T, H, W;       // shape of the convolution's input (after resampling)
-  void* in[2];       // fp16 [T][H][W][cin]: this chunk's input / the previous chunk's
+  bool up;           // input kept at H/2 x W/2, upsampled 2x2 by the convolution's reads
+  void* in[2];       // fp16 [T][H][W][cin] (H/2, W/2 with up): this chunk's input / the previous chunk's
   int par;           // which of in[] the next chunk uses
   void* w16;         // fp16 copy of the weights [cout][27 cin]
 };
@@ -47,16 +48,20 @@ int validate(const sd_vae_config& c, std::string* err) {
 void layers_of(const sd_vae_config& c, VaeLayer* L) {
   const int T = c.latent_t, h = c.latent_h, w = c.latent_w, z = c.latent_c;
   const int Tp = 2 * T, H = 8 * h, W = 8 * w;
-  L[SD_VAE_E0] = {8, c.c1, -1, true, Tp, H, W, {nullptr, nullptr}, 0, nullptr};
-  L[SD_VAE_E1] = {c.c1, c.c2, 0, true, Tp, H / 2, W / 2, {nullptr, nullptr}, 0, nullptr};
-  L[SD_VAE_E2] = {c.c2, c.c3, 0, true, Tp, H / 4, W / 4, {nullptr, nullptr}, 0, nullptr};
-  L[SD_VAE_E3] = {c.c3, c.c3, 1, true, T, h, w, {nullptr, nullptr}, 0, nullptr};
-  L[SD_VAE_E_OUT] = {c.c3, z, -1, false, T, h, w, {nullptr, nullptr}, 0, nullptr};
-  L[SD_VAE_D0] = {z, c.c3, -1, true, T, h, w, {nullptr, nullptr}, 0, nullptr};
-  L[SD_VAE_D1] = {c.c3, c.c3, 3, true, Tp, H / 4, W / 4, {nullptr, nullptr}, 0, nullptr};
-  L[SD_VAE_D2] = {c.c3, c.c2, 2, true, Tp, H / 2, W / 2, {nullptr, nullptr}, 0, nullptr};
-  L[SD_VAE_D3] = {c.c2, c.c1, 2, true, Tp, H, W, {nullptr, nullptr}, 0, nullptr};
-  L[SD_VAE_D_OUT] = {c.c1, 3, -1, false, Tp, H, W, {nullptr, nullptr}, 0, nullptr};
+  L[SD_VAE_E0] = {8, c.c1, -1, true, Tp, H, W, false, {nullptr, nullptr}, 0, nullptr};
+  L[SD_VAE_E1] = {c.c1, c.c2, 0, true, Tp, H / 2, W / 2, false, {nullptr, nullptr}, 0, nullptr};
+  L[SD_VAE_E2] = {c.c2, c.c3, 0, true, Tp, H / 4, W / 4, false, {nullptr, nullptr}, 0, nullptr};
+  L[SD_VAE_E3] = {c.c3, c.c3, 1, true, T, h, w, false, {nullptr, nullptr}, 0, nullptr};
+  L[SD_VAE_E_OUT] = {c.c3, z, -1, false, T, h, w, false, {nullptr, nullptr}, 0, nullptr};
+  L[SD_VAE_D0] = {z, c.c3, -1, true, T, h, w, false, {nullptr, nullptr}, 0, nullptr};
+  L[SD_VAE_D1] = {c.c3, c.c3, 3, true, Tp, H / 4, W / 4, false, {nullptr, nullptr}, 0, nullptr};
+  L[SD_VAE_D2] = {c.c3, c.c2, 2, true, Tp, H / 2, W / 2, false, {nullptr, nullptr}, 0, nullptr};
+  L[SD_VAE_D3] = {c.c2, c.c1, 2, true, Tp, H, W, false, {nullptr, nullptr}, 0, nullptr};
+  L[SD_VAE_D_OUT] = {c.c1, 3, -1, false, Tp, H, W, false, {nullptr, nullptr}, 0, nullptr};
+  // 2x2 nearest upsampling folded into the next convolution's input reads
+  // where its kernel can do it: the layer stores its input at half size
+  for (int i = 0; i < SD_VAE_LAYERS; ++i)
+    L[i].up = L[i].mode == 2 && sdk::conv3d_upsample_ok(L[i].T, L[i].H, L[i].W, L[i].cin, L[i].cout);
 }
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -66,11 +71,12 @@ size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 size_t act_bytes(const VaeLayer* L) {
   size_t m = 0;
   for (int i = 0; i + 1 < SD_VAE_LAYERS; ++i)
-    if (L[i + 1].mode >= 0) m = std::max(m, (size_t)L[i].T * L[i].H * L[i].W * L[i].cout);
+    if (L[i + 1].mode >= 0 && !L[i + 1].up) m = std::max(m, (size_t)L[i].T * L[i].H * L[i].W * L[i].cout);
   return align256(m * 2);
 }
 
-size_t input_bytes(const VaeLayer& l) { return align256((size_t)l.T * l.H * l.W * l.cin * 2); }
+size_t input_frame(const VaeLayer& l) { return (size_t)(l.up ? l.H / 2 : l.H) * (l.up ? l.W / 2 : l.W) * l.cin; }
+size_t input_bytes(const VaeLayer& l) { return align256((size_t)l.T * input_frame(l) * 2); }
 size_t weight_bytes(const VaeLayer& l) { return align256((size_t)27 * l.cin * l.cout * 2); }
 
 }  // namespace
@@ -108,9 +114,11 @@ sd_status run_layers(sd_vae* v, int first, int last, float* out) {
     VaeLayer* nx = li < last ? &v->L[li + 1] : nullptr;
     // this layer's output: the next layer's input buffer of this chunk, or
     // the staging buffer when the next layer resamples it first
-    void* dst = nx ? (nx->mode >= 0 ? v->act : nx->in[nx->par]) : nullptr;
-    const size_t frame = (size_t)l.H * l.W * l.cin;
+    const bool stage = nx && nx->mode >= 0 && !nx->up;
+    void* dst = nx ? (stage ? v->act : nx->in[nx->par]) : nullptr;
+    const size_t frame = input_frame(l);
     sdk::ConvArgs a;
+    a.up = l.up;
     a.x = (const bf16*)l.in[l.par];
     a.cache = (const bf16*)((const char*)l.in[l.par ^ 1] + (size_t)(l.T - 2) * frame * 2);
     a.w = (const bf16*)l.w16;
@@ -129,8 +137,7 @@ sd_status run_layers(sd_vae* v, int first, int last, float* out) {
     if (!nx) break;
     if (l.norm)
       VHIP(sdk::norm_silu(v->st, dst, v->w.g[li], (int64_t)l.T * l.H * l.W, l.cout, 1e-6f, true));
-    if (nx->mode >= 0)
-      VHIP(sdk::resample(v->st, v->act, nx->in[nx->par], l.T, l.H, l.W, l.cout, nx->mode, true));
+    if (stage) VHIP(sdk::resample(v->st, v->act, nx->in[nx->par], l.T, l.H, l.W, l.cout, nx->mode, true));
   }
   return SD_OK;
 }

@@ -229,6 +229,12 @@ def test_vae_and_conv_argument_errors(lib):
     assert lib.sd_k_conv3d(8, None, 8, None, 8, None, 1, 4, 4, 12, 8, None) == L.SD_ERR_SHAPE       # Cin % 8
     assert lib.sd_k_conv3d(8, None, 8, None, 8, None, 1, 4, 4, 8, 6, None) == L.SD_ERR_SHAPE        # Cout % 4
     assert lib.sd_k_conv3d(8, None, 8, None, None, 8, 1, 4, 4, 8, 17, None) == L.SD_ERR_SHAPE       # narrow > 16
+    # the upsampled-input form takes only the halo kernel's shapes
+    assert lib.sd_k_conv3d_up2(8, None, 8, None, 8, 3, 128, 256, 32, 64, None) == L.SD_ERR_SHAPE    # T != 4
+    assert lib.sd_k_conv3d_up2(8, None, 8, None, 8, 4, 127, 256, 32, 64, None) == L.SD_ERR_SHAPE    # odd H
+    assert lib.sd_k_conv3d_up2(8, None, 8, None, 8, 4, 128, 256, 24, 64, None) == L.SD_ERR_SHAPE    # Cin % 32
+    assert lib.sd_k_conv3d_up2(8, None, 8, None, 8, 4, 16, 32, 32, 64, None) == L.SD_ERR_SHAPE      # too few tiles
+    assert lib.sd_k_conv3d_up2(None, None, 8, None, 8, 4, 128, 256, 32, 64, None) == L.SD_ERR_ARG
     assert lib.sd_k_conv3d(None, None, 8, None, 8, None, 1, 4, 4, 8, 8, None) == L.SD_ERR_ARG
 
 

@@ -156,6 +156,28 @@ def test_conv3d_wide_paths_bit_exact_sampled(lib, T, H, W, Ci, Co):
     assert np.array_equal(got, bf16_of(ref))
 
 
+@pytest.mark.parametrize("T,H,W,Ci,Co", [(4, 128, 256, 32, 64), (4, 124, 200, 64, 192)])
+def test_conv3d_upsampled_input_bit_exact_sampled(lib, T, H, W, Ci, Co):
+    """sd_k_conv3d_up2: the halo kernel reading a half-size input (and cache)
+    upsampled 2x2 (nearest) on the fly, as the decoder's upsampling layers do;
+    against the definition on the explicitly upsampled operands (ragged
+    124 x 200 frame, 192 channels included)."""
+    print(f"conv3d up2 T={T} H={H} W={W} Cin={Ci} Cout={Co}", flush=True)
+    x, cache, w, b = int_operands(T * 13 + Co, T, H // 2, W // 2, Ci, Co)
+    dx, dc, dw, db = (to_dev(a, torch.bfloat16) for a in (x, cache, w, b))
+    y = torch.empty((T, H, W, Co), dtype=torch.bfloat16, device=device())
+    call(lib.sd_k_conv3d_up2(dx.data_ptr(), dc.data_ptr(), dw.data_ptr(), db.data_ptr(), y.data_ptr(),
+                             T, H, W, Ci, Co, stream_ptr()))
+    torch.cuda.synchronize()
+    up = lambda a: np.repeat(np.repeat(a, 2, axis=1), 2, axis=2)
+    xu, cu = up(x), up(cache)
+    yc = y.float().cpu().numpy().astype(np.float64)
+    pts = sampled_positions(np.random.default_rng(9), T, H, W, n=64)
+    got = np.stack([yc[t, i, j] for t, i, j in pts])
+    ref = np.stack([conv_at(xu, cu, w, b, t, i, j) for t, i, j in pts])
+    assert np.array_equal(got, bf16_of(ref))
+
+
 @pytest.mark.parametrize("layer", ["d3", "d_out"])
 def test_conv3d_full_video_shape_sampled(lib, layer):
     """The video decoder's two full-resolution layers (4 x 480 x 832): d3
