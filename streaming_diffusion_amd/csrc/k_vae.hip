@@ -876,6 +876,86 @@ hipError_t norm_silu(hipStream_t s, void* x, const void* g, int64_t P, int C, fl
   return hipGetLastError();
 }
 
+// RMS norm + SiLU of every input position followed by the 2 x 2 (x 2 in
+// time) average pooling of the normalised values, in one pass: the encoder's
+// layer outputs are read once and only the pooled quarter (eighth) is
+// written.  C / 8 lanes per pooled position, 8 channels each; for each of
+// its 4 (8) input positions the group reduces the sum of squares with
+// butterfly shuffles, normalises its 8 channels and adds them in.
+template <int C, bool H16, bool TEMPORAL>
+__global__ __launch_bounds__(256) void norm_silu_pool_kernel(const bf16* __restrict__ x, const bf16* __restrict__ g,
+                                                             bf16* __restrict__ y, int T, int H, int W, float eps) {
+  constexpr int LP = C / 8;
+  const int To = TEMPORAL ? T / 2 : T, Ho = H / 2, Wo = W / 2;
+  const int64_t P = (int64_t)To * Ho * Wo;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t po = gid / LP;
+  const int c0 = (int)(gid % LP) * 8;
+  const bool ok = po < P;
+  const int64_t pc = ok ? po : 0;
+  const int xo = (int)(pc % Wo), yo = (int)((pc / Wo) % Ho), to = (int)(pc / ((int64_t)Wo * Ho));
+  const bf16x8 gv = *(const bf16x8*)(g + c0);
+  float acc[8] = {};
+  constexpr int NT = TEMPORAL ? 2 : 1;
+#pragma unroll
+  for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+    for (int dy = 0; dy < 2; ++dy)
+#pragma unroll
+      for (int dx = 0; dx < 2; ++dx) {
+        const int t = TEMPORAL ? 2 * to + dt : to;
+        const bf16x8 v = *(const bf16x8*)(x + (((int64_t)t * H + 2 * yo + dy) * W + 2 * xo + dx) * C + c0);
+        float f[8], ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          f[e] = from16<H16>(v[e]);
+          ss = fmaf(f[e], f[e], ss);
+        }
+#pragma unroll
+        for (int off = LP / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, LP);
+        const float r = 1.0f / sqrtf(ss / (float)C + eps);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float n = f[e] * r * (float)gv[e];
+          acc[e] += n * __builtin_amdgcn_rcpf(1.0f + __expf(-n));
+        }
+      }
+  if (!ok) return;
+  constexpr float sc = TEMPORAL ? 0.125f : 0.25f;
+  bf16x8 o;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = to16<H16>(acc[e] * sc);
+  *(bf16x8*)(y + po * C + c0) = o;
+}
+
+hipError_t norm_silu_pool(hipStream_t s, const void* x, const void* g, void* y, int T, int H, int W, int C,
+                          bool temporal, float eps, bool h16) {
+  if ((H & 1) || (W & 1) || (temporal && (T & 1)) || T < 1 || H < 2 || W < 2) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)(temporal ? T / 2 : T) * (H / 2) * (W / 2) * (C / 8);
+  const unsigned grid = (unsigned)((n + 255) / 256);
+#define SD_NSP(CC)                                                                                          \
+  case CC:                                                                                                  \
+    if (h16 && temporal)                                                                                    \
+      norm_silu_pool_kernel<CC, true, true><<<grid, 256, 0, s>>>((const bf16*)x, (const bf16*)g, (bf16*)y, T, H, W, eps); \
+    else if (h16)                                                                                           \
+      norm_silu_pool_kernel<CC, true, false><<<grid, 256, 0, s>>>((const bf16*)x, (const bf16*)g, (bf16*)y, T, H, W, eps); \
+    else if (temporal)                                                                                      \
+      norm_silu_pool_kernel<CC, false, true><<<grid, 256, 0, s>>>((const bf16*)x, (const bf16*)g, (bf16*)y, T, H, W, eps); \
+    else                                                                                                    \
+      norm_silu_pool_kernel<CC, false, false><<<grid, 256, 0, s>>>((const bf16*)x, (const bf16*)g, (bf16*)y, T, H, W, eps); \
+    break;
+  switch (C) {
+    SD_NSP(16)
+    SD_NSP(32)
+    SD_NSP(64)
+    SD_NSP(128)
+    SD_NSP(256)
+    default: return hipErrorInvalidValue;
+  }
+#undef SD_NSP
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // 2 x 2 (x 2 in time) average pooling and nearest 2x upsampling, one thread
 // per 8-channel chunk of an output position.

@@ -153,6 +153,10 @@ bool conv3d_upsample_ok(int T, int H, int W, int Cin, int Cout);
 // In place on [P][C] (bf16, or fp16 with h16): RMS norm over C (gain g bf16
 // [C]) then SiLU.
 hipError_t norm_silu(hipStream_t s, void* x, const void* g, int64_t P, int C, float eps, bool h16 = false);
+// RMS norm + SiLU as above, then 2 x 2 (x 2 in time with temporal) average
+// pooling: x [T][H][W][C] -> y [T'][H/2][W/2][C] (T' = T / 2 with temporal).
+hipError_t norm_silu_pool(hipStream_t s, const void* x, const void* g, void* y, int T, int H, int W, int C,
+                          bool temporal, float eps, bool h16);
 // bf16 channels-last resampling: mode 0 pool 2x2, 1 pool 2x2x2, 2 nearest
 // upsample 2x2, 3 nearest upsample 2x2x2; (T, H, W) is the input's shape.
 hipError_t resample(hipStream_t s, const void* x, void* y, int T, int H, int W, int C, int mode, bool h16 = false);

@@ -135,6 +135,12 @@ sd_status run_layers(sd_vae* v, int first, int last, float* out) {
     // the input just read is the next chunk's cache
     l.par ^= 1;
     if (!nx) break;
+    if (l.norm && stage && nx->mode <= 1) {
+      // the encoder's norm and pooling in one pass: only the pooled values are written
+      VHIP(sdk::norm_silu_pool(v->st, v->act, v->w.g[li], nx->in[nx->par], l.T, l.H, l.W, l.cout, nx->mode == 1,
+                               1e-6f, true));
+      continue;
+    }
     if (l.norm)
       VHIP(sdk::norm_silu(v->st, dst, v->w.g[li], (int64_t)l.T * l.H * l.W, l.cout, 1e-6f, true));
     if (stage) VHIP(sdk::resample(v->st, v->act, nx->in[nx->par], l.T, l.H, l.W, l.cout, nx->mode, true));
