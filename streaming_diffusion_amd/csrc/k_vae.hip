@@ -735,6 +735,121 @@ __global__ __launch_bounds__(64 * NW, NBUF == 1 ? 2 : 1) void conv3d_halo16_kern
   }
 }
 
+// The halo scheme for the first encoder layer, whose input has 8 channels
+// (RGB and zero padding): the halo rows are 16 bytes (all channels of a
+// position) and one 32 x 32 x 16 product covers two taps -- lanes 0-31
+// supply tap 2s, lanes 32-63 tap 2s + 1 (the 28th tap is zero weights) -- so
+// a tile needs 14 products per 32 x 32 block and its whole weight slice (14
+// fragments) stays in registers.  One halo, one DMA round: 4 x 8 x 16
+// positions x BN channels per workgroup of 8 waves (4 along positions x 2
+// along channels).
+template <int BN, bool H16>
+__global__ __launch_bounds__(512) void conv3d_halo8_kernel(ConvArgs a) {
+  constexpr int TT = 4, TY = 8, TX = 16;
+  constexpr int HY = TY + 2, HX = TX + 2, HT = TT + 2;
+  constexpr int HROWS = HT * HY * HX;                   // 1080 rows of 16 bytes
+  constexpr int HINS = (HROWS + 63) / 64;               // DMA instructions (64 rows each)
+  constexpr int HQ = (HINS + 7) / 8;
+  constexpr int WMW = 4, WNW = 2;
+  constexpr int TMP = TT * TY * TX / WMW, TNC = BN / WNW;
+  constexpr int MB = TMP / 32, NB = TNC / 32, KS = 14;
+  static_assert(MB >= 1 && NB >= 1, "wave tile");
+  __shared__ __attribute__((aligned(1024))) bf16 halo[HINS * 64 * 8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WMW, wn = wave / WMW;
+  const int HW = a.H * a.W;
+  const int tiles_x = (a.W + TX - 1) / TX, tiles_n = a.Cout / BN;
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int tn = lid % tiles_n, txy = lid / tiles_n;
+  const int y0 = (txy / tiles_x) * TY, x0 = (txy % tiles_x) * TX, n0 = tn * BN;
+  const bf16* const zero = conv_zero_row;
+#pragma unroll
+  for (int q = 0; q < HQ; ++q) {
+    const int ins = wave * HQ + q;
+    const int row = ins * 64 + lane;
+    if (ins < HINS) {
+      const bf16* src = zero;
+      if (row < HROWS) {
+        const int ft = row / (HY * HX), hy = (row / HX) % HY, hx = row % HX;
+        const int ti = ft - 2, y = y0 + hy - 1, x = x0 + hx - 1;
+        if ((unsigned)y < (unsigned)a.H && (unsigned)x < (unsigned)a.W) {
+          if (ti >= 0)
+            src = a.x + ((int64_t)ti * HW + (int64_t)y * a.W + x) * 8;
+          else if (a.cache)
+            src = a.cache + ((int64_t)(ti + 2) * HW + (int64_t)y * a.W + x) * 8;
+        }
+      }
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(halo + ins * 64 * 8), 16, 0, 0);
+    }
+  }
+  // weights: lane -> output channel (l % 32) of each block, tap 2 s + l / 32
+  const int lr = lane & 31, lh = lane >> 5;
+  bf16x8 wf[KS][NB];
+#pragma unroll
+  for (int s2 = 0; s2 < KS; ++s2) {
+    const int tap = 2 * s2 + lh;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      bf16x8 v = {};
+      if (tap < 27) v = *(const bf16x8*)(a.w + (int64_t)(n0 + wn * TNC + i * 32 + lr) * 216 + tap * 8);
+      wf[s2][i] = v;
+    }
+  }
+  int hbase[MB];
+#pragma unroll
+  for (int j = 0; j < MB; ++j) {
+    const int pw = wm * TMP + j * 32 + lr;
+    const int tf = pw / (TY * TX), r = (pw / TX) % TY, c = pw % TX;
+    hbase[j] = (tf * HY + r) * HX + c;
+  }
+  f32x16 acc[NB][MB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int j = 0; j < MB; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+  __builtin_amdgcn_s_waitcnt(0x0070);                   // vmcnt(0) lgkmcnt(0): halo and weights landed
+  __builtin_amdgcn_s_barrier();
+#pragma unroll
+  for (int s2 = 0; s2 < KS; ++s2) {
+    const int tap = min(2 * s2 + lh, 26);               // tap 27 reads a real row against zero weights
+    const int dt = tap / 9, dy = (tap / 3) % 3, dx = tap % 3;
+    const int toff = (dt * HY + dy) * HX + dx;
+    bf16x8 fp[MB];
+#pragma unroll
+    for (int j = 0; j < MB; ++j) fp[j] = *(const bf16x8*)(halo + (hbase[j] + toff) * 8);
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int j = 0; j < MB; ++j) {
+        if constexpr (H16)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, wf[s2][i]),
+                                                             __builtin_bit_cast(f16x8, fp[j]), acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[s2][i], fp[j], acc[i][j], 0, 0, 0);
+      }
+  }
+#pragma unroll
+  for (int j = 0; j < MB; ++j) {
+    const int pw = wm * TMP + j * 32 + lr;
+    const int tf = pw / (TY * TX), y = y0 + (pw / TX) % TY, x = x0 + pw % TX;
+    if (y >= a.H || x >= a.W) continue;
+    const int64_t p = (int64_t)tf * HW + (int64_t)y * a.W + x;
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * TNC + i * 32 + 8 * g + 4 * lh;
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = to16<H16>(acc[i][j][4 * g + e] + (a.b ? (float)a.b[n + e] : 0.f));
+        *(bf16x4*)(a.y + p * a.Cout + n) = o;
+      }
+  }
+}
+
 bool conv3d_upsample_ok(int T, int H, int W, int Cin, int Cout) {
   if (T != 4 || Cin % 32 || Cout % 64 || (H & 1) || (W & 1)) return false;
   const int64_t tiles = (int64_t)((H + 7) / 8) * ((W + 15) / 16) * (Cout / (Cout % 128 == 0 ? 128 : 64));
@@ -771,6 +886,15 @@ hipError_t conv3d(hipStream_t s, const ConvArgs& a) {
       }
       return hipGetLastError();
     }
+  }
+  // 4-frame layers with 8 input channels (the first encoder layer): one
+  // halo of 16-byte rows, two taps per product
+  if (a.T == 4 && a.Cin == 8 && !a.ycf && a.Cout % 64 == 0 &&
+      (int64_t)((a.H + 7) / 8) * ((a.W + 15) / 16) * (a.Cout / 64) >= 256) {
+    const unsigned g = (unsigned)(((a.H + 7) / 8) * ((a.W + 15) / 16) * (a.Cout / 64));
+    if (a.h16) conv3d_halo8_kernel<64, true><<<g, 512, 0, s>>>(a);
+    else conv3d_halo8_kernel<64, false><<<g, 512, 0, s>>>(a);
+    return hipGetLastError();
   }
   // layers with at most 16 output channels (latent and pixel projections):
   // the narrow halo kernel, 4 x 8 x 16 tiles for 4 frames, 2 x 2 x 16 for 2

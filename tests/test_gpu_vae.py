@@ -131,7 +131,7 @@ def conv_at(x, cache, w, b, t, i, j):
 
 @pytest.mark.parametrize("T,H,W,Ci,Co", [(4, 128, 160, 64, 256), (4, 128, 256, 128, 128), (4, 256, 256, 128, 64),
                                          (4, 124, 200, 96, 192), (2, 256, 256, 64, 128), (3, 256, 352, 64, 64),
-                                         (2, 60, 104, 256, 256)])
+                                         (2, 60, 104, 256, 256), (4, 128, 256, 8, 64), (4, 124, 250, 8, 128)])
 def test_conv3d_wide_paths_bit_exact_sampled(lib, T, H, W, Ci, Co):
     """The wide-layer kernels: 4-frame layers take the halo kernel (4 x 8 x 16
     output tiles, the 6 x 10 x 18 input halo per 32-channel chunk in LDS, all
@@ -139,7 +139,8 @@ def test_conv3d_wide_paths_bit_exact_sampled(lib, T, H, W, Ci, Co):
     included), other layers with at least 512 tiles the DMA-fed implicit GEMM
     (256 x 128 and 512 x 64 tiles, 64-deep k-tiles inside one tap), the
     encoder's latent-resolution layer (2 x 60 x 104, 256 channels, too few
-    tiles for both) its 128 x 64 tiles.  Integer
+    tiles for both) its 128 x 64 tiles, 4-frame layers with 8 input
+    channels the 16-byte-row halo kernel (two taps per product).  Integer
     operands: outputs at borders, cache frames and random positions equal the
     exact sum rounded once to bf16."""
     print(f"conv3d DMA path T={T} H={H} W={W} Cin={Ci} Cout={Co}", flush=True)
