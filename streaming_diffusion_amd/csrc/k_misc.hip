@@ -236,6 +236,66 @@ __global__ __launch_bounds__(256) void ln_mod_kernel(const float* __restrict__ x
   }
 }
 
+// The same LayerNorm + modulation for few rows (the chunks below the batch
+// knee): one workgroup of d / 4 threads per row, one float4 per thread, so
+// the row, its shift / scale vectors and the block table are all requested
+// at once and the reductions span the workgroup (wave sums, then the waves
+// through LDS).  With 128 rows the one-wave-per-row form leaves most of the
+// chip idle and runs its loads, its two reductions and the modulation reads
+// one after another.
+template <typename T, bool SPLIT = false>
+__global__ __launch_bounds__(512) void ln_mod_row_kernel(const float* __restrict__ x, T* __restrict__ out, int d,
+                                                         int L, const float* __restrict__ mod,
+                                                         const T* __restrict__ blk, int shift_off, int scale_off,
+                                                         int six_d, float eps) {
+  __shared__ float red[2][8];
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  const int j = tid;                                     // float4 index in the row (blockDim = d / 4)
+  const float4 v = ((const float4*)(x + (int64_t)row * d))[j];
+  const float* mr = mod ? mod + (int64_t)(row / L) * six_d : nullptr;
+  float sh[4] = {0.f, 0.f, 0.f, 0.f}, sc[4] = {0.f, 0.f, 0.f, 0.f};
+  if (mr) {
+    load4(mr + shift_off + 4 * j, sh);
+    load4(mr + scale_off + 4 * j, sc);
+    if (blk) {
+      float bs[4], bc[4];
+      load4(blk + shift_off + 4 * j, bs);
+      load4(blk + scale_off + 4 * j, bc);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        sh[q] += bs[q];
+        sc[q] += bc[q];
+      }
+    }
+  }
+  const float s1 = wave_sum((v.x + v.y) + (v.z + v.w));
+  if (lane == 0) red[0][wave] = s1;
+  __syncthreads();
+  float tot = 0.f;
+  for (int w = 0; w < nw; ++w) tot += red[0][w];
+  const float mu = tot / (float)d;
+  const float a0 = v.x - mu, a1 = v.y - mu, a2 = v.z - mu, a3 = v.w - mu;
+  const float s2 = wave_sum((a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3));
+  if (lane == 0) red[1][wave] = s2;
+  __syncthreads();
+  float sq = 0.f;
+  for (int w = 0; w < nw; ++w) sq += red[1][w];
+  const float rstd = 1.0f / sqrtf(sq / (float)d + eps);
+  float o[4] = {a0 * rstd, a1 * rstd, a2 * rstd, a3 * rstd};
+  if (mr) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = o[q] * (1.0f + sc[q]) + sh[q];
+  }
+  T* orow = out + (int64_t)row * (SPLIT ? 2 * d : d);
+  store4<T>(orow + 4 * j, o);
+  if constexpr (SPLIT) {
+    float lo[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lo[q] = o[q] - (float)(T)o[q];
+    store4<T>(orow + d + 4 * j, lo);
+  }
+}
+
 void rope_table_fill(float2* out, int npos, int width, double base) {
   const int np = width / 2;
   for (int p = 0; p < npos; ++p) {
@@ -253,6 +313,22 @@ hipError_t ln_mod(hipStream_t s, bool bf, const float* x, void* out, int M, int 
   if ((d & 3) || d > 4 * 64 * LN_MAXV || (shift_off & 3) || (scale_off & 3) || (six_d & 3)) return hipErrorInvalidValue;
   if (form != LN_PLAIN && !bf) return hipErrorInvalidValue;
   if (form == LN_F16 && mod) return hipErrorInvalidValue;
+  // few rows: a workgroup per row (d / 4 threads, whole waves, at most 512)
+  if (M <= 1024 && d % 256 == 0 && d <= 2048) {
+    const unsigned g = (unsigned)M, nt = (unsigned)(d / 4);
+    if (form == LN_F16)
+      ln_mod_row_kernel<f16><<<g, nt, 0, s>>>(x, (f16*)out, d, L, nullptr, nullptr, 0, 0, six_d, eps);
+    else if (form == LN_SPLIT)
+      ln_mod_row_kernel<bf16, true><<<g, nt, 0, s>>>(x, (bf16*)out, d, L, mod, (const bf16*)blk, shift_off,
+                                                      scale_off, six_d, eps);
+    else if (bf)
+      ln_mod_row_kernel<bf16><<<g, nt, 0, s>>>(x, (bf16*)out, d, L, mod, (const bf16*)blk, shift_off, scale_off,
+                                               six_d, eps);
+    else
+      ln_mod_row_kernel<float><<<g, nt, 0, s>>>(x, (float*)out, d, L, mod, (const float*)blk, shift_off,
+                                                scale_off, six_d, eps);
+    return hipGetLastError();
+  }
   const unsigned g = (unsigned)((M + 3) / 4);
 #define SD_LN_LAUNCH(NV)                                                                                           \
   do {                                                                                                             \

@@ -197,12 +197,14 @@ def test_head_epilogue_unpatchifies_exactly(lib, rows, t, hp, wp, ch):
 
 
 # ------------------------------------------------------------------ LayerNorm + adaLN modulation
-@pytest.mark.parametrize("M,d,Lr", [(R * L, D, L), (L, 5120, L), (2048, 1024, 1024), (37, 128, 10)])
+@pytest.mark.parametrize("M,d,Lr", [(R * L, D, L), (L, 5120, L), (2048, 1024, 1024), (37, 128, 10), (128, D, 128),
+                                    (300, 768, 100), (1024, 1024, 512)])
 def test_ln_mod_against_oracle(lib, M, d, Lr):
     """bf16 output of LN(x) * (1 + scale) + shift, scale / shift = the row's
     modulation slots plus the block table (the attention slots 0 and 1 of
     6d); register-resident rows of 4 (d <= 1024), 8 (1536) and 20 (5120)
-    vectors per lane.  Bound: the stored bf16 rounding plus 1e-4 of the RMS."""
+    vectors per lane, and up to 1024 rows of width 768 - 2048 a workgroup per
+    row.  Bound: the stored bf16 rounding plus 1e-4 of the RMS."""
     print(f"ln_mod M={M} d={d}", flush=True)
     rng = np.random.default_rng(d + M)
     rows = (M + Lr - 1) // Lr
@@ -222,8 +224,8 @@ def test_ln_mod_against_oracle(lib, M, d, Lr):
     assert excess <= 1e-4, f"excess {excess:.3e}"
 
 
-@pytest.mark.parametrize("M,d", [(R * L, D), (L, 5120)])
-def test_ln_split_and_fp16_forms(lib, M, d):
+@pytest.mark.parametrize("M,d,Lr", [(R * L, D, L), (L, 5120, L), (128, D, 128), (256, 1024, 128)])
+def test_ln_split_and_fp16_forms(lib, M, d, Lr):
     """The head's input as hi + lo bf16 pairs (SD_LN_SPLIT, with the final
     layer's (shift, scale) slots of a 2d vector) reconstructs the modulated
     LayerNorm to fp32 accuracy; the cross-attention's fp16 input (SD_LN_F16,
@@ -231,17 +233,17 @@ def test_ln_split_and_fp16_forms(lib, M, d):
     print(f"ln split / f16 M={M} d={d}", flush=True)
     rng = np.random.default_rng(d + 3 * M)
     x = rng.standard_normal((M, d)).astype(np.float32) * 2 - 0.3
-    mod = (0.3 * rng.standard_normal((M // L, 2 * d))).astype(np.float32)
+    mod = (0.3 * rng.standard_normal((M // Lr, 2 * d))).astype(np.float32)
     xd, md = to_dev(x, torch.float32), to_dev(mod, torch.float32)
     ln = dit.layer_norm(x.astype(np.float64))
     split = torch.empty((M, 2 * d), dtype=torch.bfloat16, device=device())
-    call(lib.sd_k_ln_mod(sdlib.SD_DTYPE_BF16, xd.data_ptr(), split.data_ptr(), M, d, L, md.data_ptr(), None, 0, d,
+    call(lib.sd_k_ln_mod(sdlib.SD_DTYPE_BF16, xd.data_ptr(), split.data_ptr(), M, d, Lr, md.data_ptr(), None, 0, d,
                          2 * d, sdlib.SD_LN_SPLIT, stream_ptr()))
     half = torch.empty((M, d), dtype=torch.float16, device=device())
-    call(lib.sd_k_ln_mod(sdlib.SD_DTYPE_BF16, xd.data_ptr(), half.data_ptr(), M, d, L, None, None, 0, 0, 0,
+    call(lib.sd_k_ln_mod(sdlib.SD_DTYPE_BF16, xd.data_ptr(), half.data_ptr(), M, d, Lr, None, None, 0, 0, 0,
                          sdlib.SD_LN_F16, stream_ptr()))
     torch.cuda.synchronize()
-    m = mod.astype(np.float64)[np.arange(M) // L]
+    m = mod.astype(np.float64)[np.arange(M) // Lr]
     ref = dit.modulate(ln, m[:, :d], m[:, d:])
     sp = split.float().cpu().numpy()
     hi, lo = sp[:, :d].astype(np.float64), sp[:, d:].astype(np.float64)
