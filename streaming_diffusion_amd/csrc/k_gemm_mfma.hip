@@ -508,14 +508,18 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restric
   constexpr int LC = BN + 4;
   static_assert(TM0 % 32 == 0 && TM0 * 2 >= BM && FM1 >= 1, "wave rows");
   static_assert(BQ >= 1 && ABLK * RPB == BM && BQ * RPB * NW == BN, "tile shape");
-  static_assert(EVEN ? AQ * NW == ABLK : NS == 2, "uneven A blocks need the full wait of two stages");
+  // uneven tiles: the first AX waves issue one A block more per k-tile
+  constexpr int AX = ABLK % NW, DQ_LO = ABLK / NW + BQ;
+  static_assert(EVEN ? AQ * NW == ABLK : NS <= 3, "uneven A blocks: at most three stages");
   static_assert(NS >= 2 && NS <= 4 && DQ * (NS - 2) < 64, "stages");
   static_assert(64 * LC * 4 <= NS * STAGE * 2, "epilogue strip must fit in the stage buffers");
   // one LDS block with the stage buffers at offset 0 (the row table and the
   // per-row RoPE bases follow them): left to the compiler, the placement of
   // the small arrays could move the stage buffers off offset 0, which costs
-  // up to half the throughput of the gated-residual kernels
+  // up to half the throughput of the gated-residual kernels.  (160 x 256
+  // tiles with three stages: 156 KB of stages + 1.2 KB of tables.)
   constexpr int SMEM_BYTES = NS * STAGE * 2;
+  static_assert(SMEM_BYTES + 64 * 16 + SD_MAX_ROWS * 4 <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(1024))) unsigned char lds[SMEM_BYTES + 64 * 16 + SD_MAX_ROWS * 4];
   bf16* const smem = (bf16*)lds;
   int4* const rowtab = (int4*)(lds + SMEM_BYTES);
@@ -638,8 +642,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restric
       else if (ahead == 1) wait_vm_barrier<DQ>();
       else wait_vm_barrier<0>();
     } else if constexpr (NS == 3) {
-      if (ahead >= 1) wait_vm_barrier<DQ>();
-      else wait_vm_barrier<0>();
+      if (ahead >= 1) {
+        // leave the next k-tile's blocks of this wave in flight
+        if (EVEN || wave < AX) wait_vm_barrier<DQ>();
+        else wait_vm_barrier<DQ_LO>();
+      } else {
+        wait_vm_barrier<0>();
+      }
     } else {
       wait_vm_barrier<0>();
     }
@@ -987,7 +996,7 @@ hipError_t gemm_mfma_mode(hipStream_t s, const bf16* A, const bf16* W, int M, in
     if (c256 == best) return launch_dma<256, 256, 8, 64, 2, true, MODE, H16>(s, A, W, M, N, K, E);
     if (c224 == best) return launch_dma<224, 256, 8, 64, 2, true, MODE, H16, 128>(s, A, W, M, N, K, E);
     if (c192 == best) return launch_dma<192, 256, 8, 64, 2, true, MODE, H16>(s, A, W, M, N, K, E);
-    return launch_dma<160, 256, 8, 64, 2, true, MODE, H16, 96>(s, A, W, M, N, K, E);
+    return launch_dma<160, 256, 8, 64, 3, true, MODE, H16, 96>(s, A, W, M, N, K, E);
   }
   const int bm = opts[best].bm, bn = opts[best].bn;
   const unsigned grid = (unsigned)(((M + bm - 1) / bm) * ((N + bn - 1) / bn));
