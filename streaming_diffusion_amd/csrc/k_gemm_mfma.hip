@@ -510,8 +510,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restric
   static_assert(BQ >= 1 && ABLK * RPB == BM && BQ * RPB * NW == BN, "tile shape");
   // uneven tiles: the first AX waves issue one A block more per k-tile
   constexpr int AX = ABLK % NW, DQ_LO = ABLK / NW + BQ;
-  static_assert(EVEN ? AQ * NW == ABLK : NS <= 3, "uneven A blocks: at most three stages");
-  static_assert(NS >= 2 && NS <= 4 && DQ * (NS - 2) < 64, "stages");
+  static_assert(NS >= 2 && NS <= 5 && DQ * (NS - 2) < 64, "stages");
   static_assert(64 * LC * 4 <= NS * STAGE * 2, "epilogue strip must fit in the stage buffers");
   // one LDS block with the stage buffers at offset 0 (the row table and the
   // per-row RoPE bases follow them): left to the compiler, the placement of
@@ -635,23 +634,26 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restric
   // one k-tile: tiles kt+1 .. kt+NS-2 may stay in flight; tile kt must have
   // landed in every wave, and every wave must be done reading tile kt-1.  WI:
   // k-tile kt+NS-1 exists and its DMA goes out during this tile's MFMAs.
-  auto step = [&](int kt, auto wi) {
-    const int ahead = min(NS - 2, KT - 1 - kt);
-    if constexpr (NS >= 4) {
-      if (ahead >= 2) wait_vm_barrier<DQ * 2>();
-      else if (ahead == 1) wait_vm_barrier<DQ>();
-      else wait_vm_barrier<0>();
-    } else if constexpr (NS == 3) {
-      if (ahead >= 1) {
-        // leave the next k-tile's blocks of this wave in flight
-        if (EVEN || wave < AX) wait_vm_barrier<DQ>();
-        else wait_vm_barrier<DQ_LO>();
-      } else {
-        wait_vm_barrier<0>();
-      }
-    } else {
-      wait_vm_barrier<0>();
+  auto wait_tiles = [](int ahead, auto dq) {
+    constexpr int D = decltype(dq)::value;
+    if constexpr (NS >= 5) {
+      if (ahead >= 3) return wait_vm_barrier<D * 3>();
     }
+    if constexpr (NS >= 4) {
+      if (ahead >= 2) return wait_vm_barrier<D * 2>();
+    }
+    if constexpr (NS >= 3) {
+      if (ahead >= 1) return wait_vm_barrier<D>();
+    }
+    wait_vm_barrier<0>();
+  };
+  auto step = [&](int kt, auto wi) {
+    // leave this wave's blocks of the next `ahead` k-tiles in flight
+    const int ahead = min(NS - 2, KT - 1 - kt);
+    // (a scalar branch: the two arms hold barriers, which must not both run
+    // under a partial exec mask)
+    if (EVEN || __builtin_amdgcn_readfirstlane(wave) < AX) wait_tiles(ahead, std::integral_constant<int, DQ>{});
+    else wait_tiles(ahead, std::integral_constant<int, DQ_LO>{});
     const int nkt = kt + NS - 1;
     if constexpr (!SPREAD && decltype(wi)::value) issue(nkt, nkt % NS, -1);
     compute(kt % NS, nkt, nkt % NS, wi);
