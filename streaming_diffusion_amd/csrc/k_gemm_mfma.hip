@@ -717,32 +717,60 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(int M, int N, Epi E) {
   }
   const int g = tid / 64, ln = tid % 64;
   const int64_t slice_st = (int64_t)tiles * 4 * 16 * 64;  // float4 granules per slice
+  // both granules of the thread, eight slices at a time: 16 loads in flight
+  // per thread (the pass is latency-bound), each sum still in slice order
+  const float4* src0 = (const float4*)E.part + (((int64_t)tile * 4 + i) * 16 + (2 * sp) * 4 + g) * 64 + ln;
+  const float4* src1 = src0 + 4 * 64;
+  float4 acc[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+  int sl = 0;
+  for (; sl + 8 <= E.ksplit; sl += 8) {
+    float4 v[2][8];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const float4* src = (const float4*)E.part + (((int64_t)tile * 4 + i) * 16 + (2 * sp + h) * 4 + g) * 64 + ln;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    int sl = 0;
-    for (; sl + 4 <= E.ksplit; sl += 4) {
-      float4 v[4];
+    for (int u = 0; u < 8; ++u) {
+      v[0][u] = src0[(sl + u) * slice_st];
+      v[1][u] = src1[(sl + u) * slice_st];
+    }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = src[(sl + u) * slice_st];
+    for (int u = 0; u < 8; ++u)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        acc.x += v[u].x;
-        acc.y += v[u].y;
-        acc.z += v[u].z;
-        acc.w += v[u].w;
+      for (int h = 0; h < 2; ++h) {
+        acc[h].x += v[h][u].x;
+        acc[h].y += v[h][u].y;
+        acc[h].z += v[h][u].z;
+        acc[h].w += v[h][u].w;
       }
-    }
-    for (; sl < E.ksplit; ++sl) {
-      const float4 v = src[sl * slice_st];
-      acc.x += v.x;
-      acc.y += v.y;
-      acc.z += v.z;
-      acc.w += v.w;
-    }
-    *(float4*)(stg + (h * 32 + ln % 32) * LC + 8 * g + 4 * (ln / 32)) = acc;
   }
+  if (sl + 4 <= E.ksplit) {
+    float4 v[2][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      v[0][u] = src0[(sl + u) * slice_st];
+      v[1][u] = src1[(sl + u) * slice_st];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        acc[h].x += v[h][u].x;
+        acc[h].y += v[h][u].y;
+        acc[h].z += v[h][u].z;
+        acc[h].w += v[h][u].w;
+      }
+    sl += 4;
+  }
+  for (; sl < E.ksplit; ++sl) {
+    const float4 v0 = src0[sl * slice_st], v1 = src1[sl * slice_st];
+    acc[0].x += v0.x;
+    acc[0].y += v0.y;
+    acc[0].z += v0.z;
+    acc[0].w += v0.w;
+    acc[1].x += v1.x;
+    acc[1].y += v1.y;
+    acc[1].z += v1.z;
+    acc[1].w += v1.w;
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) *(float4*)(stg + (h * 32 + ln % 32) * LC + 8 * g + 4 * (ln / 32)) = acc[h];
   __syncthreads();
   epi_rows<MODE>(E, rowtab, m_base, M, tid, t0s);
   __syncthreads();
