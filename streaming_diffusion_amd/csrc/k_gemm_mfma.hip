@@ -700,7 +700,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restric
 // 32 i + 8 g + 4 (l / 32) + 0..3), so both passes move whole 1 KB wave rows.
 // One workgroup takes one tile, one 64-row strip and one feature block: it
 // sums the K slices in slice order (fixed, so results do not depend on
-// scheduling) and runs the epilogue of MODE on the 64 x 32 strip.
+// scheduling) and runs the epilogue of MODE on the 64 x 32 strip -- the
+// row-major modes straight from the sums, the scatters through LDS.
 template <int MODE>
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(int M, int N, Epi E) {
   constexpr int BN = 32, NT = 256, LC = BN + 4;
@@ -716,6 +717,38 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(int M, int N, Epi E) {
     if (tid < SD_MAX_ROWS) t0s[tid] = E.t0_dev ? E.t0_dev[tid] : E.t0[tid];
   }
   const int g = tid / 64, ln = tid % 64;
+  // Row-major epilogues run straight from the sums: this thread's outputs are
+  // features n0 + 8 g + 4 (ln / 32) + 0..3 of rows m_base + 32 h + ln % 32,
+  // and every epilogue operand (bias, gates, residual) is requested before
+  // the partial sums, so the pass takes one memory round trip
+  constexpr bool DIRECT = MODE == EPI_F32 || MODE == EPI_RESID || MODE == EPI_GATE_RESID ||
+                          MODE == EPI_STORE || MODE == EPI_GELU;
+  const int nf = n0 + 8 * g + 4 * (ln / 32);
+  const int mr[2] = {m_base + ln % 32, m_base + 32 + ln % 32};
+  float bq[4] = {0.f, 0.f, 0.f, 0.f}, gq[4] = {0.f, 0.f, 0.f, 0.f};
+  float4 rin[2], gin[2];
+  if constexpr (DIRECT) {
+    if (nf < N) {
+      if (E.bias) {
+        const bf16x4 bv = *(const bf16x4*)((const bf16*)E.bias + nf);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bq[e] = (float)bv[e];
+      }
+      if constexpr (MODE == EPI_GATE_RESID) {
+        const bf16x4 gv = *(const bf16x4*)((const bf16*)E.blk + E.gate_off + nf);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gq[e] = (float)gv[e];
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (mr[h] >= M) continue;
+        if constexpr (MODE == EPI_RESID || MODE == EPI_GATE_RESID)
+          rin[h] = *(const float4*)(E.resid + (int64_t)mr[h] * N + nf);
+        if constexpr (MODE == EPI_GATE_RESID)
+          gin[h] = *(const float4*)(E.mod + (int64_t)(mr[h] / E.L) * E.six_d + E.gate_off + nf);
+      }
+    }
+  }
   const int64_t slice_st = (int64_t)tiles * 4 * 16 * 64;  // float4 granules per slice
   // both granules of the thread, eight slices at a time: 16 loads in flight
   // per thread (the pass is latency-bound), each sum still in slice order
@@ -769,12 +802,54 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(int M, int N, Epi E) {
     acc[1].z += v1.z;
     acc[1].w += v1.w;
   }
+  if constexpr (DIRECT) {
+    if (nf >= N) return;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) *(float4*)(stg + (h * 32 + ln % 32) * LC + 8 * g + 4 * (ln / 32)) = acc[h];
-  __syncthreads();
-  epi_rows<MODE>(E, rowtab, m_base, M, tid, t0s);
-  __syncthreads();
-  epi_strip<BN, NT, MODE>(E, stg, LC, m_base, n0, M, N, tid, rowtab);
+    for (int h = 0; h < 2; ++h) {
+      if (mr[h] >= M) continue;
+      float v[4] = {acc[h].x + bq[0], acc[h].y + bq[1], acc[h].z + bq[2], acc[h].w + bq[3]};
+      if constexpr (MODE == EPI_F32) {
+        float* const o = (float*)E.out + (int64_t)mr[h] * E.ldo + nf;
+        if (E.ldo & 3) {          // rows not 16-byte aligned: element by element
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = v[e];
+        } else {
+          *(float4*)o = make_float4(v[0], v[1], v[2], v[3]);
+        }
+      } else if constexpr (MODE == EPI_STORE || MODE == EPI_GELU) {
+        bf16x4 ov;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[e] = (bf16)(MODE == EPI_GELU ? gelu_f(v[e]) : v[e]);
+        bf16* const o = (bf16*)E.out + (int64_t)mr[h] * E.ldo + nf;
+        if (E.ldo & 3) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = ov[e];
+        } else {
+          *(bf16x4*)o = ov;
+        }
+      } else {
+        if constexpr (MODE == EPI_GATE_RESID) {
+          v[0] *= gin[h].x + gq[0];
+          v[1] *= gin[h].y + gq[1];
+          v[2] *= gin[h].z + gq[2];
+          v[3] *= gin[h].w + gq[3];
+        }
+        float4 r = rin[h];
+        r.x += v[0];
+        r.y += v[1];
+        r.z += v[2];
+        r.w += v[3];
+        *(float4*)(E.resid + (int64_t)mr[h] * N + nf) = r;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) *(float4*)(stg + (h * 32 + ln % 32) * LC + 8 * g + 4 * (ln / 32)) = acc[h];
+    __syncthreads();
+    epi_rows<MODE>(E, rowtab, m_base, M, tid, t0s);
+    __syncthreads();
+    epi_strip<BN, NT, MODE>(E, stg, LC, m_base, n0, M, N, tid, rowtab);
+  }
 }
 
 // compute units of the current device (queried once; 256 on MI355X)

@@ -295,8 +295,10 @@ def test_split_k_epilogues_exact(lib, M, N, K):
     """Below the knee (M <= 256 rows: the sub-knee video diagnostic's 128 or
     256 tokens per forward) the product is split over K into fp32 partials
     that a second pass sums in slice order before the epilogue; on exact
-    operands the sums are exact, so F32, RESID and the gated residual are
-    bit for bit the integer arithmetic, and STORE the bf16 rounding of it."""
+    operands the sums are exact, so F32 (also into rows not 16-byte
+    aligned), RESID and the gated residual are bit for bit the integer
+    arithmetic, STORE the bf16 rounding of it, and GELU within the bound of
+    the full-size GELU test."""
     print(f"split-K M={M} N={N} K={K}", flush=True)
     A, W, b, acc = int_operands(M, N, K, 21)
     ws, wsp, wsb = split_ws()
@@ -324,6 +326,27 @@ def test_split_k_epilogues_exact(lib, M, N, K):
                           workspace_bytes=wsb)
     run(lib, A, W, M, N, K, e)
     assert np.array_equal(st.float().cpu().numpy(), bf16_round(acc.astype(np.float32)))
+    # the plain residual: resid += A W^T + b, exact
+    resid = to_dev(c0, torch.float32)
+    e = sdlib.sd_gemm_epi(mode=sdlib.SD_EPI_RESID, bias=b.data_ptr(), resid=resid.data_ptr(), workspace=wsp,
+                          workspace_bytes=wsb)
+    run(lib, A, W, M, N, K, e)
+    assert np.array_equal(resid.cpu().numpy().astype(np.float64), c0 + acc)
+    # GELU against the oracle's exact-erf GELU (bound as in test_gelu_epilogue)
+    e = sdlib.sd_gemm_epi(mode=sdlib.SD_EPI_GELU, bias=b.data_ptr(), out=st.data_ptr(), ldo=N, workspace=wsp,
+                          workspace_bytes=wsb)
+    run(lib, A, W, M, N, K, e)
+    ref = dit.gelu(acc)
+    err = np.abs(st.float().cpu().numpy() - ref) - 2.0 ** -8 * np.abs(ref) - 2e-6 * np.abs(acc) - 1e-7
+    assert err.max() <= 0.0, f"gelu excess {err.max():.3e}"
+    # output rows two elements longer than N (not 16-byte aligned): element stores
+    ld = N + 2
+    wide = torch.full((M, ld), -1.0, dtype=torch.float32, device=device())
+    e = sdlib.sd_gemm_epi(mode=sdlib.SD_EPI_F32, bias=b.data_ptr(), out=wide.data_ptr(), ldo=ld, workspace=wsp,
+                          workspace_bytes=wsb)
+    run(lib, A, W, M, N, K, e)
+    wg = wide.cpu().numpy().astype(np.float64)
+    assert np.array_equal(wg[:, :N], acc) and np.all(wg[:, N:] == -1.0)
 
 
 def packed_copy(lib, W, N, K):
