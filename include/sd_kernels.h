@@ -172,6 +172,30 @@ sd_status sd_k_attention(int32_t dtype, const void* q, int64_t q_row_stride, int
                          int32_t nsplit, void* workspace, size_t workspace_bytes, void* stream);
 size_t sd_k_attention_workspace_bytes(int32_t R, int32_t H, int32_t L, int32_t hd, int32_t nsplit);
 
+/* sd_k_attention with a split plan: the query tiles of heads
+ * 0 .. unsplit_heads-1 each run as one workgroup over the whole key sequence
+ * (O written directly), and only heads unsplit_heads .. H-1 are split nsplit
+ * ways and combined.  The unsplit workgroups are dispatched first, so the
+ * short split pieces fill the compute units they leave free (the plan the
+ * stream uses for self-attention when the query tiles outnumber the resident
+ * workgroups).  0 <= unsplit_heads <= H, else SD_ERR_ARG; unsplit_heads = 0
+ * is sd_k_attention; with nsplit = 1 it is ignored.  Workspace as for
+ * sd_k_attention with the same nsplit.  Results per head equal
+ * sd_k_attention's with nsplit 1 (unsplit heads) or nsplit (split heads). */
+sd_status sd_k_attention_plan(int32_t dtype, const void* q, int64_t q_row_stride, int64_t q_head_stride, void* o,
+                              int32_t R, int32_t H, int32_t L, int32_t hd, int32_t nseg, const sd_kv_segment* segs,
+                              int32_t nsplit, int32_t unsplit_heads, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* The plan the stream picks for H heads of units_per_head query tiles over
+ * `tiles` key tiles of 64, at most max_split splits and `concurrent`
+ * resident workgroups: a greedy schedule of the workgroups in grid order
+ * over the resident slots, the split share charged 4 % for its partials and
+ * combine pass.  Host-only (no HIP call).  SD_ERR_ARG on a non-positive
+ * argument or a NULL output. */
+sd_status sd_k_attention_pick_plan(int32_t H, int32_t units_per_head, int32_t tiles, int32_t max_split,
+                                   int32_t concurrent, int32_t* nsplit, int32_t* unsplit_heads);
+
 /* sd_k_attention without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  The split partials use a fixed array of

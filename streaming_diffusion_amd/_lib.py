@@ -159,6 +159,11 @@ SIGNATURES = {
                                  C.c_int32, C.c_int32, C.c_int32, C.POINTER(sd_kv_segment), C.c_int32, C.c_void_p,
                                  C.c_size_t, C.c_void_p]),
     "sd_k_attention_workspace_bytes": (C.c_size_t, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32]),
+    "sd_k_attention_plan": (C.c_int, [C.c_int32, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int32, C.c_int32,
+                                      C.c_int32, C.c_int32, C.c_int32, C.POINTER(sd_kv_segment), C.c_int32, C.c_int32,
+                                      C.c_void_p, C.c_size_t, C.c_void_p]),
+    "sd_k_attention_pick_plan": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                           C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
     "sd_k_attention_noalloc": (C.c_int, [C.c_int32, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int32,
                                          C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.POINTER(sd_kv_segment),
                                          C.c_int32, C.c_void_p]),

@@ -15,7 +15,10 @@
 // the row index swapped) so that the score accumulators are directly the B
 // operand of O^T = V^T P^T with 8 consecutive keys per lane.
 // fp32 path: one thread per query on the vector ALUs.
+#include <algorithm>
 #include <cmath>
+#include <queue>
+#include <vector>
 
 #include "kernels.h"
 
@@ -124,13 +127,18 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nqt = (a.L + BQ - 1) / BQ;
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  // order (head, split, row, q-tile): the workgroups resident on one XCD at
-  // a time are the q-tiles of every row for the same key range -- the rows
-  // share the sink and the window, which then stream through that XCD's L2
-  // once for all of them
+  // The first nfull workgroups take the query tiles of heads [0, h_full)
+  // whole, the rest the split pieces of heads [h_full, H); each class is
+  // mapped XCD-contiguously on its own.  Order (head, split, row, q-tile):
+  // the workgroups resident on one XCD at a time are the q-tiles of every
+  // row for the same key range -- the rows share the sink and the window,
+  // which then stream through that XCD's L2 once for all of them.
+  const int nfull = a.h_full * nqt * a.R;
+  const bool whole = (int)blockIdx.x < nfull;
+  const int nsp = whole ? 1 : a.nsplit;
+  const int lid = whole ? xcd_remap(blockIdx.x, nfull) : xcd_remap(blockIdx.x - nfull, gridDim.x - nfull);
   const int qt = lid % nqt, r = a.r0 + (lid / nqt) % a.R;
-  const int sp = (lid / (nqt * a.R)) % a.nsplit, h = lid / (nqt * a.R * a.nsplit);
+  const int sp = (lid / (nqt * a.R)) % nsp, h = (whole ? 0 : a.h_full) + lid / (nqt * a.R * nsp);
   const int q0 = qt * BQ;
 
   // segments of this (row, head) as plain scalars, uniform over the
@@ -141,7 +149,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   const int c2 = a.nseg > 2 ? a.seg[2].count : 0;
   const int nt0 = (c0 + KB - 1) / KB, nt1 = (c1 + KB - 1) / KB, nt2 = (c2 + KB - 1) / KB;
   const int NT_all = nt0 + nt1 + nt2;
-  const int tps = (NT_all + a.nsplit - 1) / a.nsplit;
+  const int tps = (NT_all + nsp - 1) / nsp;
   const int T0 = min(NT_all, sp * tps), NT = min(NT_all, T0 + tps);   // this split's key tiles [T0, NT)
   const bf16* const kbase0 = (const bf16*)a.seg[0].k + (int64_t)r * a.seg[0].k_rs + (int64_t)h * a.seg[0].k_hs;
   const bf16* const kbase1 = (const bf16*)a.seg[1].k + (int64_t)r * a.seg[1].k_rs + (int64_t)h * a.seg[1].k_hs;
@@ -356,7 +364,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   }
 
   const float l_tot = halves_sum(l_run);
-  if (a.nsplit > 1) {
+  if (nsp > 1) {
     // partial result of this key range: unnormalised O and (reference max, sum)
     if (myq < a.L) {
       bf16* po = a.part_o + sp * a.part_so + ((int64_t)r * a.L + myq) * a.d + (int64_t)h * HD;
@@ -579,7 +587,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Combine of split partials: O = sum_s w_s O_s / sum_s w_s l_s with
+// Combine of split partials (heads h_full .. H-1): O = sum_s w_s O_s / sum_s w_s l_s with
 // w_s = 2^((m_s - max_s m_s) * scale * log2 e) (a split without keys has
 // m_s = -inf and weight 0).  One thread per 8 head-dim elements of one
 // (token, head); NS > 0 fixes the split count so every split's loads are in
@@ -587,11 +595,11 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
 // R * L * H * hd / 8 fits in 31 bits.
 template <int NS>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
-  const int c8 = a.hd >> 3, per_tok = a.H * c8;
+  const int c8 = a.hd >> 3, per_tok = (a.H - a.h_full) * c8;
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= a.R * a.L * per_tok) return;
   const int tok = i / per_tok, rem = i - tok * per_tok;
-  const int h = rem / c8, e = (rem - h * c8) * 8;
+  const int h = a.h_full + rem / c8, e = (rem - (h - a.h_full) * c8) * 8;
   const int rr = tok / a.L, t = tok - rr * a.L;
   const int r = a.r0 + rr;
   const float sl2 = a.scale * 1.4426950408889634f;
@@ -658,9 +666,67 @@ int attention_pick_split(int units, int tiles, int max_split, int concurrent) {
   return best;
 }
 
+// Greedy list schedule of n_long workgroups of len_long key tiles followed
+// by n_short of len_short on `slots` resident slots (each workgroup starts
+// on the earliest free slot, in grid order): the finishing time.
+static int64_t list_makespan(int64_t n_long, int64_t len_long, int64_t n_short, int64_t len_short, int slots) {
+  std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> free_at;
+  for (int i = 0; i < slots; ++i) free_at.push(0);
+  int64_t end = 0;
+  auto place = [&](int64_t n, int64_t len) {
+    for (int64_t j = 0; j < n; ++j) {
+      const int64_t t = free_at.top() + len;
+      free_at.pop();
+      free_at.push(t);
+      end = std::max(end, t);
+    }
+  };
+  place(n_long, len_long);
+  place(n_short, len_short);
+  return end;
+}
+
+void attention_pick_plan(int heads, int units_per_head, int tiles, int max_split, int concurrent, int* nsplit,
+                         int* h_full) {
+  // remembered per arguments (the step asks with the same ones every block)
+  static thread_local int memo[7] = {-1, -1, -1, -1, -1, 1, 0};
+  if (memo[0] == heads && memo[1] == units_per_head && memo[2] == tiles && memo[3] == max_split &&
+      memo[4] == concurrent) {
+    *nsplit = memo[5];
+    *h_full = memo[6];
+    return;
+  }
+  const int units = heads * units_per_head;
+  int best_ns = attention_pick_split(units, tiles, max_split, concurrent), best_hf = 0;
+  // the uniform plan, priced by the same schedule, with 4 % for the split's
+  // partial traffic and combine pass in proportion to the heads it splits
+  double best_cost = (double)list_makespan(0, 0, (int64_t)units * best_ns, (tiles + best_ns - 1) / best_ns,
+                                           concurrent) * (best_ns > 1 ? 1.04 : 1.0);
+  if (units > concurrent && best_ns > 1) {
+    // whole heads filling the first full rounds, the rest split
+    const int hf_max = std::min(heads - 1, (units / concurrent) * concurrent / std::max(1, units_per_head));
+    // (most whole heads first: on a tie they leave the least to combine)
+    for (int hf = hf_max; hf >= std::max(1, hf_max - 2); --hf)
+      for (int ns = 2; ns <= max_split && ns <= tiles; ++ns) {
+        const int64_t n_short = (int64_t)(heads - hf) * units_per_head * ns;
+        const double cost = (double)list_makespan((int64_t)hf * units_per_head, tiles, n_short, (tiles + ns - 1) / ns,
+                                                  concurrent) * (1.0 + 0.04 * (heads - hf) / heads);
+        if (cost < best_cost * 0.995) {
+          best_cost = cost;
+          best_ns = ns;
+          best_hf = hf;
+        }
+      }
+  }
+  const int v[7] = {heads, units_per_head, tiles, max_split, concurrent, best_ns, best_hf};
+  std::copy(v, v + 7, memo);
+  *nsplit = best_ns;
+  *h_full = best_hf;
+}
+
 hipError_t attention_combine(hipStream_t s, const AttnArgs& a) {
-  if (a.nsplit <= 1 || a.R == 0 || a.L == 0) return hipSuccess;
-  const int64_t n = (int64_t)a.R * a.L * a.H * (a.hd / 8);
+  if (a.nsplit <= 1 || a.R == 0 || a.L == 0 || a.h_full >= a.H) return hipSuccess;
+  const int64_t n = (int64_t)a.R * a.L * (a.H - a.h_full) * (a.hd / 8);
   if (a.hd % 8 || n > 0x7fffffff) return hipErrorInvalidValue;
   const unsigned g = (unsigned)((n + 255) / 256);
   switch (a.nsplit) {
@@ -680,9 +746,11 @@ hipError_t attention(hipStream_t s, bool bf, const AttnArgs& args, bool combine)
   if (args.R == 0 || args.L == 0) return hipSuccess;
   AttnArgs a = args;
   if (a.nsplit < 1 || !bf) a.nsplit = 1;
+  if (a.nsplit == 1 || a.h_full < 0 || a.h_full > a.H) a.h_full = 0;
   if (bf) {
     const int nsplit = a.nsplit;
-    const dim3 g(((a.L + 127) / 128) * a.H * a.R * nsplit);
+    const int64_t per_head = (int64_t)((a.L + 127) / 128) * a.R;
+    const dim3 g((unsigned)(per_head * (a.h_full + (int64_t)(a.H - a.h_full) * nsplit)));
     switch (a.hd) {
       case 32:
         if (a.nseg == 1) attn_bf16_kernel<32, 1><<<g, 256, 0, s>>>(a);
@@ -698,7 +766,7 @@ hipError_t attention(hipStream_t s, bool bf, const AttnArgs& args, bool combine)
         break;
       default: return hipErrorInvalidValue;
     }
-    if (nsplit > 1 && combine) {
+    if (nsplit > 1 && a.h_full < a.H && combine) {
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       return attention_combine(s, a);

@@ -109,6 +109,12 @@ struct AttnArgs {
   // absolute, strides part_so / part_sml elements), then a combine pass
   // normalises.  nsplit = 1 writes O directly.
   int nsplit;
+  // heads [0, h_full) are not split: each of their query tiles is one
+  // workgroup over the whole key sequence that writes O directly; only heads
+  // [h_full, H) are split nsplit ways (and combined).  The unsplit
+  // workgroups come first in the grid, so they are dispatched first and the
+  // short split pieces fill the slots they leave.
+  int h_full;
   bf16* part_o;
   float2* part_ml;
   long long part_so, part_sml;
@@ -126,6 +132,11 @@ int attention_wg_per_cu(bool bf, int hd);
 // Split count that best fills `concurrent` resident workgroups for `units`
 // query tiles over `tiles` key tiles (1 .. max_split).
 int attention_pick_split(int units, int tiles, int max_split, int concurrent);
+// Split plan for `heads` heads of `units_per_head` query tiles each over
+// `tiles` key tiles: the first *h_full heads unsplit, the others split
+// *nsplit ways (*h_full = 0: every head split, *nsplit = 1: none).
+void attention_pick_plan(int heads, int units_per_head, int tiles, int max_split, int concurrent, int* nsplit,
+                         int* h_full);
 
 // ---------------------------------------------------------------- Stream-VAE
 // Causal 3x3x3 convolution: x bf16 [T][H][W][Cin], cache bf16 [2][H][W][Cin]

@@ -265,7 +265,16 @@ static void attach_partials(sdk::AttnArgs& a, void* workspace) {
 sd_status sd_k_attention(int32_t dtype, const void* q, int64_t q_row_stride, int64_t q_head_stride, void* o,
                          int32_t R, int32_t H, int32_t L, int32_t hd, int32_t nseg, const sd_kv_segment* segs,
                          int32_t nsplit, void* workspace, size_t workspace_bytes, void* stream) {
+  return sd_k_attention_plan(dtype, q, q_row_stride, q_head_stride, o, R, H, L, hd, nseg, segs, nsplit, 0, workspace,
+                             workspace_bytes, stream);
+}
+
+sd_status sd_k_attention_plan(int32_t dtype, const void* q, int64_t q_row_stride, int64_t q_head_stride, void* o,
+                              int32_t R, int32_t H, int32_t L, int32_t hd, int32_t nseg, const sd_kv_segment* segs,
+                              int32_t nsplit, int32_t unsplit_heads, void* workspace, size_t workspace_bytes,
+                              void* stream) {
   if (nsplit < 1 || nsplit > 64) return SD_ERR_ARG;
+  if (unsplit_heads < 0 || unsplit_heads > H) return SD_ERR_ARG;
   if (nsplit > 1) {
     if (dtype != SD_DTYPE_BF16 || !workspace || ((uintptr_t)workspace & 255)) return SD_ERR_ARG;
     if (workspace_bytes < sd_k_attention_workspace_bytes(R, H, L, hd, nsplit)) return SD_ERR_WORKSPACE;
@@ -275,8 +284,20 @@ sd_status sd_k_attention(int32_t dtype, const void* q, int64_t q_row_stride, int
   const sd_status st = attention_prepare(dtype, q, q_row_stride, q_head_stride, o, R, H, L, hd, nseg, segs, nsplit,
                                          &a, &bf);
   if (st != SD_OK) return st;
+  a.h_full = nsplit > 1 ? unsplit_heads : 0;
   attach_partials(a, workspace);
   return sdk::attention((hipStream_t)stream, bf, a) == hipSuccess ? SD_OK : SD_ERR_HIP;
+}
+
+sd_status sd_k_attention_pick_plan(int32_t H, int32_t units_per_head, int32_t tiles, int32_t max_split,
+                                   int32_t concurrent, int32_t* nsplit, int32_t* unsplit_heads) {
+  if (H < 1 || units_per_head < 1 || tiles < 1 || max_split < 1 || concurrent < 1 || !nsplit || !unsplit_heads)
+    return SD_ERR_ARG;
+  int ns = 1, hf = 0;
+  sdk::attention_pick_plan(H, units_per_head, tiles, max_split, concurrent, &ns, &hf);
+  *nsplit = ns;
+  *unsplit_heads = hf;
+  return SD_OK;
 }
 
 // ---------------------------------------------------------------------------

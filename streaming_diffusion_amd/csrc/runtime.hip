@@ -823,8 +823,8 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, const StepDyn* dd
       if (s->attn_split_max > 1) {
         const int nk = ((sk.count + 7) & ~7) + sw.count + so.count;
         const int qt = sdk::attention_q_tile(bf, hd);
-        A.nsplit = sdk::attention_pick_split(R * H * ((L + qt - 1) / qt), (nk + 63) / 64, s->attn_split_max,
-                                             s->cus * sdk::attention_wg_per_cu(bf, hd));
+        sdk::attention_pick_plan(H, R * ((L + qt - 1) / qt), (nk + 63) / 64, s->attn_split_max,
+                                 s->cus * sdk::attention_wg_per_cu(bf, hd), &A.nsplit, &A.h_full);
         A.part_o = s->part_o;
         A.part_ml = s->part_ml;
         A.part_so = (long long)s->Rmax * L * d;
@@ -833,9 +833,11 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, const StepDyn* dd
       const double shared = (double)sk.count + sw.count;
       PROF(SD_PROF_ATTN_SELF, 4.0 * R * L * (shared + so.count) * d,
            (double)es * d * (2.0 * R * L + 2.0 * shared + 2.0 * R * L), sdk::attention(st, bf, A, false));
-      if (A.nsplit > 1)
-        PROF(SD_PROF_ATTN_COMBINE, 0.0, (double)A.nsplit * R * L * (d * 2.0 + H * 8.0) + (double)R * L * d * es,
+      if (A.nsplit > 1 && A.h_full < H) {
+        const double hs = (double)(H - A.h_full) / H;     // share of the heads that were split
+        PROF(SD_PROF_ATTN_COMBINE, 0.0, hs * ((double)A.nsplit * R * L * (d * 2.0 + H * 8.0) + (double)R * L * d * es),
              sdk::attention_combine(st, A));
+      }
     }
     // the leaving chunks append their K / V^T in push order (ring positions
     // ptr_old + k L); a capturing chunk also fills its sink entry, with B > 1

@@ -121,6 +121,13 @@ def test_create_rejects_bad_arguments_before_any_device_call(lib):
     assert lib.sd_k_attention(1, 8, 0, 0, 8, 1, 1, 8, 48, 1, C.byref(seg), 1, None, 0, None) == L.SD_ERR_SHAPE
     assert lib.sd_k_attention(1, 8, 0, 0, 8, 1, 1, 8, 64, 1, C.byref(seg), 2, None, 0, None) == L.SD_ERR_ARG
     assert lib.sd_k_attention(1, 8, 0, 0, 8, 1, 1, 8, 64, 1, C.byref(seg), 2, 256, 16, None) == L.SD_ERR_WORKSPACE
+    assert lib.sd_k_attention_plan(1, 8, 0, 0, 8, 1, 2, 8, 64, 1, C.byref(seg), 2, 3, 256, 1 << 20,
+                                   None) == L.SD_ERR_ARG       # unsplit heads > H
+    assert lib.sd_k_attention_plan(1, 8, 0, 0, 8, 1, 2, 8, 64, 1, C.byref(seg), 2, -1, 256, 1 << 20,
+                                   None) == L.SD_ERR_ARG
+    ns, hf = C.c_int32(), C.c_int32()
+    assert lib.sd_k_attention_pick_plan(0, 1, 1, 8, 512, C.byref(ns), C.byref(hf)) == L.SD_ERR_ARG
+    assert lib.sd_k_attention_pick_plan(1, 1, 1, 8, 512, None, C.byref(hf)) == L.SD_ERR_ARG
     assert lib.sd_k_attention_workspace_bytes(2, 3, 40, 64, 1) == 0
     assert lib.sd_k_attention_workspace_bytes(2, 3, 40, 64, 3) == ((3 * 2 * 40 * 3 * 64 * 2 + 255) // 256 * 256
                                                                   + 3 * 2 * 3 * 40 * 8)
@@ -333,3 +340,41 @@ def test_attention_noalloc_rejects_before_any_device_call(lib):
     assert lib.sd_k_attention_noalloc(1, None, 0, 0, 8, 1, 1, 8, 64, 1, C.byref(seg), 1, None) == L.SD_ERR_ARG
     # the video step's own split (5 splits, 2 rows) fits
     assert lib.sd_k_attention_workspace_bytes(2, 12, 3120, 128, 5) <= L.SD_ATTENTION_NOALLOC_SCRATCH_BYTES
+
+
+# ------------------------------------------------------------------ attention split plan (host only)
+def _greedy_finish(jobs, slots):
+    """Workgroups started in grid order on the earliest free of `slots`
+    resident slots; jobs = list of (count, length)."""
+    import heapq
+    free = [0] * slots
+    end = 0
+    for n, length in jobs:
+        for _ in range(n):
+            t = heapq.heappop(free) + length
+            heapq.heappush(free, t)
+            end = max(end, t)
+    return end
+
+
+@pytest.mark.parametrize("H,uph,tiles,cap,slots", [(12, 50, 221, 8, 512), (12, 1, 10, 8, 512),
+                                                   (40, 25, 221, 8, 512), (16, 8, 40, 8, 512),
+                                                   (12, 25, 74, 8, 512), (12, 100, 221, 4, 512)])
+def test_attention_split_plan(lib, H, uph, tiles, cap, slots):
+    """The plan is within 5 % of the best greedy schedule over every
+    (unsplit heads, splits) pair, never splits more than asked, and with few
+    query tiles (fewer than the resident slots) splits every head."""
+    ns, hf = C.c_int32(), C.c_int32()
+    assert lib.sd_k_attention_pick_plan(H, uph, tiles, cap, slots, C.byref(ns), C.byref(hf)) == L.SD_OK
+    ns, hf = ns.value, hf.value
+    assert 1 <= ns <= cap and 0 <= hf < H
+
+    def finish(h, s):
+        return _greedy_finish([(h * uph, tiles), ((H - h) * uph * s, -(-tiles // s))], slots)
+
+    best = min(finish(h, s) for h in range(H) for s in range(1, cap + 1))
+    assert finish(hf, ns) <= 1.05 * best
+    if H * uph <= slots:
+        assert hf == 0
+    if (H, uph, tiles) == (12, 50, 221):      # the 1.3B-shaped video step: 10 heads whole, 2 split in 5
+        assert (hf, ns) == (10, 5)

@@ -203,6 +203,80 @@ def test_attention_full_video_shape_sampled(lib):
         check_close(got[r][sample], ref, "bf16", f"row {r}", stored_bf16=True)
 
 
+def _attn_call(lib, entry, qd, o, R, H, L, hd, segs, nsplit, extra=()):
+    wsb = lib.sd_k_attention_workspace_bytes(R, H, L, hd, nsplit)
+    ws = torch.empty(max(wsb, 1) + 256, dtype=torch.uint8, device=device())
+    wsp = (ws.data_ptr() + 255) // 256 * 256 if wsb else None
+    call(entry(1, qd.data_ptr(), H * L * hd, L * hd, o.data_ptr(), R, H, L, hd, 3, segs, nsplit, *extra, wsp, wsb,
+               stream_ptr()))
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().reshape(R, L, H, hd).copy()
+
+
+@pytest.mark.parametrize("H,hd,L,sink_count,W,ring_start,ring_count,nsplit,unsplit", [
+    (3, 64, 72, 4, 64, 40, 48, 2, 1),          # ring wraps, ragged queries; one head whole, two split
+    (3, 128, 200, 12, 512, 136, 504, 3, 2),
+    (4, 128, 136, 8, 256, 0, 256, 5, 3),       # more splits than some key ranges fill
+    (3, 32, 64, 0, 64, 0, 0, 2, 3),            # every head whole: no combine
+])
+def test_attention_plan_matches_oracle(lib, H, hd, L, sink_count, W, ring_start, ring_count, nsplit, unsplit):
+    """A split plan (heads 0 .. unsplit-1 whole, the others split): every
+    head bit for bit what sd_k_attention gives it unsplit or split, and all
+    of them against the brute-force oracle attention."""
+    print(f"attention plan H={H} hd={hd} L={L} nsplit={nsplit} unsplit={unsplit}", flush=True)
+    rng = np.random.default_rng(hd + L + H)
+    R = 2
+    sink_cap = max(8, (sink_count + 7) // 8 * 8)
+    dev, segs, keys, vals = make_segments(rng, H, hd, R, L, sink_count, sink_cap, W, ring_start, ring_count,
+                                          torch.bfloat16)
+    q = bf16_round(rng.standard_normal((R, H, L, hd)).astype(np.float32))
+    qd = to_dev(q, torch.bfloat16)
+    o = torch.empty((R * L, H * hd), dtype=torch.bfloat16, device=device())
+    got = _attn_call(lib, lib.sd_k_attention_plan, qd, o, R, H, L, hd, segs, nsplit, (unsplit,))
+    whole = _attn_call(lib, lib.sd_k_attention, qd, o, R, H, L, hd, segs, 1)
+    split = _attn_call(lib, lib.sd_k_attention, qd, o, R, H, L, hd, segs, nsplit)
+    assert np.array_equal(got[:, :, :unsplit], whole[:, :, :unsplit])
+    assert np.array_equal(got[:, :, unsplit:], split[:, :, unsplit:])
+    for r in range(R):
+        ref = oracle_attention(q[r].transpose(1, 0, 2).astype(np.float64), keys[r].astype(np.float64),
+                               vals[r].astype(np.float64))
+        check_close(got[r], ref, "bf16", f"attention plan row {r}", stored_bf16=True)
+
+
+def test_attention_plan_full_video_shape(lib):
+    """The 1.3B-shaped video self-attention as the stream launches it: 12
+    heads, 2 rows of 3120 queries, 1560 sink + wrapped 9360 window + 3120 own
+    keys, with the plan the stream picks (10 heads whole, 2 split 5 ways).
+    Every head bit for bit its unsplit or split result; sampled queries of a
+    whole and a split head against the oracle."""
+    print("attention plan full video shape", flush=True)
+    rng = np.random.default_rng(12)
+    H, R, hd, L, S, W = 12, 2, 128, 3120, 1560, 9360
+    ns, hf = C.c_int32(), C.c_int32()
+    call(lib.sd_k_attention_pick_plan(H, R * ((L + 127) // 128), (S + W + L + 63) // 64, 8, 512, C.byref(ns),
+                                      C.byref(hf)))
+    nsplit, unsplit = ns.value, hf.value
+    print(f"  plan: {unsplit} heads whole, the rest split {nsplit} ways", flush=True)
+    assert 0 < unsplit < H and nsplit > 1
+    dev, segs, keys, vals = make_segments(rng, H, hd, R, L, S, S, W, 3120, W, torch.bfloat16)
+    q = bf16_round(rng.standard_normal((R, H, L, hd)).astype(np.float32))
+    qd = to_dev(q, torch.bfloat16)
+    o = torch.empty((R * L, H * hd), dtype=torch.bfloat16, device=device())
+    got = _attn_call(lib, lib.sd_k_attention_plan, qd, o, R, H, L, hd, segs, nsplit, (unsplit,))
+    whole = _attn_call(lib, lib.sd_k_attention, qd, o, R, H, L, hd, segs, 1)
+    assert np.array_equal(got[:, :, :unsplit], whole[:, :, :unsplit])
+    del whole
+    split = _attn_call(lib, lib.sd_k_attention, qd, o, R, H, L, hd, segs, nsplit)
+    assert np.array_equal(got[:, :, unsplit:], split[:, :, unsplit:])
+    del split
+    sample = np.concatenate([np.arange(0, 3), rng.integers(0, L, 20), np.arange(L - 3, L)])
+    for r in range(R):
+        for h in (0, unsplit - 1, unsplit, H - 1):
+            qh = q[r, h][sample].astype(np.float64)[:, None, :]
+            ref = oracle_attention(qh, keys[r][:, h:h + 1].astype(np.float64), vals[r][:, h:h + 1].astype(np.float64))
+            check_close(got[r][sample][:, h:h + 1], ref, "bf16", f"row {r} head {h}", stored_bf16=True)
+
+
 # ------------------------------------------------------------------ SSF / motion reductions
 def test_ssf_sums_bit_exact_u8(lib):
     cfg = get_config("tiny")
