@@ -346,6 +346,8 @@ hipError_t ln_mod(hipStream_t s, bool bf, const float* x, void* out, int M, int 
   } while (0)
   if (d <= 1024)
     SD_LN_LAUNCH(4);
+  else if (d <= 1536)
+    SD_LN_LAUNCH(6);
   else if (d <= 2048)
     SD_LN_LAUNCH(8);
   else

@@ -198,13 +198,13 @@ def test_head_epilogue_unpatchifies_exactly(lib, rows, t, hp, wp, ch):
 
 # ------------------------------------------------------------------ LayerNorm + adaLN modulation
 @pytest.mark.parametrize("M,d,Lr", [(R * L, D, L), (L, 5120, L), (2048, 1024, 1024), (37, 128, 10), (128, D, 128),
-                                    (300, 768, 100), (1024, 1024, 512)])
+                                    (300, 768, 100), (1024, 1024, 512), (3000, 2048, 1500), (2100, 1280, 700)])
 def test_ln_mod_against_oracle(lib, M, d, Lr):
     """bf16 output of LN(x) * (1 + scale) + shift, scale / shift = the row's
     modulation slots plus the block table (the attention slots 0 and 1 of
-    6d); register-resident rows of 4 (d <= 1024), 8 (1536) and 20 (5120)
-    vectors per lane, and up to 1024 rows of width 768 - 2048 a workgroup per
-    row.  Bound: the stored bf16 rounding plus 1e-4 of the RMS."""
+    6d); register-resident rows of 4 (d <= 1024), 6 (1280, 1536), 8 (2048)
+    and 20 (5120) vectors per lane, and up to 1024 rows of width 768 - 2048 a
+    workgroup per row.  Bound: the stored bf16 rounding plus 1e-4 of the RMS."""
     print(f"ln_mod M={M} d={d}", flush=True)
     rng = np.random.default_rng(d + M)
     rows = (M + Lr - 1) // Lr
