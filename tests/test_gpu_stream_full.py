@@ -76,3 +76,52 @@ def test_video13b_subknee_graph_replay():
     print("video13b sub-knee, 2 blocks, graph replay", flush=True)
     orc, _ = run_parity(cfg, 8, oracle_dtype=np.float32, progress=True, graph=True)
     assert orc.graph_stats[1] >= 3
+
+
+def test_video13b_graph_replay_matches_launched():
+    """The 1.3B-shaped video step (full width, 2 blocks) replayed as a
+    captured graph gives bit for bit what the launched step gives, step by
+    step, while the window fills and wraps: the same kernels read the
+    per-step values from device memory in both, and the attention's split
+    plan (10 heads whole, 2 split) is part of the captured launch
+    sequence."""
+    import torch
+
+    import streaming_diffusion_amd._lib as L
+    from streaming_diffusion_amd.runner import StreamRunner, upload_weights
+    from workloads import gen
+    from gpu_helpers import to_dev
+
+    device()
+    cfg = get_config("video13b", n_blocks=2)
+    print("video13b full width, 2 blocks, graph replay vs launched", flush=True)
+    weights = gen.make_weights(cfg)
+    ctx = to_dev(gen.make_context(cfg), torch.bfloat16)
+    side = torch.cuda.Stream()
+    runs = [StreamRunner(cfg, upload_weights(cfg, weights)), StreamRunner(cfg, upload_weights(cfg, weights),
+                                                                          stream=side)]
+    torch.cuda.synchronize()
+    runs[1].set_graph(True)
+    for r in runs:
+        r.set_context(ctx, None)
+    src, nz, us = gen.LatentSource(cfg), gen.NoiseSource(cfg), gen.UniformSource()
+    lat = cfg.latent_elems
+    for k in range(8):
+        x0, e, u = to_dev(src.next(), torch.float32), to_dev(gen.frame_noise(cfg, nz), torch.float32), us.next()
+        res = []
+        for i, r in enumerate(runs):
+            with torch.cuda.stream(side if i == 1 else torch.cuda.current_stream()):
+                r.push(x0, e, None, u)
+            sg = r.step()
+            torch.cuda.synchronize()
+            eps = r.buffer(L.SD_BUF_EPS, torch.float32, (sg.rows, lat)).cpu().numpy()
+            out = r.out.cpu().numpy() if sg.has_output else None
+            res.append((sg.rows, sg.kv_valid, sg.kv_ptr, eps, out))
+        (ra, va, pa, ea, oa), (rb, vb, pb, eb, ob) = res
+        assert (ra, va, pa) == (rb, vb, pb), k
+        assert np.array_equal(ea, eb), f"step {k}: eps differs"
+        assert (oa is None) == (ob is None) and (oa is None or np.array_equal(oa, ob)), f"step {k}: output differs"
+        print(f"  step {k + 1}: {ra} rows, kv_valid {va}: identical", flush=True)
+    assert runs[1].graph_stats()[1] >= 3
+    for r in runs:
+        r.close()
