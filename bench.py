@@ -273,8 +273,8 @@ def measure(cfg, weights, steps: int, warmup: int, dev, io_stream: bool = False,
         per_launch_ms = attn["ms"] / attn["launches"]
         per_launch_bytes = attn["bytes"] / attn["launches"]
         achieved = per_launch_bytes / (per_launch_ms * 1e-3) / 1e9
-        roofline = {"kernel": f"{dom_kind}: gemm_wstream_kernel + gemm_reduce_kernel (weight-streaming GEMM, "
-                              f"K split over the CUs)",
+        roofline = {"kernel": f"{dom_kind}: gemm_wstream_kernel + gemm_reduce_ln_kernel (weight-streaming GEMM, "
+                              f"K split over the CUs; the reduction pass also runs the next block's LayerNorm)",
                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": measured_traffic(PMC_FILE_KNEE, GEMM_SOURCE) if dom_kind == "gemm_ffn2" else None,

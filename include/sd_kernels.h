@@ -77,6 +77,16 @@ typedef struct {
   size_t workspace_bytes;
   const void* wpack;           /* optional: W rearranged by sd_k_pack_weight(); with M <= 256 and a
                                   workspace the product reads W from here (NULL: from W) */
+  void* ln_out;                /* optional, GATE_RESID / RESID of a bf16 product: after the update,
+                                  the LayerNorm of each residual row as sd_k_ln_mod() computes it
+                                  (form ln_form, modulation ln_mod / ln_blk at ln_shift_off /
+                                  ln_scale_off of ln_six_d, row r = m / L), written here; on the
+                                  few-row path the reduction pass does it in the same launch
+                                  (N a multiple of 256, at most 2048), otherwise a LayerNorm pass
+                                  follows.  NULL: none. */
+  const float* ln_mod;
+  const void* ln_blk;
+  int32_t ln_shift_off, ln_scale_off, ln_six_d, ln_form;
 } sd_gemm_epi;
 
 /* One bf16 GEMM with the epilogue e->mode, on the kernels and launch

@@ -101,7 +101,9 @@ class sd_gemm_epi(C.Structure):
                 ("rope_positions", C.c_int32), ("t0", C.c_int32 * SD_MAX_ROWS), ("eps", C.c_void_p),
                 ("C", C.c_int32), ("Hl", C.c_int32), ("Wl", C.c_int32), ("p", C.c_int32), ("T", C.c_int32),
                 ("f16", C.c_int32), ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
-                ("wpack", C.c_void_p)]
+                ("wpack", C.c_void_p), ("ln_out", C.c_void_p), ("ln_mod", C.c_void_p), ("ln_blk", C.c_void_p),
+                ("ln_shift_off", C.c_int32), ("ln_scale_off", C.c_int32), ("ln_six_d", C.c_int32),
+                ("ln_form", C.c_int32)]
 
 
 SD_LN_PLAIN, SD_LN_F16, SD_LN_SPLIT = 0, 1, 2

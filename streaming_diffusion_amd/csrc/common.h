@@ -134,7 +134,18 @@ struct Epi {
   float* part;
   int64_t part_cap;
   int ksplit;
+  int part_rows;        // partials row-major [slice][M][N] instead (for the fused LayerNorm pass)
   // the same W in fragment order (pack_weight), read by the few-row product
   // when set (null: W is read as [N][K])
   const void* wpack;
+  // EPI_RESID / EPI_GATE_RESID on the few-row path: when ln_out is set the
+  // reduction pass also writes the LayerNorm (+ modulation) of each updated
+  // residual row to ln_out (form 0 plain in the GEMM's type, 1 fp16 without
+  // modulation, 2 bf16 hi / lo pair), the computation of the LayerNorm
+  // kernel; gemm_fuses_ln() says whether a call takes that path
+  void* ln_out;
+  const float* ln_mod;  // [R][ln_six] modulation rows (null: none)
+  const void* ln_blk;   // [ln_six] block table (null: none)
+  int ln_shift, ln_scale, ln_six, ln_form;
+  float ln_eps;
 };

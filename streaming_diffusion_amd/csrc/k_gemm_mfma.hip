@@ -18,6 +18,7 @@
 #include <type_traits>
 
 #include "kernels.h"
+#include "ln_row.h"
 
 namespace sdk {
 
@@ -852,6 +853,82 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(int M, int N, Epi E) {
   }
 }
 
+// The reduction pass of a residual GEMM fused with the LayerNorm that reads
+// the residual next: one workgroup per row, thread j owns features
+// 4 j .. 4 j + 3, read from row-major partials (the streaming kernel stores
+// them so with part_rows; in the fragment order a row is 16 bytes of every
+// 128-byte line, eight times the traffic).  It
+// sums the K slices in slice order and applies the epilogue exactly as
+// gemm_reduce_kernel does (the same residual values), stores the row, then
+// normalises and modulates it as the LayerNorm row kernel does (ln_row), so
+// the output is the one the separate passes would give.  Saves a launch and
+// the residual's read-back per block below the knee.  N a multiple of 256,
+// at most 2048 (blockDim = N / 4, at most 8 waves).
+template <int MODE, typename T, bool SPLIT>
+__global__ __launch_bounds__(512) void gemm_reduce_ln_kernel(int M, int N, Epi E) {
+  __shared__ float red[2][8];
+  const int m = blockIdx.x, j = threadIdx.x, lane = j & 63, wave = j >> 6, nw = blockDim.x >> 6;
+  const int n = 4 * j;
+  // row-major partials (part_rows): slice sl of this float4 at sl M N + m N + n
+  const float4* src = (const float4*)(E.part + (int64_t)m * N + n);
+  const int64_t slice_st = (int64_t)M * N / 4;
+  // epilogue and LayerNorm operands, requested before the partial sums
+  float bq[4] = {0.f, 0.f, 0.f, 0.f}, gq[4] = {0.f, 0.f, 0.f, 0.f};
+  if (E.bias) {
+    const bf16x4 bv = *(const bf16x4*)((const bf16*)E.bias + n);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bq[e] = (float)bv[e];
+  }
+  float4 gin = make_float4(0.f, 0.f, 0.f, 0.f);
+  if constexpr (MODE == EPI_GATE_RESID) {
+    const bf16x4 gv = *(const bf16x4*)((const bf16*)E.blk + E.gate_off + n);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) gq[e] = (float)gv[e];
+    gin = *(const float4*)(E.mod + (int64_t)(m / E.L) * E.six_d + E.gate_off + n);
+  }
+  const float4 rin = *(const float4*)(E.resid + (int64_t)m * N + n);
+  const float* mr = E.ln_mod ? E.ln_mod + (int64_t)(m / E.L) * E.ln_six : nullptr;
+  float sh[4] = {0.f, 0.f, 0.f, 0.f}, sc[4] = {0.f, 0.f, 0.f, 0.f};
+  if (mr) ln_row_mod(mr, (const T*)E.ln_blk, E.ln_shift, E.ln_scale, j, sh, sc);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  int sl = 0;
+  for (; sl + 8 <= E.ksplit; sl += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = src[(sl + u) * slice_st];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      acc.x += v[u].x;
+      acc.y += v[u].y;
+      acc.z += v[u].z;
+      acc.w += v[u].w;
+    }
+  }
+  for (; sl < E.ksplit; ++sl) {
+    const float4 v = src[sl * slice_st];
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  float v[4] = {acc.x + bq[0], acc.y + bq[1], acc.z + bq[2], acc.w + bq[3]};
+  if constexpr (MODE == EPI_GATE_RESID) {
+    v[0] *= gin.x + gq[0];
+    v[1] *= gin.y + gq[1];
+    v[2] *= gin.z + gq[2];
+    v[3] *= gin.w + gq[3];
+  }
+  float4 r = rin;
+  r.x += v[0];
+  r.y += v[1];
+  r.z += v[2];
+  r.w += v[3];
+  *(float4*)(E.resid + (int64_t)m * N + n) = r;
+  float o[4];
+  ln_row(r, N, E.ln_eps, mr != nullptr, sh, sc, red, nw, lane, wave, o);
+  ln_row_store<T, SPLIT>((T*)E.ln_out + (int64_t)m * (SPLIT ? 2 * N : N), N, j, o);
+}
+
 // compute units of the current device (queried once; 256 on MI355X)
 static int device_cus() {
   static int cus = 0;
@@ -895,7 +972,9 @@ __global__ __launch_bounds__(256) void gemm_wstream_kernel(const bf16* __restric
                                                            int M, int N, int K, Epi E) {
   constexpr int BN = 128, BK = 64;
   constexpr int ATILE = 128 * BK;                         // bf16 elements of one k-tile of A
-  __shared__ __attribute__((aligned(1024))) bf16 as[KT * ATILE];
+  constexpr int RL = 132;                                 // fp32 row pitch of the row-major staging
+  constexpr int AS = KT * ATILE > 64 * RL * 2 ? KT * ATILE : 64 * RL * 2;
+  __shared__ __attribute__((aligned(1024))) bf16 as[AS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tiles_n = (N + BN - 1) / BN, tiles = tiles_n * ((M + 127) / 128);
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
@@ -953,6 +1032,30 @@ __global__ __launch_bounds__(256) void gemm_wstream_kernel(const bf16* __restric
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[j] = mfma32<H16>(wf[t * 4 + kk], bfr[j], acc[j]);
     }
+  if (E.part_rows) {
+    // row-major partials [slice][M][N], 64 rows at a time through LDS (the A
+    // slice has been consumed), each row's 128 features one 512-byte store
+    float* const st = (float*)as;
+    float* const dst = E.part + (int64_t)slice * M * N;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      __syncthreads();
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *(float4*)(st + (32 * jj + lr) * RL + 32 * wave + 8 * g + 4 * lh) =
+              make_float4(acc[2 * h + jj][4 * g], acc[2 * h + jj][4 * g + 1], acc[2 * h + jj][4 * g + 2],
+                          acc[2 * h + jj][4 * g + 3]);
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = tid / 32 + 8 * i, m = m0 + 64 * h + row, n = n0 + 4 * (tid % 32);
+        if (m < M && n < N) *(float4*)(dst + (int64_t)m * N + n) = *(const float4*)(st + row * RL + 4 * (tid % 32));
+      }
+    }
+    return;
+  }
   // granules [slice][tile][feature block = wave][row block j][g][lane]: lane l
   // holds row 32 j + l % 32, features 32 w + 8 g + 4 (l / 32) + 0..3
   float4* dst = (float4*)E.part + ((((int64_t)slice * tiles + tile) * 4 + wave) * 16) * 64 + lane;
@@ -1007,11 +1110,10 @@ hipError_t pack_weight(hipStream_t s, const void* W, int N, int K, void* out) {
 // slices of KT k-tiles (K = 64 ks KT), then gemm_reduce_kernel.  KT is chosen
 // by a small cost model: one memory round trip per workgroup plus the bytes
 // of W and A over the bandwidth the workgroups can draw, plus the partials'
-// write and read-back when ks > 1.  Returns false when the shape does not
-// take this path (M > 256, K % 64, no partial buffer, N % 4).
-template <int MODE, bool H16>
-bool launch_stream(hipStream_t s, const bf16* A, const bf16* W, int M, int N, int K, const Epi& E0, hipError_t* err) {
-  if (M > 256 || K % 64 || (N & 3) || M < 1) return false;
+// write and read-back when ks > 1.  0 when the shape does not take this path
+// (M > 256, K % 64, no partial buffer, N % 4).
+static int stream_pick_kt(int M, int N, int K, const Epi& E0) {
+  if (M > 256 || K % 64 || (N & 3) || M < 1) return 0;
   const int KT64 = K / 64;
   const int64_t tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
   const double w_bytes = 2.0 * N * K, a_bytes = 2.0 * M * K * ((N + 127) / 128);
@@ -1032,9 +1134,29 @@ bool launch_stream(hipStream_t s, const bf16* A, const bf16* W, int M, int N, in
       best_kt = kt;
     }
   }
+  return best_kt;
+}
+
+// the reduction pass also runs the LayerNorm of the updated rows (residual
+// modes, a workgroup of N / 4 threads per row, at most 8 waves)
+static bool ln_fusable(int M, int N, int K, const Epi& E) {
+  if (!E.ln_out || (E.mode != EPI_RESID && E.mode != EPI_GATE_RESID)) return false;
+  if (N % 256 || N > 2048 || E.ln_form < 0 || E.ln_form > 2) return false;
+  return stream_pick_kt(M, N, K, E) > 0;
+}
+
+bool gemm_fuses_ln(int M, int N, int K, const Epi& E) { return ln_fusable(M, N, K, E); }
+
+template <int MODE, bool H16>
+bool launch_stream(hipStream_t s, const bf16* A, const bf16* W, int M, int N, int K, const Epi& E0, hipError_t* err) {
+  const int best_kt = stream_pick_kt(M, N, K, E0);
   if (!best_kt) return false;
+  const int KT64 = K / 64;
+  const int64_t tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
   Epi E = E0;
   E.ksplit = KT64 / best_kt;
+  E.part_rows = 0;
+  if constexpr (MODE == EPI_RESID || MODE == EPI_GATE_RESID) E.part_rows = ln_fusable(M, N, K, E0) ? 1 : 0;
   switch (best_kt) {
     case 1: *err = launch_wstream<1, H16>(s, A, W, M, N, K, E); break;
     case 2: *err = launch_wstream<2, H16>(s, A, W, M, N, K, E); break;
@@ -1046,6 +1168,19 @@ bool launch_stream(hipStream_t s, const bf16* A, const bf16* W, int M, int N, in
     default: *err = launch_wstream<8, H16>(s, A, W, M, N, K, E); break;
   }
   if (*err == hipSuccess) {
+    if constexpr (MODE == EPI_RESID || MODE == EPI_GATE_RESID) {
+      if (E.part_rows) {
+        const unsigned nt = (unsigned)(N / 4);
+        if (E.ln_form == 1)
+          gemm_reduce_ln_kernel<MODE, f16, false><<<(unsigned)M, nt, 0, s>>>(M, N, E);
+        else if (E.ln_form == 2)
+          gemm_reduce_ln_kernel<MODE, bf16, true><<<(unsigned)M, nt, 0, s>>>(M, N, E);
+        else
+          gemm_reduce_ln_kernel<MODE, bf16, false><<<(unsigned)M, nt, 0, s>>>(M, N, E);
+        *err = hipGetLastError();
+        return true;
+      }
+    }
     gemm_reduce_kernel<MODE><<<(unsigned)(tiles * 8), 256, 0, s>>>(M, N, E);
     *err = hipGetLastError();
   }

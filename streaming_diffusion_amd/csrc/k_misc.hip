@@ -5,6 +5,7 @@
 #include <cmath>
 
 #include "kernels.h"
+#include "ln_row.h"
 
 namespace sdk {
 
@@ -137,40 +138,6 @@ hipError_t patchify(hipStream_t s, bool bf, const RowTable* rt, int R, const flo
 // store four at a time.
 constexpr int LN_MAXV = 20;     // largest NV: d up to 5120
 
-template <typename T>
-SD_DEV void store4(T* p, const float* o);
-template <>
-SD_DEV void store4<float>(float* p, const float* o) { *(float4*)p = make_float4(o[0], o[1], o[2], o[3]); }
-template <>
-SD_DEV void store4<bf16>(bf16* p, const float* o) {
-  bf16x4 v;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) v[q] = (bf16)o[q];
-  *(bf16x4*)p = v;
-}
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-template <>
-SD_DEV void store4<f16>(f16* p, const float* o) {
-  f16x4 v;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) v[q] = (f16)o[q];
-  *(f16x4*)p = v;
-}
-SD_DEV void load4(const float* p, float* o) {
-  const float4 v = *(const float4*)p;
-  o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
-}
-SD_DEV void load4(const bf16* p, float* o) {
-  const bf16x4 v = *(const bf16x4*)p;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) o[q] = (float)v[q];
-}
-SD_DEV void load4(const f16* p, float* o) {
-  const f16x4 v = *(const f16x4*)p;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) o[q] = (float)v[q];
-}
-
 // SPLIT (bf16): the row of 2d outputs holds hi = bf16(y) in [0, d) and
 // lo = bf16(y - hi) in [d, 2d), so hi + lo carries y to about 16 bits; a GEMM
 // over K = 2d against the weights stored twice ([W | W]) then sees y itself.
@@ -254,46 +221,10 @@ __global__ __launch_bounds__(512) void ln_mod_row_kernel(const float* __restrict
   const float4 v = ((const float4*)(x + (int64_t)row * d))[j];
   const float* mr = mod ? mod + (int64_t)(row / L) * six_d : nullptr;
   float sh[4] = {0.f, 0.f, 0.f, 0.f}, sc[4] = {0.f, 0.f, 0.f, 0.f};
-  if (mr) {
-    load4(mr + shift_off + 4 * j, sh);
-    load4(mr + scale_off + 4 * j, sc);
-    if (blk) {
-      float bs[4], bc[4];
-      load4(blk + shift_off + 4 * j, bs);
-      load4(blk + scale_off + 4 * j, bc);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        sh[q] += bs[q];
-        sc[q] += bc[q];
-      }
-    }
-  }
-  const float s1 = wave_sum((v.x + v.y) + (v.z + v.w));
-  if (lane == 0) red[0][wave] = s1;
-  __syncthreads();
-  float tot = 0.f;
-  for (int w = 0; w < nw; ++w) tot += red[0][w];
-  const float mu = tot / (float)d;
-  const float a0 = v.x - mu, a1 = v.y - mu, a2 = v.z - mu, a3 = v.w - mu;
-  const float s2 = wave_sum((a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3));
-  if (lane == 0) red[1][wave] = s2;
-  __syncthreads();
-  float sq = 0.f;
-  for (int w = 0; w < nw; ++w) sq += red[1][w];
-  const float rstd = 1.0f / sqrtf(sq / (float)d + eps);
-  float o[4] = {a0 * rstd, a1 * rstd, a2 * rstd, a3 * rstd};
-  if (mr) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) o[q] = o[q] * (1.0f + sc[q]) + sh[q];
-  }
-  T* orow = out + (int64_t)row * (SPLIT ? 2 * d : d);
-  store4<T>(orow + 4 * j, o);
-  if constexpr (SPLIT) {
-    float lo[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) lo[q] = o[q] - (float)(T)o[q];
-    store4<T>(orow + d + 4 * j, lo);
-  }
+  if (mr) ln_row_mod(mr, blk, shift_off, scale_off, j, sh, sc);
+  float o[4];
+  ln_row(v, d, eps, mr != nullptr, sh, sc, red, nw, lane, wave, o);
+  ln_row_store<T, SPLIT>(out + (int64_t)row * (SPLIT ? 2 * d : d), d, j, o);
 }
 
 void rope_table_fill(float2* out, int npos, int width, double base) {

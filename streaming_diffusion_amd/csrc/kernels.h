@@ -76,6 +76,10 @@ hipError_t sink_score(hipStream_t s, const float* x, double* partial, int L, int
 hipError_t gemm(hipStream_t s, bool bf, const void* A, const void* W, int M, int N, int K, const Epi& E);
 // bf16 matrix-core path of gemm() (K a multiple of 8).
 hipError_t gemm_mfma(hipStream_t s, const void* A, const void* W, int M, int N, int K, const Epi& E);
+// Whether gemm_mfma / gemm_mfma_f16 with these arguments runs the LayerNorm
+// of E.ln_out itself (the few-row path, residual modes, row width a multiple
+// of 256 up to 4096); when false the caller runs ln_mod after the GEMM.
+bool gemm_fuses_ln(int M, int N, int K, const Epi& E);
 // The same with fp16 operands A and W (bias stays bf16); EPI_F32 and EPI_RESID.
 hipError_t gemm_mfma_f16(hipStream_t s, const void* A, const void* W, int M, int N, int K, const Epi& E);
 // A weight W [N][K] (16-bit elements, K a multiple of 64) rearranged for the

@@ -158,8 +158,29 @@ sd_status sd_k_gemm_epi(const void* A, const void* W, int32_t M, int32_t N, int3
     if (K % 64) return SD_ERR_SHAPE;
     E.wpack = e->wpack;
   }
-  const hipError_t r = e->f16 ? sdk::gemm_mfma_f16((hipStream_t)stream, A, W, M, N, K, E)
-                             : sdk::gemm_mfma((hipStream_t)stream, A, W, M, N, K, E);
+  if (e->ln_out) {
+    if (e->mode != SD_EPI_GATE_RESID && e->mode != SD_EPI_RESID) return SD_ERR_ARG;
+    if (e->ln_form != SD_LN_PLAIN && e->ln_form != SD_LN_F16 && e->ln_form != SD_LN_SPLIT) return SD_ERR_ARG;
+    if (e->ln_form == SD_LN_F16 && e->ln_mod) return SD_ERR_ARG;
+    if (N % 4 || N > 5120) return SD_ERR_SHAPE;
+    if (e->ln_mod && (e->ln_shift_off < 0 || e->ln_scale_off < 0 || e->ln_shift_off % 4 || e->ln_scale_off % 4 ||
+                      e->ln_six_d % 4 || e->ln_shift_off + N > e->ln_six_d || e->ln_scale_off + N > e->ln_six_d))
+      return SD_ERR_SHAPE;
+    E.ln_out = e->ln_out;
+    E.ln_mod = e->ln_mod;
+    E.ln_blk = e->ln_mod ? e->ln_blk : nullptr;
+    E.ln_shift = e->ln_shift_off;
+    E.ln_scale = e->ln_scale_off;
+    E.ln_six = e->ln_mod ? e->ln_six_d : 4;
+    E.ln_form = e->ln_form;
+    E.ln_eps = 1e-6f;
+  }
+  const bool fused = E.ln_out && sdk::gemm_fuses_ln(M, N, K, E);
+  hipError_t r = e->f16 ? sdk::gemm_mfma_f16((hipStream_t)stream, A, W, M, N, K, E)
+                        : sdk::gemm_mfma((hipStream_t)stream, A, W, M, N, K, E);
+  if (r == hipSuccess && E.ln_out && !fused)
+    r = sdk::ln_mod((hipStream_t)stream, true, E.resid, E.ln_out, M, N, E.L, E.ln_mod, E.ln_blk, E.ln_shift,
+                    E.ln_scale, E.ln_six, E.ln_eps, E.ln_form);
   return r == hipSuccess ? SD_OK : SD_ERR_HIP;
 }
 

@@ -352,6 +352,26 @@ Epi epi_base(const sd_stream* s, int mode) {
   return E;
 }
 
+// Ask the residual GEMM described by E to also write the LayerNorm that
+// reads the residual next (into xm: form, modulation mod / blk at shift /
+// scale of six).  True when the GEMM's launch does it in its reduction pass
+// (few rows, bf16); otherwise the caller runs the LayerNorm itself.
+static bool fuse_ln(const sd_stream* s, Epi& E, int M, int N, int K, const float* mod, const void* blk, int shift,
+                    int scale, int six, int form) {
+  if (!s->bf) return false;
+  E.ln_out = s->xm;
+  E.ln_mod = mod;
+  E.ln_blk = mod ? blk : nullptr;
+  E.ln_shift = shift;
+  E.ln_scale = scale;
+  E.ln_six = mod ? six : 4;
+  E.ln_form = form;
+  E.ln_eps = 1e-6f;
+  if (sdk::gemm_fuses_ln(M, N, K, E)) return true;
+  E.ln_out = nullptr;
+  return false;
+}
+
 // Start timing a launch of `kind` (returns -1 when that kind is not profiled).
 int prof_begin(sd_stream* s, int kind) {
   if (!(s->prof_mask & (1u << kind))) return -1;
@@ -760,10 +780,16 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, const StepDyn* dd
   // key range of cross-frame batch attention)
   const int64_t own_stride = (int64_t)H * L * hd;
   const int64_t kv_hs = (int64_t)R * L * hd;
+  // set when the residual GEMM before a LayerNorm already wrote its output
+  // into xm (fuse_ln)
+  bool ln_ready = false;
   for (int b = 0; b < s->nb; ++b) {
     const void* blk = P(s->w.blk_mod, (int64_t)b * 6 * d, es);
     // self-attention
-    PROF(SD_PROF_LN, 0.0, (4.0 + es) * M * d, sdk::ln_mod(st, bf, s->resid, s->xm, M, d, L, s->mod, blk, 0, d, 6 * d, 1e-6f));
+    if (!ln_ready)
+      PROF(SD_PROF_LN, 0.0, (4.0 + es) * M * d,
+           sdk::ln_mod(st, bf, s->resid, s->xm, M, d, L, s->mod, blk, 0, d, 6 * d, 1e-6f));
+    ln_ready = false;
     {
       Epi E = epi_base(s, EPI_QKV);
       E.bias = P(s->w.qkv_b, (int64_t)b * 3 * d, es);
@@ -873,13 +899,21 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, const StepDyn* dd
       E.blk = blk;
       E.gate_off = 2 * d;
       E.wpack = packed_at(s->wp_o, b, d, d);
-      PROF(SD_PROF_GEMM_O, gflop(M, d, d), gbytes(M, d, d, es, 8),
+      // the LayerNorm after it: the cross-attention input (fp16 when folded),
+      // or the feed-forward one when there is no prompt
+      if (c.ctx_len > 0)
+        ln_ready = fuse_ln(s, E, M, d, d, nullptr, nullptr, 0, 0, 6 * d, s->fold ? sdk::LN_F16 : sdk::LN_PLAIN);
+      else
+        ln_ready = fuse_ln(s, E, M, d, d, s->mod, blk, 3 * d, 4 * d, 6 * d, sdk::LN_PLAIN);
+      PROF(SD_PROF_GEMM_O, gflop(M, d, d), gbytes(M, d, d, es, 8) + (ln_ready ? (double)M * d * es : 0.0),
            sdk::gemm(st, bf, s->ao, P(s->w.o_w, (int64_t)b * d * d, es), M, d, d, E));
     }
     // cross-attention to the pre-computed prompt K/V
     if (c.ctx_len > 0 && s->fold) {
-      PROF(SD_PROF_LN, 0.0, (4.0 + es) * M * d,
-           sdk::ln_mod(st, bf, s->resid, s->xm, M, d, L, nullptr, nullptr, 0, 0, 6 * d, 1e-6f, sdk::LN_F16));
+      if (!ln_ready)
+        PROF(SD_PROF_LN, 0.0, (4.0 + es) * M * d,
+             sdk::ln_mod(st, bf, s->resid, s->xm, M, d, L, nullptr, nullptr, 0, 0, 6 * d, 1e-6f, sdk::LN_F16));
+      ln_ready = false;
       const int ncol = H * s->ctx8;
       float* sc = (float*)s->hid;
       f16* pc = (f16*)((char*)s->hid + (size_t)M * ncol * 4);
@@ -902,13 +936,17 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, const StepDyn* dd
           E.bias = P(s->w.co_b, (int64_t)b * d, es);
           E.resid = s->resid + t0 * d;
           E.wpack = packed_at(s->wp_fo, (int)bc, d, ncol);
-          PROF(SD_PROF_GEMM_CROSS, gflop(Mp, d, ncol), gbytes(Mp, d, ncol, es, 8),
+          // one context: the feed-forward LayerNorm of every row follows
+          if (nneg == 0) ln_ready = fuse_ln(s, E, (int)Mp, d, ncol, s->mod, blk, 3 * d, 4 * d, 6 * d, sdk::LN_PLAIN);
+          PROF(SD_PROF_GEMM_CROSS, gflop(Mp, d, ncol), gbytes(Mp, d, ncol, es, 8) + (ln_ready ? (double)Mp * d * es : 0.0),
                sdk::gemm_mfma_f16(st, pc + t0 * ncol, P(s->fold_o, bc * d * ncol, es), (int)Mp, d, ncol, E));
         }
       }
     } else if (c.ctx_len > 0) {
-      PROF(SD_PROF_LN, 0.0, (4.0 + es) * M * d,
-           sdk::ln_mod(st, bf, s->resid, s->xm, M, d, L, nullptr, nullptr, 0, 0, 6 * d, 1e-6f));
+      if (!ln_ready)
+        PROF(SD_PROF_LN, 0.0, (4.0 + es) * M * d,
+             sdk::ln_mod(st, bf, s->resid, s->xm, M, d, L, nullptr, nullptr, 0, 0, 6 * d, 1e-6f));
+      ln_ready = false;
       {
         Epi E = epi_base(s, EPI_QKV);
         E.bias = P(s->w.cq_b, (int64_t)b * d, es);
@@ -948,13 +986,16 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, const StepDyn* dd
         E.bias = P(s->w.co_b, (int64_t)b * d, es);
         E.resid = s->resid;
         E.wpack = packed_at(s->wp_co, b, d, d);
-        PROF(SD_PROF_GEMM_CROSS, gflop(M, d, d), gbytes(M, d, d, es, 8),
+        ln_ready = fuse_ln(s, E, M, d, d, s->mod, blk, 3 * d, 4 * d, 6 * d, sdk::LN_PLAIN);
+        PROF(SD_PROF_GEMM_CROSS, gflop(M, d, d), gbytes(M, d, d, es, 8) + (ln_ready ? (double)M * d * es : 0.0),
              sdk::gemm(st, bf, s->ao, P(s->w.co_w, (int64_t)b * d * d, es), M, d, d, E));
       }
     }
     // feed-forward
-    PROF(SD_PROF_LN, 0.0, (4.0 + es) * M * d,
-         sdk::ln_mod(st, bf, s->resid, s->xm, M, d, L, s->mod, blk, 3 * d, 4 * d, 6 * d, 1e-6f));
+    if (!ln_ready)
+      PROF(SD_PROF_LN, 0.0, (4.0 + es) * M * d,
+           sdk::ln_mod(st, bf, s->resid, s->xm, M, d, L, s->mod, blk, 3 * d, 4 * d, 6 * d, 1e-6f));
+    ln_ready = false;
     {
       Epi E = epi_base(s, EPI_GELU);
       E.bias = P(s->w.f1_b, (int64_t)b * s->F, es);
@@ -972,7 +1013,16 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, const StepDyn* dd
       E.blk = blk;
       E.gate_off = 5 * d;
       E.wpack = packed_at(s->wp_f2, b, d, s->F);
-      PROF(SD_PROF_GEMM_FFN2, gflop(M, d, s->F), gbytes(M, d, s->F, es, 8),
+      // the next block's attention LayerNorm, or after the last block the
+      // final layer's (hi / lo pairs in bf16)
+      if (b + 1 < s->nb)
+        ln_ready = fuse_ln(s, E, M, d, s->F, s->mod, P(s->w.blk_mod, (int64_t)(b + 1) * 6 * d, es), 0, d, 6 * d,
+                           sdk::LN_PLAIN);
+      else
+        ln_ready = fuse_ln(s, E, M, d, s->F, s->fmod, nullptr, 0, d, 2 * d, sdk::LN_SPLIT);
+      // (with the LayerNorm fused: its output too, hi / lo pairs after the last block)
+      PROF(SD_PROF_GEMM_FFN2, gflop(M, d, s->F),
+           gbytes(M, d, s->F, es, 8) + (ln_ready ? (double)M * d * es * (b + 1 < s->nb ? 1 : 2) : 0.0),
            sdk::gemm(st, bf, s->hid, P(s->w.f2_w, (int64_t)b * d * s->F, es), M, d, s->F, E));
     }
   }
@@ -997,9 +1047,10 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, const StepDyn* dd
   // ---- final layer and unpatchify -> eps_c
   // (bf16: the normalised rows as hi + lo pairs against the doubled head, K = 2d)
   const int KH = bf ? 2 * d : d;
-  PROF(SD_PROF_LN, 0.0, (4.0 + es * KH / d) * M * d,
-       sdk::ln_mod(st, bf, s->resid, s->xm, M, d, L, s->fmod, nullptr, 0, d, 2 * d, 1e-6f,
-                   bf ? sdk::LN_SPLIT : sdk::LN_PLAIN));
+  if (!ln_ready)
+    PROF(SD_PROF_LN, 0.0, (4.0 + es * KH / d) * M * d,
+         sdk::ln_mod(st, bf, s->resid, s->xm, M, d, L, s->fmod, nullptr, 0, d, 2 * d, 1e-6f,
+                     bf ? sdk::LN_SPLIT : sdk::LN_PLAIN));
   {
     Epi E = epi_base(s, EPI_HEAD);
     E.bias = s->w.head_b;

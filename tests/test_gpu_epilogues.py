@@ -457,3 +457,59 @@ def test_split_k_qkv_rope_and_fp16(lib):
     e.t0[0], e.t0[1] = 3, 1020
     run(lib, A, W, M, N, K, e)
     assert torch.equal(q2, q) and torch.equal(k2, k) and torch.equal(vt2, vt)
+
+
+@pytest.mark.parametrize("M,N,K,mode,form,with_blk", [
+    (128, 1536, 8960, "gate", sdlib.SD_LN_PLAIN, True),    # FFN2 -> next block's attention LayerNorm
+    (256, 1536, 1536, "gate", sdlib.SD_LN_SPLIT, False),   # last FFN2 -> the head's hi / lo input
+    (128, 1536, 1536, "gate", sdlib.SD_LN_F16, False),     # O-projection -> cross-attention input
+    (128, 1536, 960, "resid", sdlib.SD_LN_PLAIN, True),    # cross-attention out -> feed-forward LayerNorm
+    (100, 1024, 1536, "resid", sdlib.SD_LN_PLAIN, True),   # ragged rows
+    (128, 520, 640, "gate", sdlib.SD_LN_PLAIN, True),      # width not a multiple of 256: a separate pass
+])
+def test_residual_gemm_with_layernorm(lib, M, N, K, mode, form, with_blk):
+    """A residual GEMM that also writes the LayerNorm of the updated rows
+    (sd_gemm_epi.ln_out; on the few-row path the reduction pass does both in
+    one launch) gives bit for bit the residual and the LayerNorm output of
+    the GEMM followed by sd_k_ln_mod."""
+    print(f"gemm + LN M={M} N={N} K={K} {mode} form={form}", flush=True)
+    rng = np.random.default_rng(M + N + K)
+    A = to_dev(rng.standard_normal((M, K)), torch.bfloat16)
+    W = to_dev(0.02 * rng.standard_normal((N, K)), torch.bfloat16)
+    b = to_dev(0.1 * rng.standard_normal(N), torch.bfloat16)
+    Lr = M // 2 if M % 2 == 0 else M
+    rows = M // Lr
+    c0 = (3 * rng.standard_normal((M, N)) + 0.5).astype(np.float32)
+    gmod = to_dev(0.3 * rng.standard_normal((rows, 6 * N)), torch.float32)
+    gblk = to_dev(0.02 * rng.standard_normal(6 * N), torch.bfloat16)
+    lmod = to_dev(0.3 * rng.standard_normal((rows, 6 * N)), torch.float32) if form != sdlib.SD_LN_F16 else None
+    lblk = to_dev(0.02 * rng.standard_normal(6 * N), torch.bfloat16) if with_blk else None
+    ws, wsp, wsb = split_ws()
+    width = 2 * N if form == sdlib.SD_LN_SPLIT else N
+    odt = torch.float16 if form == sdlib.SD_LN_F16 else torch.bfloat16
+
+    def epi(resid, ln_out):
+        e = sdlib.sd_gemm_epi(mode=sdlib.SD_EPI_GATE_RESID if mode == "gate" else sdlib.SD_EPI_RESID,
+                              bias=b.data_ptr(), resid=resid.data_ptr(), L=Lr, workspace=wsp, workspace_bytes=wsb)
+        if mode == "gate":
+            e.mod, e.blk, e.gate_off, e.six_d = gmod.data_ptr(), gblk.data_ptr(), 5 * N, 6 * N
+        if ln_out is not None:
+            e.ln_out, e.ln_form = ln_out.data_ptr(), form
+            if lmod is not None:
+                e.ln_mod, e.ln_shift_off, e.ln_scale_off, e.ln_six_d = lmod.data_ptr(), 3 * N, 4 * N, 6 * N
+                e.ln_blk = lblk.data_ptr() if lblk is not None else None
+        return e
+
+    r1 = to_dev(c0, torch.float32)
+    y1 = torch.full((M, width), 7.0, dtype=odt, device=device())
+    run(lib, A, W, M, N, K, epi(r1, y1))
+    r2 = to_dev(c0, torch.float32)
+    y2 = torch.full((M, width), 7.0, dtype=odt, device=device())
+    run(lib, A, W, M, N, K, epi(r2, None))
+    call(lib.sd_k_ln_mod(sdlib.SD_DTYPE_BF16, r2.data_ptr(), y2.data_ptr(), M, N, Lr,
+                         lmod.data_ptr() if lmod is not None else None,
+                         lblk.data_ptr() if lblk is not None else None, 3 * N, 4 * N, 6 * N, form, stream_ptr()))
+    torch.cuda.synchronize()
+    assert torch.equal(r1, r2), "residual differs"
+    assert torch.equal(y1, y2), "LayerNorm output differs"
+    assert not torch.equal(r1, to_dev(c0, torch.float32))
