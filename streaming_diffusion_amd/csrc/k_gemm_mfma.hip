@@ -1110,12 +1110,21 @@ hipError_t pack_weight(hipStream_t s, const void* W, int N, int K, void* out) {
 // slices of KT k-tiles (K = 64 ks KT), then gemm_reduce_kernel.  KT is chosen
 // by a small cost model: one memory round trip per workgroup plus the bytes
 // of W and A over the bandwidth the workgroups can draw, plus the partials'
-// write and read-back when ks > 1.  0 when the shape does not take this path
-// (M > 256, K % 64, no partial buffer, N % 4).
+// write and read-back when ks > 1.  Up to 2048 rows it also takes products
+// whose 128 x 128 tiles would occupy at most half of the CUs (the image
+// DiT's N = 768 GEMMs: 96 tiles), with the matrix-core time of a slice in the
+// model.  0 when the shape does not take this path (more rows, K % 64, no
+// partial buffer, N % 4).
 static int stream_pick_kt(int M, int N, int K, const Epi& E0) {
-  if (M > 256 || K % 64 || (N & 3) || M < 1) return 0;
+  if (M > 2048 || K % 64 || (N & 3) || M < 1) return 0;
   const int KT64 = K / 64;
   const int64_t tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+  const bool few_rows = M <= 256;
+  // above 256 rows only the row-major epilogues (the scatters through the
+  // reduction's LDS strips measured slower there than the one-pass tile)
+  if (!few_rows && (tiles * 2 > device_cus() || E0.mode == EPI_QKV || E0.mode == EPI_CTXKV ||
+                    E0.mode == EPI_HEAD || E0.mode == EPI_PATCH))
+    return 0;
   const double w_bytes = 2.0 * N * K, a_bytes = 2.0 * M * K * ((N + 127) / 128);
   int best_kt = 0;
   double best_t = 1e30;
@@ -1128,6 +1137,7 @@ static int stream_pick_kt(int M, int N, int K, const Epi& E0) {
     const double rounds = (double)((wgs + 255) / 256);
     const double bw = std::min(8.0e12 * 0.8, (double)std::min<int64_t>(wgs, 256) * 40.0e9);   // bytes/s
     double t = rounds * 2.0e-6 + (w_bytes + a_bytes) / bw;
+    if (!few_rows) t += rounds * kt * (64.0 * 128 * 128 * 2) / 4.0e12;     // a slice's products per CU
     if (ks > 1) t += 3.0e-6 + 2.0 * ks * M * N * 4.0 / 10.0e12;
     if (t < best_t * 0.999) {
       best_t = t;

@@ -242,9 +242,14 @@ size_t carve(sd_stream* s, char* base) {
       s->fold_c = cv.take<float>((size_t)s->nb * nctx * ncol * 4);
     }
   }
-  if (s->bf && s->L <= 256) {
-    s->gpart_cap = (int64_t)16 << 20;          // 64 MiB of fp32 partials
+  // fp32 partials of the products split over K: every GEMM of a forward of
+  // at most 256 tokens, and those of at most 2048 tokens whose tiles would
+  // leave most of the chip idle (rows of up to 2048 tokens)
+  if (s->bf && s->L <= 2048) {
+    s->gpart_cap = (int64_t)16 << 20;          // 64 MiB
     s->gpart = cv.take<float>((size_t)s->gpart_cap * 4);
+  }
+  if (s->bf && s->L <= 256) {
     const int d = s->d, F = s->F, nb = s->nb;
     auto take_packed = [&](int N, int K, int count) -> void* {
       return K % 64 ? nullptr : cv.take<void>(packed_bytes(N, K) * count);

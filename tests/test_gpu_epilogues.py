@@ -290,10 +290,12 @@ def split_ws(nbytes=64 << 20):
 
 
 @pytest.mark.parametrize("M,N,K", [(128, 4608, 1536), (256, 8960, 1536), (128, 1536, 8960), (256, 1536, 1536),
-                                   (96, 200, 640)])
+                                   (96, 200, 640), (2048, 768, 3072), (2048, 768, 768), (1000, 760, 1536)])
 def test_split_k_epilogues_exact(lib, M, N, K):
     """Below the knee (M <= 256 rows: the sub-knee video diagnostic's 128 or
-    256 tokens per forward) the product is split over K into fp32 partials
+    256 tokens per forward; and up to 2048 rows when 128 x 128 tiles would
+    leave most CUs idle, the image DiT's N = 768 GEMMs) the product is split
+    over K into fp32 partials
     that a second pass sums in slice order before the epilogue; on exact
     operands the sums are exact, so F32 (also into rows not 16-byte
     aligned), RESID and the gated residual are bit for bit the integer
