@@ -87,6 +87,14 @@ typedef struct {
   const float* ln_mod;
   const void* ln_blk;
   int32_t ln_shift_off, ln_scale_off, ln_six_d, ln_form;
+  void* sm_out;                /* optional, F32 without bias: fp16 [M][N] softmax over each of the
+                                  sm_heads groups of sm_cp (<= 128) columns of C + sm_bias (fp32
+                                  [N]), N = sm_heads * sm_cp (the folded cross-attention's
+                                  probabilities); on the few-row path the reduction pass writes it
+                                  and out is not written, otherwise C goes to out and a softmax
+                                  pass follows.  NULL: none. */
+  const float* sm_bias;
+  int32_t sm_heads, sm_cp;
 } sd_gemm_epi;
 
 /* One bf16 GEMM with the epilogue e->mode, on the kernels and launch

@@ -103,7 +103,8 @@ class sd_gemm_epi(C.Structure):
                 ("f16", C.c_int32), ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
                 ("wpack", C.c_void_p), ("ln_out", C.c_void_p), ("ln_mod", C.c_void_p), ("ln_blk", C.c_void_p),
                 ("ln_shift_off", C.c_int32), ("ln_scale_off", C.c_int32), ("ln_six_d", C.c_int32),
-                ("ln_form", C.c_int32)]
+                ("ln_form", C.c_int32), ("sm_out", C.c_void_p), ("sm_bias", C.c_void_p), ("sm_heads", C.c_int32),
+                ("sm_cp", C.c_int32)]
 
 
 SD_LN_PLAIN, SD_LN_F16, SD_LN_SPLIT = 0, 1, 2

@@ -148,4 +148,11 @@ struct Epi {
   const void* ln_blk;   // [ln_six] block table (null: none)
   int ln_shift, ln_scale, ln_six, ln_form;
   float ln_eps;
+  // EPI_F32 on the few-row path: when sm_out is set the reduction pass writes
+  // softmax over each of the sm_heads groups of sm_cp columns of (C + sm_bias)
+  // to sm_out in fp16 instead of C itself (the folded cross-attention's
+  // probabilities); gemm_fuses_softmax() says whether a call does
+  f16* sm_out;
+  const float* sm_bias;
+  int sm_heads, sm_cp;
 };

@@ -929,6 +929,67 @@ __global__ __launch_bounds__(512) void gemm_reduce_ln_kernel(int M, int N, Epi E
   ln_row_store<T, SPLIT>((T*)E.ln_out + (int64_t)m * (SPLIT ? 2 * N : N), N, j, o);
 }
 
+// The reduction pass of the folded cross-attention's score product fused
+// with its grouped softmax: 16 lanes per (row, group of sm_cp columns), each
+// lane summing the K slices (row-major partials, slice order, as the other
+// reduction) of columns l, l + 16, ... and then the softmax of the folded
+// attention (max, exponentials, sum, scale) on them, written in fp16; the
+// scores themselves are not stored.
+__global__ __launch_bounds__(256) void gemm_reduce_softmax_kernel(int M, int N, Epi E) {
+  const int64_t g = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int l = threadIdx.x & 15;
+  if (g >= (int64_t)M * E.sm_heads) return;        // whole 16-lane groups leave together
+  const int64_t m = g / E.sm_heads;
+  const int h = (int)(g - m * E.sm_heads), Cp = E.sm_cp;
+  const float* const src = E.part + m * N + (int64_t)h * Cp;
+  const int64_t slice_st = (int64_t)M * N;
+  // four slices' loads in flight at a time, each sum in slice order
+  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int sl = 0;
+  for (; sl + 4 <= E.ksplit; sl += 4) {
+    float t[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t[u][i] = l + 16 * i < Cp ? src[(sl + u) * slice_st + l + 16 * i] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] += t[u][i];
+  }
+  for (; sl < E.ksplit; ++sl) {
+    float t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = l + 16 * i < Cp ? src[sl * slice_st + l + 16 * i] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] += t[i];
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int j = l + 16 * i;
+    v[i] = j < Cp ? v[i] + E.sm_bias[h * Cp + j] : -INFINITY;
+    mx = fmaxf(mx, v[i]);
+  }
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 16));
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[i] = l + 16 * i < Cp ? __expf(v[i] - mx) : 0.f;
+    sum += v[i];
+  }
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 16);
+  const float inv = 1.0f / sum;
+  f16* const out = E.sm_out + m * N + (int64_t)h * Cp;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int j = l + 16 * i;
+    if (j < Cp) out[j] = (f16)(v[i] * inv);
+  }
+}
+
 // compute units of the current device (queried once; 256 on MI355X)
 static int device_cus() {
   static int cus = 0;
@@ -1157,6 +1218,16 @@ static bool ln_fusable(int M, int N, int K, const Epi& E) {
 
 bool gemm_fuses_ln(int M, int N, int K, const Epi& E) { return ln_fusable(M, N, K, E); }
 
+// the reduction pass also runs the grouped softmax of the product (F32
+// without a bias, groups of at most 128 columns covering N)
+static bool sm_fusable(int M, int N, int K, const Epi& E) {
+  if (!E.sm_out || E.mode != EPI_F32 || E.bias || E.sm_cp < 1 || E.sm_cp > 128 || E.sm_heads * E.sm_cp != N)
+    return false;
+  return stream_pick_kt(M, N, K, E) > 0;
+}
+
+bool gemm_fuses_softmax(int M, int N, int K, const Epi& E) { return sm_fusable(M, N, K, E); }
+
 template <int MODE, bool H16>
 bool launch_stream(hipStream_t s, const bf16* A, const bf16* W, int M, int N, int K, const Epi& E0, hipError_t* err) {
   const int best_kt = stream_pick_kt(M, N, K, E0);
@@ -1167,6 +1238,7 @@ bool launch_stream(hipStream_t s, const bf16* A, const bf16* W, int M, int N, in
   E.ksplit = KT64 / best_kt;
   E.part_rows = 0;
   if constexpr (MODE == EPI_RESID || MODE == EPI_GATE_RESID) E.part_rows = ln_fusable(M, N, K, E0) ? 1 : 0;
+  if constexpr (MODE == EPI_F32) E.part_rows = sm_fusable(M, N, K, E0) ? 1 : 0;
   switch (best_kt) {
     case 1: *err = launch_wstream<1, H16>(s, A, W, M, N, K, E); break;
     case 2: *err = launch_wstream<2, H16>(s, A, W, M, N, K, E); break;
@@ -1187,6 +1259,14 @@ bool launch_stream(hipStream_t s, const bf16* A, const bf16* W, int M, int N, in
           gemm_reduce_ln_kernel<MODE, bf16, true><<<(unsigned)M, nt, 0, s>>>(M, N, E);
         else
           gemm_reduce_ln_kernel<MODE, bf16, false><<<(unsigned)M, nt, 0, s>>>(M, N, E);
+        *err = hipGetLastError();
+        return true;
+      }
+    }
+    if constexpr (MODE == EPI_F32) {
+      if (E.part_rows) {
+        const int64_t groups = (int64_t)M * E.sm_heads;
+        gemm_reduce_softmax_kernel<<<(unsigned)((groups + 15) / 16), 256, 0, s>>>(M, N, E);
         *err = hipGetLastError();
         return true;
       }

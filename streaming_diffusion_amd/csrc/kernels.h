@@ -80,6 +80,9 @@ hipError_t gemm_mfma(hipStream_t s, const void* A, const void* W, int M, int N, 
 // of E.ln_out itself (the few-row path, residual modes, row width a multiple
 // of 256 up to 4096); when false the caller runs ln_mod after the GEMM.
 bool gemm_fuses_ln(int M, int N, int K, const Epi& E);
+// Whether a call with E.sm_out set writes the grouped softmax itself (the
+// few-row path); when false the caller stores C and runs ctx_softmax.
+bool gemm_fuses_softmax(int M, int N, int K, const Epi& E);
 // The same with fp16 operands A and W (bias stays bf16); EPI_F32 and EPI_RESID.
 hipError_t gemm_mfma_f16(hipStream_t s, const void* A, const void* W, int M, int N, int K, const Epi& E);
 // A weight W [N][K] (16-bit elements, K a multiple of 64) rearranged for the

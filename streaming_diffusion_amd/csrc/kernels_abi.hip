@@ -175,9 +175,24 @@ sd_status sd_k_gemm_epi(const void* A, const void* W, int32_t M, int32_t N, int3
     E.ln_form = e->ln_form;
     E.ln_eps = 1e-6f;
   }
+  if (e->sm_out) {
+    if (e->mode != SD_EPI_F32 || e->bias || !e->sm_bias) return SD_ERR_ARG;
+    if (e->sm_cp < 1 || e->sm_cp > 128 || e->sm_heads < 1 || e->sm_heads * e->sm_cp != N) return SD_ERR_SHAPE;
+    E.sm_out = (f16*)e->sm_out;
+    E.sm_bias = e->sm_bias;
+    E.sm_heads = e->sm_heads;
+    E.sm_cp = e->sm_cp;
+  }
+  const bool sm_fused = E.sm_out && sdk::gemm_fuses_softmax(M, N, K, E);
+  if (E.sm_out && !sm_fused) E.sm_out = nullptr;
   const bool fused = E.ln_out && sdk::gemm_fuses_ln(M, N, K, E);
   hipError_t r = e->f16 ? sdk::gemm_mfma_f16((hipStream_t)stream, A, W, M, N, K, E)
                         : sdk::gemm_mfma((hipStream_t)stream, A, W, M, N, K, E);
+  if (r == hipSuccess && e->sm_out && !sm_fused) {
+    if (E.ldo != N) return SD_ERR_SHAPE;          // the softmax pass reads C densely
+    r = sdk::ctx_softmax((hipStream_t)stream, (const float*)E.out, e->sm_bias, (f16*)e->sm_out, M, e->sm_heads,
+                         e->sm_cp);
+  }
   if (r == hipSuccess && E.ln_out && !fused)
     r = sdk::ln_mod((hipStream_t)stream, true, E.resid, E.ln_out, M, N, E.L, E.ln_mod, E.ln_blk, E.ln_shift,
                     E.ln_scale, E.ln_six, E.ln_eps, E.ln_form);

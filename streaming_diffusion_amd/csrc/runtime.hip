@@ -926,16 +926,25 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, const StepDyn* dd
       for (int part = 0; part < (nneg > 0 ? 2 : 1); ++part) {
         const int64_t t0 = (int64_t)(part == 0 ? 0 : R_pos) * L, Mp = (int64_t)(part == 0 ? R_pos : nneg) * L;
         const int64_t bc = (int64_t)b * nctx + part;
+        bool sm_fused = false;
         {
           Epi E = epi_base(s, EPI_F32);
           E.out = sc + t0 * ncol;
           E.ldo = ncol;
           E.wpack = packed_at(s->wp_fq, (int)bc, ncol, d);
-          PROF(SD_PROF_GEMM_CROSS, gflop(Mp, ncol, d), gbytes(Mp, ncol, d, es, 4),
+          // few rows: the reduction pass writes the probabilities itself
+          E.sm_out = pc + t0 * ncol;
+          E.sm_bias = s->fold_c + bc * ncol;
+          E.sm_heads = H;
+          E.sm_cp = s->ctx8;
+          sm_fused = sdk::gemm_fuses_softmax((int)Mp, ncol, d, E);
+          if (!sm_fused) E.sm_out = nullptr;
+          PROF(SD_PROF_GEMM_CROSS, gflop(Mp, ncol, d), gbytes(Mp, ncol, d, es, sm_fused ? 2 : 4),
                sdk::gemm_mfma_f16(st, P(s->xm, t0 * d, es), P(s->fold_q, bc * ncol * d, es), (int)Mp, ncol, d, E));
         }
-        PROF(SD_PROF_ATTN_CROSS, 4.0 * Mp * ncol, 6.0 * Mp * ncol,
-             sdk::ctx_softmax(st, sc + t0 * ncol, s->fold_c + bc * ncol, pc + t0 * ncol, Mp, H, s->ctx8));
+        if (!sm_fused)
+          PROF(SD_PROF_ATTN_CROSS, 4.0 * Mp * ncol, 6.0 * Mp * ncol,
+               sdk::ctx_softmax(st, sc + t0 * ncol, s->fold_c + bc * ncol, pc + t0 * ncol, Mp, H, s->ctx8));
         {
           Epi E = epi_base(s, EPI_RESID);
           E.bias = P(s->w.co_b, (int64_t)b * d, es);

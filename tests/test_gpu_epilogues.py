@@ -515,3 +515,40 @@ def test_residual_gemm_with_layernorm(lib, M, N, K, mode, form, with_blk):
     assert torch.equal(r1, r2), "residual differs"
     assert torch.equal(y1, y2), "LayerNorm output differs"
     assert not torch.equal(r1, to_dev(c0, torch.float32))
+
+
+@pytest.mark.parametrize("M,H,Cp,K", [(128, 12, 80, 1536), (256, 12, 80, 1536), (96, 4, 40, 640)])
+def test_score_gemm_with_grouped_softmax(lib, M, H, Cp, K):
+    """The folded cross-attention's score product with its grouped softmax in
+    the reduction pass (sd_gemm_epi.sm_out, few rows): bit for bit the
+    probabilities of the product stored in fp32 followed by the softmax pass
+    (taken here by giving the scores a wider row pitch), and within fp16
+    rounding of the softmax of the exact products."""
+    print(f"score gemm + softmax M={M} H={H} Cp={Cp} K={K}", flush=True)
+    N = H * Cp
+    A, W, b, acc = int_operands(M, N, K, 41)
+    acc = acc - b.float().cpu().numpy().astype(np.float64)      # no bias on this product
+    rng = np.random.default_rng(42)
+    c = to_dev(rng.standard_normal(N), torch.float32)
+    ws, wsp, wsb = split_ws()
+    p1 = torch.full((M, N), 7.0, dtype=torch.float16, device=device())
+    sc = torch.full((M, N), 7.0, dtype=torch.float32, device=device())
+    e = sdlib.sd_gemm_epi(mode=sdlib.SD_EPI_F32, out=sc.data_ptr(), ldo=N, workspace=wsp, workspace_bytes=wsb,
+                          sm_out=p1.data_ptr(), sm_bias=c.data_ptr(), sm_heads=H, sm_cp=Cp)
+    run(lib, A, W, M, N, K, e)
+    assert torch.all(sc == 7.0), "fused pass wrote the scores"
+    p2 = torch.full((M, N), 7.0, dtype=torch.float16, device=device())
+    e = sdlib.sd_gemm_epi(mode=sdlib.SD_EPI_F32, out=sc.data_ptr(), ldo=N, workspace=wsp, workspace_bytes=wsb)
+    run(lib, A, W, M, N, K, e)
+    assert np.array_equal(sc.cpu().numpy().astype(np.float64), acc)
+    # the separate softmax pass on the stored scores, through a GEMM whose
+    # output is the same scores but not split (no workspace)
+    e = sdlib.sd_gemm_epi(mode=sdlib.SD_EPI_F32, out=sc.data_ptr(), ldo=N, sm_out=p2.data_ptr(),
+                          sm_bias=c.data_ptr(), sm_heads=H, sm_cp=Cp)
+    run(lib, A, W, M, N, K, e)
+    assert torch.equal(p1, p2), "fused and separate softmax differ"
+    z = (acc + c.cpu().numpy().astype(np.float64)).reshape(M, H, Cp)
+    z = np.exp(z - z.max(axis=-1, keepdims=True))
+    ref = (z / z.sum(axis=-1, keepdims=True)).reshape(M, N)
+    got = p1.float().cpu().numpy()
+    assert np.max(np.abs(got - ref) - 2.0 ** -11 * ref) <= 1e-6
