@@ -21,6 +21,7 @@
 #include <vector>
 
 #include "kernels.h"
+#include "kv_append.h"
 
 namespace sdk {
 
@@ -594,9 +595,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
 // flight together, NS = 0 loops over a.nsplit.  The host guarantees that
 // R * L * H * hd / 8 fits in 31 bits.
 template <int NS>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+SD_DEV void combine_one(const AttnArgs& a, int i) {
   const int c8 = a.hd >> 3, per_tok = (a.H - a.h_full) * c8;
-  const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= a.R * a.L * per_tok) return;
   const int tok = i / per_tok, rem = i - tok * per_tok;
   const int h = a.h_full + rem / c8, e = (rem - (h - a.h_full) * c8) * 8;
@@ -643,6 +643,23 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) ov[j] = (bf16)(acc[j] * inv);
   *(bf16x8*)((bf16*)a.o + ((int64_t)r * a.L + t) * a.d + (int64_t)h * a.hd + e) = ov;
+}
+
+template <int NS>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+  combine_one<NS>(a, blockIdx.x * 256 + threadIdx.x);
+}
+
+// The combine pass and the KV append of the leaving chunk in one launch
+// (both only wait for the attention; the append may overwrite ring entries
+// the attention has just read): workgroups [0, ncomb) combine, the rest
+// append.
+template <int NS>
+__global__ __launch_bounds__(256) void attn_combine_append_kernel(AttnArgs a, KvAppendArgs k, int ncomb) {
+  if ((int)blockIdx.x < ncomb)
+    combine_one<NS>(a, blockIdx.x * 256 + threadIdx.x);
+  else
+    kv_append_chunk(k, (int64_t)(blockIdx.x - ncomb) * 256 + threadIdx.x);
 }
 
 int attention_q_tile(bool bf, int hd) { return !bf ? 64 : 128; }
@@ -738,6 +755,26 @@ hipError_t attention_combine(hipStream_t s, const AttnArgs& a) {
     case 7: attn_combine_kernel<7><<<g, 256, 0, s>>>(a); break;
     case 8: attn_combine_kernel<8><<<g, 256, 0, s>>>(a); break;
     default: attn_combine_kernel<0><<<g, 256, 0, s>>>(a); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t attention_combine_append(hipStream_t s, const AttnArgs& a, const KvAppendArgs& k) {
+  const int64_t n = a.nsplit > 1 && a.h_full < a.H ? (int64_t)a.R * a.L * (a.H - a.h_full) * (a.hd / 8) : 0;
+  const int64_t chunks = 2 * ((int64_t)k.H * k.L * k.hd / 8);
+  if (a.hd % 8 || n > 0x7fffffff) return hipErrorInvalidValue;
+  const int64_t gc = (n + 255) / 256, ga = (chunks + 255) / 256;
+  if (gc + ga == 0) return hipSuccess;
+  const unsigned g = (unsigned)(gc + ga);
+  switch (a.nsplit) {
+    case 2: attn_combine_append_kernel<2><<<g, 256, 0, s>>>(a, k, (int)gc); break;
+    case 3: attn_combine_append_kernel<3><<<g, 256, 0, s>>>(a, k, (int)gc); break;
+    case 4: attn_combine_append_kernel<4><<<g, 256, 0, s>>>(a, k, (int)gc); break;
+    case 5: attn_combine_append_kernel<5><<<g, 256, 0, s>>>(a, k, (int)gc); break;
+    case 6: attn_combine_append_kernel<6><<<g, 256, 0, s>>>(a, k, (int)gc); break;
+    case 7: attn_combine_append_kernel<7><<<g, 256, 0, s>>>(a, k, (int)gc); break;
+    case 8: attn_combine_append_kernel<8><<<g, 256, 0, s>>>(a, k, (int)gc); break;
+    default: attn_combine_append_kernel<0><<<g, 256, 0, s>>>(a, k, (int)gc); break;
   }
   return hipGetLastError();
 }

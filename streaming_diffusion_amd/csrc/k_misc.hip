@@ -5,6 +5,7 @@
 #include <cmath>
 
 #include "kernels.h"
+#include "kv_append.h"
 #include "ln_row.h"
 
 namespace sdk {
@@ -442,39 +443,16 @@ __global__ void kv_append_kernel(const T* __restrict__ kown, const T* __restrict
 
 // bf16 with every token range a multiple of 8 and L <= W: 16-byte chunks (8
 // head-dim elements of one K row, or 8 consecutive tokens of one V^T row), one
-// conditional wrap per chunk.  Chunk i < H*L*hd/8 is a K chunk, the rest V^T.
-__global__ void kv_append_vec_kernel(const bf16* __restrict__ kown, const bf16* __restrict__ vtown, int64_t k_hs,
-                                     int64_t vt_ps, bf16* __restrict__ ringK, bf16* __restrict__ ringVT, int H, int hd,
-                                     int L, int W, int ptr, bf16* __restrict__ sinkK, bf16* __restrict__ sinkVT, int S8,
-                                     int sink_off, int Se, const int* __restrict__ ptr_dev) {
-  if (ptr_dev) ptr = *ptr_dev;
-  const int64_t nk = (int64_t)H * L * (hd / 8);
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= 2 * nk) return;
-  if (i < nk) {
-    const int c = (int)(i % (hd / 8));
-    const int64_t ht = i / (hd / 8);
-    const int h = (int)(ht / L), t = (int)(ht % L);
-    const bf16x8 v = *(const bf16x8*)(kown + h * k_hs + (int64_t)t * hd + c * 8);
-    if (W > 0) {
-      int p = ptr + t;
-      if (p >= W) p -= W;
-      *(bf16x8*)(ringK + ((int64_t)h * W + p) * hd + c * 8) = v;
-    }
-    if (sinkK && t < Se) *(bf16x8*)(sinkK + ((int64_t)h * S8 + sink_off + t) * hd + c * 8) = v;
-  } else {
-    i -= nk;
-    const int tc = (int)(i % (L / 8));
-    const int64_t he = i / (L / 8);          // h * hd + e
-    const int t = tc * 8;
-    const bf16x8 v = *(const bf16x8*)(vtown + he * vt_ps + t);
-    if (W > 0) {
-      int p = ptr + t;
-      if (p >= W) p -= W;
-      *(bf16x8*)(ringVT + he * W + p) = v;
-    }
-    if (sinkVT && t < Se) *(bf16x8*)(sinkVT + he * S8 + sink_off + t) = v;
-  }
+// conditional wrap per chunk (kv_append_chunk).
+__global__ void kv_append_vec_kernel(KvAppendArgs a) {
+  kv_append_chunk(a, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+}
+
+bool kv_append_vec_ok(bool bf, int64_t k_hs, int64_t vt_ps, int H, int hd, int L, int W, int ptr, const void* sinkK,
+                      int S8, int sink_off, int Se) {
+  return bf && (hd % 8) == 0 && (L % 8) == 0 && (W % 8) == 0 && (ptr % 8) == 0 && ptr < (W > 0 ? W : 1) &&
+         (W == 0 || L <= W) && (k_hs % 8) == 0 && (vt_ps % 8) == 0 && k_hs >= (int64_t)L * hd && vt_ps >= L &&
+         (!sinkK || ((S8 % 8) == 0 && (sink_off % 8) == 0 && (Se % 8) == 0));
 }
 
 hipError_t kv_append(hipStream_t s, bool bf, const void* kown, const void* vtown, int64_t k_hs, int64_t vt_ps,
@@ -482,13 +460,11 @@ hipError_t kv_append(hipStream_t s, bool bf, const void* kown, const void* vtown
                      int sink_off, int Se, const int* ptr_dev) {
   const int64_t n = (int64_t)H * L * hd;
   if (k_hs < (int64_t)L * hd || vt_ps < L) return hipErrorInvalidValue;
-  if (bf && (hd % 8) == 0 && (L % 8) == 0 && (W % 8) == 0 && (ptr % 8) == 0 && ptr < (W > 0 ? W : 1) && (W == 0 || L <= W) &&
-      (k_hs % 8) == 0 && (vt_ps % 8) == 0 &&
-      (!sinkK || ((S8 % 8) == 0 && (sink_off % 8) == 0 && (Se % 8) == 0))) {
+  if (kv_append_vec_ok(bf, k_hs, vt_ps, H, hd, L, W, ptr, sinkK, S8, sink_off, Se)) {
     const int64_t chunks = 2 * (n / 8);
-    kv_append_vec_kernel<<<grid1(chunks, 256), 256, 0, s>>>((const bf16*)kown, (const bf16*)vtown, k_hs, vt_ps,
-                                                             (bf16*)ringK, (bf16*)ringVT, H, hd, L, W, ptr,
-                                                             (bf16*)sinkK, (bf16*)sinkVT, S8, sink_off, Se, ptr_dev);
+    const KvAppendArgs a{(const bf16*)kown, (const bf16*)vtown, k_hs, vt_ps, (bf16*)ringK, (bf16*)ringVT, H, hd, L,
+                         W, ptr, (bf16*)sinkK, (bf16*)sinkVT, S8, sink_off, Se, ptr_dev};
+    kv_append_vec_kernel<<<grid1(chunks, 256), 256, 0, s>>>(a);
     return hipGetLastError();
   }
   if (bf)

@@ -133,6 +133,12 @@ struct AttnArgs {
 // attention_combine() call (so the two passes can be timed apart).
 hipError_t attention(hipStream_t s, bool bf, const AttnArgs& a, bool combine = true);
 hipError_t attention_combine(hipStream_t s, const AttnArgs& a);
+// The combine pass of a split launch (none when nothing was split) and the
+// vectorised KV append k in one launch (k must satisfy kv_append_vec_ok).
+struct KvAppendArgs;
+hipError_t attention_combine_append(hipStream_t s, const AttnArgs& a, const KvAppendArgs& k);
+bool kv_append_vec_ok(bool bf, int64_t k_hs, int64_t vt_ps, int H, int hd, int L, int W, int ptr, const void* sinkK,
+                      int S8, int sink_off, int Se);
 // Queries per attention workgroup and resident attention workgroups per CU.
 int attention_q_tile(bool bf, int hd);
 int attention_wg_per_cu(bool bf, int hd);

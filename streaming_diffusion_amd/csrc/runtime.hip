@@ -11,6 +11,7 @@
 
 #include "host_state.h"
 #include "kernels.h"
+#include "kv_append.h"
 
 using sdk::AttnArgs;
 using sdk::KvSeg;
@@ -791,6 +792,8 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, const StepDyn* dd
   for (int b = 0; b < s->nb; ++b) {
     const void* blk = P(s->w.blk_mod, (int64_t)b * 6 * d, es);
     // self-attention
+    AttnArgs combine_args;
+    bool combine_pending = false;
     if (!ln_ready)
       PROF(SD_PROF_LN, 0.0, (4.0 + es) * M * d,
            sdk::ln_mod(st, bf, s->resid, s->xm, M, d, L, s->mod, blk, 0, d, 6 * d, 1e-6f));
@@ -865,11 +868,16 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, const StepDyn* dd
       PROF(SD_PROF_ATTN_SELF, 4.0 * R * L * (shared + so.count) * d,
            (double)es * d * (2.0 * R * L + 2.0 * shared + 2.0 * R * L), sdk::attention(st, bf, A, false));
       if (A.nsplit > 1 && A.h_full < H) {
-        const double hs = (double)(H - A.h_full) / H;     // share of the heads that were split
-        PROF(SD_PROF_ATTN_COMBINE, 0.0, hs * ((double)A.nsplit * R * L * (d * 2.0 + H * 8.0) + (double)R * L * d * es),
-             sdk::attention_combine(st, A));
+        combine_args = A;
+        combine_pending = true;
       }
     }
+    // the combine pass of the split heads (run below, in the append's launch
+    // when a single chunk leaves)
+    const double comb_bytes =
+        combine_pending ? (double)(H - combine_args.h_full) / H *
+                              ((double)combine_args.nsplit * R * L * (d * 2.0 + H * 8.0) + (double)R * L * d * es)
+                        : 0.0;
     // the leaving chunks append their K / V^T in push order (ring positions
     // ptr_old + k L); a capturing chunk also fills its sink entry, with B > 1
     // a refresh candidate stages its first S_e tokens
@@ -890,11 +898,27 @@ static sd_status run_forward(sd_stream* s, const RowTable& rt, const StepDyn* dd
       }
       if (s->Wt == 0 && !dK) continue;
       const int pk = s->Wt > 0 ? (int)(((int64_t)ptr_old + (int64_t)k * L) % s->Wt) : 0;
+      if (combine_pending && nexit == 1 &&
+          sdk::kv_append_vec_ok(bf, kv_hs, (int64_t)R * L, H, hd, L, s->Wt, pk, dK, dcap, doff, s->Se)) {
+        const sdk::KvAppendArgs ka{(const bf16*)P(s->kown, (int64_t)exit_rows[k] * L * hd, es),
+                                   (const bf16*)P(s->vtown, (int64_t)exit_rows[k] * L, es), kv_hs, (int64_t)R * L,
+                                   (bf16*)Pm(s->ringK, (int64_t)b * H * s->Wt * hd, es),
+                                   (bf16*)Pm(s->ringVT, (int64_t)b * H * s->Wt * hd, es), H, hd, L, s->Wt, pk,
+                                   (bf16*)dK, (bf16*)dVT, dcap, doff, s->Se, &dd->kv_pos[k]};
+        PROF(SD_PROF_ATTN_COMBINE, 0.0, comb_bytes + 4.0 * L * d * es,
+             sdk::attention_combine_append(st, combine_args, ka));
+        combine_pending = false;
+        continue;
+      }
       PROF(SD_PROF_KV, 0.0, 4.0 * L * d * es,
            sdk::kv_append(st, bf, P(s->kown, (int64_t)exit_rows[k] * L * hd, es), P(s->vtown, (int64_t)exit_rows[k] * L, es),
                           kv_hs, (int64_t)R * L,
                           Pm(s->ringK, (int64_t)b * H * s->Wt * hd, es), Pm(s->ringVT, (int64_t)b * H * s->Wt * hd, es),
                           H, hd, L, s->Wt, pk, dK, dVT, dcap, doff, s->Se, &dd->kv_pos[k]));
+    }
+    if (combine_pending) {
+      PROF(SD_PROF_ATTN_COMBINE, 0.0, comb_bytes, sdk::attention_combine(st, combine_args));
+      combine_pending = false;
     }
     {
       Epi E = epi_base(s, EPI_GATE_RESID);
