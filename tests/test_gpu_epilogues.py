@@ -468,6 +468,7 @@ def test_split_k_qkv_rope_and_fp16(lib):
     (128, 1536, 960, "resid", sdlib.SD_LN_PLAIN, True),    # cross-attention out -> feed-forward LayerNorm
     (100, 1024, 1536, "resid", sdlib.SD_LN_PLAIN, True),   # ragged rows
     (128, 520, 640, "gate", sdlib.SD_LN_PLAIN, True),      # width not a multiple of 256: a separate pass
+    (128, 1536, 960, "resid16", sdlib.SD_LN_PLAIN, True),  # fp16 operands (the folded cross-attention out)
 ])
 def test_residual_gemm_with_layernorm(lib, M, N, K, mode, form, with_blk):
     """A residual GEMM that also writes the LayerNorm of the updated rows
@@ -476,8 +477,9 @@ def test_residual_gemm_with_layernorm(lib, M, N, K, mode, form, with_blk):
     the GEMM followed by sd_k_ln_mod."""
     print(f"gemm + LN M={M} N={N} K={K} {mode} form={form}", flush=True)
     rng = np.random.default_rng(M + N + K)
-    A = to_dev(rng.standard_normal((M, K)), torch.bfloat16)
-    W = to_dev(0.02 * rng.standard_normal((N, K)), torch.bfloat16)
+    f16 = mode == "resid16"
+    A = to_dev(rng.standard_normal((M, K)), torch.float16 if f16 else torch.bfloat16)
+    W = to_dev(0.02 * rng.standard_normal((N, K)), torch.float16 if f16 else torch.bfloat16)
     b = to_dev(0.1 * rng.standard_normal(N), torch.bfloat16)
     Lr = M // 2 if M % 2 == 0 else M
     rows = M // Lr
@@ -492,7 +494,8 @@ def test_residual_gemm_with_layernorm(lib, M, N, K, mode, form, with_blk):
 
     def epi(resid, ln_out):
         e = sdlib.sd_gemm_epi(mode=sdlib.SD_EPI_GATE_RESID if mode == "gate" else sdlib.SD_EPI_RESID,
-                              bias=b.data_ptr(), resid=resid.data_ptr(), L=Lr, workspace=wsp, workspace_bytes=wsb)
+                              bias=b.data_ptr(), resid=resid.data_ptr(), L=Lr, workspace=wsp, workspace_bytes=wsb,
+                              f16=int(f16))
         if mode == "gate":
             e.mod, e.blk, e.gate_off, e.six_d = gmod.data_ptr(), gblk.data_ptr(), 5 * N, 6 * N
         if ln_out is not None:
