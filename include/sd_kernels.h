@@ -91,8 +91,8 @@ typedef struct {
                                   sm_heads groups of sm_cp (<= 128) columns of C + sm_bias (fp32
                                   [N]), N = sm_heads * sm_cp (the folded cross-attention's
                                   probabilities); on the few-row path the reduction pass writes it
-                                  and out is not written, otherwise C goes to out and a softmax
-                                  pass follows.  NULL: none. */
+                                  and out is not written, otherwise C goes to out (ldo = N, else
+                                  SD_ERR_SHAPE) and a softmax pass follows.  NULL: none. */
   const float* sm_bias;
   int32_t sm_heads, sm_cp;
 } sd_gemm_epi;

@@ -184,12 +184,14 @@ sd_status sd_k_gemm_epi(const void* A, const void* W, int32_t M, int32_t N, int3
     E.sm_cp = e->sm_cp;
   }
   const bool sm_fused = E.sm_out && sdk::gemm_fuses_softmax(M, N, K, E);
-  if (E.sm_out && !sm_fused) E.sm_out = nullptr;
+  if (E.sm_out && !sm_fused) {
+    if (E.ldo != N) return SD_ERR_SHAPE;          // the softmax pass reads C densely
+    E.sm_out = nullptr;
+  }
   const bool fused = E.ln_out && sdk::gemm_fuses_ln(M, N, K, E);
   hipError_t r = e->f16 ? sdk::gemm_mfma_f16((hipStream_t)stream, A, W, M, N, K, E)
                         : sdk::gemm_mfma((hipStream_t)stream, A, W, M, N, K, E);
   if (r == hipSuccess && e->sm_out && !sm_fused) {
-    if (E.ldo != N) return SD_ERR_SHAPE;          // the softmax pass reads C densely
     r = sdk::ctx_softmax((hipStream_t)stream, (const float*)E.out, e->sm_bias, (f16*)e->sm_out, M, e->sm_heads,
                          e->sm_cp);
   }

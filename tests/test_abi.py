@@ -280,6 +280,25 @@ def test_gemm_epi_and_ln_mod_reject_bad_arguments_before_any_device_call(lib):
     e.rope, e.rope_table, e.Hp, e.Wp, e.rope_positions = 1, 8, 8, 8, 4
     e.t0[0], e.t0[1] = 0, 4
     assert lib.sd_k_gemm_epi(8, 8, 128, 192, 64, C.byref(e), None) == L.SD_ERR_SHAPE    # position 4 not in table
+    # the fused LayerNorm only after a residual epilogue, fp16 form without modulation, slots inside the rows
+    e = L.sd_gemm_epi(mode=L.SD_EPI_F32, out=8, ldo=64, ln_out=8)
+    assert lib.sd_k_gemm_epi(8, 8, 64, 64, 64, C.byref(e), None) == L.SD_ERR_ARG
+    e = L.sd_gemm_epi(mode=L.SD_EPI_RESID, resid=8, ln_out=8, ln_form=L.SD_LN_F16, ln_mod=8, ln_six_d=384)
+    assert lib.sd_k_gemm_epi(8, 8, 64, 64, 64, C.byref(e), None) == L.SD_ERR_ARG
+    e = L.sd_gemm_epi(mode=L.SD_EPI_RESID, resid=8, ln_out=8, ln_form=3)
+    assert lib.sd_k_gemm_epi(8, 8, 64, 64, 64, C.byref(e), None) == L.SD_ERR_ARG
+    e = L.sd_gemm_epi(mode=L.SD_EPI_RESID, resid=8, ln_out=8, ln_mod=8, ln_shift_off=0, ln_scale_off=340,
+                      ln_six_d=384)
+    assert lib.sd_k_gemm_epi(8, 8, 64, 64, 64, C.byref(e), None) == L.SD_ERR_SHAPE      # scale beyond the row
+    # the fused softmax only on F32 without bias, groups covering N, scores dense when not fused
+    e = L.sd_gemm_epi(mode=L.SD_EPI_RESID, resid=8, sm_out=8, sm_bias=8, sm_heads=2, sm_cp=32)
+    assert lib.sd_k_gemm_epi(8, 8, 64, 64, 64, C.byref(e), None) == L.SD_ERR_ARG
+    e = L.sd_gemm_epi(mode=L.SD_EPI_F32, out=8, ldo=64, bias=8, sm_out=8, sm_bias=8, sm_heads=2, sm_cp=32)
+    assert lib.sd_k_gemm_epi(8, 8, 64, 64, 64, C.byref(e), None) == L.SD_ERR_ARG
+    e = L.sd_gemm_epi(mode=L.SD_EPI_F32, out=8, ldo=64, sm_out=8, sm_bias=8, sm_heads=3, sm_cp=32)
+    assert lib.sd_k_gemm_epi(8, 8, 64, 64, 64, C.byref(e), None) == L.SD_ERR_SHAPE      # 3 x 32 != 64
+    e = L.sd_gemm_epi(mode=L.SD_EPI_F32, out=8, ldo=72, sm_out=8, sm_bias=8, sm_heads=2, sm_cp=32)
+    assert lib.sd_k_gemm_epi(8, 8, 64, 64, 64, C.byref(e), None) == L.SD_ERR_SHAPE      # unfused, ldo != N
     e = L.sd_gemm_epi(mode=L.SD_EPI_HEAD, bias=8, eps=8, L=64, C=4, p=2, T=1, Hp=8, Wp=8, Hl=16, Wl=15)
     assert lib.sd_k_gemm_epi(8, 8, 64, 16, 128, C.byref(e), None) == L.SD_ERR_SHAPE
     assert lib.sd_k_ln_mod(1, 8, 8, 4, 5124, 1, None, None, 0, 0, 0, 0, None) == L.SD_ERR_SHAPE
